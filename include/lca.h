@@ -1,0 +1,192 @@
+/*
+ * lca.h -- C ABI of the MI355X (gfx950) compressed-attention library.
+ *
+ * The library implements the data-parallel hot path of the hybrid attention
+ * described on the DeepSeek-V4 pages:
+ *   [R] "DeepSeek-V4 中文翻译" (cnblogs translation of the technical report
+ *       "DeepSeek-V4: Towards Highly Efficient Million-Token Context
+ *       Intelligence"), section 2.3 and 5.2.1;
+ *   [H] "DeepSeek-V4：百万 token 上下文，真正可供 Agent 使用" (translation of the
+ *       Hugging Face blog post), section "混合注意力：CSA 与 HCA".
+ * CSA = compressor (m = 4) -> lightning indexer -> top-k -> shared-KV MQA over
+ * the selected entries plus a sliding window; HCA = compressor (m' = 128) ->
+ * dense shared-KV MQA over every visible entry plus the window.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every tensor argument is DEVICE memory owned by the caller, row-major and
+ *   contiguous, 16-byte aligned.  The library never allocates, frees or
+ *   synchronises; each call enqueues its kernels on `stream` (a hipStream_t
+ *   passed as void*, NULL = the null stream) and returns at once.
+ * - Position arrays (`first_pos`, `q_pos`, length B) are HOST memory, read
+ *   during the call; B <= LCA_MAX_BATCH.
+ * - All arguments are validated on the host before anything is launched: on
+ *   error the call returns a nonzero status, enqueues nothing and leaves every
+ *   output untouched; lca_last_error() then describes the problem.
+ * - Raw position p of a sequence is the p-th token.  Compressed entry s of a
+ *   stream with ratio m pools raw rows [s*m, s*m + m).  Entry s is visible to
+ *   a query at position t iff its last row is not after t:
+ *   vis(t) = floor((t + 1) / m) entries are visible.
+ *
+ * KV storage (lca_kv) -- [R] 2.3.4: FP8 storage for most dims, BF16 for the
+ * RoPE dims.  Three formats, as planes of one row per entry:
+ *   LCA_F32 : nope f32 [B][cap][d_nope], rope f32 [B][cap][d_rope]
+ *   LCA_BF16: nope bf16, rope bf16
+ *   LCA_FP8 : nope OCP e4m3fn bytes [B][cap][d_nope] with one f32 power-of-two
+ *             scale per 128 nope dims, scale [B][cap][d_nope/128]; rope bf16.
+ *             Stored value = code * scale (exact in bf16).
+ * The attended vector of a row is nope ++ rope (c = d_nope + d_rope dims).
+ */
+#ifndef LCA_H
+#define LCA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LCA_VERSION 1
+#define LCA_MAX_BATCH 64
+
+/* status codes */
+#define LCA_OK 0
+#define LCA_EINVAL 1      /* null pointer, bad flag or enum value          */
+#define LCA_ESHAPE 2      /* inconsistent or unsupported sizes             */
+#define LCA_EDTYPE 3      /* unsupported dtype / storage format            */
+#define LCA_EALIGN 4      /* pointer not 16-byte aligned                   */
+#define LCA_EWORKSPACE 5  /* workspace missing or too small                */
+#define LCA_EHIP 6        /* the HIP runtime refused a launch              */
+
+/* dtypes / storage formats */
+#define LCA_F32 0
+#define LCA_BF16 1
+#define LCA_FP8 2         /* KV storage only (see above)                   */
+
+typedef struct lca_kv {
+    void* nope;       /* [B][cap][d_nope]                                  */
+    void* rope;       /* [B][cap][d_rope]; may be NULL when d_rope == 0    */
+    float* scale;     /* [B][cap][d_nope/128] for LCA_FP8, else NULL       */
+    int32_t fmt;      /* LCA_F32 / LCA_BF16 / LCA_FP8                      */
+    int32_t d_nope;
+    int32_t d_rope;   /* even                                              */
+    int64_t cap;      /* rows per sequence (batch stride = cap rows)       */
+} lca_kv;
+
+/*
+ * lca_kv_compress -- the compressor of [R] 2.3.1 ("compressed KV entries")
+ * and 2.3.2, [H] CSA/HCA: softmax-gated pooling with a learnable
+ * per-position bias, then RMSNorm ([R] 2.3.3), partial RoPE ([R] 2.3.3) and
+ * the store into `out`.
+ *
+ * Inputs c_a, z_a, c_b, z_b: [B][n_rows][c], dtype in_dtype (LCA_F32 or
+ * LCA_BF16), c = out.d_nope + out.d_rope; row i of sequence b is position
+ * first_pos[b] + i.  bias_a, bias_b: f32 [m][c] (NULL = zero).  For entry s
+ * and channel j the logits are z_a[s*m+i][j] + bias_a[i][j] (i < m) and, when
+ * overlap != 0 and s >= 1, z_b[(s-1)*m+i][j] + bias_b[i][j]; one softmax over
+ * them weights the matching c_a / c_b values.  c_b, z_b may be NULL when
+ * overlap == 0.  gamma: f32 [c] RMSNorm weight over all c dims with epsilon
+ * eps, NULL = no norm.  rope_theta > 0: rotate dims [d_nope, c) (half-split
+ * pairs (i, i + d_rope/2), inverse frequency theta^(-2i/d_rope)) by the
+ * entry's first position s*m; 0 = no rotation.
+ *
+ * Entries written: exactly those s whose rows are all in range -- block s,
+ * and block s-1 when overlap != 0 and s >= 1.  Entry s goes to row s of
+ * sequence b in `out` (ring != 0: row s mod out.cap, and only the newest
+ * out.cap entries of the call are written).  m = 1 with overlap = 0 is the
+ * raw-row store used for the sliding window.
+ * Errors: LCA_EINVAL (null inputs, m < 1, overlap not 0/1), LCA_EDTYPE,
+ * LCA_ESHAPE (B out of range, c != d_nope + d_rope, fp8 with d_nope % 128,
+ * a non-ring entry row >= cap), LCA_EALIGN.
+ */
+int lca_kv_compress(const void* c_a, const void* z_a, const void* c_b, const void* z_b,
+                    int32_t in_dtype, const float* bias_a, const float* bias_b,
+                    const float* gamma, float eps, double rope_theta,
+                    int32_t m, int32_t overlap, int32_t B, int64_t n_rows,
+                    const int64_t* first_pos, lca_kv out, int32_t ring, void* stream);
+
+/*
+ * lca_indexer_score -- the lightning indexer of [R] 2.3.1 and [H] CSA: a
+ * multi-head dot product scored by ReLU between each query and every
+ * compressed indexer key, with BF16 scores as in [R] 5.2.1.
+ *   S[b][i][s] = sum_h w[b][i][h] * max(0, q[b][i][h] . k[b][s])   for s < vis(t)
+ * with t = q_pos[b] + i; columns s >= vis(t) are left unspecified.
+ * q: [B][T][H_I][d_I], k: [B][k_cap][d_I] (one key per compressed entry,
+ * shared by all indexer heads), both in_dtype (LCA_BF16, or LCA_F32);
+ * w: f32 [B][T][H_I] (NULL = all ones).  scores: [B][T][s_stride] of
+ * score_dtype (LCA_F32, or LCA_BF16 = nearest-even rounding of the f32
+ * score, -0 stored as +0).  Arithmetic: products accumulated in f32.
+ * Requires vis(q_pos[b] + T - 1) <= min(k_cap, s_stride); d_I % 32 == 0,
+ * H_I <= 64.
+ */
+int lca_indexer_score(const void* q, const float* w, const void* k, int32_t in_dtype,
+                      int64_t k_cap, int32_t H_I, int32_t d_I, int32_t B, int32_t T,
+                      const int64_t* q_pos, int32_t m, void* scores, int32_t score_dtype,
+                      int64_t s_stride, void* stream);
+
+/*
+ * lca_topk_select -- the top-k selector of [R] 2.3.1 (keeps a subset of the
+ * compressed entries for the core attention).  For row (b, i) with
+ * t = q_pos[b] + i the candidates are s < vis(t); the K = min(k, vis(t))
+ * entries with the largest scores are kept, ties broken by the lower index
+ * (-0 equals +0); idx[b][i][0..K) lists them in ascending order and the rest
+ * of the row is -1.  scores: [B][T][s_stride] (LCA_F32 or LCA_BF16, finite);
+ * idx: int32 [B][T][k].  ws: device workspace of at least
+ * lca_topk_workspace_size(...) bytes (may be NULL when that is 0).
+ */
+int lca_topk_select(const void* scores, int32_t score_dtype, int64_t s_stride, int32_t B,
+                    int32_t T, const int64_t* q_pos, int32_t m, int32_t k, int32_t* idx,
+                    void* ws, size_t ws_bytes, void* stream);
+size_t lca_topk_workspace_size(int32_t B, int32_t T, int64_t s_stride, int32_t k);
+
+/*
+ * lca_csa_attn -- CSA core attention, [R] 2.3.1 (shared-KV MQA: each stored
+ * row is both key and value, one KV head for all H query heads) and 2.3.3
+ * (sliding-window branch, attention sink, output RoPE).  For query row
+ * (b, i), t = q_pos[b] + i, head h, the attended rows are
+ *   comp rows idx[b][i][j] >= 0 (j < k)  and  window rows p in
+ *   [max(0, t - n_win + 1), t], stored at win row p mod win.cap,
+ * under one softmax with logits sm_scale * <q[b][i][h], row> and an optional
+ * sink logit sink[h] that adds e^sink[h] to the denominator only:
+ *   o = sum_j e^(l_j - mu) row_j / (e^(sink - mu) + sum_j e^(l_j - mu)).
+ * rope_theta > 0: the last d_rope dims of o are rotated by -t (same pairing
+ * as lca_kv_compress).  lse (f32 [B][T][H], NULL = skip) = mu + ln(den).
+ * An empty set without a sink gives o = 0, lse = -inf.
+ * q: [B][T][H][c] (LCA_BF16, or LCA_F32 with f32 caches); out: [B][T][H][c]
+ * of out_dtype (LCA_F32 or LCA_BF16).  comp and win share d_nope / d_rope;
+ * supported shapes: (d_nope, d_rope) = (512, 64) with H % 16 == 0 for
+ * bf16/fp8 caches, any c <= 1024 for f32.  The window ring must hold every
+ * needed row: n_win + T - 1 <= win.cap (n_win = 0: no window).  Every
+ * idx value must be < comp.cap.  ws: device workspace of at least
+ * lca_attn_workspace_size(B, T, H, c, max keys per query) bytes.
+ */
+int lca_csa_attn(const void* q, int32_t q_dtype, int32_t H, int32_t B, int32_t T,
+                 const int64_t* q_pos, lca_kv comp, int32_t m, const int32_t* idx, int32_t k,
+                 lca_kv win, int32_t n_win, const float* sink, float sm_scale, double rope_theta,
+                 void* out, int32_t out_dtype, float* lse, void* ws, size_t ws_bytes,
+                 void* stream);
+
+/*
+ * lca_hca_attn -- HCA core attention, [R] 2.3.2 and [H] HCA: as lca_csa_attn
+ * but over EVERY visible compressed entry s < vis(t) (dense attention over the
+ * heavily compressed stream) plus the same window.  Requires
+ * vis(q_pos[b] + T - 1) <= comp.cap.
+ */
+int lca_hca_attn(const void* q, int32_t q_dtype, int32_t H, int32_t B, int32_t T,
+                 const int64_t* q_pos, lca_kv comp, int32_t m, lca_kv win, int32_t n_win,
+                 const float* sink, float sm_scale, double rope_theta, void* out,
+                 int32_t out_dtype, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for lca_csa_attn / lca_hca_attn with at most max_keys
+ * attended rows per query (selected or visible entries + window). */
+size_t lca_attn_workspace_size(int32_t B, int32_t T, int32_t H, int32_t c, int64_t max_keys);
+
+/* Message for the last failed call on this thread ("" if none). */
+const char* lca_last_error(void);
+int lca_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,190 @@
+"""Python binding of the MI355X compressed-attention library (liblca.so, C ABI in include/lca.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  torch supplies device memory and the current stream.  There is no
+fallback: when the built library is missing every call raises.
+
+Calls (same names as the C ABI):
+    kv_compress, indexer_score, topk_select, csa_attn, hca_attn
+and helpers KV (the lca_kv storage planes), attn_workspace_size.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+import torch
+
+F32, BF16, FP8 = 0, 1, 2
+MAX_BATCH = 64
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblca.so")
+_lib = None
+
+
+class LcaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"lca error {code}: {msg}")
+        self.code = code
+
+
+class _KV(C.Structure):
+    _fields_ = [("nope", C.c_void_p), ("rope", C.c_void_p), ("scale", C.c_void_p),
+                ("fmt", C.c_int32), ("d_nope", C.c_int32), ("d_rope", C.c_int32),
+                ("cap", C.c_int64)]
+
+
+def lib():
+    """Load liblca.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m long_context_attention_22_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        vp, i32, i64, f32, f64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_double, C.c_size_t
+        L.lca_version.restype = C.c_int
+        L.lca_last_error.restype = C.c_char_p
+        L.lca_kv_compress.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, f32, f64, i32, i32, i32, i64, vp,
+                                      _KV, i32, vp]
+        L.lca_indexer_score.argtypes = [vp, vp, vp, i32, i64, i32, i32, i32, i32, vp, i32, vp, i32, i64,
+                                        vp]
+        L.lca_topk_select.argtypes = [vp, i32, i64, i32, i32, vp, i32, i32, vp, vp, sz, vp]
+        L.lca_topk_workspace_size.argtypes = [i32, i32, i64, i32]
+        L.lca_topk_workspace_size.restype = sz
+        L.lca_csa_attn.argtypes = [vp, i32, i32, i32, i32, vp, _KV, i32, vp, i32, _KV, i32, vp, f32, f64,
+                                   vp, i32, vp, vp, sz, vp]
+        L.lca_hca_attn.argtypes = [vp, i32, i32, i32, i32, vp, _KV, i32, _KV, i32, vp, f32, f64, vp, i32,
+                                   vp, vp, sz, vp]
+        L.lca_attn_workspace_size.argtypes = [i32, i32, i32, i32, i64]
+        L.lca_attn_workspace_size.restype = sz
+        for name in ("lca_kv_compress", "lca_indexer_score", "lca_topk_select", "lca_csa_attn",
+                     "lca_hca_attn"):
+            getattr(L, name).restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _pos(p, B: int):
+    arr = (C.c_int64 * B)(*[int(x) for x in (p if hasattr(p, "__len__") else [p] * B)])
+    return arr
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise LcaError(rc, lib().lca_last_error().decode())
+
+
+@dataclass
+class KV:
+    """Storage planes of one KV stream: nope [B][cap][d_nope], rope [B][cap][d_rope], scale [B][cap][d_nope/128]."""
+    nope: torch.Tensor
+    rope: torch.Tensor | None
+    scale: torch.Tensor | None
+    fmt: int
+    d_nope: int
+    d_rope: int
+    cap: int
+
+    @staticmethod
+    def empty(fmt: int, B: int, cap: int, d_nope: int, d_rope: int, device="cuda") -> "KV":
+        if fmt == F32:
+            nope = torch.zeros(B, cap, d_nope, dtype=torch.float32, device=device)
+            rope = torch.zeros(B, cap, d_rope, dtype=torch.float32, device=device)
+            scale = None
+        elif fmt == BF16:
+            nope = torch.zeros(B, cap, d_nope, dtype=torch.bfloat16, device=device)
+            rope = torch.zeros(B, cap, d_rope, dtype=torch.bfloat16, device=device)
+            scale = None
+        elif fmt == FP8:
+            nope = torch.zeros(B, cap, d_nope, dtype=torch.uint8, device=device)
+            rope = torch.zeros(B, cap, d_rope, dtype=torch.bfloat16, device=device)
+            scale = torch.ones(B, cap, d_nope // 128, dtype=torch.float32, device=device)
+        else:
+            raise ValueError(fmt)
+        return KV(nope, rope if d_rope > 0 else None, scale, fmt, d_nope, d_rope, cap)
+
+    @property
+    def B(self) -> int:
+        return self.nope.shape[0]
+
+    def c(self) -> _KV:
+        return _KV(self.nope.data_ptr(), 0 if self.rope is None else self.rope.data_ptr(),
+                   0 if self.scale is None else self.scale.data_ptr(), self.fmt, self.d_nope,
+                   self.d_rope, self.cap)
+
+
+def kv_compress(c_a, z_a, c_b, z_b, out: KV, *, m: int, overlap: int, first_pos, bias_a=None,
+                bias_b=None, gamma=None, eps: float = 1e-6, rope_theta: float = 0.0, ring: int = 0,
+                stream=None):
+    B, n_rows, _ = c_a.shape
+    _check(lib().lca_kv_compress(_ptr(c_a), _ptr(z_a), _ptr(c_b), _ptr(z_b), _dtype(c_a), _ptr(bias_a),
+                                 _ptr(bias_b), _ptr(gamma), float(eps), float(rope_theta), int(m),
+                                 int(overlap), int(B), int(n_rows), _pos(first_pos, B), out.c(),
+                                 int(ring), _stream(stream)))
+
+
+def indexer_score(q, w, k, scores, *, q_pos, m: int, stream=None):
+    """q [B][T][H_I][d_I], w [B][T][H_I] f32 or None, k [B][k_cap][d_I], scores [B][T][s_stride]."""
+    B, T, H_I, d_I = q.shape
+    _check(lib().lca_indexer_score(_ptr(q), _ptr(w), _ptr(k), _dtype(q), int(k.shape[1]), int(H_I),
+                                   int(d_I), int(B), int(T), _pos(q_pos, B), int(m), _ptr(scores),
+                                   _dtype(scores), int(scores.shape[2]), _stream(stream)))
+
+
+def topk_select(scores, idx, *, q_pos, m: int, ws=None, stream=None):
+    """scores [B][T][s_stride] -> idx [B][T][k] int32."""
+    B, T, s_stride = scores.shape
+    k = idx.shape[2]
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().lca_topk_select(_ptr(scores), _dtype(scores), int(s_stride), int(B), int(T),
+                                 _pos(q_pos, B), int(m), int(k), _ptr(idx), _ptr(ws), nbytes,
+                                 _stream(stream)))
+
+
+def attn_workspace_size(B: int, T: int, H: int, c: int, max_keys: int) -> int:
+    return int(lib().lca_attn_workspace_size(int(B), int(T), int(H), int(c), int(max_keys)))
+
+
+def _empty_kv():
+    return _KV(0, 0, 0, 0, 0, 0, 0)
+
+
+def csa_attn(q, out, *, q_pos, comp: KV, m: int, idx, win: KV | None, n_win: int, sink=None,
+             sm_scale: float, rope_theta: float = 0.0, lse=None, ws=None, stream=None):
+    B, T, H, _ = q.shape
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().lca_csa_attn(_ptr(q), _dtype(q), int(H), int(B), int(T), _pos(q_pos, B), comp.c(),
+                              int(m), _ptr(idx), int(idx.shape[2]),
+                              win.c() if win is not None else _empty_kv(), int(n_win), _ptr(sink),
+                              float(sm_scale), float(rope_theta), _ptr(out), _dtype(out), _ptr(lse),
+                              _ptr(ws), nbytes, _stream(stream)))
+
+
+def hca_attn(q, out, *, q_pos, comp: KV, m: int, win: KV | None, n_win: int, sink=None,
+             sm_scale: float, rope_theta: float = 0.0, lse=None, ws=None, stream=None):
+    B, T, H, _ = q.shape
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().lca_hca_attn(_ptr(q), _dtype(q), int(H), int(B), int(T), _pos(q_pos, B), comp.c(),
+                              int(m), win.c() if win is not None else _empty_kv(), int(n_win),
+                              _ptr(sink), float(sm_scale), float(rope_theta), _ptr(out), _dtype(out),
+                              _ptr(lse), _ptr(ws), nbytes, _stream(stream)))

@@ -1,0 +1,486 @@
+// attn.hip -- core attention of the DeepSeek-V4 hybrid attention
+// ("DeepSeek-V4 中文翻译" sections 2.3.1 - 2.3.3): shared-KV MQA (each stored
+// row is both key and value, one KV head for every query head) over
+//   CSA: the top-k selected compressed entries, or
+//   HCA: every visible compressed entry,
+// plus the sliding window of raw rows, with a per-head sink logit and RoPE
+// applied to the output by -t.
+//
+// bf16 / fp8 caches, c = 512 + 64, H a multiple of 16 (up to 64): MFMA path.
+//   One workgroup (4 waves) per (query row, key split).  The attended rows are
+//   a list of "slots": compressed slots (idx entries, or 0..vis-1) followed by
+//   window slots.  Per tile of 32 slots the workgroup gathers the rows from HBM
+//   (fp8 codes are expanded to bf16 exactly: the scale is a power of two) into
+//   LDS twice: row-major (K operand of Q.K^T, 16 contiguous bytes per lane) and
+//   transposed (V operand of P.V, 8 consecutive keys of one dim per lane).  The
+//   next tile's rows are fetched into registers while the current tile is
+//   computed.  Wave w owns heads [16w, 16w+16): S = Q K^T with
+//   v_mfma_f32_16x16x32_bf16 (M = heads, N = keys, K = 576 in 18 steps, Q kept
+//   in registers), online softmax in the accumulator layout (row max / sum over
+//   16 lanes), P goes through a small per-wave LDS buffer into A-operand
+//   layout as a bf16 hi + lo pair, O += P V (N = 576 dims in 36 blocks, O
+//   kept in registers).
+//   Decode-sized launches split the slot list across workgroups; a second
+//   kernel merges the partial (O, max, sum) triples in a fixed order.
+// f32 caches: one wave per (query row, head), f32 FMA, for fp32 workloads.
+#include "device.h"
+#include "kernels.h"
+
+namespace lca {
+
+constexpr int kDN = 512, kDR = 64, kC = 576;
+constexpr int kKT = 32;             // slots per tile
+constexpr int kKS = kC + 8;         // row stride of the row-major tile (bf16 elements)
+constexpr int kVS = kKT + 8;        // row stride of the transposed tile
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct SlotMap {
+    int64_t ncs;    // compressed slots
+    int64_t w_lo;   // first window position
+    int64_t nslots;
+};
+
+__device__ __forceinline__ SlotMap slot_map(const AttnArgs& a, int64_t t) {
+    SlotMap s;
+    const int64_t vis = min((t + 1) / a.m, a.comp.cap);
+    s.ncs = a.idx ? (int64_t)a.k : vis;
+    s.w_lo = t - a.n_win + 1 < 0 ? 0 : t - a.n_win + 1;
+    const int64_t nw = a.n_win > 0 ? t - s.w_lo + 1 : 0;
+    s.nslots = s.ncs + nw;
+    return s;
+}
+
+// source row of a slot: 0 = invalid, 1 = compressed row, 2 = window row
+__device__ __forceinline__ int slot_row(const AttnArgs& a, const SlotMap& sm, int64_t rowid, int b,
+                                        int64_t slot, int64_t s_end, int64_t* row) {
+    if (slot >= s_end) return 0;
+    if (slot < sm.ncs) {
+        int64_t e = a.idx ? (int64_t)a.idx[rowid * a.k + slot] : slot;
+        if (e < 0 || e >= a.comp.cap) return 0;
+        *row = (int64_t)b * a.comp.cap + e;
+        return 1;
+    }
+    const int64_t p = sm.w_lo + (slot - sm.ncs);
+    *row = (int64_t)b * a.win.cap + p % a.win.cap;
+    return 2;
+}
+
+// One 16-byte chunk per (slot, chunk) of the gathered tile, held in registers.
+// bf16 rows: 72 chunks of 8 dims; fp8 rows: 32 chunks of 16 codes + 8 rope chunks.
+template <int FMT>
+struct Gather {
+    static constexpr int kChunks = FMT == LCA_FP8 ? 5 : 9;  // per thread
+    u32x4 v[kChunks];
+    float sc[FMT == LCA_FP8 ? 4 : 1];
+    int src;
+
+    __device__ __forceinline__ void load(const AttnArgs& a, const SlotMap& sm, int64_t rowid, int b,
+                                         int64_t slot, int64_t s_end, int cg) {
+        int64_t row = 0;
+        src = slot_row(a, sm, rowid, b, slot, s_end, &row);
+        const lca_kv& kv = src == 2 ? a.win : a.comp;
+#pragma unroll
+        for (int u = 0; u < kChunks; ++u) v[u] = u32x4{0u, 0u, 0u, 0u};
+        if (!src) return;
+        if (FMT == LCA_FP8) {
+            const u32x4* np = (const u32x4*)((const uint8_t*)kv.nope + row * kDN);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = np[cg + 8 * u];
+            v[4] = ((const u32x4*)((const uint16_t*)kv.rope + row * kDR))[cg];
+            // chunk cg + 8u covers dims 16(cg + 8u) .. +15: scale group (cg + 8u) / 8 = u
+#pragma unroll
+            for (int u = 0; u < 4; ++u) sc[u] = kv.scale[row * 4 + u];
+        } else {
+            const u32x4* np = (const u32x4*)((const uint16_t*)kv.nope + row * kDN);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = np[cg + 8 * u];
+            v[8] = ((const u32x4*)((const uint16_t*)kv.rope + row * kDR))[cg];
+        }
+    }
+};
+
+__device__ __forceinline__ void put8(uint16_t* Kt, uint16_t* Vt, int j, int d0, u32x4 v) {
+    *(u32x4*)(Kt + j * kKS + d0) = v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        Vt[(d0 + 2 * e) * kVS + j] = (uint16_t)(v[e] & 0xffffu);
+        Vt[(d0 + 2 * e + 1) * kVS + j] = (uint16_t)(v[e] >> 16);
+    }
+}
+
+// fp8 code -> bf16 bits of code * scale (exact)
+__device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t two_codes, float sc) {
+    const float lo = fp8_to_f32(two_codes & 0xffu) * sc;
+    const float hi = fp8_to_f32((two_codes >> 8) & 0xffu) * sc;
+    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+}
+
+template <int FMT>
+__device__ __forceinline__ void store_tile(const Gather<FMT>& g, uint16_t* Kt, uint16_t* Vt, int j,
+                                           int cg) {
+    if (FMT == LCA_FP8) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int d0 = 16 * (cg + 8 * u);
+            u32x4 lo, hi;
+            lo[0] = fp8x2_bf16(g.v[u][0], g.sc[u]);
+            lo[1] = fp8x2_bf16(g.v[u][0] >> 16, g.sc[u]);
+            lo[2] = fp8x2_bf16(g.v[u][1], g.sc[u]);
+            lo[3] = fp8x2_bf16(g.v[u][1] >> 16, g.sc[u]);
+            hi[0] = fp8x2_bf16(g.v[u][2], g.sc[u]);
+            hi[1] = fp8x2_bf16(g.v[u][2] >> 16, g.sc[u]);
+            hi[2] = fp8x2_bf16(g.v[u][3], g.sc[u]);
+            hi[3] = fp8x2_bf16(g.v[u][3] >> 16, g.sc[u]);
+            if (!g.src) lo = hi = u32x4{0u, 0u, 0u, 0u};
+            put8(Kt, Vt, j, d0, lo);
+            put8(Kt, Vt, j, d0 + 8, hi);
+        }
+        put8(Kt, Vt, j, kDN + 8 * cg, g.v[4]);
+    } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) put8(Kt, Vt, j, 8 * (cg + 8 * u), g.v[u]);
+        put8(Kt, Vt, j, kDN + 8 * cg, g.v[8]);
+    }
+}
+
+template <int FMT>
+__global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int64_t split_len, int nsplit) {
+    __shared__ __attribute__((aligned(16))) uint16_t Kt[kKT * kKS];
+    __shared__ __attribute__((aligned(16))) uint16_t Vt[kC * kVS];
+    __shared__ __attribute__((aligned(16))) uint16_t Ps[4][32 * kVS];
+    __shared__ int valid[kKT];
+
+    const int64_t rowid = blockIdx.x;
+    const int split = blockIdx.y;
+    const int b = (int)(rowid / a.T);
+    const int64_t t = a.q_pos.v[b] + rowid % a.T;
+    const SlotMap sm = slot_map(a, t);
+    const int64_t s_begin = (int64_t)split * split_len;
+    const int64_t s_end = min(sm.nslots, s_begin + split_len);
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int hrow = lane & 15, kgrp = lane >> 4;
+    const int h0 = 16 * wv;
+
+    // Q fragments: A[row = head h0 + hrow][k = 32 ks + 8 kgrp + e]
+    bf16x8 qf[18];
+    {
+        const bool hv = h0 + hrow < a.H;
+        const u32x4* qp = (const u32x4*)((const uint16_t*)a.q + ((rowid * a.H) + h0 + hrow) * kC);
+#pragma unroll
+        for (int ks = 0; ks < 18; ++ks)
+            qf[ks] = __builtin_bit_cast(bf16x8, hv ? qp[4 * ks + kgrp] : u32x4{0u, 0u, 0u, 0u});
+    }
+    f32x4 o[36];
+#pragma unroll
+    for (int nb = 0; nb < 36; ++nb) o[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float mrun[4], lrun[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        mrun[r] = -INFINITY;
+        lrun[r] = 0.0f;
+    }
+    const float qk_scale = a.sm_scale * kLog2e;
+
+    const int gj = tid & 31, gcg = tid >> 5;  // gather role: slot gj, chunk group gcg
+    Gather<FMT> g;
+    if (s_begin < s_end) g.load(a, sm, rowid, b, s_begin + gj, s_end, gcg);
+
+    for (int64_t s0 = s_begin; s0 < s_end; s0 += kKT) {
+        __syncthreads();  // previous tile fully consumed
+        store_tile<FMT>(g, Kt, Vt, gj, gcg);
+        if (gcg == 0) valid[gj] = g.src != 0;
+        __syncthreads();
+        if (s0 + kKT < s_end) g.load(a, sm, rowid, b, s0 + kKT + gj, s_end, gcg);
+
+        // S = Q K^T for two 16-slot blocks
+        f32x4 s[2];
+#pragma unroll
+        for (int bl = 0; bl < 2; ++bl) {
+            s[bl] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            const uint16_t* kr = Kt + (16 * bl + hrow) * kKS + 8 * kgrp;
+#pragma unroll
+            for (int ks = 0; ks < 18; ++ks) {
+                const bf16x8 kb = __builtin_bit_cast(bf16x8, *(const u32x4*)(kr + 32 * ks));
+                s[bl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], kb, s[bl], 0, 0, 0);
+            }
+        }
+        // online softmax; lane holds rows (heads) 4 kgrp + r, columns (slots) hrow and 16 + hrow
+        const bool v0 = valid[hrow], v1 = valid[16 + hrow];
+        float p0[4], p1[4], corr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float x0 = v0 ? s[0][r] * qk_scale : -INFINITY;
+            const float x1 = v1 ? s[1][r] * qk_scale : -INFINITY;
+            const float mx = max16(fmaxf(x0, x1));
+            const float mnew = fmaxf(mrun[r], mx);
+            const float muse = mnew == -INFINITY ? 0.0f : mnew;
+            p0[r] = exp2f(x0 - muse);
+            p1[r] = exp2f(x1 - muse);
+            corr[r] = exp2f(mrun[r] - muse);
+            lrun[r] = lrun[r] * corr[r] + sum16(p0[r] + p1[r]);
+            mrun[r] = mnew;
+        }
+#pragma unroll
+        for (int nb = 0; nb < 36; ++nb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[nb][r] *= corr[r];
+        // P through LDS into A layout, A[row = head hrow][k = slot 8 kgrp + e], as two bf16
+        // terms P = hi + lo (hi = bf16(P), lo = bf16(P - hi)): both multiply the same V
+        // fragment, so P V keeps ~16 mantissa bits at no extra LDS traffic.
+        uint16_t* pw = Ps[wv];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint16_t h0b = f2bf(p0[r]), h1b = f2bf(p1[r]);
+            pw[(4 * kgrp + r) * kVS + hrow] = h0b;
+            pw[(4 * kgrp + r) * kVS + 16 + hrow] = h1b;
+            pw[(16 + 4 * kgrp + r) * kVS + hrow] = f2bf(p0[r] - bf2f(h0b));
+            pw[(16 + 4 * kgrp + r) * kVS + 16 + hrow] = f2bf(p1[r] - bf2f(h1b));
+        }
+        __syncthreads();
+        const bf16x8 pa = __builtin_bit_cast(bf16x8, *(const u32x4*)(pw + hrow * kVS + 8 * kgrp));
+        const bf16x8 pl = __builtin_bit_cast(bf16x8, *(const u32x4*)(pw + (16 + hrow) * kVS + 8 * kgrp));
+        // O += P V: B[k = slot 8 kgrp + e][n = dim 16 nb + hrow]
+        const uint16_t* vr = Vt + hrow * kVS + 8 * kgrp;
+#pragma unroll
+        for (int nb = 0; nb < 36; ++nb) {
+            const bf16x8 vb = __builtin_bit_cast(bf16x8, *(const u32x4*)(vr + 16 * nb * kVS));
+            o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[nb], 0, 0, 0);
+            o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, o[nb], 0, 0, 0);
+        }
+    }
+
+    // epilogue
+    const int64_t nrows = (int64_t)gridDim.x;
+    if (nsplit > 1) {
+        float* wo = (float*)a.ws;
+        float* wml = wo + (int64_t)nsplit * nrows * a.H * kC;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int h = h0 + 4 * kgrp + r;
+            if (h >= a.H) continue;
+            const int64_t pr = ((int64_t)split * nrows + rowid) * a.H + h;
+            float* dst = wo + pr * kC + hrow;
+#pragma unroll
+            for (int nb = 0; nb < 36; ++nb) dst[16 * nb] = o[nb][r];
+            if (hrow == 0) {
+                wml[2 * pr] = mrun[r];
+                wml[2 * pr + 1] = lrun[r];
+            }
+        }
+        return;
+    }
+    float sn[2] = {0.0f, 0.0f}, cs[2] = {1.0f, 1.0f};
+    if (a.rope_theta != 0.0) {
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) rope_sincos(a.rope_theta, 16 * q2 + hrow, kDR, -(double)t, &sn[q2], &cs[q2]);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int h = h0 + 4 * kgrp + r;
+        if (h >= a.H) continue;
+        float mu = mrun[r];
+        float den = lrun[r];
+        if (a.sink) {
+            const float z = a.sink[h] * kLog2e;
+            mu = fmaxf(mrun[r], z);
+            den = (mrun[r] == -INFINITY ? 0.0f : lrun[r] * exp2f(mrun[r] - mu)) + exp2f(z - mu);
+        }
+        const float f = den > 0.0f && mrun[r] != -INFINITY ? exp2f(mrun[r] - mu) / den : 0.0f;
+        float ov[36];
+#pragma unroll
+        for (int nb = 0; nb < 36; ++nb) ov[nb] = o[nb][r] * f;
+        if (a.rope_theta != 0.0) {
+#pragma unroll
+            for (int q2 = 0; q2 < 2; ++q2) {
+                const float x0 = ov[32 + q2], x1 = ov[34 + q2];
+                ov[32 + q2] = x0 * cs[q2] - x1 * sn[q2];
+                ov[34 + q2] = x0 * sn[q2] + x1 * cs[q2];
+            }
+        }
+        const int64_t orow = (rowid * a.H + h) * kC + hrow;
+        if (a.out_dtype == LCA_F32) {
+            float* dst = (float*)a.out + orow;
+#pragma unroll
+            for (int nb = 0; nb < 36; ++nb) dst[16 * nb] = ov[nb];
+        } else {
+            uint16_t* dst = (uint16_t*)a.out + orow;
+#pragma unroll
+            for (int nb = 0; nb < 36; ++nb) dst[16 * nb] = f2bf(ov[nb]);
+        }
+        if (a.lse && hrow == 0)
+            a.lse[rowid * a.H + h] = den > 0.0f ? (mu + log2f(den)) * kLn2 : -INFINITY;
+    }
+}
+
+// Merge nsplit partial (O, m, l) triples of one (row, head) in split order.
+__global__ void __launch_bounds__(1024) attn_combine(AttnArgs a, int nsplit, int c, int d_nope,
+                                                     int d_rope) {
+    const int64_t rowid = blockIdx.x;
+    const int h = blockIdx.y;
+    const int d = threadIdx.x;
+    const int64_t nrows = gridDim.x;
+    const float* wo = (const float*)a.ws;
+    const float* wml = wo + (int64_t)nsplit * nrows * a.H * c;
+    const int b = (int)(rowid / a.T);
+    const int64_t t = a.q_pos.v[b] + rowid % a.T;
+
+    float M = -INFINITY;
+    for (int j = 0; j < nsplit; ++j) M = fmaxf(M, wml[2 * ((j * nrows + rowid) * a.H + h)]);
+    float mu = M;
+    const float z = a.sink ? a.sink[h] * kLog2e : -INFINITY;
+    if (a.sink) mu = fmaxf(M, z);
+    const float muse = mu == -INFINITY ? 0.0f : mu;
+    float den = a.sink ? exp2f(z - muse) : 0.0f;
+    for (int j = 0; j < nsplit; ++j) {
+        const int64_t pr = (j * nrows + rowid) * a.H + h;
+        den += wml[2 * pr + 1] * exp2f(wml[2 * pr] - muse);
+    }
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    if (d >= c) return;
+    // this thread's dim, and its RoPE partner when the output is rotated
+    const int half = d_rope / 2;
+    const bool rot = a.rope_theta != 0.0 && d >= d_nope;
+    const int r = d - d_nope;
+    const int dp = !rot ? d : (r < half ? d + half : d - half);
+    float acc = 0.0f, accp = 0.0f;
+    for (int j = 0; j < nsplit; ++j) {
+        const int64_t pr = (j * nrows + rowid) * a.H + h;
+        const float wgt = exp2f(wml[2 * pr] - muse);
+        acc = fmaf(wo[pr * c + d], wgt, acc);
+        if (rot) accp = fmaf(wo[pr * c + dp], wgt, accp);
+    }
+    float v = acc * inv;
+    if (rot) {
+        float sn, cs;
+        rope_sincos(a.rope_theta, r < half ? r : r - half, d_rope, -(double)t, &sn, &cs);
+        const float vp = accp * inv;
+        v = r < half ? v * cs - vp * sn : vp * sn + v * cs;
+    }
+    const int64_t oi = (rowid * a.H + h) * c + d;
+    if (a.out_dtype == LCA_F32) ((float*)a.out)[oi] = v;
+    else ((uint16_t*)a.out)[oi] = f2bf(v);
+    if (a.lse && d == 0) a.lse[rowid * a.H + h] = den > 0.0f ? (mu + log2f(den)) * kLn2 : -INFINITY;
+}
+
+// f32 caches: one wave per (row, head); lane owns dims lane + 64 u.
+__global__ void __launch_bounds__(64) attn_f32(AttnArgs a) {
+    const int64_t rowid = blockIdx.x;
+    const int h = blockIdx.y;
+    const int lane = threadIdx.x;
+    const int b = (int)(rowid / a.T);
+    const int64_t t = a.q_pos.v[b] + rowid % a.T;
+    const SlotMap sm = slot_map(a, t);
+    const int d_nope = a.comp.d_nope, d_rope = a.comp.d_rope, c = d_nope + d_rope;
+    constexpr int U = 16;  // c <= 1024
+    __shared__ float osh[1024];
+
+    const float* q = (const float*)a.q + (rowid * a.H + h) * c;
+    float qv[U], ov[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int d = lane + 64 * u;
+        qv[u] = d < c ? q[d] : 0.0f;
+        ov[u] = 0.0f;
+    }
+    float mrun = -INFINITY, lrun = 0.0f;
+    const float qk_scale = a.sm_scale * kLog2e;
+    for (int64_t slot = 0; slot < sm.nslots; ++slot) {
+        int64_t row = 0;
+        const int src = slot_row(a, sm, rowid, b, slot, sm.nslots, &row);
+        if (!src) continue;
+        const lca_kv& kv = src == 2 ? a.win : a.comp;
+        const float* np = (const float*)kv.nope + row * d_nope;
+        const float* rp = (const float*)kv.rope + row * d_rope;
+        float kvv[U];
+        float dot = 0.0f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int d = lane + 64 * u;
+            kvv[u] = d < d_nope ? np[d] : (d < c ? rp[d - d_nope] : 0.0f);
+            dot = fmaf(qv[u], kvv[u], dot);
+        }
+        const float x = wave_sum(dot) * qk_scale;
+        const float mnew = fmaxf(mrun, x);
+        const float corr = exp2f(mrun - mnew);
+        const float p = exp2f(x - mnew);
+        lrun = lrun * corr + p;
+#pragma unroll
+        for (int u = 0; u < U; ++u) ov[u] = fmaf(p, kvv[u], ov[u] * corr);
+        mrun = mnew;
+    }
+    float mu = mrun, den = lrun;
+    if (a.sink) {
+        const float z = a.sink[h] * kLog2e;
+        mu = fmaxf(mrun, z);
+        den = (mrun == -INFINITY ? 0.0f : lrun * exp2f(mrun - mu)) + exp2f(z - mu);
+    }
+    const float f = den > 0.0f && mrun != -INFINITY ? exp2f(mrun - mu) / den : 0.0f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int d = lane + 64 * u;
+        if (d < c) osh[d] = ov[u] * f;
+    }
+    __syncthreads();
+    const int half = d_rope / 2;
+    for (int d = lane; d < c; d += 64) {
+        float v = osh[d];
+        if (a.rope_theta != 0.0 && d >= d_nope) {
+            const int r = d - d_nope;
+            float sn, cs;
+            rope_sincos(a.rope_theta, r < half ? r : r - half, d_rope, -(double)t, &sn, &cs);
+            v = r < half ? v * cs - osh[d + half] * sn : osh[d - half] * sn + v * cs;
+        }
+        const int64_t oi = (rowid * a.H + h) * c + d;
+        if (a.out_dtype == LCA_F32) ((float*)a.out)[oi] = v;
+        else ((uint16_t*)a.out)[oi] = f2bf(v);
+    }
+    if (a.lse && lane == 0) a.lse[rowid * a.H + h] = den > 0.0f ? (mu + log2f(den)) * kLn2 : -INFINITY;
+}
+
+// Split policy: decode-sized launches split the slot list so that the grid
+// covers the chip; prefill-sized launches use one split per row.
+int attn_num_splits(int64_t rows, int64_t max_keys, int32_t c) {
+    if (c != kC || rows >= 128 || max_keys <= 2 * kKT) return 1;
+    int64_t want = (512 + rows - 1) / rows;
+    int64_t most = (max_keys + 63) / 64;  // at least 64 slots per split
+    if (want > most) want = most;
+    if (want < 1) want = 1;
+    int64_t len = (max_keys + want - 1) / want;
+    len = (len + kKT - 1) / kKT * kKT;
+    return (int)((max_keys + len - 1) / len);
+}
+
+static int64_t split_len_of(int64_t max_keys, int nsplit) {
+    int64_t len = (max_keys + nsplit - 1) / nsplit;
+    return (len + kKT - 1) / kKT * kKT;
+}
+
+size_t attn_ws_bytes(int64_t rows, int32_t H, int32_t c, int64_t max_keys) {
+    const int ns = attn_num_splits(rows, max_keys, c);
+    if (ns <= 1) return 0;
+    return (size_t)ns * rows * H * (c + 2) * sizeof(float);
+}
+
+hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
+    const int64_t rows = (int64_t)a.B * a.T;
+    if (rows <= 0) return hipSuccess;
+    const int c = a.comp.d_nope + a.comp.d_rope;
+    if (a.comp.fmt == LCA_F32) {
+        hipLaunchKernelGGL(attn_f32, dim3((unsigned)rows, (unsigned)a.H), dim3(64), 0, st, a);
+        return hipGetLastError();
+    }
+    const int ns = attn_num_splits(rows, a.max_keys, c);
+    const int64_t len = ns > 1 ? split_len_of(a.max_keys, ns) : (a.max_keys + kKT - 1) / kKT * kKT;
+    dim3 grid((unsigned)rows, (unsigned)ns);
+    if (a.comp.fmt == LCA_FP8) hipLaunchKernelGGL((attn_mfma<LCA_FP8>), grid, dim3(256), 0, st, a, len, ns);
+    else hipLaunchKernelGGL((attn_mfma<LCA_BF16>), grid, dim3(256), 0, st, a, len, ns);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || ns <= 1) return e;
+    hipLaunchKernelGGL(attn_combine, dim3((unsigned)rows, (unsigned)a.H), dim3((unsigned)((c + 63) / 64 * 64)), 0,
+                       st, a, ns, c, a.comp.d_nope, a.comp.d_rope);
+    return hipGetLastError();
+}
+
+}  // namespace lca

@@ -1,0 +1,264 @@
+// capi.cpp -- the library's C ABI (declared in include/lca.h): host-side
+// validation of every argument, then one launch on the caller's stream.
+// Nothing is launched when validation fails.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/lca.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_kv(const lca_kv& kv, const char* name, bool need_rows) {
+    if (kv.fmt != LCA_F32 && kv.fmt != LCA_BF16 && kv.fmt != LCA_FP8)
+        return fail(LCA_EDTYPE, "%s: unknown storage format %d", name, kv.fmt);
+    if (kv.d_nope < 0 || kv.d_rope < 0 || (kv.d_rope & 1) || kv.d_nope + kv.d_rope < 1 ||
+        kv.d_nope + kv.d_rope > 1024)
+        return fail(LCA_ESHAPE, "%s: bad dims d_nope=%d d_rope=%d", name, kv.d_nope, kv.d_rope);
+    if (kv.fmt == LCA_FP8 && (kv.d_nope % 128 != 0 || kv.d_nope == 0))
+        return fail(LCA_ESHAPE, "%s: fp8 storage needs d_nope a positive multiple of 128", name);
+    if (need_rows && kv.cap < 1) return fail(LCA_ESHAPE, "%s: cap must be >= 1", name);
+    if (!kv.nope && kv.d_nope > 0) return fail(LCA_EINVAL, "%s: nope plane is NULL", name);
+    if (!kv.rope && kv.d_rope > 0) return fail(LCA_EINVAL, "%s: rope plane is NULL", name);
+    if (kv.fmt == LCA_FP8 && !kv.scale) return fail(LCA_EINVAL, "%s: fp8 storage needs scales", name);
+    if (!aligned16(kv.nope) || !aligned16(kv.rope) || !aligned16(kv.scale))
+        return fail(LCA_EALIGN, "%s: planes must be 16-byte aligned", name);
+    return LCA_OK;
+}
+
+int check_batch(int32_t B, const int64_t* pos, const char* name) {
+    if (B < 1 || B > LCA_MAX_BATCH) return fail(LCA_ESHAPE, "B=%d outside [1, %d]", B, LCA_MAX_BATCH);
+    if (!pos) return fail(LCA_EINVAL, "%s is NULL", name);
+    for (int b = 0; b < B; ++b)
+        if (pos[b] < 0) return fail(LCA_ESHAPE, "%s[%d] = %lld is negative", name, b, (long long)pos[b]);
+    return LCA_OK;
+}
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return LCA_OK;
+    return fail(LCA_EHIP, "HIP launch failed: %s", hipGetErrorString(e));
+}
+
+lca::Pos to_pos(const int64_t* p, int32_t B) {
+    lca::Pos r;
+    memset(&r, 0, sizeof r);
+    for (int b = 0; b < B; ++b) r.v[b] = p[b];
+    return r;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lca_version(void) { return LCA_VERSION; }
+
+const char* lca_last_error(void) { return g_err; }
+
+int lca_kv_compress(const void* c_a, const void* z_a, const void* c_b, const void* z_b,
+                    int32_t in_dtype, const float* bias_a, const float* bias_b, const float* gamma,
+                    float eps, double rope_theta, int32_t m, int32_t overlap, int32_t B, int64_t n_rows,
+                    const int64_t* first_pos, lca_kv out, int32_t ring, void* stream) {
+    g_err[0] = 0;
+    if (!c_a || !z_a) return fail(LCA_EINVAL, "c_a / z_a is NULL");
+    if (m < 1) return fail(LCA_EINVAL, "m must be >= 1 (got %d)", m);
+    if (overlap != 0 && overlap != 1) return fail(LCA_EINVAL, "overlap must be 0 or 1");
+    if (overlap && (!c_b || !z_b)) return fail(LCA_EINVAL, "overlap needs c_b and z_b");
+    if (ring != 0 && ring != 1) return fail(LCA_EINVAL, "ring must be 0 or 1");
+    if (in_dtype != LCA_F32 && in_dtype != LCA_BF16) return fail(LCA_EDTYPE, "in_dtype must be f32 or bf16");
+    if (n_rows < 0) return fail(LCA_ESHAPE, "n_rows < 0");
+    if (!(rope_theta >= 0.0)) return fail(LCA_EINVAL, "rope_theta must be >= 0");
+    if (!(eps >= 0.0f)) return fail(LCA_EINVAL, "eps must be >= 0");
+    int rc = check_batch(B, first_pos, "first_pos");
+    if (rc) return rc;
+    if ((rc = check_kv(out, "out", true))) return rc;
+    for (const void* p : {c_a, z_a, c_b, z_b, (const void*)bias_a, (const void*)bias_b, (const void*)gamma})
+        if (!aligned16(p)) return fail(LCA_EALIGN, "input pointers must be 16-byte aligned");
+
+    lca::CompressArgs a;
+    memset(&a, 0, sizeof a);
+    a.c_a = c_a; a.z_a = z_a; a.c_b = c_b; a.z_b = z_b;
+    a.bias_a = bias_a; a.bias_b = bias_b; a.gamma = gamma;
+    a.eps = eps; a.rope_theta = rope_theta; a.in_dtype = in_dtype;
+    a.m = m; a.overlap = overlap; a.B = B; a.n_rows = n_rows; a.out = out; a.ring = ring;
+    a.first_pos = to_pos(first_pos, B);
+    int64_t most = 0;
+    for (int b = 0; b < B; ++b) {
+        const int64_t p0 = first_pos[b];
+        int64_t s_lo = (p0 + m - 1) / m;
+        if (overlap && s_lo > 0) s_lo += 1;
+        const int64_t s_hi = (p0 + n_rows) / m;
+        if (ring && s_hi - s_lo > out.cap) s_lo = s_hi - out.cap;
+        a.s_lo.v[b] = s_lo;
+        if (s_hi > s_lo) {
+            if (!ring && s_hi > out.cap)
+                return fail(LCA_ESHAPE, "entry %lld of sequence %d does not fit cap %lld",
+                            (long long)(s_hi - 1), b, (long long)out.cap);
+            if (s_hi - s_lo > most) most = s_hi - s_lo;
+        }
+    }
+    if (most > 0x7fffffff) return fail(LCA_ESHAPE, "too many entries in one call");
+    a.max_entries = most;
+    return hip_status(lca::launch_kv_compress(a, (hipStream_t)stream));
+}
+
+int lca_indexer_score(const void* q, const float* w, const void* k, int32_t in_dtype, int64_t k_cap,
+                      int32_t H_I, int32_t d_I, int32_t B, int32_t T, const int64_t* q_pos, int32_t m,
+                      void* scores, int32_t score_dtype, int64_t s_stride, void* stream) {
+    g_err[0] = 0;
+    if (!q || !k || !scores) return fail(LCA_EINVAL, "q, k and scores must be non-NULL");
+    if (m < 1) return fail(LCA_EINVAL, "m must be >= 1");
+    if (in_dtype != LCA_BF16 && in_dtype != LCA_F32) return fail(LCA_EDTYPE, "in_dtype must be bf16 or f32");
+    if (score_dtype != LCA_BF16 && score_dtype != LCA_F32) return fail(LCA_EDTYPE, "score_dtype must be bf16 or f32");
+    if (T < 0 || k_cap < 1 || s_stride < 1) return fail(LCA_ESHAPE, "bad T / k_cap / s_stride");
+    if (in_dtype == LCA_BF16 && (H_I != 16 || d_I != 128))
+        return fail(LCA_ESHAPE, "bf16 indexer supports H_I = 16, d_I = 128 (got %d x %d)", H_I, d_I);
+    if (H_I < 1 || H_I > 64 || d_I < 1 || d_I > 1024) return fail(LCA_ESHAPE, "bad H_I / d_I");
+    int rc = check_batch(B, q_pos, "q_pos");
+    if (rc) return rc;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(w) || !aligned16(scores))
+        return fail(LCA_EALIGN, "pointers must be 16-byte aligned");
+    int64_t max_vis = 0;
+    for (int b = 0; b < B && T > 0; ++b) {
+        const int64_t vis = (q_pos[b] + T) / m;
+        if (vis > k_cap || vis > s_stride)
+            return fail(LCA_ESHAPE, "sequence %d sees %lld entries: more than k_cap %lld or s_stride %lld", b,
+                        (long long)vis, (long long)k_cap, (long long)s_stride);
+        if (vis > max_vis) max_vis = vis;
+    }
+    lca::IndexerArgs a;
+    memset(&a, 0, sizeof a);
+    a.q = q; a.w = w; a.k = k; a.in_dtype = in_dtype; a.k_cap = k_cap; a.H_I = H_I; a.d_I = d_I;
+    a.B = B; a.T = T; a.m = m; a.scores = scores; a.score_dtype = score_dtype; a.s_stride = s_stride;
+    a.q_pos = to_pos(q_pos, B);
+    a.max_vis = max_vis;
+    return hip_status(lca::launch_indexer(a, (hipStream_t)stream));
+}
+
+size_t lca_topk_workspace_size(int32_t, int32_t, int64_t, int32_t) { return 0; }
+
+int lca_topk_select(const void* scores, int32_t score_dtype, int64_t s_stride, int32_t B, int32_t T,
+                    const int64_t* q_pos, int32_t m, int32_t k, int32_t* idx, void*, size_t,
+                    void* stream) {
+    g_err[0] = 0;
+    if (!scores || !idx) return fail(LCA_EINVAL, "scores and idx must be non-NULL");
+    if (m < 1) return fail(LCA_EINVAL, "m must be >= 1");
+    if (k < 1) return fail(LCA_EINVAL, "k must be >= 1");
+    if (score_dtype != LCA_BF16 && score_dtype != LCA_F32) return fail(LCA_EDTYPE, "score_dtype must be bf16 or f32");
+    if (T < 0 || s_stride < 1) return fail(LCA_ESHAPE, "bad T / s_stride");
+    int rc = check_batch(B, q_pos, "q_pos");
+    if (rc) return rc;
+    if (!aligned16(scores) || !aligned16(idx)) return fail(LCA_EALIGN, "pointers must be 16-byte aligned");
+    for (int b = 0; b < B && T > 0; ++b)
+        if ((q_pos[b] + T) / m > s_stride)
+            return fail(LCA_ESHAPE, "sequence %d sees more entries than s_stride", b);
+    lca::TopkArgs a;
+    memset(&a, 0, sizeof a);
+    a.scores = scores; a.score_dtype = score_dtype; a.s_stride = s_stride; a.B = B; a.T = T; a.m = m;
+    a.k = k; a.idx = idx; a.q_pos = to_pos(q_pos, B);
+    return hip_status(lca::launch_topk(a, (hipStream_t)stream));
+}
+
+size_t lca_attn_workspace_size(int32_t B, int32_t T, int32_t H, int32_t c, int64_t max_keys) {
+    if (B < 1 || T < 1 || H < 1 || c < 1 || max_keys < 1) return 0;
+    return lca::attn_ws_bytes((int64_t)B * T, H, c, max_keys);
+}
+
+static int attn_common(const void* q, int32_t q_dtype, int32_t H, int32_t B, int32_t T,
+                       const int64_t* q_pos, lca_kv comp, int32_t m, const int32_t* idx, int32_t k,
+                       lca_kv win, int32_t n_win, const float* sink, float sm_scale, double rope_theta,
+                       void* out, int32_t out_dtype, float* lse, void* ws, size_t ws_bytes, void* stream) {
+    if (!q || !out) return fail(LCA_EINVAL, "q and out must be non-NULL");
+    if (m < 1) return fail(LCA_EINVAL, "m must be >= 1");
+    if (H < 1 || T < 0) return fail(LCA_ESHAPE, "bad H / T");
+    if (n_win < 0) return fail(LCA_EINVAL, "n_win must be >= 0");
+    if (!(rope_theta >= 0.0)) return fail(LCA_EINVAL, "rope_theta must be >= 0");
+    if (!(sm_scale == sm_scale)) return fail(LCA_EINVAL, "sm_scale is NaN");
+    if (out_dtype != LCA_F32 && out_dtype != LCA_BF16) return fail(LCA_EDTYPE, "out_dtype must be f32 or bf16");
+    int rc = check_batch(B, q_pos, "q_pos");
+    if (rc) return rc;
+    if ((rc = check_kv(comp, "comp", true))) return rc;
+    if (n_win > 0) {
+        if ((rc = check_kv(win, "win", true))) return rc;
+        if (win.fmt != comp.fmt || win.d_nope != comp.d_nope || win.d_rope != comp.d_rope)
+            return fail(LCA_ESHAPE, "window and compressed caches must share format and dims");
+        if ((int64_t)n_win + T - 1 > win.cap)
+            return fail(LCA_ESHAPE, "window ring too small: n_win + T - 1 = %lld > cap %lld",
+                        (long long)n_win + T - 1, (long long)win.cap);
+    }
+    const int c = comp.d_nope + comp.d_rope;
+    if (comp.fmt == LCA_F32) {
+        if (q_dtype != LCA_F32) return fail(LCA_EDTYPE, "f32 caches need f32 queries");
+    } else {
+        if (q_dtype != LCA_BF16) return fail(LCA_EDTYPE, "bf16 / fp8 caches need bf16 queries");
+        if (comp.d_nope != 512 || comp.d_rope != 64)
+            return fail(LCA_ESHAPE, "bf16 / fp8 caches support d_nope = 512, d_rope = 64");
+        if (H % 16 != 0 || H > 64) return fail(LCA_ESHAPE, "H must be a multiple of 16, at most 64");
+    }
+    if (!aligned16(q) || !aligned16(out) || !aligned16(lse) || !aligned16(idx) || !aligned16(sink) ||
+        !aligned16(ws))
+        return fail(LCA_EALIGN, "pointers must be 16-byte aligned");
+    if (T == 0) return LCA_OK;
+    int64_t max_keys = 1;
+    for (int b = 0; b < B; ++b) {
+        const int64_t t_last = q_pos[b] + T - 1;
+        int64_t keys = n_win > 0 ? (n_win < t_last + 1 ? n_win : t_last + 1) : 0;
+        if (idx) {
+            keys += k;
+        } else {
+            const int64_t vis = (t_last + 1) / m;
+            if (vis > comp.cap)
+                return fail(LCA_ESHAPE, "sequence %d sees %lld entries, cap is %lld", b, (long long)vis,
+                            (long long)comp.cap);
+            keys += vis;
+        }
+        if (keys > max_keys) max_keys = keys;
+    }
+    const size_t need = lca::attn_ws_bytes((int64_t)B * T, H, c, max_keys);
+    if (need > 0 && (!ws || ws_bytes < need))
+        return fail(LCA_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+    lca::AttnArgs a;
+    memset(&a, 0, sizeof a);
+    a.q = q; a.q_dtype = q_dtype; a.H = H; a.B = B; a.T = T; a.m = m; a.comp = comp; a.idx = idx; a.k = k;
+    a.win = win; a.n_win = n_win; a.sink = sink; a.sm_scale = sm_scale; a.rope_theta = rope_theta;
+    a.out = out; a.out_dtype = out_dtype; a.lse = lse; a.ws = ws; a.q_pos = to_pos(q_pos, B);
+    a.max_keys = max_keys;
+    if (n_win == 0) a.win = comp;  // never read
+    return hip_status(lca::launch_attn(a, (hipStream_t)stream));
+}
+
+int lca_csa_attn(const void* q, int32_t q_dtype, int32_t H, int32_t B, int32_t T, const int64_t* q_pos,
+                 lca_kv comp, int32_t m, const int32_t* idx, int32_t k, lca_kv win, int32_t n_win,
+                 const float* sink, float sm_scale, double rope_theta, void* out, int32_t out_dtype,
+                 float* lse, void* ws, size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    if (!idx) return fail(LCA_EINVAL, "idx is NULL");
+    if (k < 1) return fail(LCA_EINVAL, "k must be >= 1");
+    return attn_common(q, q_dtype, H, B, T, q_pos, comp, m, idx, k, win, n_win, sink, sm_scale, rope_theta,
+                       out, out_dtype, lse, ws, ws_bytes, stream);
+}
+
+int lca_hca_attn(const void* q, int32_t q_dtype, int32_t H, int32_t B, int32_t T, const int64_t* q_pos,
+                 lca_kv comp, int32_t m, lca_kv win, int32_t n_win, const float* sink, float sm_scale,
+                 double rope_theta, void* out, int32_t out_dtype, float* lse, void* ws, size_t ws_bytes,
+                 void* stream) {
+    g_err[0] = 0;
+    return attn_common(q, q_dtype, H, B, T, q_pos, comp, m, nullptr, 0, win, n_win, sink, sm_scale,
+                       rope_theta, out, out_dtype, lse, ws, ws_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,92 @@
+// device.h -- gfx950 device helpers shared by the library's kernels:
+// bf16 / OCP-e4m3fn conversions, wave reductions, MFMA fragment types.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lca {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// nearest-even fp32 -> bf16 (inputs are finite)
+__device__ __forceinline__ uint16_t f2bf(float x) {
+    uint32_t u = __float_as_uint(x);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// OCP e4m3fn -> fp32.  Normal codes: (1 + m/8) 2^(e-7); exponent 0: m 2^-9.
+__device__ __forceinline__ float fp8_to_f32(uint32_t code) {
+    uint32_t s = (code & 0x80u) << 24, e = (code >> 3) & 15u, mt = code & 7u;
+    float sub = (float)mt * 0.001953125f;
+    float nrm = __uint_as_float(((e + 120u) << 23) | (mt << 20));
+    return __uint_as_float(__float_as_uint(e ? nrm : sub) | s);
+}
+
+// fp32 -> OCP e4m3fn, nearest with ties to the even code, saturating at 448.
+// With e = max(floor(log2|x|), -6) the code is 8(e+6) + rint(|x| 2^(3-e)) for
+// e > -6 and rint(|x| 2^9) below: code order follows value order, so a
+// mantissa carry simply moves to the next binade.
+__device__ __forceinline__ uint32_t f32_to_fp8(float x) {
+    uint32_t u = __float_as_uint(x);
+    uint32_t s = (u >> 24) & 0x80u;
+    float a = __uint_as_float(u & 0x7fffffffu);
+    int e = (int)((u >> 23) & 0xffu) - 127;
+    uint32_t code;
+    if (e <= -6) {
+        code = (uint32_t)__builtin_rintf(a * 512.0f);
+    } else {
+        float q = __builtin_rintf(__uint_as_float(__float_as_uint(a) - ((uint32_t)(e - 3) << 23)));
+        code = (uint32_t)(8 * (e + 6)) + (uint32_t)q;
+    }
+    code = code > 126u ? 126u : code;
+    return code | s;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+// reduction over the 16 lanes that share l / 16 (one MFMA column group)
+__device__ __forceinline__ float max16(float v) {
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+__device__ __forceinline__ float sum16(float v) {
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// RoPE inverse frequency theta^(-2i/d_rope) and the angle pos*inv_freq
+// reduced to [-pi, pi) in fp64 (positions reach 2^20 and beyond).
+__device__ __forceinline__ void rope_sincos(double theta, int i, int d_rope, double pos, float* sn,
+                                            float* cs) {
+    double inv = exp2(-2.0 * (double)i / (double)d_rope * log2(theta));
+    double ang = pos * inv;
+    const double two_pi = 6.283185307179586476925;
+    ang = ang - two_pi * rint(ang / two_pi);
+    double s, c;
+    sincos(ang, &s, &c);
+    *sn = (float)s;
+    *cs = (float)c;
+}
+
+}  // namespace lca

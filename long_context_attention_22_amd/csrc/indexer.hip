@@ -1,0 +1,154 @@
+// indexer.hip -- the lightning indexer ("DeepSeek-V4 中文翻译" section 2.3.1;
+// BF16 index scores, section 5.2.1):
+//   S[t][s] = sum_h w[t][h] * ReLU(q_I[t][h] . k_I[s])  for s < vis(t).
+//
+// bf16 path (H_I = 16, d_I = 128): a bf16 MFMA contraction.  The 16 heads of
+// one query token are the M = 16 rows of v_mfma_f32_16x16x32_bf16, 16 keys
+// are its N columns and d_I = 128 is four K = 32 steps.  Each wave keeps the
+// A fragments of TOK tokens in registers and streams 64-key chunks of the key
+// cache straight from HBM into B fragments (each lane loads 16 contiguous
+// bytes of one key row, so a chunk is one contiguous 16 KB read).  The
+// epilogue applies ReLU and the head weights in the accumulator layout, sums
+// the 16 heads with two cross-lane shuffles and writes 64 consecutive scores
+// per token with one coalesced store.  Key chunks beyond the last token's
+// visible count are skipped (causal tile skip).
+//
+// f32 path: one thread per (token, key), f32 FMA (used for fp32 workloads).
+#include "device.h"
+#include "kernels.h"
+
+namespace lca {
+
+constexpr int kIdxH = 16, kIdxD = 128;
+
+template <typename TS>
+__device__ __forceinline__ void store_score(TS* p, float v);
+template <>
+__device__ __forceinline__ void store_score<float>(float* p, float v) {
+    *p = v == 0.0f ? 0.0f : v;
+}
+template <>
+__device__ __forceinline__ void store_score<uint16_t>(uint16_t* p, float v) {
+    *p = f2bf(v == 0.0f ? 0.0f : v);
+}
+
+template <int TOK, typename TS>
+__global__ void __launch_bounds__(256) indexer_mfma(IndexerArgs a, int64_t keys_per_wg) {
+    const int b = blockIdx.z;
+    const int i0 = blockIdx.y * TOK;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int ntok = min(TOK, a.T - i0);
+    const int64_t pos0 = a.q_pos.v[b] + i0;
+    const int64_t vis_last = min((pos0 + ntok) / a.m, a.k_cap);
+    const int64_t key_lo = (int64_t)blockIdx.x * keys_per_wg;
+    const int64_t key_hi = min(key_lo + keys_per_wg, vis_last);
+    if (key_lo >= key_hi) return;
+
+    const int hrow = lane & 15, kgrp = lane >> 4;
+    bf16x8 qa[TOK][4];
+    float wt[TOK][4];
+#pragma unroll
+    for (int tk = 0; tk < TOK; ++tk) {
+        const int64_t qi = ((int64_t)b * a.T + i0 + tk) * kIdxH;
+        const u32x4* qp = (const u32x4*)((const uint16_t*)a.q + (qi + hrow) * kIdxD);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            u32x4 v = tk < ntok ? qp[4 * ks + kgrp] : u32x4{0u, 0u, 0u, 0u};
+            qa[tk][ks] = __builtin_bit_cast(bf16x8, v);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            wt[tk][r] = tk < ntok ? (a.w ? a.w[qi + 4 * kgrp + r] : 1.0f) : 0.0f;
+    }
+
+    const uint16_t* kbase = (const uint16_t*)a.k + (int64_t)b * a.k_cap * kIdxD;
+    TS* sbase = (TS*)a.scores + ((int64_t)b * a.T + i0) * a.s_stride;
+
+    for (int64_t c0 = key_lo + 64 * wv; c0 < key_hi; c0 += 256) {
+        // B fragments of four 16-key blocks: block bl, lane -> key c0 + 16 bl + (lane & 15)
+        bf16x8 kf[4][4];
+#pragma unroll
+        for (int bl = 0; bl < 4; ++bl) {
+            const int64_t key = c0 + 16 * bl + hrow;
+            const u32x4* kp = (const u32x4*)(kbase + key * kIdxD);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                u32x4 v = key < key_hi ? kp[4 * ks + kgrp] : u32x4{0u, 0u, 0u, 0u};
+                kf[bl][ks] = __builtin_bit_cast(bf16x8, v);
+            }
+        }
+        const int64_t mykey = c0 + lane;  // the score this lane stores
+#pragma unroll
+        for (int tk = 0; tk < TOK; ++tk) {
+            float mine = 0.0f;
+#pragma unroll
+            for (int bl = 0; bl < 4; ++bl) {
+                f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[tk][ks], kf[bl][ks], acc, 0, 0, 0);
+                // lane holds heads 4*kgrp + r of key 16 bl + hrow
+                float v = wt[tk][0] * fmaxf(acc[0], 0.0f);
+                v = fmaf(wt[tk][1], fmaxf(acc[1], 0.0f), v);
+                v = fmaf(wt[tk][2], fmaxf(acc[2], 0.0f), v);
+                v = fmaf(wt[tk][3], fmaxf(acc[3], 0.0f), v);
+                v += __shfl_xor(v, 16, kWave);
+                v += __shfl_xor(v, 32, kWave);
+                if (kgrp == bl) mine = v;
+            }
+            if (tk < ntok) {
+                const int64_t vis_t = min((pos0 + tk + 1) / a.m, a.k_cap);
+                if (mykey < vis_t) store_score<TS>(sbase + (int64_t)tk * a.s_stride + mykey, mine);
+            }
+        }
+    }
+}
+
+template <typename TIn, typename TS>
+__global__ void __launch_bounds__(256) indexer_f32(IndexerArgs a) {
+    const int b = blockIdx.z, i = blockIdx.y;
+    const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t t = a.q_pos.v[b] + i;
+    const int64_t vis = min((t + 1) / a.m, a.k_cap);
+    if (s >= vis) return;
+    const float* q = (const float*)a.q + ((int64_t)b * a.T + i) * a.H_I * a.d_I;
+    const float* k = (const float*)a.k + ((int64_t)b * a.k_cap + s) * a.d_I;
+    const float* w = a.w ? a.w + ((int64_t)b * a.T + i) * a.H_I : nullptr;
+    float acc = 0.0f;
+    for (int h = 0; h < a.H_I; ++h) {
+        float dot = 0.0f;
+        for (int d = 0; d < a.d_I; ++d) dot = fmaf(q[h * a.d_I + d], k[d], dot);
+        acc = fmaf(w ? w[h] : 1.0f, fmaxf(dot, 0.0f), acc);
+    }
+    store_score<TS>((TS*)a.scores + ((int64_t)b * a.T + i) * a.s_stride + s, acc);
+}
+
+hipError_t launch_indexer(const IndexerArgs& a, hipStream_t st) {
+    if (a.max_vis <= 0 || a.T <= 0) return hipSuccess;
+    const bool bf_scores = a.score_dtype == LCA_BF16;
+    if (a.in_dtype == LCA_F32) {
+        dim3 grid((unsigned)((a.max_vis + 255) / 256), (unsigned)a.T, (unsigned)a.B);
+        if (bf_scores) hipLaunchKernelGGL((indexer_f32<float, uint16_t>), grid, dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((indexer_f32<float, float>), grid, dim3(256), 0, st, a);
+        return hipGetLastError();
+    }
+    const int tok = a.T >= 64 ? 8 : 1;
+    const int64_t groups = ((int64_t)a.T + tok - 1) / tok;
+    // enough workgroups to cover the chip: split the key range in 256-key multiples
+    int64_t want_split = (2048 + (int64_t)a.B * groups - 1) / ((int64_t)a.B * groups);
+    int64_t kpw = (a.max_vis + want_split - 1) / want_split;
+    kpw = ((kpw + 255) / 256) * 256;
+    if (kpw < 256) kpw = 256;
+    const int64_t nsplit = (a.max_vis + kpw - 1) / kpw;
+    dim3 grid((unsigned)nsplit, (unsigned)groups, (unsigned)a.B);
+    if (tok == 8) {
+        if (bf_scores) hipLaunchKernelGGL((indexer_mfma<8, uint16_t>), grid, dim3(256), 0, st, a, kpw);
+        else hipLaunchKernelGGL((indexer_mfma<8, float>), grid, dim3(256), 0, st, a, kpw);
+    } else {
+        if (bf_scores) hipLaunchKernelGGL((indexer_mfma<1, uint16_t>), grid, dim3(256), 0, st, a, kpw);
+        else hipLaunchKernelGGL((indexer_mfma<1, float>), grid, dim3(256), 0, st, a, kpw);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace lca

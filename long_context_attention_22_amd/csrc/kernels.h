@@ -1,0 +1,86 @@
+// kernels.h -- launch entry points of the HIP kernels (host side), called by
+// the C ABI in capi.cpp after it has validated every argument.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/lca.h"
+
+namespace lca {
+
+struct Pos {
+    int64_t v[LCA_MAX_BATCH];
+};
+
+// kv_compress: entries [s_lo[b], s_hi[b]) of each sequence.
+struct CompressArgs {
+    const void* c_a;
+    const void* z_a;
+    const void* c_b;
+    const void* z_b;
+    const float* bias_a;
+    const float* bias_b;
+    const float* gamma;
+    float eps;
+    double rope_theta;
+    int32_t in_dtype;
+    int32_t m, overlap, B;
+    int64_t n_rows;
+    lca_kv out;
+    int32_t ring;
+    Pos first_pos;
+    Pos s_lo;
+    int64_t max_entries;
+};
+hipError_t launch_kv_compress(const CompressArgs& a, hipStream_t st);
+
+struct IndexerArgs {
+    const void* q;
+    const float* w;
+    const void* k;
+    int32_t in_dtype;
+    int64_t k_cap;
+    int32_t H_I, d_I, B, T, m;
+    void* scores;
+    int32_t score_dtype;
+    int64_t s_stride;
+    Pos q_pos;
+    int64_t max_vis;
+};
+hipError_t launch_indexer(const IndexerArgs& a, hipStream_t st);
+
+struct TopkArgs {
+    const void* scores;
+    int32_t score_dtype;
+    int64_t s_stride;
+    int32_t B, T, m, k;
+    int32_t* idx;
+    Pos q_pos;
+};
+hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+
+struct AttnArgs {
+    const void* q;
+    int32_t q_dtype;
+    int32_t H, B, T, m;
+    lca_kv comp;
+    const int32_t* idx;  // NULL: dense over every visible entry (HCA)
+    int32_t k;
+    lca_kv win;
+    int32_t n_win;
+    const float* sink;
+    float sm_scale;
+    double rope_theta;
+    void* out;
+    int32_t out_dtype;
+    float* lse;
+    void* ws;
+    Pos q_pos;
+    int64_t max_keys;   // attended rows per query, upper bound
+};
+int attn_num_splits(int64_t rows, int64_t max_keys, int32_t c);
+size_t attn_ws_bytes(int64_t rows, int32_t H, int32_t c, int64_t max_keys);
+hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
+
+}  // namespace lca

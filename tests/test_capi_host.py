@@ -1,0 +1,148 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+symbol include/lca.h declares, and rejects bad arguments before launching.
+
+Only error paths are exercised: a call that passed validation would launch a
+kernel, which needs a GPU.  Device pointers are fake aligned addresses, never
+dereferenced on the host.
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import long_context_attention_22_amd as lca
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7F0000000000          # 16-byte aligned, never dereferenced
+FAKE2 = 0x7F0000100000
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(lca.LIB_PATH):
+        import long_context_attention_22_amd.build as bld
+        bld.build()
+    return lca.lib()
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "lca.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(lca_\w+)\s*\(", txt, re.M)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert set(names) >= {"lca_kv_compress", "lca_indexer_score", "lca_topk_select", "lca_csa_attn",
+                          "lca_hca_attn", "lca_attn_workspace_size", "lca_topk_workspace_size",
+                          "lca_last_error", "lca_version"}
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.lca_version() == 1
+
+
+def kv(fmt=lca.BF16, d_nope=512, d_rope=64, cap=64, scale=True):
+    return lca._KV(FAKE, FAKE2, FAKE + 4096 if (fmt == lca.FP8 and scale) else 0, fmt, d_nope, d_rope, cap)
+
+
+def pos(*v):
+    return (C.c_int64 * len(v))(*v)
+
+
+def compress(L, **kw):
+    a = dict(c_a=FAKE, z_a=FAKE, c_b=FAKE, z_b=FAKE, in_dtype=lca.BF16, bias_a=None, bias_b=None,
+             gamma=None, eps=1e-6, theta=0.0, m=4, overlap=1, B=1, n_rows=64, first_pos=pos(0),
+             out=kv(), ring=0)
+    a.update(kw)
+    return L.lca_kv_compress(a["c_a"], a["z_a"], a["c_b"], a["z_b"], a["in_dtype"], a["bias_a"], a["bias_b"],
+                             a["gamma"], a["eps"], a["theta"], a["m"], a["overlap"], a["B"], a["n_rows"],
+                             a["first_pos"], a["out"], a["ring"], None)
+
+
+def test_kv_compress_validation(L):
+    assert compress(L, c_a=None) == 1
+    assert compress(L, m=0) == 1
+    assert compress(L, overlap=2) == 1
+    assert compress(L, c_b=None) == 1                       # overlap needs the b-set
+    assert compress(L, in_dtype=2) == 3
+    assert compress(L, B=0, first_pos=pos()) == 2
+    assert compress(L, B=65, first_pos=pos(*([0] * 65))) == 2
+    assert compress(L, first_pos=pos(-4)) == 2
+    assert compress(L, out=kv(lca.FP8, d_nope=96, d_rope=32)) == 2      # fp8 needs d_nope % 128
+    assert compress(L, out=kv(lca.FP8, scale=False)) == 1
+    assert compress(L, out=kv(d_rope=63)) == 2
+    assert compress(L, out=kv(fmt=7)) == 3
+    assert compress(L, c_a=FAKE + 8) == 4
+    # 64 rows at m=4 make entries 0..15: does not fit cap 8 without a ring
+    assert compress(L, out=kv(cap=8)) == 2
+    assert b"cap" in L.lca_last_error()
+    assert compress(L, theta=-1.0) == 1
+
+
+def indexer(L, **kw):
+    a = dict(q=FAKE, w=None, k=FAKE, dt=lca.BF16, k_cap=100, H=16, d=128, B=1, T=8, q_pos=pos(0), m=4,
+             s=FAKE2, sdt=lca.BF16, stride=100)
+    a.update(kw)
+    return L.lca_indexer_score(a["q"], a["w"], a["k"], a["dt"], a["k_cap"], a["H"], a["d"], a["B"], a["T"],
+                               a["q_pos"], a["m"], a["s"], a["sdt"], a["stride"], None)
+
+
+def test_indexer_validation(L):
+    assert indexer(L, q=None) == 1
+    assert indexer(L, m=0) == 1
+    assert indexer(L, dt=2) == 3
+    assert indexer(L, sdt=2) == 3
+    assert indexer(L, H=8) == 2                 # bf16 path is 16 heads x 128
+    assert indexer(L, q_pos=pos(400)) == 2      # (400 + 8) / 4 = 102 visible > k_cap
+    assert indexer(L, stride=1) == 2
+    assert indexer(L, k=FAKE + 2) == 4
+
+
+def topk(L, **kw):
+    a = dict(s=FAKE, sdt=lca.BF16, stride=128, B=1, T=4, q_pos=pos(0), m=4, k=16, idx=FAKE2)
+    a.update(kw)
+    return L.lca_topk_select(a["s"], a["sdt"], a["stride"], a["B"], a["T"], a["q_pos"], a["m"], a["k"],
+                             a["idx"], None, 0, None)
+
+
+def test_topk_validation(L):
+    assert topk(L, s=None) == 1
+    assert topk(L, k=0) == 1
+    assert topk(L, sdt=2) == 3
+    assert topk(L, q_pos=pos(600)) == 2
+    assert topk(L, idx=FAKE2 + 4) == 4
+    assert L.lca_topk_workspace_size(1, 1, 1024, 16) == 0
+
+
+def attn(L, csa=True, **kw):
+    a = dict(q=FAKE, qdt=lca.BF16, H=64, B=1, T=4, q_pos=pos(100), comp=kv(), m=4, idx=FAKE2, k=16,
+             win=kv(cap=256), n_win=128, sink=None, scale=0.04, theta=0.0, out=FAKE2, odt=lca.F32,
+             lse=None, ws=None, wsb=0)
+    a.update(kw)
+    if csa:
+        return L.lca_csa_attn(a["q"], a["qdt"], a["H"], a["B"], a["T"], a["q_pos"], a["comp"], a["m"],
+                              a["idx"], a["k"], a["win"], a["n_win"], a["sink"], a["scale"], a["theta"],
+                              a["out"], a["odt"], a["lse"], a["ws"], a["wsb"], None)
+    return L.lca_hca_attn(a["q"], a["qdt"], a["H"], a["B"], a["T"], a["q_pos"], a["comp"], a["m"], a["win"],
+                          a["n_win"], a["sink"], a["scale"], a["theta"], a["out"], a["odt"], a["lse"],
+                          a["ws"], a["wsb"], None)
+
+
+def test_attn_validation(L):
+    assert attn(L, idx=None) == 1
+    assert attn(L, k=0) == 1
+    assert attn(L, n_win=-1) == 1
+    assert attn(L, odt=2) == 3
+    assert attn(L, qdt=lca.F32) == 3                              # bf16 cache with f32 queries
+    assert attn(L, H=40) == 2                                     # MFMA path: multiple of 16
+    assert attn(L, comp=kv(d_nope=256)) == 2                      # MFMA path: 512 + 64
+    assert attn(L, win=kv(cap=100)) == 2                          # n_win + T - 1 > cap
+    assert attn(L, win=kv(fmt=lca.FP8, cap=256)) == 2             # window format differs
+    assert attn(L, csa=False, comp=kv(cap=10)) == 2               # 26 visible entries > cap
+    assert attn(L, out=FAKE2 + 4) == 4
+    # decode-sized launches need a workspace for the split partials
+    need = L.lca_attn_workspace_size(1, 1, 64, 576, 1152)
+    assert need > 0
+    assert attn(L, T=1, q_pos=pos(4000), k=1024) == 5
+    assert attn(L, T=1, q_pos=pos(4000), k=1024, ws=FAKE2, wsb=need - 1) == 5
+    assert L.lca_attn_workspace_size(1, 4096, 64, 576, 2176) == 0   # prefill: one split per row
