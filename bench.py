@@ -1,0 +1,471 @@
+#!/usr/bin/env python3
+"""Benchmark of the CSA / HCA compressed-attention path on one MI355X.
+
+Headline (one JSON line on stdout): decode tokens/s of the interleaved
+4-layer stack (HCA, HCA, CSA, HCA) for one sequence at 1,048,576 tokens of
+context -- CSA holds 262,144 fp8 entries with top-k 2048, each HCA layer 8,192
+entries at m' = 128, window 128, 64 query heads of 512 + 64 -- one step being
+one decode token through all four layers (window store, compression when a
+block completes, indexer, top-k, attention).  Inputs are synthetic and
+already resident in HBM; the K timed steps are one HIP-graph replay.  To keep
+the per-step working set (about 85 MB) out of the 256 MB Infinity Cache, the
+stack state is replicated R times and consecutive steps rotate through the
+replicas (as a deeper model would), so every step reads its caches from HBM.
+
+Also reported (key "extra"): the same stack's 4096-token chunked prefill at
+1M context, and CSA decode for 32 sequences at 131,072 tokens.  "roofline"
+covers the dominant decode kernel (indexer_score, HBM-bound), timed with HIP
+events on its stream inside the timed graph.  "cpu_baseline" is the fp64
+oracle timed on host cores on a bounded sample (two decode steps of the
+stack).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import lca_synth as S  # noqa: E402
+import long_context_attention_22_amd as lca  # noqa: E402
+from long_context_attention_22_amd.stack import Layer, LayerSpec, Params, RawStream  # noqa: E402
+
+METRIC = "CSA/HCA decode tokens/s at 128K–1M ctx (HBM GB/s %) + prefill tokens/s"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+T0_1M = 1 << 20
+C = 576
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------
+# synthetic workload construction (library calls only; inputs from lca_synth)
+# ----------------------------------------------------------------------------
+
+def to_dev(x: np.ndarray, dtype=None):
+    if x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def make_params(seed: int, spec: LayerSpec, tag: str) -> Params:
+    m, c = spec.m, spec.c
+    p = Params(bias_a=to_dev(S.normal(seed, f"{tag}/bias_a", (m, c), 0.5)),
+               bias_b=to_dev(S.normal(seed, f"{tag}/bias_b", (m, c), 0.5)),
+               gamma=to_dev((1.0 + 0.1 * S.normal(seed, f"{tag}/gamma", (c,))).astype(np.float32)),
+               sink=to_dev(S.normal(seed, f"{tag}/sink", (spec.H,))))
+    if spec.kind == "csa":
+        p.i_bias_a = to_dev(S.normal(seed, f"{tag}/ibias_a", (m, spec.d_I), 0.5))
+        p.i_bias_b = to_dev(S.normal(seed, f"{tag}/ibias_b", (m, spec.d_I), 0.5))
+    return p
+
+
+def make_raw(seed: int, spec: LayerSpec, tag: str, B: int, base: int, rows: int) -> RawStream:
+    def act(name, c):
+        return to_dev(S.to_bf16(S.activations(seed, f"{tag}/{name}", (B, rows, c))))
+    r = RawStream(base, act("ca", C), act("za", C), act("cb", C), act("zb", C))
+    if spec.kind == "csa":
+        r.i_ca, r.i_za, r.i_cb, r.i_zb = (act(n, spec.d_I) for n in ("ica", "iza", "icb", "izb"))
+    return r
+
+
+def fill_entries(layer: Layer, seed: int, tag: str, n: int, chunk: int = 65536):
+    """Entries [0, n) of every sequence: N(0,1)^576 times a per-entry scale log-uniform in [0.1, 10],
+    stored by the library's compressor at m = 1 (no norm, no RoPE); indexer keys N(0,1) bf16."""
+    for b in range(layer.B):
+        x = S.block_scaled(seed, f"{tag}/entries", b, n, C)
+        for lo in range(0, n, chunk):
+            xs = torch.from_numpy(x[None, lo:lo + chunk]).cuda()
+            lca.kv_compress(xs, torch.zeros_like(xs), None, None, _seq_view(layer.comp, b), m=1, overlap=0,
+                            first_pos=lo)
+        if layer.keys is not None:
+            k = S.to_bf16(S.normal(seed, f"{tag}/keys/{b}", (n, layer.spec.d_I)))
+            layer.keys.nope[b, :n].copy_(to_dev(k))
+    torch.cuda.synchronize()
+
+
+def fill_window(layer: Layer, seed: int, tag: str, t0: int):
+    """Ring rows for positions [t0 - cap, t0) (same law as the entries)."""
+    cap = layer.win.cap
+    p0 = max(0, t0 - cap)
+    for b in range(layer.B):
+        x = S.block_scaled(seed, f"{tag}/window", b, t0 - p0, C)
+        xs = torch.from_numpy(x[None]).cuda()
+        lca.kv_compress(xs, torch.zeros_like(xs), None, None, _seq_view(layer.win, b), m=1, overlap=0,
+                        first_pos=p0, ring=1)
+    torch.cuda.synchronize()
+
+
+def _seq_view(kv: lca.KV, b: int) -> lca.KV:
+    return lca.KV(kv.nope[b:b + 1], None if kv.rope is None else kv.rope[b:b + 1],
+                  None if kv.scale is None else kv.scale[b:b + 1], kv.fmt, kv.d_nope, kv.d_rope, kv.cap)
+
+
+def clone_layer(src: Layer) -> Layer:
+    dst = Layer.__new__(Layer)
+    dst.__dict__.update(src.__dict__)
+    dst.comp = lca.KV(src.comp.nope.clone(), src.comp.rope.clone(), src.comp.scale.clone(), src.comp.fmt,
+                      src.comp.d_nope, src.comp.d_rope, src.comp.cap)
+    dst.win = lca.KV(src.win.nope.clone(), src.win.rope.clone(), src.win.scale.clone(), src.win.fmt,
+                     src.win.d_nope, src.win.d_rope, src.win.cap)
+    if src.keys is not None:
+        dst.keys = lca.KV(src.keys.nope.clone(), None, None, src.keys.fmt, src.keys.d_nope, 0, src.keys.cap)
+        dst.scores = torch.empty_like(src.scores)
+        dst.idx = torch.empty_like(src.idx)
+        dst.topk_ws = torch.empty_like(src.topk_ws)
+    dst.ws = torch.empty_like(src.ws)
+    return dst
+
+
+class Stack:
+    """Layers of one sequence group with their raw streams and per-position queries."""
+
+    def __init__(self, specs, tags, B, t0, n_pos, t_chunk, seed, win_cap, raw_span=0):
+        self.specs, self.B, self.t0 = specs, B, t0
+        self.layers, self.raws, self.q, self.qi, self.w = [], [], [], [], []
+        span = max(n_pos, t_chunk, raw_span) + 8
+        for spec, tag in zip(specs, tags):
+            vis0 = (t0 + 1) // spec.m
+            cap = (t0 + span) // spec.m + 2
+            layer = Layer(spec, B, cap, win_cap, t_chunk, make_params(seed, spec, tag))
+            fill_entries(layer, seed, tag, vis0)
+            fill_window(layer, seed, tag, t0)
+            self.layers.append(layer)
+            self.raws.append(make_raw(seed, spec, tag, B, t0 - 2 * spec.m, span + 2 * spec.m))
+            self.q.append(to_dev(S.to_bf16(S.normal(seed, f"{tag}/q", (n_pos, B, 1, spec.H, C)))))
+            if spec.kind == "csa":
+                self.qi.append(to_dev(S.to_bf16(S.normal(seed, f"{tag}/qi", (n_pos, B, 1, spec.H_I, spec.d_I)))))
+                self.w.append(to_dev(S.normal(seed, f"{tag}/w", (n_pos, B, 1, spec.H_I), 0.25)))
+            else:
+                self.qi.append(None)
+                self.w.append(None)
+        self.out = [torch.empty(B, 1, s.H, C, dtype=torch.bfloat16, device="cuda") for s in specs]
+
+    def replicate(self):
+        other = Stack.__new__(Stack)
+        other.__dict__.update(self.__dict__)
+        other.layers = [clone_layer(l) for l in self.layers]
+        other.out = [torch.empty_like(o) for o in self.out]
+        return other
+
+    def decode(self, j: int, record=None):
+        """Decode token j (position t0 + j) through every layer."""
+        t = self.t0 + j
+        for li, layer in enumerate(self.layers):
+            layer.step(self.raws[li], t, self.q[li][j], self.out[li],
+                       q_idx=None if self.qi[li] is None else self.qi[li][j],
+                       w=None if self.w[li] is None else self.w[li][j], record=record)
+
+
+class KernelTimer:
+    """HIP events around every launch of one kernel, recorded on its stream."""
+
+    def __init__(self, name: str):
+        self.name, self.pairs = name, []
+
+    def __call__(self, name, fn):
+        if name != self.name:
+            return fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        self.pairs.append((a, b))
+
+    def mean_ms(self) -> float:
+        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs]))
+
+
+def timed_graph_decode(stacks, W: int, K: int, timer: KernelTimer | None):
+    """W eager warm-up steps, then K steps captured as one graph; replayed once untimed, once timed."""
+    R = len(stacks)
+    for i in range(W):
+        stacks[i % R].decode(i // R)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(W, W + K):
+            stacks[i % R].decode(i // R, record=timer)
+    g.replay()
+    torch.cuda.synchronize()
+    if timer is not None:
+        warm = [(a.elapsed_time(b)) for a, b in timer.pairs]
+        del warm
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e), g
+
+
+# ----------------------------------------------------------------------------
+# workloads
+# ----------------------------------------------------------------------------
+
+STACK_SPECS = [LayerSpec("hca", 128), LayerSpec("hca", 128), LayerSpec("csa", 4, k=2048), LayerSpec("hca", 128)]
+STACK_TAGS = ["L0_hca", "L1_hca", "L2_csa", "L3_hca"]
+
+
+def indexer_bytes(vis: int, B: int, d_I: int = 128, H_I: int = 16) -> int:
+    """Algorithmic bytes of one decode indexer launch: keys read once, scores written, q and w read."""
+    return B * (vis * d_I * 2 + vis * 2 + H_I * d_I * 2 + H_I * 4)
+
+
+def bench_decode_1m(W: int, K: int, R: int, seed: int = 1005):
+    n_pos = (W + K + R - 1) // R + 2
+    log(f"building the 1M-context stack ({R} replicas, {n_pos} positions each)")
+    t_build = time.time()
+    base = Stack(STACK_SPECS, STACK_TAGS, 1, T0_1M, n_pos, 1, seed, win_cap=8192, raw_span=4096)
+    stacks = [base] + [base.replicate() for _ in range(R - 1)]
+    torch.cuda.synchronize()
+    log(f"built in {time.time() - t_build:.1f} s")
+    timer = KernelTimer("indexer_score")
+    timing = "HIP events on the launch stream, recorded inside the timed graph"
+    try:
+        ms, g = timed_graph_decode(stacks, W, K, timer)
+        ind_ms = timer.mean_ms()
+    except Exception as ex:  # event nodes unsupported in capture: time the kernel on eager launches
+        log(f"events inside the graph failed ({ex}); timing the indexer on eager launches")
+        ms, g = timed_graph_decode(stacks, W, K, None)
+        timer = KernelTimer("indexer_score")
+        for i in range(W, W + K):
+            stacks[i % R].decode(i // R, record=timer)
+        torch.cuda.synchronize()
+        ind_ms = timer.mean_ms()
+        timing = "HIP events on the launch stream, eager launches of the timed steps"
+    vis = (T0_1M + 1) // 4
+    nbytes = indexer_bytes(vis, 1)
+    achieved = nbytes / (ind_ms * 1e-3) / 1e9
+    del g
+    return dict(ms=ms, ms_per_step=ms / K, tokens_per_s=K / (ms * 1e-3), indexer_ms=ind_ms,
+                roofline=dict(kernel="indexer_score", bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS,
+                              unit="GB/s", frac=achieved / HBM_PEAK_GBS, traffic=None,
+                              bytes_per_launch=nbytes, launch_ms=ind_ms, timing=timing)), stacks
+
+
+def attn_flops(T: int, t0: int, m: int, H: int, n_win: int, k: int | None) -> float:
+    """Multiply-add flops (2 per MAC) of Q K^T and P V over the attended rows of T queries."""
+    tot = 0
+    for i in range(T):
+        t = t0 + i
+        keys = (k if k is not None else (t + 1) // m) + min(n_win, t + 1)
+        tot += keys
+    return 4.0 * tot * H * C
+
+
+def bench_prefill_1m(stack: Stack, reps: int = 3, T: int = 4096, seed: int = 1005):
+    """The stack's 4096-token chunk at 1M context; every rep restarts from the same cache state."""
+    log("building the 4096-token prefill inputs")
+    qs, qis, ws = [], [], []
+    for spec, tag in zip(stack.specs, STACK_TAGS):
+        qs.append(to_dev(S.to_bf16(S.normal(seed, f"{tag}/qp", (1, T, spec.H, C)))))
+        if spec.kind == "csa":
+            qis.append(to_dev(S.to_bf16(S.normal(seed, f"{tag}/qip", (1, T, spec.H_I, spec.d_I)))))
+            ws.append(to_dev(S.normal(seed, f"{tag}/wp", (1, T, spec.H_I), 0.25)))
+        else:
+            qis.append(None)
+            ws.append(None)
+    # the chunk needs T rows of scores / idx and prefill-sized scratch
+    for layer in stack.layers:
+        if layer.spec.kind == "csa" and layer.scores.shape[1] < T:
+            layer.scores = torch.empty(1, T, layer.comp.cap, dtype=torch.bfloat16, device="cuda")
+            layer.idx = torch.empty(1, T, layer.spec.k, dtype=torch.int32, device="cuda")
+    outs = [torch.empty(1, T, s.H, C, dtype=torch.bfloat16, device="cuda") for s in stack.specs]
+    timers = {n: KernelTimer(n) for n in ("indexer_score", "topk_select", "csa_attn", "hca_attn")}
+
+    def rec(name, fn):
+        if name in timers:
+            return timers[name](name, fn)
+        return fn()
+
+    def chunk(record=None):
+        for li, layer in enumerate(stack.layers):
+            layer.step(stack.raws[li], stack.t0, qs[li], outs[li], q_idx=qis[li], w=ws[li], record=record)
+
+    chunk()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        chunk()
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    chunk(record=rec)
+    torch.cuda.synchronize()
+    kt = {n: t.mean_ms() for n, t in timers.items() if t.pairs}
+    hca_fl = attn_flops(T, stack.t0, 128, 64, 128, None)
+    csa_fl = attn_flops(T, stack.t0, 4, 64, 128, 2048)
+    idx_fl = 2.0 * 16 * 128 * sum((stack.t0 + i + 1) // 4 for i in range(T))
+    tot_fl = 3 * hca_fl + csa_fl + idx_fl
+    hca_tf = hca_fl / (kt["hca_attn"] * 1e-3) / 1e12
+    return dict(tokens=T, ms=ms, tokens_per_s=T / (ms * 1e-3), tflops=tot_fl / (ms * 1e-3) / 1e12,
+                mfma_frac=tot_fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, kernel_ms=kt,
+                hca_attn=dict(flops=hca_fl, tflops=hca_tf, frac=hca_tf / BF16_PEAK_TFLOPS),
+                indexer=dict(flops=idx_fl, tflops=idx_fl / (kt["indexer_score"] * 1e-3) / 1e12),
+                csa_attn=dict(flops=csa_fl, tflops=csa_fl / (kt["csa_attn"] * 1e-3) / 1e12))
+
+
+def bench_decode_c4(W: int, K: int, seed: int = 1004):
+    """CSA decode, 32 sequences at 131,072 tokens (32,768 fp8 entries each), top-k 1024, window 128."""
+    B, t0 = 32, 131072
+    spec = LayerSpec("csa", 4, k=1024)
+    n_pos = W + K + 2
+    log("building the 32 x 128K CSA decode state")
+    st = Stack([spec], ["c4_csa"], B, t0, n_pos, 1, seed, win_cap=256)
+    timer = KernelTimer("indexer_score")
+    try:
+        ms, g = timed_graph_decode([st], W, K, timer)
+        ind_ms = timer.mean_ms()
+    except Exception:
+        ms, g = timed_graph_decode([st], W, K, None)
+        timer = KernelTimer("indexer_score")
+        for i in range(W, W + K):
+            st.decode(i, record=timer)
+        torch.cuda.synchronize()
+        ind_ms = timer.mean_ms()
+    del g
+    vis = (t0 + 1) // 4
+    nbytes = indexer_bytes(vis, B)
+    gbs = nbytes / (ind_ms * 1e-3) / 1e9
+    step_bytes = nbytes + B * (1024 + 128) * 656 + B * 64 * C * 2 * 2
+    return dict(batch=B, ctx=t0, ms_per_step=ms / K, tokens_per_s=B * K / (ms * 1e-3),
+                step_hbm_gbs=step_bytes / (ms / K * 1e-3) / 1e9,
+                indexer=dict(launch_ms=ind_ms, gbs=gbs, frac=gbs / HBM_PEAK_GBS, bytes=nbytes))
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on a bounded sample of the 1M decode workload
+# ----------------------------------------------------------------------------
+
+def cpu_baseline(n_steps: int = 2, seed: int = 1005):
+    import oracle as orc
+    log(f"cpu baseline: oracle, {n_steps} decode steps of the 1M stack")
+    t0 = T0_1M
+    g = S.stream(seed, "cpu/bytes")
+
+    def kv_random(n, fmt=orc.FP8):
+        kv = orc.KV.empty(fmt, 1, n, 512, 64)
+        codes = g.integers(0, 256, size=kv.nope.shape, dtype=np.uint8)
+        codes[(codes & 0x7F) == 0x7F] &= 0xFE          # no NaN codes
+        kv.nope[...] = codes
+        kv.scale[...] = np.exp2(g.integers(-9, -4, size=kv.scale.shape)).astype(np.float32)
+        kv.rope[...] = S.to_bf16(g.standard_normal(kv.rope.shape).astype(np.float32))
+        return kv
+
+    layers = []
+    for spec, tag in zip(STACK_SPECS, STACK_TAGS):
+        cap = (t0 + n_steps + 8) // spec.m + 2
+        d = dict(spec=spec, comp=kv_random(cap), win=kv_random(8192))
+        if spec.kind == "csa":
+            d["keys"] = S.to_bf16(g.standard_normal((1, cap, 128)).astype(np.float32))
+        d["raw"] = [S.to_bf16(S.activations(seed, f"cpu/{tag}/{n}", (1, 2 * spec.m + n_steps, C)))
+                    for n in ("ca", "za", "cb", "zb")]
+        d["iraw"] = [S.to_bf16(S.activations(seed, f"cpu/{tag}/i{n}", (1, 2 * spec.m + n_steps, 128)))
+                     for n in ("ca", "za", "cb", "zb")]
+        layers.append(d)
+    q = S.to_bf16(S.normal(seed, "cpu/q", (1, 1, 64, C)))
+    qi = S.to_bf16(S.normal(seed, "cpu/qi", (1, 1, 16, 128)))
+    w = S.normal(seed, "cpu/w", (1, 1, 16), 0.25)
+    sink = S.normal(seed, "cpu/sink", (64,))
+    gamma = np.ones(C, np.float32)
+    start = time.perf_counter()
+    for j in range(n_steps):
+        t = t0 + j
+        for d in layers:
+            spec = d["spec"]
+            base = t0 - 2 * spec.m
+            r = [x[:, t - base:t - base + 1] for x in d["raw"]]
+            orc.kv_compress(r[0], r[1], None, None, d["win"], m=1, overlap=0, first_pos=[t], gamma=gamma,
+                            rope_theta=1e4, ring=1)
+            if (t + 1) % spec.m == 0:
+                lo = t + 1 - (1 + spec.overlap) * spec.m
+                rr = [x[:, lo - base:t + 1 - base] for x in d["raw"]]
+                orc.kv_compress(rr[0], rr[1], rr[2] if spec.overlap else None, rr[3] if spec.overlap else None,
+                                d["comp"], m=spec.m, overlap=spec.overlap, first_pos=[lo], gamma=gamma,
+                                rope_theta=1e4)
+            if spec.kind == "csa":
+                sc = orc.indexer_score(qi, w, d["keys"], q_pos=[t], m=4, score_fmt=orc.BF16)
+                idx = orc.topk_select(sc, q_pos=[t], m=4, k=spec.k)
+                orc.attention(q, q_pos=[t], comp=d["comp"], m=4, idx=idx, win=d["win"], n_win=128, sink=sink,
+                              sm_scale=C ** -0.5, rope_theta=1e4, out_fmt=orc.BF16)
+            else:
+                orc.attention(q, q_pos=[t], comp=d["comp"], m=128, idx=None, win=d["win"], n_win=128, sink=sink,
+                              sm_scale=C ** -0.5, rope_theta=1e4, out_fmt=orc.BF16)
+    el = time.perf_counter() - start
+    return dict(value=n_steps / el, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"{n_steps} decode steps of the 1M-context 4-layer stack (fp64 oracle; one query row "
+                       f"per call, so one host thread does the work); {el:.1f} s; random stored cache bytes of "
+                       f"the benchmark's shapes")
+
+
+# ----------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--replicas", type=int, default=6)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-extra", action="store_true", help="skip the prefill and the 32 x 128K decode")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    lca.lib()  # fail loudly when the HIP library is missing
+    torch.cuda.set_device(0)
+    K, W, R = args.steps, args.warmup, args.replicas
+
+    d = bench_decode_1m(W, K, R)
+    res, stacks = d
+    log(f"1M decode: {res['ms_per_step'] * 1e3:.1f} us/step, {res['tokens_per_s']:.0f} tok/s; indexer "
+        f"{res['indexer_ms'] * 1e3:.1f} us = {res['roofline']['achieved']:.0f} GB/s")
+    extra = {}
+    if not args.no_extra:
+        pf = bench_prefill_1m(stacks[0])
+        log(f"1M prefill chunk: {pf['ms']:.2f} ms, {pf['tokens_per_s']:.0f} tok/s, {pf['tflops']:.0f} TFLOP/s")
+        extra["prefill_1m_chunk4096"] = pf
+        del stacks
+        torch.cuda.empty_cache()
+        c4 = bench_decode_c4(W, min(K, 64))
+        log(f"32 x 128K decode: {c4['ms_per_step'] * 1e3:.1f} us/step, {c4['tokens_per_s']:.0f} tok/s")
+        extra["decode_csa_b32_128k"] = c4
+    else:
+        del stacks
+    cpu = None if args.no_cpu else cpu_baseline()
+    line = {
+        "metric": METRIC, "value": res["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": res["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "decode, 4-layer HCA/HCA/CSA/HCA stack, 1 sequence at 1,048,576 tokens",
+                   "global_batch": 1, "seq_len": T0_1M, "layers": "HCA,HCA,CSA,HCA", "csa_entries": 262144,
+                   "hca_entries": 8192, "top_k": 2048, "n_win": 128, "heads": 64, "head_dim": "512+64",
+                   "kv": "fp8-e4m3 (pow2 scale / 128 dims) + bf16 rope", "indexer": "16x128 bf16, bf16 scores",
+                   "replicas": R, "parallelism": "single GPU"},
+        "roofline": res["roofline"],
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

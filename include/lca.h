@@ -80,9 +80,10 @@ typedef struct lca_kv {
  * per-position bias, then RMSNorm ([R] 2.3.3), partial RoPE ([R] 2.3.3) and
  * the store into `out`.
  *
- * Inputs c_a, z_a, c_b, z_b: [B][n_rows][c], dtype in_dtype (LCA_F32 or
- * LCA_BF16), c = out.d_nope + out.d_rope; row i of sequence b is position
- * first_pos[b] + i.  bias_a, bias_b: f32 [m][c] (NULL = zero).  For entry s
+ * Inputs c_a, z_a, c_b, z_b: B sequences of n_rows rows of c values, dtype
+ * in_dtype (LCA_F32 or LCA_BF16), c = out.d_nope + out.d_rope; sequence b
+ * starts in_stride rows after sequence b-1 (in_stride = 0 means n_rows, i.e.
+ * [B][n_rows][c]); row i of sequence b is position first_pos[b] + i.  bias_a, bias_b: f32 [m][c] (NULL = zero).  For entry s
  * and channel j the logits are z_a[s*m+i][j] + bias_a[i][j] (i < m) and, when
  * overlap != 0 and s >= 1, z_b[(s-1)*m+i][j] + bias_b[i][j]; one softmax over
  * them weights the matching c_a / c_b values.  c_b, z_b may be NULL when
@@ -97,13 +98,14 @@ typedef struct lca_kv {
  * out.cap entries of the call are written).  m = 1 with overlap = 0 is the
  * raw-row store used for the sliding window.
  * Errors: LCA_EINVAL (null inputs, m < 1, overlap not 0/1), LCA_EDTYPE,
+ * LCA_ESHAPE (0 < in_stride < n_rows, ...),
  * LCA_ESHAPE (B out of range, c != d_nope + d_rope, fp8 with d_nope % 128,
  * a non-ring entry row >= cap), LCA_EALIGN.
  */
 int lca_kv_compress(const void* c_a, const void* z_a, const void* c_b, const void* z_b,
                     int32_t in_dtype, const float* bias_a, const float* bias_b,
                     const float* gamma, float eps, double rope_theta,
-                    int32_t m, int32_t overlap, int32_t B, int64_t n_rows,
+                    int32_t m, int32_t overlap, int32_t B, int64_t n_rows, int64_t in_stride,
                     const int64_t* first_pos, lca_kv out, int32_t ring, void* stream);
 
 /*
@@ -133,7 +135,9 @@ int lca_indexer_score(const void* q, const float* w, const void* k, int32_t in_d
  * (-0 equals +0); idx[b][i][0..K) lists them in ascending order and the rest
  * of the row is -1.  scores: [B][T][s_stride] (LCA_F32 or LCA_BF16, finite);
  * idx: int32 [B][T][k].  ws: device workspace of at least
- * lca_topk_workspace_size(...) bytes (may be NULL when that is 0).
+ * lca_topk_workspace_size(B, T, s_stride, k) bytes (may be NULL when that
+ * is 0; nonzero only for few long rows, where each row is split across
+ * workgroups).  The workspace needs no initialisation.
  */
 int lca_topk_select(const void* scores, int32_t score_dtype, int64_t s_stride, int32_t B,
                     int32_t T, const int64_t* q_pos, int32_t m, int32_t k, int32_t* idx,

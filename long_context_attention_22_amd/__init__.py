@@ -46,8 +46,8 @@ def lib():
         vp, i32, i64, f32, f64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_double, C.c_size_t
         L.lca_version.restype = C.c_int
         L.lca_last_error.restype = C.c_char_p
-        L.lca_kv_compress.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, f32, f64, i32, i32, i32, i64, vp,
-                                      _KV, i32, vp]
+        L.lca_kv_compress.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, f32, f64, i32, i32, i32, i64, i64,
+                                      vp, _KV, i32, vp]
         L.lca_indexer_score.argtypes = [vp, vp, vp, i32, i64, i32, i32, i32, i32, vp, i32, vp, i32, i64,
                                         vp]
         L.lca_topk_select.argtypes = [vp, i32, i64, i32, i32, vp, i32, i32, vp, vp, sz, vp]
@@ -136,11 +136,18 @@ class KV:
 def kv_compress(c_a, z_a, c_b, z_b, out: KV, *, m: int, overlap: int, first_pos, bias_a=None,
                 bias_b=None, gamma=None, eps: float = 1e-6, rope_theta: float = 0.0, ring: int = 0,
                 stream=None):
-    B, n_rows, _ = c_a.shape
+    """Inputs [B][n_rows][c]; each may be a row window of a longer per-sequence stream (rows contiguous,
+    the same sequence stride for all four)."""
+    B, n_rows, c = c_a.shape
+    for t in (c_a, z_a, c_b, z_b):
+        if t is not None and (t.shape != c_a.shape or t.stride() != c_a.stride() or t.stride(2) != 1
+                              or t.stride(1) != c):
+            raise ValueError("kv_compress inputs must share shape and row-contiguous strides")
+    in_stride = c_a.stride(0) // c if B > 1 else n_rows
     _check(lib().lca_kv_compress(_ptr(c_a), _ptr(z_a), _ptr(c_b), _ptr(z_b), _dtype(c_a), _ptr(bias_a),
                                  _ptr(bias_b), _ptr(gamma), float(eps), float(rope_theta), int(m),
-                                 int(overlap), int(B), int(n_rows), _pos(first_pos, B), out.c(),
-                                 int(ring), _stream(stream)))
+                                 int(overlap), int(B), int(n_rows), int(in_stride), _pos(first_pos, B),
+                                 out.c(), int(ring), _stream(stream)))
 
 
 def indexer_score(q, w, k, scores, *, q_pos, m: int, stream=None):
@@ -159,6 +166,10 @@ def topk_select(scores, idx, *, q_pos, m: int, ws=None, stream=None):
     _check(lib().lca_topk_select(_ptr(scores), _dtype(scores), int(s_stride), int(B), int(T),
                                  _pos(q_pos, B), int(m), int(k), _ptr(idx), _ptr(ws), nbytes,
                                  _stream(stream)))
+
+
+def topk_workspace_size(B: int, T: int, s_stride: int, k: int) -> int:
+    return int(lib().lca_topk_workspace_size(int(B), int(T), int(s_stride), int(k)))
 
 
 def attn_workspace_size(B: int, T: int, H: int, c: int, max_keys: int) -> int:

@@ -315,41 +315,74 @@ __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int64_t split_len, 
 }
 
 // Merge nsplit partial (O, m, l) triples of one (row, head) in split order.
-__global__ void __launch_bounds__(1024) attn_combine(AttnArgs a, int nsplit, int c, int d_nope,
-                                                     int d_rope) {
+// Block (row, head, dim chunk of 192): wave 0 turns the splits' (m, l) into
+// weights in LDS, then every thread reduces its dim over the splits.
+constexpr int kCombDims = 192;
+__global__ void __launch_bounds__(kCombDims) attn_combine(AttnArgs a, int nsplit, int c, int d_nope,
+                                                          int d_rope) {
     const int64_t rowid = blockIdx.x;
     const int h = blockIdx.y;
-    const int d = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int d = blockIdx.z * kCombDims + tid;
     const int64_t nrows = gridDim.x;
     const float* wo = (const float*)a.ws;
     const float* wml = wo + (int64_t)nsplit * nrows * a.H * c;
     const int b = (int)(rowid / a.T);
     const int64_t t = a.q_pos.v[b] + rowid % a.T;
-
-    float M = -INFINITY;
-    for (int j = 0; j < nsplit; ++j) M = fmaxf(M, wml[2 * ((j * nrows + rowid) * a.H + h)]);
-    float mu = M;
-    const float z = a.sink ? a.sink[h] * kLog2e : -INFINITY;
-    if (a.sink) mu = fmaxf(M, z);
-    const float muse = mu == -INFINITY ? 0.0f : mu;
-    float den = a.sink ? exp2f(z - muse) : 0.0f;
-    for (int j = 0; j < nsplit; ++j) {
-        const int64_t pr = (j * nrows + rowid) * a.H + h;
-        den += wml[2 * pr + 1] * exp2f(wml[2 * pr] - muse);
+    __shared__ float wsp[1024];
+    __shared__ float s_mu, s_den;
+    if (tid < 64) {
+        float M = -INFINITY;
+        for (int j = lane; j < nsplit; j += 64) M = fmaxf(M, wml[2 * ((j * nrows + rowid) * a.H + h)]);
+        M = wave_max(M);
+        float mu = M;
+        const float z = a.sink ? a.sink[h] * kLog2e : -INFINITY;
+        if (a.sink) mu = fmaxf(M, z);
+        const float muse = mu == -INFINITY ? 0.0f : mu;
+        float den = 0.0f;
+        for (int j = lane; j < nsplit; j += 64) {
+            const int64_t pr = (j * nrows + rowid) * a.H + h;
+            const float wgt = exp2f(wml[2 * pr] - muse);
+            wsp[j] = wgt;
+            den += wml[2 * pr + 1] * wgt;
+        }
+        den = wave_sum(den) + (a.sink ? exp2f(z - muse) : 0.0f);
+        if (lane == 0) {
+            s_mu = mu;
+            s_den = den;
+        }
     }
+    __syncthreads();
+    const float den = s_den, mu = s_mu;
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    if (a.lse && blockIdx.z == 0 && tid == 0)
+        a.lse[rowid * a.H + h] = den > 0.0f ? (mu + log2f(den)) * kLn2 : -INFINITY;
     if (d >= c) return;
     // this thread's dim, and its RoPE partner when the output is rotated
     const int half = d_rope / 2;
     const bool rot = a.rope_theta != 0.0 && d >= d_nope;
     const int r = d - d_nope;
     const int dp = !rot ? d : (r < half ? d + half : d - half);
+    const int64_t stride = nrows * a.H * c;  // between splits
+    const float* p0 = wo + (rowid * a.H + h) * c;
     float acc = 0.0f, accp = 0.0f;
-    for (int j = 0; j < nsplit; ++j) {
-        const int64_t pr = (j * nrows + rowid) * a.H + h;
-        const float wgt = exp2f(wml[2 * pr] - muse);
-        acc = fmaf(wo[pr * c + d], wgt, acc);
-        if (rot) accp = fmaf(wo[pr * c + dp], wgt, accp);
+    int j = 0;
+    for (; j + 4 <= nsplit; j += 4) {
+        float v[4], vp[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            v[u] = p0[(j + u) * stride + d];
+            vp[u] = rot ? p0[(j + u) * stride + dp] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            acc = fmaf(v[u], wsp[j + u], acc);
+            accp = fmaf(vp[u], wsp[j + u], accp);
+        }
+    }
+    for (; j < nsplit; ++j) {
+        acc = fmaf(p0[j * stride + d], wsp[j], acc);
+        if (rot) accp = fmaf(p0[j * stride + dp], wsp[j], accp);
     }
     float v = acc * inv;
     if (rot) {
@@ -361,7 +394,6 @@ __global__ void __launch_bounds__(1024) attn_combine(AttnArgs a, int nsplit, int
     const int64_t oi = (rowid * a.H + h) * c + d;
     if (a.out_dtype == LCA_F32) ((float*)a.out)[oi] = v;
     else ((uint16_t*)a.out)[oi] = f2bf(v);
-    if (a.lse && d == 0) a.lse[rowid * a.H + h] = den > 0.0f ? (mu + log2f(den)) * kLn2 : -INFINITY;
 }
 
 // f32 caches: one wave per (row, head); lane owns dims lane + 64 u.
@@ -442,10 +474,11 @@ __global__ void __launch_bounds__(64) attn_f32(AttnArgs a) {
 // Split policy: decode-sized launches split the slot list so that the grid
 // covers the chip; prefill-sized launches use one split per row.
 int attn_num_splits(int64_t rows, int64_t max_keys, int32_t c) {
-    if (c != kC || rows >= 128 || max_keys <= 2 * kKT) return 1;
-    int64_t want = (512 + rows - 1) / rows;
-    int64_t most = (max_keys + 63) / 64;  // at least 64 slots per split
+    if (c != kC || rows >= 128 || max_keys <= 4 * kKT) return 1;
+    int64_t want = (256 + rows - 1) / rows;     // about one workgroup per CU
+    int64_t most = (max_keys + 127) / 128;      // at least four tiles per split
     if (want > most) want = most;
+    if (want > 1024) want = 1024;
     if (want < 1) want = 1;
     int64_t len = (max_keys + want - 1) / want;
     len = (len + kKT - 1) / kKT * kKT;
@@ -478,8 +511,8 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     else hipLaunchKernelGGL((attn_mfma<LCA_BF16>), grid, dim3(256), 0, st, a, len, ns);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns <= 1) return e;
-    hipLaunchKernelGGL(attn_combine, dim3((unsigned)rows, (unsigned)a.H), dim3((unsigned)((c + 63) / 64 * 64)), 0,
-                       st, a, ns, c, a.comp.d_nope, a.comp.d_rope);
+    hipLaunchKernelGGL(attn_combine, dim3((unsigned)rows, (unsigned)a.H, (unsigned)((c + kCombDims - 1) / kCombDims)),
+                       dim3(kCombDims), 0, st, a, ns, c, a.comp.d_nope, a.comp.d_rope);
     return hipGetLastError();
 }
 

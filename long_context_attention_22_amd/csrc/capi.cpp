@@ -72,7 +72,7 @@ const char* lca_last_error(void) { return g_err; }
 int lca_kv_compress(const void* c_a, const void* z_a, const void* c_b, const void* z_b,
                     int32_t in_dtype, const float* bias_a, const float* bias_b, const float* gamma,
                     float eps, double rope_theta, int32_t m, int32_t overlap, int32_t B, int64_t n_rows,
-                    const int64_t* first_pos, lca_kv out, int32_t ring, void* stream) {
+                    int64_t in_stride, const int64_t* first_pos, lca_kv out, int32_t ring, void* stream) {
     g_err[0] = 0;
     if (!c_a || !z_a) return fail(LCA_EINVAL, "c_a / z_a is NULL");
     if (m < 1) return fail(LCA_EINVAL, "m must be >= 1 (got %d)", m);
@@ -81,6 +81,8 @@ int lca_kv_compress(const void* c_a, const void* z_a, const void* c_b, const voi
     if (ring != 0 && ring != 1) return fail(LCA_EINVAL, "ring must be 0 or 1");
     if (in_dtype != LCA_F32 && in_dtype != LCA_BF16) return fail(LCA_EDTYPE, "in_dtype must be f32 or bf16");
     if (n_rows < 0) return fail(LCA_ESHAPE, "n_rows < 0");
+    if (in_stride < 0 || (in_stride > 0 && in_stride < n_rows))
+        return fail(LCA_ESHAPE, "in_stride %lld is smaller than n_rows %lld", (long long)in_stride, (long long)n_rows);
     if (!(rope_theta >= 0.0)) return fail(LCA_EINVAL, "rope_theta must be >= 0");
     if (!(eps >= 0.0f)) return fail(LCA_EINVAL, "eps must be >= 0");
     int rc = check_batch(B, first_pos, "first_pos");
@@ -95,6 +97,7 @@ int lca_kv_compress(const void* c_a, const void* z_a, const void* c_b, const voi
     a.bias_a = bias_a; a.bias_b = bias_b; a.gamma = gamma;
     a.eps = eps; a.rope_theta = rope_theta; a.in_dtype = in_dtype;
     a.m = m; a.overlap = overlap; a.B = B; a.n_rows = n_rows; a.out = out; a.ring = ring;
+    a.in_stride = in_stride > 0 ? in_stride : n_rows;
     a.first_pos = to_pos(first_pos, B);
     int64_t most = 0;
     for (int b = 0; b < B; ++b) {
@@ -149,10 +152,13 @@ int lca_indexer_score(const void* q, const float* w, const void* k, int32_t in_d
     return hip_status(lca::launch_indexer(a, (hipStream_t)stream));
 }
 
-size_t lca_topk_workspace_size(int32_t, int32_t, int64_t, int32_t) { return 0; }
+size_t lca_topk_workspace_size(int32_t B, int32_t T, int64_t s_stride, int32_t) {
+    if (B < 1 || T < 1 || s_stride < 1) return 0;
+    return lca::topk_ws_bytes(B, T, s_stride, LCA_BF16);
+}
 
 int lca_topk_select(const void* scores, int32_t score_dtype, int64_t s_stride, int32_t B, int32_t T,
-                    const int64_t* q_pos, int32_t m, int32_t k, int32_t* idx, void*, size_t,
+                    const int64_t* q_pos, int32_t m, int32_t k, int32_t* idx, void* ws, size_t ws_bytes,
                     void* stream) {
     g_err[0] = 0;
     if (!scores || !idx) return fail(LCA_EINVAL, "scores and idx must be non-NULL");
@@ -162,14 +168,21 @@ int lca_topk_select(const void* scores, int32_t score_dtype, int64_t s_stride, i
     if (T < 0 || s_stride < 1) return fail(LCA_ESHAPE, "bad T / s_stride");
     int rc = check_batch(B, q_pos, "q_pos");
     if (rc) return rc;
-    if (!aligned16(scores) || !aligned16(idx)) return fail(LCA_EALIGN, "pointers must be 16-byte aligned");
-    for (int b = 0; b < B && T > 0; ++b)
-        if ((q_pos[b] + T) / m > s_stride)
-            return fail(LCA_ESHAPE, "sequence %d sees more entries than s_stride", b);
+    if (!aligned16(scores) || !aligned16(idx) || !aligned16(ws)) return fail(LCA_EALIGN, "pointers must be 16-byte aligned");
+    int64_t max_n = 0;
+    for (int b = 0; b < B && T > 0; ++b) {
+        const int64_t n = (q_pos[b] + T) / m;
+        if (n > s_stride) return fail(LCA_ESHAPE, "sequence %d sees more entries than s_stride", b);
+        if (n > max_n) max_n = n;
+    }
+    if (T == 0) return LCA_OK;
+    const size_t need = lca::topk_ws_bytes(B, T, s_stride, score_dtype);
+    if (need > 0 && (!ws || ws_bytes < need))
+        return fail(LCA_EWORKSPACE, "top-k workspace of %zu bytes needed (got %zu)", need, ws_bytes);
     lca::TopkArgs a;
     memset(&a, 0, sizeof a);
     a.scores = scores; a.score_dtype = score_dtype; a.s_stride = s_stride; a.B = B; a.T = T; a.m = m;
-    a.k = k; a.idx = idx; a.q_pos = to_pos(q_pos, B);
+    a.k = k; a.idx = idx; a.ws = ws; a.max_n = max_n; a.q_pos = to_pos(q_pos, B);
     return hip_status(lca::launch_topk(a, (hipStream_t)stream));
 }
 

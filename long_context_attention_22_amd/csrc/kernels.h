@@ -26,7 +26,7 @@ struct CompressArgs {
     double rope_theta;
     int32_t in_dtype;
     int32_t m, overlap, B;
-    int64_t n_rows;
+    int64_t n_rows, in_stride;
     lca_kv out;
     int32_t ring;
     Pos first_pos;
@@ -56,8 +56,11 @@ struct TopkArgs {
     int64_t s_stride;
     int32_t B, T, m, k;
     int32_t* idx;
+    void* ws;
+    int64_t max_n;   // largest candidate count over the rows
     Pos q_pos;
 };
+size_t topk_ws_bytes(int32_t B, int32_t T, int64_t s_stride, int32_t score_dtype);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 
 struct AttnArgs {

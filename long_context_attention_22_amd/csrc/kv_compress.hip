@@ -79,7 +79,7 @@ __global__ void __launch_bounds__(1024) kv_compress_kernel(CompressArgs a) {
     float y = 0.0f;
     if (j < c) {
         float mx = -INFINITY, den = 0.0f, num = 0.0f;
-        const int64_t ra = (int64_t)b * a.n_rows + (s * m - p0);
+        const int64_t ra = (int64_t)b * a.in_stride + (s * m - p0);
         pool_rows<T>((const T*)a.z_a + ra * c + j, (const T*)a.c_a + ra * c + j,
                      a.bias_a ? a.bias_a + j : nullptr, m, c, mx, den, num);
         if (a.overlap && s >= 1) {

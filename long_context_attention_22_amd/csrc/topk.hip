@@ -3,15 +3,24 @@
 // with the largest scores, ties to the lower index, emitted in ascending
 // index order and padded with -1.
 //
-// One 1024-thread workgroup per row.  Scores become monotone unsigned keys
-// (bf16: 16 bits, f32: 32 bits; -0 folded onto +0).  An MSB-first radix
-// select with 8-bit digits finds the K-th largest key tau and how many keys
-// equal to tau are taken (the lowest-indexed ones): one LDS histogram pass
-// per digit, with 16 sub-histograms (one per lane mod 16) so that lanes that
-// share a bin rarely hit the same LDS word.  A final pass walks the row in
-// index order and compacts the winners with a block-wide exclusive scan
-// (wave shuffles + LDS), which yields ascending output and the
-// lower-index tie rule directly.
+// Scores become monotone unsigned keys (bf16: 16 bits, f32: 32 bits; -0 is
+// folded onto +0).  An MSB-first radix select with 8-bit digits finds the
+// K-th largest key tau and how many keys equal to tau are taken (the
+// lowest-indexed ones); a final pass walks the row in index order and
+// compacts the winners with a block-wide exclusive scan, which yields the
+// ascending output and the lower-index tie rule directly.  Histograms live
+// in LDS with 16 copies (one per lane mod 16) so that lanes sharing a bin
+// rarely hit the same LDS word; rows are read with 16-byte loads, four in
+// flight per thread.
+//
+// Two schedules:
+//   row   -- one 1024-thread workgroup per row (many rows: prefill).
+//   split -- bf16 rows that are few and long (decode): each row is cut into
+//            4096-key chunks, one workgroup per chunk, in three launches
+//            (high-byte histograms, low-byte histograms of the chosen high
+//            byte, emit).  Every workgroup re-derives the digits and its
+//            output offset from the per-chunk histograms in the workspace,
+//            so no launch needs a grid-wide barrier or zeroed memory.
 #include "device.h"
 #include "kernels.h"
 
@@ -19,6 +28,8 @@ namespace lca {
 
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kChunk = 4096;           // keys per workgroup in the split schedule
+constexpr int kSplitThreads = 256;
 
 __device__ __forceinline__ uint32_t mono_key(uint16_t h) {
     if (h == 0x8000u) h = 0;
@@ -30,7 +41,53 @@ __device__ __forceinline__ uint32_t mono_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// inclusive prefix sum over the workgroup; returns the inclusive value and the total
+template <typename TS>
+struct Vec;
+template <>
+struct Vec<uint16_t> {
+    static constexpr int N = 8;
+    __device__ static __forceinline__ uint32_t key(const u32x4& v, int u) {
+        return mono_key((uint16_t)((v[u >> 1] >> (16 * (u & 1))) & 0xffffu));
+    }
+};
+template <>
+struct Vec<float> {
+    static constexpr int N = 4;
+    __device__ static __forceinline__ uint32_t key(const u32x4& v, int u) {
+        return mono_key(__uint_as_float(v[u]));
+    }
+};
+
+// f(index, key) for every element of row[lo, hi); NT threads, order unspecified.
+template <typename TS, int NT, typename F>
+__device__ __forceinline__ void for_each_key(const TS* row, int64_t lo, int64_t hi, F f) {
+    constexpr int V = Vec<TS>::N;
+    const int tid = threadIdx.x;
+    const uintptr_t addr = (uintptr_t)(row + lo);
+    int64_t head = (int64_t)(((16u - (addr & 15u)) & 15u) / sizeof(TS));
+    if (head > hi - lo) head = hi - lo;
+    for (int64_t e = lo + tid; e < lo + head; e += NT) f(e, mono_key(row[e]));
+    const int64_t b0 = lo + head;
+    const int64_t nv = (hi - b0) / V;
+    const u32x4* vp = (const u32x4*)(row + b0);
+    for (int64_t v = tid; v < nv; v += 4 * NT) {
+        u32x4 x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (v + j * NT < nv) x[j] = vp[v + j * NT];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (v + j * NT < nv) {
+#pragma unroll
+                for (int u = 0; u < V; ++u) f(b0 + (v + j * NT) * V + u, Vec<TS>::key(x[j], u));
+            }
+        }
+    }
+    for (int64_t e = b0 + nv * V + tid; e < hi; e += NT) f(e, mono_key(row[e]));
+}
+
+// inclusive prefix sum over the workgroup; also returns the total
+template <int NW>
 __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
 #pragma unroll
@@ -42,7 +99,7 @@ __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* wsum, 
     __syncthreads();
     uint32_t off = 0, tot = 0;
 #pragma unroll
-    for (int w = 0; w < kTopkWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
         uint32_t x = wsum[w];
         off += w < wv ? x : 0u;
         tot += x;
@@ -52,8 +109,40 @@ __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* wsum, 
     return v + off;
 }
 
+// Find the digit d with (count of digits > d) < rem <= (count of digits >= d).
+// Run by one wave over hsum[256]; writes *digit and *rem_out (rem minus keys above d).
+__device__ __forceinline__ void pick_digit(const uint32_t* hsum, uint32_t rem, uint32_t* digit,
+                                           uint32_t* rem_out) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t h0 = hsum[4 * lane], h1 = hsum[4 * lane + 1], h2 = hsum[4 * lane + 2],
+                   h3 = hsum[4 * lane + 3];
+    const uint32_t loc = h0 + h1 + h2 + h3;
+    uint32_t suf = loc;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        uint32_t nb = __shfl_down(suf, o, kWave);
+        if (lane + o < 64) suf += nb;
+    }
+    const uint32_t above = suf - loc;
+    if (above < rem && suf >= rem) {
+        uint32_t acc = above;
+        const uint32_t hs[4] = {h0, h1, h2, h3};
+        for (int d = 3; d >= 0; --d) {
+            if (acc + hs[d] >= rem) {
+                *digit = 4 * lane + d;
+                *rem_out = rem - acc;
+                break;
+            }
+            acc += hs[d];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// row schedule
+// ---------------------------------------------------------------------------
 template <typename TS, int BITS>
-__global__ void __launch_bounds__(kTopkThreads) topk_kernel(TopkArgs a) {
+__global__ void __launch_bounds__(kTopkThreads) topk_row(TopkArgs a) {
     const int b = blockIdx.y, i = blockIdx.x;
     const int64_t t = a.q_pos.v[b] + i;
     const int64_t n = min((t + 1) / a.m, a.s_stride);
@@ -73,60 +162,34 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(TopkArgs a) {
     __shared__ uint32_t wsum[kTopkWaves];
     __shared__ uint32_t sel_digit, sel_rem;
 
-    uint32_t prefix = 0;          // digits fixed so far (in place)
-    uint32_t rem = (uint32_t)K;   // how many of the keys matching the prefix are still to take
+    uint32_t prefix = 0;
+    uint32_t rem = (uint32_t)K;
 #pragma unroll 1
     for (int shift = BITS - 8; shift >= 0; shift -= 8) {
         for (int j = tid; j < 256 * 16; j += kTopkThreads) hist[j] = 0;
         __syncthreads();
         const uint32_t hmask = (shift + 8 >= 32) ? 0u : (0xffffffffu << (shift + 8));
-        for (int64_t e = tid; e < n; e += kTopkThreads) {
-            const uint32_t key = mono_key(row[e]);
-            if ((key & hmask) == (prefix & hmask))
-                atomicAdd(&hist[((key >> shift) & 255u) * 16 + (lane & 15)], 1u);
-        }
+        const uint32_t want = prefix & hmask;
+        const int sub = lane & 15;
+        for_each_key<TS, kTopkThreads>(row, 0, n, [&](int64_t, uint32_t key) {
+            if ((key & hmask) == want) atomicAdd(&hist[((key >> shift) & 255u) * 16 + sub], 1u);
+        });
         __syncthreads();
         if (tid < 256) {
             uint32_t s = 0;
 #pragma unroll
-            for (int c = 0; c < 16; ++c) s += hist[tid * 16 + c];
+            for (int c = 0; c < 16; ++c) s += hist[tid * 16 + ((c + tid) & 15)];
             hsum[tid] = s;
         }
         __syncthreads();
-        if (tid < 64) {
-            // lane owns digits 4*lane .. 4*lane+3; suffix sums from the top digit down
-            uint32_t h0 = hsum[4 * tid], h1 = hsum[4 * tid + 1], h2 = hsum[4 * tid + 2],
-                     h3 = hsum[4 * tid + 3];
-            uint32_t loc = h0 + h1 + h2 + h3;
-            uint32_t suf = loc;  // sum over lanes >= tid
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                uint32_t nb = __shfl_down(suf, o, kWave);
-                if (tid + o < 64) suf += nb;
-            }
-            const uint32_t above = suf - loc;  // keys in higher lanes' digits
-            if (above < rem && suf >= rem) {
-                uint32_t acc = above;
-                uint32_t hs[4] = {h0, h1, h2, h3};
-                for (int d = 3; d >= 0; --d) {
-                    if (acc + hs[d] >= rem) {
-                        sel_digit = 4 * tid + d;
-                        sel_rem = rem - acc;
-                        break;
-                    }
-                    acc += hs[d];
-                }
-            }
-        }
+        if (tid < 64) pick_digit(hsum, rem, &sel_digit, &sel_rem);
         __syncthreads();
         prefix |= sel_digit << shift;
         rem = sel_rem;
         __syncthreads();
     }
-    const uint32_t tau = prefix;   // the K-th largest key
-    // rem = number of keys equal to tau to take (lowest indices first)
+    const uint32_t tau = prefix;
 
-    // emit: each thread takes 8 consecutive elements per round, in index order
     uint32_t gt_base = 0, eq_base = 0;
     for (int64_t base = 0; base < n; base += 8 * kTopkThreads) {
         const int64_t e0 = base + 8 * (int64_t)tid;
@@ -134,14 +197,14 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(TopkArgs a) {
         uint32_t ngt = 0, neq = 0;
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            keys[u] = (e0 + u < n) ? mono_key(row[e0 + u]) : 0u;
             const bool valid = e0 + u < n;
+            keys[u] = valid ? mono_key(row[e0 + u]) : 0u;
             ngt += (valid && keys[u] > tau) ? 1u : 0u;
             neq += (valid && keys[u] == tau) ? 1u : 0u;
         }
         uint32_t tot;
-        const uint32_t incl = block_incl_scan(ngt | (neq << 16), wsum, &tot);
-        const uint32_t excl = incl - (ngt | (neq << 16));
+        const uint32_t packed = ngt | (neq << 16);
+        const uint32_t excl = block_incl_scan<kTopkWaves>(packed, wsum, &tot) - packed;
         uint32_t gt_before = gt_base + (excl & 0xffffu);
         uint32_t eq_before = eq_base + (excl >> 16);
 #pragma unroll
@@ -162,13 +225,197 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(TopkArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// split schedule (bf16 scores)
+// ---------------------------------------------------------------------------
+struct SplitRow {
+    const uint16_t* row;
+    int32_t* out;
+    int64_t n, K;
+    uint32_t* h1;   // [G][256] high-byte histograms of this row
+    uint32_t* h2;   // [G][256] low-byte histograms (keys with the chosen high byte)
+};
+
+__device__ __forceinline__ SplitRow split_row(const TopkArgs& a, int G) {
+    SplitRow r;
+    const int64_t rowid = blockIdx.y;
+    const int b = (int)(rowid / a.T);
+    const int64_t t = a.q_pos.v[b] + rowid % a.T;
+    r.n = min((t + 1) / a.m, a.s_stride);
+    r.K = min((int64_t)a.k, r.n);
+    r.row = (const uint16_t*)a.scores + rowid * a.s_stride;
+    r.out = a.idx + rowid * a.k;
+    r.h1 = (uint32_t*)a.ws + rowid * (int64_t)G * 512;
+    r.h2 = r.h1 + (int64_t)G * 256;
+    return r;
+}
+
+// local histogram of the chunk into LDS (16 copies), reduced into hs[256]
+template <int NT, typename F>
+__device__ __forceinline__ void chunk_hist(const uint16_t* row, int64_t lo, int64_t hi, uint32_t* hist,
+                                           uint32_t* hs, F bin_of) {
+    const int tid = threadIdx.x, sub = tid & 15;
+    for (int j = tid; j < 256 * 16; j += NT) hist[j] = 0;
+    __syncthreads();
+    for_each_key<uint16_t, NT>(row, lo, hi, [&](int64_t, uint32_t key) {
+        const int bin = bin_of(key);
+        if (bin >= 0) atomicAdd(&hist[bin * 16 + sub], 1u);
+    });
+    __syncthreads();
+    if (tid < 256) {
+        uint32_t s = 0;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) s += hist[tid * 16 + ((c + tid) & 15)];
+        hs[tid] = s;
+    }
+    __syncthreads();
+}
+
+// digits of the K-th largest key from the per-chunk histograms: hi byte and the count still to take
+__device__ __forceinline__ void reduce_pick(const uint32_t* h, int G, uint32_t rem, uint32_t* tot,
+                                            uint32_t* digit, uint32_t* rem_out) {
+    const int tid = threadIdx.x;
+    if (tid < 256) {
+        uint32_t s = 0;
+        for (int g = 0; g < G; ++g) s += h[g * 256 + tid];
+        tot[tid] = s;
+    }
+    __syncthreads();
+    if (tid < 64) pick_digit(tot, rem, digit, rem_out);
+    __syncthreads();
+}
+
+__global__ void __launch_bounds__(kSplitThreads) topk_split_h1(TopkArgs a, int G) {
+    const SplitRow r = split_row(a, G);
+    const int g = blockIdx.x;
+    const int64_t lo = (int64_t)g * kChunk, hi = min(lo + kChunk, r.n);
+    __shared__ uint32_t hist[256 * 16];
+    __shared__ uint32_t hs[256];
+    if (r.n <= r.K) return;  // trivial row: the emit launch handles it
+    chunk_hist<kSplitThreads>(r.row, lo, hi < lo ? lo : hi, hist, hs, [](uint32_t key) { return (int)(key >> 8); });
+    if (threadIdx.x < 256) r.h1[g * 256 + threadIdx.x] = hs[threadIdx.x];
+}
+
+__global__ void __launch_bounds__(kSplitThreads) topk_split_h2(TopkArgs a, int G) {
+    const SplitRow r = split_row(a, G);
+    const int g = blockIdx.x;
+    const int64_t lo = (int64_t)g * kChunk, hi = min(lo + kChunk, r.n);
+    __shared__ uint32_t hist[256 * 16];
+    __shared__ uint32_t hs[256];
+    __shared__ uint32_t d1, rem1;
+    if (r.n <= r.K) return;
+    reduce_pick(r.h1, G, (uint32_t)r.K, hs, &d1, &rem1);
+    const uint32_t hb = d1;
+    chunk_hist<kSplitThreads>(r.row, lo, hi < lo ? lo : hi, hist, hs,
+                              [hb](uint32_t key) { return (key >> 8) == hb ? (int)(key & 255u) : -1; });
+    if (threadIdx.x < 256) r.h2[g * 256 + threadIdx.x] = hs[threadIdx.x];
+}
+
+__global__ void __launch_bounds__(kSplitThreads) topk_split_emit(TopkArgs a, int G) {
+    const SplitRow r = split_row(a, G);
+    const int g = blockIdx.x, tid = threadIdx.x;
+    const int64_t lo = (int64_t)g * kChunk, hi = min(lo + kChunk, r.n);
+    if (r.n <= r.K) {  // fewer candidates than k: all of them, in order
+        for (int64_t j = lo + tid; j < lo + kChunk && j < a.k; j += kSplitThreads)
+            r.out[j] = j < r.n ? (int32_t)j : -1;
+        if (g == G - 1)
+            for (int64_t j = (int64_t)G * kChunk + tid; j < a.k; j += kSplitThreads) r.out[j] = j < r.n ? (int32_t)j : -1;
+        return;
+    }
+    __shared__ uint32_t tot[256];
+    __shared__ uint32_t d1, rem1, d2, rem2;
+    __shared__ uint32_t wsum[kSplitThreads / 64];
+    __shared__ uint32_t base_gt, base_eq;
+    reduce_pick(r.h1, G, (uint32_t)r.K, tot, &d1, &rem1);
+    reduce_pick(r.h2, G, rem1, tot, &d2, &rem2);
+    const uint32_t tau = (d1 << 8) | d2, rem = rem2;
+    if (g == 0)
+        for (int64_t j = r.K + tid; j < a.k; j += kSplitThreads) r.out[j] = -1;
+    // keys above tau and equal to tau in the chunks before this one
+    {
+        uint32_t gt = 0, eq = 0;
+        for (int gg = tid; gg < g; gg += kSplitThreads) {
+            const uint32_t* p1 = r.h1 + gg * 256;
+            const uint32_t* p2 = r.h2 + gg * 256;
+            for (int bin = d1 + 1; bin < 256; ++bin) gt += p1[bin];
+            for (int bin = d2 + 1; bin < 256; ++bin) gt += p2[bin];
+            eq += p2[d2];
+        }
+        uint32_t t1, t2;
+        block_incl_scan<kSplitThreads / 64>(gt, wsum, &t1);
+        block_incl_scan<kSplitThreads / 64>(eq, wsum, &t2);
+        if (tid == 0) {
+            base_gt = t1;
+            base_eq = t2;
+        }
+        __syncthreads();
+    }
+    uint32_t gt_base = base_gt, eq_base = base_eq;
+    for (int64_t base = lo; base < hi; base += 8 * kSplitThreads) {
+        const int64_t e0 = base + 8 * (int64_t)tid;
+        uint32_t keys[8];
+        uint32_t ngt = 0, neq = 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const bool valid = e0 + u < hi;
+            keys[u] = valid ? mono_key(r.row[e0 + u]) : 0u;
+            ngt += (valid && keys[u] > tau) ? 1u : 0u;
+            neq += (valid && keys[u] == tau) ? 1u : 0u;
+        }
+        uint32_t t;
+        const uint32_t packed = ngt | (neq << 16);
+        const uint32_t excl = block_incl_scan<kSplitThreads / 64>(packed, wsum, &t) - packed;
+        uint32_t gt_before = gt_base + (excl & 0xffffu);
+        uint32_t eq_before = eq_base + (excl >> 16);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (e0 + u >= hi) break;
+            const uint32_t pos = gt_before + min(eq_before, rem);
+            if (keys[u] > tau) {
+                r.out[pos] = (int32_t)(e0 + u);
+                ++gt_before;
+            } else if (keys[u] == tau) {
+                if (eq_before < rem) r.out[pos] = (int32_t)(e0 + u);
+                ++eq_before;
+            }
+        }
+        gt_base += t & 0xffffu;
+        eq_base += t >> 16;
+    }
+}
+
+// split schedule for few long bf16 rows
+static bool use_split(const TopkArgs& a, int64_t max_n) {
+    const int64_t rows = (int64_t)a.B * a.T;
+    return a.score_dtype == LCA_BF16 && rows < 128 && max_n > 2 * kChunk;
+}
+
+static int split_chunks(int64_t max_n) { return (int)((max_n + kChunk - 1) / kChunk); }
+
+size_t topk_ws_bytes(int32_t B, int32_t T, int64_t s_stride, int32_t score_dtype) {
+    TopkArgs a;
+    a.B = B;
+    a.T = T;
+    a.score_dtype = score_dtype;
+    if (!use_split(a, s_stride)) return 0;
+    return (size_t)B * T * split_chunks(s_stride) * 512 * sizeof(uint32_t);
+}
+
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
+    if (use_split(a, a.max_n)) {
+        const int G = split_chunks(a.s_stride);
+        dim3 grid((unsigned)G, (unsigned)(a.B * a.T));
+        hipLaunchKernelGGL(topk_split_h1, grid, dim3(kSplitThreads), 0, st, a, G);
+        hipLaunchKernelGGL(topk_split_h2, grid, dim3(kSplitThreads), 0, st, a, G);
+        hipLaunchKernelGGL(topk_split_emit, grid, dim3(kSplitThreads), 0, st, a, G);
+        return hipGetLastError();
+    }
     dim3 grid((unsigned)a.T, (unsigned)a.B);
     if (a.score_dtype == LCA_BF16)
-        hipLaunchKernelGGL((topk_kernel<uint16_t, 16>), grid, dim3(kTopkThreads), 0, st, a);
+        hipLaunchKernelGGL((topk_row<uint16_t, 16>), grid, dim3(kTopkThreads), 0, st, a);
     else
-        hipLaunchKernelGGL((topk_kernel<float, 32>), grid, dim3(kTopkThreads), 0, st, a);
+        hipLaunchKernelGGL((topk_row<float, 32>), grid, dim3(kTopkThreads), 0, st, a);
     return hipGetLastError();
 }
 

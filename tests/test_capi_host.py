@@ -51,12 +51,12 @@ def pos(*v):
 
 def compress(L, **kw):
     a = dict(c_a=FAKE, z_a=FAKE, c_b=FAKE, z_b=FAKE, in_dtype=lca.BF16, bias_a=None, bias_b=None,
-             gamma=None, eps=1e-6, theta=0.0, m=4, overlap=1, B=1, n_rows=64, first_pos=pos(0),
-             out=kv(), ring=0)
+             gamma=None, eps=1e-6, theta=0.0, m=4, overlap=1, B=1, n_rows=64, in_stride=0,
+             first_pos=pos(0), out=kv(), ring=0)
     a.update(kw)
     return L.lca_kv_compress(a["c_a"], a["z_a"], a["c_b"], a["z_b"], a["in_dtype"], a["bias_a"], a["bias_b"],
                              a["gamma"], a["eps"], a["theta"], a["m"], a["overlap"], a["B"], a["n_rows"],
-                             a["first_pos"], a["out"], a["ring"], None)
+                             a["in_stride"], a["first_pos"], a["out"], a["ring"], None)
 
 
 def test_kv_compress_validation(L):
@@ -77,6 +77,7 @@ def test_kv_compress_validation(L):
     assert compress(L, out=kv(cap=8)) == 2
     assert b"cap" in L.lca_last_error()
     assert compress(L, theta=-1.0) == 1
+    assert compress(L, in_stride=63) == 2
 
 
 def indexer(L, **kw):

@@ -119,8 +119,11 @@ def test_indexer_f32_path():
 @pytest.mark.parametrize("sfmt", [orc.F32, orc.BF16])
 @pytest.mark.parametrize("k,q_pos,T,stride,ties", [(16, [0], 300, 80, True), (512, [130000], 2, 40000, True),
                                                    (2048, [160000], 1, 40960, False), (1, [50, 9], 6, 64, True),
-                                                   (1024, [131071, 100], 3, 32768, False)])
+                                                   (1024, [131071, 100], 3, 32768, False),
+                                                   (2048, [1048575], 1, 262150, False),
+                                                   (64, [40000, 3], 130, 10100, True)])
 def test_topk(sfmt, k, q_pos, T, stride, ties):
+    """Bit-exact against the oracle; bf16 rows that are few and long take the split schedule."""
     m, B = 4, len(q_pos)
     raw = S.normal(9, "scores", (B, T, stride), 3.0)
     if ties:
@@ -129,7 +132,8 @@ def test_topk(sfmt, k, q_pos, T, stride, ties):
     sc = raw.astype(np.float32) if sfmt == orc.F32 else S.to_bf16(raw.astype(np.float32))
     o = orc.topk_select(sc, q_pos=q_pos, m=m, k=k)
     ig = torch.full((B, T, k), 7, dtype=torch.int32, device="cuda")
-    lca.topk_select(dev(sc), ig, q_pos=q_pos, m=m)
+    ws = torch.empty(max(16, lca.topk_workspace_size(B, T, stride, k)), dtype=torch.uint8, device="cuda")
+    lca.topk_select(dev(sc), ig, q_pos=q_pos, m=m, ws=ws)
     assert np.array_equal(host(ig), o)
 
 
