@@ -11,10 +11,14 @@
 //   a list of "slots": compressed slots (idx entries, or 0..vis-1) followed by
 //   window slots.  Per tile of 32 slots the workgroup gathers the rows from HBM
 //   (fp8 codes are expanded to bf16 exactly: the scale is a power of two) into
-//   LDS twice: row-major (K operand of Q.K^T, 16 contiguous bytes per lane) and
-//   transposed (V operand of P.V, 8 consecutive keys of one dim per lane).  The
-//   next tile's rows are fetched into registers while the current tile is
-//   computed.  Wave w owns heads [16w, 16w+16): S = Q K^T with
+//   one row-major LDS tile.  It serves both operands: the K operand of Q.K^T
+//   (16 contiguous bytes of one key per lane, ds_read_b128) and the V operand
+//   of P.V (8 consecutive keys of one dim per lane) through gfx950's
+//   transposing LDS read ds_read_b64_tr_b16: within each 16-lane group, lane i
+//   receives element i mod 4 of the 8-byte rows addressed by lanes i/4 + 4e,
+//   so lanes addressing (key r/4, dims 4(r mod 4)..+3) hand lane i four
+//   consecutive keys of dim i.  The next tile's rows are fetched into
+//   registers while the current tile is computed.  Wave w owns heads [16w, 16w+16): S = Q K^T with
 //   v_mfma_f32_16x16x32_bf16 (M = heads, N = keys, K = 576 in 18 steps, Q kept
 //   in registers), online softmax in the accumulator layout (row max / sum over
 //   16 lanes), P goes through a small per-wave LDS buffer into A-operand
@@ -31,7 +35,7 @@ namespace lca {
 constexpr int kDN = 512, kDR = 64, kC = 576;
 constexpr int kKT = 32;             // slots per tile
 constexpr int kKS = kC + 8;         // row stride of the row-major tile (bf16 elements)
-constexpr int kVS = kKT + 8;        // row stride of the transposed tile
+constexpr int kVS = kKT + 8;        // row stride of the per-wave P tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -100,54 +104,57 @@ struct Gather {
     }
 };
 
-__device__ __forceinline__ void put8(uint16_t* Kt, uint16_t* Vt, int j, int d0, u32x4 v) {
+__device__ __forceinline__ void put8(uint16_t* Kt, int j, int d0, u32x4 v) {
     *(u32x4*)(Kt + j * kKS + d0) = v;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        Vt[(d0 + 2 * e) * kVS + j] = (uint16_t)(v[e] & 0xffffu);
-        Vt[(d0 + 2 * e + 1) * kVS + j] = (uint16_t)(v[e] >> 16);
-    }
 }
 
-// fp8 code -> bf16 bits of code * scale (exact)
-__device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t two_codes, float sc) {
-    const float lo = fp8_to_f32(two_codes & 0xffu) * sc;
-    const float hi = fp8_to_f32((two_codes >> 8) & 0xffu) * sc;
-    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+// transposing LDS read (see the header comment)
+__device__ __forceinline__ s16x4 lds_tr16(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)p);
+}
+
+// two fp8 codes (low 16 bits when !high_half) -> packed bf16 bits of code * scale.  The hardware
+// conversion decodes OCP e4m3fn exactly; the power-of-two scale keeps the product exact and a
+// 4-significant-bit value loses nothing when the low 16 bits are dropped.
+template <bool kHigh>
+__device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t codes, float sc) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const f2 v = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes, kHigh);
+    const uint32_t lo = __float_as_uint(v[0] * sc), hi = __float_as_uint(v[1] * sc);
+    return __builtin_amdgcn_perm(hi, lo, 0x07060302u);
 }
 
 template <int FMT>
-__device__ __forceinline__ void store_tile(const Gather<FMT>& g, uint16_t* Kt, uint16_t* Vt, int j,
-                                           int cg) {
+__device__ __forceinline__ void store_tile(const Gather<FMT>& g, uint16_t* Kt, int j, int cg) {
     if (FMT == LCA_FP8) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int d0 = 16 * (cg + 8 * u);
             u32x4 lo, hi;
-            lo[0] = fp8x2_bf16(g.v[u][0], g.sc[u]);
-            lo[1] = fp8x2_bf16(g.v[u][0] >> 16, g.sc[u]);
-            lo[2] = fp8x2_bf16(g.v[u][1], g.sc[u]);
-            lo[3] = fp8x2_bf16(g.v[u][1] >> 16, g.sc[u]);
-            hi[0] = fp8x2_bf16(g.v[u][2], g.sc[u]);
-            hi[1] = fp8x2_bf16(g.v[u][2] >> 16, g.sc[u]);
-            hi[2] = fp8x2_bf16(g.v[u][3], g.sc[u]);
-            hi[3] = fp8x2_bf16(g.v[u][3] >> 16, g.sc[u]);
+            lo[0] = fp8x2_bf16<false>(g.v[u][0], g.sc[u]);
+            lo[1] = fp8x2_bf16<true>(g.v[u][0], g.sc[u]);
+            lo[2] = fp8x2_bf16<false>(g.v[u][1], g.sc[u]);
+            lo[3] = fp8x2_bf16<true>(g.v[u][1], g.sc[u]);
+            hi[0] = fp8x2_bf16<false>(g.v[u][2], g.sc[u]);
+            hi[1] = fp8x2_bf16<true>(g.v[u][2], g.sc[u]);
+            hi[2] = fp8x2_bf16<false>(g.v[u][3], g.sc[u]);
+            hi[3] = fp8x2_bf16<true>(g.v[u][3], g.sc[u]);
             if (!g.src) lo = hi = u32x4{0u, 0u, 0u, 0u};
-            put8(Kt, Vt, j, d0, lo);
-            put8(Kt, Vt, j, d0 + 8, hi);
+            put8(Kt, j, d0, lo);
+            put8(Kt, j, d0 + 8, hi);
         }
-        put8(Kt, Vt, j, kDN + 8 * cg, g.v[4]);
+        put8(Kt, j, kDN + 8 * cg, g.v[4]);
     } else {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) put8(Kt, Vt, j, 8 * (cg + 8 * u), g.v[u]);
-        put8(Kt, Vt, j, kDN + 8 * cg, g.v[8]);
+        for (int u = 0; u < 8; ++u) put8(Kt, j, 8 * (cg + 8 * u), g.v[u]);
+        put8(Kt, j, kDN + 8 * cg, g.v[8]);
     }
 }
 
 template <int FMT>
 __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int64_t split_len, int nsplit) {
     __shared__ __attribute__((aligned(16))) uint16_t Kt[kKT * kKS];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[kC * kVS];
     __shared__ __attribute__((aligned(16))) uint16_t Ps[4][32 * kVS];
     __shared__ int valid[kKT];
 
@@ -189,7 +196,7 @@ __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int64_t split_len, 
 
     for (int64_t s0 = s_begin; s0 < s_end; s0 += kKT) {
         __syncthreads();  // previous tile fully consumed
-        store_tile<FMT>(g, Kt, Vt, gj, gcg);
+        store_tile<FMT>(g, Kt, gj, gcg);
         if (gcg == 0) valid[gj] = g.src != 0;
         __syncthreads();
         if (s0 + kKT < s_end) g.load(a, sm, rowid, b, s0 + kKT + gj, s_end, gcg);
@@ -206,26 +213,40 @@ __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int64_t split_len, 
                 s[bl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], kb, s[bl], 0, 0, 0);
             }
         }
-        // online softmax; lane holds rows (heads) 4 kgrp + r, columns (slots) hrow and 16 + hrow
+        // online softmax; lane holds rows (heads) 4 kgrp + r, columns (slots) hrow and 16 + hrow.
+        // The reference max moves only when a row's max exceeds it by more than 2^8 (weights stay
+        // <= 256), so O is rescaled on few tiles instead of every tile.
         const bool v0 = valid[hrow], v1 = valid[16 + hrow];
-        float p0[4], p1[4], corr[4];
+        float p0[4], p1[4], x0[4], x1[4], mx[4];
+        bool grow = false;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float x0 = v0 ? s[0][r] * qk_scale : -INFINITY;
-            const float x1 = v1 ? s[1][r] * qk_scale : -INFINITY;
-            const float mx = max16(fmaxf(x0, x1));
-            const float mnew = fmaxf(mrun[r], mx);
-            const float muse = mnew == -INFINITY ? 0.0f : mnew;
-            p0[r] = exp2f(x0 - muse);
-            p1[r] = exp2f(x1 - muse);
-            corr[r] = exp2f(mrun[r] - muse);
-            lrun[r] = lrun[r] * corr[r] + sum16(p0[r] + p1[r]);
-            mrun[r] = mnew;
+            x0[r] = v0 ? s[0][r] * qk_scale : -INFINITY;
+            x1[r] = v1 ? s[1][r] * qk_scale : -INFINITY;
+            mx[r] = max16(fmaxf(x0[r], x1[r]));
+            grow |= mx[r] > mrun[r] + 8.0f;
+        }
+        if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform
+            float corr[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float mnew = fmaxf(mrun[r], mx[r]);
+                corr[r] = mnew == -INFINITY ? 1.0f : exp2f(mrun[r] - mnew);
+                lrun[r] *= corr[r];
+                mrun[r] = mnew;
+            }
+#pragma unroll
+            for (int nb = 0; nb < 36; ++nb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[nb][r] *= corr[r];
         }
 #pragma unroll
-        for (int nb = 0; nb < 36; ++nb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) o[nb][r] *= corr[r];
+        for (int r = 0; r < 4; ++r) {
+            const float muse = mrun[r] == -INFINITY ? 0.0f : mrun[r];
+            p0[r] = exp2f(x0[r] - muse);
+            p1[r] = exp2f(x1[r] - muse);
+            lrun[r] += sum16(p0[r] + p1[r]);
+        }
         // P through LDS into A layout, A[row = head hrow][k = slot 8 kgrp + e], as two bf16
         // terms P = hi + lo (hi = bf16(P), lo = bf16(P - hi)): both multiply the same V
         // fragment, so P V keeps ~16 mantissa bits at no extra LDS traffic.
@@ -241,11 +262,14 @@ __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int64_t split_len, 
         __syncthreads();
         const bf16x8 pa = __builtin_bit_cast(bf16x8, *(const u32x4*)(pw + hrow * kVS + 8 * kgrp));
         const bf16x8 pl = __builtin_bit_cast(bf16x8, *(const u32x4*)(pw + (16 + hrow) * kVS + 8 * kgrp));
-        // O += P V: B[k = slot 8 kgrp + e][n = dim 16 nb + hrow]
-        const uint16_t* vr = Vt + hrow * kVS + 8 * kgrp;
+        // O += P V: B[k = slot 8 kgrp + e][n = dim 16 nb + hrow], two transposing reads of
+        // four slots each; this lane addresses slot 8 kgrp + hrow / 4 (+4), dims 4 (hrow % 4)
+        const uint16_t* vr = Kt + (8 * kgrp + (hrow >> 2)) * kKS + 4 * (hrow & 3);
 #pragma unroll
         for (int nb = 0; nb < 36; ++nb) {
-            const bf16x8 vb = __builtin_bit_cast(bf16x8, *(const u32x4*)(vr + 16 * nb * kVS));
+            const s16x4 v0 = lds_tr16(vr + 16 * nb);
+            const s16x4 v1 = lds_tr16(vr + 4 * kKS + 16 * nb);
+            const bf16x8 vb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
             o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[nb], 0, 0, 0);
             o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, o[nb], 0, 0, 0);
         }
@@ -367,15 +391,15 @@ __global__ void __launch_bounds__(kCombDims) attn_combine(AttnArgs a, int nsplit
     const float* p0 = wo + (rowid * a.H + h) * c;
     float acc = 0.0f, accp = 0.0f;
     int j = 0;
-    for (; j + 4 <= nsplit; j += 4) {
-        float v[4], vp[4];
+    for (; j + 16 <= nsplit; j += 16) {
+        float v[16], vp[16];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 16; ++u) {
             v[u] = p0[(j + u) * stride + d];
             vp[u] = rot ? p0[(j + u) * stride + dp] : 0.0f;
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 16; ++u) {
             acc = fmaf(v[u], wsp[j + u], acc);
             accp = fmaf(vp[u], wsp[j + u], accp);
         }

@@ -271,15 +271,23 @@ __device__ __forceinline__ void chunk_hist(const uint16_t* row, int64_t lo, int6
     __syncthreads();
 }
 
+// sum of bin `bin` over the first n chunk histograms (8 independent loads in flight)
+__device__ __forceinline__ uint32_t col_sum(const uint32_t* h, int n, int bin) {
+    uint32_t s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int g = 0;
+    for (; g + 8 <= n; g += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s[u] += h[(g + u) * 256 + bin];
+    }
+    for (; g < n; ++g) s[0] += h[g * 256 + bin];
+    return s[0] + s[1] + s[2] + s[3] + s[4] + s[5] + s[6] + s[7];
+}
+
 // digits of the K-th largest key from the per-chunk histograms: hi byte and the count still to take
 __device__ __forceinline__ void reduce_pick(const uint32_t* h, int G, uint32_t rem, uint32_t* tot,
                                             uint32_t* digit, uint32_t* rem_out) {
     const int tid = threadIdx.x;
-    if (tid < 256) {
-        uint32_t s = 0;
-        for (int g = 0; g < G; ++g) s += h[g * 256 + tid];
-        tot[tid] = s;
-    }
+    if (tid < 256) tot[tid] = col_sum(h, G, tid);
     __syncthreads();
     if (tid < 64) pick_digit(tot, rem, digit, rem_out);
     __syncthreads();
@@ -333,14 +341,10 @@ __global__ void __launch_bounds__(kSplitThreads) topk_split_emit(TopkArgs a, int
         for (int64_t j = r.K + tid; j < a.k; j += kSplitThreads) r.out[j] = -1;
     // keys above tau and equal to tau in the chunks before this one
     {
-        uint32_t gt = 0, eq = 0;
-        for (int gg = tid; gg < g; gg += kSplitThreads) {
-            const uint32_t* p1 = r.h1 + gg * 256;
-            const uint32_t* p2 = r.h2 + gg * 256;
-            for (int bin = d1 + 1; bin < 256; ++bin) gt += p1[bin];
-            for (int bin = d2 + 1; bin < 256; ++bin) gt += p2[bin];
-            eq += p2[d2];
-        }
+        // thread = bin: its counts over the earlier chunks, then a block sum of the bins above tau
+        const uint32_t c1 = col_sum(r.h1, g, tid), c2 = col_sum(r.h2, g, tid);
+        const uint32_t gt = ((uint32_t)tid > d1 ? c1 : 0u) + ((uint32_t)tid > d2 ? c2 : 0u);
+        const uint32_t eq = (uint32_t)tid == d2 ? c2 : 0u;
         uint32_t t1, t2;
         block_incl_scan<kSplitThreads / 64>(gt, wsum, &t1);
         block_incl_scan<kSplitThreads / 64>(eq, wsum, &t2);
