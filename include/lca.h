@@ -161,7 +161,7 @@ size_t lca_topk_workspace_size(int32_t B, int32_t T, int64_t s_stride, int32_t k
  * of out_dtype (LCA_F32 or LCA_BF16).  comp and win share d_nope / d_rope;
  * supported shapes: (d_nope, d_rope) = (512, 64) with H % 16 == 0 for
  * bf16/fp8 caches, any c <= 1024 for f32.  The window ring must hold every
- * needed row: n_win + T - 1 <= win.cap (n_win = 0: no window).  Every
+ * needed row: min(n_win - 1, q_pos[b]) + T <= win.cap (n_win = 0: no window).  Every
  * idx value must be < comp.cap.  ws: device workspace of at least
  * lca_attn_workspace_size(B, T, H, c, max keys per query) bytes.
  */

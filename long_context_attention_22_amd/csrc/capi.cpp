@@ -209,9 +209,12 @@ static int attn_common(const void* q, int32_t q_dtype, int32_t H, int32_t B, int
         if ((rc = check_kv(win, "win", true))) return rc;
         if (win.fmt != comp.fmt || win.d_nope != comp.d_nope || win.d_rope != comp.d_rope)
             return fail(LCA_ESHAPE, "window and compressed caches must share format and dims");
-        if ((int64_t)n_win + T - 1 > win.cap)
-            return fail(LCA_ESHAPE, "window ring too small: n_win + T - 1 = %lld > cap %lld",
-                        (long long)n_win + T - 1, (long long)win.cap);
+        for (int b = 0; b < B; ++b) {  // rows [q_pos - n_win + 1, q_pos + T - 1] that exist
+            const int64_t back = (int64_t)n_win - 1 < q_pos[b] ? (int64_t)n_win - 1 : q_pos[b];
+            if (back + T > win.cap)
+                return fail(LCA_ESHAPE, "window ring too small for sequence %d: %lld rows > cap %lld", b,
+                            (long long)(back + T), (long long)win.cap);
+        }
     }
     const int c = comp.d_nope + comp.d_rope;
     if (comp.fmt == LCA_F32) {

@@ -137,7 +137,8 @@ def test_attn_validation(L):
     assert attn(L, qdt=lca.F32) == 3                              # bf16 cache with f32 queries
     assert attn(L, H=40) == 2                                     # MFMA path: multiple of 16
     assert attn(L, comp=kv(d_nope=256)) == 2                      # MFMA path: 512 + 64
-    assert attn(L, win=kv(cap=100)) == 2                          # n_win + T - 1 > cap
+    assert attn(L, win=kv(cap=100)) == 2                          # min(n_win - 1, q_pos) + T > cap
+    assert attn(L, q_pos=pos(0), T=100, win=kv(cap=99)) == 2
     assert attn(L, win=kv(fmt=lca.FP8, cap=256)) == 2             # window format differs
     assert attn(L, csa=False, comp=kv(cap=10)) == 2               # 26 visible entries > cap
     assert attn(L, out=FAKE2 + 4) == 4
