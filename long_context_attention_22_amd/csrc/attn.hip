@@ -223,7 +223,7 @@ __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int64_t split_len, 
         for (int r = 0; r < 4; ++r) {
             x0[r] = v0 ? s[0][r] * qk_scale : -INFINITY;
             x1[r] = v1 ? s[1][r] * qk_scale : -INFINITY;
-            mx[r] = max16(fmaxf(x0[r], x1[r]));
+            mx[r] = row_max16(fmaxf(x0[r], x1[r]));
             grow |= mx[r] > mrun[r] + 8.0f;
         }
         if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform
@@ -245,7 +245,7 @@ __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int64_t split_len, 
             const float muse = mrun[r] == -INFINITY ? 0.0f : mrun[r];
             p0[r] = exp2f(x0[r] - muse);
             p1[r] = exp2f(x1[r] - muse);
-            lrun[r] += sum16(p0[r] + p1[r]);
+            lrun[r] += row_sum16(p0[r] + p1[r]);
         }
         // P through LDS into A layout, A[row = head hrow][k = slot 8 kgrp + e], as two bf16
         // terms P = hi + lo (hi = bf16(P), lo = bf16(P - hi)): both multiply the same V
@@ -298,7 +298,7 @@ __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int64_t split_len, 
     float sn[2] = {0.0f, 0.0f}, cs[2] = {1.0f, 1.0f};
     if (a.rope_theta != 0.0) {
 #pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2) rope_sincos(a.rope_theta, 16 * q2 + hrow, kDR, -(double)t, &sn[q2], &cs[q2]);
+        for (int q2 = 0; q2 < 2; ++q2) rope_sincos(a.rope.inv, 16 * q2 + hrow, -(double)t, &sn[q2], &cs[q2]);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -411,7 +411,7 @@ __global__ void __launch_bounds__(kCombDims) attn_combine(AttnArgs a, int nsplit
     float v = acc * inv;
     if (rot) {
         float sn, cs;
-        rope_sincos(a.rope_theta, r < half ? r : r - half, d_rope, -(double)t, &sn, &cs);
+        rope_sincos(a.rope.inv, r < half ? r : r - half, -(double)t, &sn, &cs);
         const float vp = accp * inv;
         v = r < half ? v * cs - vp * sn : vp * sn + v * cs;
     }
@@ -485,7 +485,7 @@ __global__ void __launch_bounds__(64) attn_f32(AttnArgs a) {
         if (a.rope_theta != 0.0 && d >= d_nope) {
             const int r = d - d_nope;
             float sn, cs;
-            rope_sincos(a.rope_theta, r < half ? r : r - half, d_rope, -(double)t, &sn, &cs);
+            rope_sincos(a.rope.inv, r < half ? r : r - half, -(double)t, &sn, &cs);
             v = r < half ? v * cs - osh[d + half] * sn : osh[d - half] * sn + v * cs;
         }
         const int64_t oi = (rowid * a.H + h) * c + d;

@@ -5,6 +5,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cmath>
 #include <cstring>
 
 #include "../../include/lca.h"
@@ -54,6 +55,14 @@ int hip_status(hipError_t e) {
     return fail(LCA_EHIP, "HIP launch failed: %s", hipGetErrorString(e));
 }
 
+lca::RopeTab rope_tab(double theta, int d_rope) {
+    lca::RopeTab r;
+    memset(&r, 0, sizeof r);
+    if (theta > 0.0)
+        for (int i = 0; i < d_rope / 2 && i < lca::kMaxRopeHalf; ++i) r.inv[i] = pow(theta, -2.0 * i / d_rope);
+    return r;
+}
+
 lca::Pos to_pos(const int64_t* p, int32_t B) {
     lca::Pos r;
     memset(&r, 0, sizeof r);
@@ -88,6 +97,8 @@ int lca_kv_compress(const void* c_a, const void* z_a, const void* c_b, const voi
     int rc = check_batch(B, first_pos, "first_pos");
     if (rc) return rc;
     if ((rc = check_kv(out, "out", true))) return rc;
+    if (rope_theta > 0.0 && out.d_rope > 2 * lca::kMaxRopeHalf)
+        return fail(LCA_ESHAPE, "RoPE supports d_rope <= %d", 2 * lca::kMaxRopeHalf);
     for (const void* p : {c_a, z_a, c_b, z_b, (const void*)bias_a, (const void*)bias_b, (const void*)gamma})
         if (!aligned16(p)) return fail(LCA_EALIGN, "input pointers must be 16-byte aligned");
 
@@ -96,6 +107,7 @@ int lca_kv_compress(const void* c_a, const void* z_a, const void* c_b, const voi
     a.c_a = c_a; a.z_a = z_a; a.c_b = c_b; a.z_b = z_b;
     a.bias_a = bias_a; a.bias_b = bias_b; a.gamma = gamma;
     a.eps = eps; a.rope_theta = rope_theta; a.in_dtype = in_dtype;
+    a.rope = rope_tab(rope_theta, out.d_rope);
     a.m = m; a.overlap = overlap; a.B = B; a.n_rows = n_rows; a.out = out; a.ring = ring;
     a.in_stride = in_stride > 0 ? in_stride : n_rows;
     a.first_pos = to_pos(first_pos, B);
@@ -217,6 +229,8 @@ static int attn_common(const void* q, int32_t q_dtype, int32_t H, int32_t B, int
         }
     }
     const int c = comp.d_nope + comp.d_rope;
+    if (rope_theta > 0.0 && comp.d_rope > 2 * lca::kMaxRopeHalf)
+        return fail(LCA_ESHAPE, "RoPE supports d_rope <= %d", 2 * lca::kMaxRopeHalf);
     if (comp.fmt == LCA_F32) {
         if (q_dtype != LCA_F32) return fail(LCA_EDTYPE, "f32 caches need f32 queries");
     } else {
@@ -251,6 +265,7 @@ static int attn_common(const void* q, int32_t q_dtype, int32_t H, int32_t B, int
     memset(&a, 0, sizeof a);
     a.q = q; a.q_dtype = q_dtype; a.H = H; a.B = B; a.T = T; a.m = m; a.comp = comp; a.idx = idx; a.k = k;
     a.win = win; a.n_win = n_win; a.sink = sink; a.sm_scale = sm_scale; a.rope_theta = rope_theta;
+    a.rope = rope_tab(rope_theta, comp.d_rope);
     a.out = out; a.out_dtype = out_dtype; a.lse = lse; a.ws = ws; a.q_pos = to_pos(q_pos, B);
     a.max_keys = max_keys;
     if (n_win == 0) a.win = comp;  // never read

@@ -75,18 +75,35 @@ __device__ __forceinline__ float sum16(float v) {
     return v;
 }
 
-// RoPE inverse frequency theta^(-2i/d_rope) and the angle pos*inv_freq
-// reduced to [-pi, pi) in fp64 (positions reach 2^20 and beyond).
-__device__ __forceinline__ void rope_sincos(double theta, int i, int d_rope, double pos, float* sn,
-                                            float* cs) {
-    double inv = exp2(-2.0 * (double)i / (double)d_rope * log2(theta));
-    double ang = pos * inv;
+// RoPE rotation for pair i at position pos: inv[i] = theta^(-2i/d_rope) is computed on the
+// host in fp64; the angle pos * inv[i] is formed and reduced to [-pi, pi] in fp64 (positions
+// reach 2^20 and beyond), then sin / cos are taken in fp32.
+__device__ __forceinline__ void rope_sincos(const double* inv, int i, double pos, float* sn, float* cs) {
+    double ang = pos * inv[i];
     const double two_pi = 6.283185307179586476925;
-    ang = ang - two_pi * rint(ang / two_pi);
-    double s, c;
-    sincos(ang, &s, &c);
-    *sn = (float)s;
-    *cs = (float)c;
+    ang = ang - two_pi * rint(ang * (1.0 / two_pi));
+    sincosf((float)ang, sn, cs);
+}
+
+// 16-lane (one MFMA column group) reductions with DPP row rotations: every lane of the
+// row ends with the result, no LDS traffic.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row_max16(float v) {
+    v = fmaxf(v, dpp<0x128>(v));  // row_ror:8
+    v = fmaxf(v, dpp<0x124>(v));  // row_ror:4
+    v = fmaxf(v, dpp<0x4e>(v));   // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp<0xb1>(v));   // quad_perm [1,0,3,2]
+    return v;
+}
+__device__ __forceinline__ float row_sum16(float v) {
+    v += dpp<0x128>(v);
+    v += dpp<0x124>(v);
+    v += dpp<0x4e>(v);
+    v += dpp<0xb1>(v);
+    return v;
 }
 
 }  // namespace lca

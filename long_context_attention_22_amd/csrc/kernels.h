@@ -13,6 +13,12 @@ struct Pos {
     int64_t v[LCA_MAX_BATCH];
 };
 
+// theta^(-2i/d_rope) for i < d_rope / 2, computed on the host in fp64
+constexpr int kMaxRopeHalf = 64;
+struct RopeTab {
+    double inv[kMaxRopeHalf];
+};
+
 // kv_compress: entries [s_lo[b], s_hi[b]) of each sequence.
 struct CompressArgs {
     const void* c_a;
@@ -24,6 +30,7 @@ struct CompressArgs {
     const float* gamma;
     float eps;
     double rope_theta;
+    RopeTab rope;
     int32_t in_dtype;
     int32_t m, overlap, B;
     int64_t n_rows, in_stride;
@@ -75,6 +82,7 @@ struct AttnArgs {
     const float* sink;
     float sm_scale;
     double rope_theta;
+    RopeTab rope;
     void* out;
     int32_t out_dtype;
     float* lse;

@@ -108,7 +108,7 @@ __global__ void __launch_bounds__(1024) kv_compress_kernel(CompressArgs a) {
             const int r = j - d_nope;
             const int i = r < half ? r : r - half;
             float sn, cs;
-            rope_sincos(a.rope_theta, i, d_rope, (double)(s * m), &sn, &cs);
+            rope_sincos(a.rope.inv, i, (double)(s * m), &sn, &cs);
             if (r < half) y = y * cs - ys[j + half] * sn;
             else y = ys[j - half] * sn + y * cs;
         }

@@ -16,7 +16,7 @@
 // Two schedules:
 //   row   -- one 1024-thread workgroup per row (many rows: prefill).
 //   split -- bf16 rows that are few and long (decode): each row is cut into
-//            4096-key chunks, one workgroup per chunk, in three launches
+//            16384-key chunks, one workgroup per chunk, in three launches
 //            (high-byte histograms, low-byte histograms of the chosen high
 //            byte, emit).  Every workgroup re-derives the digits and its
 //            output offset from the per-chunk histograms in the workspace,
@@ -28,8 +28,8 @@ namespace lca {
 
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
-constexpr int kChunk = 4096;           // keys per workgroup in the split schedule
-constexpr int kSplitThreads = 256;
+constexpr int kChunk = 16384;          // keys per workgroup in the split schedule
+constexpr int kSplitThreads = 512;
 
 __device__ __forceinline__ uint32_t mono_key(uint16_t h) {
     if (h == 0x8000u) h = 0;
@@ -342,9 +342,12 @@ __global__ void __launch_bounds__(kSplitThreads) topk_split_emit(TopkArgs a, int
     // keys above tau and equal to tau in the chunks before this one
     {
         // thread = bin: its counts over the earlier chunks, then a block sum of the bins above tau
-        const uint32_t c1 = col_sum(r.h1, g, tid), c2 = col_sum(r.h2, g, tid);
-        const uint32_t gt = ((uint32_t)tid > d1 ? c1 : 0u) + ((uint32_t)tid > d2 ? c2 : 0u);
-        const uint32_t eq = (uint32_t)tid == d2 ? c2 : 0u;
+        uint32_t gt = 0, eq = 0;
+        if (tid < 256) {
+            const uint32_t c1 = col_sum(r.h1, g, tid), c2 = col_sum(r.h2, g, tid);
+            gt = ((uint32_t)tid > d1 ? c1 : 0u) + ((uint32_t)tid > d2 ? c2 : 0u);
+            eq = (uint32_t)tid == d2 ? c2 : 0u;
+        }
         uint32_t t1, t2;
         block_incl_scan<kSplitThreads / 64>(gt, wsum, &t1);
         block_incl_scan<kSplitThreads / 64>(eq, wsum, &t2);
@@ -391,7 +394,7 @@ __global__ void __launch_bounds__(kSplitThreads) topk_split_emit(TopkArgs a, int
 // split schedule for few long bf16 rows
 static bool use_split(const TopkArgs& a, int64_t max_n) {
     const int64_t rows = (int64_t)a.B * a.T;
-    return a.score_dtype == LCA_BF16 && rows < 128 && max_n > 2 * kChunk;
+    return a.score_dtype == LCA_BF16 && rows < 128 && max_n > kChunk;
 }
 
 static int split_chunks(int64_t max_n) { return (int)((max_n + kChunk - 1) / kChunk); }
