@@ -19,8 +19,12 @@ LIB = os.path.join(HERE, "liblca.so")
 OBJ = os.path.join(ROOT, "_build", "lca")
 
 SOURCES = ["kv_compress.hip", "indexer.hip", "topk.hip", "attn.hip", "capi.cpp"]
+# MFMA accumulators stay in VGPRs (-amdgpu-mfma-vgpr-form): the kernels keep their accumulators
+# within 256 VGPRs, and AGPR accumulators made the compiler copy them back and forth around the
+# attention loop's conditional rescale.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-I", os.path.join(ROOT, "include")]
 
 

@@ -155,6 +155,7 @@ __device__ __forceinline__ void store_tile(const Gather<FMT>& g, uint16_t* Kt, i
 template <int FMT>
 __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int64_t split_len, int nsplit) {
     __shared__ __attribute__((aligned(16))) uint16_t Kt[kKT * kKS];
+    __shared__ __attribute__((aligned(16))) uint16_t Qs[64 * kKS];   // the row's queries, row-major
     __shared__ __attribute__((aligned(16))) uint16_t Ps[4][32 * kVS];
     __shared__ int valid[kKT];
 
@@ -170,14 +171,14 @@ __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int64_t split_len, 
     const int hrow = lane & 15, kgrp = lane >> 4;
     const int h0 = 16 * wv;
 
-    // Q fragments: A[row = head h0 + hrow][k = 32 ks + 8 kgrp + e]
-    bf16x8 qf[18];
+    // queries to LDS (heads >= H read as zero); A fragments are read from there per tile,
+    // which keeps the accumulators and the prefetched rows within the register file
     {
-        const bool hv = h0 + hrow < a.H;
-        const u32x4* qp = (const u32x4*)((const uint16_t*)a.q + ((rowid * a.H) + h0 + hrow) * kC);
-#pragma unroll
-        for (int ks = 0; ks < 18; ++ks)
-            qf[ks] = __builtin_bit_cast(bf16x8, hv ? qp[4 * ks + kgrp] : u32x4{0u, 0u, 0u, 0u});
+        const u32x4* qp = (const u32x4*)((const uint16_t*)a.q + rowid * a.H * kC);
+        for (int c = tid; c < 64 * (kC / 8); c += 256) {
+            const int h = c / (kC / 8), j = c % (kC / 8);
+            *(u32x4*)(Qs + h * kKS + 8 * j) = h < a.H ? qp[c] : u32x4{0u, 0u, 0u, 0u};
+        }
     }
     f32x4 o[36];
 #pragma unroll
@@ -201,16 +202,19 @@ __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int64_t split_len, 
         __syncthreads();
         if (s0 + kKT < s_end) g.load(a, sm, rowid, b, s0 + kKT + gj, s_end, gcg);
 
-        // S = Q K^T for two 16-slot blocks
-        f32x4 s[2];
-#pragma unroll
-        for (int bl = 0; bl < 2; ++bl) {
-            s[bl] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            const uint16_t* kr = Kt + (16 * bl + hrow) * kKS + 8 * kgrp;
+        // S = Q K^T for two 16-slot blocks; A[row = head h0 + hrow][k = 32 ks + 8 kgrp + e]
+        f32x4 s[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+        {
+            const uint16_t* qr = Qs + (h0 + hrow) * kKS + 8 * kgrp;
+            const uint16_t* kr0 = Kt + hrow * kKS + 8 * kgrp;
+            const uint16_t* kr1 = Kt + (16 + hrow) * kKS + 8 * kgrp;
 #pragma unroll
             for (int ks = 0; ks < 18; ++ks) {
-                const bf16x8 kb = __builtin_bit_cast(bf16x8, *(const u32x4*)(kr + 32 * ks));
-                s[bl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], kb, s[bl], 0, 0, 0);
+                const bf16x8 qa = __builtin_bit_cast(bf16x8, *(const u32x4*)(qr + 32 * ks));
+                const bf16x8 k0 = __builtin_bit_cast(bf16x8, *(const u32x4*)(kr0 + 32 * ks));
+                const bf16x8 k1 = __builtin_bit_cast(bf16x8, *(const u32x4*)(kr1 + 32 * ks));
+                s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, k0, s[0], 0, 0, 0);
+                s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, k1, s[1], 0, 0, 0);
             }
         }
         // online softmax; lane holds rows (heads) 4 kgrp + r, columns (slots) hrow and 16 + hrow.
