@@ -87,7 +87,7 @@ struct Gather {
 #pragma unroll
         for (int u = 0; u < kChunks; ++u) v[u] = u32x4{0u, 0u, 0u, 0u};
         if (!src) return;
-        if (FMT == LCA_FP8) {
+        if constexpr (FMT == LCA_FP8) {
             const u32x4* np = (const u32x4*)((const uint8_t*)kv.nope + row * kDN);
 #pragma unroll
             for (int u = 0; u < 4; ++u) v[u] = np[cg + 8 * u];
@@ -127,7 +127,7 @@ __device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t codes, float sc) {
 
 template <int FMT>
 __device__ __forceinline__ void store_tile(const Gather<FMT>& g, uint16_t* Kt, int j, int cg) {
-    if (FMT == LCA_FP8) {
+    if constexpr (FMT == LCA_FP8) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int d0 = 16 * (cg + 8 * u);
@@ -501,12 +501,18 @@ __global__ void __launch_bounds__(64) attn_f32(AttnArgs a) {
 
 // Split policy: decode-sized launches split the slot list so that the grid
 // covers the chip; prefill-sized launches use one split per row.
+#ifndef LCA_SPLIT_TARGET
+#define LCA_SPLIT_TARGET 256   // workgroups a decode-sized launch aims for (one per CU)
+#endif
+#ifndef LCA_SPLIT_MIN_SLOTS
+#define LCA_SPLIT_MIN_SLOTS 128  // fewest slots per split
+#endif
 int attn_num_splits(int64_t rows, int64_t max_keys, int32_t c) {
-    if (c != kC || rows >= 128 || max_keys <= 4 * kKT) return 1;
-    int64_t want = (256 + rows - 1) / rows;     // about one workgroup per CU
-    int64_t most = (max_keys + 127) / 128;      // at least four tiles per split
+    if (c != kC || rows >= 128 || max_keys <= LCA_SPLIT_MIN_SLOTS) return 1;
+    int64_t want = (LCA_SPLIT_TARGET + rows - 1) / rows;
+    int64_t most = (max_keys + LCA_SPLIT_MIN_SLOTS - 1) / LCA_SPLIT_MIN_SLOTS;
     if (want > most) want = most;
-    if (want > 1024) want = 1024;
+    if (want > 1024) want = 1024;           // combine keeps the split weights in LDS
     if (want < 1) want = 1;
     int64_t len = (max_keys + want - 1) / want;
     len = (len + kKT - 1) / kKT * kKT;
