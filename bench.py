@@ -16,7 +16,7 @@ Also reported (key "extra"): the same stack's 4096-token chunked prefill at
 1M context, and CSA decode for 32 sequences at 131,072 tokens.  "roofline"
 covers the dominant decode kernel (indexer_score, HBM-bound), timed with HIP
 events on its stream inside the timed graph.  "cpu_baseline" is the fp64
-oracle timed on host cores on a bounded sample (two decode steps of the
+oracle timed on host cores on a bounded sample (four decode steps of the
 stack).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
@@ -42,6 +42,11 @@ import long_context_attention_22_amd as lca  # noqa: E402
 from long_context_attention_22_amd.stack import Layer, LayerSpec, Params, RawStream  # noqa: E402
 
 METRIC = "CSA/HCA decode tokens/s at 128K–1M ctx (HBM GB/s %) + prefill tokens/s"
+# HBM traffic of the decode indexer launch from rocprofv3 FETCH_SIZE / WRITE_SIZE passes, scaled by
+# the same counters on a plain copy; used only while the indexer source is unchanged since then.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_decode_1m_traffic.json")
+INDEXER_SOURCES = ["long_context_attention_22_amd/csrc/indexer.hip", "long_context_attention_22_amd/csrc/device.h",
+                   "long_context_attention_22_amd/csrc/kernels.h"]
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 T0_1M = 1 << 20
@@ -172,15 +177,17 @@ class Stack:
 
 
 class KernelTimer:
-    """HIP events around every launch of one kernel, recorded on its stream."""
+    """HIP events around every launch of one kernel, recorded on its stream (inside a graph capture
+    they become event-record nodes: external=True)."""
 
-    def __init__(self, name: str):
-        self.name, self.pairs = name, []
+    def __init__(self, name: str, external: bool = False):
+        self.name, self.pairs, self.external = name, [], external
 
     def __call__(self, name, fn):
         if name != self.name:
             return fn()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a = torch.cuda.Event(enable_timing=True, external=self.external)
+        b = torch.cuda.Event(enable_timing=True, external=self.external)
         a.record()
         fn()
         b.record()
@@ -188,6 +195,31 @@ class KernelTimer:
 
     def mean_ms(self) -> float:
         return float(np.mean([a.elapsed_time(b) for a, b in self.pairs]))
+
+
+def graph_kernel_ms(stacks, W: int, K: int, name: str) -> float:
+    """Mean duration of one kernel's launches of the timed steps, replayed back to back in a graph."""
+    R = len(stacks)
+    launches = []
+
+    def grab(n, fn):
+        if n == name:
+            launches.append(fn)
+
+    for i in range(W, W + K):  # collect the launches (nothing runs: only the named one is kept)
+        stacks[i % R].decode(i // R, record=lambda n, fn: grab(n, fn) if n == name else None)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for fn in launches:
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / len(launches)
 
 
 def timed_graph_decode(stacks, W: int, K: int, timer: KernelTimer | None):
@@ -222,6 +254,37 @@ STACK_SPECS = [LayerSpec("hca", 128), LayerSpec("hca", 128), LayerSpec("csa", 4,
 STACK_TAGS = ["L0_hca", "L1_hca", "L2_csa", "L3_hca"]
 
 
+def indexer_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in INDEXER_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """Counter-derived HBM bytes per decode indexer launch, or None when absent or stale."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            d = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_sha256") != indexer_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def calibrate_copy(nbytes: int = 256 << 20, reps: int = 3):
+    """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"calibration copy: {reps} x {nbytes} bytes read and written")
+
+
 def indexer_bytes(vis: int, B: int, d_I: int = 128, H_I: int = 16) -> int:
     """Algorithmic bytes of one decode indexer launch: keys read once, scores written, q and w read."""
     return B * (vis * d_I * 2 + vis * 2 + H_I * d_I * 2 + H_I * 4)
@@ -235,27 +298,17 @@ def bench_decode_1m(W: int, K: int, R: int, seed: int = 1005):
     stacks = [base] + [base.replicate() for _ in range(R - 1)]
     torch.cuda.synchronize()
     log(f"built in {time.time() - t_build:.1f} s")
-    timer = KernelTimer("indexer_score")
-    timing = "HIP events on the launch stream, recorded inside the timed graph"
-    try:
-        ms, g = timed_graph_decode(stacks, W, K, timer)
-        ind_ms = timer.mean_ms()
-    except Exception as ex:  # event nodes unsupported in capture: time the kernel on eager launches
-        log(f"events inside the graph failed ({ex}); timing the indexer on eager launches")
-        ms, g = timed_graph_decode(stacks, W, K, None)
-        timer = KernelTimer("indexer_score")
-        for i in range(W, W + K):
-            stacks[i % R].decode(i // R, record=timer)
-        torch.cuda.synchronize()
-        ind_ms = timer.mean_ms()
-        timing = "HIP events on the launch stream, eager launches of the timed steps"
+    ms, g = timed_graph_decode(stacks, W, K, None)
+    ind_ms = graph_kernel_ms(stacks, W, K, "indexer_score")
+    timing = ("HIP events on the launch stream around one graph replay of the timed steps' indexer launches "
+              "(back to back, same arguments and caches), divided by the launch count")
     vis = (T0_1M + 1) // 4
     nbytes = indexer_bytes(vis, 1)
     achieved = nbytes / (ind_ms * 1e-3) / 1e9
     del g
     return dict(ms=ms, ms_per_step=ms / K, tokens_per_s=K / (ms * 1e-3), indexer_ms=ind_ms,
                 roofline=dict(kernel="indexer_score", bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS,
-                              unit="GB/s", frac=achieved / HBM_PEAK_GBS, traffic=None,
+                              unit="GB/s", frac=achieved / HBM_PEAK_GBS, traffic=measured_traffic(),
                               bytes_per_launch=nbytes, launch_ms=ind_ms, timing=timing)), stacks
 
 
@@ -329,17 +382,8 @@ def bench_decode_c4(W: int, K: int, seed: int = 1004):
     n_pos = W + K + 2
     log("building the 32 x 128K CSA decode state")
     st = Stack([spec], ["c4_csa"], B, t0, n_pos, 1, seed, win_cap=256)
-    timer = KernelTimer("indexer_score")
-    try:
-        ms, g = timed_graph_decode([st], W, K, timer)
-        ind_ms = timer.mean_ms()
-    except Exception:
-        ms, g = timed_graph_decode([st], W, K, None)
-        timer = KernelTimer("indexer_score")
-        for i in range(W, W + K):
-            st.decode(i, record=timer)
-        torch.cuda.synchronize()
-        ind_ms = timer.mean_ms()
+    ms, g = timed_graph_decode([st], W, K, None)
+    ind_ms = graph_kernel_ms([st], W, K, "indexer_score")
     del g
     vis = (t0 + 1) // 4
     nbytes = indexer_bytes(vis, B)
@@ -354,7 +398,7 @@ def bench_decode_c4(W: int, K: int, seed: int = 1004):
 # CPU baseline: the fp64 oracle on a bounded sample of the 1M decode workload
 # ----------------------------------------------------------------------------
 
-def cpu_baseline(n_steps: int = 2, seed: int = 1005):
+def cpu_baseline(n_steps: int = 4, seed: int = 1005):
     import oracle as orc
     log(f"cpu baseline: oracle, {n_steps} decode steps of the 1M stack")
     t0 = T0_1M
@@ -425,6 +469,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=6)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the prefill and the 32 x 128K decode")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 256 MiB device copy (reference for rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -433,6 +479,8 @@ def main():
     lca.lib()  # fail loudly when the HIP library is missing
     torch.cuda.set_device(0)
     K, W, R = args.steps, args.warmup, args.replicas
+    if args.calibrate_copy:
+        calibrate_copy()
 
     d = bench_decode_1m(W, K, R)
     res, stacks = d
