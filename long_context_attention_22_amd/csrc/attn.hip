@@ -70,13 +70,14 @@ __device__ __forceinline__ int slot_row(const AttnArgs& a, const SlotMap& sm, in
     return 2;
 }
 
-// One 16-byte chunk per (slot, chunk) of the gathered tile, held in registers.
-// bf16 rows: 72 chunks of 8 dims; fp8 rows: 32 chunks of 16 codes + 8 rope chunks.
+// The gathered tile's 16-byte chunks held by one thread: thread (slot j = tid % 32, chunk group
+// cg = tid / 32 in [0, 16)).  fp8 rows: nope chunks of 16 codes cg and cg + 16, plus RoPE chunk cg
+// (8 bf16) when cg < 8; bf16 rows: nope chunks of 8 dims cg + 16u (u < 4), plus RoPE chunk cg.
 template <int FMT>
 struct Gather {
-    static constexpr int kChunks = FMT == LCA_FP8 ? 5 : 9;  // per thread
-    u32x4 v[kChunks];
-    float sc[FMT == LCA_FP8 ? 4 : 1];
+    static constexpr int kN = FMT == LCA_FP8 ? 2 : 4;  // nope chunks per thread
+    u32x4 v[kN + 1];
+    float sc[FMT == LCA_FP8 ? 2 : 1];
     int src;
 
     __device__ __forceinline__ void load(const AttnArgs& a, const SlotMap& sm, int64_t rowid, int b,
@@ -85,22 +86,21 @@ struct Gather {
         src = slot_row(a, sm, rowid, b, slot, s_end, &row);
         const lca_kv& kv = src == 2 ? a.win : a.comp;
 #pragma unroll
-        for (int u = 0; u < kChunks; ++u) v[u] = u32x4{0u, 0u, 0u, 0u};
+        for (int u = 0; u <= kN; ++u) v[u] = u32x4{0u, 0u, 0u, 0u};
         if (!src) return;
         if constexpr (FMT == LCA_FP8) {
             const u32x4* np = (const u32x4*)((const uint8_t*)kv.nope + row * kDN);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) v[u] = np[cg + 8 * u];
-            v[4] = ((const u32x4*)((const uint16_t*)kv.rope + row * kDR))[cg];
-            // chunk cg + 8u covers dims 16(cg + 8u) .. +15: scale group (cg + 8u) / 8 = u
-#pragma unroll
-            for (int u = 0; u < 4; ++u) sc[u] = kv.scale[row * 4 + u];
+            v[0] = np[cg];
+            v[1] = np[cg + 16];
+            // 16-code chunk c covers dims 16c .. 16c+15: scale group c / 8
+            sc[0] = kv.scale[row * 4 + (cg >> 3)];
+            sc[1] = kv.scale[row * 4 + 2 + (cg >> 3)];
         } else {
             const u32x4* np = (const u32x4*)((const uint16_t*)kv.nope + row * kDN);
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = np[cg + 8 * u];
-            v[8] = ((const u32x4*)((const uint16_t*)kv.rope + row * kDR))[cg];
+            for (int u = 0; u < 4; ++u) v[u] = np[cg + 16 * u];
         }
+        if (cg < 8) v[kN] = ((const u32x4*)((const uint16_t*)kv.rope + row * kDR))[cg];
     }
 };
 
@@ -129,8 +129,8 @@ template <int FMT>
 __device__ __forceinline__ void store_tile(const Gather<FMT>& g, uint16_t* Kt, int j, int cg) {
     if constexpr (FMT == LCA_FP8) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int d0 = 16 * (cg + 8 * u);
+        for (int u = 0; u < 2; ++u) {
+            const int d0 = 16 * (cg + 16 * u);
             u32x4 lo, hi;
             lo[0] = fp8x2_bf16<false>(g.v[u][0], g.sc[u]);
             lo[1] = fp8x2_bf16<true>(g.v[u][0], g.sc[u]);
@@ -144,19 +144,24 @@ __device__ __forceinline__ void store_tile(const Gather<FMT>& g, uint16_t* Kt, i
             put8(Kt, j, d0, lo);
             put8(Kt, j, d0 + 8, hi);
         }
-        put8(Kt, j, kDN + 8 * cg, g.v[4]);
     } else {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) put8(Kt, j, 8 * (cg + 8 * u), g.v[u]);
-        put8(Kt, j, kDN + 8 * cg, g.v[8]);
+        for (int u = 0; u < 4; ++u) put8(Kt, j, 8 * (cg + 16 * u), g.v[u]);
     }
+    if (cg < 8) put8(Kt, j, kDN + 8 * cg, g.v[Gather<FMT>::kN]);
 }
 
+// Eight waves: wave w owns heads [16 (w % 4), +16) and output dims [288 (w / 4), +288).
+// Q.K^T: each wave of a pair contracts its 288 dims (9 MFMA k-steps per 16-slot block); the two
+// partial score tiles are exchanged through LDS and summed in the same order by both waves, so
+// both hold identical scores and run the identical online softmax.  P.V fills the wave's half
+// of O (18 column blocks).  Per wave: Q fragments 36 VGPRs, O 72 VGPRs -> two waves per SIMD.
+constexpr int kHalf = kC / 2;  // 288
 template <int FMT>
-__global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int64_t split_len, int nsplit) {
+__global__ void __launch_bounds__(512) attn_mfma(AttnArgs a, int64_t split_len, int nsplit) {
     __shared__ __attribute__((aligned(16))) uint16_t Kt[kKT * kKS];
-    __shared__ __attribute__((aligned(16))) uint16_t Qs[64 * kKS];   // the row's queries, row-major
-    __shared__ __attribute__((aligned(16))) uint16_t Ps[4][32 * kVS];
+    __shared__ __attribute__((aligned(16))) f32x4 Sx[8][2][64];           // partial scores
+    __shared__ __attribute__((aligned(16))) uint16_t Ps[8][32 * kVS];     // P hi / lo, per wave
     __shared__ int valid[kKT];
 
     const int64_t rowid = blockIdx.x;
@@ -169,20 +174,21 @@ __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int64_t split_len, 
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int hrow = lane & 15, kgrp = lane >> 4;
-    const int h0 = 16 * wv;
+    const int hg = wv & 3, dh = wv >> 2;      // head group, dim half
+    const int h0 = 16 * hg, dbase = kHalf * dh;
 
-    // queries to LDS (heads >= H read as zero); A fragments are read from there per tile,
-    // which keeps the accumulators and the prefetched rows within the register file
+    // Q fragments of this wave: A[row = head h0 + hrow][k = dbase + 32 ks + 8 kgrp + e]
+    bf16x8 qf[9];
     {
-        const u32x4* qp = (const u32x4*)((const uint16_t*)a.q + rowid * a.H * kC);
-        for (int c = tid; c < 64 * (kC / 8); c += 256) {
-            const int h = c / (kC / 8), j = c % (kC / 8);
-            *(u32x4*)(Qs + h * kKS + 8 * j) = h < a.H ? qp[c] : u32x4{0u, 0u, 0u, 0u};
-        }
-    }
-    f32x4 o[36];
+        const bool hv = h0 + hrow < a.H;
+        const u32x4* qp = (const u32x4*)((const uint16_t*)a.q + (rowid * a.H + h0 + hrow) * kC + dbase);
 #pragma unroll
-    for (int nb = 0; nb < 36; ++nb) o[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int ks = 0; ks < 9; ++ks)
+            qf[ks] = __builtin_bit_cast(bf16x8, hv ? qp[4 * ks + kgrp] : u32x4{0u, 0u, 0u, 0u});
+    }
+    f32x4 o[18];
+#pragma unroll
+    for (int nb = 0; nb < 18; ++nb) o[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     float mrun[4], lrun[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -191,9 +197,14 @@ __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int64_t split_len, 
     }
     const float qk_scale = a.sm_scale * kLog2e;
 
-    const int gj = tid & 31, gcg = tid >> 5;  // gather role: slot gj, chunk group gcg
+    const int gj = tid & 31, gcg = tid >> 5;  // gather role: slot gj, chunk group gcg (0..15)
     Gather<FMT> g;
     if (s_begin < s_end) g.load(a, sm, rowid, b, s_begin + gj, s_end, gcg);
+
+    uint16_t* pw = Ps[wv];
+    const uint16_t* kr0 = Kt + hrow * kKS + dbase + 8 * kgrp;
+    const uint16_t* kr1 = Kt + (16 + hrow) * kKS + dbase + 8 * kgrp;
+    const uint16_t* vr = Kt + (8 * kgrp + (hrow >> 2)) * kKS + dbase + 4 * (hrow & 3);
 
     for (int64_t s0 = s_begin; s0 < s_end; s0 += kKT) {
         __syncthreads();  // previous tile fully consumed
@@ -202,21 +213,26 @@ __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int64_t split_len, 
         __syncthreads();
         if (s0 + kKT < s_end) g.load(a, sm, rowid, b, s0 + kKT + gj, s_end, gcg);
 
-        // S = Q K^T for two 16-slot blocks; A[row = head h0 + hrow][k = 32 ks + 8 kgrp + e]
+        // partial S over this wave's 288 dims, two 16-slot blocks
         f32x4 s[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
-        {
-            const uint16_t* qr = Qs + (h0 + hrow) * kKS + 8 * kgrp;
-            const uint16_t* kr0 = Kt + hrow * kKS + 8 * kgrp;
-            const uint16_t* kr1 = Kt + (16 + hrow) * kKS + 8 * kgrp;
 #pragma unroll
-            for (int ks = 0; ks < 18; ++ks) {
-                const bf16x8 qa = __builtin_bit_cast(bf16x8, *(const u32x4*)(qr + 32 * ks));
-                const bf16x8 k0 = __builtin_bit_cast(bf16x8, *(const u32x4*)(kr0 + 32 * ks));
-                const bf16x8 k1 = __builtin_bit_cast(bf16x8, *(const u32x4*)(kr1 + 32 * ks));
-                s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, k0, s[0], 0, 0, 0);
-                s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, k1, s[1], 0, 0, 0);
-            }
+        for (int ks = 0; ks < 9; ++ks) {
+            const bf16x8 k0 = __builtin_bit_cast(bf16x8, *(const u32x4*)(kr0 + 32 * ks));
+            const bf16x8 k1 = __builtin_bit_cast(bf16x8, *(const u32x4*)(kr1 + 32 * ks));
+            s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], k0, s[0], 0, 0, 0);
+            s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], k1, s[1], 0, 0, 0);
         }
+        Sx[wv][0][lane] = s[0];
+        Sx[wv][1][lane] = s[1];
+        __syncthreads();
+        {
+            const int pv = wv ^ 4;  // the partner wave (same heads, other dim half)
+            const f32x4 o0 = Sx[pv][0][lane], o1 = Sx[pv][1][lane];
+            // dim half 0 + dim half 1 in both waves (the same additions, the same results)
+            s[0] = dh == 0 ? s[0] + o0 : o0 + s[0];
+            s[1] = dh == 0 ? s[1] + o1 : o1 + s[1];
+        }
+
         // online softmax; lane holds rows (heads) 4 kgrp + r, columns (slots) hrow and 16 + hrow.
         // The reference max moves only when a row's max exceeds it by more than 2^8 (weights stay
         // <= 256), so O is rescaled on few tiles instead of every tile.
@@ -240,7 +256,7 @@ __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int64_t split_len, 
                 mrun[r] = mnew;
             }
 #pragma unroll
-            for (int nb = 0; nb < 36; ++nb)
+            for (int nb = 0; nb < 18; ++nb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) o[nb][r] *= corr[r];
         }
@@ -251,10 +267,9 @@ __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int64_t split_len, 
             p1[r] = exp2f(x1[r] - muse);
             lrun[r] += row_sum16(p0[r] + p1[r]);
         }
-        // P through LDS into A layout, A[row = head hrow][k = slot 8 kgrp + e], as two bf16
-        // terms P = hi + lo (hi = bf16(P), lo = bf16(P - hi)): both multiply the same V
+        // P through this wave's LDS buffer into A layout, A[row = head hrow][k = slot 8 kgrp + e], as
+        // two bf16 terms P = hi + lo (hi = bf16(P), lo = bf16(P - hi)): both multiply the same V
         // fragment, so P V keeps ~16 mantissa bits at no extra LDS traffic.
-        uint16_t* pw = Ps[wv];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const uint16_t h0b = f2bf(p0[r]), h1b = f2bf(p1[r]);
@@ -263,23 +278,25 @@ __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int64_t split_len, 
             pw[(16 + 4 * kgrp + r) * kVS + hrow] = f2bf(p0[r] - bf2f(h0b));
             pw[(16 + 4 * kgrp + r) * kVS + 16 + hrow] = f2bf(p1[r] - bf2f(h1b));
         }
-        __syncthreads();
+        // the buffer is this wave's own: order its LDS writes before its reads
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         const bf16x8 pa = __builtin_bit_cast(bf16x8, *(const u32x4*)(pw + hrow * kVS + 8 * kgrp));
         const bf16x8 pl = __builtin_bit_cast(bf16x8, *(const u32x4*)(pw + (16 + hrow) * kVS + 8 * kgrp));
-        // O += P V: B[k = slot 8 kgrp + e][n = dim 16 nb + hrow], two transposing reads of
-        // four slots each; this lane addresses slot 8 kgrp + hrow / 4 (+4), dims 4 (hrow % 4)
-        const uint16_t* vr = Kt + (8 * kgrp + (hrow >> 2)) * kKS + 4 * (hrow & 3);
+        // O += P V over this wave's dims: B[k = slot 8 kgrp + e][n = dim dbase + 16 nb + hrow], two
+        // transposing reads of four slots each (this lane addresses slot 8 kgrp + hrow / 4 (+4))
 #pragma unroll
-        for (int nb = 0; nb < 36; ++nb) {
-            const s16x4 v0 = lds_tr16(vr + 16 * nb);
-            const s16x4 v1 = lds_tr16(vr + 4 * kKS + 16 * nb);
-            const bf16x8 vb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+        for (int nb = 0; nb < 18; ++nb) {
+            const s16x4 w0 = lds_tr16(vr + 16 * nb);
+            const s16x4 w1 = lds_tr16(vr + 4 * kKS + 16 * nb);
+            const bf16x8 vb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7));
             o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[nb], 0, 0, 0);
             o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, o[nb], 0, 0, 0);
         }
     }
 
-    // epilogue
+    // epilogue: this wave's heads h0 + 4 kgrp + r and dims dbase + 16 nb + hrow
     const int64_t nrows = (int64_t)gridDim.x;
     if (nsplit > 1) {
         float* wo = (float*)a.ws;
@@ -289,18 +306,20 @@ __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int64_t split_len, 
             const int h = h0 + 4 * kgrp + r;
             if (h >= a.H) continue;
             const int64_t pr = ((int64_t)split * nrows + rowid) * a.H + h;
-            float* dst = wo + pr * kC + hrow;
+            float* dst = wo + pr * kC + dbase + hrow;
 #pragma unroll
-            for (int nb = 0; nb < 36; ++nb) dst[16 * nb] = o[nb][r];
-            if (hrow == 0) {
+            for (int nb = 0; nb < 18; ++nb) dst[16 * nb] = o[nb][r];
+            if (hrow == 0 && dh == 0) {
                 wml[2 * pr] = mrun[r];
                 wml[2 * pr + 1] = lrun[r];
             }
         }
         return;
     }
+    // output RoPE: dims 512 + i and 544 + i (i < 32) sit in this half's blocks 14 + q2 and 16 + q2
     float sn[2] = {0.0f, 0.0f}, cs[2] = {1.0f, 1.0f};
-    if (a.rope_theta != 0.0) {
+    const bool rot = a.rope_theta != 0.0 && dh == 1;
+    if (rot) {
 #pragma unroll
         for (int q2 = 0; q2 < 2; ++q2) rope_sincos(a.rope.inv, 16 * q2 + hrow, -(double)t, &sn[q2], &cs[q2]);
     }
@@ -316,28 +335,28 @@ __global__ void __launch_bounds__(256) attn_mfma(AttnArgs a, int64_t split_len, 
             den = (mrun[r] == -INFINITY ? 0.0f : lrun[r] * exp2f(mrun[r] - mu)) + exp2f(z - mu);
         }
         const float f = den > 0.0f && mrun[r] != -INFINITY ? exp2f(mrun[r] - mu) / den : 0.0f;
-        float ov[36];
+        float ov[18];
 #pragma unroll
-        for (int nb = 0; nb < 36; ++nb) ov[nb] = o[nb][r] * f;
-        if (a.rope_theta != 0.0) {
+        for (int nb = 0; nb < 18; ++nb) ov[nb] = o[nb][r] * f;
+        if (rot) {
 #pragma unroll
             for (int q2 = 0; q2 < 2; ++q2) {
-                const float x0 = ov[32 + q2], x1 = ov[34 + q2];
-                ov[32 + q2] = x0 * cs[q2] - x1 * sn[q2];
-                ov[34 + q2] = x0 * sn[q2] + x1 * cs[q2];
+                const float x0 = ov[14 + q2], x1 = ov[16 + q2];
+                ov[14 + q2] = x0 * cs[q2] - x1 * sn[q2];
+                ov[16 + q2] = x0 * sn[q2] + x1 * cs[q2];
             }
         }
-        const int64_t orow = (rowid * a.H + h) * kC + hrow;
+        const int64_t orow = (rowid * a.H + h) * kC + dbase + hrow;
         if (a.out_dtype == LCA_F32) {
             float* dst = (float*)a.out + orow;
 #pragma unroll
-            for (int nb = 0; nb < 36; ++nb) dst[16 * nb] = ov[nb];
+            for (int nb = 0; nb < 18; ++nb) dst[16 * nb] = ov[nb];
         } else {
             uint16_t* dst = (uint16_t*)a.out + orow;
 #pragma unroll
-            for (int nb = 0; nb < 36; ++nb) dst[16 * nb] = f2bf(ov[nb]);
+            for (int nb = 0; nb < 18; ++nb) dst[16 * nb] = f2bf(ov[nb]);
         }
-        if (a.lse && hrow == 0)
+        if (a.lse && hrow == 0 && dh == 0)
             a.lse[rowid * a.H + h] = den > 0.0f ? (mu + log2f(den)) * kLn2 : -INFINITY;
     }
 }
@@ -541,8 +560,8 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     const int ns = attn_num_splits(rows, a.max_keys, c);
     const int64_t len = ns > 1 ? split_len_of(a.max_keys, ns) : (a.max_keys + kKT - 1) / kKT * kKT;
     dim3 grid((unsigned)rows, (unsigned)ns);
-    if (a.comp.fmt == LCA_FP8) hipLaunchKernelGGL((attn_mfma<LCA_FP8>), grid, dim3(256), 0, st, a, len, ns);
-    else hipLaunchKernelGGL((attn_mfma<LCA_BF16>), grid, dim3(256), 0, st, a, len, ns);
+    if (a.comp.fmt == LCA_FP8) hipLaunchKernelGGL((attn_mfma<LCA_FP8>), grid, dim3(512), 0, st, a, len, ns);
+    else hipLaunchKernelGGL((attn_mfma<LCA_BF16>), grid, dim3(512), 0, st, a, len, ns);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns <= 1) return e;
     hipLaunchKernelGGL(attn_combine, dim3((unsigned)rows, (unsigned)a.H, (unsigned)((c + kCombDims - 1) / kCombDims)),
