@@ -26,12 +26,15 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-I", os.path.join(ROOT, "include")]
+# Per-source additions.  attn.hip: its softmax never sees a NaN, and without the NaN guarantee
+# every fmaxf of a value moved across lanes gets an extra canonicalising max.
+EXTRA = {"attn.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(OBJ, src + ".o")
     lang = ["-x", "hip"]
-    cmd = ["hipcc", *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = ["hipcc", *FLAGS, *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -7,23 +7,25 @@
 // applied to the output by -t.
 //
 // bf16 / fp8 caches, c = 512 + 64, H a multiple of 16 (up to 64): MFMA path.
-//   One workgroup (4 waves) per (query row, key split).  The attended rows are
+//   One workgroup (8 waves) per (query row, key split).  The attended rows are
 //   a list of "slots": compressed slots (idx entries, or 0..vis-1) followed by
 //   window slots.  Per tile of 32 slots the workgroup gathers the rows from HBM
 //   (fp8 codes are expanded to bf16 exactly: the scale is a power of two) into
-//   one row-major LDS tile.  It serves both operands: the K operand of Q.K^T
-//   (16 contiguous bytes of one key per lane, ds_read_b128) and the V operand
-//   of P.V (8 consecutive keys of one dim per lane) through gfx950's
+//   one row-major LDS tile (three tiles rotate, see the pipeline below).  The
+//   tile serves both operands: the K operand of the score product (16
+//   contiguous bytes of one key per lane, ds_read_b128) and the V operand of
+//   the value product (four keys of one dim per lane) through gfx950's
 //   transposing LDS read ds_read_b64_tr_b16: within each 16-lane group, lane i
 //   receives element i mod 4 of the 8-byte rows addressed by lanes i/4 + 4e,
-//   so lanes addressing (key r/4, dims 4(r mod 4)..+3) hand lane i four
-//   consecutive keys of dim i.  The next tile's rows are fetched into
-//   registers while the current tile is computed.  Wave w owns heads [16w, 16w+16): S = Q K^T with
-//   v_mfma_f32_16x16x32_bf16 (M = heads, N = keys, K = 576 in 18 steps, Q kept
-//   in registers), online softmax in the accumulator layout (row max / sum over
-//   16 lanes), P goes through a small per-wave LDS buffer into A-operand
-//   layout as a bf16 hi + lo pair, O += P V (N = 576 dims in 36 blocks, O
-//   kept in registers).
+//   so lanes addressing (key r/4, dims 4(r mod 4)..+3) hand lane i four keys of
+//   dim i.
+//   Wave w owns heads [16 (w % 4), +16) and dims [288 (w / 4), +288).  Scores
+//   are computed transposed, S^T = K Q^T (v_mfma_f32_16x16x32_bf16, rows =
+//   slots, columns = heads, Q^T fragments in registers), so each lane holds one
+//   head: the softmax row statistics are per-lane values, and the bf16 weights
+//   (as a hi + lo pair) go from the accumulator registers straight into the
+//   B operand of O^T += V^T P^T.  The two waves of a head group exchange their
+//   288-dim partial scores through LDS and add them in the same order.
 //   Decode-sized launches split the slot list across workgroups; a second
 //   kernel merges the partial (O, max, sum) triples in a fixed order.
 // f32 caches: one wave per (query row, head), f32 FMA, for fp32 workloads.
@@ -34,14 +36,13 @@ namespace lca {
 
 constexpr int kDN = 512, kDR = 64, kC = 576;
 constexpr int kKT = 32;             // slots per tile
-constexpr int kKS = kC + 8;         // row stride of the row-major tile (bf16 elements)
-constexpr int kVS = kKT + 8;        // row stride of the per-wave P tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 struct SlotMap {
-    int64_t ncs;    // compressed slots
-    int64_t w_lo;   // first window position
+    int64_t ncs;     // compressed slots
+    int64_t w_lo;    // first window position
+    int64_t w_row;   // its ring row, w_lo mod win.cap
     int64_t nslots;
 };
 
@@ -51,11 +52,13 @@ __device__ __forceinline__ SlotMap slot_map(const AttnArgs& a, int64_t t) {
     s.ncs = a.idx ? (int64_t)a.k : vis;
     s.w_lo = t - a.n_win + 1 < 0 ? 0 : t - a.n_win + 1;
     const int64_t nw = a.n_win > 0 ? t - s.w_lo + 1 : 0;
+    s.w_row = nw > 0 ? s.w_lo % a.win.cap : 0;
     s.nslots = s.ncs + nw;
     return s;
 }
 
-// source row of a slot: 0 = invalid, 1 = compressed row, 2 = window row
+// source row of a slot: 0 = invalid, 1 = compressed row, 2 = window row.  Window slots are
+// consecutive positions, fewer than win.cap of them, so their ring rows wrap at most once.
 __device__ __forceinline__ int slot_row(const AttnArgs& a, const SlotMap& sm, int64_t rowid, int b,
                                         int64_t slot, int64_t s_end, int64_t* row) {
     if (slot >= s_end) return 0;
@@ -65,47 +68,165 @@ __device__ __forceinline__ int slot_row(const AttnArgs& a, const SlotMap& sm, in
         *row = (int64_t)b * a.comp.cap + e;
         return 1;
     }
-    const int64_t p = sm.w_lo + (slot - sm.ncs);
-    *row = (int64_t)b * a.win.cap + p % a.win.cap;
+    int64_t r = sm.w_row + (slot - sm.ncs);
+    if (r >= a.win.cap) r -= a.win.cap;
+    *row = (int64_t)b * a.win.cap + r;
     return 2;
 }
 
-// The gathered tile's 16-byte chunks held by one thread: thread (slot j = tid % 32, chunk group
-// cg = tid / 32 in [0, 16)).  fp8 rows: nope chunks of 16 codes cg and cg + 16, plus RoPE chunk cg
-// (8 bf16) when cg < 8; bf16 rows: nope chunks of 8 dims cg + 16u (u < 4), plus RoPE chunk cg.
-template <int FMT>
-struct Gather {
-    static constexpr int kN = FMT == LCA_FP8 ? 2 : 4;  // nope chunks per thread
-    u32x4 v[kN + 1];
-    float sc[FMT == LCA_FP8 ? 2 : 1];
-    int src;
+// Kernel-argument pointers pinned in scalar registers.  A per-lane choice between two of them
+// must be a choice between register values: written as a choice between struct fields, the
+// compiler turns it into a per-lane load of the chosen field from the argument segment, which
+// puts a dependent memory round trip in front of every gathered row.
+// (global address space kept explicit: through the integer round trip it would be lost and
+// the loads would become flat loads)
+#define GMEM __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ const GMEM T* sptr(const void* p) {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const GMEM T*)(((uint64_t)hi << 32) | lo);
+}
+struct KvPtrs {  // rows of one sequence: [0] compressed rows, [1] window rows
+    const GMEM uint8_t* nope[2];
+    const GMEM uint16_t* rope[2];
+    const GMEM float* scale[2];
+};
 
-    __device__ __forceinline__ void load(const AttnArgs& a, const SlotMap& sm, int64_t rowid, int b,
-                                         int64_t slot, int64_t s_end, int cg) {
-        int64_t row = 0;
-        src = slot_row(a, sm, rowid, b, slot, s_end, &row);
-        const lca_kv& kv = src == 2 ? a.win : a.comp;
-#pragma unroll
-        for (int u = 0; u <= kN; ++u) v[u] = u32x4{0u, 0u, 0u, 0u};
-        if (!src) return;
-        if constexpr (FMT == LCA_FP8) {
-            const u32x4* np = (const u32x4*)((const uint8_t*)kv.nope + row * kDN);
-            v[0] = np[cg];
-            v[1] = np[cg + 16];
-            // 16-code chunk c covers dims 16c .. 16c+15: scale group c / 8
-            sc[0] = kv.scale[row * 4 + (cg >> 3)];
-            sc[1] = kv.scale[row * 4 + 2 + (cg >> 3)];
+// The gather: half-wave h = tid / 32 (16 of them) moves tile rows h and h + 16, one whole row
+// per load instruction (fp8 rows: 32 lanes x 16 codes; bf16 rows: 32 lanes x 8 dims, twice),
+// RoPE chunk c (8 bf16) by lane c < 8.  An invalid slot loads nothing; its tile row is zeros.
+// DENSE (HCA): compressed slot s is entry s.  Otherwise (CSA) the entry ids come from idx and are
+// fetched one tile ahead of the rows (fetch_idx), so the row loads never wait on them.
+template <int FMT, bool DENSE>
+struct Gather {
+    static constexpr int kN = FMT == LCA_FP8 ? 1 : 2;              // nope chunks per row and thread
+    static constexpr uint32_t kRow = FMT == LCA_FP8 ? kDN : 2 * kDN;  // nope bytes per row
+    u32x4 v[2][kN + 1];
+    float sc[2];
+    int src[2];
+    int32_t ent[2];  // entry ids of the next tile's rows (CSA)
+    // byte offsets of row h, chunk c from a tile's first row (row h + 16 adds 16 rows)
+    uint32_t on, os, orp;
+    int h, c;
+
+    __device__ __forceinline__ void init(int h_, int c_) {
+        h = h_;
+        c = c_;
+        on = h * kRow + 16u * c;
+        os = h * 16u + 4u * (c >> 3);  // 16-code chunk c covers dims 16c .. 16c+15: scale group c / 8
+        orp = h * 128u + 16u * c;
+    }
+
+    __device__ __forceinline__ void fetch_idx(const SlotMap& sm, const GMEM int32_t* irow, int64_t s0, int64_t s_end) {
+        const int64_t lim = min(sm.ncs, s_end);
+        const GMEM int32_t* ip = irow + s0 + h;  // this lane's slots of the tile
+        if (s0 + kKT <= lim) {                   // wave-uniform
+            ent[0] = ip[0];
+            ent[1] = ip[16];
         } else {
-            const u32x4* np = (const u32x4*)((const uint16_t*)kv.nope + row * kDN);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) v[u] = np[cg + 16 * u];
+            for (int u = 0; u < 2; ++u) ent[u] = s0 + h + 16 * u < lim ? ip[16 * u] : -1;
         }
-        if (cg < 8) v[kN] = ((const u32x4*)((const uint16_t*)kv.rope + row * kDR))[cg];
+    }
+
+    // Common case, decided per tile (wave-uniform): every slot of the tile is a compressed slot.
+    // Rows are addressed from a per-tile scalar base (dense) or from 32-bit row offsets (CSA;
+    // off32: the sequence's rows span less than 4 GiB).
+    __device__ __forceinline__ void load_comp(const AttnArgs& a, const KvPtrs& P, int64_t s0) {
+        if constexpr (DENSE) {
+            const GMEM uint8_t* bn = P.nope[0] + s0 * kRow;
+            const GMEM uint8_t* bs = (const GMEM uint8_t*)P.scale[0] + s0 * 16;
+            const GMEM uint8_t* br = (const GMEM uint8_t*)P.rope[0] + s0 * 128;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                src[u] = 1;
+                v[u][0] = *(const GMEM u32x4*)(bn + (on + 16u * kRow * u));
+                if constexpr (FMT == LCA_FP8) sc[u] = *(const GMEM float*)(bs + (os + 256u * u));
+                else v[u][1] = *(const GMEM u32x4*)(bn + (on + 16u * kRow * u + 512u));
+                if (c < 8) v[u][kN] = *(const GMEM u32x4*)(br + (orp + 2048u * u));
+            }
+        } else {
+            bool ok[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) ok[u] = ent[u] >= 0 && ent[u] < a.comp.cap;
+            const bool all = !__builtin_amdgcn_ballot_w64(!(ok[0] && ok[1]));  // wave-uniform
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                src[u] = ok[u];
+                if (!all) {
+#pragma unroll
+                    for (int q = 0; q <= kN; ++q) v[u][q] = u32x4{0u, 0u, 0u, 0u};
+                    sc[u] = 0.0f;
+                    if (!ok[u]) continue;
+                }
+                const uint32_t eu = (uint32_t)ent[u];
+                v[u][0] = *(const GMEM u32x4*)(P.nope[0] + (eu * kRow + 16u * c));
+                if constexpr (FMT == LCA_FP8) sc[u] = *(const GMEM float*)((const GMEM uint8_t*)P.scale[0] + (eu * 16u + 4u * (c >> 3)));
+                else v[u][1] = *(const GMEM u32x4*)(P.nope[0] + (eu * kRow + 16u * c + 512u));
+                if (c < 8) v[u][kN] = *(const GMEM u32x4*)((const GMEM uint8_t*)P.rope[0] + (eu * 128u + 16u * c));
+            }
+        }
+    }
+
+    // General case: window slots, slots past the end, or rows beyond 32-bit offsets.
+    __device__ __forceinline__ void load(const AttnArgs& a, const SlotMap& sm, const KvPtrs& P, bool off32,
+                                         int64_t s0, int64_t s_end) {
+        if (off32 && s0 + kKT <= min(sm.ncs, s_end)) {  // wave-uniform
+            load_comp(a, P, s0);
+            return;
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int64_t slot = s0 + h + 16 * u;
+            // source row: compressed slot (entry id, or the slot itself when dense) or window slot;
+            // window slots are consecutive positions, fewer than win.cap, wrapping at most once
+            int64_t row = 0;
+            int sr = 0;
+            if (slot < s_end) {
+                if (slot < sm.ncs) {
+                    const int64_t e = DENSE ? slot : (int64_t)ent[u];
+                    if (e >= 0 && e < a.comp.cap) {
+                        row = e;
+                        sr = 1;
+                    }
+                } else {
+                    int64_t r = sm.w_row + (slot - sm.ncs);
+                    if (r >= a.win.cap) r -= a.win.cap;
+                    row = r;
+                    sr = 2;
+                }
+            }
+            src[u] = sr;
+            const int w = sr == 2;
+            const GMEM uint8_t* nope = w ? P.nope[1] : P.nope[0];
+            const GMEM uint16_t* rope = w ? P.rope[1] : P.rope[0];
+#pragma unroll
+            for (int q = 0; q <= kN; ++q) v[u][q] = u32x4{0u, 0u, 0u, 0u};
+            sc[u] = 0.0f;
+            if (!sr) continue;
+            if constexpr (FMT == LCA_FP8) {
+                const GMEM float* scale = w ? P.scale[1] : P.scale[0];
+                v[u][0] = ((const GMEM u32x4*)(nope + row * kDN))[c];
+                sc[u] = scale[row * 4 + (c >> 3)];
+            } else {
+                const GMEM u32x4* np = (const GMEM u32x4*)(nope + row * kDN * 2);
+                v[u][0] = np[c];
+                v[u][1] = np[c + 32];
+            }
+            if (c < 8) v[u][kN] = ((const GMEM u32x4*)(rope + row * kDR))[c];
+        }
     }
 };
 
-__device__ __forceinline__ void put8(uint16_t* Kt, int j, int d0, u32x4 v) {
-    *(u32x4*)(Kt + j * kKS + d0) = v;
+// Tile layout: row r (slot) at r * kKS, dims contiguous.  The 16-element pad (row stride
+// 1184 bytes) keeps both reads near the conflict-free LDS rate on gfx950: the 16 rows of one
+// ds_read_b128 phase and the four 32-byte row pieces of one transposing read fall on
+// different banks (measured against other strides and XOR swizzles).
+constexpr int kKS = kC + 16;
+
+__device__ __forceinline__ void put8(uint16_t* Kt, int j, int chunk, u32x4 v) {
+    *(u32x4*)(Kt + j * kKS + 8 * chunk) = v;
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -125,44 +246,71 @@ __device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t codes, float sc) {
     return __builtin_amdgcn_perm(hi, lo, 0x07060302u);
 }
 
-template <int FMT>
-__device__ __forceinline__ void store_tile(const Gather<FMT>& g, uint16_t* Kt, int j, int cg) {
-    if constexpr (FMT == LCA_FP8) {
+// Expand and store one tile; flags[r] = slot r valid (read back as 32-bit words of 4 slots).
+template <int FMT, bool DENSE>
+__device__ __forceinline__ void store_tile(const Gather<FMT, DENSE>& g, uint16_t* Kt, uint8_t* flags) {
+    const int h = g.h, c = g.c;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int d0 = 16 * (cg + 16 * u);
+    for (int u = 0; u < 2; ++u) {
+        const int r = h + 16 * u;
+        if constexpr (FMT == LCA_FP8) {
             u32x4 lo, hi;
-            lo[0] = fp8x2_bf16<false>(g.v[u][0], g.sc[u]);
-            lo[1] = fp8x2_bf16<true>(g.v[u][0], g.sc[u]);
-            lo[2] = fp8x2_bf16<false>(g.v[u][1], g.sc[u]);
-            lo[3] = fp8x2_bf16<true>(g.v[u][1], g.sc[u]);
-            hi[0] = fp8x2_bf16<false>(g.v[u][2], g.sc[u]);
-            hi[1] = fp8x2_bf16<true>(g.v[u][2], g.sc[u]);
-            hi[2] = fp8x2_bf16<false>(g.v[u][3], g.sc[u]);
-            hi[3] = fp8x2_bf16<true>(g.v[u][3], g.sc[u]);
-            if (!g.src) lo = hi = u32x4{0u, 0u, 0u, 0u};
-            put8(Kt, j, d0, lo);
-            put8(Kt, j, d0 + 8, hi);
+            lo[0] = fp8x2_bf16<false>(g.v[u][0][0], g.sc[u]);
+            lo[1] = fp8x2_bf16<true>(g.v[u][0][0], g.sc[u]);
+            lo[2] = fp8x2_bf16<false>(g.v[u][0][1], g.sc[u]);
+            lo[3] = fp8x2_bf16<true>(g.v[u][0][1], g.sc[u]);
+            hi[0] = fp8x2_bf16<false>(g.v[u][0][2], g.sc[u]);
+            hi[1] = fp8x2_bf16<true>(g.v[u][0][2], g.sc[u]);
+            hi[2] = fp8x2_bf16<false>(g.v[u][0][3], g.sc[u]);
+            hi[3] = fp8x2_bf16<true>(g.v[u][0][3], g.sc[u]);
+            put8(Kt, r, 2 * c, lo);
+            put8(Kt, r, 2 * c + 1, hi);
+        } else {
+            put8(Kt, r, c, g.v[u][0]);
+            put8(Kt, r, c + 32, g.v[u][1]);
         }
-    } else {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) put8(Kt, j, 8 * (cg + 16 * u), g.v[u]);
+        if (c < 8) put8(Kt, r, kDN / 8 + c, g.v[u][Gather<FMT, DENSE>::kN]);
+        if (c == 0) flags[r] = g.src[u] != 0;
     }
-    if (cg < 8) put8(Kt, j, kDN + 8 * cg, g.v[Gather<FMT>::kN]);
+}
+
+__device__ __forceinline__ float xlane32(float v, bool mx) {  // combine with lane ^ 32
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const float a = __uint_as_float(p[0]), b = __uint_as_float(p[1]);
+    return mx ? fmaxf(a, b) : a + b;
+}
+__device__ __forceinline__ float xlane16(float v, bool mx) {  // combine with lane ^ 16
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const float a = __uint_as_float(p[0]), b = __uint_as_float(p[1]);
+    return mx ? fmaxf(a, b) : a + b;
+}
+// over the four 16-lane groups: every lane gets the same value, summed in the same order
+__device__ __forceinline__ float max4g(float v) { return xlane32(xlane16(v, true), true); }
+__device__ __forceinline__ float sum4g(float v) { return xlane32(xlane16(v, false), false); }
+
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 v = {(__bf16)lo, (__bf16)hi};  // nearest-even (v_cvt_pk_bf16_f32)
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // Eight waves: wave w owns heads [16 (w % 4), +16) and output dims [288 (w / 4), +288).
-// Q.K^T: each wave of a pair contracts its 288 dims (9 MFMA k-steps per 16-slot block); the two
-// partial score tiles are exchanged through LDS and summed in the same order by both waves, so
-// both hold identical scores and run the identical online softmax.  P.V fills the wave's half
-// of O (18 column blocks).  Per wave: Q fragments 36 VGPRs, O 72 VGPRs -> two waves per SIMD.
+// Per wave: Q^T fragments 36 VGPRs, O^T 72 VGPRs -> two waves per SIMD.
+//
+// The tile loop is software-pipelined over three LDS tiles so that every phase has both matrix
+// and vector work:
+//   phase 1 (tile t):  S^T partial = K Q^T over the wave's dims  |  expand + store tile t+1,
+//                      fetch tile t+2 into registers
+//   phase 2:           O^T += V^T P^T of tile t-1               |  exchange + softmax of tile t
+// The running max can move in phase 2 of tile t; O is rescaled at the end of that phase, after
+// tile t-1's product has been added and before tile t's is.
 constexpr int kHalf = kC / 2;  // 288
-template <int FMT>
+constexpr int kTileElems = kKT * kKS;
+template <int FMT, bool DENSE>
 __global__ void __launch_bounds__(512) attn_mfma(AttnArgs a, int64_t split_len, int nsplit) {
-    __shared__ __attribute__((aligned(16))) uint16_t Kt[kKT * kKS];
-    __shared__ __attribute__((aligned(16))) f32x4 Sx[8][2][64];           // partial scores
-    __shared__ __attribute__((aligned(16))) uint16_t Ps[8][32 * kVS];     // P hi / lo, per wave
-    __shared__ int valid[kKT];
+    __shared__ __attribute__((aligned(16))) uint16_t Kt[3][kTileElems];
+    __shared__ __attribute__((aligned(16))) f32x4 Sx[8][2][64];  // partial scores
+    __shared__ uint32_t vflag[3][kKT / 4];                         // slot valid flags, per tile
 
     const int64_t rowid = blockIdx.x;
     const int split = blockIdx.y;
@@ -171,194 +319,223 @@ __global__ void __launch_bounds__(512) attn_mfma(AttnArgs a, int64_t split_len, 
     const SlotMap sm = slot_map(a, t);
     const int64_t s_begin = (int64_t)split * split_len;
     const int64_t s_end = min(sm.nslots, s_begin + split_len);
+    const int ntile = s_end > s_begin ? (int)((s_end - s_begin + kKT - 1) / kKT) : 0;
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int hrow = lane & 15, kgrp = lane >> 4;
+    const int n = lane & 15, g4 = lane >> 4;  // MFMA lane coordinates
     const int hg = wv & 3, dh = wv >> 2;      // head group, dim half
     const int h0 = 16 * hg, dbase = kHalf * dh;
+    const bool active = h0 < a.H;             // wave-uniform
 
-    // Q fragments of this wave: A[row = head h0 + hrow][k = dbase + 32 ks + 8 kgrp + e]
+    // Q^T fragments: B[k = dim dbase + 32 ks + 8 g4 + e][n = head h0 + n]
     bf16x8 qf[9];
     {
-        const bool hv = h0 + hrow < a.H;
-        const u32x4* qp = (const u32x4*)((const uint16_t*)a.q + (rowid * a.H + h0 + hrow) * kC + dbase);
+        const u32x4* qp = (const u32x4*)((const uint16_t*)a.q + (rowid * a.H + h0 + n) * kC + dbase);
 #pragma unroll
         for (int ks = 0; ks < 9; ++ks)
-            qf[ks] = __builtin_bit_cast(bf16x8, hv ? qp[4 * ks + kgrp] : u32x4{0u, 0u, 0u, 0u});
+            qf[ks] = __builtin_bit_cast(bf16x8, active ? qp[4 * ks + g4] : u32x4{0u, 0u, 0u, 0u});
     }
+    // O^T: lane holds dims dbase + 16 nb + 4 g4 + i (i < 4) of head h0 + n
     f32x4 o[18];
 #pragma unroll
     for (int nb = 0; nb < 18; ++nb) o[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    float mrun[4], lrun[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        mrun[r] = -INFINITY;
-        lrun[r] = 0.0f;
-    }
+    float mrun = -INFINITY;  // running max (log2 domain) of head h0 + n
+    float lpart = 0.0f;      // this lane's share of the running sum
     const float qk_scale = a.sm_scale * kLog2e;
 
-    const int gj = tid & 31, gcg = tid >> 5;  // gather role: slot gj, chunk group gcg (0..15)
-    Gather<FMT> g;
-    if (s_begin < s_end) g.load(a, sm, rowid, b, s_begin + gj, s_end, gcg);
+    // K operand: rows n and 16 + n, dims dbase + 32 ks + 8 g4
+    const int koff = n * kKS + dbase + 8 * g4;
+    // V operand: rows 4 g4 + n / 4 and 16 + that (slots 4 g4 + e, 16 + 4 g4 + e), dims
+    // dbase + 16 nb + 4 (n & 3)
+    const int voff = (4 * g4 + (n >> 2)) * kKS + dbase + 4 * (n & 3);
 
-    uint16_t* pw = Ps[wv];
-    const uint16_t* kr0 = Kt + hrow * kKS + dbase + 8 * kgrp;
-    const uint16_t* kr1 = Kt + (16 + hrow) * kKS + dbase + 8 * kgrp;
-    const uint16_t* vr = Kt + (8 * kgrp + (hrow >> 2)) * kKS + dbase + 4 * (hrow & 3);
+    constexpr int64_t kRowBytes = FMT == LCA_FP8 ? kDN : 2 * kDN;
+    KvPtrs P;  // this sequence's rows
+    P.nope[0] = sptr<uint8_t>(a.comp.nope) + (int64_t)b * a.comp.cap * kRowBytes;
+    P.nope[1] = sptr<uint8_t>(a.win.nope) + (int64_t)b * a.win.cap * kRowBytes;
+    P.rope[0] = sptr<uint16_t>(a.comp.rope) + (int64_t)b * a.comp.cap * kDR;
+    P.rope[1] = sptr<uint16_t>(a.win.rope) + (int64_t)b * a.win.cap * kDR;
+    P.scale[0] = FMT == LCA_FP8 ? sptr<float>(a.comp.scale) + (int64_t)b * a.comp.cap * 4 : nullptr;
+    P.scale[1] = FMT == LCA_FP8 ? sptr<float>(a.win.scale) + (int64_t)b * a.win.cap * 4 : nullptr;
+    const GMEM int32_t* irow = DENSE ? nullptr : sptr<int32_t>(a.idx) + rowid * a.k;  // this row's entry ids
+    const bool off32 = a.comp.cap * kRowBytes < (int64_t)1 << 32;
+    Gather<FMT, DENSE> g;
+    g.init(tid >> 5, tid & 31);
+    if (ntile > 0) {
+        if constexpr (!DENSE) g.fetch_idx(sm, irow, s_begin, s_end);
+        g.load(a, sm, P, off32, s_begin, s_end);
+        if constexpr (!DENSE) g.fetch_idx(sm, irow, s_begin + kKT, s_end);
+        store_tile(g, Kt[0], (uint8_t*)vflag[0]);
+        if (ntile > 1) {
+            g.load(a, sm, P, off32, s_begin + kKT, s_end);
+            if constexpr (!DENSE) g.fetch_idx(sm, irow, s_begin + 2 * kKT, s_end);
+        }
+    }
+    // The Q loads were issued before tile 0's, which store_tile has waited for.  Consume them
+    // here, on every path into the loop, so that the waits inside the loop cover only the gather
+    // loads in flight (otherwise the first Q use in the loop waits for every load).
+#pragma unroll
+    for (int ks = 0; ks < 9; ++ks) asm volatile("" ::"v"(qf[ks]));
 
-    for (int64_t s0 = s_begin; s0 < s_end; s0 += kKT) {
-        __syncthreads();  // previous tile fully consumed
-        store_tile<FMT>(g, Kt, gj, gcg);
-        if (gcg == 0) valid[gj] = g.src != 0;
-        __syncthreads();
-        if (s0 + kKT < s_end) g.load(a, sm, rowid, b, s0 + kKT + gj, s_end, gcg);
-
-        // partial S over this wave's 288 dims, two 16-slot blocks
-        f32x4 s[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
-#pragma unroll
-        for (int ks = 0; ks < 9; ++ks) {
-            const bf16x8 k0 = __builtin_bit_cast(bf16x8, *(const u32x4*)(kr0 + 32 * ks));
-            const bf16x8 k1 = __builtin_bit_cast(bf16x8, *(const u32x4*)(kr1 + 32 * ks));
-            s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], k0, s[0], 0, 0, 0);
-            s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], k1, s[1], 0, 0, 0);
-        }
-        Sx[wv][0][lane] = s[0];
-        Sx[wv][1][lane] = s[1];
-        __syncthreads();
-        {
-            const int pv = wv ^ 4;  // the partner wave (same heads, other dim half)
-            const f32x4 o0 = Sx[pv][0][lane], o1 = Sx[pv][1][lane];
-            // dim half 0 + dim half 1 in both waves (the same additions, the same results)
-            s[0] = dh == 0 ? s[0] + o0 : o0 + s[0];
-            s[1] = dh == 0 ? s[1] + o1 : o1 + s[1];
-        }
-
-        // online softmax; lane holds rows (heads) 4 kgrp + r, columns (slots) hrow and 16 + hrow.
-        // The reference max moves only when a row's max exceeds it by more than 2^8 (weights stay
-        // <= 256), so O is rescaled on few tiles instead of every tile.
-        const bool v0 = valid[hrow], v1 = valid[16 + hrow];
-        float p0[4], p1[4], x0[4], x1[4], mx[4];
-        bool grow = false;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            x0[r] = v0 ? s[0][r] * qk_scale : -INFINITY;
-            x1[r] = v1 ? s[1][r] * qk_scale : -INFINITY;
-            mx[r] = row_max16(fmaxf(x0[r], x1[r]));
-            grow |= mx[r] > mrun[r] + 8.0f;
-        }
-        if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform
-            float corr[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float mnew = fmaxf(mrun[r], mx[r]);
-                corr[r] = mnew == -INFINITY ? 1.0f : exp2f(mrun[r] - mnew);
-                lrun[r] *= corr[r];
-                mrun[r] = mnew;
-            }
-#pragma unroll
-            for (int nb = 0; nb < 18; ++nb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) o[nb][r] *= corr[r];
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float muse = mrun[r] == -INFINITY ? 0.0f : mrun[r];
-            p0[r] = exp2f(x0[r] - muse);
-            p1[r] = exp2f(x1[r] - muse);
-            lrun[r] += row_sum16(p0[r] + p1[r]);
-        }
-        // P through this wave's LDS buffer into A layout, A[row = head hrow][k = slot 8 kgrp + e], as
-        // two bf16 terms P = hi + lo (hi = bf16(P), lo = bf16(P - hi)): both multiply the same V
-        // fragment, so P V keeps ~16 mantissa bits at no extra LDS traffic.
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const uint16_t h0b = f2bf(p0[r]), h1b = f2bf(p1[r]);
-            pw[(4 * kgrp + r) * kVS + hrow] = h0b;
-            pw[(4 * kgrp + r) * kVS + 16 + hrow] = h1b;
-            pw[(16 + 4 * kgrp + r) * kVS + hrow] = f2bf(p0[r] - bf2f(h0b));
-            pw[(16 + 4 * kgrp + r) * kVS + 16 + hrow] = f2bf(p1[r] - bf2f(h1b));
-        }
-        // the buffer is this wave's own: order its LDS writes before its reads
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const bf16x8 pa = __builtin_bit_cast(bf16x8, *(const u32x4*)(pw + hrow * kVS + 8 * kgrp));
-        const bf16x8 pl = __builtin_bit_cast(bf16x8, *(const u32x4*)(pw + (16 + hrow) * kVS + 8 * kgrp));
-        // O += P V over this wave's dims: B[k = slot 8 kgrp + e][n = dim dbase + 16 nb + hrow], two
-        // transposing reads of four slots each (this lane addresses slot 8 kgrp + hrow / 4 (+4))
+    // O^T += V^T P^T over one tile: A[row = dim dbase + 16 nb + n][k = slot pi(8 g4 + e)], two
+    // transposing reads (slots 4 g4 + e and 16 + 4 g4 + e); P as bf16 hi + lo
+    auto pv = [&](const uint16_t* K, const bf16x8& pa, const bf16x8& pb) {
+        const uint16_t* vr = K + voff;
 #pragma unroll
         for (int nb = 0; nb < 18; ++nb) {
             const s16x4 w0 = lds_tr16(vr + 16 * nb);
-            const s16x4 w1 = lds_tr16(vr + 4 * kKS + 16 * nb);
-            const bf16x8 vb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7));
-            o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[nb], 0, 0, 0);
-            o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, o[nb], 0, 0, 0);
+            const s16x4 w1 = lds_tr16(vr + 16 * kKS + 16 * nb);
+            const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7));
+            o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pa, o[nb], 0, 0, 0);
+            o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[nb], 0, 0, 0);
+        }
+    };
+
+    bf16x8 pa = {}, pb = {};  // P^T of the previous tile (B operand, hi / lo)
+    for (int it = 0; it < ntile; ++it) {
+        __syncthreads();  // tile it stored; tile it - 2 (this phase's store target) consumed
+        // ---- phase 1 ----
+        const uint16_t* K = Kt[it % 3];
+        f32x4 s[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+        if (active) {
+            const uint16_t* kr = K + koff;
+#pragma unroll
+            for (int ks = 0; ks < 9; ++ks) {
+                const bf16x8 k0 = __builtin_bit_cast(bf16x8, *(const u32x4*)(kr + 32 * ks));
+                const bf16x8 k1 = __builtin_bit_cast(bf16x8, *(const u32x4*)(kr + 16 * kKS + 32 * ks));
+                s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[ks], s[0], 0, 0, 0);
+                s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[ks], s[1], 0, 0, 0);
+            }
+        }
+        if (it + 1 < ntile) {
+            store_tile(g, Kt[(it + 1) % 3], (uint8_t*)vflag[(it + 1) % 3]);
+            if (it + 2 < ntile) {
+                g.load(a, sm, P, off32, s_begin + (int64_t)(it + 2) * kKT, s_end);
+                if constexpr (!DENSE) g.fetch_idx(sm, irow, s_begin + (int64_t)(it + 3) * kKT, s_end);
+            }
+        }
+        if (active) {
+            // invalid slots (zero rows) get -inf in both partial sums; lane holds slots
+            // 16 kb + 4 g4 + i of head h0 + n
+            const uint32_t f0 = vflag[it % 3][g4], f1 = vflag[it % 3][4 + g4];
+            if (__builtin_amdgcn_ballot_w64((f0 & f1) != 0x01010101u)) {  // wave-uniform
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (!((f0 >> (8 * i)) & 1u)) s[0][i] = -INFINITY;
+                    if (!((f1 >> (8 * i)) & 1u)) s[1][i] = -INFINITY;
+                }
+            }
+            Sx[wv][0][lane] = s[0];
+            Sx[wv][1][lane] = s[1];
+        }
+        __syncthreads();
+        // ---- phase 2 ----
+        if (active) {
+            if (it > 0) pv(Kt[(it + 2) % 3], pa, pb);  // tile it - 1
+            {
+                const int pw = wv ^ 4;  // the partner wave (same heads, other dim half)
+                const f32x4 o0 = Sx[pw][0][lane], o1 = Sx[pw][1][lane];
+                // dim half 0 + dim half 1 in both waves (the same additions, the same results)
+                s[0] = dh == 0 ? s[0] + o0 : o0 + s[0];
+                s[1] = dh == 0 ? s[1] + o1 : o1 + s[1];
+            }
+            const float smax = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+            const float tmax = max4g(smax) * qk_scale;
+            // The reference max moves only when the tile max exceeds it by more than 2^8 (weights
+            // stay <= 256), so O is rescaled on few tiles instead of every tile.
+            const bool grow = __builtin_amdgcn_ballot_w64(tmax > mrun + 8.0f) != 0;  // wave-uniform
+            const float mnew = grow ? fmaxf(mrun, tmax) : mrun;
+            const float corr = mnew == mrun ? 1.0f : exp2f(mrun - mnew);  // mrun = -inf -> 0
+            mrun = mnew;
+            const float mneg = mrun == -INFINITY ? 0.0f : -mrun;
+            float p[2][4];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) p[kb][i] = __builtin_amdgcn_exp2f(fmaf(s[kb][i], qk_scale, mneg));
+            lpart = lpart * corr +
+                    (((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) + ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3])));
+            // B operand P^T as hi + lo = bf16(P) + bf16(P - hi): k-slot 8 g4 + e is slot 4 g4 + e
+            // (e < 4) or 16 + 4 g4 + e - 4
+            uint32_t ph[4], pl[4];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const float x0 = p[kb][2 * q], x1 = p[kb][2 * q + 1];
+                    const uint32_t hb = pk_bf16(x0, x1);
+                    ph[2 * kb + q] = hb;
+                    pl[2 * kb + q] = pk_bf16(x0 - __uint_as_float(hb << 16), x1 - __uint_as_float(hb & 0xffff0000u));
+                }
+            pa = __builtin_bit_cast(bf16x8, u32x4{ph[0], ph[1], ph[2], ph[3]});
+            pb = __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
+            if (grow) {  // after tile it - 1's product, before tile it's
+#pragma unroll
+                for (int nb = 0; nb < 18; ++nb) o[nb] *= corr;
+            }
         }
     }
+    if (!active) return;
+    if (ntile > 0) pv(Kt[(ntile - 1) % 3], pa, pb);  // the last tile (no store follows it)
+    const float lrun = sum4g(lpart);
 
-    // epilogue: this wave's heads h0 + 4 kgrp + r and dims dbase + 16 nb + hrow
+    // epilogue: head h = h0 + n, dims dbase + 16 nb + 4 g4 + i
+    const int h = h0 + n;
     const int64_t nrows = (int64_t)gridDim.x;
     if (nsplit > 1) {
         float* wo = (float*)a.ws;
         float* wml = wo + (int64_t)nsplit * nrows * a.H * kC;
+        const int64_t pr = ((int64_t)split * nrows + rowid) * a.H + h;
+        float* dst = wo + pr * kC + dbase + 4 * g4;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int h = h0 + 4 * kgrp + r;
-            if (h >= a.H) continue;
-            const int64_t pr = ((int64_t)split * nrows + rowid) * a.H + h;
-            float* dst = wo + pr * kC + dbase + hrow;
-#pragma unroll
-            for (int nb = 0; nb < 18; ++nb) dst[16 * nb] = o[nb][r];
-            if (hrow == 0 && dh == 0) {
-                wml[2 * pr] = mrun[r];
-                wml[2 * pr + 1] = lrun[r];
-            }
+        for (int nb = 0; nb < 18; ++nb) *(f32x4*)(dst + 16 * nb) = o[nb];
+        if (g4 == 0 && dh == 0) {
+            wml[2 * pr] = mrun;
+            wml[2 * pr + 1] = lrun;
         }
         return;
     }
-    // output RoPE: dims 512 + i and 544 + i (i < 32) sit in this half's blocks 14 + q2 and 16 + q2
-    float sn[2] = {0.0f, 0.0f}, cs[2] = {1.0f, 1.0f};
-    const bool rot = a.rope_theta != 0.0 && dh == 1;
-    if (rot) {
-#pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2) rope_sincos(a.rope.inv, 16 * q2 + hrow, -(double)t, &sn[q2], &cs[q2]);
+    float mu = mrun, den = lrun;
+    if (a.sink) {
+        const float z = a.sink[h] * kLog2e;
+        mu = fmaxf(mrun, z);
+        den = (mrun == -INFINITY ? 0.0f : lrun * exp2f(mrun - mu)) + exp2f(z - mu);
     }
+    const float f = den > 0.0f && mrun != -INFINITY ? exp2f(mrun - mu) / den : 0.0f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int h = h0 + 4 * kgrp + r;
-        if (h >= a.H) continue;
-        float mu = mrun[r];
-        float den = lrun[r];
-        if (a.sink) {
-            const float z = a.sink[h] * kLog2e;
-            mu = fmaxf(mrun[r], z);
-            den = (mrun[r] == -INFINITY ? 0.0f : lrun[r] * exp2f(mrun[r] - mu)) + exp2f(z - mu);
-        }
-        const float f = den > 0.0f && mrun[r] != -INFINITY ? exp2f(mrun[r] - mu) / den : 0.0f;
-        float ov[18];
+    for (int nb = 0; nb < 18; ++nb) o[nb] *= f;
+    // output RoPE by -t: dims 512 + j and 544 + j (j < 32) are blocks 14 + q2 and 16 + q2 of the
+    // upper half, j = 16 q2 + 4 g4 + i
+    if (a.rope_theta != 0.0 && dh == 1) {
 #pragma unroll
-        for (int nb = 0; nb < 18; ++nb) ov[nb] = o[nb][r] * f;
-        if (rot) {
+        for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
-            for (int q2 = 0; q2 < 2; ++q2) {
-                const float x0 = ov[14 + q2], x1 = ov[16 + q2];
-                ov[14 + q2] = x0 * cs[q2] - x1 * sn[q2];
-                ov[16 + q2] = x0 * sn[q2] + x1 * cs[q2];
+            for (int i = 0; i < 4; ++i) {
+                float sn, cs;
+                rope_sincos(a.rope.inv, 16 * q2 + 4 * g4 + i, -(double)t, &sn, &cs);
+                const float x0 = o[14 + q2][i], x1 = o[16 + q2][i];
+                o[14 + q2][i] = x0 * cs - x1 * sn;
+                o[16 + q2][i] = x0 * sn + x1 * cs;
             }
-        }
-        const int64_t orow = (rowid * a.H + h) * kC + dbase + hrow;
-        if (a.out_dtype == LCA_F32) {
-            float* dst = (float*)a.out + orow;
-#pragma unroll
-            for (int nb = 0; nb < 18; ++nb) dst[16 * nb] = ov[nb];
-        } else {
-            uint16_t* dst = (uint16_t*)a.out + orow;
-#pragma unroll
-            for (int nb = 0; nb < 18; ++nb) dst[16 * nb] = f2bf(ov[nb]);
-        }
-        if (a.lse && hrow == 0 && dh == 0)
-            a.lse[rowid * a.H + h] = den > 0.0f ? (mu + log2f(den)) * kLn2 : -INFINITY;
     }
+    const int64_t orow = (rowid * a.H + h) * kC + dbase + 4 * g4;
+    if (a.out_dtype == LCA_F32) {
+        float* dst = (float*)a.out + orow;
+#pragma unroll
+        for (int nb = 0; nb < 18; ++nb) *(f32x4*)(dst + 16 * nb) = o[nb];
+    } else {
+        uint16_t* dst = (uint16_t*)a.out + orow;
+#pragma unroll
+        for (int nb = 0; nb < 18; ++nb) {
+            uint2 w;
+            w.x = (uint32_t)f2bf(o[nb][0]) | ((uint32_t)f2bf(o[nb][1]) << 16);
+            w.y = (uint32_t)f2bf(o[nb][2]) | ((uint32_t)f2bf(o[nb][3]) << 16);
+            *(uint2*)(dst + 16 * nb) = w;
+        }
+    }
+    if (a.lse && g4 == 0 && dh == 0)
+        a.lse[rowid * a.H + h] = den > 0.0f ? (mu + log2f(den)) * kLn2 : -INFINITY;
 }
 
 // Merge nsplit partial (O, m, l) triples of one (row, head) in split order.
@@ -560,8 +737,14 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     const int ns = attn_num_splits(rows, a.max_keys, c);
     const int64_t len = ns > 1 ? split_len_of(a.max_keys, ns) : (a.max_keys + kKT - 1) / kKT * kKT;
     dim3 grid((unsigned)rows, (unsigned)ns);
-    if (a.comp.fmt == LCA_FP8) hipLaunchKernelGGL((attn_mfma<LCA_FP8>), grid, dim3(512), 0, st, a, len, ns);
-    else hipLaunchKernelGGL((attn_mfma<LCA_BF16>), grid, dim3(512), 0, st, a, len, ns);
+    const bool dense = a.idx == nullptr;
+    if (a.comp.fmt == LCA_FP8) {
+        if (dense) hipLaunchKernelGGL((attn_mfma<LCA_FP8, true>), grid, dim3(512), 0, st, a, len, ns);
+        else hipLaunchKernelGGL((attn_mfma<LCA_FP8, false>), grid, dim3(512), 0, st, a, len, ns);
+    } else {
+        if (dense) hipLaunchKernelGGL((attn_mfma<LCA_BF16, true>), grid, dim3(512), 0, st, a, len, ns);
+        else hipLaunchKernelGGL((attn_mfma<LCA_BF16, false>), grid, dim3(512), 0, st, a, len, ns);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns <= 1) return e;
     hipLaunchKernelGGL(attn_combine, dim3((unsigned)rows, (unsigned)a.H, (unsigned)((c + kCombDims - 1) / kCombDims)),
