@@ -230,9 +230,12 @@ __device__ __forceinline__ void put8(uint16_t* Kt, int j, int chunk, u32x4 v) {
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-// transposing LDS read (see the header comment)
-__device__ __forceinline__ s16x4 lds_tr16(const uint16_t* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)p);
+// transposing LDS read (see the header comment) at an LDS byte address
+__device__ __forceinline__ s16x4 lds_tr16(uint32_t addr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(uintptr_t)addr);
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
 // two fp8 codes (low 16 bits when !high_half) -> packed bf16 bits of code * scale.  The hardware
@@ -379,12 +382,15 @@ __global__ void __launch_bounds__(512) attn_mfma(AttnArgs a, int64_t split_len, 
 
     // O^T += V^T P^T over one tile: A[row = dim dbase + 16 nb + n][k = slot pi(8 g4 + e)], two
     // transposing reads (slots 4 g4 + e and 16 + 4 g4 + e); P as bf16 hi + lo
-    auto pv = [&](const uint16_t* K, const bf16x8& pa, const bf16x8& pb) {
-        const uint16_t* vr = K + voff;
+    // (tile buffers are addressed by uniform byte offsets that rotate every tile, so that every
+    // read is one base register plus an immediate offset)
+    const uint32_t vbase = lds_addr(&Kt[0][0]) + 2 * voff;
+    auto pv = [&](uint32_t boff, const bf16x8& pa, const bf16x8& pb) {
+        const uint32_t vr = vbase + boff;
 #pragma unroll
         for (int nb = 0; nb < 18; ++nb) {
-            const s16x4 w0 = lds_tr16(vr + 16 * nb);
-            const s16x4 w1 = lds_tr16(vr + 16 * kKS + 16 * nb);
+            const s16x4 w0 = lds_tr16(vr + 32 * nb);
+            const s16x4 w1 = lds_tr16(vr + 32 * kKS + 32 * nb);
             const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7));
             o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pa, o[nb], 0, 0, 0);
             o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[nb], 0, 0, 0);
@@ -392,10 +398,13 @@ __global__ void __launch_bounds__(512) attn_mfma(AttnArgs a, int64_t split_len, 
     };
 
     bf16x8 pa = {}, pb = {};  // P^T of the previous tile (B operand, hi / lo)
+    constexpr uint32_t kTileBytes = 2 * kTileElems;
+    uint32_t bq = 0, bs = kTileBytes, bp = 2 * kTileBytes;  // byte offsets: tiles it, it + 1, it - 1
+    int fq = 0, fs = 1;                                      // their flag sets
     for (int it = 0; it < ntile; ++it) {
         __syncthreads();  // tile it stored; tile it - 2 (this phase's store target) consumed
         // ---- phase 1 ----
-        const uint16_t* K = Kt[it % 3];
+        const uint16_t* K = (const uint16_t*)((const char*)&Kt[0][0] + bq);
         f32x4 s[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
         if (active) {
             const uint16_t* kr = K + koff;
@@ -408,7 +417,7 @@ __global__ void __launch_bounds__(512) attn_mfma(AttnArgs a, int64_t split_len, 
             }
         }
         if (it + 1 < ntile) {
-            store_tile(g, Kt[(it + 1) % 3], (uint8_t*)vflag[(it + 1) % 3]);
+            store_tile(g, (uint16_t*)((char*)&Kt[0][0] + bs), (uint8_t*)vflag[fs]);
             if (it + 2 < ntile) {
                 g.load(a, sm, P, off32, s_begin + (int64_t)(it + 2) * kKT, s_end);
                 if constexpr (!DENSE) g.fetch_idx(sm, irow, s_begin + (int64_t)(it + 3) * kKT, s_end);
@@ -417,7 +426,7 @@ __global__ void __launch_bounds__(512) attn_mfma(AttnArgs a, int64_t split_len, 
         if (active) {
             // invalid slots (zero rows) get -inf in both partial sums; lane holds slots
             // 16 kb + 4 g4 + i of head h0 + n
-            const uint32_t f0 = vflag[it % 3][g4], f1 = vflag[it % 3][4 + g4];
+            const uint32_t f0 = vflag[fq][g4], f1 = vflag[fq][4 + g4];
             if (__builtin_amdgcn_ballot_w64((f0 & f1) != 0x01010101u)) {  // wave-uniform
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -431,7 +440,7 @@ __global__ void __launch_bounds__(512) attn_mfma(AttnArgs a, int64_t split_len, 
         __syncthreads();
         // ---- phase 2 ----
         if (active) {
-            if (it > 0) pv(Kt[(it + 2) % 3], pa, pb);  // tile it - 1
+            if (it > 0) pv(bp, pa, pb);  // tile it - 1
             {
                 const int pw = wv ^ 4;  // the partner wave (same heads, other dim half)
                 const f32x4 o0 = Sx[pw][0][lane], o1 = Sx[pw][1][lane];
@@ -471,13 +480,22 @@ __global__ void __launch_bounds__(512) attn_mfma(AttnArgs a, int64_t split_len, 
             pa = __builtin_bit_cast(bf16x8, u32x4{ph[0], ph[1], ph[2], ph[3]});
             pb = __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
             if (grow) {  // after tile it - 1's product, before tile it's
+                // (the empty asm keeps this a branch: if-converted, the 72 products would run on
+                // every tile)
+                asm volatile("");
 #pragma unroll
                 for (int nb = 0; nb < 18; ++nb) o[nb] *= corr;
             }
         }
+        const uint32_t bt = bp;  // tile it - 1's buffer takes tile it + 2
+        bp = bq;
+        bq = bs;
+        bs = bt;
+        fq = fs;
+        fs = fs == 2 ? 0 : fs + 1;
     }
     if (!active) return;
-    if (ntile > 0) pv(Kt[(ntile - 1) % 3], pa, pb);  // the last tile (no store follows it)
+    if (ntile > 0) pv(bp, pa, pb);  // the last tile (after the final rotation bp is its buffer)
     const float lrun = sum4g(lpart);
 
     // epilogue: head h = h0 + n, dims dbase + 16 nb + 4 g4 + i
