@@ -29,6 +29,8 @@
 //   Decode-sized launches split the slot list across workgroups; a second
 //   kernel merges the partial (O, max, sum) triples in a fixed order.
 // f32 caches: one wave per (query row, head), f32 FMA, for fp32 workloads.
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -46,15 +48,38 @@ struct SlotMap {
     int64_t nslots;
 };
 
-__device__ __forceinline__ SlotMap slot_map(const AttnArgs& a, int64_t t) {
+// Row i of sequence b (position t = q_pos[b] + i).  No 64-bit division: the window ring row of
+// the first window position comes from the host's per-sequence base (i < T <= win.cap, so one
+// subtraction wraps it), and m is a shift when it is a power of two.
+__device__ __forceinline__ SlotMap slot_map(const AttnArgs& a, int b, int i, int64_t* tp) {
     SlotMap s;
-    const int64_t vis = min((t + 1) / a.m, a.comp.cap);
+    const int64_t t = a.q_pos.v[b] + i;
+    *tp = t;
+    const int64_t q1 = a.m_shift >= 0 ? (t + 1) >> a.m_shift : (t + 1) / a.m;
+    const int64_t vis = min(q1, a.comp.cap);
     s.ncs = a.idx ? (int64_t)a.k : vis;
-    s.w_lo = t - a.n_win + 1 < 0 ? 0 : t - a.n_win + 1;
+    const int64_t d = a.q_pos.v[b] - a.n_win + 1;  // first window position of row 0
+    const int64_t wl = d + i;
+    s.w_lo = wl < 0 ? 0 : wl;
     const int64_t nw = a.n_win > 0 ? t - s.w_lo + 1 : 0;
-    s.w_row = nw > 0 ? s.w_lo % a.win.cap : 0;
+    int64_t wr = 0;
+    if (nw > 0 && wl > 0) {
+        if (d < 0) wr = wl;  // below win.cap: i < T <= win.cap
+        else {
+            wr = a.w_base.v[b] + i;
+            if (wr >= a.win.cap) wr -= a.win.cap;
+        }
+    }
+    s.w_row = wr;
     s.nslots = s.ncs + nw;
     return s;
+}
+
+// (rowid = b * T + i, 32-bit)
+__device__ __forceinline__ void row_coords(const AttnArgs& a, int64_t rowid, int* b, int* i) {
+    const uint32_t r = (uint32_t)rowid, T = (uint32_t)a.T;
+    *b = (int)(r / T);
+    *i = (int)(r - (uint32_t)*b * T);
 }
 
 // source row of a slot: 0 = invalid, 1 = compressed row, 2 = window row.  Window slots are
@@ -317,9 +342,10 @@ __global__ void __launch_bounds__(512) attn_mfma(AttnArgs a, int64_t split_len, 
 
     const int64_t rowid = blockIdx.x;
     const int split = blockIdx.y;
-    const int b = (int)(rowid / a.T);
-    const int64_t t = a.q_pos.v[b] + rowid % a.T;
-    const SlotMap sm = slot_map(a, t);
+    int b, ri;
+    row_coords(a, rowid, &b, &ri);
+    int64_t t;
+    const SlotMap sm = slot_map(a, b, ri, &t);
     const int64_t s_begin = (int64_t)split * split_len;
     const int64_t s_end = min(sm.nslots, s_begin + split_len);
     const int ntile = s_end > s_begin ? (int)((s_end - s_begin + kKT - 1) / kKT) : 0;
@@ -502,6 +528,7 @@ __global__ void __launch_bounds__(512) attn_mfma(AttnArgs a, int64_t split_len, 
     const int h = h0 + n;
     const int64_t nrows = (int64_t)gridDim.x;
     if (nsplit > 1) {
+        // partial O (unnormalised, f32), then the (max, sum) pairs
         float* wo = (float*)a.ws;
         float* wml = wo + (int64_t)nsplit * nrows * a.H * kC;
         const int64_t pr = ((int64_t)split * nrows + rowid) * a.H + h;
@@ -556,21 +583,20 @@ __global__ void __launch_bounds__(512) attn_mfma(AttnArgs a, int64_t split_len, 
         a.lse[rowid * a.H + h] = den > 0.0f ? (mu + log2f(den)) * kLn2 : -INFINITY;
 }
 
-// Merge nsplit partial (O, m, l) triples of one (row, head) in split order.
-// Block (row, head, dim chunk of 192): wave 0 turns the splits' (m, l) into
-// weights in LDS, then every thread reduces its dim over the splits.
-constexpr int kCombDims = 192;
-__global__ void __launch_bounds__(kCombDims) attn_combine(AttnArgs a, int nsplit, int c, int d_nope,
-                                                          int d_rope) {
+// Merge nsplit partial (O, m, l) triples of one (row, head) in split order.  Block (row, head):
+// wave 0 turns the splits' (m, l) into weights in LDS, then thread j reduces dims 2j, 2j + 1
+// (and, for RoPE dims, their rotation partners) over the splits.
+constexpr int kCombThreads = kC / 2;  // 288
+__global__ void __launch_bounds__(kCombThreads) attn_combine(AttnArgs a, int nsplit) {
     const int64_t rowid = blockIdx.x;
     const int h = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63;
-    const int d = blockIdx.z * kCombDims + tid;
     const int64_t nrows = gridDim.x;
     const float* wo = (const float*)a.ws;
-    const float* wml = wo + (int64_t)nsplit * nrows * a.H * c;
-    const int b = (int)(rowid / a.T);
-    const int64_t t = a.q_pos.v[b] + rowid % a.T;
+    const float* wml = wo + (int64_t)nsplit * nrows * a.H * kC;
+    int b, ri;
+    row_coords(a, rowid, &b, &ri);
+    const int64_t t = a.q_pos.v[b] + ri;
     __shared__ float wsp[1024];
     __shared__ float s_mu, s_den;
     if (tid < 64) {
@@ -597,45 +623,64 @@ __global__ void __launch_bounds__(kCombDims) attn_combine(AttnArgs a, int nsplit
     __syncthreads();
     const float den = s_den, mu = s_mu;
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-    if (a.lse && blockIdx.z == 0 && tid == 0)
-        a.lse[rowid * a.H + h] = den > 0.0f ? (mu + log2f(den)) * kLn2 : -INFINITY;
-    if (d >= c) return;
-    // this thread's dim, and its RoPE partner when the output is rotated
-    const int half = d_rope / 2;
-    const bool rot = a.rope_theta != 0.0 && d >= d_nope;
-    const int r = d - d_nope;
-    const int dp = !rot ? d : (r < half ? d + half : d - half);
-    const int64_t stride = nrows * a.H * c;  // between splits
-    const float* p0 = wo + (rowid * a.H + h) * c;
-    float acc = 0.0f, accp = 0.0f;
+    if (a.lse && tid == 0) a.lse[rowid * a.H + h] = den > 0.0f ? (mu + log2f(den)) * kLn2 : -INFINITY;
+    const int d = 2 * tid;
+    // RoPE dims 512 + j pair with 544 + j (j < 32)
+    const bool rot = a.rope_theta != 0.0 && d >= kDN;
+    const int r = d - kDN;
+    const int dp = !rot ? d : (r < kDR / 2 ? d + kDR / 2 : d - kDR / 2);
+    const int64_t stride = nrows * a.H * kC / 2;  // between splits, in float2
+    const float2* p0 = (const float2*)(wo + (rowid * a.H + h) * kC);
+    float acc0 = 0.0f, acc1 = 0.0f, accp0 = 0.0f, accp1 = 0.0f;
     int j = 0;
-    for (; j + 16 <= nsplit; j += 16) {
-        float v[16], vp[16];
+    auto chunk = [&](auto U) {  // U splits at once: all loads first, then the sums in split order
+        constexpr int kU = decltype(U)::value;
+        float2 v[kU], vp[kU];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            v[u] = p0[(j + u) * stride + d];
-            vp[u] = rot ? p0[(j + u) * stride + dp] : 0.0f;
+        for (int u = 0; u < kU; ++u) {
+            v[u] = p0[(j + u) * stride + d / 2];
+            vp[u] = rot ? p0[(j + u) * stride + dp / 2] : float2{0.0f, 0.0f};
         }
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            acc = fmaf(v[u], wsp[j + u], acc);
-            accp = fmaf(vp[u], wsp[j + u], accp);
+        for (int u = 0; u < kU; ++u) {
+            const float wgt = wsp[j + u];
+            acc0 = fmaf(v[u].x, wgt, acc0);
+            acc1 = fmaf(v[u].y, wgt, acc1);
+            accp0 = fmaf(vp[u].x, wgt, accp0);
+            accp1 = fmaf(vp[u].y, wgt, accp1);
         }
-    }
+        j += kU;
+    };
+    while (j + 8 <= nsplit) chunk(std::integral_constant<int, 8>());
+    if (j + 4 <= nsplit) chunk(std::integral_constant<int, 4>());
     for (; j < nsplit; ++j) {
-        acc = fmaf(p0[j * stride + d], wsp[j], acc);
-        if (rot) accp = fmaf(p0[j * stride + dp], wsp[j], accp);
+        const float wgt = wsp[j];
+        const float2 v = p0[j * stride + d / 2];
+        acc0 = fmaf(v.x, wgt, acc0);
+        acc1 = fmaf(v.y, wgt, acc1);
+        if (rot) {
+            const float2 vp = p0[j * stride + dp / 2];
+            accp0 = fmaf(vp.x, wgt, accp0);
+            accp1 = fmaf(vp.y, wgt, accp1);
+        }
     }
-    float v = acc * inv;
+    float o0 = acc0 * inv, o1 = acc1 * inv;
     if (rot) {
         float sn, cs;
-        rope_sincos(a.rope.inv, r < half ? r : r - half, -(double)t, &sn, &cs);
-        const float vp = accp * inv;
-        v = r < half ? v * cs - vp * sn : vp * sn + v * cs;
+        const int pi = r < kDR / 2 ? r : r - kDR / 2;
+        const float q0 = accp0 * inv, q1 = accp1 * inv;
+        rope_sincos(a.rope.inv, pi, -(double)t, &sn, &cs);
+        o0 = r < kDR / 2 ? o0 * cs - q0 * sn : q0 * sn + o0 * cs;
+        rope_sincos(a.rope.inv, pi + 1, -(double)t, &sn, &cs);
+        o1 = r < kDR / 2 ? o1 * cs - q1 * sn : q1 * sn + o1 * cs;
     }
-    const int64_t oi = (rowid * a.H + h) * c + d;
-    if (a.out_dtype == LCA_F32) ((float*)a.out)[oi] = v;
-    else ((uint16_t*)a.out)[oi] = f2bf(v);
+    const int64_t oi = (rowid * a.H + h) * kC + d;
+    if (a.out_dtype == LCA_F32) {
+        ((float*)a.out)[oi] = o0;
+        ((float*)a.out)[oi + 1] = o1;
+    } else {
+        ((uint32_t*)a.out)[oi / 2] = (uint32_t)f2bf(o0) | ((uint32_t)f2bf(o1) << 16);
+    }
 }
 
 // f32 caches: one wave per (row, head); lane owns dims lane + 64 u.
@@ -643,9 +688,10 @@ __global__ void __launch_bounds__(64) attn_f32(AttnArgs a) {
     const int64_t rowid = blockIdx.x;
     const int h = blockIdx.y;
     const int lane = threadIdx.x;
-    const int b = (int)(rowid / a.T);
-    const int64_t t = a.q_pos.v[b] + rowid % a.T;
-    const SlotMap sm = slot_map(a, t);
+    int b, ri;
+    row_coords(a, rowid, &b, &ri);
+    int64_t t;
+    const SlotMap sm = slot_map(a, b, ri, &t);
     const int d_nope = a.comp.d_nope, d_rope = a.comp.d_rope, c = d_nope + d_rope;
     constexpr int U = 16;  // c <= 1024
     __shared__ float osh[1024];
@@ -765,8 +811,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns <= 1) return e;
-    hipLaunchKernelGGL(attn_combine, dim3((unsigned)rows, (unsigned)a.H, (unsigned)((c + kCombDims - 1) / kCombDims)),
-                       dim3(kCombDims), 0, st, a, ns, c, a.comp.d_nope, a.comp.d_rope);
+    hipLaunchKernelGGL(attn_combine, dim3((unsigned)rows, (unsigned)a.H), dim3(kCombThreads), 0, st, a, ns);
     return hipGetLastError();
 }
 

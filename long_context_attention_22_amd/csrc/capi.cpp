@@ -268,6 +268,13 @@ static int attn_common(const void* q, int32_t q_dtype, int32_t H, int32_t B, int
     a.rope = rope_tab(rope_theta, comp.d_rope);
     a.out = out; a.out_dtype = out_dtype; a.lse = lse; a.ws = ws; a.q_pos = to_pos(q_pos, B);
     a.max_keys = max_keys;
+    a.m_shift = -1;
+    for (int sh = 0; sh < 31; ++sh)
+        if (((int64_t)1 << sh) == m) a.m_shift = sh;
+    for (int b = 0; b < B; ++b) {
+        const int64_t d = q_pos[b] - n_win + 1;
+        a.w_base.v[b] = d >= 0 && win.cap > 0 ? d % win.cap : 0;
+    }
     if (n_win == 0) a.win = comp;  // never read
     return hip_status(lca::launch_attn(a, (hipStream_t)stream));
 }

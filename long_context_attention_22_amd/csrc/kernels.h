@@ -88,6 +88,8 @@ struct AttnArgs {
     float* lse;
     void* ws;
     Pos q_pos;
+    Pos w_base;         // (q_pos[b] - n_win + 1) mod win.cap, where that position is >= 0
+    int32_t m_shift;    // log2(m) when m is a power of two, else -1
     int64_t max_keys;   // attended rows per query, upper bound
 };
 int attn_num_splits(int64_t rows, int64_t max_keys, int32_t c);
