@@ -330,6 +330,27 @@ __global__ void __launch_bounds__(kSplitThreads) topk_split_emit(TopkArgs a, int
             for (int64_t j = (int64_t)G * kChunk + tid; j < a.k; j += kSplitThreads) r.out[j] = j < r.n ? (int32_t)j : -1;
         return;
     }
+    // This thread's 32 consecutive scores, fetched before the digits are known so that the
+    // loads overlap the histogram reductions.
+    constexpr int kPer = kChunk / kSplitThreads;  // 32
+    const int64_t e0 = lo + (int64_t)kPer * tid;
+    uint32_t raw[kPer / 2];                       // bf16 pairs, element e0 + 2q in the low half
+    const bool vec = (((uintptr_t)(r.row + lo)) & 15u) == 0 && e0 + kPer <= hi;
+    if (vec) {
+#pragma unroll
+        for (int q = 0; q < kPer / 8; ++q) {
+            const u32x4 x = ((const u32x4*)(r.row + e0))[q];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) raw[4 * q + w] = x[w];
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < kPer / 2; ++q) {
+            const uint32_t l = e0 + 2 * q < hi ? r.row[e0 + 2 * q] : 0u;
+            const uint32_t h = e0 + 2 * q + 1 < hi ? r.row[e0 + 2 * q + 1] : 0u;
+            raw[q] = l | (h << 16);
+        }
+    }
     __shared__ uint32_t tot[256];
     __shared__ uint32_t d1, rem1, d2, rem2;
     __shared__ uint32_t wsum[kSplitThreads / 64];
@@ -357,37 +378,32 @@ __global__ void __launch_bounds__(kSplitThreads) topk_split_emit(TopkArgs a, int
         }
         __syncthreads();
     }
-    uint32_t gt_base = base_gt, eq_base = base_eq;
-    for (int64_t base = lo; base < hi; base += 8 * kSplitThreads) {
-        const int64_t e0 = base + 8 * (int64_t)tid;
-        uint32_t keys[8];
-        uint32_t ngt = 0, neq = 0;
+    uint32_t keys[kPer];
+    uint32_t ngt = 0, neq = 0;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const bool valid = e0 + u < hi;
-            keys[u] = valid ? mono_key(r.row[e0 + u]) : 0u;
-            ngt += (valid && keys[u] > tau) ? 1u : 0u;
-            neq += (valid && keys[u] == tau) ? 1u : 0u;
-        }
-        uint32_t t;
-        const uint32_t packed = ngt | (neq << 16);
-        const uint32_t excl = block_incl_scan<kSplitThreads / 64>(packed, wsum, &t) - packed;
-        uint32_t gt_before = gt_base + (excl & 0xffffu);
-        uint32_t eq_before = eq_base + (excl >> 16);
+    for (int u = 0; u < kPer; ++u) {
+        const bool valid = e0 + u < hi;
+        keys[u] = valid ? mono_key((uint16_t)(raw[u >> 1] >> (16 * (u & 1)))) : 0u;
+        ngt += (valid && keys[u] > tau) ? 1u : 0u;
+        neq += (valid && keys[u] == tau) ? 1u : 0u;
+    }
+    uint32_t t;
+    const uint32_t packed = ngt | (neq << 16);  // at most 16384 each
+    const uint32_t excl = block_incl_scan<kSplitThreads / 64>(packed, wsum, &t) - packed;
+    uint32_t gt_before = base_gt + (excl & 0xffffu);
+    uint32_t eq_before = base_eq + (excl >> 16);
+    if (ngt + neq == 0) return;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            if (e0 + u >= hi) break;
-            const uint32_t pos = gt_before + min(eq_before, rem);
-            if (keys[u] > tau) {
-                r.out[pos] = (int32_t)(e0 + u);
-                ++gt_before;
-            } else if (keys[u] == tau) {
-                if (eq_before < rem) r.out[pos] = (int32_t)(e0 + u);
-                ++eq_before;
-            }
+    for (int u = 0; u < kPer; ++u) {
+        if (e0 + u >= hi) break;
+        const uint32_t pos = gt_before + min(eq_before, rem);
+        if (keys[u] > tau) {
+            r.out[pos] = (int32_t)(e0 + u);
+            ++gt_before;
+        } else if (keys[u] == tau) {
+            if (eq_before < rem) r.out[pos] = (int32_t)(e0 + u);
+            ++eq_before;
         }
-        gt_base += t & 0xffffu;
-        eq_base += t >> 16;
     }
 }
 
