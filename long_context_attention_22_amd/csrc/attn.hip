@@ -583,11 +583,16 @@ __global__ void __launch_bounds__(512) attn_mfma(AttnArgs a, int64_t split_len, 
         a.lse[rowid * a.H + h] = den > 0.0f ? (mu + log2f(den)) * kLn2 : -INFINITY;
 }
 
-// Merge nsplit partial (O, m, l) triples of one (row, head) in split order.  Block (row, head):
-// wave 0 turns the splits' (m, l) into weights in LDS, then thread j reduces dims 2j, 2j + 1
-// (and, for RoPE dims, their rotation partners) over the splits.
-constexpr int kCombThreads = kC / 2;  // 288
+// Merge nsplit partial (O, m, l) triples of one (row, head).  Block (row, head), ng x 144 threads
+// (ng = one split group per 8 splits, at most 4): wave 0 turns the splits' (m, l) into weights in
+// LDS; then split group q = tid / 144 sums splits q, q + ng, ... for dims 4 (tid % 144) .. +3 (and,
+// for RoPE dims, their rotation partners), and the group sums are added in group order.  Each
+// thread keeps a short chain of loads: the merge is bound by load latency, not bandwidth.
+constexpr int kCombGroups = 4, kCombPer = kC / 4;  // at most 4 groups of 144 threads, 4 dims each
+constexpr int kCombThreads = kCombGroups * kCombPer;
+static int comb_groups(int nsplit) { return nsplit >= 32 ? 4 : nsplit >= 16 ? 2 : 1; }
 __global__ void __launch_bounds__(kCombThreads) attn_combine(AttnArgs a, int nsplit) {
+    const int ng = blockDim.x / kCombPer;
     const int64_t rowid = blockIdx.x;
     const int h = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -599,6 +604,7 @@ __global__ void __launch_bounds__(kCombThreads) attn_combine(AttnArgs a, int nsp
     const int64_t t = a.q_pos.v[b] + ri;
     __shared__ float wsp[1024];
     __shared__ float s_mu, s_den;
+    __shared__ f32x4 part[kCombGroups - 1][kCombPer][2];
     if (tid < 64) {
         float M = -INFINITY;
         for (int j = lane; j < nsplit; j += 64) M = fmaxf(M, wml[2 * ((j * nrows + rowid) * a.H + h)]);
@@ -621,65 +627,71 @@ __global__ void __launch_bounds__(kCombThreads) attn_combine(AttnArgs a, int nsp
         }
     }
     __syncthreads();
-    const float den = s_den, mu = s_mu;
-    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-    if (a.lse && tid == 0) a.lse[rowid * a.H + h] = den > 0.0f ? (mu + log2f(den)) * kLn2 : -INFINITY;
-    const int d = 2 * tid;
+    const int q = tid / kCombPer, e = tid - q * kCombPer;
+    const int d = 4 * e;
     // RoPE dims 512 + j pair with 544 + j (j < 32)
     const bool rot = a.rope_theta != 0.0 && d >= kDN;
     const int r = d - kDN;
     const int dp = !rot ? d : (r < kDR / 2 ? d + kDR / 2 : d - kDR / 2);
-    const int64_t stride = nrows * a.H * kC / 2;  // between splits, in float2
-    const float2* p0 = (const float2*)(wo + (rowid * a.H + h) * kC);
-    float acc0 = 0.0f, acc1 = 0.0f, accp0 = 0.0f, accp1 = 0.0f;
-    int j = 0;
-    auto chunk = [&](auto U) {  // U splits at once: all loads first, then the sums in split order
+    const int64_t stride = nrows * a.H * kC / 4;  // between splits, in f32x4
+    const f32x4* p0 = (const f32x4*)(wo + (rowid * a.H + h) * kC);
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f}, accp = {0.0f, 0.0f, 0.0f, 0.0f};
+    int j = q;
+    auto chunk = [&](auto U) {  // U of this group's splits: all loads first, then the sums in order
         constexpr int kU = decltype(U)::value;
-        float2 v[kU], vp[kU];
+        f32x4 v[kU], vp[kU];
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            v[u] = p0[(j + u) * stride + d / 2];
-            vp[u] = rot ? p0[(j + u) * stride + dp / 2] : float2{0.0f, 0.0f};
+            v[u] = p0[(j + ng * u) * stride + e];
+            if (rot) vp[u] = p0[(j + ng * u) * stride + dp / 4];
         }
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            const float wgt = wsp[j + u];
-            acc0 = fmaf(v[u].x, wgt, acc0);
-            acc1 = fmaf(v[u].y, wgt, acc1);
-            accp0 = fmaf(vp[u].x, wgt, accp0);
-            accp1 = fmaf(vp[u].y, wgt, accp1);
+            const float wgt = wsp[j + ng * u];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                acc[c] = fmaf(v[u][c], wgt, acc[c]);
+                if (rot) accp[c] = fmaf(vp[u][c], wgt, accp[c]);
+            }
         }
-        j += kU;
+        j += ng * kU;
     };
-    while (j + 8 <= nsplit) chunk(std::integral_constant<int, 8>());
-    if (j + 4 <= nsplit) chunk(std::integral_constant<int, 4>());
-    for (; j < nsplit; ++j) {
-        const float wgt = wsp[j];
-        const float2 v = p0[j * stride + d / 2];
-        acc0 = fmaf(v.x, wgt, acc0);
-        acc1 = fmaf(v.y, wgt, acc1);
-        if (rot) {
-            const float2 vp = p0[j * stride + dp / 2];
-            accp0 = fmaf(vp.x, wgt, accp0);
-            accp1 = fmaf(vp.y, wgt, accp1);
-        }
+    while (j + ng * 7 < nsplit) chunk(std::integral_constant<int, 8>());
+    while (j + ng * 3 < nsplit) chunk(std::integral_constant<int, 4>());
+    while (j < nsplit) chunk(std::integral_constant<int, 1>());
+    if (q > 0) {
+        part[q - 1][e][0] = acc;
+        part[q - 1][e][1] = accp;
     }
-    float o0 = acc0 * inv, o1 = acc1 * inv;
+    __syncthreads();
+    if (q > 0) return;
+#pragma unroll
+    for (int g = 0; g < ng - 1; ++g) {
+        acc += part[g][e][0];
+        if (rot) accp += part[g][e][1];
+    }
+    const float den = s_den, mu = s_mu;
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    if (a.lse && tid == 0) a.lse[rowid * a.H + h] = den > 0.0f ? (mu + log2f(den)) * kLn2 : -INFINITY;
+    f32x4 ov = acc * inv;
     if (rot) {
-        float sn, cs;
         const int pi = r < kDR / 2 ? r : r - kDR / 2;
-        const float q0 = accp0 * inv, q1 = accp1 * inv;
-        rope_sincos(a.rope.inv, pi, -(double)t, &sn, &cs);
-        o0 = r < kDR / 2 ? o0 * cs - q0 * sn : q0 * sn + o0 * cs;
-        rope_sincos(a.rope.inv, pi + 1, -(double)t, &sn, &cs);
-        o1 = r < kDR / 2 ? o1 * cs - q1 * sn : q1 * sn + o1 * cs;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            float sn, cs;
+            rope_sincos(a.rope.inv, pi + c, -(double)t, &sn, &cs);
+            const float x = ov[c], y = accp[c] * inv;
+            ov[c] = r < kDR / 2 ? x * cs - y * sn : y * sn + x * cs;
+        }
     }
     const int64_t oi = (rowid * a.H + h) * kC + d;
     if (a.out_dtype == LCA_F32) {
-        ((float*)a.out)[oi] = o0;
-        ((float*)a.out)[oi + 1] = o1;
+        *(f32x4*)((float*)a.out + oi) = ov;
     } else {
-        ((uint32_t*)a.out)[oi / 2] = (uint32_t)f2bf(o0) | ((uint32_t)f2bf(o1) << 16);
+        uint2 w;
+        w.x = (uint32_t)f2bf(ov[0]) | ((uint32_t)f2bf(ov[1]) << 16);
+        w.y = (uint32_t)f2bf(ov[2]) | ((uint32_t)f2bf(ov[3]) << 16);
+        *(uint2*)((uint16_t*)a.out + oi) = w;
     }
 }
 
@@ -811,7 +823,8 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns <= 1) return e;
-    hipLaunchKernelGGL(attn_combine, dim3((unsigned)rows, (unsigned)a.H), dim3(kCombThreads), 0, st, a, ns);
+    hipLaunchKernelGGL(attn_combine, dim3((unsigned)rows, (unsigned)a.H), dim3(comb_groups(ns) * kCombPer), 0, st,
+                       a, ns);
     return hipGetLastError();
 }
 
