@@ -432,7 +432,8 @@ __global__ void __launch_bounds__(512) attn_mfma(AttnArgs a, int64_t split_len, 
         // ---- phase 1 ----
         const uint16_t* K = (const uint16_t*)((const char*)&Kt[0][0] + bq);
         f32x4 s[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
-        if (active) {
+        {  // (every wave: with H < 64 an idle wave multiplies zero queries; no branch here lets
+           // the tile store below fill the waits of these reads)
             const uint16_t* kr = K + koff;
 #pragma unroll
             for (int ks = 0; ks < 9; ++ks) {
@@ -442,8 +443,10 @@ __global__ void __launch_bounds__(512) attn_mfma(AttnArgs a, int64_t split_len, 
                 s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[ks], s[1], 0, 0, 0);
             }
         }
-        if (it + 1 < ntile) {
-            store_tile(g, (uint16_t*)((char*)&Kt[0][0] + bs), (uint8_t*)vflag[fs]);
+        // Tile it + 1 (after the last tile: a harmless store of stale rows into the free buffer;
+        // unconditional so that its VALU work can fill the waits of the score product).
+        store_tile(g, (uint16_t*)((char*)&Kt[0][0] + bs), (uint8_t*)vflag[fs]);
+        {
             if (it + 2 < ntile) {
                 g.load(a, sm, P, off32, s_begin + (int64_t)(it + 2) * kKT, s_end);
                 if constexpr (!DENSE) g.fetch_idx(sm, irow, s_begin + (int64_t)(it + 3) * kKT, s_end);
