@@ -339,6 +339,10 @@ def bench_prefill_1m(stack: Stack, reps: int = 3, T: int = 4096, seed: int = 100
         if layer.spec.kind == "csa" and layer.scores.shape[1] < T:
             layer.scores = torch.empty(1, T, layer.comp.cap, dtype=torch.bfloat16, device="cuda")
             layer.idx = torch.empty(1, T, layer.spec.k, dtype=torch.int32, device="cuda")
+        keys = (layer.spec.k if layer.spec.kind == "csa" else layer.comp.cap) + layer.spec.n_win
+        need = lca.attn_workspace_size(1, T, layer.spec.H, C, keys)
+        if need > layer.ws.numel():
+            layer.ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     outs = [torch.empty(1, T, s.H, C, dtype=torch.bfloat16, device="cuda") for s in stack.specs]
     timers = {n: KernelTimer(n) for n in ("indexer_score", "topk_select", "csa_attn", "hca_attn")}
 

@@ -183,7 +183,11 @@ int lca_hca_attn(const void* q, int32_t q_dtype, int32_t H, int32_t B, int32_t T
                  int32_t out_dtype, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes for lca_csa_attn / lca_hca_attn with at most max_keys
- * attended rows per query (selected or visible entries + window). */
+ * attended rows per query (selected or visible entries + window).  Covers the
+ * split partials of short (decode-sized) launches and, from 128 query rows on,
+ * room for lca_hca_attn to expand an fp8 launch's rows to bf16 once instead of
+ * per query row; with less workspace a long launch expands per tile (same
+ * results).  No initialisation is needed. */
 size_t lca_attn_workspace_size(int32_t B, int32_t T, int32_t H, int32_t c, int64_t max_keys);
 
 /* Message for the last failed call on this thread ("" if none). */

@@ -805,6 +805,39 @@ size_t attn_ws_bytes(int64_t rows, int32_t H, int32_t c, int64_t max_keys) {
     return (size_t)ns * rows * H * (c + 2) * sizeof(float);
 }
 
+// Expansion of fp8 rows to bf16: 8 rows per 256-thread block; thread (row r = tid / 32, lane c)
+// expands nope codes 16c .. 16c+15 (two 16-byte bf16 stores), lanes c < 8 copy RoPE chunk c.
+__global__ void __launch_bounds__(256) kv_expand(ExpandArgs a) {
+    const int b = blockIdx.y;
+    const int r = threadIdx.x >> 5, c = threadIdx.x & 31;
+    const int64_t i = (int64_t)blockIdx.x * 8 + r;
+    if (i >= a.count.v[b]) return;
+    const int64_t p = a.first.v[b] + i;
+    const int64_t sr = (int64_t)b * a.src.cap + p % a.src.cap;
+    const int64_t dr = (int64_t)b * a.dst.cap + p % a.dst.cap;
+    const u32x4 codes = ((const u32x4*)((const uint8_t*)a.src.nope + sr * kDN))[c];
+    const float sc = a.src.scale[sr * 4 + (c >> 3)];
+    u32x4 lo, hi;
+    lo[0] = fp8x2_bf16<false>(codes[0], sc);
+    lo[1] = fp8x2_bf16<true>(codes[0], sc);
+    lo[2] = fp8x2_bf16<false>(codes[1], sc);
+    lo[3] = fp8x2_bf16<true>(codes[1], sc);
+    hi[0] = fp8x2_bf16<false>(codes[2], sc);
+    hi[1] = fp8x2_bf16<true>(codes[2], sc);
+    hi[2] = fp8x2_bf16<false>(codes[3], sc);
+    hi[3] = fp8x2_bf16<true>(codes[3], sc);
+    u32x4* dn = (u32x4*)((uint16_t*)a.dst.nope + dr * kDN);
+    dn[2 * c] = lo;
+    dn[2 * c + 1] = hi;
+    if (c < 8) ((u32x4*)((uint16_t*)a.dst.rope + dr * kDR))[c] = ((const u32x4*)((const uint16_t*)a.src.rope + sr * kDR))[c];
+}
+
+hipError_t launch_kv_expand(const ExpandArgs& a, hipStream_t st) {
+    if (a.max_count <= 0) return hipSuccess;
+    hipLaunchKernelGGL(kv_expand, dim3((unsigned)((a.max_count + 7) / 8), (unsigned)a.B), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     const int64_t rows = (int64_t)a.B * a.T;
     if (rows <= 0) return hipSuccess;

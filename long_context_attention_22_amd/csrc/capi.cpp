@@ -198,9 +198,19 @@ int lca_topk_select(const void* scores, int32_t score_dtype, int64_t s_stride, i
     return hip_status(lca::launch_topk(a, (hipStream_t)stream));
 }
 
+// Bytes of one expanded (bf16) row, and the expansion's bound: at most max_keys compressed rows
+// plus a window ring of at most max_keys + T - 1 rows per sequence.
+static constexpr size_t kExpandRowBytes = (512 + 64) * sizeof(uint16_t);
+static size_t expand_bound(int64_t B, int64_t T, int64_t max_keys) {
+    if (B * T < lca::kExpandMinRows) return 0;
+    return (size_t)B * (size_t)(2 * max_keys + T) * kExpandRowBytes;
+}
+
 size_t lca_attn_workspace_size(int32_t B, int32_t T, int32_t H, int32_t c, int64_t max_keys) {
     if (B < 1 || T < 1 || H < 1 || c < 1 || max_keys < 1) return 0;
-    return lca::attn_ws_bytes((int64_t)B * T, H, c, max_keys);
+    const size_t split = lca::attn_ws_bytes((int64_t)B * T, H, c, max_keys);
+    const size_t expand = c == 576 ? expand_bound(B, T, max_keys) : 0;
+    return split > expand ? split : expand;
 }
 
 static int attn_common(const void* q, int32_t q_dtype, int32_t H, int32_t B, int32_t T,
@@ -276,6 +286,65 @@ static int attn_common(const void* q, int32_t q_dtype, int32_t H, int32_t B, int
         a.w_base.v[b] = d >= 0 && win.cap > 0 ? d % win.cap : 0;
     }
     if (n_win == 0) a.win = comp;  // never read
+
+    // Dense fp8 launches with many query rows share every row: expand the rows they read to bf16
+    // once (compressed rows [0, vis) and the window positions the rows need, into a ring of
+    // min(n_win - 1, q_pos) + T rows), when the workspace holds them; otherwise the attention
+    // expands per tile.
+    if (!idx && comp.fmt == LCA_FP8 && (int64_t)B * T >= lca::kExpandMinRows &&
+        lca::attn_ws_bytes((int64_t)B * T, H, c, max_keys) == 0) {
+        int64_t cap_c = 1, cap_w = 1;
+        for (int b = 0; b < B; ++b) {
+            const int64_t vis = (q_pos[b] + T) / m;
+            if (vis > cap_c) cap_c = vis;
+        }
+        if (n_win > 0) {  // the ring rule: min(n_win - 1, q_pos) + T rows
+            int64_t back = 0;
+            for (int b = 0; b < B; ++b) {
+                const int64_t k1 = (int64_t)n_win - 1 < q_pos[b] ? (int64_t)n_win - 1 : q_pos[b];
+                if (k1 > back) back = k1;
+            }
+            cap_w = back + T;
+        }
+        const size_t bytes = (size_t)B * (size_t)(cap_c + (n_win > 0 ? cap_w : 0)) * kExpandRowBytes;
+        if (ws && ws_bytes >= bytes) {
+            uint16_t* base = (uint16_t*)ws;
+            lca_kv ec;
+            ec.fmt = LCA_BF16; ec.d_nope = 512; ec.d_rope = 64; ec.scale = nullptr; ec.cap = cap_c;
+            ec.nope = base;
+            ec.rope = base + (size_t)B * cap_c * 512;
+            lca::ExpandArgs x;
+            memset(&x, 0, sizeof x);
+            x.src = comp; x.dst = ec; x.B = B;
+            for (int b = 0; b < B; ++b) {
+                x.first.v[b] = 0;
+                x.count.v[b] = (q_pos[b] + T) / m;
+                if (x.count.v[b] > x.max_count) x.max_count = x.count.v[b];
+            }
+            hipError_t e = lca::launch_kv_expand(x, (hipStream_t)stream);
+            if (e != hipSuccess) return hip_status(e);
+            a.comp = ec;
+            if (n_win > 0) {
+                lca_kv ew = ec;
+                ew.cap = cap_w;
+                ew.nope = base + (size_t)B * cap_c * 576;
+                ew.rope = (uint16_t*)ew.nope + (size_t)B * cap_w * 512;
+                x.src = win; x.dst = ew; x.max_count = 0;
+                for (int b = 0; b < B; ++b) {
+                    const int64_t lo = q_pos[b] - n_win + 1 < 0 ? 0 : q_pos[b] - n_win + 1;
+                    x.first.v[b] = lo;
+                    x.count.v[b] = q_pos[b] + T - lo;
+                    if (x.count.v[b] > x.max_count) x.max_count = x.count.v[b];
+                    const int64_t d = q_pos[b] - n_win + 1;
+                    a.w_base.v[b] = d >= 0 ? d % cap_w : 0;
+                }
+                if ((e = lca::launch_kv_expand(x, (hipStream_t)stream)) != hipSuccess) return hip_status(e);
+                a.win = ew;
+            } else {
+                a.win = ec;
+            }
+        }
+    }
     return hip_status(lca::launch_attn(a, (hipStream_t)stream));
 }
 

@@ -92,6 +92,18 @@ struct AttnArgs {
     int32_t m_shift;    // log2(m) when m is a power of two, else -1
     int64_t max_keys;   // attended rows per query, upper bound
 };
+// fp8 rows -> bf16 rows (nope codes times their scale, RoPE dims copied): for each sequence b,
+// positions p in [first[b], first[b] + count[b]) of src (row b * src.cap + (p mod src.cap)) go to
+// dst row b * dst.cap + (p mod dst.cap).  Used to expand a dense (HCA) launch's rows once when
+// many query rows share them.
+struct ExpandArgs {
+    lca_kv src, dst;
+    Pos first, count;
+    int32_t B;
+    int64_t max_count;
+};
+hipError_t launch_kv_expand(const ExpandArgs& a, hipStream_t st);
+constexpr int64_t kExpandMinRows = 128;  // query rows from which a dense launch expands its rows
 int attn_num_splits(int64_t rows, int64_t max_keys, int32_t c);
 size_t attn_ws_bytes(int64_t rows, int32_t H, int32_t c, int64_t max_keys);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);

@@ -147,4 +147,6 @@ def test_attn_validation(L):
     assert need > 0
     assert attn(L, T=1, q_pos=pos(4000), k=1024) == 5
     assert attn(L, T=1, q_pos=pos(4000), k=1024, ws=FAKE2, wsb=need - 1) == 5
-    assert L.lca_attn_workspace_size(1, 4096, 64, 576, 2176) == 0   # prefill: one split per row
+    # prefill: one split per row; the size covers the optional bf16 expansion of a dense launch's
+    # rows (2 max_keys + T rows of 1152 bytes)
+    assert L.lca_attn_workspace_size(1, 4096, 64, 576, 2176) == (2 * 2176 + 4096) * 1152
