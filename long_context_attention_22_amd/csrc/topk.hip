@@ -250,44 +250,17 @@ __device__ __forceinline__ SplitRow split_row(const TopkArgs& a, int G) {
     return r;
 }
 
-// This thread's 32 consecutive scores of chunk [lo, hi) as bf16 pairs (element lo + 32 tid + 2q in
-// the low half of raw[q]); 16-byte loads when the chunk is aligned and full.
-constexpr int kPer = kChunk / kSplitThreads;  // 32
-__device__ __forceinline__ void load_chunk(const uint16_t* row, int64_t lo, int64_t hi, uint32_t* raw) {
-    const int64_t e0 = lo + (int64_t)kPer * threadIdx.x;
-    if ((((uintptr_t)(row + lo)) & 15u) == 0 && e0 + kPer <= hi) {
-#pragma unroll
-        for (int q = 0; q < kPer / 8; ++q) {
-            const u32x4 x = ((const u32x4*)(row + e0))[q];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) raw[4 * q + w] = x[w];
-        }
-    } else {
-#pragma unroll
-        for (int q = 0; q < kPer / 2; ++q) {
-            const uint32_t l = e0 + 2 * q < hi ? row[e0 + 2 * q] : 0u;
-            const uint32_t h = e0 + 2 * q + 1 < hi ? row[e0 + 2 * q + 1] : 0u;
-            raw[q] = l | (h << 16);
-        }
-    }
-}
-__device__ __forceinline__ uint32_t key_of(const uint32_t* raw, int u) {
-    return mono_key((uint16_t)(raw[u >> 1] >> (16 * (u & 1))));
-}
-
-// histogram of the chunk's keys (bin_of < 0: skipped) into LDS (16 copies), reduced into hs[256]
-template <typename F>
-__device__ __forceinline__ void regs_hist(const uint32_t* raw, int64_t lo, int64_t hi, uint32_t* hist, uint32_t* hs,
-                                          F bin_of) {
+// local histogram of the chunk into LDS (16 copies), reduced into hs[256]
+template <int NT, typename F>
+__device__ __forceinline__ void chunk_hist(const uint16_t* row, int64_t lo, int64_t hi, uint32_t* hist,
+                                           uint32_t* hs, F bin_of) {
     const int tid = threadIdx.x, sub = tid & 15;
-    for (int j = tid; j < 256 * 16; j += kSplitThreads) hist[j] = 0;
+    for (int j = tid; j < 256 * 16; j += NT) hist[j] = 0;
     __syncthreads();
-    const int64_t e0 = lo + (int64_t)kPer * tid;
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-        const int bin = e0 + u < hi ? bin_of(key_of(raw, u)) : -1;
+    for_each_key<uint16_t, NT>(row, lo, hi, [&](int64_t, uint32_t key) {
+        const int bin = bin_of(key);
         if (bin >= 0) atomicAdd(&hist[bin * 16 + sub], 1u);
-    }
+    });
     __syncthreads();
     if (tid < 256) {
         uint32_t s = 0;
@@ -298,22 +271,26 @@ __device__ __forceinline__ void regs_hist(const uint32_t* raw, int64_t lo, int64
     __syncthreads();
 }
 
-// bin `bin` of the G chunk histograms: total, and the sum over the chunks before chunk g.  All
-// loads of a column (up to 32 chunks) are in flight together.
-__device__ __forceinline__ void col_sums(const uint32_t* h, int G, int g, int bin, uint32_t* total, uint32_t* before) {
-    uint32_t t = 0, bf = 0;
-    for (int c0 = 0; c0 < G; c0 += 32) {
-        uint32_t v[32];
+// sum of bin `bin` over the first n chunk histograms (8 independent loads in flight)
+__device__ __forceinline__ uint32_t col_sum(const uint32_t* h, int n, int bin) {
+    uint32_t s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int g = 0;
+    for (; g + 8 <= n; g += 8) {
 #pragma unroll
-        for (int u = 0; u < 32; ++u) v[u] = c0 + u < G ? h[(c0 + u) * 256 + bin] : 0u;
-#pragma unroll
-        for (int u = 0; u < 32; ++u) {
-            t += v[u];
-            bf += c0 + u < g ? v[u] : 0u;
-        }
+        for (int u = 0; u < 8; ++u) s[u] += h[(g + u) * 256 + bin];
     }
-    *total = t;
-    *before = bf;
+    for (; g < n; ++g) s[0] += h[g * 256 + bin];
+    return s[0] + s[1] + s[2] + s[3] + s[4] + s[5] + s[6] + s[7];
+}
+
+// digits of the K-th largest key from the per-chunk histograms: hi byte and the count still to take
+__device__ __forceinline__ void reduce_pick(const uint32_t* h, int G, uint32_t rem, uint32_t* tot,
+                                            uint32_t* digit, uint32_t* rem_out) {
+    const int tid = threadIdx.x;
+    if (tid < 256) tot[tid] = col_sum(h, G, tid);
+    __syncthreads();
+    if (tid < 64) pick_digit(tot, rem, digit, rem_out);
+    __syncthreads();
 }
 
 __global__ void __launch_bounds__(kSplitThreads) topk_split_h1(TopkArgs a, int G) {
@@ -323,33 +300,23 @@ __global__ void __launch_bounds__(kSplitThreads) topk_split_h1(TopkArgs a, int G
     __shared__ uint32_t hist[256 * 16];
     __shared__ uint32_t hs[256];
     if (r.n <= r.K) return;  // trivial row: the emit launch handles it
-    uint32_t raw[kPer / 2];
-    load_chunk(r.row, lo, hi, raw);
-    regs_hist(raw, lo, hi, hist, hs, [](uint32_t key) { return (int)(key >> 8); });
+    chunk_hist<kSplitThreads>(r.row, lo, hi < lo ? lo : hi, hist, hs, [](uint32_t key) { return (int)(key >> 8); });
     if (threadIdx.x < 256) r.h1[g * 256 + threadIdx.x] = hs[threadIdx.x];
 }
 
 __global__ void __launch_bounds__(kSplitThreads) topk_split_h2(TopkArgs a, int G) {
     const SplitRow r = split_row(a, G);
-    const int g = blockIdx.x, tid = threadIdx.x;
+    const int g = blockIdx.x;
     const int64_t lo = (int64_t)g * kChunk, hi = min(lo + kChunk, r.n);
     __shared__ uint32_t hist[256 * 16];
     __shared__ uint32_t hs[256];
     __shared__ uint32_t d1, rem1;
     if (r.n <= r.K) return;
-    uint32_t raw[kPer / 2];
-    load_chunk(r.row, lo, hi, raw);  // in flight while the high digit is found
-    if (tid < 256) {
-        uint32_t t, bf;
-        col_sums(r.h1, G, 0, tid, &t, &bf);
-        hs[tid] = t;
-    }
-    __syncthreads();
-    if (tid < 64) pick_digit(hs, (uint32_t)r.K, &d1, &rem1);
-    __syncthreads();
+    reduce_pick(r.h1, G, (uint32_t)r.K, hs, &d1, &rem1);
     const uint32_t hb = d1;
-    regs_hist(raw, lo, hi, hist, hs, [hb](uint32_t key) { return (key >> 8) == hb ? (int)(key & 255u) : -1; });
-    if (tid < 256) r.h2[g * 256 + tid] = hs[tid];
+    chunk_hist<kSplitThreads>(r.row, lo, hi < lo ? lo : hi, hist, hs,
+                              [hb](uint32_t key) { return (key >> 8) == hb ? (int)(key & 255u) : -1; });
+    if (threadIdx.x < 256) r.h2[g * 256 + threadIdx.x] = hs[threadIdx.x];
 }
 
 __global__ void __launch_bounds__(kSplitThreads) topk_split_emit(TopkArgs a, int G) {
@@ -363,35 +330,44 @@ __global__ void __launch_bounds__(kSplitThreads) topk_split_emit(TopkArgs a, int
             for (int64_t j = (int64_t)G * kChunk + tid; j < a.k; j += kSplitThreads) r.out[j] = j < r.n ? (int32_t)j : -1;
         return;
     }
-    // the chunk's scores and both histogram columns, all in flight together
-    uint32_t raw[kPer / 2];
-    load_chunk(r.row, lo, hi, raw);
-    __shared__ uint32_t tot1[256], tot2[256];
+    // This thread's 32 consecutive scores, fetched before the digits are known so that the
+    // loads overlap the histogram reductions.
+    constexpr int kPer = kChunk / kSplitThreads;  // 32
+    const int64_t e0 = lo + (int64_t)kPer * tid;
+    uint32_t raw[kPer / 2];                       // bf16 pairs, element e0 + 2q in the low half
+    const bool vec = (((uintptr_t)(r.row + lo)) & 15u) == 0 && e0 + kPer <= hi;
+    if (vec) {
+#pragma unroll
+        for (int q = 0; q < kPer / 8; ++q) {
+            const u32x4 x = ((const u32x4*)(r.row + e0))[q];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) raw[4 * q + w] = x[w];
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < kPer / 2; ++q) {
+            const uint32_t l = e0 + 2 * q < hi ? r.row[e0 + 2 * q] : 0u;
+            const uint32_t h = e0 + 2 * q + 1 < hi ? r.row[e0 + 2 * q + 1] : 0u;
+            raw[q] = l | (h << 16);
+        }
+    }
+    __shared__ uint32_t tot[256];
     __shared__ uint32_t d1, rem1, d2, rem2;
     __shared__ uint32_t wsum[kSplitThreads / 64];
     __shared__ uint32_t base_gt, base_eq;
-    uint32_t bf1 = 0, bf2 = 0;
-    if (tid < 256) {
-        uint32_t t1, t2;
-        col_sums(r.h1, G, g, tid, &t1, &bf1);
-        col_sums(r.h2, G, g, tid, &t2, &bf2);
-        tot1[tid] = t1;
-        tot2[tid] = t2;
-    }
-    __syncthreads();
-    if (tid < 64) pick_digit(tot1, (uint32_t)r.K, &d1, &rem1);
-    __syncthreads();
-    if (tid < 64) pick_digit(tot2, rem1, &d2, &rem2);
-    __syncthreads();
+    reduce_pick(r.h1, G, (uint32_t)r.K, tot, &d1, &rem1);
+    reduce_pick(r.h2, G, rem1, tot, &d2, &rem2);
     const uint32_t tau = (d1 << 8) | d2, rem = rem2;
     if (g == 0)
         for (int64_t j = r.K + tid; j < a.k; j += kSplitThreads) r.out[j] = -1;
-    // keys above tau and equal to tau in the chunks before this one: thread = bin
+    // keys above tau and equal to tau in the chunks before this one
     {
+        // thread = bin: its counts over the earlier chunks, then a block sum of the bins above tau
         uint32_t gt = 0, eq = 0;
         if (tid < 256) {
-            gt = ((uint32_t)tid > d1 ? bf1 : 0u) + ((uint32_t)tid > d2 ? bf2 : 0u);
-            eq = (uint32_t)tid == d2 ? bf2 : 0u;
+            const uint32_t c1 = col_sum(r.h1, g, tid), c2 = col_sum(r.h2, g, tid);
+            gt = ((uint32_t)tid > d1 ? c1 : 0u) + ((uint32_t)tid > d2 ? c2 : 0u);
+            eq = (uint32_t)tid == d2 ? c2 : 0u;
         }
         uint32_t t1, t2;
         block_incl_scan<kSplitThreads / 64>(gt, wsum, &t1);
@@ -402,14 +378,14 @@ __global__ void __launch_bounds__(kSplitThreads) topk_split_emit(TopkArgs a, int
         }
         __syncthreads();
     }
-    const int64_t e0 = lo + (int64_t)kPer * tid;
+    uint32_t keys[kPer];
     uint32_t ngt = 0, neq = 0;
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
         const bool valid = e0 + u < hi;
-        const uint32_t key = key_of(raw, u);
-        ngt += (valid && key > tau) ? 1u : 0u;
-        neq += (valid && key == tau) ? 1u : 0u;
+        keys[u] = valid ? mono_key((uint16_t)(raw[u >> 1] >> (16 * (u & 1)))) : 0u;
+        ngt += (valid && keys[u] > tau) ? 1u : 0u;
+        neq += (valid && keys[u] == tau) ? 1u : 0u;
     }
     uint32_t t;
     const uint32_t packed = ngt | (neq << 16);  // at most 16384 each
@@ -420,12 +396,11 @@ __global__ void __launch_bounds__(kSplitThreads) topk_split_emit(TopkArgs a, int
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
         if (e0 + u >= hi) break;
-        const uint32_t key = key_of(raw, u);
         const uint32_t pos = gt_before + min(eq_before, rem);
-        if (key > tau) {
+        if (keys[u] > tau) {
             r.out[pos] = (int32_t)(e0 + u);
             ++gt_before;
-        } else if (key == tau) {
+        } else if (keys[u] == tau) {
             if (eq_before < rem) r.out[pos] = (int32_t)(e0 + u);
             ++eq_before;
         }
