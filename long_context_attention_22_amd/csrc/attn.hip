@@ -586,16 +586,17 @@ __global__ void __launch_bounds__(512) attn_mfma(AttnArgs a, int64_t split_len, 
         a.lse[rowid * a.H + h] = den > 0.0f ? (mu + log2f(den)) * kLn2 : -INFINITY;
 }
 
-// Merge nsplit partial (O, m, l) triples of one (row, head).  Block (row, head), ng x 144 threads
-// (ng = one split group per 8 splits, at most 4): wave 0 turns the splits' (m, l) into weights in
-// LDS; then split group q = tid / 144 sums splits q, q + ng, ... for dims 4 (tid % 144) .. +3 (and,
-// for RoPE dims, their rotation partners), and the group sums are added in group order.  Each
-// thread keeps a short chain of loads: the merge is bound by load latency, not bandwidth.
-constexpr int kCombGroups = 4, kCombPer = kC / 4;  // at most 4 groups of 144 threads, 4 dims each
+// Merge nsplit partial (O, m, l) triples of one (row, head).  Block (row, head, dim quarter z),
+// ng x 36 threads (ng = one split group per 8 splits, at most 4): wave 0 turns the splits' (m, l)
+// into weights in LDS; then split group q = tid / 36 sums splits q, q + ng, ... for dims
+// 144 z + 4 (tid % 36) .. +3 (and, for RoPE dims, their rotation partners, which lie in the same
+// quarter), and the group sums are added in group order.  Each thread keeps a short chain of
+// loads: the merge is bound by load latency, not bandwidth.
+constexpr int kCombGroups = 4, kCombQuarters = 4, kCombPer = kC / 4 / kCombQuarters;  // 36 threads x 4 dims
 constexpr int kCombThreads = kCombGroups * kCombPer;
 static int comb_groups(int nsplit) { return nsplit >= 32 ? 4 : nsplit >= 16 ? 2 : 1; }
 __global__ void __launch_bounds__(kCombThreads) attn_combine(AttnArgs a, int nsplit) {
-    const int ng = blockDim.x / kCombPer;
+    const int ng = blockDim.x / kCombPer;  // blockDim.x = max(64, ng x 36): wave 0 is whole
     const int64_t rowid = blockIdx.x;
     const int h = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -608,6 +609,7 @@ __global__ void __launch_bounds__(kCombThreads) attn_combine(AttnArgs a, int nsp
     __shared__ float wsp[1024];
     __shared__ float s_mu, s_den;
     __shared__ f32x4 part[kCombGroups - 1][kCombPer][2];
+    const int el = tid % kCombPer;  // this thread's slot in the group exchange
     if (tid < 64) {
         float M = -INFINITY;
         for (int j = lane; j < nsplit; j += 64) M = fmaxf(M, wml[2 * ((j * nrows + rowid) * a.H + h)]);
@@ -630,7 +632,8 @@ __global__ void __launch_bounds__(kCombThreads) attn_combine(AttnArgs a, int nsp
         }
     }
     __syncthreads();
-    const int q = tid / kCombPer, e = tid - q * kCombPer;
+    const int q = tid / kCombPer;
+    const int e = (int)blockIdx.z * kCombPer + (tid - q * kCombPer);  // float4 index in the row
     const int d = 4 * e;
     // RoPE dims 512 + j pair with 544 + j (j < 32)
     const bool rot = a.rope_theta != 0.0 && d >= kDN;
@@ -659,23 +662,25 @@ __global__ void __launch_bounds__(kCombThreads) attn_combine(AttnArgs a, int nsp
         }
         j += ng * kU;
     };
-    while (j + ng * 7 < nsplit) chunk(std::integral_constant<int, 8>());
-    while (j + ng * 3 < nsplit) chunk(std::integral_constant<int, 4>());
-    while (j < nsplit) chunk(std::integral_constant<int, 1>());
-    if (q > 0) {
-        part[q - 1][e][0] = acc;
-        part[q - 1][e][1] = accp;
+    if (q < ng) {  // (padding lanes of a one-group block skip the sums)
+        while (j + ng * 7 < nsplit) chunk(std::integral_constant<int, 8>());
+        while (j + ng * 3 < nsplit) chunk(std::integral_constant<int, 4>());
+        while (j < nsplit) chunk(std::integral_constant<int, 1>());
+    }
+    if (q > 0 && q < ng) {
+        part[q - 1][el][0] = acc;
+        part[q - 1][el][1] = accp;
     }
     __syncthreads();
     if (q > 0) return;
-#pragma unroll
     for (int g = 0; g < ng - 1; ++g) {
-        acc += part[g][e][0];
-        if (rot) accp += part[g][e][1];
+        acc += part[g][el][0];
+        if (rot) accp += part[g][el][1];
     }
     const float den = s_den, mu = s_mu;
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-    if (a.lse && tid == 0) a.lse[rowid * a.H + h] = den > 0.0f ? (mu + log2f(den)) * kLn2 : -INFINITY;
+    if (a.lse && tid == 0 && blockIdx.z == 0)
+        a.lse[rowid * a.H + h] = den > 0.0f ? (mu + log2f(den)) * kLn2 : -INFINITY;
     f32x4 ov = acc * inv;
     if (rot) {
         const int pi = r < kDR / 2 ? r : r - kDR / 2;
@@ -859,8 +864,9 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns <= 1) return e;
-    hipLaunchKernelGGL(attn_combine, dim3((unsigned)rows, (unsigned)a.H), dim3(comb_groups(ns) * kCombPer), 0, st,
-                       a, ns);
+    const int ct = comb_groups(ns) * kCombPer;
+    hipLaunchKernelGGL(attn_combine, dim3((unsigned)rows, (unsigned)a.H, kCombQuarters), dim3(ct < 64 ? 64 : ct), 0,
+                       st, a, ns);
     return hipGetLastError();
 }
 
