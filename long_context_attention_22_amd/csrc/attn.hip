@@ -263,15 +263,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// two fp8 codes (low 16 bits when !high_half) -> packed bf16 bits of code * scale.  The hardware
-// conversion decodes OCP e4m3fn exactly; the power-of-two scale keeps the product exact and a
-// 4-significant-bit value loses nothing when the low 16 bits are dropped.
+// two fp8 codes (low 16 bits when !kHigh) -> packed bf16 bits of code * scale, in one gfx950
+// scaled conversion (v_cvt_scalef32_pk_bf16_fp8).  It decodes OCP e4m3fn exactly and applies the
+// power-of-two scale; a 4-significant-bit product is exact in bf16.  (Checked bit for bit against
+// decode, multiply and truncation to bf16 for every code pair and the scales 2^-20 .. 2^9.)
 template <bool kHigh>
 __device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t codes, float sc) {
-    typedef float f2 __attribute__((ext_vector_type(2)));
-    const f2 v = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes, kHigh);
-    const uint32_t lo = __float_as_uint(v[0] * sc), hi = __float_as_uint(v[1] * sc);
-    return __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, sc, kHigh));
 }
 
 // Expand and store one tile; flags[r] = slot r valid (read back as 32-bit words of 4 slots).
@@ -703,6 +701,371 @@ __global__ void __launch_bounds__(kCombThreads) attn_combine(AttnArgs a, int nsp
     }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Decode-sized launches (fewer than kDecRows query rows).  A launch of one or a few query rows
+// has too little work to fill the chip with one workgroup per (row, split) over all 64 heads, and
+// the partial outputs of many splits would cost more than the rows they cover (64 x 576 f32 per
+// split).  Here a workgroup of four waves serves one (query row, slot split, group of 16 heads):
+// the splits' partial outputs stay 16 x 576, and the four head groups of one (row, split) are
+// launched on the same XCD (workgroups are dealt to the eight XCDs round-robin), so three of the
+// four gathers of each row hit that XCD's L2.
+//   The split's raw rows are fetched into registers up to NP tiles ahead (one HBM round trip
+// before the first tile instead of one per tile); a tile is expanded into one of three LDS
+// buffers (the layout of attn_mfma), so one barrier per tile separates the producers from the
+// readers.  Scores: wave w computes S^T = K Q^T over dims [d0(w), +32 nks(w)) (160, 160, 128 and
+// 128 dims), the four partial sums meet in LDS and every wave adds them in the same order, so
+// all four hold identical scores and softmax states.  Values: wave w owns output dims
+// [144 w, +144), O^T += V^T P^T with P as a bf16 hi + lo pair (as attn_mfma).
+constexpr int kDecRows = 128;      // query rows below which a launch takes the decode kernel
+constexpr int kDecMaxTiles = 8;    // tiles per split at most: the tile loop is unrolled in full
+constexpr int kDecMaxLen = kDecMaxTiles * kKT;
+constexpr int kDecWGs = 256;       // workgroups a decode launch aims for (one per CU)
+
+template <int FMT>
+struct DecRegs {  // one tile's raw rows for this thread
+    static constexpr int kN = FMT == LCA_FP8 ? 1 : 2;  // nope chunks of 16 bytes per row
+    u32x4 v[4][kN];                                    // nope chunk(s) c of rows hw + 8 u (u < 4)
+    u32x4 rp;                                          // RoPE chunk c % 8 of row hw + 8 (c / 8)
+    float sc[4];                                       // fp8: scale group c / 8 of rows hw + 8 u
+    uint32_t ok;                                       // bit u: row hw + 8 u is a valid slot
+};
+
+// Issue the loads of tile [s0, s0 + 32) (nothing is waited for here).  Slot -> row as slot_row;
+// for CSA the entry ids come from LDS.  hw = thread / 32 (eight half-waves), c = thread % 32:
+// 16-byte nope chunk c of rows hw + 8 u (fp8: codes 16c .. 16c+15; bf16: dims 8c .. 8c+7 and
+// 256 + 8c ..), RoPE chunk c % 8 of row hw + 8 (c / 8), scale group c / 8.  Every call issues the
+// same loads with no branch: a slot that is past the end or invalid reads compressed row 0 (its
+// data is dropped in dec_store), so the compiler can count the loads in flight across tiles and
+// each tile waits only for its own rows.  Offsets are 32-bit (the caller checks that every plane
+// of one sequence spans less than 4 GiB).
+template <int FMT, bool DENSE>
+__device__ __forceinline__ void dec_load(DecRegs<FMT>& R, int ncs, int w_row, int s_end, int comp_cap, int win_cap,
+                                         const KvPtrs& P, const int32_t* ent, int s_begin, int s0, int hw,
+                                         int c) {
+    constexpr int kN = DecRegs<FMT>::kN;
+    constexpr uint32_t kRow = FMT == LCA_FP8 ? kDN : 2 * kDN;
+    R.ok = 0;
+    uint32_t rrow = 0;
+    bool rw = false;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int slot = s0 + hw + 8 * u;
+        const bool wnd = slot >= ncs;
+        int r = w_row + (slot - ncs);
+        if (r >= win_cap) r -= win_cap;
+        // (entry ids are read only for slots of this split: the index is clamped for the rest)
+        const int e = DENSE ? slot : ent[min(slot - s_begin, kDecMaxLen - 1)];
+        const bool ok = slot < s_end && (wnd || (uint32_t)e < (uint32_t)comp_cap);
+        const uint32_t row = !ok ? 0u : (uint32_t)(wnd ? r : e);
+        const bool w = ok && wnd;
+        R.ok |= (uint32_t)ok << u;
+        if (u == (c >> 3)) {
+            rrow = row;
+            rw = w;
+        }
+        const GMEM uint8_t* nope = w ? P.nope[1] : P.nope[0];
+        R.v[u][0] = *(const GMEM u32x4*)(nope + (row * kRow + 16u * c));
+        if constexpr (FMT == LCA_FP8) {
+            const GMEM float* scale = w ? P.scale[1] : P.scale[0];
+            R.sc[u] = *(const GMEM float*)((const GMEM uint8_t*)scale + (row * 16u + 4u * (c >> 3)));
+        } else {
+            R.v[u][1] = *(const GMEM u32x4*)(nope + (row * kRow + 16u * c + 512u));
+        }
+    }
+    const GMEM uint16_t* rope = rw ? P.rope[1] : P.rope[0];
+    R.rp = *(const GMEM u32x4*)((const GMEM uint8_t*)rope + (rrow * 128u + 16u * (c & 7)));
+}
+
+// Expand one tile into an LDS buffer (fp8 codes times their power-of-two scale, exact in bf16);
+// rows of invalid slots become zeros; flags[r] = slot r valid.
+template <int FMT>
+__device__ __forceinline__ void dec_store(DecRegs<FMT>& R, uint16_t* Kt, uint8_t* flags, int hw, int c) {
+    constexpr int kN = DecRegs<FMT>::kN;
+    if (__builtin_amdgcn_ballot_w64(R.ok != 0xfu)) {  // wave-uniform
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const bool ok = (R.ok >> u) & 1u;
+#pragma unroll
+            for (int q = 0; q < kN; ++q)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) R.v[u][q][i] = ok ? R.v[u][q][i] : 0u;
+            if constexpr (FMT == LCA_FP8) R.sc[u] = ok ? R.sc[u] : 0.0f;
+        }
+        const bool okr = (R.ok >> (c >> 3)) & 1u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) R.rp[i] = okr ? R.rp[i] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int r = hw + 8 * u;
+        if constexpr (FMT == LCA_FP8) {
+            u32x4 lo, hi;
+            lo[0] = fp8x2_bf16<false>(R.v[u][0][0], R.sc[u]);
+            lo[1] = fp8x2_bf16<true>(R.v[u][0][0], R.sc[u]);
+            lo[2] = fp8x2_bf16<false>(R.v[u][0][1], R.sc[u]);
+            lo[3] = fp8x2_bf16<true>(R.v[u][0][1], R.sc[u]);
+            hi[0] = fp8x2_bf16<false>(R.v[u][0][2], R.sc[u]);
+            hi[1] = fp8x2_bf16<true>(R.v[u][0][2], R.sc[u]);
+            hi[2] = fp8x2_bf16<false>(R.v[u][0][3], R.sc[u]);
+            hi[3] = fp8x2_bf16<true>(R.v[u][0][3], R.sc[u]);
+            put8(Kt, r, 2 * c, lo);
+            put8(Kt, r, 2 * c + 1, hi);
+        } else {
+            put8(Kt, r, c, R.v[u][0]);
+            put8(Kt, r, c + 32, R.v[u][1]);
+        }
+        if (c == 0) flags[r] = (R.ok >> u) & 1u;
+    }
+    put8(Kt, hw + 8 * (c >> 3), kDN / 8 + (c & 7), R.rp);
+}
+
+// Workgroup L: XCD x = L mod 8, j = L / 8; head group j mod ng, unit (j / ng) * 8 + x, where unit =
+// row * nsplit + split.  Grid: ceil(nunits / 8) * 8 * ng workgroups of 256 threads.
+template <int FMT, bool DENSE, int NP>
+__global__ void __launch_bounds__(256) attn_dec(AttnArgs a, int64_t split_len, int nsplit, uint32_t nunits) {
+    __shared__ __attribute__((aligned(16))) uint16_t Kt[3][kTileElems];
+    __shared__ __attribute__((aligned(16))) f32x4 Sx[2][4][2][64];  // partial scores, two tiles
+    __shared__ uint32_t vflag[3][kKT / 4];
+    __shared__ int32_t ent[DENSE ? 1 : kDecMaxLen];
+
+    const uint32_t ng = (uint32_t)a.H >> 4;
+    const uint32_t L = blockIdx.x, jj = L >> 3;
+    const int hg = (int)(jj % ng);
+    const uint32_t unit = (jj / ng) * 8u + (L & 7u);
+    if (unit >= nunits) return;
+    const uint32_t rowu = unit / (uint32_t)nsplit;
+    const int split = (int)(unit - rowu * (uint32_t)nsplit);
+    const int64_t rowid = rowu;
+    int b, ri;
+    row_coords(a, rowid, &b, &ri);
+    int64_t t;
+    const SlotMap sm = slot_map(a, b, ri, &t);
+    // slot bookkeeping in 32 bits (slot counts and ring rows are below 2^31)
+    const int s_begin = split * (int)split_len;
+    const int s_end = (int)min(sm.nslots, (int64_t)s_begin + split_len);
+    const int ntile = s_end > s_begin ? (s_end - s_begin + kKT - 1) / kKT : 0;
+    const int ncs = (int)sm.ncs, w_row = (int)sm.w_row;
+    const int comp_cap = (int)a.comp.cap, win_cap = (int)a.win.cap;
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int n = lane & 15, g4 = lane >> 4;  // MFMA lane coordinates
+    const int hw = tid >> 5, c = tid & 31;     // gather coordinates
+    const int h0 = 16 * hg;
+
+    // Q^T fragments for this wave's score dims: B[k = dim d0 + 32 ks + 8 g4 + e][n = head h0 + n]
+    const int d0 = wv < 2 ? 160 * wv : 320 + 128 * (wv - 2);
+    const int nks = wv < 2 ? 5 : 4;
+    bf16x8 qf[5];
+    {
+        const u32x4* qp = (const u32x4*)((const uint16_t*)a.q + (rowid * a.H + h0 + n) * kC + d0);
+#pragma unroll
+        for (int ks = 0; ks < 5; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, ks < nks ? qp[4 * ks + g4] : u32x4{0u, 0u, 0u, 0u});
+    }
+    if constexpr (!DENSE) {  // this split's entry ids
+        const int lim = min(ncs, s_end);
+        const int nent = lim > s_begin ? lim - s_begin : 0;
+        const GMEM int32_t* irow = sptr<int32_t>(a.idx) + rowid * a.k + s_begin;
+        for (int i = tid; i < nent; i += 256) ent[i] = irow[i];
+        __syncthreads();
+    }
+
+    constexpr int64_t kRowBytes = FMT == LCA_FP8 ? kDN : 2 * kDN;
+    KvPtrs P;
+    P.nope[0] = sptr<uint8_t>(a.comp.nope) + (int64_t)b * a.comp.cap * kRowBytes;
+    P.nope[1] = sptr<uint8_t>(a.win.nope) + (int64_t)b * a.win.cap * kRowBytes;
+    P.rope[0] = sptr<uint16_t>(a.comp.rope) + (int64_t)b * a.comp.cap * kDR;
+    P.rope[1] = sptr<uint16_t>(a.win.rope) + (int64_t)b * a.win.cap * kDR;
+    P.scale[0] = FMT == LCA_FP8 ? sptr<float>(a.comp.scale) + (int64_t)b * a.comp.cap * 4 : nullptr;
+    P.scale[1] = FMT == LCA_FP8 ? sptr<float>(a.win.scale) + (int64_t)b * a.win.cap * 4 : nullptr;
+
+    // (loads of tiles past the end read row 0 and are dropped: the same loads on every path)
+    DecRegs<FMT> R[NP];
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+        dec_load<FMT, DENSE>(R[j], ncs, w_row, s_end, comp_cap, win_cap, P, ent, s_begin, s_begin + j * kKT, hw, c);
+        // (tile by tile, in the order the loop consumes them: the loop's waits count on it)
+        asm volatile("" ::: "memory");
+    }
+    constexpr uint32_t kTileBytes = 2 * kTileElems;
+    uint32_t bq = 0, bn = kTileBytes, bo = 2 * kTileBytes;  // byte offsets: tiles t, t + 1, t - 1
+    int fq = 0, fn = 1;
+    dec_store<FMT>(R[0], &Kt[0][0], (uint8_t*)vflag[0], hw, c);
+    if (NP < kDecMaxTiles)
+        dec_load<FMT, DENSE>(R[0], ncs, w_row, s_end, comp_cap, win_cap, P, ent, s_begin, s_begin + NP * kKT, hw, c);
+#pragma unroll
+    for (int ks = 0; ks < 5; ++ks) asm volatile("" ::"v"(qf[ks]));
+    __syncthreads();
+
+    f32x4 o[9];
+#pragma unroll
+    for (int nb = 0; nb < 9; ++nb) o[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float mrun = -INFINITY, lpart = 0.0f;
+    const float qk_scale = a.sm_scale * kLog2e;
+    const int koff = n * kKS + d0 + 8 * g4;
+    const int dbase = 144 * wv;
+    const uint32_t vbase = lds_addr(&Kt[0][0]) + 2 * ((4 * g4 + (n >> 2)) * kKS + dbase + 4 * (n & 3));
+
+    // The tile loop is unrolled in full (at most kDecMaxTiles tiles): with no back edge the
+    // compiler counts the loads in flight exactly, and tile t + 1 waits only for its own rows.
+#pragma unroll
+    for (int t = 0; t < kDecMaxTiles; ++t) {
+        {
+            if (t >= ntile) break;
+            // partial scores of tile t over this wave's dims
+            f32x4 s[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+            {
+                const uint16_t* kr = (const uint16_t*)((const char*)&Kt[0][0] + bq) + koff;
+#pragma unroll
+                for (int ks = 0; ks < 5; ++ks) {
+                    if (ks < nks) {
+                        const bf16x8 k0 = __builtin_bit_cast(bf16x8, *(const u32x4*)(kr + 32 * ks));
+                        const bf16x8 k1 = __builtin_bit_cast(bf16x8, *(const u32x4*)(kr + 16 * kKS + 32 * ks));
+                        s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[ks], s[0], 0, 0, 0);
+                        s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[ks], s[1], 0, 0, 0);
+                    }
+                }
+            }
+            Sx[t & 1][wv][0][lane] = s[0];
+            Sx[t & 1][wv][1][lane] = s[1];
+            // tile t + 1 into the buffer tile t - 2 used; its registers take tile t + 1 + NP (after
+            // the last tile: a harmless store of dropped rows into the free buffer)
+            if (t + 1 < kDecMaxTiles) {
+                DecRegs<FMT>& Rn = R[(t + 1) % NP];
+                dec_store<FMT>(Rn, (uint16_t*)((char*)&Kt[0][0] + bn), (uint8_t*)vflag[fn], hw, c);
+                if (t + 1 + NP < kDecMaxTiles)
+                    dec_load<FMT, DENSE>(Rn, ncs, w_row, s_end, comp_cap, win_cap, P, ent, s_begin,
+                                         s_begin + (t + 1 + NP) * kKT, hw, c);
+            }
+            __syncthreads();
+            // the four partial sums in a fixed order: identical scores in every wave
+            f32x4 sc0 = Sx[t & 1][0][0][lane], sc1 = Sx[t & 1][0][1][lane];
+#pragma unroll
+            for (int w = 1; w < 4; ++w) {
+                sc0 += Sx[t & 1][w][0][lane];
+                sc1 += Sx[t & 1][w][1][lane];
+            }
+            {
+                const uint32_t f0 = vflag[fq][g4], f1 = vflag[fq][4 + g4];
+                if (__builtin_amdgcn_ballot_w64((f0 & f1) != 0x01010101u)) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        if (!((f0 >> (8 * i)) & 1u)) sc0[i] = -INFINITY;
+                        if (!((f1 >> (8 * i)) & 1u)) sc1[i] = -INFINITY;
+                    }
+                }
+            }
+            const float smax = fmaxf(fmaxf(fmaxf(sc0[0], sc0[1]), fmaxf(sc0[2], sc0[3])),
+                                     fmaxf(fmaxf(sc1[0], sc1[1]), fmaxf(sc1[2], sc1[3])));
+            const float tmax = max4g(smax) * qk_scale;
+            const bool grow = __builtin_amdgcn_ballot_w64(tmax > mrun + 8.0f) != 0;  // lazy rescale, as attn_mfma
+            const float mnew = grow ? fmaxf(mrun, tmax) : mrun;
+            const float corr = mnew == mrun ? 1.0f : exp2f(mrun - mnew);
+            mrun = mnew;
+            const float mneg = mrun == -INFINITY ? 0.0f : -mrun;
+            float p[2][4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[0][i] = __builtin_amdgcn_exp2f(fmaf(sc0[i], qk_scale, mneg));
+                p[1][i] = __builtin_amdgcn_exp2f(fmaf(sc1[i], qk_scale, mneg));
+            }
+            lpart = lpart * corr +
+                    (((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) + ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3])));
+            uint32_t ph[4], pl[4];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const float x0 = p[kb][2 * q], x1 = p[kb][2 * q + 1];
+                    const uint32_t hb = pk_bf16(x0, x1);
+                    ph[2 * kb + q] = hb;
+                    pl[2 * kb + q] = pk_bf16(x0 - __uint_as_float(hb << 16), x1 - __uint_as_float(hb & 0xffff0000u));
+                }
+            const bf16x8 pa = __builtin_bit_cast(bf16x8, u32x4{ph[0], ph[1], ph[2], ph[3]});
+            const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
+            if (grow) {
+                asm volatile("");
+#pragma unroll
+                for (int nb = 0; nb < 9; ++nb) o[nb] *= corr;
+            }
+            {
+                const uint32_t vr = vbase + bq;
+#pragma unroll
+                for (int nb = 0; nb < 9; ++nb) {
+                    const s16x4 w0 = lds_tr16(vr + 32 * nb);
+                    const s16x4 w1 = lds_tr16(vr + 32 * kKS + 32 * nb);
+                    const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7));
+                    o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pa, o[nb], 0, 0, 0);
+                    o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[nb], 0, 0, 0);
+                }
+            }
+            const uint32_t bt = bo;
+            bo = bq;
+            bq = bn;
+            bn = bt;
+            fq = fn;
+            fn = fn == 2 ? 0 : fn + 1;
+        }
+    }
+    const float lrun = sum4g(lpart);
+
+    // epilogue: head h = h0 + n, dims dbase + 16 nb + 4 g4 + i
+    const int h = h0 + n;
+    const int64_t nrows = (int64_t)a.B * a.T;
+    if (nsplit > 1) {
+        float* wo = (float*)a.ws;
+        float* wml = wo + (int64_t)nsplit * nrows * a.H * kC;
+        const int64_t pr = ((int64_t)split * nrows + rowid) * a.H + h;
+        float* dst = wo + pr * kC + dbase + 4 * g4;
+#pragma unroll
+        for (int nb = 0; nb < 9; ++nb) *(f32x4*)(dst + 16 * nb) = o[nb];
+        if (g4 == 0 && wv == 0) {
+            wml[2 * pr] = mrun;
+            wml[2 * pr + 1] = lrun;
+        }
+        return;
+    }
+    float mu = mrun, den = lrun;
+    if (a.sink) {
+        const float z = a.sink[h] * kLog2e;
+        mu = fmaxf(mrun, z);
+        den = (mrun == -INFINITY ? 0.0f : lrun * exp2f(mrun - mu)) + exp2f(z - mu);
+    }
+    const float f = den > 0.0f && mrun != -INFINITY ? exp2f(mrun - mu) / den : 0.0f;
+#pragma unroll
+    for (int nb = 0; nb < 9; ++nb) o[nb] *= f;
+    // output RoPE by -t: wave 3 holds dims 432 ..; 512 + j and 544 + j (j = 16 q2 + 4 g4 + i) are
+    // blocks 5 + q2 and 7 + q2
+    if (a.rope_theta != 0.0 && wv == 3) {
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float sn, cs;
+                rope_sincos(a.rope.inv, 16 * q2 + 4 * g4 + i, -(double)t, &sn, &cs);
+                const float x0 = o[5 + q2][i], x1 = o[7 + q2][i];
+                o[5 + q2][i] = x0 * cs - x1 * sn;
+                o[7 + q2][i] = x0 * sn + x1 * cs;
+            }
+    }
+    const int64_t orow = (rowid * a.H + h) * kC + dbase + 4 * g4;
+    if (a.out_dtype == LCA_F32) {
+        float* dst = (float*)a.out + orow;
+#pragma unroll
+        for (int nb = 0; nb < 9; ++nb) *(f32x4*)(dst + 16 * nb) = o[nb];
+    } else {
+        uint16_t* dst = (uint16_t*)a.out + orow;
+#pragma unroll
+        for (int nb = 0; nb < 9; ++nb) {
+            uint2 w;
+            w.x = (uint32_t)f2bf(o[nb][0]) | ((uint32_t)f2bf(o[nb][1]) << 16);
+            w.y = (uint32_t)f2bf(o[nb][2]) | ((uint32_t)f2bf(o[nb][3]) << 16);
+            *(uint2*)(dst + 16 * nb) = w;
+        }
+    }
+    if (a.lse && g4 == 0 && wv == 0)
+        a.lse[rowid * a.H + h] = den > 0.0f ? (mu + log2f(den)) * kLn2 : -INFINITY;
+}
+
 // f32 caches: one wave per (row, head); lane owns dims lane + 64 u.
 __global__ void __launch_bounds__(64) attn_f32(AttnArgs a) {
     const int64_t rowid = blockIdx.x;
@@ -779,33 +1142,75 @@ __global__ void __launch_bounds__(64) attn_f32(AttnArgs a) {
     if (a.lse && lane == 0) a.lse[rowid * a.H + h] = den > 0.0f ? (mu + log2f(den)) * kLn2 : -INFINITY;
 }
 
-// Split policy: decode-sized launches split the slot list so that the grid
-// covers the chip; prefill-sized launches use one split per row.
-#ifndef LCA_SPLIT_TARGET
-#define LCA_SPLIT_TARGET 256   // workgroups a decode-sized launch aims for (one per CU)
-#endif
-#ifndef LCA_SPLIT_MIN_SLOTS
-#define LCA_SPLIT_MIN_SLOTS 128  // fewest slots per split
-#endif
-int attn_num_splits(int64_t rows, int64_t max_keys, int32_t c) {
-    if (c != kC || rows >= 128 || max_keys <= LCA_SPLIT_MIN_SLOTS) return 1;
-    int64_t want = (LCA_SPLIT_TARGET + rows - 1) / rows;
-    int64_t most = (max_keys + LCA_SPLIT_MIN_SLOTS - 1) / LCA_SPLIT_MIN_SLOTS;
-    if (want > most) want = most;
-    if (want > 1024) want = 1024;           // combine keeps the split weights in LDS
-    if (want < 1) want = 1;
-    int64_t len = (max_keys + want - 1) / want;
-    len = (len + kKT - 1) / kKT * kKT;
-    return (int)((max_keys + len - 1) / len);
+// Split policy.  Short launches (rows x head groups <= kDecMaxUnits) take attn_dec: the slot list
+// is cut into ns_t = kDecWGs / (rows x head groups) splits of whole tiles (32 .. kDecMaxLen
+// slots), so that the launch comes near kDecWGs workgroups.  Other launches of fewer than kDecRows
+// rows take attn_mfma (64 heads per workgroup, which amortises each gathered tile over four times
+// the work) with up to ceil(256 / rows) splits of at least 128 slots; longer launches one split
+// per row.  Either way the split count never exceeds a bound that does not fall as max_keys grows
+// (dec: max(ns_t, ceil(max_keys / kDecMaxLen)); split: ceil(256 / rows)), which the workspace size
+// for "at most max_keys" rows uses.
+constexpr int kDecMaxUnits = 64;
+struct AttnPlan {
+    bool dec;
+    int nsplit;
+    int64_t len;  // slots per split
+};
+static bool dec_eligible(int64_t rows, int32_t H, int32_t c) {
+    return c == kC && H >= 16 && rows * (H / 16) <= kDecMaxUnits;
+}
+static bool split_eligible(int64_t rows, int32_t c) { return c == kC && rows < kDecRows; }
+static int64_t dec_target(int64_t rows, int32_t H) {
+    const int64_t per = rows * (H / 16);  // workgroups per split index
+    return per >= kDecWGs ? 1 : kDecWGs / per;
+}
+static int64_t split_target(int64_t rows) { return (kDecWGs + rows - 1) / rows; }
+static AttnPlan attn_plan(int64_t rows, int32_t H, int32_t c, int64_t max_keys) {
+    AttnPlan p = {false, 1, (max_keys + kKT - 1) / kKT * kKT};
+    if (dec_eligible(rows, H, c)) {
+        const int64_t nt = dec_target(rows, H);
+        int64_t len = (max_keys + nt - 1) / nt;
+        len = (len + kKT - 1) / kKT * kKT;
+        if (len < kKT) len = kKT;
+        if (len > kDecMaxLen) len = kDecMaxLen;
+        int64_t ns = (max_keys + len - 1) / len;
+        if (ns < 1) ns = 1;
+        if (ns <= 1024) {  // (the merge keeps the split weights in LDS)
+            p.dec = true;
+            p.nsplit = (int)ns;
+            p.len = len;
+        }
+        return p;
+    }
+    if (split_eligible(rows, c) && max_keys > 128) {
+        int64_t want = split_target(rows);
+        const int64_t most = (max_keys + 127) / 128;
+        if (want > most) want = most;
+        if (want > 1024) want = 1024;
+        int64_t len = (max_keys + want - 1) / want;
+        len = (len + kKT - 1) / kKT * kKT;
+        p.nsplit = (int)((max_keys + len - 1) / len);
+        p.len = len;
+    }
+    return p;
 }
 
-static int64_t split_len_of(int64_t max_keys, int nsplit) {
-    int64_t len = (max_keys + nsplit - 1) / nsplit;
-    return (len + kKT - 1) / kKT * kKT;
+size_t attn_ws_need(int64_t rows, int32_t H, int32_t c, int64_t max_keys) {
+    const AttnPlan p = attn_plan(rows, H, c, max_keys);
+    if (p.nsplit <= 1) return 0;
+    return (size_t)p.nsplit * rows * H * (c + 2) * sizeof(float);
 }
 
 size_t attn_ws_bytes(int64_t rows, int32_t H, int32_t c, int64_t max_keys) {
-    const int ns = attn_num_splits(rows, max_keys, c);
+    int64_t ns = 1;
+    if (dec_eligible(rows, H, c)) {
+        ns = dec_target(rows, H);
+        const int64_t hi = (max_keys + kDecMaxLen - 1) / kDecMaxLen;
+        if (hi > ns) ns = hi;
+    } else if (split_eligible(rows, c)) {
+        ns = split_target(rows);
+    }
+    if (ns > 1024) ns = 1024;
     if (ns <= 1) return 0;
     return (size_t)ns * rows * H * (c + 2) * sizeof(float);
 }
@@ -851,16 +1256,32 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
         hipLaunchKernelGGL(attn_f32, dim3((unsigned)rows, (unsigned)a.H), dim3(64), 0, st, a);
         return hipGetLastError();
     }
-    const int ns = attn_num_splits(rows, a.max_keys, c);
-    const int64_t len = ns > 1 ? split_len_of(a.max_keys, ns) : (a.max_keys + kKT - 1) / kKT * kKT;
-    dim3 grid((unsigned)rows, (unsigned)ns);
+    const AttnPlan p = attn_plan(rows, a.H, c, a.max_keys);
+    const int ns = p.nsplit;
     const bool dense = a.idx == nullptr;
-    if (a.comp.fmt == LCA_FP8) {
-        if (dense) hipLaunchKernelGGL((attn_mfma<LCA_FP8, true>), grid, dim3(512), 0, st, a, len, ns);
-        else hipLaunchKernelGGL((attn_mfma<LCA_FP8, false>), grid, dim3(512), 0, st, a, len, ns);
+    // attn_dec addresses one sequence's rows with 32-bit offsets; larger planes take attn_mfma
+    // (same splits, same workspace layout)
+    const int64_t rb = a.comp.fmt == LCA_FP8 ? kDN : 2 * kDN;
+    const bool off32 = a.comp.cap * rb < ((int64_t)1 << 32) && a.win.cap * rb < ((int64_t)1 << 32);
+    if (p.dec && off32) {
+        const uint32_t nunits = (uint32_t)(rows * ns);
+        dim3 grid((unsigned)((nunits + 7) / 8 * 8 * (uint32_t)(a.H / 16)));
+        if (a.comp.fmt == LCA_FP8) {
+            if (dense) hipLaunchKernelGGL((attn_dec<LCA_FP8, true, 4>), grid, dim3(256), 0, st, a, p.len, ns, nunits);
+            else hipLaunchKernelGGL((attn_dec<LCA_FP8, false, 4>), grid, dim3(256), 0, st, a, p.len, ns, nunits);
+        } else {
+            if (dense) hipLaunchKernelGGL((attn_dec<LCA_BF16, true, 3>), grid, dim3(256), 0, st, a, p.len, ns, nunits);
+            else hipLaunchKernelGGL((attn_dec<LCA_BF16, false, 3>), grid, dim3(256), 0, st, a, p.len, ns, nunits);
+        }
     } else {
-        if (dense) hipLaunchKernelGGL((attn_mfma<LCA_BF16, true>), grid, dim3(512), 0, st, a, len, ns);
-        else hipLaunchKernelGGL((attn_mfma<LCA_BF16, false>), grid, dim3(512), 0, st, a, len, ns);
+        dim3 grid((unsigned)rows, (unsigned)ns);
+        if (a.comp.fmt == LCA_FP8) {
+            if (dense) hipLaunchKernelGGL((attn_mfma<LCA_FP8, true>), grid, dim3(512), 0, st, a, p.len, ns);
+            else hipLaunchKernelGGL((attn_mfma<LCA_FP8, false>), grid, dim3(512), 0, st, a, p.len, ns);
+        } else {
+            if (dense) hipLaunchKernelGGL((attn_mfma<LCA_BF16, true>), grid, dim3(512), 0, st, a, p.len, ns);
+            else hipLaunchKernelGGL((attn_mfma<LCA_BF16, false>), grid, dim3(512), 0, st, a, p.len, ns);
+        }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns <= 1) return e;

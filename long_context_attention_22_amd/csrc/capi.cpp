@@ -268,7 +268,7 @@ static int attn_common(const void* q, int32_t q_dtype, int32_t H, int32_t B, int
         }
         if (keys > max_keys) max_keys = keys;
     }
-    const size_t need = lca::attn_ws_bytes((int64_t)B * T, H, c, max_keys);
+    const size_t need = lca::attn_ws_need((int64_t)B * T, H, c, max_keys);
     if (need > 0 && (!ws || ws_bytes < need))
         return fail(LCA_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
     lca::AttnArgs a;
@@ -292,7 +292,7 @@ static int attn_common(const void* q, int32_t q_dtype, int32_t H, int32_t B, int
     // min(n_win - 1, q_pos) + T rows), when the workspace holds them; otherwise the attention
     // expands per tile.
     if (!idx && comp.fmt == LCA_FP8 && (int64_t)B * T >= lca::kExpandMinRows &&
-        lca::attn_ws_bytes((int64_t)B * T, H, c, max_keys) == 0) {
+        lca::attn_ws_need((int64_t)B * T, H, c, max_keys) == 0) {
         int64_t cap_c = 1, cap_w = 1;
         for (int b = 0; b < B; ++b) {
             const int64_t vis = (q_pos[b] + T) / m;

@@ -104,7 +104,9 @@ struct ExpandArgs {
 };
 hipError_t launch_kv_expand(const ExpandArgs& a, hipStream_t st);
 constexpr int64_t kExpandMinRows = 128;  // query rows from which a dense launch expands its rows
-int attn_num_splits(int64_t rows, int64_t max_keys, int32_t c);
+// workspace bytes a launch with this max_keys needs, and an upper bound for every launch with at
+// most max_keys attended rows per query
+size_t attn_ws_need(int64_t rows, int32_t H, int32_t c, int64_t max_keys);
 size_t attn_ws_bytes(int64_t rows, int32_t H, int32_t c, int64_t max_keys);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
 

@@ -26,6 +26,15 @@ def L():
     return lca.lib()
 
 
+@pytest.fixture(scope="module")
+def no_gpu():
+    """Calls that pass validation launch a kernel on the fake pointers: only where no GPU is visible
+    (the launch then fails with LCA_EHIP)."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible: a valid call would launch on fake pointers")
+
+
 def _declared():
     txt = open(os.path.join(ROOT, "include", "lca.h")).read()
     return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(lca_\w+)\s*\(", txt, re.M)))
@@ -146,7 +155,29 @@ def test_attn_validation(L):
     need = L.lca_attn_workspace_size(1, 1, 64, 576, 1152)
     assert need > 0
     assert attn(L, T=1, q_pos=pos(4000), k=1024) == 5
-    assert attn(L, T=1, q_pos=pos(4000), k=1024, ws=FAKE2, wsb=need - 1) == 5
+    assert attn(L, T=1, q_pos=pos(4000), k=1024, ws=FAKE2, wsb=64) == 5
+
     # prefill: one split per row; the size covers the optional bf16 expansion of a dense launch's
     # rows (2 max_keys + T rows of 1152 bytes)
     assert L.lca_attn_workspace_size(1, 4096, 64, 576, 2176) == (2 * 2176 + 4096) * 1152
+
+
+@pytest.mark.parametrize("B,T,H", [(1, 1, 64), (1, 1, 16), (32, 1, 64), (3, 5, 48), (1, 127, 64)])
+def test_attn_workspace_covers_smaller_launches(L, no_gpu, B, T, H):
+    """lca_attn_workspace_size(..., M) covers every launch with at most M attended rows per query: no
+    such launch is refused for its workspace (it passes validation and only then fails to launch,
+    here without a GPU).  The split count is not monotone in the row count; the size is."""
+    m, n_win, M = 4, 128, 4224
+    need = L.lca_attn_workspace_size(B, T, H, 576, M)
+    sizes = []
+    for qp in range(0, 4 * (M - n_win) - T, 37):          # HCA: vis + window grows with the position
+        rc = attn(L, csa=False, B=B, T=T, H=H, q_pos=pos(*([qp] * B)), m=m, comp=kv(cap=M), win=kv(cap=512),
+                  ws=FAKE2, wsb=need)
+        assert rc != 5, (qp, L.lca_last_error())
+        sizes.append(L.lca_attn_workspace_size(B, T, H, 576, min(M, (qp + T) // m + n_win)))
+    for k in list(range(1, 300, 7)) + [1024, 2048, M - n_win]:   # CSA: k + window
+        rc = attn(L, B=B, T=T, H=H, q_pos=pos(*([100000] * B)), k=k, comp=kv(cap=1 << 16), win=kv(cap=512),
+                  ws=FAKE2, wsb=need)
+        assert rc != 5, (k, L.lca_last_error())
+    assert max(sizes) <= need
+    assert sizes == sorted(sizes)

@@ -195,6 +195,41 @@ def test_attention(fmt, mode, B, T, q_pos, k):
     assert np.all(np.abs(gb - o) <= 2e-2 + np.abs(o) * 2 ** -8)
 
 
+@pytest.mark.parametrize("H", [16, 48])
+@pytest.mark.parametrize("mode", ["csa", "hca"])
+def test_attention_decode_shapes(mode, H):
+    """Short launches (few rows x head groups) take the split decode kernel: fewer than 64 heads,
+    a window ring that wraps inside the attended range, splits ending mid-tile."""
+    B, T, n_win, m = 2, 2, 128, 4 if mode == "csa" else 16
+    q_pos = [3001, 5000]
+    ncomp = (max(q_pos) + T) // m + 1
+    comp = _cache(51, B, ncomp, orc.FP8, "comp")
+    win_cap = n_win + T + 3                       # rows p live at p mod 133: the window wraps
+    win = _cache(52, B, win_cap, orc.FP8, "win")
+    q = _q(53, B, T, H)
+    sink = S.normal(54, "sink", (H,))
+    idx, k = None, 600
+    if mode == "csa":
+        sc = S.normal(55, "sc", (B, T, ncomp))
+        idx = orc.topk_select(sc, q_pos=q_pos, m=m, k=k)
+    scale = 1.0 / np.sqrt(576)
+    o, lse = orc.attention(q, q_pos=q_pos, comp=comp, m=m, idx=idx, win=win, n_win=n_win, sink=sink,
+                           sm_scale=scale, rope_theta=10000.0)
+    maxk = (k if mode == "csa" else ncomp) + n_win
+    ws = torch.empty(max(16, lca.attn_workspace_size(B, T, H, 576, maxk)), dtype=torch.uint8, device="cuda")
+    out = torch.zeros(B, T, H, 576, dtype=torch.float32, device="cuda")
+    lg = torch.zeros(B, T, H, dtype=torch.float32, device="cuda")
+    kw = dict(q_pos=q_pos, comp=kv_dev(comp), m=m, win=kv_dev(win), n_win=n_win, sink=dev(sink),
+              sm_scale=scale, rope_theta=10000.0, lse=lg, ws=ws)
+    if mode == "csa":
+        lca.csa_attn(dev(q), out, idx=dev(idx), **kw)
+    else:
+        lca.hca_attn(dev(q), out, **kw)
+    err = np.abs(host(out) - o).max()
+    assert err <= 2e-2, err
+    np.testing.assert_allclose(host(lg), lse, atol=1e-3, rtol=1e-4)
+
+
 def test_attention_f32_path():
     """Tiny fp32 shapes (8 heads of 48 + 16): f32 caches, f32 queries, 1e-4."""
     B, T, H, dn, dr, m, n_win = 1, 256, 8, 48, 16, 4, 32
@@ -241,7 +276,9 @@ def test_attention_nan_poison_and_empty():
     gw.scale[:, q_pos[0] + T:] = float("nan")      # future window rows
     gw.scale[:, :q_pos[0] - n_win + 1] = float("nan")
     out = torch.zeros(B, T, H, 576, dtype=torch.float32, device="cuda")
-    lca.hca_attn(dev(q), out, q_pos=q_pos, comp=gc, m=m, win=gw, n_win=n_win, sm_scale=0.05)
+    ws = torch.empty(max(16, lca.attn_workspace_size(B, T, H, 576, vis_last + n_win)), dtype=torch.uint8,
+                     device="cuda")
+    lca.hca_attn(dev(q), out, q_pos=q_pos, comp=gc, m=m, win=gw, n_win=n_win, sm_scale=0.05, ws=ws)
     g = host(out)
     assert np.isfinite(g).all()
     assert np.abs(g - o).max() <= 2e-2
