@@ -300,19 +300,6 @@ __device__ __forceinline__ void store_tile(const Gather<FMT, DENSE>& g, uint16_t
     }
 }
 
-__device__ __forceinline__ float xlane32(float v, bool mx) {  // combine with lane ^ 32
-    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    const float a = __uint_as_float(p[0]), b = __uint_as_float(p[1]);
-    return mx ? fmaxf(a, b) : a + b;
-}
-__device__ __forceinline__ float xlane16(float v, bool mx) {  // combine with lane ^ 16
-    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    const float a = __uint_as_float(p[0]), b = __uint_as_float(p[1]);
-    return mx ? fmaxf(a, b) : a + b;
-}
-// over the four 16-lane groups: every lane gets the same value, summed in the same order
-__device__ __forceinline__ float max4g(float v) { return xlane32(xlane16(v, true), true); }
-__device__ __forceinline__ float sum4g(float v) { return xlane32(xlane16(v, false), false); }
 
 __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

@@ -76,13 +76,24 @@ __device__ __forceinline__ float sum16(float v) {
 }
 
 // RoPE rotation for pair i at position pos: inv[i] = theta^(-2i/d_rope) is computed on the
-// host in fp64; the angle pos * inv[i] is formed and reduced to [-pi, pi] in fp64 (positions
-// reach 2^20 and beyond), then sin / cos are taken in fp32.
+// host in fp64; the angle pos * inv[i] is formed and reduced by the nearest multiple k of pi/2 in
+// fp64 (positions reach 2^20 and beyond), and sin / cos of the remainder |x| <= pi/4 come from
+// their Taylor series in fp32 (terms to x^9 / x^10: truncation below 2e-10, far under one f32
+// ulp), placed in the quadrant k mod 4.  A few dozen instructions instead of a library sincos,
+// whose general argument reduction would be dead code here.
 __device__ __forceinline__ void rope_sincos(const double* inv, int i, double pos, float* sn, float* cs) {
-    double ang = pos * inv[i];
-    const double two_pi = 6.283185307179586476925;
-    ang = ang - two_pi * rint(ang * (1.0 / two_pi));
-    sincosf((float)ang, sn, cs);
+    const double ang = pos * inv[i];
+    const double k = rint(ang * 0.63661977236758134308);  // 2 / pi
+    const float x = (float)(ang - k * 1.57079632679489661923);
+    const float x2 = x * x;
+    const float sp = x * fmaf(x2, fmaf(x2, fmaf(x2, fmaf(x2, 1.0f / 362880.0f, -1.0f / 5040.0f), 1.0f / 120.0f),
+                                       -1.0f / 6.0f), 1.0f);
+    const float cp = fmaf(x2, fmaf(x2, fmaf(x2, fmaf(x2, fmaf(x2, -1.0f / 3628800.0f, 1.0f / 40320.0f), -1.0f / 720.0f),
+                                        1.0f / 24.0f), -0.5f), 1.0f);
+    const int q = (int)((int64_t)k & 3);
+    const float s0 = (q & 1) ? cp : sp, c0 = (q & 1) ? sp : cp;
+    *sn = (q & 2) ? -s0 : s0;
+    *cs = ((q + 1) & 2) ? -c0 : c0;
 }
 
 // 16-lane (one MFMA column group) reductions with DPP row rotations: every lane of the
@@ -105,5 +116,23 @@ __device__ __forceinline__ float row_sum16(float v) {
     v += dpp<0xb1>(v);
     return v;
 }
+
+// Cross-row exchanges of gfx950 (v_permlane16_swap / v_permlane32_swap), no LDS traffic.
+__device__ __forceinline__ float xlane32(float v, bool mx) {  // combine with lane ^ 32
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const float a = __uint_as_float(p[0]), b = __uint_as_float(p[1]);
+    return mx ? fmaxf(a, b) : a + b;
+}
+__device__ __forceinline__ float xlane16(float v, bool mx) {  // combine with lane ^ 16
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const float a = __uint_as_float(p[0]), b = __uint_as_float(p[1]);
+    return mx ? fmaxf(a, b) : a + b;
+}
+// over the four 16-lane groups: every lane gets the same value, summed in the same order
+__device__ __forceinline__ float max4g(float v) { return xlane32(xlane16(v, true), true); }
+__device__ __forceinline__ float sum4g(float v) { return xlane32(xlane16(v, false), false); }
+// whole-wave reductions without LDS: DPP within each 16-lane row, then the row swaps
+__device__ __forceinline__ float wave_max_dpp(float v) { return max4g(row_max16(v)); }
+__device__ __forceinline__ float wave_sum_dpp(float v) { return sum4g(row_sum16(v)); }
 
 }  // namespace lca

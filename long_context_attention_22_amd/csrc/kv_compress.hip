@@ -145,12 +145,158 @@ __global__ void __launch_bounds__(1024) kv_compress_kernel(CompressArgs a) {
     }
 }
 
+// m = 1 (the window / state-cache store, [R] 2.3.3 and 3.5.1): the softmax over one position is 1,
+// so the entry is the row itself, then RMSNorm, RoPE and the store.  One wave per row, lane l
+// owns channels l + 64 j (j < J): every reduction is a wave reduction.  This store is one small
+// launch per layer and decode token, so its latency is what counts: every argument is read at
+// the top, before the first branch (the scalar loads go out in one batch instead of a chain of
+// round trips), and the row, gamma and the RoPE frequencies are loaded in one round.
+template <typename T, int FMT, int J>
+__global__ void __launch_bounds__(64) kv_store_rows(CompressArgs a) {
+    const int b = blockIdx.y, lane = threadIdx.x;
+    const int64_t p0 = a.first_pos.v[b], s = a.s_lo.v[b] + blockIdx.x, n_rows = a.n_rows;
+    const int d_nope = a.out.d_nope, d_rope = a.out.d_rope, c = d_nope + d_rope;
+    const int64_t in_stride = a.in_stride, cap = a.out.cap;
+    const T* c_a = (const T*)a.c_a;
+    const float* gamma = a.gamma;
+    const float eps = a.eps;
+    const bool rope = a.rope_theta != 0.0 && d_rope > 0;
+    const int ring = a.ring;
+    void* const onope = a.out.nope;
+    void* const orope = a.out.rope;
+    float* const oscale = a.out.scale;
+    const int half = d_rope >> 1;
+    // this lane's RoPE pair index (channel d_nope + lane, when lane < d_rope <= 64)
+    const int ri = half > 0 ? (lane < half ? lane : lane - half) : 0;
+    const double inv = a.rope.inv[ri < kMaxRopeHalf ? ri : 0];
+    asm volatile("" ::"s"(p0), "s"(s), "s"(n_rows), "s"(d_nope), "s"(d_rope), "s"(in_stride), "s"(cap), "s"(c_a),
+                 "s"(gamma), "s"(eps), "s"(ring), "s"(onope), "s"(orope), "s"(oscale));
+    // (a workgroup past the last row reads row 0 of its sequence and stores nothing)
+    const bool live = s < p0 + n_rows;
+    const T* src = c_a + ((int64_t)b * in_stride + (live ? s - p0 : 0)) * c;
+    // (channels past c load channel c - 1 and are zeroed: no branch around the loads)
+    float y[J], g[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int ch = lane + 64 * j;
+        const float v = ldin(src, ch < c ? ch : c - 1);
+        y[j] = ch < c ? v : 0.0f;
+    }
+    if (gamma) {
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int ch = lane + 64 * j;
+            const float v = gamma[ch < c ? ch : c - 1];
+            g[j] = ch < c ? v : 0.0f;
+        }
+    }
+    if (!live) return;
+    if (gamma) {
+        float ss = 0.0f;
+#pragma unroll
+        for (int j = 0; j < J; ++j) ss = fmaf(y[j], y[j], ss);
+        const float r = 1.0f / sqrtf(wave_sum_dpp(ss) / (float)c + eps);
+#pragma unroll
+        for (int j = 0; j < J; ++j) y[j] = g[j] * y[j] * r;
+    }
+    if (rope) {
+        // channels d_nope .. c - 1 through LDS: lane l < d_rope rotates channel d_nope + l with its
+        // partner d_nope + (l +- half) (d_rope <= 64 in this kernel's shapes)
+        __shared__ float ys[64 * J];
+#pragma unroll
+        for (int j = 0; j < J; ++j) ys[lane + 64 * j] = y[j];
+        __syncthreads();
+        float rot = 0.0f;
+        if (lane < d_rope) {
+            float sn, cs;
+            const double ang = (double)s;
+            rope_sincos(&inv, 0, ang, &sn, &cs);
+            const float x = ys[d_nope + lane];
+            rot = lane < half ? x * cs - ys[d_nope + lane + half] * sn : ys[d_nope + lane - half] * sn + x * cs;
+        }
+        __syncthreads();
+        if (lane < d_rope) ys[d_nope + lane] = rot;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+            if (lane + 64 * j >= d_nope) y[j] = ys[lane + 64 * j];
+    }
+    const int64_t row = (int64_t)b * cap + (ring ? s % cap : s);
+    if (FMT == LCA_FP8) {
+        // power-of-two scale per 128 nope dims (d_nope % 128 == 0): channels 128 g .. are j = 2g, 2g+1
+        float isc[J / 2 + 1];  // 1 / scale, exact
+#pragma unroll
+        for (int g2 = 0; 2 * g2 < J; ++g2) {
+            float am = 0.0f;
+            if (128 * g2 < d_nope) {
+                am = fabsf(y[2 * g2]);
+                if (2 * g2 + 1 < J) am = fmaxf(am, fabsf(y[2 * g2 + 1]));
+            }
+            const float amax = wave_max_dpp(am);
+            int e8 = 0;  // scale = 2^e8
+            if (amax > 0.0f) {
+                int ex = 0;
+                frexpf(amax, &ex);  // amax in [2^(ex-1), 2^ex)
+                const int e = ex - 1;
+                e8 = (amax <= ldexpf(1.75f, e)) ? e - 8 : e - 7;
+            }
+            isc[g2] = ldexpf(1.0f, -e8);
+            if (lane == 0 && 128 * g2 < d_nope) oscale[row * (d_nope >> 7) + g2] = ldexpf(1.0f, e8);
+        }
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int ch = lane + 64 * j;
+            if (ch < d_nope)
+                ((uint8_t*)onope)[row * d_nope + ch] = (uint8_t)f32_to_fp8(y[j] * isc[j >> 1]);
+            else if (ch < c)
+                ((uint16_t*)orope)[row * d_rope + (ch - d_nope)] = f2bf(y[j]);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int ch = lane + 64 * j;
+            if (FMT == LCA_BF16) {
+                if (ch < d_nope) ((uint16_t*)onope)[row * d_nope + ch] = f2bf(y[j]);
+                else if (ch < c) ((uint16_t*)orope)[row * d_rope + (ch - d_nope)] = f2bf(y[j]);
+            } else {
+                if (ch < d_nope) ((float*)onope)[row * d_nope + ch] = y[j];
+                else if (ch < c) ((float*)orope)[row * d_rope + (ch - d_nope)] = y[j];
+            }
+        }
+    }
+}
+
+template <typename T, int FMT>
+static void launch_store_rows(const CompressArgs& a, int c, dim3 grid, hipStream_t st) {
+    if (c <= 64) hipLaunchKernelGGL((kv_store_rows<T, FMT, 1>), grid, dim3(64), 0, st, a);
+    else if (c <= 128) hipLaunchKernelGGL((kv_store_rows<T, FMT, 2>), grid, dim3(64), 0, st, a);
+    else if (c <= 576) hipLaunchKernelGGL((kv_store_rows<T, FMT, 9>), grid, dim3(64), 0, st, a);
+    else hipLaunchKernelGGL((kv_store_rows<T, FMT, 16>), grid, dim3(64), 0, st, a);
+}
+
 hipError_t launch_kv_compress(const CompressArgs& a, hipStream_t st) {
     if (a.max_entries <= 0) return hipSuccess;
     const int c = a.out.d_nope + a.out.d_rope;
     dim3 grid((unsigned)a.max_entries, (unsigned)a.B);
     dim3 block((unsigned)((c + 63) / 64 * 64));
     const bool bf = a.in_dtype == LCA_BF16;
+    if (a.m == 1 && !a.overlap && a.out.d_rope <= 64) {
+        switch (a.out.fmt) {
+            case LCA_F32:
+                if (bf) launch_store_rows<uint16_t, LCA_F32>(a, c, grid, st);
+                else launch_store_rows<float, LCA_F32>(a, c, grid, st);
+                break;
+            case LCA_BF16:
+                if (bf) launch_store_rows<uint16_t, LCA_BF16>(a, c, grid, st);
+                else launch_store_rows<float, LCA_BF16>(a, c, grid, st);
+                break;
+            default:
+                if (bf) launch_store_rows<uint16_t, LCA_FP8>(a, c, grid, st);
+                else launch_store_rows<float, LCA_FP8>(a, c, grid, st);
+                break;
+        }
+        return hipGetLastError();
+    }
     switch (a.out.fmt) {
         case LCA_F32:
             if (bf) hipLaunchKernelGGL((kv_compress_kernel<uint16_t, LCA_F32>), grid, block, 0, st, a);
