@@ -571,88 +571,108 @@ __global__ void __launch_bounds__(512) attn_mfma(AttnArgs a, int64_t split_len, 
         a.lse[rowid * a.H + h] = den > 0.0f ? (mu + log2f(den)) * kLn2 : -INFINITY;
 }
 
-// Merge nsplit partial (O, m, l) triples of one (row, head).  Block (row, head, dim quarter z),
-// ng x 36 threads (ng = one split group per 8 splits, at most 4): wave 0 turns the splits' (m, l)
-// into weights in LDS; then split group q = tid / 36 sums splits q, q + ng, ... for dims
-// 144 z + 4 (tid % 36) .. +3 (and, for RoPE dims, their rotation partners, which lie in the same
-// quarter), and the group sums are added in group order.  Each thread keeps a short chain of
-// loads: the merge is bound by load latency, not bandwidth.
+// Merge nsplit partial (O, m, l) triples of one (row, head).  Grid (T, H x 4, B): row i =
+// blockIdx.x of sequence b = blockIdx.z, head h and dim quarter z from blockIdx.y.  ng x 36 threads
+// (ng = one split group per 8 splits, at most 4): split group q = tid / 36 sums splits q, q + ng,
+// ... for dims 144 z + 4 (tid % 36) .. +3 (and, for RoPE dims, their rotation partners, which lie
+// in the same quarter); the group sums are added in group order.  The merge is bound by load
+// latency: the arguments, each thread's first eight partials and wave 0's (m, l) pairs are all
+// fetched in one round, before the weights are formed (wave 0, through LDS).
 constexpr int kCombGroups = 4, kCombQuarters = 4, kCombPer = kC / 4 / kCombQuarters;  // 36 threads x 4 dims
 constexpr int kCombThreads = kCombGroups * kCombPer;
 static int comb_groups(int nsplit) { return nsplit >= 32 ? 4 : nsplit >= 16 ? 2 : 1; }
 __global__ void __launch_bounds__(kCombThreads) attn_combine(AttnArgs a, int nsplit) {
     const int ng = blockDim.x / kCombPer;  // blockDim.x = max(64, ng x 36): wave 0 is whole
-    const int64_t rowid = blockIdx.x;
-    const int h = blockIdx.y;
+    const int ri = blockIdx.x, h = blockIdx.y >> 2, qz = blockIdx.y & 3, b = blockIdx.z;
+    const int64_t nrows = (int64_t)gridDim.x * gridDim.z;
+    const int64_t rowid = (int64_t)b * gridDim.x + ri;
     const int tid = threadIdx.x, lane = tid & 63;
-    const int64_t nrows = gridDim.x;
+    const int H = a.H;
     const float* wo = (const float*)a.ws;
-    const float* wml = wo + (int64_t)nsplit * nrows * a.H * kC;
-    int b, ri;
-    row_coords(a, rowid, &b, &ri);
+    const float* sink = a.sink;
     const int64_t t = a.q_pos.v[b] + ri;
+    asm volatile("" ::"s"(H), "s"(wo), "s"(sink), "s"(t));
+    const float* wml = wo + (int64_t)nsplit * nrows * H * kC;
     __shared__ float wsp[1024];
     __shared__ float s_mu, s_den;
     __shared__ f32x4 part[kCombGroups - 1][kCombPer][2];
     const int el = tid % kCombPer;  // this thread's slot in the group exchange
+    const int q = tid / kCombPer;
+    const int e = qz * kCombPer + (tid - q * kCombPer);  // float4 index in the row
+    const int d = 4 * e;
+    // RoPE dims 512 + j pair with 544 + j (j < 32)
+    const bool rot = a.rope_theta != 0.0 && d >= kDN;
+    const int r = d - kDN;
+    const int dp = !rot ? d : (r < kDR / 2 ? d + kDR / 2 : d - kDR / 2);
+    const int64_t stride = nrows * H * kC / 4;  // between splits, in f32x4
+    const f32x4* p0 = (const f32x4*)(wo + (rowid * H + h) * kC);
+    // this group's first eight splits q + ng u (indices past the end read split q; weight 0)
+    constexpr int kPre = 8;
+    f32x4 v0[kPre], vp0[kPre];
+    const bool grp = q < ng;  // (the padding lanes of a one-group block hold no split)
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+        const int jx = q + ng * u < nsplit && grp ? q + ng * u : 0;
+        v0[u] = p0[jx * stride + e];
+        vp0[u] = p0[jx * stride + dp / 4];
+    }
     if (tid < 64) {
+        // (m, l) of splits lane, lane + 64, ..: the first pair in the same round as the partials
         float M = -INFINITY;
-        for (int j = lane; j < nsplit; j += 64) M = fmaxf(M, wml[2 * ((j * nrows + rowid) * a.H + h)]);
-        M = wave_max(M);
+        for (int j = lane; j < nsplit; j += 64) M = fmaxf(M, wml[2 * ((j * nrows + rowid) * H + h)]);
+        M = wave_max_dpp(M);
         float mu = M;
-        const float z = a.sink ? a.sink[h] * kLog2e : -INFINITY;
-        if (a.sink) mu = fmaxf(M, z);
+        const float z = sink ? sink[h] * kLog2e : -INFINITY;
+        if (sink) mu = fmaxf(M, z);
         const float muse = mu == -INFINITY ? 0.0f : mu;
         float den = 0.0f;
         for (int j = lane; j < nsplit; j += 64) {
-            const int64_t pr = (j * nrows + rowid) * a.H + h;
+            const int64_t pr = (j * nrows + rowid) * H + h;
             const float wgt = exp2f(wml[2 * pr] - muse);
             wsp[j] = wgt;
             den += wml[2 * pr + 1] * wgt;
         }
-        den = wave_sum(den) + (a.sink ? exp2f(z - muse) : 0.0f);
+        den = wave_sum_dpp(den) + (sink ? exp2f(z - muse) : 0.0f);
         if (lane == 0) {
             s_mu = mu;
             s_den = den;
         }
     }
     __syncthreads();
-    const int q = tid / kCombPer;
-    const int e = (int)blockIdx.z * kCombPer + (tid - q * kCombPer);  // float4 index in the row
-    const int d = 4 * e;
-    // RoPE dims 512 + j pair with 544 + j (j < 32)
-    const bool rot = a.rope_theta != 0.0 && d >= kDN;
-    const int r = d - kDN;
-    const int dp = !rot ? d : (r < kDR / 2 ? d + kDR / 2 : d - kDR / 2);
-    const int64_t stride = nrows * a.H * kC / 4;  // between splits, in f32x4
-    const f32x4* p0 = (const f32x4*)(wo + (rowid * a.H + h) * kC);
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f}, accp = {0.0f, 0.0f, 0.0f, 0.0f};
-    int j = q;
-    auto chunk = [&](auto U) {  // U of this group's splits: all loads first, then the sums in order
-        constexpr int kU = decltype(U)::value;
-        f32x4 v[kU], vp[kU];
+    if (grp) {
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-            v[u] = p0[(j + ng * u) * stride + e];
-            if (rot) vp[u] = p0[(j + ng * u) * stride + dp / 4];
-        }
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-            const float wgt = wsp[j + ng * u];
+        for (int u = 0; u < kPre; ++u) {
+            const int jx = q + ng * u;
+            const float wgt = jx < nsplit ? wsp[jx] : 0.0f;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                acc[c] = fmaf(v[u][c], wgt, acc[c]);
-                if (rot) accp[c] = fmaf(vp[u][c], wgt, accp[c]);
+                acc[c] = fmaf(v0[u][c], wgt, acc[c]);
+                if (rot) accp[c] = fmaf(vp0[u][c], wgt, accp[c]);
             }
         }
-        j += ng * kU;
-    };
-    if (q < ng) {  // (padding lanes of a one-group block skip the sums)
-        while (j + ng * 7 < nsplit) chunk(std::integral_constant<int, 8>());
-        while (j + ng * 3 < nsplit) chunk(std::integral_constant<int, 4>());
-        while (j < nsplit) chunk(std::integral_constant<int, 1>());
+        // the rest, eight splits at a time: all loads first, then the sums in order
+        for (int j = q + ng * kPre; j < nsplit; j += ng * kPre) {
+            f32x4 v[kPre], vp[kPre];
+#pragma unroll
+            for (int u = 0; u < kPre; ++u) {
+                const int jx = j + ng * u < nsplit ? j + ng * u : j;
+                v[u] = p0[jx * stride + e];
+                vp[u] = p0[jx * stride + dp / 4];
+            }
+#pragma unroll
+            for (int u = 0; u < kPre; ++u) {
+                const int jx = j + ng * u;
+                const float wgt = jx < nsplit ? wsp[jx] : 0.0f;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    acc[c] = fmaf(v[u][c], wgt, acc[c]);
+                    if (rot) accp[c] = fmaf(vp[u][c], wgt, accp[c]);
+                }
+            }
+        }
     }
-    if (q > 0 && q < ng) {
+    if (q > 0 && grp) {
         part[q - 1][el][0] = acc;
         part[q - 1][el][1] = accp;
     }
@@ -664,8 +684,8 @@ __global__ void __launch_bounds__(kCombThreads) attn_combine(AttnArgs a, int nsp
     }
     const float den = s_den, mu = s_mu;
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-    if (a.lse && tid == 0 && blockIdx.z == 0)
-        a.lse[rowid * a.H + h] = den > 0.0f ? (mu + log2f(den)) * kLn2 : -INFINITY;
+    if (a.lse && tid == 0 && qz == 0)
+        a.lse[rowid * H + h] = den > 0.0f ? (mu + log2f(den)) * kLn2 : -INFINITY;
     f32x4 ov = acc * inv;
     if (rot) {
         const int pi = r < kDR / 2 ? r : r - kDR / 2;
@@ -677,7 +697,7 @@ __global__ void __launch_bounds__(kCombThreads) attn_combine(AttnArgs a, int nsp
             ov[c] = r < kDR / 2 ? x * cs - y * sn : y * sn + x * cs;
         }
     }
-    const int64_t oi = (rowid * a.H + h) * kC + d;
+    const int64_t oi = (rowid * H + h) * kC + d;
     if (a.out_dtype == LCA_F32) {
         *(f32x4*)((float*)a.out + oi) = ov;
     } else {
@@ -687,6 +707,7 @@ __global__ void __launch_bounds__(kCombThreads) attn_combine(AttnArgs a, int nsp
         *(uint2*)((uint16_t*)a.out + oi) = w;
     }
 }
+
 
 // ---------------------------------------------------------------------------------------------
 // Decode-sized launches (fewer than kDecRows query rows).  A launch of one or a few query rows
@@ -806,25 +827,34 @@ __device__ __forceinline__ void dec_store(DecRegs<FMT>& R, uint16_t* Kt, uint8_t
     put8(Kt, hw + 8 * (c >> 3), kDN / 8 + (c & 7), R.rp);
 }
 
-// Workgroup L: XCD x = L mod 8, j = L / 8; head group j mod ng, unit (j / ng) * 8 + x, where unit =
-// row * nsplit + split.  Grid: ceil(nunits / 8) * 8 * ng workgroups of 256 threads.
+// Grid (x, T, B): query row i = blockIdx.y of sequence b = blockIdx.z, so the row's position
+// comes from the first batch of argument loads.  Along x (a multiple of 8 workgroups, so x mod 8
+// is the XCD): x = 8 j + xcd, head group j mod ng, split (j / ng) * 8 + xcd.
 template <int FMT, bool DENSE, int NP>
-__global__ void __launch_bounds__(256) attn_dec(AttnArgs a, int64_t split_len, int nsplit, uint32_t nunits) {
+__global__ void __launch_bounds__(256) attn_dec(AttnArgs a, int64_t split_len, int nsplit) {
     __shared__ __attribute__((aligned(16))) uint16_t Kt[3][kTileElems];
     __shared__ __attribute__((aligned(16))) f32x4 Sx[2][4][2][64];  // partial scores, two tiles
     __shared__ uint32_t vflag[3][kKT / 4];
     __shared__ int32_t ent[DENSE ? 1 : kDecMaxLen];
 
-    const uint32_t ng = (uint32_t)a.H >> 4;
+    // Every argument the prologue needs is read here, before the first branch: the scalar loads
+    // then go out together instead of as a chain of dependent round trips.
+    const int b = blockIdx.z, ri = blockIdx.y;
+    const int64_t rowid = (int64_t)b * gridDim.y + ri;
+    const int H = a.H;
+    {
+        const int64_t qp = a.q_pos.v[b], wb = a.w_base.v[b], cc = a.comp.cap, wc = a.win.cap;
+        const int msh = a.m_shift, mm = a.m, kk = a.k, nw = a.n_win;
+        const void *pq = a.q, *pi = a.idx, *pn0 = a.comp.nope, *pn1 = a.win.nope, *pr0 = a.comp.rope,
+                   *pr1 = a.win.rope, *ps0 = a.comp.scale, *ps1 = a.win.scale;
+        asm volatile("" ::"s"(qp), "s"(wb), "s"(cc), "s"(wc), "s"(msh), "s"(mm), "s"(kk), "s"(nw), "s"(H), "s"(pq),
+                     "s"(pi), "s"(pn0), "s"(pn1), "s"(pr0), "s"(pr1), "s"(ps0), "s"(ps1));
+    }
+    const uint32_t ng = (uint32_t)H >> 4;
     const uint32_t L = blockIdx.x, jj = L >> 3;
     const int hg = (int)(jj % ng);
-    const uint32_t unit = (jj / ng) * 8u + (L & 7u);
-    if (unit >= nunits) return;
-    const uint32_t rowu = unit / (uint32_t)nsplit;
-    const int split = (int)(unit - rowu * (uint32_t)nsplit);
-    const int64_t rowid = rowu;
-    int b, ri;
-    row_coords(a, rowid, &b, &ri);
+    const int split = (int)((jj / ng) * 8u + (L & 7u));
+    if (split >= nsplit) return;
     int64_t t;
     const SlotMap sm = slot_map(a, b, ri, &t);
     // slot bookkeeping in 32 bits (slot counts and ring rows are below 2^31)
@@ -1251,14 +1281,13 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     const int64_t rb = a.comp.fmt == LCA_FP8 ? kDN : 2 * kDN;
     const bool off32 = a.comp.cap * rb < ((int64_t)1 << 32) && a.win.cap * rb < ((int64_t)1 << 32);
     if (p.dec && off32) {
-        const uint32_t nunits = (uint32_t)(rows * ns);
-        dim3 grid((unsigned)((nunits + 7) / 8 * 8 * (uint32_t)(a.H / 16)));
+        dim3 grid((unsigned)((ns + 7) / 8 * 8 * (a.H / 16)), (unsigned)a.T, (unsigned)a.B);
         if (a.comp.fmt == LCA_FP8) {
-            if (dense) hipLaunchKernelGGL((attn_dec<LCA_FP8, true, 4>), grid, dim3(256), 0, st, a, p.len, ns, nunits);
-            else hipLaunchKernelGGL((attn_dec<LCA_FP8, false, 4>), grid, dim3(256), 0, st, a, p.len, ns, nunits);
+            if (dense) hipLaunchKernelGGL((attn_dec<LCA_FP8, true, 4>), grid, dim3(256), 0, st, a, p.len, ns);
+            else hipLaunchKernelGGL((attn_dec<LCA_FP8, false, 4>), grid, dim3(256), 0, st, a, p.len, ns);
         } else {
-            if (dense) hipLaunchKernelGGL((attn_dec<LCA_BF16, true, 3>), grid, dim3(256), 0, st, a, p.len, ns, nunits);
-            else hipLaunchKernelGGL((attn_dec<LCA_BF16, false, 3>), grid, dim3(256), 0, st, a, p.len, ns, nunits);
+            if (dense) hipLaunchKernelGGL((attn_dec<LCA_BF16, true, 3>), grid, dim3(256), 0, st, a, p.len, ns);
+            else hipLaunchKernelGGL((attn_dec<LCA_BF16, false, 3>), grid, dim3(256), 0, st, a, p.len, ns);
         }
     } else {
         dim3 grid((unsigned)rows, (unsigned)ns);
@@ -1273,8 +1302,8 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns <= 1) return e;
     const int ct = comb_groups(ns) * kCombPer;
-    hipLaunchKernelGGL(attn_combine, dim3((unsigned)rows, (unsigned)a.H, kCombQuarters), dim3(ct < 64 ? 64 : ct), 0,
-                       st, a, ns);
+    hipLaunchKernelGGL(attn_combine, dim3((unsigned)a.T, (unsigned)(a.H * kCombQuarters), (unsigned)a.B),
+                       dim3(ct < 64 ? 64 : ct), 0, st, a, ns);
     return hipGetLastError();
 }
 

@@ -228,114 +228,48 @@ __global__ void __launch_bounds__(kTopkThreads) topk_row(TopkArgs a) {
 // ---------------------------------------------------------------------------
 // split schedule (bf16 scores)
 // ---------------------------------------------------------------------------
+// Grid (G, T, B): chunk g = blockIdx.x of row i = blockIdx.y of sequence b = blockIdx.z.  Each
+// launch is short and bound by latency, so every kernel reads its arguments, its 32 keys per
+// thread and every histogram column it needs in one round of loads before any of them is used.
+constexpr int kPer = kChunk / kSplitThreads;  // 32 keys per thread
 struct SplitRow {
     const uint16_t* row;
     int32_t* out;
-    int64_t n, K;
+    int64_t n, K, stride;
     uint32_t* h1;   // [G][256] high-byte histograms of this row
     uint32_t* h2;   // [G][256] low-byte histograms (keys with the chosen high byte)
 };
 
 __device__ __forceinline__ SplitRow split_row(const TopkArgs& a, int G) {
+    // arguments first, all in one batch of scalar loads (see the launch comment above)
+    const int b = blockIdx.z;
+    const int64_t qp = a.q_pos.v[b], stride = a.s_stride;
+    const int m = a.m, k = a.k;
+    const void* sc = a.scores;
+    int32_t* idx = a.idx;
+    void* ws = a.ws;
+    asm volatile("" ::"s"(qp), "s"(stride), "s"(m), "s"(k), "s"(sc), "s"(idx), "s"(ws));
     SplitRow r;
-    const int64_t rowid = blockIdx.y;
-    const int b = (int)(rowid / a.T);
-    const int64_t t = a.q_pos.v[b] + rowid % a.T;
-    r.n = min((t + 1) / a.m, a.s_stride);
-    r.K = min((int64_t)a.k, r.n);
-    r.row = (const uint16_t*)a.scores + rowid * a.s_stride;
-    r.out = a.idx + rowid * a.k;
-    r.h1 = (uint32_t*)a.ws + rowid * (int64_t)G * 512;
+    const int64_t rowid = (int64_t)b * gridDim.y + blockIdx.y;
+    const int64_t t1 = qp + blockIdx.y + 1;
+    const int64_t vis = (m & (m - 1)) == 0 ? t1 >> __builtin_ctz((unsigned)m) : t1 / m;  // (t + 1) / m
+    r.n = min(vis, stride);
+    r.K = min((int64_t)k, r.n);
+    r.stride = stride;
+    r.row = (const uint16_t*)sc + rowid * stride;
+    r.out = idx + rowid * k;
+    r.h1 = (uint32_t*)ws + rowid * (int64_t)G * 512;
     r.h2 = r.h1 + (int64_t)G * 256;
     return r;
 }
 
-// local histogram of the chunk into LDS (16 copies), reduced into hs[256]
-template <int NT, typename F>
-__device__ __forceinline__ void chunk_hist(const uint16_t* row, int64_t lo, int64_t hi, uint32_t* hist,
-                                           uint32_t* hs, F bin_of) {
-    const int tid = threadIdx.x, sub = tid & 15;
-    for (int j = tid; j < 256 * 16; j += NT) hist[j] = 0;
-    __syncthreads();
-    for_each_key<uint16_t, NT>(row, lo, hi, [&](int64_t, uint32_t key) {
-        const int bin = bin_of(key);
-        if (bin >= 0) atomicAdd(&hist[bin * 16 + sub], 1u);
-    });
-    __syncthreads();
-    if (tid < 256) {
-        uint32_t s = 0;
-#pragma unroll
-        for (int c = 0; c < 16; ++c) s += hist[tid * 16 + ((c + tid) & 15)];
-        hs[tid] = s;
-    }
-    __syncthreads();
-}
-
-// sum of bin `bin` over the first n chunk histograms (8 independent loads in flight)
-__device__ __forceinline__ uint32_t col_sum(const uint32_t* h, int n, int bin) {
-    uint32_t s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    int g = 0;
-    for (; g + 8 <= n; g += 8) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) s[u] += h[(g + u) * 256 + bin];
-    }
-    for (; g < n; ++g) s[0] += h[g * 256 + bin];
-    return s[0] + s[1] + s[2] + s[3] + s[4] + s[5] + s[6] + s[7];
-}
-
-// digits of the K-th largest key from the per-chunk histograms: hi byte and the count still to take
-__device__ __forceinline__ void reduce_pick(const uint32_t* h, int G, uint32_t rem, uint32_t* tot,
-                                            uint32_t* digit, uint32_t* rem_out) {
-    const int tid = threadIdx.x;
-    if (tid < 256) tot[tid] = col_sum(h, G, tid);
-    __syncthreads();
-    if (tid < 64) pick_digit(tot, rem, digit, rem_out);
-    __syncthreads();
-}
-
-__global__ void __launch_bounds__(kSplitThreads) topk_split_h1(TopkArgs a, int G) {
-    const SplitRow r = split_row(a, G);
-    const int g = blockIdx.x;
-    const int64_t lo = (int64_t)g * kChunk, hi = min(lo + kChunk, r.n);
-    __shared__ uint32_t hist[256 * 16];
-    __shared__ uint32_t hs[256];
-    if (r.n <= r.K) return;  // trivial row: the emit launch handles it
-    chunk_hist<kSplitThreads>(r.row, lo, hi < lo ? lo : hi, hist, hs, [](uint32_t key) { return (int)(key >> 8); });
-    if (threadIdx.x < 256) r.h1[g * 256 + threadIdx.x] = hs[threadIdx.x];
-}
-
-__global__ void __launch_bounds__(kSplitThreads) topk_split_h2(TopkArgs a, int G) {
-    const SplitRow r = split_row(a, G);
-    const int g = blockIdx.x;
-    const int64_t lo = (int64_t)g * kChunk, hi = min(lo + kChunk, r.n);
-    __shared__ uint32_t hist[256 * 16];
-    __shared__ uint32_t hs[256];
-    __shared__ uint32_t d1, rem1;
-    if (r.n <= r.K) return;
-    reduce_pick(r.h1, G, (uint32_t)r.K, hs, &d1, &rem1);
-    const uint32_t hb = d1;
-    chunk_hist<kSplitThreads>(r.row, lo, hi < lo ? lo : hi, hist, hs,
-                              [hb](uint32_t key) { return (key >> 8) == hb ? (int)(key & 255u) : -1; });
-    if (threadIdx.x < 256) r.h2[g * 256 + threadIdx.x] = hs[threadIdx.x];
-}
-
-__global__ void __launch_bounds__(kSplitThreads) topk_split_emit(TopkArgs a, int G) {
-    const SplitRow r = split_row(a, G);
-    const int g = blockIdx.x, tid = threadIdx.x;
-    const int64_t lo = (int64_t)g * kChunk, hi = min(lo + kChunk, r.n);
-    if (r.n <= r.K) {  // fewer candidates than k: all of them, in order
-        for (int64_t j = lo + tid; j < lo + kChunk && j < a.k; j += kSplitThreads)
-            r.out[j] = j < r.n ? (int32_t)j : -1;
-        if (g == G - 1)
-            for (int64_t j = (int64_t)G * kChunk + tid; j < a.k; j += kSplitThreads) r.out[j] = j < r.n ? (int32_t)j : -1;
-        return;
-    }
-    // This thread's 32 consecutive scores, fetched before the digits are known so that the
-    // loads overlap the histogram reductions.
-    constexpr int kPer = kChunk / kSplitThreads;  // 32
-    const int64_t e0 = lo + (int64_t)kPer * tid;
-    uint32_t raw[kPer / 2];                       // bf16 pairs, element e0 + 2q in the low half
-    const bool vec = (((uintptr_t)(r.row + lo)) & 15u) == 0 && e0 + kPer <= hi;
+// This thread's 32 consecutive scores of chunk [lo, hi) as bf16 pairs (element lo + 32 tid + 2q in
+// the low half of raw[q]).  Elements at or past hi are never counted: a thread whose 32 keys lie
+// inside the row's s_stride reads them as two 16-byte pairs whatever their validity, the others
+// element by element.
+__device__ __forceinline__ void load_keys(const SplitRow& r, int64_t lo, int64_t hi, uint32_t* raw) {
+    const int64_t e0 = lo + (int64_t)kPer * threadIdx.x;
+    const bool vec = (((uintptr_t)(r.row + lo)) & 15u) == 0 && e0 + kPer <= r.stride;
     if (vec) {
 #pragma unroll
         for (int q = 0; q < kPer / 8; ++q) {
@@ -351,33 +285,148 @@ __global__ void __launch_bounds__(kSplitThreads) topk_split_emit(TopkArgs a, int
             raw[q] = l | (h << 16);
         }
     }
-    __shared__ uint32_t tot[256];
+}
+
+__device__ __forceinline__ uint32_t raw_key(const uint32_t* raw, int u) {
+    return mono_key((uint16_t)(raw[u >> 1] >> (16 * (u & 1))));
+}
+
+// histogram (16 LDS copies, one per lane mod 16) of bin_of(key) over this thread's valid keys,
+// reduced into hs[256]
+template <typename F>
+__device__ __forceinline__ void keys_hist(const uint32_t* raw, int64_t e0, int64_t hi, uint32_t* hist, uint32_t* hs,
+                                          F bin_of) {
+    const int tid = threadIdx.x, sub = tid & 15;
+    for (int j = tid; j < 256 * 16; j += kSplitThreads) hist[j] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        if (e0 + u < hi) {
+            const int bin = bin_of(raw_key(raw, u));
+            if (bin >= 0) atomicAdd(&hist[bin * 16 + sub], 1u);
+        }
+    }
+    __syncthreads();
+    if (tid < 256) {
+        uint32_t s = 0;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) s += hist[tid * 16 + ((c + tid) & 15)];
+        hs[tid] = s;
+    }
+    __syncthreads();
+}
+
+// Column sums of bin `bin` over the G chunk histograms h[g][256] of NH histograms (h2 = h1 + 256 G):
+// the totals and the sums over the chunks before g_me.  All loads of a batch of 24 chunks go out
+// before any sum (one round for G <= 24).
+template <int NH>
+__device__ __forceinline__ void col_sums(const uint32_t* h1, int G, int g_me, int bin, uint32_t* tot, uint32_t* pre) {
+    constexpr int kB = 24;
+#pragma unroll
+    for (int k = 0; k < NH; ++k) tot[k] = pre[k] = 0;
+    for (int g0 = 0; g0 < G; g0 += kB) {
+        uint32_t v[NH][kB];
+#pragma unroll
+        for (int k = 0; k < NH; ++k)
+#pragma unroll
+            for (int u = 0; u < kB; ++u) v[k][u] = h1[(int64_t)k * G * 256 + (g0 + u < G ? g0 + u : 0) * 256 + bin];
+#pragma unroll
+        for (int k = 0; k < NH; ++k)
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                const uint32_t x = g0 + u < G ? v[k][u] : 0u;
+                tot[k] += x;
+                pre[k] += g0 + u < g_me ? x : 0u;
+            }
+    }
+}
+
+__global__ void __launch_bounds__(kSplitThreads) topk_split_h1(TopkArgs a, int G) {
+    const SplitRow r = split_row(a, G);
+    const int g = blockIdx.x;
+    const int64_t lo = (int64_t)g * kChunk, hi = min(lo + kChunk, r.n);
+    __shared__ uint32_t hist[256 * 16];
+    __shared__ uint32_t hs[256];
+    if (r.n <= r.K) return;  // trivial row: the emit launch handles it
+    uint32_t raw[kPer / 2];
+    load_keys(r, lo, hi, raw);
+    keys_hist(raw, lo + (int64_t)kPer * threadIdx.x, hi, hist, hs, [](uint32_t key) { return (int)(key >> 8); });
+    if (threadIdx.x < 256) r.h1[g * 256 + threadIdx.x] = hs[threadIdx.x];
+}
+
+__global__ void __launch_bounds__(kSplitThreads) topk_split_h2(TopkArgs a, int G) {
+    const SplitRow r = split_row(a, G);
+    const int g = blockIdx.x, tid = threadIdx.x;
+    const int64_t lo = (int64_t)g * kChunk, hi = min(lo + kChunk, r.n);
+    __shared__ uint32_t hist[256 * 16];
+    __shared__ uint32_t hs[256];
+    __shared__ uint32_t d1, rem1;
+    if (r.n <= r.K) return;
+    uint32_t raw[kPer / 2];
+    load_keys(r, lo, hi, raw);
+    uint32_t t1[1] = {0}, p1[1] = {0};
+    if (tid < 256) col_sums<1>(r.h1, G, 0, tid, t1, p1);
+    if (tid < 256) hs[tid] = t1[0];
+    __syncthreads();
+    if (tid < 64) pick_digit(hs, (uint32_t)r.K, &d1, &rem1);
+    __syncthreads();
+    const uint32_t hb = d1;
+    keys_hist(raw, lo + (int64_t)kPer * tid, hi, hist, hs,
+              [hb](uint32_t key) { return (key >> 8) == hb ? (int)(key & 255u) : -1; });
+    if (tid < 256) r.h2[g * 256 + tid] = hs[tid];
+}
+
+__global__ void __launch_bounds__(kSplitThreads) topk_split_emit(TopkArgs a, int G) {
+    const SplitRow r = split_row(a, G);
+    const int g = blockIdx.x, tid = threadIdx.x;
+    const int64_t lo = (int64_t)g * kChunk, hi = min(lo + kChunk, r.n);
+    const int kk = a.k;
+    if (r.n <= r.K) {  // fewer candidates than k: all of them, in order
+        for (int64_t j = lo + tid; j < lo + kChunk && j < kk; j += kSplitThreads)
+            r.out[j] = j < r.n ? (int32_t)j : -1;
+        if (g == G - 1)
+            for (int64_t j = (int64_t)G * kChunk + tid; j < kk; j += kSplitThreads) r.out[j] = j < r.n ? (int32_t)j : -1;
+        return;
+    }
+    // one round: this thread's keys and (thread = bin) both histograms' columns
+    uint32_t raw[kPer / 2];
+    load_keys(r, lo, hi, raw);
+    uint32_t tt[2] = {0, 0}, pp[2] = {0, 0};
+    if (tid < 256) col_sums<2>(r.h1, G, g, tid, tt, pp);
+    const uint32_t t1 = tt[0], p1 = pp[0], t2 = tt[1], p2 = pp[1];
+    __shared__ uint32_t tot1[256], tot2[256];
     __shared__ uint32_t d1, rem1, d2, rem2;
     __shared__ uint32_t wsum[kSplitThreads / 64];
     __shared__ uint32_t base_gt, base_eq;
-    reduce_pick(r.h1, G, (uint32_t)r.K, tot, &d1, &rem1);
-    reduce_pick(r.h2, G, rem1, tot, &d2, &rem2);
+    if (tid < 256) {
+        tot1[tid] = t1;
+        tot2[tid] = t2;
+    }
+    __syncthreads();
+    if (tid < 64) pick_digit(tot1, (uint32_t)r.K, &d1, &rem1);
+    __syncthreads();
+    if (tid < 64) pick_digit(tot2, rem1, &d2, &rem2);
+    __syncthreads();
     const uint32_t tau = (d1 << 8) | d2, rem = rem2;
     if (g == 0)
-        for (int64_t j = r.K + tid; j < a.k; j += kSplitThreads) r.out[j] = -1;
-    // keys above tau and equal to tau in the chunks before this one
+        for (int64_t j = r.K + tid; j < kk; j += kSplitThreads) r.out[j] = -1;
+    // keys above tau and equal to tau in the chunks before this one: thread = bin
     {
-        // thread = bin: its counts over the earlier chunks, then a block sum of the bins above tau
         uint32_t gt = 0, eq = 0;
         if (tid < 256) {
-            const uint32_t c1 = col_sum(r.h1, g, tid), c2 = col_sum(r.h2, g, tid);
-            gt = ((uint32_t)tid > d1 ? c1 : 0u) + ((uint32_t)tid > d2 ? c2 : 0u);
-            eq = (uint32_t)tid == d2 ? c2 : 0u;
+            gt = ((uint32_t)tid > d1 ? p1 : 0u) + ((uint32_t)tid > d2 ? p2 : 0u);
+            eq = (uint32_t)tid == d2 ? p2 : 0u;
         }
-        uint32_t t1, t2;
-        block_incl_scan<kSplitThreads / 64>(gt, wsum, &t1);
-        block_incl_scan<kSplitThreads / 64>(eq, wsum, &t2);
+        uint32_t s1, s2;
+        block_incl_scan<kSplitThreads / 64>(gt, wsum, &s1);
+        block_incl_scan<kSplitThreads / 64>(eq, wsum, &s2);
         if (tid == 0) {
-            base_gt = t1;
-            base_eq = t2;
+            base_gt = s1;
+            base_eq = s2;
         }
         __syncthreads();
     }
+    const int64_t e0 = lo + (int64_t)kPer * tid;
     uint32_t keys[kPer];
     uint32_t ngt = 0, neq = 0;
 #pragma unroll
@@ -428,7 +477,7 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
     if (use_split(a, a.max_n)) {
         const int G = split_chunks(a.s_stride);
-        dim3 grid((unsigned)G, (unsigned)(a.B * a.T));
+        dim3 grid((unsigned)G, (unsigned)a.T, (unsigned)a.B);
         hipLaunchKernelGGL(topk_split_h1, grid, dim3(kSplitThreads), 0, st, a, G);
         hipLaunchKernelGGL(topk_split_h2, grid, dim3(kSplitThreads), 0, st, a, G);
         hipLaunchKernelGGL(topk_split_emit, grid, dim3(kSplitThreads), 0, st, a, G);
