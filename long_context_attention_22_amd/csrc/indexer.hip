@@ -9,7 +9,7 @@
 // cache straight from HBM into B fragments (each lane loads 16 contiguous
 // bytes of one key row, so a chunk is one contiguous 16 KB read).  The
 // epilogue applies ReLU and the head weights in the accumulator layout, sums
-// the 16 heads with two cross-lane shuffles and writes 64 consecutive scores
+// the 16 heads with two lane swaps (v_permlane16/32_swap) and writes 64 consecutive scores
 // per token with one coalesced store.  Key chunks beyond the last token's
 // visible count are skipped (causal tile skip).
 //
@@ -32,14 +32,25 @@ __device__ __forceinline__ void store_score<uint16_t>(uint16_t* p, float v) {
     *p = f2bf(v == 0.0f ? 0.0f : v);
 }
 
+// (visible count (t + 1) / m: a shift when m is a power of two)
+__device__ __forceinline__ int64_t vis_of(int64_t t1, int m) {
+    return (m & (m - 1)) == 0 ? t1 >> __builtin_ctz((unsigned)m) : t1 / m;
+}
+
 template <int TOK, typename TS>
 __global__ void __launch_bounds__(256) indexer_mfma(IndexerArgs a, int64_t keys_per_wg) {
     const int b = blockIdx.z;
     const int i0 = blockIdx.y * TOK;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int ntok = min(TOK, a.T - i0);
-    const int64_t pos0 = a.q_pos.v[b] + i0;
-    const int64_t vis_last = min((pos0 + ntok) / a.m, a.k_cap);
+    // the arguments in one batch of scalar loads, before the first branch
+    const int T = a.T, m = a.m;
+    const int64_t p0 = a.q_pos.v[b], k_cap = a.k_cap, s_stride = a.s_stride;
+    const void *pq = a.q, *pk = a.k, *psc = a.scores;
+    const float* pw = a.w;
+    asm volatile("" ::"s"(T), "s"(m), "s"(p0), "s"(k_cap), "s"(s_stride), "s"(pq), "s"(pk), "s"(psc), "s"(pw));
+    const int ntok = min(TOK, T - i0);
+    const int64_t pos0 = p0 + i0;
+    const int64_t vis_last = min(vis_of(pos0 + ntok, m), k_cap);
     const int64_t key_lo = (int64_t)blockIdx.x * keys_per_wg;
     const int64_t key_hi = min(key_lo + keys_per_wg, vis_last);
     if (key_lo >= key_hi) return;
@@ -92,12 +103,11 @@ __global__ void __launch_bounds__(256) indexer_mfma(IndexerArgs a, int64_t keys_
                 v = fmaf(wt[tk][1], fmaxf(acc[1], 0.0f), v);
                 v = fmaf(wt[tk][2], fmaxf(acc[2], 0.0f), v);
                 v = fmaf(wt[tk][3], fmaxf(acc[3], 0.0f), v);
-                v += __shfl_xor(v, 16, kWave);
-                v += __shfl_xor(v, 32, kWave);
+                v = sum4g(v);  // the four head quartets of this key (lanes key + 16 kgrp)
                 if (kgrp == bl) mine = v;
             }
             if (tk < ntok) {
-                const int64_t vis_t = min((pos0 + tk + 1) / a.m, a.k_cap);
+                const int64_t vis_t = min(vis_of(pos0 + tk + 1, m), k_cap);
                 if (mykey < vis_t) store_score<TS>(sbase + (int64_t)tk * a.s_stride + mykey, mine);
             }
         }
