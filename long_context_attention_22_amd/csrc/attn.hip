@@ -573,14 +573,14 @@ __global__ void __launch_bounds__(512) attn_mfma(AttnArgs a, int64_t split_len, 
 
 // Merge nsplit partial (O, m, l) triples of one (row, head).  Grid (T, H x 4, B): row i =
 // blockIdx.x of sequence b = blockIdx.z, head h and dim quarter z from blockIdx.y.  ng x 36 threads
-// (ng = one split group per 8 splits, at most 4): split group q = tid / 36 sums splits q, q + ng,
+// (ng = one split group per 8 splits, at most 8): split group q = tid / 36 sums splits q, q + ng,
 // ... for dims 144 z + 4 (tid % 36) .. +3 (and, for RoPE dims, their rotation partners, which lie
 // in the same quarter); the group sums are added in group order.  The merge is bound by load
 // latency: the arguments, each thread's first eight partials and wave 0's (m, l) pairs are all
 // fetched in one round, before the weights are formed (wave 0, through LDS).
-constexpr int kCombGroups = 4, kCombQuarters = 4, kCombPer = kC / 4 / kCombQuarters;  // 36 threads x 4 dims
+constexpr int kCombGroups = 8, kCombQuarters = 4, kCombPer = kC / 4 / kCombQuarters;  // 36 threads x 4 dims
 constexpr int kCombThreads = kCombGroups * kCombPer;
-static int comb_groups(int nsplit) { return nsplit >= 32 ? 4 : nsplit >= 16 ? 2 : 1; }
+static int comb_groups(int nsplit) { return nsplit > 32 ? 8 : nsplit > 16 ? 4 : nsplit > 8 ? 2 : 1; }
 __global__ void __launch_bounds__(kCombThreads) attn_combine(AttnArgs a, int nsplit) {
     const int ng = blockDim.x / kCombPer;  // blockDim.x = max(64, ng x 36): wave 0 is whole
     const int ri = blockIdx.x, h = blockIdx.y >> 2, qz = blockIdx.y & 3, b = blockIdx.z;
