@@ -5,7 +5,8 @@ CPU-baseline leg may import this package.  The HIP library never calls it and
 it never serves as a fallback for it.
 
 Arrays are numpy: float32 for f32, uint16 bit patterns for bf16, uint8 codes
-for fp8.  Shapes follow the library's layouts ([B][rows][dims], row-major).
+for fp8, and for MXFP4 uint8 bytes holding two E2M1 codes (even element in the
+low nibble) with uint8 E8M0 scale bytes, one per 32 elements.  Shapes follow the library's layouts ([B][rows][dims], row-major).
 """
 from __future__ import annotations
 
@@ -17,7 +18,7 @@ import numpy as np
 
 from . import build as _build
 
-F32, BF16, FP8 = 0, 1, 2
+F32, BF16, FP8, MXFP4 = 0, 1, 2, 3
 _lib = None
 
 
@@ -47,6 +48,14 @@ def _declare(L):
     L.orc_fp8_to_f64.restype = f64
     L.orc_f64_to_fp8.argtypes = [f64]
     L.orc_f64_to_fp8.restype = C.c_uint8
+    L.orc_e2m1_to_f64.argtypes = [C.c_uint8]
+    L.orc_e2m1_to_f64.restype = f64
+    L.orc_f64_to_e2m1.argtypes = [f64]
+    L.orc_f64_to_e2m1.restype = C.c_uint8
+    L.orc_mxfp4_block.argtypes = [vp, vp]
+    L.orc_mxfp4_block.restype = C.c_uint8
+    L.orc_indexer_score_mxfp4.argtypes = [vp, i32, vp, _KV, i32, i32, i32, i32, vp, i32, vp, i32, i64]
+    L.orc_indexer_score_mxfp4.restype = C.c_int
     L.orc_kv_decode.argtypes = [_KV, i64, i64, i64, vp]
     L.orc_kv_decode.restype = None
     L.orc_kv_compress.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, f64, f64, i32, i32, i32, i64,
@@ -100,6 +109,11 @@ class KV:
             nope = np.zeros((B, cap, d_nope), np.uint8)
             rope = np.zeros((B, cap, d_rope), np.uint16)
             scale = np.ones((B, cap, d_nope // 128), np.float32)
+        elif fmt == MXFP4:
+            assert d_nope % 32 == 0 and d_rope == 0
+            nope = np.zeros((B, cap, d_nope // 2), np.uint8)
+            rope = np.zeros((B, cap, 0), np.uint16)
+            scale = np.full((B, cap, d_nope // 32), 127, np.uint8)
         else:
             raise ValueError(fmt)
         return KV(nope, rope, scale, fmt, d_nope, d_rope, cap)
@@ -133,6 +147,33 @@ def fp8_to_f64(code: int) -> float:
 
 def f64_to_fp8(x: float) -> int:
     return int(lib().orc_f64_to_fp8(float(x)))
+
+
+def e2m1_to_f64(code: int) -> float:
+    return lib().orc_e2m1_to_f64(int(code))
+
+
+def f64_to_e2m1(x: float) -> int:
+    return int(lib().orc_f64_to_e2m1(float(x)))
+
+
+def mxfp4_block(v) -> tuple[int, np.ndarray]:
+    """32 values -> (E8M0 scale byte, 32 E2M1 codes)."""
+    v = np.ascontiguousarray(np.asarray(v, np.float64).reshape(32))
+    codes = np.zeros(32, np.uint8)
+    sc = lib().orc_mxfp4_block(_p(v), _p(codes))
+    return int(sc), codes
+
+
+def mxfp4_quantize(x) -> tuple[np.ndarray, np.ndarray]:
+    """[..., d] values (d % 32 == 0) -> (codes [..., d] uint8, scale bytes [..., d/32] uint8)."""
+    x = np.asarray(x, np.float64)
+    blocks = x.reshape(-1, 32)
+    codes = np.zeros(blocks.shape, np.uint8)
+    scales = np.zeros(blocks.shape[0], np.uint8)
+    for i, blk in enumerate(blocks):
+        scales[i], codes[i] = mxfp4_block(blk)
+    return codes.reshape(x.shape), scales.reshape(x.shape[:-1] + (x.shape[-1] // 32,))
 
 
 def kv_compress(c_a, z_a, c_b, z_b, out: KV, *, m: int, overlap: int, first_pos,
@@ -172,6 +213,24 @@ def indexer_score(q, w, k, *, q_pos, m: int, score_fmt: int, s_stride: int | Non
     wc = None if w is None else np.ascontiguousarray(w, np.float32)
     rc = lib().orc_indexer_score(_p(q), _fmt_of(q), _p(wc), _p(k), _fmt_of(k), k_cap, H_I, d_I, B, T,
                                  _p(qp), m, _p(out), score_fmt, s_stride)
+    assert rc == 0
+    return out
+
+
+def indexer_score_mxfp4(q, w, k: KV, *, q_pos, m: int, score_fmt: int, s_stride: int | None = None,
+                        out=None):
+    """q [B][T][H_I][d_I] (f32 or bf16 bits), keys stored MXFP4 in `k` -> scores [B][T][s_stride]."""
+    B, T, H_I, d_I = q.shape
+    assert k.fmt == MXFP4 and k.d_nope == d_I
+    if s_stride is None:
+        s_stride = k.cap
+    if out is None:
+        out = np.zeros((B, T, s_stride), np.float32 if score_fmt == F32 else np.uint16)
+    qp = np.ascontiguousarray(np.asarray(q_pos, np.int64).reshape(B))
+    q = np.ascontiguousarray(q)
+    wc = None if w is None else np.ascontiguousarray(w, np.float32)
+    rc = lib().orc_indexer_score_mxfp4(_p(q), _fmt_of(q), _p(wc), k.c(), H_I, d_I, B, T, _p(qp), m,
+                                       _p(out), score_fmt, s_stride)
     assert rc == 0
     return out
 

@@ -72,6 +72,47 @@ uint8_t orc_f64_to_fp8(double x) {
     return (uint8_t)(c | (neg << 7));
 }
 
+/* OCP FP4 E2M1 (OCP Microscaling Formats v1.0): 1 sign, 2 exponent (bias 1),
+ * 1 mantissa bit; exponent 0 is subnormal (m/2); no NaN or infinity; max 6. */
+double orc_e2m1_to_f64(uint8_t code) {
+    int s = (code >> 3) & 1, e = (code >> 1) & 3, mt = code & 1;
+    double v = e == 0 ? 0.5 * mt : ldexp(1.0 + 0.5 * mt, e - 1);
+    return s ? -v : v;
+}
+
+/* Nearest magnitude among codes 0..7 (monotone in value); exact ties go to the
+ * even code; beyond 6 the result saturates. */
+uint8_t orc_f64_to_e2m1(double x) {
+    int neg = signbit(x) ? 1 : 0;
+    double a = fabs(x);
+    uint8_t c = 7;
+    if (a < 6.0) {
+        int lo = 0;
+        while (lo < 6 && orc_e2m1_to_f64((uint8_t)(lo + 1)) <= a) ++lo;   /* value(lo) <= a < value(lo+1) */
+        double dl = a - orc_e2m1_to_f64((uint8_t)lo), dh = orc_e2m1_to_f64((uint8_t)(lo + 1)) - a;
+        if (dl < dh) c = (uint8_t)lo;
+        else if (dh < dl) c = (uint8_t)(lo + 1);
+        else c = (uint8_t)((lo & 1) ? lo + 1 : lo);
+    }
+    return (uint8_t)(c | (neg << 3));
+}
+
+/* MX block conversion (OCP Microscaling Formats v1.0, conversion of a block of
+ * 32 values to MXFP4): the shared scale is X = 2^(floor(log2(amax)) - 2), 2
+ * being the largest exponent of E2M1, and each element is the E2M1 value
+ * nearest to v / X (ties to even, saturating).  Reading: an all-zero block gets
+ * scale 2^0 (E8M0 127) and zero codes; the E8M0 byte is clamped to [0, 254]. */
+uint8_t orc_mxfp4_block(const double* v, uint8_t* codes) {
+    double amax = 0.0;
+    for (int j = 0; j < 32; ++j) amax = fmax(amax, fabs(v[j]));
+    int sh = 0;
+    if (amax > 0.0) sh = ilogb(amax) - 2;
+    if (sh < -127) sh = -127;
+    if (sh > 127) sh = 127;
+    for (int j = 0; j < 32; ++j) codes[j] = orc_f64_to_e2m1(ldexp(v[j], -sh));
+    return (uint8_t)(sh + 127);
+}
+
 static double load_in(const void* p, int32_t fmt, int64_t i) {
     if (fmt == ORC_F32) return (double)((const float*)p)[i];
     return orc_bf16_to_f64(((const uint16_t*)p)[i]);
@@ -88,6 +129,12 @@ void orc_kv_decode(orc_kv kv, int64_t b, int64_t row0, int64_t nrows, double* ou
         double* o = out + r * c;
         for (int j = 0; j < kv.d_nope; ++j) {
             int64_t e = row * kv.d_nope + j;
+            if (kv.fmt == ORC_MXFP4) {
+                const uint8_t byte = ((const uint8_t*)kv.nope)[e / 2];
+                const uint8_t sc = ((const uint8_t*)kv.scale)[row * (kv.d_nope / 32) + j / 32];
+                o[j] = ldexp(orc_e2m1_to_f64((uint8_t)((j & 1) ? byte >> 4 : byte & 15)), (int)sc - 127);
+                continue;
+            }
             if (kv.fmt == ORC_F32) o[j] = ((const float*)kv.nope)[e];
             else if (kv.fmt == ORC_BF16) o[j] = orc_bf16_to_f64(((const uint16_t*)kv.nope)[e]);
             else o[j] = orc_fp8_to_f64(((const uint8_t*)kv.nope)[e]) *
@@ -111,6 +158,14 @@ static void store_row(orc_kv kv, int64_t row, const double* y) {
         int64_t e = row * kv.d_nope + j;
         if (kv.fmt == ORC_F32) ((float*)kv.nope)[e] = (float)y[j];
         else if (kv.fmt == ORC_BF16) ((uint16_t*)kv.nope)[e] = orc_f32_to_bf16((float)y[j]);
+    }
+    if (kv.fmt == ORC_MXFP4) {
+        uint8_t codes[32];
+        for (int g = 0; g < kv.d_nope / 32; ++g) {
+            ((uint8_t*)kv.scale)[row * (kv.d_nope / 32) + g] = orc_mxfp4_block(y + 32 * g, codes);
+            for (int j = 0; j < 32; j += 2)
+                ((uint8_t*)kv.nope)[(row * kv.d_nope + 32 * g + j) / 2] = (uint8_t)(codes[j] | (codes[j + 1] << 4));
+        }
     }
     if (kv.fmt == ORC_FP8) {
         int ng = kv.d_nope / 128;
@@ -285,6 +340,58 @@ int orc_indexer_score(const void* q, int32_t q_fmt, const float* w, const void* 
                 if (score_fmt == ORC_F32) ((float*)scores)[e] = f;
                 else ((uint16_t*)scores)[e] = orc_f32_to_bf16(f);
             }
+        }
+    }
+    return 0;
+}
+
+/*
+ * The MXFP4 QK path ([R] 5.2.1: QK activations cached, loaded and multiplied
+ * in FP4 (MXFP4)): every query head is quantised per 32-element block with
+ * the rule of orc_mxfp4_block, the keys are read as stored, and the score is
+ * the definition above on the decoded values (exact products, fp64 sums).
+ */
+int orc_indexer_score_mxfp4(const void* q, int32_t q_fmt, const float* w, orc_kv k, int32_t H_I,
+                            int32_t d_I, int32_t B, int32_t T, const int64_t* q_pos, int32_t m,
+                            void* scores, int32_t score_fmt, int64_t s_stride) {
+    if (!q || !scores || k.fmt != ORC_MXFP4 || k.d_nope != d_I || k.d_rope != 0 || d_I % 32 || H_I < 1 ||
+        B < 1 || T < 0 || m < 1)
+        return -1;
+    for (int32_t b = 0; b < B; ++b) {
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int32_t i = 0; i < T; ++i) {
+            const int64_t t = q_pos[b] + i;
+            int64_t vis = vis_count(t, m);
+            if (vis > k.cap) vis = k.cap;
+            const int64_t qrow = ((int64_t)b * T + i) * H_I;
+            double* qd = (double*)malloc(sizeof(double) * (size_t)H_I * d_I);
+            double* kd = (double*)malloc(sizeof(double) * (size_t)d_I);
+            for (int h = 0; h < H_I; ++h) {
+                double blk[32];
+                uint8_t codes[32];
+                for (int g = 0; g < d_I / 32; ++g) {
+                    for (int j = 0; j < 32; ++j) blk[j] = load_in(q, q_fmt, (qrow + h) * d_I + 32 * g + j);
+                    const int sc = (int)orc_mxfp4_block(blk, codes) - 127;
+                    for (int j = 0; j < 32; ++j) qd[h * d_I + 32 * g + j] = ldexp(orc_e2m1_to_f64(codes[j]), sc);
+                }
+            }
+            for (int64_t s = 0; s < vis; ++s) {
+                orc_kv_decode(k, b, s, 1, kd);
+                double acc = 0.0;
+                for (int h = 0; h < H_I; ++h) {
+                    double dot = 0.0;
+                    for (int d = 0; d < d_I; ++d) dot += qd[h * d_I + d] * kd[d];
+                    double wh = w ? (double)w[qrow + h] : 1.0;
+                    acc += wh * (dot > 0.0 ? dot : 0.0);
+                }
+                float f = (float)acc;
+                if (f == 0.0f) f = 0.0f;
+                int64_t e = ((int64_t)b * T + i) * s_stride + s;
+                if (score_fmt == ORC_F32) ((float*)scores)[e] = f;
+                else ((uint16_t*)scores)[e] = orc_f32_to_bf16(f);
+            }
+            free(qd);
+            free(kd);
         }
     }
     return 0;

@@ -21,6 +21,12 @@
  *   ORC_BF16: nope bf16, rope bf16
  *   ORC_FP8 : nope OCP e4m3fn with one f32 power-of-two scale per 128 nope
  *             dims, rope bf16.
+ *   ORC_MXFP4: nope OCP MXFP4 (E2M1 elements, two per byte with the even
+ *             element in the low nibble, and one E8M0 scale byte per 32
+ *             elements, stored through the `scale` pointer as uint8_t);
+ *             no rope dims.  Used for the indexer keys ([R] 5.2.1: the QK
+ *             path of the CSA indexer is cached, loaded and multiplied in
+ *             FP4 (MXFP4)).
  * bf16 arrays are passed as uint16_t bit patterns.
  */
 #ifndef LCA_ORACLE_H
@@ -31,12 +37,13 @@
 extern "C" {
 #endif
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8 = 2 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8 = 2, ORC_MXFP4 = 3 };
 
 typedef struct {
     void*   nope;   /* [B][cap][d_nope]                                   */
     void*   rope;   /* [B][cap][d_rope]                                   */
-    float*  scale;  /* [B][cap][d_nope/128] for ORC_FP8, else unused      */
+    float*  scale;  /* [B][cap][d_nope/128] for ORC_FP8; uint8_t E8M0
+                       [B][cap][d_nope/32] for ORC_MXFP4; else unused     */
     int32_t fmt;
     int32_t d_nope, d_rope;
     int64_t cap;    /* rows per sequence                                  */
@@ -47,6 +54,11 @@ double   orc_bf16_to_f64(uint16_t h);
 uint16_t orc_f32_to_bf16(float x);            /* round to nearest even     */
 double   orc_fp8_to_f64(uint8_t code);        /* OCP e4m3fn; NaN codes -> NaN */
 uint8_t  orc_f64_to_fp8(double x);            /* nearest, ties to even code, saturating at +-448 */
+
+double   orc_e2m1_to_f64(uint8_t code);       /* OCP FP4 E2M1 (low 4 bits)  */
+uint8_t  orc_f64_to_e2m1(double x);           /* nearest, ties to even code, saturating at +-6 */
+/* One MXFP4 block of 32 values: the E8M0 scale byte and 32 E2M1 codes. */
+uint8_t  orc_mxfp4_block(const double* v, uint8_t* codes);
 
 /* decode stored rows [row0, row0+nrows) of sequence b into out[nrows][d_nope+d_rope] */
 void orc_kv_decode(orc_kv kv, int64_t b, int64_t row0, int64_t nrows, double* out);
@@ -64,6 +76,14 @@ int orc_indexer_score(const void* q, int32_t q_fmt, const float* w, const void* 
                       int64_t k_cap, int32_t H_I, int32_t d_I, int32_t B, int32_t T,
                       const int64_t* q_pos, int32_t m, void* scores, int32_t score_fmt,
                       int64_t s_stride);
+
+/* The same scores with the QK path in MXFP4 ([R] 5.2.1): q (bf16 or f32) is
+ * quantised per head and 32-element block, the keys are stored MXFP4 (k.fmt
+ * == ORC_MXFP4, k.d_nope == d_I), and the products of the decoded values are
+ * summed exactly (fp64). */
+int orc_indexer_score_mxfp4(const void* q, int32_t q_fmt, const float* w, orc_kv k, int32_t H_I,
+                            int32_t d_I, int32_t B, int32_t T, const int64_t* q_pos, int32_t m,
+                            void* scores, int32_t score_fmt, int64_t s_stride);
 
 /* Top-k selection by (score desc, index asc), emitted ascending, -1 padded. */
 int orc_topk_select(const void* scores, int32_t score_fmt, int64_t s_stride, int32_t B, int32_t T,

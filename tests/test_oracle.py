@@ -467,3 +467,179 @@ def test_fp8_cache_reads_decoded_values(orc):
     b, lb = orc.attention(q, q_pos=[0], comp=f32, m=1, sm_scale=0.05)
     np.testing.assert_array_equal(a, b)
     np.testing.assert_array_equal(la, lb)
+
+
+# --------------------------------------------------------------------------
+# MXFP4 QK path ("DeepSeek-V4 中文翻译" section 5.2.1: the indexer's QK
+# activations are cached, loaded and multiplied in FP4 (MXFP4))
+# --------------------------------------------------------------------------
+
+def _e2m1_grid():
+    """The 16 E2M1 values built from the format's fields (bias 1, 1 mantissa bit, subnormals)."""
+    out = []
+    for code in range(16):
+        s, e, mt = code >> 3, (code >> 1) & 3, code & 1
+        v = mt * 0.5 if e == 0 else (1 + mt / 2) * 2.0 ** (e - 1)
+        out.append(-v if s else v)
+    return np.array(out)
+
+
+def test_e2m1_decode_matches_ocp_table(orc):
+    rows = [l.split() for l in open(os.path.join(GOLD, "ocp_e2m1_values.txt")) if l.strip() and l[0] != "#"]
+    assert len(rows) == 16
+    grid = _e2m1_grid()
+    for code, val in rows:
+        got = orc.e2m1_to_f64(int(code, 16))
+        assert got == float(val) and math.copysign(1, got) == math.copysign(1, float(val))
+        assert got == grid[int(code, 16)] and math.copysign(1, got) == math.copysign(1, grid[int(code, 16)])
+
+
+def test_e2m1_encode_is_nearest_ties_even_saturating(orc):
+    """Brute force over the 16 codes: nearest value, exact ties to the code with mantissa bit 0."""
+    grid = _e2m1_grid()
+    g = np.random.default_rng(71)
+    mids = (grid[:7] + grid[1:8]) / 2
+    x = np.concatenate([g.uniform(-7, 7, 3000), g.standard_normal(500) * 0.3, mids, -mids,
+                        grid[:8], -grid[:8], [6.5, 100.0, -1e9, 5.999, 0.2500001, 0.2499999]])
+    for v in x:
+        c = orc.f64_to_e2m1(v)
+        mag = min(abs(v), 6.0)
+        d = np.abs(grid[:8] - mag)
+        best = np.flatnonzero(d == d.min())
+        want = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
+        assert c & 7 == want, (v, c)
+        assert (c >> 3) == (1 if math.copysign(1, v) < 0 else 0)
+
+
+def test_mxfp4_block_scale_rule_and_codes(orc):
+    """Scale 2^(floor(log2 amax) - 2) puts amax/X in [4, 8); codes are nearest of v/X (brute force)."""
+    grid = _e2m1_grid()
+    g = np.random.default_rng(72)
+    for trial in range(300):
+        sc = 2.0 ** g.integers(-30, 30)
+        v = g.standard_normal(32) * sc
+        if trial % 7 == 0:
+            v[g.integers(0, 32)] = 2.0 ** g.integers(-20, 20)    # amax exactly a power of two
+        e, codes = orc.mxfp4_block(v)
+        X = 2.0 ** (e - 127)
+        amax = np.abs(v).max()
+        assert 4 <= amax / X < 8
+        for j in range(32):
+            mag = min(abs(v[j]) / X, 6.0)
+            d = np.abs(grid[:8] - mag)
+            best = np.flatnonzero(d == d.min())
+            want = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
+            assert codes[j] & 7 == want
+    # an all-zero block: scale byte 127 (2^0), zero codes
+    e, codes = orc.mxfp4_block(np.zeros(32))
+    assert e == 127 and not codes.any()
+    # values in [6, 8) x X saturate to +-6 X
+    v = np.zeros(32)
+    v[0], v[1] = 7.5, -7.0
+    e, codes = orc.mxfp4_block(v)
+    assert e == 127 and codes[0] == 7 and codes[1] == 15
+
+
+def test_mxfp4_block_roundtrip_exact_on_grid(orc):
+    """A block of E2M1 grid values times a common power of two is stored exactly."""
+    grid = _e2m1_grid()
+    g = np.random.default_rng(73)
+    for _ in range(200):
+        k = int(g.integers(-40, 40))
+        v = grid[g.integers(0, 16, 32)] * 2.0 ** k
+        if not np.any(v):
+            continue
+        e, codes = orc.mxfp4_block(v)
+        dec = np.array([orc.e2m1_to_f64(c) for c in codes]) * 2.0 ** (e - 127)
+        np.testing.assert_array_equal(np.abs(dec), np.abs(v))
+
+
+def test_compress_mxfp4_store_is_nearest_grid(orc):
+    """MXFP4 rows of the compressor: per 32-block, the decoded value is the nearest point of the
+    block's grid X * E2M1 to the fp32 row (ties excepted), X from the block's amax."""
+    dn, N = 128, 48
+    x = S.block_scaled(74, "kv", 0, N, dn)[None]
+    x[0, 3, 32:64] = 0.0
+    z = np.zeros_like(x)
+    f4 = orc.KV.empty(orc.MXFP4, 1, N, dn, 0)
+    orc.kv_compress(x, z, None, None, f4, m=1, overlap=0, first_pos=[0])
+    assert f4.scale[0, 3, 1] == 127 and not f4.nope[0, 3, 16:32].any()
+    dec = f4.decode(0)
+    grid = _e2m1_grid()
+    for r in range(N):
+        for blk in range(dn // 32):
+            v = x[0, r, 32 * blk:32 * blk + 32].astype(np.float64)
+            a = np.abs(v).max()
+            if a == 0:
+                continue
+            X = 2.0 ** (math.floor(math.log2(a)) - 2)
+            assert f4.scale[0, r, blk] == 127 + round(math.log2(X))
+            cand = np.sign(v)[:, None] * grid[None, :8] * X
+            dist = np.abs(cand - v[:, None])
+            got = dec[r, 32 * blk:32 * blk + 32]
+            assert np.all(np.abs(got - v) <= dist.min(1) * (1 + 1e-12) + 1e-300)
+    # byte packing: even element in the low nibble
+    e0 = orc.e2m1_to_f64(f4.nope[0, 0, 0] & 15) * 2.0 ** (int(f4.scale[0, 0, 0]) - 127)
+    e1 = orc.e2m1_to_f64(f4.nope[0, 0, 0] >> 4) * 2.0 ** (int(f4.scale[0, 0, 0]) - 127)
+    assert dec[0, 0] == e0 and dec[0, 1] == e1
+
+
+def _mxfp4_keys(orc, k):
+    """[B][N][d] f32 keys stored MXFP4 through the compressor at m = 1."""
+    B, N, d = k.shape
+    kv = orc.KV.empty(orc.MXFP4, B, N, d, 0)
+    orc.kv_compress(k, np.zeros_like(k), None, None, kv, m=1, overlap=0, first_pos=[0] * B)
+    return kv
+
+
+def test_indexer_mxfp4_on_grid_is_matrix_formula(orc):
+    """q and keys already on MXFP4 grids: the scores are the plain formula (numpy, fp64)."""
+    grid = _e2m1_grid()
+    g = np.random.default_rng(75)
+    B, T, H, d, m, N = 2, 9, 3, 64, 2, 12
+    eq = 2.0 ** g.integers(-3, 3, (B, T, H, d // 32))
+    q = (grid[g.integers(0, 16, (B, T, H, d))] * eq.repeat(32, -1)).astype(np.float32)
+    q[..., ::32] = 6.0 * eq                      # every block reaches its grid's top value
+    ek = 2.0 ** g.integers(-4, 4, (B, N, d // 32))
+    k = (grid[g.integers(0, 16, (B, N, d))] * ek.repeat(32, -1)).astype(np.float32)
+    k[..., ::32] = -4.0 * ek
+    w = _f32(B, T, H, seed=76)
+    kv = _mxfp4_keys(orc, k)
+    np.testing.assert_array_equal(kv.decode(0), k[0])
+    pos = [5, 20]
+    s = orc.indexer_score_mxfp4(q, w, kv, q_pos=pos, m=m, score_fmt=orc.F32)
+    for b in range(B):
+        dots = np.einsum("thd,nd->thn", q[b].astype(np.float64), k[b].astype(np.float64))
+        ref = np.einsum("th,thn->tn", w[b].astype(np.float64), np.maximum(dots, 0.0)).astype(np.float32)
+        for t in range(T):
+            vis = min(N, (pos[b] + t + 1) // m)
+            np.testing.assert_array_equal(s[b, t, :vis], ref[t, :vis] + np.float32(0))
+            assert not s[b, t, vis:].any()
+
+
+def test_indexer_mxfp4_quantises_q_per_head_block(orc):
+    """General bf16 q: the scores equal the formula on q quantised block by block (each block's
+    quantisation pinned above) and the stored keys; bf16 scores are RNE of the f32 ones."""
+    B, T, H, d, m, N = 1, 7, 4, 128, 1, 7
+    q = S.to_bf16(_f32(B, T, H, d, seed=77) * 3)
+    k = _f32(B, N, d, seed=78)
+    w = _f32(B, T, H, seed=79)
+    kv = _mxfp4_keys(orc, k)
+    qf = np.array([orc.bf16_to_f64(h) for h in q.reshape(-1)]).reshape(q.shape)
+    codes, scales = orc.mxfp4_quantize(qf)
+    grid = _e2m1_grid()
+    qd = grid[codes] * (2.0 ** (scales.astype(np.float64) - 127)).repeat(32, -1)
+    kd = kv.decode(0)
+    s = orc.indexer_score_mxfp4(q, w, kv, q_pos=[0], m=m, score_fmt=orc.F32)
+    sb = orc.indexer_score_mxfp4(q, w, kv, q_pos=[0], m=m, score_fmt=orc.BF16)
+    dots = np.einsum("thd,nd->thn", qd[0], kd)
+    ref = np.einsum("th,thn->tn", w[0].astype(np.float64), np.maximum(dots, 0.0))
+    for t in range(T):
+        np.testing.assert_allclose(s[0, t, :t + 1], ref[t, :t + 1], rtol=1e-6, atol=1e-6)
+        assert np.array_equal(sb[0, t, :t + 1], S.to_bf16(s[0, t, :t + 1] + np.float32(0)))
+    # and the MXFP4 scores track the full-precision scores of the same inputs
+    k2 = _f32(1, 512, d, seed=80)
+    e = orc.indexer_score(q, w, S.to_bf16(k2), q_pos=[600], m=m, score_fmt=orc.F32)
+    f = orc.indexer_score_mxfp4(q, w, _mxfp4_keys(orc, k2), q_pos=[600], m=m, score_fmt=orc.F32)
+    for t in range(T):
+        assert np.corrcoef(e[0, t], f[0, t])[0, 1] > 0.95
