@@ -29,12 +29,20 @@
  *   vis(t) = floor((t + 1) / m) entries are visible.
  *
  * KV storage (lca_kv) -- [R] 2.3.4: FP8 storage for most dims, BF16 for the
- * RoPE dims.  Three formats, as planes of one row per entry:
+ * RoPE dims; [R] 5.2.1: the indexer's QK path in FP4 (MXFP4).  Four formats,
+ * as planes of one row per entry:
  *   LCA_F32 : nope f32 [B][cap][d_nope], rope f32 [B][cap][d_rope]
  *   LCA_BF16: nope bf16, rope bf16
  *   LCA_FP8 : nope OCP e4m3fn bytes [B][cap][d_nope] with one f32 power-of-two
  *             scale per 128 nope dims, scale [B][cap][d_nope/128]; rope bf16.
  *             Stored value = code * scale (exact in bf16).
+ *   LCA_MXFP4: OCP MXFP4 (Microscaling Formats v1.0), indexer keys only:
+ *             nope = bytes [B][cap][d_nope/2] holding two FP4 E2M1 codes each
+ *             (element 2i in the low nibble of byte i), scale = uint8 E8M0
+ *             bytes [B][cap][d_nope/32] (block exponent e stored as e + 127);
+ *             d_rope = 0, d_nope % 32 == 0.  Stored value = E2M1(code) * 2^e.
+ *             Rows are written by lca_kv_compress, read by
+ *             lca_indexer_score_mxfp4; the attention calls reject them.
  * The attended vector of a row is nope ++ rope (c = d_nope + d_rope dims).
  */
 #ifndef LCA_H
@@ -63,12 +71,14 @@ extern "C" {
 #define LCA_F32 0
 #define LCA_BF16 1
 #define LCA_FP8 2         /* KV storage only (see above)                   */
+#define LCA_MXFP4 3       /* indexer-key storage only (see above)          */
 
 typedef struct lca_kv {
     void* nope;       /* [B][cap][d_nope]                                  */
     void* rope;       /* [B][cap][d_rope]; may be NULL when d_rope == 0    */
-    float* scale;     /* [B][cap][d_nope/128] for LCA_FP8, else NULL       */
-    int32_t fmt;      /* LCA_F32 / LCA_BF16 / LCA_FP8                      */
+    void* scale;      /* f32 [B][cap][d_nope/128] for LCA_FP8, uint8
+                         [B][cap][d_nope/32] for LCA_MXFP4, else NULL      */
+    int32_t fmt;      /* LCA_F32 / LCA_BF16 / LCA_FP8 / LCA_MXFP4          */
     int32_t d_nope;
     int32_t d_rope;   /* even                                              */
     int64_t cap;      /* rows per sequence (batch stride = cap rows)       */
@@ -101,6 +111,11 @@ typedef struct lca_kv {
  * LCA_ESHAPE (0 < in_stride < n_rows, ...),
  * LCA_ESHAPE (B out of range, c != d_nope + d_rope, fp8 with d_nope % 128,
  * a non-ring entry row >= cap), LCA_EALIGN.
+ * MXFP4 output (the indexer keys): every 32 dims share the exponent
+ * e = floor(log2 amax) - 2 of their largest magnitude (clamped to [-127, 127];
+ * 0 for an all-zero block) and each value is stored as the E2M1 code nearest
+ * to value * 2^-e (ties to the even code, saturating at 6).  Needs
+ * out.d_rope == 0 and out.d_nope % 32 == 0 (else LCA_ESHAPE).
  */
 int lca_kv_compress(const void* c_a, const void* z_a, const void* c_b, const void* z_b,
                     int32_t in_dtype, const float* bias_a, const float* bias_b,
@@ -126,6 +141,23 @@ int lca_indexer_score(const void* q, const float* w, const void* k, int32_t in_d
                       int64_t k_cap, int32_t H_I, int32_t d_I, int32_t B, int32_t T,
                       const int64_t* q_pos, int32_t m, void* scores, int32_t score_dtype,
                       int64_t s_stride, void* stream);
+
+/*
+ * lca_indexer_score_mxfp4 -- the same scores with the QK path in FP4
+ * ([R] 5.2.1: the indexer's query and key activations are cached, loaded and
+ * multiplied in MXFP4).  q: bf16 [B][T][H_I][d_I]; each head's 32-element
+ * blocks are quantised to MXFP4 inside the call by the rule stated for
+ * lca_kv_compress (bf16 in, so the codes are exact functions of the input).
+ * k: MXFP4 key rows (k.fmt == LCA_MXFP4, k.d_nope == d_I, k.d_rope == 0,
+ * k.cap rows per sequence), as written by lca_kv_compress.  The products of
+ * the decoded values are accumulated in f32; w, scores, s_stride and the
+ * visibility rule as for lca_indexer_score.  Supports H_I = 16, d_I = 128.
+ * Errors: LCA_EINVAL (NULL pointers, m < 1), LCA_EDTYPE (k not MXFP4, score
+ * dtype), LCA_ESHAPE (H_I / d_I, vis beyond k.cap or s_stride, B), LCA_EALIGN.
+ */
+int lca_indexer_score_mxfp4(const void* q, const float* w, lca_kv k, int32_t H_I, int32_t d_I, int32_t B,
+                            int32_t T, const int64_t* q_pos, int32_t m, void* scores, int32_t score_dtype,
+                            int64_t s_stride, void* stream);
 
 /*
  * lca_topk_select -- the top-k selector of [R] 2.3.1 (keeps a subset of the

@@ -5,7 +5,7 @@ kernels.  torch supplies device memory and the current stream.  There is no
 fallback: when the built library is missing every call raises.
 
 Calls (same names as the C ABI):
-    kv_compress, indexer_score, topk_select, csa_attn, hca_attn
+    kv_compress, indexer_score, indexer_score_mxfp4, topk_select, csa_attn, hca_attn
 and helpers KV (the lca_kv storage planes), attn_workspace_size.
 """
 from __future__ import annotations
@@ -16,7 +16,7 @@ from dataclasses import dataclass
 
 import torch
 
-F32, BF16, FP8 = 0, 1, 2
+F32, BF16, FP8, MXFP4 = 0, 1, 2, 3
 MAX_BATCH = 64
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblca.so")
@@ -50,6 +50,7 @@ def lib():
                                       vp, _KV, i32, vp]
         L.lca_indexer_score.argtypes = [vp, vp, vp, i32, i64, i32, i32, i32, i32, vp, i32, vp, i32, i64,
                                         vp]
+        L.lca_indexer_score_mxfp4.argtypes = [vp, vp, _KV, i32, i32, i32, i32, vp, i32, vp, i32, i64, vp]
         L.lca_topk_select.argtypes = [vp, i32, i64, i32, i32, vp, i32, i32, vp, vp, sz, vp]
         L.lca_topk_workspace_size.argtypes = [i32, i32, i64, i32]
         L.lca_topk_workspace_size.restype = sz
@@ -59,8 +60,8 @@ def lib():
                                    vp, vp, sz, vp]
         L.lca_attn_workspace_size.argtypes = [i32, i32, i32, i32, i64]
         L.lca_attn_workspace_size.restype = sz
-        for name in ("lca_kv_compress", "lca_indexer_score", "lca_topk_select", "lca_csa_attn",
-                     "lca_hca_attn"):
+        for name in ("lca_kv_compress", "lca_indexer_score", "lca_indexer_score_mxfp4", "lca_topk_select",
+                     "lca_csa_attn", "lca_hca_attn"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -96,7 +97,8 @@ def _check(rc: int):
 
 @dataclass
 class KV:
-    """Storage planes of one KV stream: nope [B][cap][d_nope], rope [B][cap][d_rope], scale [B][cap][d_nope/128]."""
+    """Storage planes of one KV stream: nope [B][cap][d_nope], rope [B][cap][d_rope], scale [B][cap][d_nope/128]
+    (fp8); MXFP4: nope uint8 [B][cap][d_nope/2] (two E2M1 codes per byte), scale uint8 [B][cap][d_nope/32]."""
     nope: torch.Tensor
     rope: torch.Tensor | None
     scale: torch.Tensor | None
@@ -119,9 +121,13 @@ class KV:
             nope = torch.zeros(B, cap, d_nope, dtype=torch.uint8, device=device)
             rope = torch.zeros(B, cap, d_rope, dtype=torch.bfloat16, device=device)
             scale = torch.ones(B, cap, d_nope // 128, dtype=torch.float32, device=device)
+        elif fmt == MXFP4:
+            nope = torch.zeros(B, cap, d_nope // 2, dtype=torch.uint8, device=device)
+            rope = None
+            scale = torch.full((B, cap, d_nope // 32), 127, dtype=torch.uint8, device=device)
         else:
             raise ValueError(fmt)
-        return KV(nope, rope if d_rope > 0 else None, scale, fmt, d_nope, d_rope, cap)
+        return KV(nope, rope if rope is not None and d_rope > 0 else None, scale, fmt, d_nope, d_rope, cap)
 
     @property
     def B(self) -> int:
@@ -156,6 +162,15 @@ def indexer_score(q, w, k, scores, *, q_pos, m: int, stream=None):
     _check(lib().lca_indexer_score(_ptr(q), _ptr(w), _ptr(k), _dtype(q), int(k.shape[1]), int(H_I),
                                    int(d_I), int(B), int(T), _pos(q_pos, B), int(m), _ptr(scores),
                                    _dtype(scores), int(scores.shape[2]), _stream(stream)))
+
+
+def indexer_score_mxfp4(q, w, k: KV, scores, *, q_pos, m: int, stream=None):
+    """q [B][T][H_I][d_I] bf16 (quantised to MXFP4 in the call), w [B][T][H_I] f32 or None, k MXFP4 key
+    rows (KV with fmt MXFP4), scores [B][T][s_stride]."""
+    B, T, H_I, d_I = q.shape
+    _check(lib().lca_indexer_score_mxfp4(_ptr(q), _ptr(w), k.c(), int(H_I), int(d_I), int(B), int(T),
+                                         _pos(q_pos, B), int(m), _ptr(scores), _dtype(scores),
+                                         int(scores.shape[2]), _stream(stream)))
 
 
 def topk_select(scores, idx, *, q_pos, m: int, ws=None, stream=None):

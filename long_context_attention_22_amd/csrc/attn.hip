@@ -1243,7 +1243,7 @@ __global__ void __launch_bounds__(256) kv_expand(ExpandArgs a) {
     const int64_t sr = (int64_t)b * a.src.cap + p % a.src.cap;
     const int64_t dr = (int64_t)b * a.dst.cap + p % a.dst.cap;
     const u32x4 codes = ((const u32x4*)((const uint8_t*)a.src.nope + sr * kDN))[c];
-    const float sc = a.src.scale[sr * 4 + (c >> 3)];
+    const float sc = ((const float*)a.src.scale)[sr * 4 + (c >> 3)];
     u32x4 lo, hi;
     lo[0] = fp8x2_bf16<false>(codes[0], sc);
     lo[1] = fp8x2_bf16<true>(codes[0], sc);

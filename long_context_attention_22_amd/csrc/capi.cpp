@@ -25,18 +25,23 @@ int fail(int code, const char* fmt, ...) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-int check_kv(const lca_kv& kv, const char* name, bool need_rows) {
-    if (kv.fmt != LCA_F32 && kv.fmt != LCA_BF16 && kv.fmt != LCA_FP8)
+int check_kv(const lca_kv& kv, const char* name, bool need_rows, bool allow_fp4) {
+    if (kv.fmt == LCA_MXFP4 && !allow_fp4)
+        return fail(LCA_EDTYPE, "%s: MXFP4 storage holds indexer keys only", name);
+    if (kv.fmt != LCA_F32 && kv.fmt != LCA_BF16 && kv.fmt != LCA_FP8 && kv.fmt != LCA_MXFP4)
         return fail(LCA_EDTYPE, "%s: unknown storage format %d", name, kv.fmt);
     if (kv.d_nope < 0 || kv.d_rope < 0 || (kv.d_rope & 1) || kv.d_nope + kv.d_rope < 1 ||
         kv.d_nope + kv.d_rope > 1024)
         return fail(LCA_ESHAPE, "%s: bad dims d_nope=%d d_rope=%d", name, kv.d_nope, kv.d_rope);
     if (kv.fmt == LCA_FP8 && (kv.d_nope % 128 != 0 || kv.d_nope == 0))
         return fail(LCA_ESHAPE, "%s: fp8 storage needs d_nope a positive multiple of 128", name);
+    if (kv.fmt == LCA_MXFP4 && (kv.d_rope != 0 || kv.d_nope % 32 != 0))
+        return fail(LCA_ESHAPE, "%s: MXFP4 storage needs d_rope = 0 and d_nope a multiple of 32", name);
     if (need_rows && kv.cap < 1) return fail(LCA_ESHAPE, "%s: cap must be >= 1", name);
     if (!kv.nope && kv.d_nope > 0) return fail(LCA_EINVAL, "%s: nope plane is NULL", name);
     if (!kv.rope && kv.d_rope > 0) return fail(LCA_EINVAL, "%s: rope plane is NULL", name);
-    if (kv.fmt == LCA_FP8 && !kv.scale) return fail(LCA_EINVAL, "%s: fp8 storage needs scales", name);
+    if ((kv.fmt == LCA_FP8 || kv.fmt == LCA_MXFP4) && !kv.scale)
+        return fail(LCA_EINVAL, "%s: fp8 / MXFP4 storage needs scales", name);
     if (!aligned16(kv.nope) || !aligned16(kv.rope) || !aligned16(kv.scale))
         return fail(LCA_EALIGN, "%s: planes must be 16-byte aligned", name);
     return LCA_OK;
@@ -96,7 +101,7 @@ int lca_kv_compress(const void* c_a, const void* z_a, const void* c_b, const voi
     if (!(eps >= 0.0f)) return fail(LCA_EINVAL, "eps must be >= 0");
     int rc = check_batch(B, first_pos, "first_pos");
     if (rc) return rc;
-    if ((rc = check_kv(out, "out", true))) return rc;
+    if ((rc = check_kv(out, "out", true, true))) return rc;
     if (rope_theta > 0.0 && out.d_rope > 2 * lca::kMaxRopeHalf)
         return fail(LCA_ESHAPE, "RoPE supports d_rope <= %d", 2 * lca::kMaxRopeHalf);
     for (const void* p : {c_a, z_a, c_b, z_b, (const void*)bias_a, (const void*)bias_b, (const void*)gamma})
@@ -164,6 +169,38 @@ int lca_indexer_score(const void* q, const float* w, const void* k, int32_t in_d
     return hip_status(lca::launch_indexer(a, (hipStream_t)stream));
 }
 
+int lca_indexer_score_mxfp4(const void* q, const float* w, lca_kv k, int32_t H_I, int32_t d_I, int32_t B,
+                            int32_t T, const int64_t* q_pos, int32_t m, void* scores, int32_t score_dtype,
+                            int64_t s_stride, void* stream) {
+    g_err[0] = 0;
+    if (!q || !scores) return fail(LCA_EINVAL, "q and scores must be non-NULL");
+    if (m < 1) return fail(LCA_EINVAL, "m must be >= 1");
+    if (k.fmt != LCA_MXFP4) return fail(LCA_EDTYPE, "keys must be stored MXFP4 (fmt %d)", LCA_MXFP4);
+    int rc = check_kv(k, "k", true, true);
+    if (rc) return rc;
+    if (score_dtype != LCA_BF16 && score_dtype != LCA_F32) return fail(LCA_EDTYPE, "score_dtype must be bf16 or f32");
+    if (H_I != 16 || d_I != 128 || k.d_nope != d_I)
+        return fail(LCA_ESHAPE, "MXFP4 indexer supports H_I = 16, d_I = k.d_nope = 128 (got %d x %d, keys %d)", H_I,
+                    d_I, k.d_nope);
+    if (T < 0 || s_stride < 1) return fail(LCA_ESHAPE, "bad T / s_stride");
+    if ((rc = check_batch(B, q_pos, "q_pos"))) return rc;
+    if (!aligned16(q) || !aligned16(w) || !aligned16(scores)) return fail(LCA_EALIGN, "pointers must be 16-byte aligned");
+    int64_t max_vis = 0;
+    for (int b = 0; b < B && T > 0; ++b) {
+        const int64_t vis = (q_pos[b] + T) / m;
+        if (vis > k.cap || vis > s_stride)
+            return fail(LCA_ESHAPE, "sequence %d sees %lld entries: more than k.cap %lld or s_stride %lld", b,
+                        (long long)vis, (long long)k.cap, (long long)s_stride);
+        if (vis > max_vis) max_vis = vis;
+    }
+    lca::IndexerArgs a;
+    memset(&a, 0, sizeof a);
+    a.q = q; a.w = w; a.k = k.nope; a.k_scale = k.scale; a.in_dtype = LCA_MXFP4; a.k_cap = k.cap;
+    a.H_I = H_I; a.d_I = d_I; a.B = B; a.T = T; a.m = m; a.scores = scores; a.score_dtype = score_dtype;
+    a.s_stride = s_stride; a.q_pos = to_pos(q_pos, B); a.max_vis = max_vis;
+    return hip_status(lca::launch_indexer(a, (hipStream_t)stream));
+}
+
 size_t lca_topk_workspace_size(int32_t B, int32_t T, int64_t s_stride, int32_t) {
     if (B < 1 || T < 1 || s_stride < 1) return 0;
     return lca::topk_ws_bytes(B, T, s_stride, LCA_BF16);
@@ -226,9 +263,9 @@ static int attn_common(const void* q, int32_t q_dtype, int32_t H, int32_t B, int
     if (out_dtype != LCA_F32 && out_dtype != LCA_BF16) return fail(LCA_EDTYPE, "out_dtype must be f32 or bf16");
     int rc = check_batch(B, q_pos, "q_pos");
     if (rc) return rc;
-    if ((rc = check_kv(comp, "comp", true))) return rc;
+    if ((rc = check_kv(comp, "comp", true, false))) return rc;
     if (n_win > 0) {
-        if ((rc = check_kv(win, "win", true))) return rc;
+        if ((rc = check_kv(win, "win", true, false))) return rc;
         if (win.fmt != comp.fmt || win.d_nope != comp.d_nope || win.d_rope != comp.d_rope)
             return fail(LCA_ESHAPE, "window and compressed caches must share format and dims");
         for (int b = 0; b < B; ++b) {  // rows [q_pos - n_win + 1, q_pos + T - 1] that exist

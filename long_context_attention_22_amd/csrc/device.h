@@ -1,5 +1,5 @@
 // device.h -- gfx950 device helpers shared by the library's kernels:
-// bf16 / OCP-e4m3fn conversions, wave reductions, MFMA fragment types.
+// bf16 / OCP-e4m3fn / MXFP4 conversions, wave reductions, MFMA fragment types.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -48,6 +48,27 @@ __device__ __forceinline__ uint32_t f32_to_fp8(float x) {
     }
     code = code > 126u ? 126u : code;
     return code | s;
+}
+
+// OCP MXFP4 (Microscaling Formats v1.0): blocks of 32 elements share an E8M0 scale 2^e and each
+// element is an FP4 E2M1 code (sign, 2 exponent bits with bias 1, 1 mantissa bit; values
+// 0, 0.5, 1, 1.5, 2, 3, 4, 6).  The block exponent puts the largest magnitude in [4, 8):
+// e = floor(log2 amax) - 2, clamped to the E8M0 range [-127, 127]; an all-zero block gets e = 0.
+__device__ __forceinline__ int mx_block_exp(float amax) {
+    if (!(amax > 0.0f)) return 0;
+    int ex = 0;
+    frexpf(amax, &ex);  // amax in [2^(ex-1), 2^ex)
+    const int e = ex - 3;
+    return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+// E2M1 code of x (already divided by the block scale): the nearest value, an exact tie going to
+// the even code, magnitudes beyond 6 saturating; the sign bit is copied from x.  Each term adds
+// one code step at the midpoint between neighbouring values (strict where the upper neighbour
+// has an odd code, inclusive where it is even).
+__device__ __forceinline__ uint32_t e2m1_code(float x) {
+    const float a = fabsf(x);
+    uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
+    return c | ((__float_as_uint(x) >> 28) & 8u);
 }
 
 template <typename T>
@@ -131,6 +152,27 @@ __device__ __forceinline__ float xlane16(float v, bool mx) {  // combine with la
 // over the four 16-lane groups: every lane gets the same value, summed in the same order
 __device__ __forceinline__ float max4g(float v) { return xlane32(xlane16(v, true), true); }
 __device__ __forceinline__ float sum4g(float v) { return xlane32(xlane16(v, false), false); }
+// bitwise OR over the eight lanes of each aligned group of 8 (quad swaps, then the half-row mirror)
+__device__ __forceinline__ uint32_t or8(uint32_t v) {
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xb1, 0xf, 0xf, false);   // quad_perm [1,0,3,2]
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4e, 0xf, 0xf, false);   // quad_perm [2,3,0,1]
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false);  // row_half_mirror
+    return v;
+}
+// One MXFP4 block per 32 lanes (lanes 0-31 and 32-63 of the wave hold elements 0..31 of two
+// blocks, one value each; lanes past the row hold 0).  Every lane of the wave must call this.
+// Lane 0 / 32 stores the block's E8M0 byte at scales[blk]; lanes 8i store the 32-bit word of
+// codes of elements 8i..8i+7 (element 8i + n in bits 4n) at codes[word].
+__device__ __forceinline__ void mxfp4_store_lane(float y, bool live, uint8_t* scales, int64_t blk, uint32_t* codes,
+                                                 int64_t word) {
+    const int lane = threadIdx.x & 63;
+    const float amax = xlane16(row_max16(fabsf(y)), true);  // over this lane's 32-lane half
+    const int e = mx_block_exp(amax);
+    const uint32_t w = or8(e2m1_code(ldexpf(y, -e)) << (4 * (lane & 7)));
+    if (live && (lane & 7) == 0) codes[word] = w;
+    if (live && (lane & 31) == 0) scales[blk] = (uint8_t)(e + 127);
+}
+
 // whole-wave reductions without LDS: DPP within each 16-lane row, then the row swaps
 __device__ __forceinline__ float wave_max_dpp(float v) { return max4g(row_max16(v)); }
 __device__ __forceinline__ float wave_sum_dpp(float v) { return sum4g(row_sum16(v)); }

@@ -13,6 +13,14 @@
 // per token with one coalesced store.  Key chunks beyond the last token's
 // visible count are skipped (causal tile skip).
 //
+// MXFP4 path (section 5.2.1: the QK path in FP4): the keys are stored MXFP4
+// (64 bytes of E2M1 codes and 4 E8M0 scale bytes per key) and every query
+// head is quantised to MXFP4 in the prologue.  One
+// v_mfma_scale_f32_16x16x128_f8f6f4 with FP4 A and B covers 16 heads x 16 keys
+// x d_I = 128: lane l supplies head (A) or key (B) l & 15, elements
+// [32 (l >> 4), +32) as 16 bytes of packed codes, and that block's scale byte.
+// Same grid, epilogue and causal skip as the bf16 path.
+//
 // f32 path: one thread per (token, key), f32 FMA (used for fp32 workloads).
 #include "device.h"
 #include "kernels.h"
@@ -114,6 +122,128 @@ __global__ void __launch_bounds__(256) indexer_mfma(IndexerArgs a, int64_t keys_
     }
 }
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+template <int TOK, typename TS>
+__global__ void __launch_bounds__(256) indexer_fp4(IndexerArgs a, int64_t keys_per_wg) {
+    const int b = blockIdx.z;
+    const int i0 = blockIdx.y * TOK;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int T = a.T, m = a.m;
+    const int64_t p0 = a.q_pos.v[b], k_cap = a.k_cap, s_stride = a.s_stride;
+    const void *pq = a.q, *pk = a.k, *pks = a.k_scale, *psc = a.scores;
+    const float* pw = a.w;
+    asm volatile("" ::"s"(T), "s"(m), "s"(p0), "s"(k_cap), "s"(s_stride), "s"(pq), "s"(pk), "s"(pks), "s"(psc),
+                 "s"(pw));
+    const int ntok = min(TOK, T - i0);
+    const int64_t pos0 = p0 + i0;
+    const int64_t vis_last = min(vis_of(pos0 + ntok, m), k_cap);
+    const int64_t key_lo = (int64_t)blockIdx.x * keys_per_wg;
+    const int64_t key_hi = min(key_lo + keys_per_wg, vis_last);
+    if (key_lo >= key_hi) return;
+
+    const int hrow = lane & 15, kgrp = lane >> 4;
+    // this lane's head and 32-element block of each token's q (bf16), and the head weights.  All
+    // loads are branch-free (rows past the last token re-read it and get weight 0; keys past the
+    // range re-read its last key and are never stored), so the waits count them exactly.
+    u32x4 qraw[TOK][4];
+    float wt[TOK][4];
+#pragma unroll
+    for (int tk = 0; tk < TOK; ++tk) {
+        const int64_t qi = ((int64_t)b * T + i0 + min(tk, ntok - 1)) * kIdxH;
+        const u32x4* qp = (const u32x4*)((const uint16_t*)pq + (qi + hrow) * kIdxD + 32 * kgrp);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) qraw[tk][r] = qp[r];
+        // (with no weights the load reads q's own memory, which is larger, and is discarded)
+        const float* wsrc = pw ? pw : (const float*)pq;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float wv_ = wsrc[qi + 4 * kgrp + r];
+            wt[tk][r] = tk < ntok ? (pw ? wv_ : 1.0f) : 0.0f;
+        }
+    }
+
+    const uint8_t* kbase = (const uint8_t*)pk + (int64_t)b * k_cap * (kIdxD / 2);
+    const uint32_t* ksbase = (const uint32_t*)pks + (int64_t)b * k_cap;  // 4 scale bytes per key
+    TS* sbase = (TS*)psc + ((int64_t)b * T + i0) * s_stride;
+
+    // the first key tile goes out before q is quantised, so the two latencies overlap
+    int64_t c0 = key_lo + 64 * wv;
+    u32x4 kc[4];
+    uint32_t ks[4];
+#pragma unroll
+    for (int bl = 0; bl < 4; ++bl) {
+        const int64_t key = min(c0 + 16 * bl + hrow, key_hi - 1);
+        kc[bl] = *(const u32x4*)(kbase + key * (kIdxD / 2) + 16 * kgrp);
+        ks[bl] = ksbase[key];
+    }
+    asm volatile("" ::: "memory");
+
+    // MXFP4 quantisation of q: block exponent from the largest magnitude (bf16 bit patterns of
+    // finite values order like their magnitudes), then the E2M1 code of each element
+    i32x8 qa[TOK];
+    int qsc[TOK];
+#pragma unroll
+    for (int tk = 0; tk < TOK; ++tk) {
+        uint32_t am = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t w = qraw[tk][r][i];
+                am = max(am, max(w & 0x7fffu, (w >> 16) & 0x7fffu));
+            }
+        const int ex = mx_block_exp(__uint_as_float(am << 16));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {  // word r: elements 8r .. 8r + 7, element 8r + n in bits 4n
+            uint32_t word = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t w = qraw[tk][r][i];
+                word |= e2m1_code(ldexpf(bf2f((uint16_t)(w & 0xffffu)), -ex)) << (8 * i);
+                word |= e2m1_code(ldexpf(bf2f((uint16_t)(w >> 16)), -ex)) << (8 * i + 4);
+            }
+            qa[tk][r] = (int)word;
+            qa[tk][r + 4] = 0;
+        }
+        qsc[tk] = ex + 127;
+    }
+
+    for (;;) {
+        const int64_t mykey = c0 + lane;  // the score this lane stores
+#pragma unroll
+        for (int tk = 0; tk < TOK; ++tk) {
+            float mine = 0.0f;
+#pragma unroll
+            for (int bl = 0; bl < 4; ++bl) {
+                const i32x8 kb = {(int)kc[bl][0], (int)kc[bl][1], (int)kc[bl][2], (int)kc[bl][3], 0, 0, 0, 0};
+                f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+                acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[tk], kb, acc, 4, 4, 0, qsc[tk], 0,
+                                                                       (int)(ks[bl] >> (8 * kgrp)));
+                // lane holds heads 4*kgrp + r of key 16 bl + hrow
+                float v = wt[tk][0] * fmaxf(acc[0], 0.0f);
+                v = fmaf(wt[tk][1], fmaxf(acc[1], 0.0f), v);
+                v = fmaf(wt[tk][2], fmaxf(acc[2], 0.0f), v);
+                v = fmaf(wt[tk][3], fmaxf(acc[3], 0.0f), v);
+                v = sum4g(v);
+                if (kgrp == bl) mine = v;
+            }
+            if (tk < ntok) {
+                const int64_t vis_t = min(vis_of(pos0 + tk + 1, m), k_cap);
+                if (mykey < vis_t) store_score<TS>(sbase + (int64_t)tk * s_stride + mykey, mine);
+            }
+        }
+        c0 += 256;
+        if (c0 >= key_hi) break;
+#pragma unroll
+        for (int bl = 0; bl < 4; ++bl) {
+            const int64_t key = min(c0 + 16 * bl + hrow, key_hi - 1);
+            kc[bl] = *(const u32x4*)(kbase + key * (kIdxD / 2) + 16 * kgrp);
+            ks[bl] = ksbase[key];
+        }
+    }
+}
+
 template <typename TIn, typename TS>
 __global__ void __launch_bounds__(256) indexer_f32(IndexerArgs a) {
     const int b = blockIdx.z, i = blockIdx.y;
@@ -142,6 +272,7 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t st) {
         else hipLaunchKernelGGL((indexer_f32<float, float>), grid, dim3(256), 0, st, a);
         return hipGetLastError();
     }
+    const bool fp4 = a.in_dtype == LCA_MXFP4;
     const int tok = a.T >= 64 ? 8 : 1;
     const int64_t groups = ((int64_t)a.T + tok - 1) / tok;
     // enough workgroups to cover the chip: split the key range in 256-key multiples
@@ -151,7 +282,15 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t st) {
     if (kpw < 256) kpw = 256;
     const int64_t nsplit = (a.max_vis + kpw - 1) / kpw;
     dim3 grid((unsigned)nsplit, (unsigned)groups, (unsigned)a.B);
-    if (tok == 8) {
+    if (fp4) {
+        if (tok == 8) {
+            if (bf_scores) hipLaunchKernelGGL((indexer_fp4<8, uint16_t>), grid, dim3(256), 0, st, a, kpw);
+            else hipLaunchKernelGGL((indexer_fp4<8, float>), grid, dim3(256), 0, st, a, kpw);
+        } else {
+            if (bf_scores) hipLaunchKernelGGL((indexer_fp4<1, uint16_t>), grid, dim3(256), 0, st, a, kpw);
+            else hipLaunchKernelGGL((indexer_fp4<1, float>), grid, dim3(256), 0, st, a, kpw);
+        }
+    } else if (tok == 8) {
         if (bf_scores) hipLaunchKernelGGL((indexer_mfma<8, uint16_t>), grid, dim3(256), 0, st, a, kpw);
         else hipLaunchKernelGGL((indexer_mfma<8, float>), grid, dim3(256), 0, st, a, kpw);
     } else {

@@ -46,6 +46,7 @@ struct IndexerArgs {
     const void* q;
     const float* w;
     const void* k;
+    const void* k_scale;  // E8M0 bytes of MXFP4 keys (in_dtype == LCA_MXFP4: bf16 q, MXFP4 keys)
     int32_t in_dtype;
     int64_t k_cap;
     int32_t H_I, d_I, B, T, m;

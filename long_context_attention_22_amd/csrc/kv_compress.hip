@@ -1,7 +1,9 @@
 // kv_compress.hip -- the compressor of the DeepSeek-V4 hybrid attention
 // ("DeepSeek-V4 中文翻译", sections 2.3.1 / 2.3.2 / 2.3.3): softmax-gated pooling
-// with a per-position bias, RMSNorm, partial RoPE and the store (f32, bf16 or
-// fp8-e4m3fn with a power-of-two scale per 128 dims and bf16 RoPE dims).
+// with a per-position bias, RMSNorm, partial RoPE and the store (f32, bf16,
+// fp8-e4m3fn with a power-of-two scale per 128 dims and bf16 RoPE dims, or
+// MXFP4 for the indexer keys, section 5.2.1: E2M1 codes with one E8M0 scale
+// per 32 dims).
 //
 // HBM-bound: every input element is read exactly once.  One workgroup per
 // (entry, sequence); thread j owns channel j, so each wave reads 64
@@ -132,10 +134,13 @@ __global__ void __launch_bounds__(1024) kv_compress_kernel(CompressArgs a) {
             }
             const float inv = 1.0f / scale;  // exact: power of two
             ((uint8_t*)a.out.nope)[row * d_nope + j] = (uint8_t)f32_to_fp8(y * inv);
-            if ((j & 127) == 0) a.out.scale[row * (d_nope >> 7) + g] = scale;
+            if ((j & 127) == 0) ((float*)a.out.scale)[row * (d_nope >> 7) + g] = scale;
         } else if (j < c) {
             ((uint16_t*)a.out.rope)[row * d_rope + (j - d_nope)] = f2bf(y);
         }
+    } else if (FMT == LCA_MXFP4) {  // d_rope == 0, c % 32 == 0: a 32-channel block is half a wave
+        mxfp4_store_lane(y, j < c, (uint8_t*)a.out.scale + row * (c >> 5), j >> 5,
+                         (uint32_t*)a.out.nope + row * (c >> 3), j >> 3);
     } else if (FMT == LCA_BF16) {
         if (j < d_nope) ((uint16_t*)a.out.nope)[row * d_nope + j] = f2bf(y);
         else if (j < c) ((uint16_t*)a.out.rope)[row * d_rope + (j - d_nope)] = f2bf(y);
@@ -164,7 +169,7 @@ __global__ void __launch_bounds__(64) kv_store_rows(CompressArgs a) {
     const int ring = a.ring;
     void* const onope = a.out.nope;
     void* const orope = a.out.rope;
-    float* const oscale = a.out.scale;
+    void* const oscale = a.out.scale;
     const int half = d_rope >> 1;
     // this lane's RoPE pair index (channel d_nope + lane, when lane < d_rope <= 64)
     const int ri = half > 0 ? (lane < half ? lane : lane - half) : 0;
@@ -241,7 +246,7 @@ __global__ void __launch_bounds__(64) kv_store_rows(CompressArgs a) {
                 e8 = (amax <= ldexpf(1.75f, e)) ? e - 8 : e - 7;
             }
             isc[g2] = ldexpf(1.0f, -e8);
-            if (lane == 0 && 128 * g2 < d_nope) oscale[row * (d_nope >> 7) + g2] = ldexpf(1.0f, e8);
+            if (lane == 0 && 128 * g2 < d_nope) ((float*)oscale)[row * (d_nope >> 7) + g2] = ldexpf(1.0f, e8);
         }
 #pragma unroll
         for (int j = 0; j < J; ++j) {
@@ -250,6 +255,13 @@ __global__ void __launch_bounds__(64) kv_store_rows(CompressArgs a) {
                 ((uint8_t*)onope)[row * d_nope + ch] = (uint8_t)f32_to_fp8(y[j] * isc[j >> 1]);
             else if (ch < c)
                 ((uint16_t*)orope)[row * d_rope + (ch - d_nope)] = f2bf(y[j]);
+        }
+    } else if (FMT == LCA_MXFP4) {  // d_rope == 0, c % 32 == 0
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int ch = lane + 64 * j;
+            mxfp4_store_lane(y[j], ch < c, (uint8_t*)oscale + row * (c >> 5), ch >> 5,
+                             (uint32_t*)onope + row * (c >> 3), ch >> 3);
         }
     } else {
 #pragma unroll
@@ -290,6 +302,10 @@ hipError_t launch_kv_compress(const CompressArgs& a, hipStream_t st) {
                 if (bf) launch_store_rows<uint16_t, LCA_BF16>(a, c, grid, st);
                 else launch_store_rows<float, LCA_BF16>(a, c, grid, st);
                 break;
+            case LCA_MXFP4:
+                if (bf) launch_store_rows<uint16_t, LCA_MXFP4>(a, c, grid, st);
+                else launch_store_rows<float, LCA_MXFP4>(a, c, grid, st);
+                break;
             default:
                 if (bf) launch_store_rows<uint16_t, LCA_FP8>(a, c, grid, st);
                 else launch_store_rows<float, LCA_FP8>(a, c, grid, st);
@@ -305,6 +321,10 @@ hipError_t launch_kv_compress(const CompressArgs& a, hipStream_t st) {
         case LCA_BF16:
             if (bf) hipLaunchKernelGGL((kv_compress_kernel<uint16_t, LCA_BF16>), grid, block, 0, st, a);
             else hipLaunchKernelGGL((kv_compress_kernel<float, LCA_BF16>), grid, block, 0, st, a);
+            break;
+        case LCA_MXFP4:
+            if (bf) hipLaunchKernelGGL((kv_compress_kernel<uint16_t, LCA_MXFP4>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((kv_compress_kernel<float, LCA_MXFP4>), grid, block, 0, st, a);
             break;
         default:
             if (bf) hipLaunchKernelGGL((kv_compress_kernel<uint16_t, LCA_FP8>), grid, block, 0, st, a);

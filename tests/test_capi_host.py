@@ -181,3 +181,29 @@ def test_attn_workspace_covers_smaller_launches(L, no_gpu, B, T, H):
         assert rc != 5, (k, L.lca_last_error())
     assert max(sizes) <= need
     assert sizes == sorted(sizes)
+
+
+def test_indexer_mxfp4_validation(L):
+    """Every rejection happens on the host, before anything is launched (no GPU needed)."""
+    V = FAKE
+    good = lca._KV(FAKE, 0, FAKE2, lca.MXFP4, 128, 0, 1024)
+    q_pos = pos(100)
+
+    def call(k=good, H=16, d=128, m=4, sdt=lca.BF16, stride=1024, q=V, s=V):
+        return L.lca_indexer_score_mxfp4(q, None, k, H, d, 1, 1, q_pos, m, s, sdt, stride, None)
+    assert call(q=None) == 1 and call(m=0) == 1
+    assert call(k=lca._KV(FAKE, 0, FAKE2, lca.BF16, 128, 0, 1024)) == 3
+    assert call(sdt=lca.FP8) == 3
+    assert call(H=8) == 2 and call(d=64) == 2
+    assert call(k=lca._KV(FAKE, 0, FAKE2, lca.MXFP4, 128, 64, 1024)) == 2     # MXFP4 has no rope dims
+    assert call(k=lca._KV(FAKE, 0, FAKE2, lca.MXFP4, 128, 0, 10)) == 2        # vis(100) = 25 > cap
+    assert call(stride=10) == 2
+    assert call(k=lca._KV(FAKE, 0, 0, lca.MXFP4, 128, 0, 1024)) == 1       # scales missing
+    assert call(s=FAKE + 2) == 4
+    # MXFP4 storage is for indexer keys: the attention calls reject it
+    comp = lca._KV(FAKE, 0, FAKE2, lca.MXFP4, 512, 0, 64)
+    assert attn(L, comp=comp) == 3
+    assert b"MXFP4" in L.lca_last_error()
+    # the compressor writes it only without rope dims and with d_nope % 32 == 0
+    assert compress(L, out=lca._KV(FAKE, FAKE2, FAKE2, lca.MXFP4, 512, 64, 64), in_dtype=lca.BF16) == 2
+    assert compress(L, out=lca._KV(FAKE, 0, FAKE2, lca.MXFP4, 80, 0, 64), in_dtype=lca.BF16) == 2

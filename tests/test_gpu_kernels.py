@@ -288,3 +288,111 @@ def test_attention_nan_poison_and_empty():
     lca.hca_attn(dev(q[:, :1]), out1, q_pos=[2], comp=gc, m=m, win=None, n_win=0, sm_scale=0.05, lse=lse1)
     assert not host(out1).any()
     assert np.all(np.isneginf(host(lse1)))
+
+
+# --------------------------------------------------------------------------
+# MXFP4 QK path of the indexer ("DeepSeek-V4 中文翻译" section 5.2.1)
+# --------------------------------------------------------------------------
+
+_E2M1_MIDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+
+
+def _nibbles(b: np.ndarray) -> np.ndarray:
+    """[..., d/2] bytes -> [..., d] E2M1 codes (element 2i in the low nibble of byte i)."""
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), np.uint8)
+    out[..., 0::2] = b & 15
+    out[..., 1::2] = b >> 4
+    return out
+
+
+@pytest.mark.parametrize("m,overlap,dn", [(4, 1, 128), (1, 0, 128), (1, 0, 64), (1, 0, 576), (128, 0, 128)])
+def test_kv_compress_mxfp4(m, overlap, dn):
+    """MXFP4 rows against the oracle: identical scale bytes and codes, except where the fp32 value the
+    library rounds sits within 1e-5 (relative) of a decision boundary of the oracle's fp64 value: a block
+    maximum at a power of two (scale one step apart), or an element at a midpoint between two codes."""
+    B, n = 2, 203 if m < 128 else 3 * m + 5
+    first = [0, 2 * m + 1]
+    ca, za, cb, zb = _raw(31 + m, B, n, dn)
+    ba = S.normal(4, "bias_a", (m, dn))
+    bb = S.normal(4, "bias_b", (m, dn))
+    cap = (first[1] + n) // m + 2
+    kw = dict(m=m, overlap=overlap, first_pos=first, bias_a=ba, bias_b=bb if overlap else None)
+    o4 = orc.KV.empty(orc.MXFP4, B, cap, dn, 0)
+    orc.kv_compress(ca, za, cb if overlap else None, zb if overlap else None, o4, **kw)
+    o32 = orc.KV.empty(orc.F32, B, cap, dn, 0)
+    orc.kv_compress(ca, za, cb if overlap else None, zb if overlap else None, o32, **kw)
+    g = lca.KV.empty(orc.MXFP4, B, cap, dn, 0)
+    lca.kv_compress(dev(ca), dev(za), dev(cb) if overlap else None, dev(zb) if overlap else None, g, m=m,
+                    overlap=overlap, first_pos=first, bias_a=dev(ba), bias_b=dev(bb) if overlap else None)
+    torch.cuda.synchronize()
+    gh = kv_host(g)
+    y = o32.nope.astype(np.float64).reshape(B, cap, dn // 32, 32)
+    amax = np.abs(y).max(-1)
+    at_pow2 = np.abs(np.log2(np.where(amax > 0, amax, 1.0)) - np.round(np.log2(np.where(amax > 0, amax, 1.0)))) < 2e-5
+    same_sc = gh.scale == o4.scale
+    assert np.all(same_sc | at_pow2)
+    assert (~same_sc).mean() < 1e-3
+    cg = _nibbles(gh.nope).reshape(B, cap, dn // 32, 32)
+    co = _nibbles(o4.nope).reshape(B, cap, dn // 32, 32)
+    X = np.exp2(o4.scale.astype(np.float64) - 127)[..., None]
+    a = np.abs(y) / X
+    near_mid = (np.abs(a[..., None] - _E2M1_MIDS) <= 1e-5 * np.maximum(a[..., None], 1e-30)).any(-1)
+    diff = (cg != co) & same_sc[..., None]
+    assert np.all(~diff | near_mid)
+    assert diff.mean() < 1e-3
+
+
+def _mxfp4_keys(seed, B, N):
+    """Seeded MXFP4 key rows: random code bytes and E8M0 scale bytes in [118, 128) (scales 2^-9 .. 1)."""
+    g = S.stream(seed, "kI/mxfp4")
+    k = orc.KV.empty(orc.MXFP4, B, N, 128, 0)
+    k.nope[:] = g.integers(0, 256, k.nope.shape, dtype=np.uint8)
+    k.scale[:] = g.integers(118, 128, k.scale.shape, dtype=np.uint8)
+    return k
+
+
+def _check_scores(g, o, sfmt, B, T, q_pos, m, stride):
+    for b in range(B):
+        for i in range(T):
+            vis = (q_pos[b] + i + 1) // m
+            if sfmt == orc.F32:
+                gv, ov = g[b, i, :vis].astype(np.float64), o[b, i, :vis].astype(np.float64)
+                tol = 1e-5 * np.abs(ov) + 1e-5 * np.abs(ov).max(initial=0)
+                assert np.all(np.abs(gv - ov) <= tol), (b, i)
+                assert np.all(g[b, i, vis:] == 7.0)                # columns past vis(t) untouched
+            else:
+                gv, ov = S.from_bf16(g[b, i, :vis]), S.from_bf16(o[b, i, :vis])
+                near = np.abs(gv - ov) <= 1e-5 * np.abs(ov).max(initial=0)
+                assert np.all((bf16_ulps(g[b, i, :vis], o[b, i, :vis]) <= 1) | near), (b, i)
+                assert np.all(g[b, i, vis:] == S.to_bf16(np.float32(7.0)))
+
+
+@pytest.mark.parametrize("T,q_pos", [(1, [4000, 9001]), (77, [0, 3000]), (8, [11, 12]), (1, [3, 1])])
+@pytest.mark.parametrize("sfmt", [orc.F32, orc.BF16])
+def test_indexer_mxfp4(T, q_pos, sfmt):
+    m, B = 4, 2
+    N = (max(q_pos) + T) // m + 3
+    q = S.to_bf16(S.activations(17, "qI", (B, T, 16, 128)))
+    w = S.normal(17, "w", (B, T, 16), 0.25)
+    k = _mxfp4_keys(18, B, N)
+    stride = N + 5
+    o = orc.indexer_score_mxfp4(q, w, k, q_pos=q_pos, m=m, score_fmt=sfmt, s_stride=stride)
+    sg = torch.full((B, T, stride), 7.0, dtype=torch.float32 if sfmt == orc.F32 else torch.bfloat16, device="cuda")
+    lca.indexer_score_mxfp4(dev(q), dev(w), kv_dev(k), sg, q_pos=q_pos, m=m)
+    _check_scores(host(sg), o, sfmt, B, T, q_pos, m, stride)
+
+
+def test_indexer_mxfp4_no_weights_and_extreme_blocks():
+    """w = NULL (all ones); q blocks that are all zero, hold one huge value, or bf16 subnormals."""
+    m, B, T = 1, 1, 20
+    q = S.activations(19, "qI", (B, T, 16, 128)).astype(np.float32)
+    q[0, 0, :, :32] = 0.0                                   # all-zero blocks: scale byte 127, zero codes
+    q[0, 1, :, 5] = 3e4                                      # one large value flattens its block
+    q[0, 2, :, 32:64] *= 1e-39                               # subnormal block: exponent clamped at -127
+    q[0, 3] = -q[0, 3]
+    q = S.to_bf16(q)
+    k = _mxfp4_keys(20, B, 64)
+    o = orc.indexer_score_mxfp4(q, None, k, q_pos=[0], m=m, score_fmt=orc.F32, s_stride=64)
+    sg = torch.full((B, T, 64), 7.0, dtype=torch.float32, device="cuda")
+    lca.indexer_score_mxfp4(dev(q), None, kv_dev(k), sg, q_pos=[0], m=m)
+    _check_scores(host(sg), o, orc.F32, B, T, [0], m, 64)
