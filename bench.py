@@ -12,8 +12,11 @@ the per-step working set (about 85 MB) out of the 256 MB Infinity Cache, the
 stack state is replicated R times and consecutive steps rotate through the
 replicas (as a deeper model would), so every step reads its caches from HBM.
 
-Also reported (key "extra"): the same stack's 4096-token chunked prefill at
-1M context, and CSA decode for 32 sequences at 131,072 tokens.  "roofline"
+Also reported (key "extra"): the same 1M decode with the CSA indexer's QK
+path in MXFP4 and the top-2048 recall of bf16 and MXFP4-QK scores against
+f32 scores; the same stack's 4096-token chunked prefill at 1M context (with
+the chunk's MXFP4 indexer call timed beside the bf16 one); and CSA decode for
+32 sequences at 131,072 tokens.  "roofline"
 covers the dominant decode kernel (indexer_score, HBM-bound), timed with HIP
 events on its stream inside the timed graph.  "cpu_baseline" is the fp64
 oracle timed on host cores on a bounded sample (four decode steps of the
@@ -24,6 +27,7 @@ stack).
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -49,6 +53,7 @@ INDEXER_SOURCES = ["long_context_attention_22_amd/csrc/indexer.hip", "long_conte
                    "long_context_attention_22_amd/csrc/kernels.h"]
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP4_PEAK_TFLOPS = 10100.0   # dense MXFP4 MFMA
 T0_1M = 1 << 20
 C = 576
 
@@ -312,6 +317,71 @@ def bench_decode_1m(W: int, K: int, R: int, seed: int = 1005):
                               bytes_per_launch=nbytes, launch_ms=ind_ms, timing=timing)), stacks
 
 
+def mxfp4_copy(src: lca.KV) -> lca.KV:
+    """bf16 indexer keys re-stored as MXFP4 through the library's compressor (m = 1, no norm, no RoPE:
+    each row is quantised as it is)."""
+    k4 = lca.KV.empty(lca.MXFP4, src.nope.shape[0], src.cap, src.d_nope, 0)
+    for b in range(src.nope.shape[0]):
+        x = src.nope[b:b + 1]
+        lca.kv_compress(x, torch.zeros_like(x), None, None, _seq_view(k4, b), m=1, overlap=0, first_pos=0)
+    return k4
+
+
+def keys_to_mxfp4(layer: Layer):
+    """Switch a CSA layer to the MXFP4 indexer, its keys re-stored as MXFP4."""
+    layer.keys = mxfp4_copy(layer.keys)
+    layer.spec = dataclasses.replace(layer.spec, key_fmt=lca.MXFP4)
+
+
+def score_recall(stack: Stack, keys_bf16: lca.KV, keys_fp4: lca.KV, rows: int, k: int = 2048):
+    """Top-k recall of bf16 scores and of MXFP4-QK scores against f32 scores of the same bf16 inputs,
+    over `rows` decode rows of the CSA layer (the selections from the library's top-k)."""
+    li = [i for i, s in enumerate(stack.specs) if s.kind == "csa"][0]
+    layer = stack.layers[li]
+    cap = keys_bf16.cap
+    s32 = torch.empty(1, 1, cap, dtype=torch.float32, device="cuda")
+    s16 = torch.empty(1, 1, cap, dtype=torch.bfloat16, device="cuda")
+    s4 = torch.empty(1, 1, cap, dtype=torch.bfloat16, device="cuda")
+    ix = [torch.empty(1, 1, k, dtype=torch.int32, device="cuda") for _ in range(3)]
+    r16, r4 = [], []
+    for j in range(rows):
+        t = stack.t0 + j
+        qi, w = stack.qi[li][j], stack.w[li][j]
+        lca.indexer_score(qi, w, keys_bf16.nope, s32, q_pos=t, m=4)
+        lca.indexer_score(qi, w, keys_bf16.nope, s16, q_pos=t, m=4)
+        lca.indexer_score_mxfp4(qi, w, keys_fp4, s4, q_pos=t, m=4)
+        for sc, o in zip((s32, s16, s4), ix):
+            lca.topk_select(sc, o, q_pos=t, m=4, ws=layer.topk_ws)
+        ref = set(ix[0].flatten().tolist())
+        r16.append(len(ref & set(ix[1].flatten().tolist())) / k)
+        r4.append(len(ref & set(ix[2].flatten().tolist())) / k)
+    return float(np.mean(r16)), float(np.mean(r4))
+
+
+def bench_decode_1m_mxfp4(stacks, W: int, K: int):
+    """The same 1M decode with the CSA layer's indexer QK path in MXFP4 (keys stored MXFP4, each query
+    head quantised in the indexer call); top-k recall against f32 scores on the benchmark's inputs."""
+    li = [i for i, s in enumerate(stacks[0].specs) if s.kind == "csa"][0]
+    saved = [(st.layers[li].keys, st.layers[li].spec) for st in stacks]
+    for st in stacks:
+        keys_to_mxfp4(st.layers[li])
+    torch.cuda.synchronize()
+    ms, g = timed_graph_decode(stacks, W, K, None)
+    del g
+    ind_ms = graph_kernel_ms(stacks, W, K, "indexer_score")
+    vis = (T0_1M + 1) // 4
+    nbytes = vis * (64 + 4 + 2) + 16 * 128 * 2 + 16 * 4
+    rows = min(16, len(stacks[0].qi[li]))
+    r16, r4 = score_recall(stacks[0], saved[0][0], stacks[0].layers[li].keys, rows)
+    for st, (keys, spec) in zip(stacks, saved):
+        st.layers[li].keys, st.layers[li].spec = keys, spec
+    gbs = nbytes / (ind_ms * 1e-3) / 1e9
+    return dict(ms_per_step=ms / K, tokens_per_s=K / (ms * 1e-3),
+                indexer=dict(launch_ms=ind_ms, bytes=nbytes, gbs=gbs, frac=gbs / HBM_PEAK_GBS),
+                recall_top2048=dict(bf16_scores_vs_f32=r16, mxfp4_qk_vs_f32=r4, rows=rows,
+                                    inputs="N(0,1) bf16 queries and keys, N(0,0.25) head weights"))
+
+
 def attn_flops(T: int, t0: int, m: int, H: int, n_win: int, k: int | None) -> float:
     """Multiply-add flops (2 per MAC) of Q K^T and P V over the attended rows of T queries."""
     tot = 0
@@ -367,6 +437,17 @@ def bench_prefill_1m(stack: Stack, reps: int = 3, T: int = 4096, seed: int = 100
     chunk(record=rec)
     torch.cuda.synchronize()
     kt = {n: t.mean_ms() for n, t in timers.items() if t.pairs}
+    # the chunk's indexer call with the QK path in MXFP4 (same queries, keys re-stored as MXFP4)
+    li = [i for i, sp in enumerate(stack.specs) if sp.kind == "csa"][0]
+    layer = stack.layers[li]
+    k4 = mxfp4_copy(layer.keys)
+    f4 = KernelTimer("indexer_mxfp4")
+    for _ in range(reps):
+        f4("indexer_mxfp4", lambda: lca.indexer_score_mxfp4(qis[li], ws[li], k4, layer.scores[:, :T],
+                                                            q_pos=stack.t0, m=layer.spec.m))
+    torch.cuda.synchronize()
+    kt["indexer_mxfp4"] = f4.mean_ms()
+    del k4
     hca_fl = attn_flops(T, stack.t0, 128, 64, 128, None)
     csa_fl = attn_flops(T, stack.t0, 4, 64, 128, 2048)
     idx_fl = 2.0 * 16 * 128 * sum((stack.t0 + i + 1) // 4 for i in range(T))
@@ -375,7 +456,10 @@ def bench_prefill_1m(stack: Stack, reps: int = 3, T: int = 4096, seed: int = 100
     return dict(tokens=T, ms=ms, tokens_per_s=T / (ms * 1e-3), tflops=tot_fl / (ms * 1e-3) / 1e12,
                 mfma_frac=tot_fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, kernel_ms=kt,
                 hca_attn=dict(flops=hca_fl, tflops=hca_tf, frac=hca_tf / BF16_PEAK_TFLOPS),
-                indexer=dict(flops=idx_fl, tflops=idx_fl / (kt["indexer_score"] * 1e-3) / 1e12),
+                indexer=dict(flops=idx_fl, tflops=idx_fl / (kt["indexer_score"] * 1e-3) / 1e12,
+                             frac=idx_fl / (kt["indexer_score"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS),
+                indexer_mxfp4=dict(ms=kt["indexer_mxfp4"], tflops=idx_fl / (kt["indexer_mxfp4"] * 1e-3) / 1e12,
+                                   frac=idx_fl / (kt["indexer_mxfp4"] * 1e-3) / 1e12 / FP4_PEAK_TFLOPS),
                 csa_attn=dict(flops=csa_fl, tflops=csa_fl / (kt["csa_attn"] * 1e-3) / 1e12))
 
 
@@ -492,6 +576,12 @@ def main():
         f"{res['indexer_ms'] * 1e3:.1f} us = {res['roofline']['achieved']:.0f} GB/s")
     extra = {}
     if not args.no_extra:
+        f4 = bench_decode_1m_mxfp4(stacks, W, K)
+        log(f"1M decode, MXFP4 indexer: {f4['ms_per_step'] * 1e3:.1f} us/step, {f4['tokens_per_s']:.0f} tok/s; "
+            f"indexer {f4['indexer']['launch_ms'] * 1e3:.1f} us = {f4['indexer']['gbs']:.0f} GB/s; top-2048 "
+            f"recall vs f32 scores: bf16 {f4['recall_top2048']['bf16_scores_vs_f32']:.4f}, MXFP4 QK "
+            f"{f4['recall_top2048']['mxfp4_qk_vs_f32']:.4f}")
+        extra["decode_1m_mxfp4_indexer"] = f4
         pf = bench_prefill_1m(stacks[0])
         log(f"1M prefill chunk: {pf['ms']:.2f} ms, {pf['tokens_per_s']:.0f} tok/s, {pf['tflops']:.0f} TFLOP/s")
         extra["prefill_1m_chunk4096"] = pf

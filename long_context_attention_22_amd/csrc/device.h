@@ -149,6 +149,17 @@ __device__ __forceinline__ float xlane16(float v, bool mx) {  // combine with la
     const float a = __uint_as_float(p[0]), b = __uint_as_float(p[1]);
     return mx ? fmaxf(a, b) : a + b;
 }
+// Reduce-scatter over the four 16-lane rows: lane l ends with the sum over the rows of v[l >> 4]
+// at its column l & 15 (each v[b] holds one partial per lane).  Two permlane16 swaps pair rows
+// (0, 1) and (2, 3) of two values at a time, one permlane32 swap pairs the halves.
+__device__ __forceinline__ float sum4g_scatter(float v0, float v1, float v2, float v3) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v0), __float_as_uint(v1), false, false);
+    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v2), __float_as_uint(v3), false, false);
+    const float s01 = __uint_as_float(p[0]) + __uint_as_float(p[1]);  // rows: v0 (0+1), v1 (0+1), v0 (2+3), v1 (2+3)
+    const float s23 = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(s01), __float_as_uint(s23), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 // over the four 16-lane groups: every lane gets the same value, summed in the same order
 __device__ __forceinline__ float max4g(float v) { return xlane32(xlane16(v, true), true); }
 __device__ __forceinline__ float sum4g(float v) { return xlane32(xlane16(v, false), false); }

@@ -9,7 +9,8 @@
 // cache straight from HBM into B fragments (each lane loads 16 contiguous
 // bytes of one key row, so a chunk is one contiguous 16 KB read).  The
 // epilogue applies ReLU and the head weights in the accumulator layout, sums
-// the 16 heads with two lane swaps (v_permlane16/32_swap) and writes 64 consecutive scores
+// the 16 heads of four 16-key blocks at once with a reduce-scatter over the
+// lane rows (two v_permlane16_swap, one v_permlane32_swap) and writes 64 consecutive scores
 // per token with one coalesced store.  Key chunks beyond the last token's
 // visible count are skipped (causal tile skip).
 //
@@ -43,6 +44,19 @@ __device__ __forceinline__ void store_score<uint16_t>(uint16_t* p, float v) {
 // (visible count (t + 1) / m: a shift when m is a power of two)
 __device__ __forceinline__ int64_t vis_of(int64_t t1, int m) {
     return (m & (m - 1)) == 0 ? t1 >> __builtin_ctz((unsigned)m) : t1 / m;
+}
+
+// the visible counts of TOK consecutive tokens, min(vis, k_cap), 0 past the last token; uniform,
+// so kept in scalar registers for the key loop
+template <int TOK>
+__device__ __forceinline__ void token_vis(int64_t (&vis)[TOK], int64_t pos0, int ntok, int m, int64_t k_cap) {
+#pragma unroll
+    for (int tk = 0; tk < TOK; ++tk) {
+        const int64_t v = tk < ntok ? min(vis_of(pos0 + tk + 1, m), k_cap) : 0;
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+        vis[tk] = (int64_t)(((uint64_t)hi << 32) | lo);
+    }
 }
 
 template <int TOK, typename TS>
@@ -83,6 +97,9 @@ __global__ void __launch_bounds__(256) indexer_mfma(IndexerArgs a, int64_t keys_
     const uint16_t* kbase = (const uint16_t*)a.k + (int64_t)b * a.k_cap * kIdxD;
     TS* sbase = (TS*)a.scores + ((int64_t)b * a.T + i0) * a.s_stride;
 
+    int64_t vis_tk[TOK];  // visible keys of each token (loop invariant)
+    token_vis<TOK>(vis_tk, pos0, ntok, m, k_cap);
+
     for (int64_t c0 = key_lo + 64 * wv; c0 < key_hi; c0 += 256) {
         // B fragments of four 16-key blocks: block bl, lane -> key c0 + 16 bl + (lane & 15)
         bf16x8 kf[4][4];
@@ -99,7 +116,7 @@ __global__ void __launch_bounds__(256) indexer_mfma(IndexerArgs a, int64_t keys_
         const int64_t mykey = c0 + lane;  // the score this lane stores
 #pragma unroll
         for (int tk = 0; tk < TOK; ++tk) {
-            float mine = 0.0f;
+            float part[4];
 #pragma unroll
             for (int bl = 0; bl < 4; ++bl) {
                 f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -110,22 +127,24 @@ __global__ void __launch_bounds__(256) indexer_mfma(IndexerArgs a, int64_t keys_
                 float v = wt[tk][0] * fmaxf(acc[0], 0.0f);
                 v = fmaf(wt[tk][1], fmaxf(acc[1], 0.0f), v);
                 v = fmaf(wt[tk][2], fmaxf(acc[2], 0.0f), v);
-                v = fmaf(wt[tk][3], fmaxf(acc[3], 0.0f), v);
-                v = sum4g(v);  // the four head quartets of this key (lanes key + 16 kgrp)
-                if (kgrp == bl) mine = v;
+                part[bl] = fmaf(wt[tk][3], fmaxf(acc[3], 0.0f), v);
             }
-            if (tk < ntok) {
-                const int64_t vis_t = min(vis_of(pos0 + tk + 1, m), k_cap);
-                if (mykey < vis_t) store_score<TS>(sbase + (int64_t)tk * a.s_stride + mykey, mine);
-            }
+            // the four head quartets of each key: lane l gets key 16 (l >> 4) + (l & 15) = l
+            const float mine = sum4g_scatter(part[0], part[1], part[2], part[3]);
+            if (mykey < vis_tk[tk]) store_score<TS>(sbase + (int64_t)tk * a.s_stride + mykey, mine);
         }
     }
 }
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// (through a parameter: a bit cast applied directly to a vector element subscript was compiled as a
+// cast of element 0)
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t x) { return __builtin_bit_cast(bf16x2, x); }
 
+// (at most 128 VGPRs: four waves per SIMD hide the key loads better than wider token pipelining)
 template <int TOK, typename TS>
-__global__ void __launch_bounds__(256) indexer_fp4(IndexerArgs a, int64_t keys_per_wg) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) indexer_fp4(IndexerArgs a, int64_t keys_per_wg) {
     const int b = blockIdx.z;
     const int i0 = blockIdx.y * TOK;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -194,26 +213,31 @@ __global__ void __launch_bounds__(256) indexer_fp4(IndexerArgs a, int64_t keys_p
                 am = max(am, max(w & 0x7fffu, (w >> 16) & 0x7fffu));
             }
         const int ex = mx_block_exp(__uint_as_float(am << 16));
+        const float xs = ldexpf(1.0f, ex);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {  // word r: elements 8r .. 8r + 7, element 8r + n in bits 4n
-            uint32_t word = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t w = qraw[tk][r][i];
-                word |= e2m1_code(ldexpf(bf2f((uint16_t)(w & 0xffffu)), -ex)) << (8 * i);
-                word |= e2m1_code(ldexpf(bf2f((uint16_t)(w >> 16)), -ex)) << (8 * i + 4);
-            }
+            // v_cvt_scalef32_pk_fp4_bf16: two bf16 divided by 2^ex, rounded to the nearest E2M1 code
+            // (ties to even, saturating, sign kept) into byte i; checked equal to e2m1_code on every
+            // finite bf16 value for exponents -127 .. 127
+            const u32x4 v = qraw[tk][r];
+            uint32_t word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, as_bf16x2(v[0]), xs, 0);
+            word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(word, as_bf16x2(v[1]), xs, 1);
+            word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(word, as_bf16x2(v[2]), xs, 2);
+            word = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(word, as_bf16x2(v[3]), xs, 3);
             qa[tk][r] = (int)word;
             qa[tk][r + 4] = 0;
         }
         qsc[tk] = ex + 127;
     }
 
+    int64_t vis_tk[TOK];  // visible keys of each token (loop invariant)
+    token_vis<TOK>(vis_tk, pos0, ntok, m, k_cap);
+
     for (;;) {
         const int64_t mykey = c0 + lane;  // the score this lane stores
 #pragma unroll
         for (int tk = 0; tk < TOK; ++tk) {
-            float mine = 0.0f;
+            float part[4];
 #pragma unroll
             for (int bl = 0; bl < 4; ++bl) {
                 const i32x8 kb = {(int)kc[bl][0], (int)kc[bl][1], (int)kc[bl][2], (int)kc[bl][3], 0, 0, 0, 0};
@@ -224,14 +248,10 @@ __global__ void __launch_bounds__(256) indexer_fp4(IndexerArgs a, int64_t keys_p
                 float v = wt[tk][0] * fmaxf(acc[0], 0.0f);
                 v = fmaf(wt[tk][1], fmaxf(acc[1], 0.0f), v);
                 v = fmaf(wt[tk][2], fmaxf(acc[2], 0.0f), v);
-                v = fmaf(wt[tk][3], fmaxf(acc[3], 0.0f), v);
-                v = sum4g(v);
-                if (kgrp == bl) mine = v;
+                part[bl] = fmaf(wt[tk][3], fmaxf(acc[3], 0.0f), v);
             }
-            if (tk < ntok) {
-                const int64_t vis_t = min(vis_of(pos0 + tk + 1, m), k_cap);
-                if (mykey < vis_t) store_score<TS>(sbase + (int64_t)tk * s_stride + mykey, mine);
-            }
+            const float mine = sum4g_scatter(part[0], part[1], part[2], part[3]);  // key c0 + lane
+            if (mykey < vis_tk[tk]) store_score<TS>(sbase + (int64_t)tk * s_stride + mykey, mine);
         }
         c0 += 256;
         if (c0 >= key_hi) break;
@@ -279,6 +299,8 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t st) {
     int64_t want_split = (2048 + (int64_t)a.B * groups - 1) / ((int64_t)a.B * groups);
     int64_t kpw = (a.max_vis + want_split - 1) / want_split;
     kpw = ((kpw + 255) / 256) * 256;
+    // MXFP4 keys are 68 bytes: a single-token launch gives each workgroup twice the keys
+    if (fp4 && tok == 1) kpw *= 2;
     if (kpw < 256) kpw = 256;
     const int64_t nsplit = (a.max_vis + kpw - 1) / kpw;
     dim3 grid((unsigned)nsplit, (unsigned)groups, (unsigned)a.B);

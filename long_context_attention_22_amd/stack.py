@@ -9,8 +9,8 @@ at positions t0 .. t0+T-1 of every sequence, Layer.step() issues:
 
     window store      kv_compress(m = 1, ring)          raw rows t0 .. t0+T-1
     compress          kv_compress(m, overlap)           entries whose block ends in the chunk
-    indexer keys      kv_compress(m, overlap, d_I)      (CSA)
-    scores            indexer_score                     (CSA)
+    indexer keys      kv_compress(m, overlap, d_I)      (CSA; bf16 or MXFP4 keys)
+    scores            indexer_score / _mxfp4            (CSA)
     selection         topk_select                       (CSA)
     attention         csa_attn / hca_attn
 
@@ -24,8 +24,8 @@ from dataclasses import dataclass
 
 import torch
 
-from . import (BF16, FP8, KV, attn_workspace_size, csa_attn, hca_attn, indexer_score,
-               kv_compress, topk_select, topk_workspace_size)
+from . import (BF16, FP8, MXFP4, KV, attn_workspace_size, csa_attn, hca_attn, indexer_score,
+               indexer_score_mxfp4, kv_compress, topk_select, topk_workspace_size)
 
 
 @dataclass
@@ -41,6 +41,7 @@ class LayerSpec:
     H_I: int = 16
     d_I: int = 128
     score_fmt: int = BF16
+    key_fmt: int = BF16        # indexer keys: BF16, or MXFP4 (the QK path in FP4)
     rope_theta: float = 10000.0
     eps: float = 1e-6
 
@@ -96,7 +97,7 @@ class Layer:
         self.spec, self.B, self.params = spec, B, params
         self.comp = KV.empty(spec.fmt, B, comp_cap, spec.d_nope, spec.d_rope, device)
         self.win = KV.empty(spec.fmt, B, win_cap, spec.d_nope, spec.d_rope, device)
-        self.keys = KV.empty(BF16, B, comp_cap, spec.d_I, 0, device) if spec.kind == "csa" else None
+        self.keys = KV.empty(spec.key_fmt, B, comp_cap, spec.d_I, 0, device) if spec.kind == "csa" else None
         self.t_max = t_max
         if spec.kind == "csa":
             sdt = torch.bfloat16 if spec.score_fmt == BF16 else torch.float32
@@ -145,7 +146,10 @@ class Layer:
         if s.kind == "csa":
             sc = self.scores[:, :T]
             ix = self.idx[:, :T]
-            run("indexer_score", lambda: indexer_score(q_idx, w, self.keys.nope, sc, q_pos=t0, m=s.m))
+            if self.keys.fmt == MXFP4:
+                run("indexer_score", lambda: indexer_score_mxfp4(q_idx, w, self.keys, sc, q_pos=t0, m=s.m))
+            else:
+                run("indexer_score", lambda: indexer_score(q_idx, w, self.keys.nope, sc, q_pos=t0, m=s.m))
             run("topk_select", lambda: topk_select(sc, ix, q_pos=t0, m=s.m, ws=self.topk_ws))
             run("csa_attn", lambda: csa_attn(q, out, q_pos=t0, comp=self.comp, m=s.m, idx=ix, win=self.win,
                                              n_win=s.n_win, sink=p.sink, sm_scale=s.sm_scale,
