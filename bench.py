@@ -49,6 +49,7 @@ METRIC = "CSA/HCA decode tokens/s at 128K–1M ctx (HBM GB/s %) + prefill tokens
 # HBM traffic of the decode indexer launch from rocprofv3 FETCH_SIZE / WRITE_SIZE passes, scaled by
 # the same counters on a plain copy; used only while the indexer source is unchanged since then.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_decode_1m_traffic.json")
+MXFP4_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_mxfp4_decode_1m_traffic.json")
 INDEXER_SOURCES = ["long_context_attention_22_amd/csrc/indexer.hip", "long_context_attention_22_amd/csrc/device.h",
                    "long_context_attention_22_amd/csrc/kernels.h"]
 HBM_PEAK_GBS = 8000.0
@@ -268,10 +269,10 @@ def indexer_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic():
+def measured_traffic(path: str = TRAFFIC_FILE):
     """Counter-derived HBM bytes per decode indexer launch, or None when absent or stale."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(path) as fh:
             d = json.load(fh)
     except (OSError, ValueError):
         return None
@@ -358,7 +359,7 @@ def score_recall(stack: Stack, keys_bf16: lca.KV, keys_fp4: lca.KV, rows: int, k
     return float(np.mean(r16)), float(np.mean(r4))
 
 
-def bench_decode_1m_mxfp4(stacks, W: int, K: int):
+def bench_decode_1m_mxfp4(stacks, W: int, K: int, recall: bool = True):
     """The same 1M decode with the CSA layer's indexer QK path in MXFP4 (keys stored MXFP4, each query
     head quantised in the indexer call); top-k recall against f32 scores on the benchmark's inputs."""
     li = [i for i, s in enumerate(stacks[0].specs) if s.kind == "csa"][0]
@@ -372,14 +373,18 @@ def bench_decode_1m_mxfp4(stacks, W: int, K: int):
     vis = (T0_1M + 1) // 4
     nbytes = vis * (64 + 4 + 2) + 16 * 128 * 2 + 16 * 4
     rows = min(16, len(stacks[0].qi[li]))
-    r16, r4 = score_recall(stacks[0], saved[0][0], stacks[0].layers[li].keys, rows)
+    rec = None
+    if recall:
+        r16, r4 = score_recall(stacks[0], saved[0][0], stacks[0].layers[li].keys, rows)
+        rec = dict(bf16_scores_vs_f32=r16, mxfp4_qk_vs_f32=r4, rows=rows,
+                   inputs="N(0,1) bf16 queries and keys, N(0,0.25) head weights")
     for st, (keys, spec) in zip(stacks, saved):
         st.layers[li].keys, st.layers[li].spec = keys, spec
     gbs = nbytes / (ind_ms * 1e-3) / 1e9
     return dict(ms_per_step=ms / K, tokens_per_s=K / (ms * 1e-3),
-                indexer=dict(launch_ms=ind_ms, bytes=nbytes, gbs=gbs, frac=gbs / HBM_PEAK_GBS),
-                recall_top2048=dict(bf16_scores_vs_f32=r16, mxfp4_qk_vs_f32=r4, rows=rows,
-                                    inputs="N(0,1) bf16 queries and keys, N(0,0.25) head weights"))
+                indexer=dict(launch_ms=ind_ms, bytes=nbytes, gbs=gbs, frac=gbs / HBM_PEAK_GBS,
+                             traffic=measured_traffic(MXFP4_TRAFFIC_FILE)),
+                recall_top2048=rec)
 
 
 def attn_flops(T: int, t0: int, m: int, H: int, n_win: int, k: int | None) -> float:
@@ -557,6 +562,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=6)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the prefill and the 32 x 128K decode")
+    ap.add_argument("--mxfp4", action="store_true",
+                    help="with --no-extra: still time the 1M decode with the MXFP4 indexer (no recall)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB device copy (reference for rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -575,13 +582,15 @@ def main():
     log(f"1M decode: {res['ms_per_step'] * 1e3:.1f} us/step, {res['tokens_per_s']:.0f} tok/s; indexer "
         f"{res['indexer_ms'] * 1e3:.1f} us = {res['roofline']['achieved']:.0f} GB/s")
     extra = {}
-    if not args.no_extra:
-        f4 = bench_decode_1m_mxfp4(stacks, W, K)
+    if not args.no_extra or args.mxfp4:
+        f4 = bench_decode_1m_mxfp4(stacks, W, K, recall=not args.no_extra)
         log(f"1M decode, MXFP4 indexer: {f4['ms_per_step'] * 1e3:.1f} us/step, {f4['tokens_per_s']:.0f} tok/s; "
-            f"indexer {f4['indexer']['launch_ms'] * 1e3:.1f} us = {f4['indexer']['gbs']:.0f} GB/s; top-2048 "
-            f"recall vs f32 scores: bf16 {f4['recall_top2048']['bf16_scores_vs_f32']:.4f}, MXFP4 QK "
-            f"{f4['recall_top2048']['mxfp4_qk_vs_f32']:.4f}")
+            f"indexer {f4['indexer']['launch_ms'] * 1e3:.1f} us = {f4['indexer']['gbs']:.0f} GB/s")
+        if f4["recall_top2048"]:
+            log(f"top-2048 recall vs f32 scores: bf16 {f4['recall_top2048']['bf16_scores_vs_f32']:.4f}, MXFP4 QK "
+                f"{f4['recall_top2048']['mxfp4_qk_vs_f32']:.4f}")
         extra["decode_1m_mxfp4_indexer"] = f4
+    if not args.no_extra:
         pf = bench_prefill_1m(stacks[0])
         log(f"1M prefill chunk: {pf['ms']:.2f} ms, {pf['tokens_per_s']:.0f} tok/s, {pf['tflops']:.0f} TFLOP/s")
         extra["prefill_1m_chunk4096"] = pf
