@@ -128,7 +128,9 @@ int lca_kv_compress(const void* c_a, const void* z_a, const void* c_b, const voi
  * multi-head dot product scored by ReLU between each query and every
  * compressed indexer key, with BF16 scores as in [R] 5.2.1.
  *   S[b][i][s] = sum_h w[b][i][h] * max(0, q[b][i][h] . k[b][s])   for s < vis(t)
- * with t = q_pos[b] + i; columns s >= vis(t) are left unspecified.
+ * with t = q_pos[b] + i; columns s >= vis(t) are left unspecified (a call
+ * with several rows per sequence may write scores there, for columns below
+ * the visible count of the call's last row of that sequence).
  * q: [B][T][H_I][d_I], k: [B][k_cap][d_I] (one key per compressed entry,
  * shared by all indexer heads), both in_dtype (LCA_BF16, or LCA_F32);
  * w: f32 [B][T][H_I] (NULL = all ones).  scores: [B][T][s_stride] of

@@ -28,7 +28,9 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-I", os.path.join(ROOT, "include")]
 # Per-source additions.  attn.hip: its softmax never sees a NaN, and without the NaN guarantee
 # every fmaxf of a value moved across lanes gets an extra canonicalising max.
-EXTRA = {"attn.hip": ["-fno-honor-nans"]}
+# indexer.hip: its scores are finite, and without the guarantee every ReLU of an MFMA result costs
+# a canonicalising max besides the max with zero.
+EXTRA = {"attn.hip": ["-fno-honor-nans"], "indexer.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -101,19 +101,21 @@ __global__ void __launch_bounds__(256) indexer_mfma(IndexerArgs a, int64_t keys_
     token_vis<TOK>(vis_tk, pos0, ntok, m, k_cap);
 
     for (int64_t c0 = key_lo + 64 * wv; c0 < key_hi; c0 += 256) {
-        // B fragments of four 16-key blocks: block bl, lane -> key c0 + 16 bl + (lane & 15)
+        // B fragments of four 16-key blocks: block bl, lane -> key c0 + 16 bl + (lane & 15).  With
+        // several tokens the loads are branch-free: keys past the range re-read its last key.
         bf16x8 kf[4][4];
 #pragma unroll
         for (int bl = 0; bl < 4; ++bl) {
-            const int64_t key = c0 + 16 * bl + hrow;
+            const int64_t key = TOK > 1 ? min(c0 + 16 * bl + hrow, key_hi - 1) : c0 + 16 * bl + hrow;
             const u32x4* kp = (const u32x4*)(kbase + key * kIdxD);
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                u32x4 v = key < key_hi ? kp[4 * ks + kgrp] : u32x4{0u, 0u, 0u, 0u};
+                u32x4 v = (TOK > 1 || key < key_hi) ? kp[4 * ks + kgrp] : u32x4{0u, 0u, 0u, 0u};
                 kf[bl][ks] = __builtin_bit_cast(bf16x8, v);
             }
         }
         const int64_t mykey = c0 + lane;  // the score this lane stores
+        float mine_all[TOK];
 #pragma unroll
         for (int tk = 0; tk < TOK; ++tk) {
             float part[4];
@@ -131,7 +133,18 @@ __global__ void __launch_bounds__(256) indexer_mfma(IndexerArgs a, int64_t keys_
             }
             // the four head quartets of each key: lane l gets key 16 (l >> 4) + (l & 15) = l
             const float mine = sum4g_scatter(part[0], part[1], part[2], part[3]);
-            if (mykey < vis_tk[tk]) store_score<TS>(sbase + (int64_t)tk * a.s_stride + mykey, mine);
+            if (TOK == 1) {
+                if (mykey < vis_tk[tk]) store_score<TS>(sbase + (int64_t)tk * a.s_stride + mykey, mine);
+            }
+            mine_all[tk] = mine;
+        }
+        // Several tokens: every key of the workgroup's range is stored for every token, after the
+        // whole chunk (one masked region instead of one per token); a token's columns in
+        // [vis(t), key_hi) hold scores of keys it cannot see, which the contract leaves unspecified.
+        if (TOK > 1 && mykey < key_hi) {
+#pragma unroll
+            for (int tk = 0; tk < TOK; ++tk)
+                if (tk < ntok) store_score<TS>(sbase + (int64_t)tk * a.s_stride + mykey, mine_all[tk]);
         }
     }
 }
@@ -235,6 +248,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
 
     for (;;) {
         const int64_t mykey = c0 + lane;  // the score this lane stores
+        float mine_all[TOK];
 #pragma unroll
         for (int tk = 0; tk < TOK; ++tk) {
             float part[4];
@@ -251,7 +265,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
                 part[bl] = fmaf(wt[tk][3], fmaxf(acc[3], 0.0f), v);
             }
             const float mine = sum4g_scatter(part[0], part[1], part[2], part[3]);  // key c0 + lane
-            if (mykey < vis_tk[tk]) store_score<TS>(sbase + (int64_t)tk * s_stride + mykey, mine);
+            if (TOK == 1) {
+                if (mykey < vis_tk[tk]) store_score<TS>(sbase + (int64_t)tk * s_stride + mykey, mine);
+            }
+            mine_all[tk] = mine;
+        }
+        // several tokens: stored after the chunk, every key of the range (as the bf16 kernel)
+        if (TOK > 1 && mykey < key_hi) {
+#pragma unroll
+            for (int tk = 0; tk < TOK; ++tk)
+                if (tk < ntok) store_score<TS>(sbase + (int64_t)tk * s_stride + mykey, mine_all[tk]);
         }
         c0 += 256;
         if (c0 >= key_hi) break;
