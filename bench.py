@@ -291,6 +291,37 @@ def calibrate_copy(nbytes: int = 256 << 20, reps: int = 3):
     log(f"calibration copy: {reps} x {nbytes} bytes read and written")
 
 
+def copy_ceiling_gbs(nbytes: int = 1 << 30, reps: int = 5) -> float:
+    """Measured device-copy rate (bytes read + written per second, best of reps), the practical HBM
+    ceiling beside the 8 TB/s nominal peak."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(reps):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        dst.copy_(src)
+        e.record()
+        torch.cuda.synchronize()
+        best = min(best, s.elapsed_time(e))
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (best * 1e-3) / 1e9
+
+
+def host_cpu() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def indexer_bytes(vis: int, B: int, d_I: int = 128, H_I: int = 16) -> int:
     """Algorithmic bytes of one decode indexer launch: keys read once, scores written, q and w read."""
     return B * (vis * d_I * 2 + vis * 2 + H_I * d_I * 2 + H_I * 4)
@@ -547,6 +578,7 @@ def cpu_baseline(n_steps: int = 4, seed: int = 1005):
                               sm_scale=C ** -0.5, rope_theta=1e4, out_fmt=orc.BF16)
     el = time.perf_counter() - start
     return dict(value=n_steps / el, unit="tokens/s", cores=1, kind="oracle",
+                host=dict(cpu=host_cpu(), nproc=os.cpu_count()),
                 sample=f"{n_steps} decode steps of the 1M-context 4-layer stack (fp64 oracle; one query row "
                        f"per call, so one host thread does the work); {el:.1f} s; random stored cache bytes of "
                        f"the benchmark's shapes")
@@ -579,6 +611,7 @@ def main():
 
     d = bench_decode_1m(W, K, R)
     res, stacks = d
+    res["roofline"]["copy_ceiling_gbs"] = copy_ceiling_gbs()
     log(f"1M decode: {res['ms_per_step'] * 1e3:.1f} us/step, {res['tokens_per_s']:.0f} tok/s; indexer "
         f"{res['indexer_ms'] * 1e3:.1f} us = {res['roofline']['achieved']:.0f} GB/s")
     extra = {}

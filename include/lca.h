@@ -216,6 +216,37 @@ int lca_hca_attn(const void* q, int32_t q_dtype, int32_t H, int32_t B, int32_t T
                  const float* sink, float sm_scale, double rope_theta, void* out,
                  int32_t out_dtype, float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * lca_csa_attn_append / lca_hca_attn_append -- the window store of the call's
+ * own rows, then the attention: first rows q_pos[b] .. q_pos[b] + T - 1 of
+ * x_win (x_dtype LCA_F32 or LCA_BF16; the raw rows of those positions: T
+ * rows of c values per sequence, sequence b starting x_stride rows after
+ * sequence b - 1, x_stride = 0 meaning T) are stored into the window ring win
+ * exactly as
+ * lca_kv_compress(x_win, ..., m = 1, overlap = 0, gamma, eps, rope_theta,
+ * ring = 1, first_pos = q_pos) stores them ([R] 2.3.3 and 3.5.1: the
+ * sliding-window rows live in the state cache), then the call is
+ * lca_csa_attn / lca_hca_attn with the same arguments, so each query row
+ * attends to its own freshly stored row.  Decode launches (T = 1, bf16
+ * x_win, bf16 / fp8 caches of 512 + 64 dims, at most 64 rows x 16-head
+ * groups) do the store inside the attention launch: one launch fewer per
+ * layer and token.  Requires n_win >= 1; gamma: f32 [c] or NULL; x_win and
+ * gamma 16-byte aligned.  Errors as lca_csa_attn / lca_hca_attn, plus
+ * LCA_EINVAL (NULL x_win, n_win < 1, eps < 0), LCA_EDTYPE (x_dtype) and
+ * LCA_ESHAPE (0 < x_stride < T).
+ */
+int lca_csa_attn_append(const void* q, int32_t q_dtype, int32_t H, int32_t B, int32_t T,
+                        const int64_t* q_pos, lca_kv comp, int32_t m, const int32_t* idx, int32_t k,
+                        lca_kv win, int32_t n_win, const void* x_win, int32_t x_dtype,
+                        int64_t x_stride, const float* gamma, float eps, const float* sink,
+                        float sm_scale, double rope_theta, void* out, int32_t out_dtype, float* lse,
+                        void* ws, size_t ws_bytes, void* stream);
+int lca_hca_attn_append(const void* q, int32_t q_dtype, int32_t H, int32_t B, int32_t T,
+                        const int64_t* q_pos, lca_kv comp, int32_t m, lca_kv win, int32_t n_win,
+                        const void* x_win, int32_t x_dtype, int64_t x_stride, const float* gamma,
+                        float eps, const float* sink, float sm_scale, double rope_theta, void* out,
+                        int32_t out_dtype, float* lse, void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes for lca_csa_attn / lca_hca_attn with at most max_keys
  * attended rows per query (selected or visible entries + window).  Covers the
  * split partials of short (decode-sized) launches and, from 128 query rows on,

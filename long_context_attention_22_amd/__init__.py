@@ -5,7 +5,8 @@ kernels.  torch supplies device memory and the current stream.  There is no
 fallback: when the built library is missing every call raises.
 
 Calls (same names as the C ABI):
-    kv_compress, indexer_score, indexer_score_mxfp4, topk_select, csa_attn, hca_attn
+    kv_compress, indexer_score, indexer_score_mxfp4, topk_select, csa_attn, hca_attn,
+    csa_attn_append, hca_attn_append
 and helpers KV (the lca_kv storage planes), attn_workspace_size.
 """
 from __future__ import annotations
@@ -58,10 +59,14 @@ def lib():
                                    vp, i32, vp, vp, sz, vp]
         L.lca_hca_attn.argtypes = [vp, i32, i32, i32, i32, vp, _KV, i32, _KV, i32, vp, f32, f64, vp, i32,
                                    vp, vp, sz, vp]
+        L.lca_csa_attn_append.argtypes = [vp, i32, i32, i32, i32, vp, _KV, i32, vp, i32, _KV, i32, vp, i32, i64,
+                                          vp, f32, vp, f32, f64, vp, i32, vp, vp, sz, vp]
+        L.lca_hca_attn_append.argtypes = [vp, i32, i32, i32, i32, vp, _KV, i32, _KV, i32, vp, i32, i64, vp, f32,
+                                          vp, f32, f64, vp, i32, vp, vp, sz, vp]
         L.lca_attn_workspace_size.argtypes = [i32, i32, i32, i32, i64]
         L.lca_attn_workspace_size.restype = sz
         for name in ("lca_kv_compress", "lca_indexer_score", "lca_indexer_score_mxfp4", "lca_topk_select",
-                     "lca_csa_attn", "lca_hca_attn"):
+                     "lca_csa_attn", "lca_hca_attn", "lca_csa_attn_append", "lca_hca_attn_append"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -214,3 +219,39 @@ def hca_attn(q, out, *, q_pos, comp: KV, m: int, win: KV | None, n_win: int, sin
                               int(m), win.c() if win is not None else _empty_kv(), int(n_win),
                               _ptr(sink), float(sm_scale), float(rope_theta), _ptr(out), _dtype(out),
                               _ptr(lse), _ptr(ws), nbytes, _stream(stream)))
+
+
+def _rows_stride(x, T: int) -> int:
+    """Rows between sequences of a [B][T][c] row window (rows contiguous)."""
+    B, _, c = x.shape
+    if x.stride(2) != 1 or x.stride(1) != c:
+        raise ValueError("x_win rows must be contiguous")
+    return x.stride(0) // c if B > 1 else T
+
+
+def csa_attn_append(q, out, x_win, *, q_pos, comp: KV, m: int, idx, win: KV, n_win: int, gamma=None,
+                    eps: float = 1e-6, sink=None, sm_scale: float, rope_theta: float = 0.0, lse=None, ws=None,
+                    stream=None):
+    """Window store of rows q_pos .. q_pos+T-1 from x_win [B][T][c] (may be a row window of a longer
+    per-sequence stream), then csa_attn."""
+    B, T, H, _ = q.shape
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().lca_csa_attn_append(_ptr(q), _dtype(q), int(H), int(B), int(T), _pos(q_pos, B), comp.c(),
+                                     int(m), _ptr(idx), int(idx.shape[2]), win.c(), int(n_win), _ptr(x_win),
+                                     _dtype(x_win), _rows_stride(x_win, T), _ptr(gamma), float(eps), _ptr(sink),
+                                     float(sm_scale), float(rope_theta), _ptr(out), _dtype(out), _ptr(lse),
+                                     _ptr(ws), nbytes, _stream(stream)))
+
+
+def hca_attn_append(q, out, x_win, *, q_pos, comp: KV, m: int, win: KV, n_win: int, gamma=None,
+                    eps: float = 1e-6, sink=None, sm_scale: float, rope_theta: float = 0.0, lse=None, ws=None,
+                    stream=None):
+    """Window store of rows q_pos .. q_pos+T-1 from x_win [B][T][c] (may be a row window of a longer
+    per-sequence stream), then hca_attn."""
+    B, T, H, _ = q.shape
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().lca_hca_attn_append(_ptr(q), _dtype(q), int(H), int(B), int(T), _pos(q_pos, B), comp.c(),
+                                     int(m), win.c(), int(n_win), _ptr(x_win), _dtype(x_win),
+                                     _rows_stride(x_win, T), _ptr(gamma), float(eps), _ptr(sink),
+                                     float(sm_scale), float(rope_theta), _ptr(out), _dtype(out), _ptr(lse),
+                                     _ptr(ws), nbytes, _stream(stream)))

@@ -33,6 +33,7 @@
 
 #include "device.h"
 #include "kernels.h"
+#include "rowstore.h"
 
 namespace lca {
 
@@ -750,7 +751,6 @@ template <int FMT, bool DENSE>
 __device__ __forceinline__ void dec_load(DecRegs<FMT>& R, int ncs, int w_row, int s_end, int comp_cap, int win_cap,
                                          const KvPtrs& P, const int32_t* ent, int s_begin, int s0, int hw,
                                          int c) {
-    constexpr int kN = DecRegs<FMT>::kN;
     constexpr uint32_t kRow = FMT == LCA_FP8 ? kDN : 2 * kDN;
     R.ok = 0;
     uint32_t rrow = 0;
@@ -827,6 +827,23 @@ __device__ __forceinline__ void dec_store(DecRegs<FMT>& R, uint16_t* Kt, uint8_t
     put8(Kt, hw + 8 * (c >> 3), kDN / 8 + (c & 7), R.rp);
 }
 
+// Tile row trow (if in [0, 32)) is the query row's own window row: after dec_store, the threads that
+// wrote it (half-wave hw = trow mod 8) overwrite it with rowt (bf16, decoded), the row the launch
+// computes and stores itself (the ring does not hold it yet when the tile's loads are issued).
+template <int FMT>
+__device__ __forceinline__ void dec_fix_row(uint16_t* Kt, int hw, int c, const uint16_t* rowt, int trow) {
+    if ((unsigned)trow >= (unsigned)kKT || hw != (trow & 7)) return;
+    const u32x4* src = (const u32x4*)rowt;  // 8 bf16 per chunk
+    if constexpr (FMT == LCA_FP8) {
+        put8(Kt, trow, 2 * c, src[2 * c]);
+        put8(Kt, trow, 2 * c + 1, src[2 * c + 1]);
+    } else {
+        put8(Kt, trow, c, src[c]);
+        put8(Kt, trow, c + 32, src[c + 32]);
+    }
+    if ((c >> 3) == (trow >> 3)) put8(Kt, trow, kDN / 8 + (c & 7), src[kDN / 8 + (c & 7)]);
+}
+
 // Grid (x, T, B): query row i = blockIdx.y of sequence b = blockIdx.z, so the row's position
 // comes from the first batch of argument loads.  Along x (a multiple of 8 workgroups, so x mod 8
 // is the XCD): x = 8 j + xcd, head group j mod ng, split (j / ng) * 8 + xcd.
@@ -846,9 +863,12 @@ __global__ void __launch_bounds__(256) attn_dec(AttnArgs a, int64_t split_len, i
         const int64_t qp = a.q_pos.v[b], wb = a.w_base.v[b], cc = a.comp.cap, wc = a.win.cap;
         const int msh = a.m_shift, mm = a.m, kk = a.k, nw = a.n_win;
         const void *pq = a.q, *pi = a.idx, *pn0 = a.comp.nope, *pn1 = a.win.nope, *pr0 = a.comp.rope,
-                   *pr1 = a.win.rope, *ps0 = a.comp.scale, *ps1 = a.win.scale;
+                   *pr1 = a.win.rope, *ps0 = a.comp.scale, *ps1 = a.win.scale, *pax = a.app_x, *pag = a.app_gamma;
+        const float aeps = a.app_eps;
+        const int64_t ast = a.app_stride;
         asm volatile("" ::"s"(qp), "s"(wb), "s"(cc), "s"(wc), "s"(msh), "s"(mm), "s"(kk), "s"(nw), "s"(H), "s"(pq),
-                     "s"(pi), "s"(pn0), "s"(pn1), "s"(pr0), "s"(pr1), "s"(ps0), "s"(ps1));
+                     "s"(pi), "s"(pn0), "s"(pn1), "s"(pr0), "s"(pr1), "s"(ps0), "s"(ps1), "s"(pax), "s"(pag),
+                     "s"(aeps), "s"(ast));
     }
     const uint32_t ng = (uint32_t)H >> 4;
     const uint32_t L = blockIdx.x, jj = L >> 3;
@@ -895,6 +915,20 @@ __global__ void __launch_bounds__(256) attn_dec(AttnArgs a, int64_t split_len, i
     P.scale[0] = FMT == LCA_FP8 ? sptr<float>(a.comp.scale) + (int64_t)b * a.comp.cap * 4 : nullptr;
     P.scale[1] = FMT == LCA_FP8 ? sptr<float>(a.win.scale) + (int64_t)b * a.win.cap * 4 : nullptr;
 
+    // Fused window store (T = 1): the split holding the last slot -- the query row's own window
+    // slot -- computes that row from the raw row (the compressor's m = 1 store) into rowt, and head
+    // group 0 also writes it to the ring.  Its loads go out first, with the tiles'.
+    __shared__ __attribute__((aligned(16))) uint16_t rowt[kC];
+    __shared__ float rys[64 * 9];
+    const bool app = a.app_x != nullptr && s_begin < s_end && s_end == (int)sm.nslots && sm.nslots > sm.ncs;
+    float ay[9], ag[9];
+    double ainv = 0.0;  // RoPE frequency of this lane's pair (channel 512 + lane, d_rope = 64)
+    if (app && wv == 0) {
+        row_load<uint16_t, 9>((const uint16_t*)a.app_x + (int64_t)b * a.app_stride * kC, a.app_gamma, kC, ay, ag);
+        ainv = a.rope.inv[lane & 31];
+    }
+    const int tl = app ? (int)sm.nslots - 1 - s_begin : -(1 << 30);  // tile row of slot t in tile 0
+
     // (loads of tiles past the end read row 0 and are dropped: the same loads on every path)
     DecRegs<FMT> R[NP];
 #pragma unroll
@@ -906,7 +940,17 @@ __global__ void __launch_bounds__(256) attn_dec(AttnArgs a, int64_t split_len, i
     constexpr uint32_t kTileBytes = 2 * kTileElems;
     uint32_t bq = 0, bn = kTileBytes, bo = 2 * kTileBytes;  // byte offsets: tiles t, t + 1, t - 1
     int fq = 0, fn = 1;
+    if (app) {
+        if (wv == 0) {
+            int trw = w_row + ((int)sm.nslots - 1 - ncs);  // ring row of position t
+            if (trw >= win_cap) trw -= win_cap;
+            row_store<FMT, 9>(ay, ag, a.app_gamma, a.app_eps, kC, kDN, kDR, a.rope_theta != 0.0, ainv, (double)t,
+                              a.win.nope, a.win.rope, a.win.scale, (int64_t)b * win_cap + trw, rys, rowt, hg == 0);
+        }
+        __syncthreads();
+    }
     dec_store<FMT>(R[0], &Kt[0][0], (uint8_t*)vflag[0], hw, c);
+    if (app) dec_fix_row<FMT>(&Kt[0][0], hw, c, rowt, tl);
     if (NP < kDecMaxTiles)
         dec_load<FMT, DENSE>(R[0], ncs, w_row, s_end, comp_cap, win_cap, P, ent, s_begin, s_begin + NP * kKT, hw, c);
 #pragma unroll
@@ -949,6 +993,7 @@ __global__ void __launch_bounds__(256) attn_dec(AttnArgs a, int64_t split_len, i
             if (t + 1 < kDecMaxTiles) {
                 DecRegs<FMT>& Rn = R[(t + 1) % NP];
                 dec_store<FMT>(Rn, (uint16_t*)((char*)&Kt[0][0] + bn), (uint8_t*)vflag[fn], hw, c);
+                if (app) dec_fix_row<FMT>((uint16_t*)((char*)&Kt[0][0] + bn), hw, c, rowt, tl - (t + 1) * kKT);
                 if (t + 1 + NP < kDecMaxTiles)
                     dec_load<FMT, DENSE>(Rn, ncs, w_row, s_end, comp_cap, win_cap, P, ent, s_begin,
                                          s_begin + (t + 1 + NP) * kKT, hw, c);
@@ -1265,6 +1310,19 @@ hipError_t launch_kv_expand(const ExpandArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// (the decode kernel is taken and its row offsets fit 32 bits)
+static bool dec_launch(const AttnArgs& a, const AttnPlan& p) {
+    const int64_t rb = a.comp.fmt == LCA_FP8 ? kDN : 2 * kDN;
+    const bool off32 = a.comp.cap * rb < ((int64_t)1 << 32) && a.win.cap * rb < ((int64_t)1 << 32);
+    return p.dec && off32;
+}
+
+bool attn_fuses_store(const AttnArgs& a) {
+    if (a.comp.fmt == LCA_F32 || a.T != 1 || a.n_win < 1) return false;
+    const int c = a.comp.d_nope + a.comp.d_rope;
+    return dec_launch(a, attn_plan((int64_t)a.B * a.T, a.H, c, a.max_keys));
+}
+
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     const int64_t rows = (int64_t)a.B * a.T;
     if (rows <= 0) return hipSuccess;
@@ -1278,9 +1336,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     const bool dense = a.idx == nullptr;
     // attn_dec addresses one sequence's rows with 32-bit offsets; larger planes take attn_mfma
     // (same splits, same workspace layout)
-    const int64_t rb = a.comp.fmt == LCA_FP8 ? kDN : 2 * kDN;
-    const bool off32 = a.comp.cap * rb < ((int64_t)1 << 32) && a.win.cap * rb < ((int64_t)1 << 32);
-    if (p.dec && off32) {
+    if (dec_launch(a, p)) {
         dim3 grid((unsigned)((ns + 7) / 8 * 8 * (a.H / 16)), (unsigned)a.T, (unsigned)a.B);
         if (a.comp.fmt == LCA_FP8) {
             if (dense) hipLaunchKernelGGL((attn_dec<LCA_FP8, true, 4>), grid, dim3(256), 0, st, a, p.len, ns);

@@ -250,10 +250,35 @@ size_t lca_attn_workspace_size(int32_t B, int32_t T, int32_t H, int32_t c, int64
     return split > expand ? split : expand;
 }
 
+// The m = 1 ring store of rows q_pos[b] .. q_pos[b] + T - 1 of x (x_stride rows per sequence) into win (what
+// lca_kv_compress does with m = 1, overlap = 0, ring = 1 and first_pos = q_pos).
+static hipError_t store_window_rows(const void* x, int32_t x_dtype, int64_t x_stride, const float* gamma, float eps,
+                                    double rope_theta, int32_t B, int32_t T, const int64_t* q_pos, const lca_kv& win,
+                                    hipStream_t st) {
+    lca::CompressArgs c;
+    memset(&c, 0, sizeof c);
+    c.c_a = x; c.z_a = x; c.gamma = gamma; c.eps = eps; c.rope_theta = rope_theta; c.in_dtype = x_dtype;
+    c.rope = rope_tab(rope_theta, win.d_rope);
+    c.m = 1; c.overlap = 0; c.B = B; c.n_rows = T; c.in_stride = x_stride; c.out = win; c.ring = 1;
+    c.first_pos = to_pos(q_pos, B);
+    int64_t most = 0;
+    for (int b = 0; b < B; ++b) {
+        int64_t s_lo = q_pos[b];
+        if (T > win.cap) s_lo = q_pos[b] + T - win.cap;
+        c.s_lo.v[b] = s_lo;
+        const int64_t n = q_pos[b] + T - s_lo;
+        if (n > most) most = n;
+    }
+    c.max_entries = most;
+    return lca::launch_kv_compress(c, st);
+}
+
 static int attn_common(const void* q, int32_t q_dtype, int32_t H, int32_t B, int32_t T,
                        const int64_t* q_pos, lca_kv comp, int32_t m, const int32_t* idx, int32_t k,
                        lca_kv win, int32_t n_win, const float* sink, float sm_scale, double rope_theta,
-                       void* out, int32_t out_dtype, float* lse, void* ws, size_t ws_bytes, void* stream) {
+                       void* out, int32_t out_dtype, float* lse, void* ws, size_t ws_bytes, void* stream,
+                       const void* x_win = nullptr, int32_t x_dtype = 0, int64_t x_stride = 0,
+                       const float* x_gamma = nullptr, float x_eps = 0.0f) {
     if (!q || !out) return fail(LCA_EINVAL, "q and out must be non-NULL");
     if (m < 1) return fail(LCA_EINVAL, "m must be >= 1");
     if (H < 1 || T < 0) return fail(LCA_ESHAPE, "bad H / T");
@@ -287,8 +312,17 @@ static int attn_common(const void* q, int32_t q_dtype, int32_t H, int32_t B, int
         if (H % 16 != 0 || H > 64) return fail(LCA_ESHAPE, "H must be a multiple of 16, at most 64");
     }
     if (!aligned16(q) || !aligned16(out) || !aligned16(lse) || !aligned16(idx) || !aligned16(sink) ||
-        !aligned16(ws))
+        !aligned16(ws) || !aligned16(x_win) || !aligned16(x_gamma))
         return fail(LCA_EALIGN, "pointers must be 16-byte aligned");
+    if (x_win) {
+        if (n_win < 1) return fail(LCA_EINVAL, "the window store needs n_win >= 1");
+        if (x_dtype != LCA_F32 && x_dtype != LCA_BF16) return fail(LCA_EDTYPE, "x_dtype must be f32 or bf16");
+        if (!(x_eps >= 0.0f)) return fail(LCA_EINVAL, "eps must be >= 0");
+        if (x_stride < 0 || (x_stride > 0 && x_stride < T))
+            return fail(LCA_ESHAPE, "x_stride %lld is smaller than T %d", (long long)x_stride, T);
+        if (rope_theta > 0.0 && win.d_rope > 2 * lca::kMaxRopeHalf)
+            return fail(LCA_ESHAPE, "RoPE supports d_rope <= %d", 2 * lca::kMaxRopeHalf);
+    }
     if (T == 0) return LCA_OK;
     int64_t max_keys = 1;
     for (int b = 0; b < B; ++b) {
@@ -323,6 +357,20 @@ static int attn_common(const void* q, int32_t q_dtype, int32_t H, int32_t B, int
         a.w_base.v[b] = d >= 0 && win.cap > 0 ? d % win.cap : 0;
     }
     if (n_win == 0) a.win = comp;  // never read
+    if (x_win) {
+        // the window store of the call's own rows: inside a decode launch when it can take it, else
+        // as its own launch before anything reads the window
+        a.app_x = x_win;
+        a.app_gamma = x_gamma;
+        a.app_eps = x_eps;
+        a.app_stride = x_stride > 0 ? x_stride : T;
+        if (x_dtype != LCA_BF16 || !lca::attn_fuses_store(a)) {
+            a.app_x = nullptr;
+            hipError_t e = store_window_rows(x_win, x_dtype, a.app_stride, x_gamma, x_eps, rope_theta, B, T, q_pos,
+                                             win, (hipStream_t)stream);
+            if (e != hipSuccess) return hip_status(e);
+        }
+    }
 
     // Dense fp8 launches with many query rows share every row: expand the rows they read to bf16
     // once (compressed rows [0, vis) and the window positions the rows need, into a ring of
@@ -394,6 +442,30 @@ int lca_csa_attn(const void* q, int32_t q_dtype, int32_t H, int32_t B, int32_t T
     if (k < 1) return fail(LCA_EINVAL, "k must be >= 1");
     return attn_common(q, q_dtype, H, B, T, q_pos, comp, m, idx, k, win, n_win, sink, sm_scale, rope_theta,
                        out, out_dtype, lse, ws, ws_bytes, stream);
+}
+
+int lca_csa_attn_append(const void* q, int32_t q_dtype, int32_t H, int32_t B, int32_t T, const int64_t* q_pos,
+                        lca_kv comp, int32_t m, const int32_t* idx, int32_t k, lca_kv win, int32_t n_win,
+                        const void* x_win, int32_t x_dtype, int64_t x_stride, const float* gamma, float eps,
+                        const float* sink, float sm_scale, double rope_theta, void* out, int32_t out_dtype,
+                        float* lse, void* ws, size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    if (!idx) return fail(LCA_EINVAL, "idx is NULL");
+    if (k < 1) return fail(LCA_EINVAL, "k must be >= 1");
+    if (!x_win) return fail(LCA_EINVAL, "x_win is NULL");
+    return attn_common(q, q_dtype, H, B, T, q_pos, comp, m, idx, k, win, n_win, sink, sm_scale, rope_theta, out,
+                       out_dtype, lse, ws, ws_bytes, stream, x_win, x_dtype, x_stride, gamma, eps);
+}
+
+int lca_hca_attn_append(const void* q, int32_t q_dtype, int32_t H, int32_t B, int32_t T, const int64_t* q_pos,
+                        lca_kv comp, int32_t m, lca_kv win, int32_t n_win, const void* x_win, int32_t x_dtype,
+                        int64_t x_stride, const float* gamma, float eps, const float* sink, float sm_scale,
+                        double rope_theta, void* out, int32_t out_dtype, float* lse, void* ws, size_t ws_bytes,
+                        void* stream) {
+    g_err[0] = 0;
+    if (!x_win) return fail(LCA_EINVAL, "x_win is NULL");
+    return attn_common(q, q_dtype, H, B, T, q_pos, comp, m, nullptr, 0, win, n_win, sink, sm_scale, rope_theta,
+                       out, out_dtype, lse, ws, ws_bytes, stream, x_win, x_dtype, x_stride, gamma, eps);
 }
 
 int lca_hca_attn(const void* q, int32_t q_dtype, int32_t H, int32_t B, int32_t T, const int64_t* q_pos,

@@ -141,10 +141,12 @@ __global__ void __launch_bounds__(256) indexer_mfma(IndexerArgs a, int64_t keys_
         // Several tokens: every key of the workgroup's range is stored for every token, after the
         // whole chunk (one masked region instead of one per token); a token's columns in
         // [vis(t), key_hi) hold scores of keys it cannot see, which the contract leaves unspecified.
-        if (TOK > 1 && mykey < key_hi) {
+        if constexpr (TOK > 1) {
+            if (mykey < key_hi) {
 #pragma unroll
-            for (int tk = 0; tk < TOK; ++tk)
-                if (tk < ntok) store_score<TS>(sbase + (int64_t)tk * a.s_stride + mykey, mine_all[tk]);
+                for (int tk = 0; tk < TOK; ++tk)
+                    if (tk < ntok) store_score<TS>(sbase + (int64_t)tk * a.s_stride + mykey, mine_all[tk]);
+            }
         }
     }
 }
@@ -271,15 +273,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
             mine_all[tk] = mine;
         }
         // several tokens: stored after the chunk, every key of the range (as the bf16 kernel)
-        if (TOK > 1 && mykey < key_hi) {
+        if constexpr (TOK > 1) {
+            if (mykey < key_hi) {
 #pragma unroll
-            for (int tk = 0; tk < TOK; ++tk)
-                if (tk < ntok) store_score<TS>(sbase + (int64_t)tk * s_stride + mykey, mine_all[tk]);
+                for (int tk = 0; tk < TOK; ++tk)
+                    if (tk < ntok) store_score<TS>(sbase + (int64_t)tk * s_stride + mykey, mine_all[tk]);
+            }
         }
         c0 += 256;
         if (c0 >= key_hi) break;
-#pragma unroll
-        for (int bl = 0; bl < 4; ++bl) {
+        for (int bl = 0; bl < 4; ++bl) {  // (unrolled by the compiler)
             const int64_t key = min(c0 + 16 * bl + hrow, key_hi - 1);
             kc[bl] = *(const u32x4*)(kbase + key * (kIdxD / 2) + 16 * kgrp);
             ks[bl] = ksbase[key];

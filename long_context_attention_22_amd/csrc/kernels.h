@@ -92,6 +92,13 @@ struct AttnArgs {
     Pos w_base;         // (q_pos[b] - n_win + 1) mod win.cap, where that position is >= 0
     int32_t m_shift;    // log2(m) when m is a power of two, else -1
     int64_t max_keys;   // attended rows per query, upper bound
+    // Window store fused into a decode launch (T = 1, bf16 raw rows): app_x holds the raw row
+    // of each query position, stored into the window ring (RMSNorm with app_gamma / app_eps, RoPE
+    // with rope_theta) by the launch itself; NULL = the window already holds it.
+    const void* app_x;
+    const float* app_gamma;
+    float app_eps;
+    int64_t app_stride;  // rows of app_x between sequences
 };
 // fp8 rows -> bf16 rows (nope codes times their scale, RoPE dims copied): for each sequence b,
 // positions p in [first[b], first[b] + count[b]) of src (row b * src.cap + (p mod src.cap)) go to
@@ -110,5 +117,8 @@ constexpr int64_t kExpandMinRows = 128;  // query rows from which a dense launch
 size_t attn_ws_need(int64_t rows, int32_t H, int32_t c, int64_t max_keys);
 size_t attn_ws_bytes(int64_t rows, int32_t H, int32_t c, int64_t max_keys);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
+// whether launch_attn runs a.app_x's window store inside the attention launch (else the caller
+// stores first)
+bool attn_fuses_store(const AttnArgs& a);
 
 }  // namespace lca

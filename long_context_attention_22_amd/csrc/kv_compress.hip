@@ -13,19 +13,9 @@
 // through LDS.
 #include "device.h"
 #include "kernels.h"
+#include "rowstore.h"
 
 namespace lca {
-
-template <typename T>
-__device__ __forceinline__ float ldin(const T* p, int64_t i);
-template <>
-__device__ __forceinline__ float ldin<float>(const float* p, int64_t i) {
-    return p[i];
-}
-template <>
-__device__ __forceinline__ float ldin<uint16_t>(const uint16_t* p, int64_t i) {
-    return bf2f(p[i]);
-}
 
 // online softmax over `cnt` rows (stride c) of one channel
 template <typename T>
@@ -179,103 +169,13 @@ __global__ void __launch_bounds__(64) kv_store_rows(CompressArgs a) {
     // (a workgroup past the last row reads row 0 of its sequence and stores nothing)
     const bool live = s < p0 + n_rows;
     const T* src = c_a + ((int64_t)b * in_stride + (live ? s - p0 : 0)) * c;
-    // (channels past c load channel c - 1 and are zeroed: no branch around the loads)
     float y[J], g[J];
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-        const int ch = lane + 64 * j;
-        const float v = ldin(src, ch < c ? ch : c - 1);
-        y[j] = ch < c ? v : 0.0f;
-    }
-    if (gamma) {
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-            const int ch = lane + 64 * j;
-            const float v = gamma[ch < c ? ch : c - 1];
-            g[j] = ch < c ? v : 0.0f;
-        }
-    }
+    row_load<T, J>(src, gamma, c, y, g);
     if (!live) return;
-    if (gamma) {
-        float ss = 0.0f;
-#pragma unroll
-        for (int j = 0; j < J; ++j) ss = fmaf(y[j], y[j], ss);
-        const float r = 1.0f / sqrtf(wave_sum_dpp(ss) / (float)c + eps);
-#pragma unroll
-        for (int j = 0; j < J; ++j) y[j] = g[j] * y[j] * r;
-    }
-    if (rope) {
-        // channels d_nope .. c - 1 through LDS: lane l < d_rope rotates channel d_nope + l with its
-        // partner d_nope + (l +- half) (d_rope <= 64 in this kernel's shapes)
-        __shared__ float ys[64 * J];
-#pragma unroll
-        for (int j = 0; j < J; ++j) ys[lane + 64 * j] = y[j];
-        __syncthreads();
-        float rot = 0.0f;
-        if (lane < d_rope) {
-            float sn, cs;
-            const double ang = (double)s;
-            rope_sincos(&inv, 0, ang, &sn, &cs);
-            const float x = ys[d_nope + lane];
-            rot = lane < half ? x * cs - ys[d_nope + lane + half] * sn : ys[d_nope + lane - half] * sn + x * cs;
-        }
-        __syncthreads();
-        if (lane < d_rope) ys[d_nope + lane] = rot;
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < J; ++j)
-            if (lane + 64 * j >= d_nope) y[j] = ys[lane + 64 * j];
-    }
+    __shared__ float ys[64 * J];
     const int64_t row = (int64_t)b * cap + (ring ? s % cap : s);
-    if (FMT == LCA_FP8) {
-        // power-of-two scale per 128 nope dims (d_nope % 128 == 0): channels 128 g .. are j = 2g, 2g+1
-        float isc[J / 2 + 1];  // 1 / scale, exact
-#pragma unroll
-        for (int g2 = 0; 2 * g2 < J; ++g2) {
-            float am = 0.0f;
-            if (128 * g2 < d_nope) {
-                am = fabsf(y[2 * g2]);
-                if (2 * g2 + 1 < J) am = fmaxf(am, fabsf(y[2 * g2 + 1]));
-            }
-            const float amax = wave_max_dpp(am);
-            int e8 = 0;  // scale = 2^e8
-            if (amax > 0.0f) {
-                int ex = 0;
-                frexpf(amax, &ex);  // amax in [2^(ex-1), 2^ex)
-                const int e = ex - 1;
-                e8 = (amax <= ldexpf(1.75f, e)) ? e - 8 : e - 7;
-            }
-            isc[g2] = ldexpf(1.0f, -e8);
-            if (lane == 0 && 128 * g2 < d_nope) ((float*)oscale)[row * (d_nope >> 7) + g2] = ldexpf(1.0f, e8);
-        }
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-            const int ch = lane + 64 * j;
-            if (ch < d_nope)
-                ((uint8_t*)onope)[row * d_nope + ch] = (uint8_t)f32_to_fp8(y[j] * isc[j >> 1]);
-            else if (ch < c)
-                ((uint16_t*)orope)[row * d_rope + (ch - d_nope)] = f2bf(y[j]);
-        }
-    } else if (FMT == LCA_MXFP4) {  // d_rope == 0, c % 32 == 0
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-            const int ch = lane + 64 * j;
-            mxfp4_store_lane(y[j], ch < c, (uint8_t*)oscale + row * (c >> 5), ch >> 5,
-                             (uint32_t*)onope + row * (c >> 3), ch >> 3);
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-            const int ch = lane + 64 * j;
-            if (FMT == LCA_BF16) {
-                if (ch < d_nope) ((uint16_t*)onope)[row * d_nope + ch] = f2bf(y[j]);
-                else if (ch < c) ((uint16_t*)orope)[row * d_rope + (ch - d_nope)] = f2bf(y[j]);
-            } else {
-                if (ch < d_nope) ((float*)onope)[row * d_nope + ch] = y[j];
-                else if (ch < c) ((float*)orope)[row * d_rope + (ch - d_nope)] = y[j];
-            }
-        }
-    }
+    row_store<FMT, J>(y, g, gamma, eps, c, d_nope, d_rope, rope, inv, (double)s, onope, orope, oscale, row, ys,
+                      nullptr, true);
 }
 
 template <typename T, int FMT>

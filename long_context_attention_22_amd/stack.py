@@ -16,7 +16,10 @@ at positions t0 .. t0+T-1 of every sequence, Layer.step() issues:
 
 Decode is T = 1; chunked prefill is T > 1.  Nothing here computes: every step
 is one library call on the current stream, so a sequence of steps can be
-captured in a HIP graph.
+captured in a HIP graph.  The window store rides on the attention call
+(csa_attn_append / hca_attn_append), which for decode-sized launches does it
+inside the attention launch; it only has to precede the attention, since
+compression reads the raw rows, not the window.
 """
 from __future__ import annotations
 
@@ -24,8 +27,8 @@ from dataclasses import dataclass
 
 import torch
 
-from . import (BF16, FP8, MXFP4, KV, attn_workspace_size, csa_attn, hca_attn, indexer_score,
-               indexer_score_mxfp4, kv_compress, topk_select, topk_workspace_size)
+from . import (BF16, FP8, MXFP4, KV, attn_workspace_size, csa_attn, csa_attn_append, hca_attn, hca_attn_append,
+               indexer_score, indexer_score_mxfp4, kv_compress, topk_select, topk_workspace_size)
 
 
 @dataclass
@@ -114,11 +117,6 @@ class Layer:
         self.ws = torch.zeros(max(16, ws), dtype=torch.uint8, device=device)
 
     # ------------------------------------------------------------------
-    def store_window(self, raw: RawStream, t0: int, T: int):
-        s, p = self.spec, self.params
-        kv_compress(raw.rows("c_a", t0, T), raw.rows("z_a", t0, T), None, None, self.win, m=1, overlap=0,
-                    first_pos=t0, gamma=p.gamma, eps=s.eps, rope_theta=s.rope_theta, ring=1)
-
     def compress(self, raw: RawStream, t0: int, T: int):
         """Entries whose block ends inside [t0, t0 + T)."""
         s, p = self.spec, self.params
@@ -138,11 +136,13 @@ class Layer:
             kv_compress(raw.rows("i_ca", lo, n), raw.rows("i_za", lo, n), b_rows("i_cb"), b_rows("i_zb"),
                         self.keys, bias_a=p.i_bias_a, bias_b=p.i_bias_b, **kw)
 
-    def attend(self, t0: int, q, out, q_idx=None, w=None, lse=None, record=None):
-        """q [B][T][H][c] bf16 -> out [B][T][H][c].  record(name, fn) wraps a launch (for timing)."""
+    def attend(self, t0: int, q, out, q_idx=None, w=None, lse=None, record=None, x_win=None):
+        """q [B][T][H][c] bf16 -> out [B][T][H][c].  record(name, fn) wraps a launch (for timing).
+        x_win: raw rows [B][T][c] of positions t0 .. t0+T-1, stored into the window by the call."""
         s, p = self.spec, self.params
         T = q.shape[1]
         run = record or (lambda name, fn: fn())
+        app = {} if x_win is None else dict(gamma=p.gamma, eps=s.eps)
         if s.kind == "csa":
             sc = self.scores[:, :T]
             ix = self.idx[:, :T]
@@ -151,18 +151,23 @@ class Layer:
             else:
                 run("indexer_score", lambda: indexer_score(q_idx, w, self.keys.nope, sc, q_pos=t0, m=s.m))
             run("topk_select", lambda: topk_select(sc, ix, q_pos=t0, m=s.m, ws=self.topk_ws))
-            run("csa_attn", lambda: csa_attn(q, out, q_pos=t0, comp=self.comp, m=s.m, idx=ix, win=self.win,
-                                             n_win=s.n_win, sink=p.sink, sm_scale=s.sm_scale,
-                                             rope_theta=s.rope_theta, lse=lse, ws=self.ws))
+            kw = dict(q_pos=t0, comp=self.comp, m=s.m, idx=ix, win=self.win, n_win=s.n_win, sink=p.sink,
+                      sm_scale=s.sm_scale, rope_theta=s.rope_theta, lse=lse, ws=self.ws, **app)
+            if x_win is None:
+                run("csa_attn", lambda: csa_attn(q, out, **kw))
+            else:
+                run("csa_attn", lambda: csa_attn_append(q, out, x_win, **kw))
         else:
-            run("hca_attn", lambda: hca_attn(q, out, q_pos=t0, comp=self.comp, m=s.m, win=self.win,
-                                             n_win=s.n_win, sink=p.sink, sm_scale=s.sm_scale,
-                                             rope_theta=s.rope_theta, lse=lse, ws=self.ws))
+            kw = dict(q_pos=t0, comp=self.comp, m=s.m, win=self.win, n_win=s.n_win, sink=p.sink,
+                      sm_scale=s.sm_scale, rope_theta=s.rope_theta, lse=lse, ws=self.ws, **app)
+            if x_win is None:
+                run("hca_attn", lambda: hca_attn(q, out, **kw))
+            else:
+                run("hca_attn", lambda: hca_attn_append(q, out, x_win, **kw))
 
     def step(self, raw: RawStream, t0: int, q, out, q_idx=None, w=None, lse=None, record=None):
         """T = q.shape[1] new rows at positions t0 .. t0+T-1 (the same for every sequence)."""
         T = q.shape[1]
         run = record or (lambda name, fn: fn())
-        run("kv_compress", lambda: self.store_window(raw, t0, T))
         run("kv_compress", lambda: self.compress(raw, t0, T))
-        self.attend(t0, q, out, q_idx, w, lse, record)
+        self.attend(t0, q, out, q_idx, w, lse, record, x_win=raw.rows("c_a", t0, T))

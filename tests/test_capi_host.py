@@ -207,3 +207,26 @@ def test_indexer_mxfp4_validation(L):
     # the compressor writes it only without rope dims and with d_nope % 32 == 0
     assert compress(L, out=lca._KV(FAKE, FAKE2, FAKE2, lca.MXFP4, 512, 64, 64), in_dtype=lca.BF16) == 2
     assert compress(L, out=lca._KV(FAKE, 0, FAKE2, lca.MXFP4, 80, 0, 64), in_dtype=lca.BF16) == 2
+
+
+def test_attn_append_validation(L):
+    """The appending calls reject a missing row source, an empty window and bad row dtypes on the host."""
+    def call(csa=True, x=FAKE, xdt=lca.BF16, n_win=128, eps=1e-6, xs=0):
+        a = dict(q=FAKE, qdt=lca.BF16, H=64, B=1, T=1, q_pos=pos(100), comp=kv(), m=4, idx=FAKE2, k=16,
+                 win=kv(cap=256), sink=None, scale=0.04, theta=0.0, out=FAKE2, odt=lca.F32, lse=None, ws=None,
+                 wsb=0)
+        if csa:
+            return L.lca_csa_attn_append(a["q"], a["qdt"], a["H"], a["B"], a["T"], a["q_pos"], a["comp"], a["m"],
+                                         a["idx"], a["k"], a["win"], n_win, x, xdt, xs, None, eps, a["sink"],
+                                         a["scale"], a["theta"], a["out"], a["odt"], a["lse"], a["ws"], a["wsb"],
+                                         None)
+        return L.lca_hca_attn_append(a["q"], a["qdt"], a["H"], a["B"], a["T"], a["q_pos"], a["comp"], a["m"],
+                                     a["win"], n_win, x, xdt, xs, None, eps, a["sink"], a["scale"], a["theta"],
+                                     a["out"], a["odt"], a["lse"], a["ws"], a["wsb"], None)
+    for csa in (True, False):
+        assert call(csa, x=None) == 1
+        assert call(csa, n_win=0) == 1
+        assert call(csa, xdt=lca.FP8) == 3
+        assert call(csa, eps=-1.0) == 1
+        assert call(csa, x=FAKE + 4) == 4
+        assert call(csa, xs=-1) == 2

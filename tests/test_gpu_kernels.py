@@ -398,3 +398,49 @@ def test_indexer_mxfp4_no_weights_and_extreme_blocks():
     sg = torch.full((B, T, 64), 7.0, dtype=torch.float32, device="cuda")
     lca.indexer_score_mxfp4(dev(q), None, kv_dev(k), sg, q_pos=[0], m=m)
     _check_scores(host(sg), o, orc.F32, B, T, [0], m, 64)
+
+
+@pytest.mark.parametrize("fmt", [orc.FP8, orc.BF16])
+@pytest.mark.parametrize("mode", ["csa", "hca"])
+@pytest.mark.parametrize("B,T,xdt", [(2, 1, "bf16"), (1, 1, "bf16"), (2, 1, "f32"), (1, 3, "bf16")])
+def test_attention_append(fmt, mode, B, T, xdt):
+    """Window store of the call's own rows, then attention (inside the decode launch for T = 1 with
+    bf16 rows, two launches otherwise), against the oracle's m = 1 ring store followed by its
+    attention: outputs and LSE to the attention bars, the ring to the storage bars."""
+    n_win, H = 128, 64
+    m = 4 if mode == "csa" else 16
+    q_pos = [3001, 5000][:B]
+    ncomp = (max(q_pos) + T) // m + 1
+    comp = _cache(61, B, ncomp, fmt, "comp")
+    win_cap = n_win + T + 3                       # rows p live at p mod cap: the window wraps
+    win_o = _cache(62, B, win_cap, fmt, "win")    # ring contents before the call
+    win_g = kv_dev(win_o)
+    x = S.activations(63, "xwin", (B, T, 576))
+    if xdt == "bf16":
+        x = S.to_bf16(x)
+    gamma = (1.0 + 0.1 * S.normal(64, "gamma", (576,))).astype(np.float32)
+    q = _q(65, B, T, H)
+    sink = S.normal(66, "sink", (H,))
+    idx, k = None, 300
+    if mode == "csa":
+        idx = orc.topk_select(S.normal(67, "sc", (B, T, ncomp)), q_pos=q_pos, m=m, k=k)
+    scale, theta = 1.0 / np.sqrt(576), 10000.0
+    orc.kv_compress(x, x, None, None, win_o, m=1, overlap=0, first_pos=q_pos, gamma=gamma, eps=1e-6,
+                    rope_theta=theta, ring=1)
+    o, lse = orc.attention(q, q_pos=q_pos, comp=comp, m=m, idx=idx, win=win_o, n_win=n_win, sink=sink,
+                           sm_scale=scale, rope_theta=theta)
+    maxk = (k if mode == "csa" else ncomp) + n_win
+    ws = torch.empty(max(16, lca.attn_workspace_size(B, T, H, 576, maxk)), dtype=torch.uint8, device="cuda")
+    out = torch.zeros(B, T, H, 576, dtype=torch.float32, device="cuda")
+    lg = torch.zeros(B, T, H, dtype=torch.float32, device="cuda")
+    kw = dict(q_pos=q_pos, comp=kv_dev(comp), m=m, win=win_g, n_win=n_win, gamma=dev(gamma), eps=1e-6,
+              sink=dev(sink), sm_scale=scale, rope_theta=theta, lse=lg, ws=ws)
+    if mode == "csa":
+        lca.csa_attn_append(dev(q), out, dev(x), idx=dev(idx), **kw)
+    else:
+        lca.hca_attn_append(dev(q), out, dev(x), **kw)
+    torch.cuda.synchronize()
+    assert_kv_close(kv_host(win_g), win_o)
+    err = np.abs(host(out) - o).max()
+    assert err <= 2e-2, err
+    np.testing.assert_allclose(host(lg), lse, atol=1e-3, rtol=1e-4)
