@@ -921,10 +921,20 @@ __global__ void __launch_bounds__(256) attn_dec(AttnArgs a, int64_t split_len, i
     __shared__ __attribute__((aligned(16))) uint16_t rowt[kC];
     __shared__ float rys[64 * 9];
     const bool app = a.app_x != nullptr && s_begin < s_end && s_end == (int)sm.nslots && sm.nslots > sm.ncs;
-    float ay[9], ag[9];
+    RowOut<9> arow;
+    // The 32-bit words holding this lane's channels lane + 64 j (the high half for odd lanes), taken
+    // apart only when the row is prepared, after the tile loads are issued: any use here would make
+    // the wave wait for these loads before the tiles' went out.
+    uint32_t xr[9];
+    float ag[9];
     double ainv = 0.0;  // RoPE frequency of this lane's pair (channel 512 + lane, d_rope = 64)
     if (app && wv == 0) {
-        row_load<uint16_t, 9>((const uint16_t*)a.app_x + (int64_t)b * a.app_stride * kC, a.app_gamma, kC, ay, ag);
+        const uint32_t* xp = (const uint32_t*)((const uint16_t*)a.app_x + (int64_t)b * a.app_stride * kC);
+#pragma unroll
+        for (int j = 0; j < 9; ++j) xr[j] = xp[(lane + 64 * j) >> 1];
+        if (a.app_gamma)
+#pragma unroll
+            for (int j = 0; j < 9; ++j) ag[j] = a.app_gamma[lane + 64 * j];
         ainv = a.rope.inv[lane & 31];
     }
     const int tl = app ? (int)sm.nslots - 1 - s_begin : -(1 << 30);  // tile row of slot t in tile 0
@@ -940,12 +950,18 @@ __global__ void __launch_bounds__(256) attn_dec(AttnArgs a, int64_t split_len, i
     constexpr uint32_t kTileBytes = 2 * kTileElems;
     uint32_t bq = 0, bn = kTileBytes, bo = 2 * kTileBytes;  // byte offsets: tiles t, t + 1, t - 1
     int fq = 0, fn = 1;
-    if (app) {
+    if (app) {  // (the ring store waits for the epilogue: a global store here would make this barrier
+                // wait for every tile load in flight)
         if (wv == 0) {
-            int trw = w_row + ((int)sm.nslots - 1 - ncs);  // ring row of position t
-            if (trw >= win_cap) trw -= win_cap;
-            row_store<FMT, 9>(ay, ag, a.app_gamma, a.app_eps, kC, kDN, kDR, a.rope_theta != 0.0, ainv, (double)t,
-                              a.win.nope, a.win.rope, a.win.scale, (int64_t)b * win_cap + trw, rys, rowt, hg == 0);
+            const uint32_t sh = (lane & 1) ? 0u : 16u, mask = (lane & 1) ? 0xffff0000u : 0xffffffffu;
+#pragma unroll
+            for (int j = 0; j < 9; ++j) {  // bf16 -> f32 (in asm: the compiler would move it up to the loads)
+                float f;
+                asm volatile("v_lshlrev_b32 %0, %1, %2\n\tv_and_b32 %0, %3, %0" : "=&v"(f) : "v"(sh), "v"(xr[j]), "v"(mask));
+                arow.y[j] = f;
+            }
+            row_prepare<FMT, 9>(arow, ag, a.app_gamma, a.app_eps, kC, kDN, kDR, a.rope_theta != 0.0, ainv, (double)t,
+                                rys, rowt);
         }
         __syncthreads();
     }
@@ -1069,6 +1085,11 @@ __global__ void __launch_bounds__(256) attn_dec(AttnArgs a, int64_t split_len, i
         }
     }
     const float lrun = sum4g(lpart);
+    if (app && hg == 0 && wv == 0) {  // the query row's window row into the ring
+        int trw = w_row + ((int)sm.nslots - 1 - ncs);  // ring row of position t
+        if (trw >= win_cap) trw -= win_cap;
+        row_commit<FMT, 9>(arow, kC, kDN, kDR, a.win.nope, a.win.rope, a.win.scale, (int64_t)b * win_cap + trw);
+    }
 
     // epilogue: head h = h0 + n, dims dbase + 16 nb + 4 g4 + i
     const int h = h0 + n;

@@ -169,13 +169,14 @@ __global__ void __launch_bounds__(64) kv_store_rows(CompressArgs a) {
     // (a workgroup past the last row reads row 0 of its sequence and stores nothing)
     const bool live = s < p0 + n_rows;
     const T* src = c_a + ((int64_t)b * in_stride + (live ? s - p0 : 0)) * c;
-    float y[J], g[J];
-    row_load<T, J>(src, gamma, c, y, g);
+    RowOut<J> o;
+    float g[J];
+    row_load<T, J>(src, gamma, c, o.y, g);
     if (!live) return;
     __shared__ float ys[64 * J];
     const int64_t row = (int64_t)b * cap + (ring ? s % cap : s);
-    row_store<FMT, J>(y, g, gamma, eps, c, d_nope, d_rope, rope, inv, (double)s, onope, orope, oscale, row, ys,
-                      nullptr, true);
+    row_prepare<FMT, J>(o, g, gamma, eps, c, d_nope, d_rope, rope, inv, (double)s, ys, nullptr);
+    row_commit<FMT, J>(o, c, d_nope, d_rope, onope, orope, oscale, row);
 }
 
 template <typename T, int FMT>
