@@ -56,6 +56,10 @@ def _declare(L):
     L.orc_mxfp4_block.restype = C.c_uint8
     L.orc_indexer_score_mxfp4.argtypes = [vp, i32, vp, _KV, i32, i32, i32, i32, vp, i32, vp, i32, i64]
     L.orc_indexer_score_mxfp4.restype = C.c_int
+    L.orc_linear.argtypes = [vp, i32, i64, i64, vp, i32, i64, i64, vp, i32, i64, i64, i32, i32, i32, i32]
+    L.orc_linear.restype = C.c_int
+    L.orc_grouped_out_proj.argtypes = [vp, i32, i32, i32, i32, i32, vp, i32, vp, i32, i32, vp, i32]
+    L.orc_grouped_out_proj.restype = C.c_int
     L.orc_kv_decode.argtypes = [_KV, i64, i64, i64, vp]
     L.orc_kv_decode.restype = None
     L.orc_kv_compress.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, f64, f64, i32, i32, i32, i64,
@@ -267,3 +271,30 @@ def attention(q, *, q_pos, comp: KV, m: int, idx=None, win: KV | None = None, n_
                              _p(lse))
     assert rc == 0
     return out, lse
+
+
+def linear(x, w, *, y_fmt: int = F32):
+    """x [batch][M][K] (or [M][K]), w [batch][N][K] (or [N][K]) -> y [batch][M][N] (f32 or bf16 bits)."""
+    x2, w2 = np.ascontiguousarray(x), np.ascontiguousarray(w)
+    squeeze = x2.ndim == 2
+    if squeeze:
+        x2, w2 = x2[None], w2[None]
+    bt, M, K = x2.shape
+    N = w2.shape[1]
+    y = np.zeros((bt, M, N), np.float32 if y_fmt == F32 else np.uint16)
+    rc = lib().orc_linear(_p(x2), _fmt_of(x2), K, M * K, _p(w2), _fmt_of(w2), K, N * K, _p(y), y_fmt, N, M * N,
+                          M, N, K, bt)
+    assert rc == 0
+    return y[0] if squeeze else y
+
+
+def grouped_out_proj(o, wg, wo, *, g: int, mid_fmt: int = BF16, out_fmt: int = F32):
+    """o [T][H][c], wg [g][d_g][H/g*c] bf16 bits, wo [d][g*d_g] bf16 bits -> out [T][d]."""
+    o = np.ascontiguousarray(o)
+    T, H, c = o.shape
+    d_g, d = wg.shape[1], wo.shape[0]
+    out = np.zeros((T, d), np.float32 if out_fmt == F32 else np.uint16)
+    rc = lib().orc_grouped_out_proj(_p(o), _fmt_of(o), T, H, c, g, _p(np.ascontiguousarray(wg)), d_g,
+                                    _p(np.ascontiguousarray(wo)), d, mid_fmt, _p(out), out_fmt)
+    assert rc == 0
+    return out

@@ -551,3 +551,47 @@ int orc_attention(const void* q, int32_t q_fmt, int32_t H, int32_t B, int32_t T,
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------- */
+/* Linear maps ([R] 2.3.1: projections of the hidden state; grouped output   */
+/* projection)                                                               */
+/* ------------------------------------------------------------------------- */
+
+int orc_linear(const void* x, int32_t x_fmt, int64_t ldx, int64_t sx, const void* w, int32_t w_fmt,
+               int64_t ldw, int64_t sw, void* y, int32_t y_fmt, int64_t ldy, int64_t sy, int32_t M,
+               int32_t N, int32_t K, int32_t batch) {
+    if (!x || !w || !y || M < 0 || N < 0 || K < 0 || batch < 1) return -1;
+    for (int32_t b = 0; b < batch; ++b) {
+#pragma omp parallel for schedule(dynamic, 4)
+        for (int32_t m = 0; m < M; ++m) {
+            double* xr = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+            for (int32_t k = 0; k < K; ++k) xr[k] = load_in(x, x_fmt, b * sx + m * ldx + k);
+            for (int32_t n = 0; n < N; ++n) {
+                double acc = 0.0;
+                for (int32_t k = 0; k < K; ++k) acc += xr[k] * load_in(w, w_fmt, b * sw + n * ldw + k);
+                const int64_t e = b * sy + m * ldy + n;
+                if (y_fmt == ORC_F32) ((float*)y)[e] = (float)acc;
+                else ((uint16_t*)y)[e] = orc_f32_to_bf16((float)acc);
+            }
+            free(xr);
+        }
+    }
+    return 0;
+}
+
+int orc_grouped_out_proj(const void* o, int32_t o_fmt, int32_t T, int32_t H, int32_t c, int32_t g,
+                         const void* wg, int32_t d_g, const void* wo, int32_t d, int32_t mid_fmt, void* out,
+                         int32_t out_fmt) {
+    if (g < 1 || H % g || T < 0 || d_g < 1 || d < 1) return -1;
+    const int32_t kg = H / g * c;  /* inputs of one group */
+    void* mid = malloc((mid_fmt == ORC_F32 ? 4 : 2) * (size_t)(T > 0 ? T : 1) * g * d_g);
+    if (!mid) return -1;
+    /* group j: rows t, inputs o[t][j * kg ..], weights wg[j] -> mid[t][j * d_g ..] */
+    int rc = orc_linear(o, o_fmt, (int64_t)H * c, kg, wg, ORC_BF16, kg, (int64_t)d_g * kg, mid, mid_fmt,
+                        (int64_t)g * d_g, d_g, T, d_g, kg, g);
+    if (rc == 0)
+        rc = orc_linear(mid, mid_fmt, (int64_t)g * d_g, 0, wo, ORC_BF16, (int64_t)g * d_g, 0, out, out_fmt, d, 0, T,
+                        d, g * d_g, 1);
+    free(mid);
+    return rc;
+}

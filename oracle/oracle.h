@@ -96,6 +96,22 @@ int orc_attention(const void* q, int32_t q_fmt, int32_t H, int32_t B, int32_t T,
                   orc_kv win, int32_t n_win, const float* sink, double sm_scale,
                   double rope_theta, void* out, int32_t out_fmt, float* lse);
 
+/* Linear maps around the path ([R] 2.3.1: the compressor inputs C, Z and the queries are linear
+ * projections of the hidden state; the grouped output projection):
+ *   Y[b][m][n] = sum_k X[b][m][k] W[b][n][k]
+ * X element (b, m, k) at x[b * sx + m * ldx + k], W at w[b * sw + n * ldw + k], Y at
+ * y[b * sy + m * ldy + n]; formats ORC_F32 / ORC_BF16; exact products, fp64 sums, one rounding. */
+int orc_linear(const void* x, int32_t x_fmt, int64_t ldx, int64_t sx, const void* w, int32_t w_fmt,
+               int64_t ldw, int64_t sw, void* y, int32_t y_fmt, int64_t ldy, int64_t sy, int32_t M,
+               int32_t N, int32_t K, int32_t batch);
+
+/* Grouped output projection ([R] 2.3.1): the H head outputs of a token (o [T][H][c]) form g groups
+ * of H/g heads; group j is projected to d_g dims by wg[j] ([g][d_g][H/g * c]), the g results are
+ * stored in mid_fmt and concatenated ([T][g * d_g]), then projected to d dims by wo ([d][g * d_g]). */
+int orc_grouped_out_proj(const void* o, int32_t o_fmt, int32_t T, int32_t H, int32_t c, int32_t g,
+                         const void* wg, int32_t d_g, const void* wo, int32_t d, int32_t mid_fmt, void* out,
+                         int32_t out_fmt);
+
 #ifdef __cplusplus
 }
 #endif

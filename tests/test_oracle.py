@@ -643,3 +643,53 @@ def test_indexer_mxfp4_quantises_q_per_head_block(orc):
     f = orc.indexer_score_mxfp4(q, w, _mxfp4_keys(orc, k2), q_pos=[600], m=m, score_fmt=orc.F32)
     for t in range(T):
         assert np.corrcoef(e[0, t], f[0, t])[0, 1] > 0.95
+
+
+# --------------------------------------------------------------------------
+# linear maps around the path ("DeepSeek-V4 中文翻译" section 2.3.1: projections of
+# the hidden state; grouped output projection)
+# --------------------------------------------------------------------------
+
+def test_linear_small_integers_brute_force(orc):
+    """Small-integer inputs: every product and sum is exact; checked against Python integer loops."""
+    g = np.random.default_rng(81)
+    bt, M, N, K = 2, 5, 7, 9
+    x = g.integers(-8, 9, (bt, M, K)).astype(np.float32)
+    w = g.integers(-8, 9, (bt, N, K))
+    y = orc.linear(x, S.to_bf16(w.astype(np.float32)))
+    for b in range(bt):
+        for m in range(M):
+            for n in range(N):
+                assert y[b, m, n] == sum(int(x[b, m, k]) * int(w[b, n, k]) for k in range(K))
+
+
+def test_linear_identity_permutation_and_strides(orc):
+    g = np.random.default_rng(82)
+    x = S.to_bf16(g.standard_normal((6, 16)).astype(np.float32))
+    eye = S.to_bf16(np.eye(16, dtype=np.float32))
+    np.testing.assert_array_equal(orc.linear(x, eye), S.from_bf16(x))          # W = I: Y = X exactly
+    perm = g.permutation(16)
+    pw = S.to_bf16(np.eye(16, dtype=np.float32)[perm])                          # row n picks column perm[n]
+    np.testing.assert_array_equal(orc.linear(x, pw), S.from_bf16(x)[:, perm])
+    # bf16 output = nearest-even rounding of the f32 result
+    w = S.to_bf16(g.standard_normal((5, 16)).astype(np.float32))
+    np.testing.assert_array_equal(orc.linear(x, w, y_fmt=orc.BF16), S.to_bf16(orc.linear(x, w) + np.float32(0)))
+
+
+def test_grouped_out_proj_is_block_diagonal_then_dense(orc):
+    """g groups projected separately then concatenated equals one map with the block-diagonal weight,
+    and g = 1 is two plain maps (numpy fp64 on the same rounded intermediate)."""
+    g_ = np.random.default_rng(83)
+    T, H, c, g, d_g, d = 3, 8, 12, 4, 5, 7
+    o = g_.standard_normal((T, H, c)).astype(np.float32)
+    wg = S.to_bf16(g_.standard_normal((g, d_g, H // g * c)).astype(np.float32))
+    wo = S.to_bf16(g_.standard_normal((d, g * d_g)).astype(np.float32))
+    for mid_fmt in (orc.F32, orc.BF16):
+        out = orc.grouped_out_proj(o, wg, wo, g=g, mid_fmt=mid_fmt)
+        blk = np.zeros((g * d_g, H * c))
+        for j in range(g):
+            blk[j * d_g:(j + 1) * d_g, j * (H // g) * c:(j + 1) * (H // g) * c] = S.from_bf16(wg[j])
+        mid = o.reshape(T, H * c).astype(np.float64) @ blk.T
+        mid = mid.astype(np.float32) if mid_fmt == orc.F32 else S.from_bf16(S.to_bf16(mid.astype(np.float32)))
+        ref = (mid.astype(np.float64) @ S.from_bf16(wo).astype(np.float64).T).astype(np.float32)
+        np.testing.assert_allclose(out, ref, rtol=1e-6, atol=1e-6)
