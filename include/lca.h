@@ -247,6 +247,37 @@ int lca_hca_attn_append(const void* q, int32_t q_dtype, int32_t H, int32_t B, in
                         float eps, const float* sink, float sm_scale, double rope_theta, void* out,
                         int32_t out_dtype, float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * lca_linear -- the linear maps around the attention ([R] 2.3.1: the
+ * compressor inputs C_a, Z_a, C_b, Z_b, the low-rank queries and the indexer
+ * queries are projections of the hidden state):
+ *   y[b][m][n] = sum_k x[b][m][k] w[b][n][k]      (b < batch, m < M, n < N)
+ * x and w bf16 (w holds one output per row, as a weight matrix), accumulated
+ * in f32, y of y_dtype (LCA_F32, or LCA_BF16 = nearest-even rounding of the
+ * f32 sum).  Element (b, m, k) of x is at x + b sx + m ldx + k, (b, n, k) of
+ * w at w + b sw + n ldw + k, (b, m, n) of y at y + b sy + m ldy + n (strides
+ * in elements).  Requires K a positive multiple of 8; ldx, ldw >= K and,
+ * with sx and sw, multiples of 8; ldy >= N; x, w 16-byte aligned.  M <= 4
+ * takes a kernel that streams w once (decode); larger M, MFMA tiles.
+ */
+int lca_linear(const void* x, int64_t ldx, int64_t sx, const void* w, int64_t ldw, int64_t sw, void* y,
+               int32_t y_dtype, int64_t ldy, int64_t sy, int32_t M, int32_t N, int32_t K,
+               int32_t batch, void* stream);
+
+/*
+ * lca_grouped_out_proj -- the grouped output projection of [R] 2.3.1: the H
+ * head outputs of each of T tokens (o: bf16 [T][H][c]) form g groups of H/g
+ * heads; group j is projected to d_g dims by wg[j] (bf16 [g][d_g][H/g * c]),
+ * the g results are rounded to bf16 into mid (caller buffer, bf16 [T][g *
+ * d_g]), and mid is projected to d dims by wo (bf16 [d][g * d_g]) into out
+ * ([T][d], out_dtype LCA_F32 or LCA_BF16).  Two lca_linear launches.
+ * Requires H % g == 0, (H / g) * c and d_g multiples of 8, 16-byte aligned
+ * pointers.
+ */
+int lca_grouped_out_proj(const void* o, int32_t T, int32_t H, int32_t c, int32_t g, const void* wg,
+                         int32_t d_g, const void* wo, int32_t d, void* mid, void* out, int32_t out_dtype,
+                         void* stream);
+
 /* Workspace bytes for lca_csa_attn / lca_hca_attn with at most max_keys
  * attended rows per query (selected or visible entries + window).  Covers the
  * split partials of short (decode-sized) launches and, from 128 query rows on,

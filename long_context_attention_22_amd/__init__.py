@@ -6,7 +6,7 @@ fallback: when the built library is missing every call raises.
 
 Calls (same names as the C ABI):
     kv_compress, indexer_score, indexer_score_mxfp4, topk_select, csa_attn, hca_attn,
-    csa_attn_append, hca_attn_append
+    csa_attn_append, hca_attn_append, linear, grouped_out_proj
 and helpers KV (the lca_kv storage planes), attn_workspace_size.
 """
 from __future__ import annotations
@@ -63,10 +63,13 @@ def lib():
                                           vp, f32, vp, f32, f64, vp, i32, vp, vp, sz, vp]
         L.lca_hca_attn_append.argtypes = [vp, i32, i32, i32, i32, vp, _KV, i32, _KV, i32, vp, i32, i64, vp, f32,
                                           vp, f32, f64, vp, i32, vp, vp, sz, vp]
+        L.lca_linear.argtypes = [vp, i64, i64, vp, i64, i64, vp, i32, i64, i64, i32, i32, i32, i32, vp]
+        L.lca_grouped_out_proj.argtypes = [vp, i32, i32, i32, i32, vp, i32, vp, i32, vp, vp, i32, vp]
         L.lca_attn_workspace_size.argtypes = [i32, i32, i32, i32, i64]
         L.lca_attn_workspace_size.restype = sz
         for name in ("lca_kv_compress", "lca_indexer_score", "lca_indexer_score_mxfp4", "lca_topk_select",
-                     "lca_csa_attn", "lca_hca_attn", "lca_csa_attn_append", "lca_hca_attn_append"):
+                     "lca_csa_attn", "lca_hca_attn", "lca_csa_attn_append", "lca_hca_attn_append", "lca_linear",
+                     "lca_grouped_out_proj"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -255,3 +258,28 @@ def hca_attn_append(q, out, x_win, *, q_pos, comp: KV, m: int, win: KV, n_win: i
                                      _rows_stride(x_win, T), _ptr(gamma), float(eps), _ptr(sink),
                                      float(sm_scale), float(rope_theta), _ptr(out), _dtype(out), _ptr(lse),
                                      _ptr(ws), nbytes, _stream(stream)))
+
+
+def linear(x, w, y, stream=None):
+    """y[b][m][n] = sum_k x[b][m][k] w[b][n][k]: x [batch][M][K] or [M][K] bf16, w [batch][N][K] or [N][K] bf16
+    (rows contiguous, any row / batch strides), y [batch][M][N] or [M][N] f32 / bf16."""
+    x3, w3, y3 = (t if t.dim() == 3 else t.unsqueeze(0) for t in (x, w, y))
+    bt, M, K = x3.shape
+    N = w3.shape[1]
+    for t in (x3, w3, y3):
+        if t.stride(2) != 1:
+            raise ValueError("linear operands need contiguous rows")
+    if x3.dtype != torch.bfloat16 or w3.dtype != torch.bfloat16:
+        raise TypeError("x and w must be bf16")
+    _check(lib().lca_linear(_ptr(x3), x3.stride(1), x3.stride(0) if bt > 1 else 0, _ptr(w3), w3.stride(1),
+                            w3.stride(0) if w3.shape[0] > 1 else 0, _ptr(y3), _dtype(y3), y3.stride(1),
+                            y3.stride(0) if bt > 1 else 0, int(M), int(N), int(K), int(bt), _stream(stream)))
+
+
+def grouped_out_proj(o, wg, wo, mid, out, *, g: int, stream=None):
+    """o [T][H][c] bf16, wg [g][d_g][H/g*c] bf16, wo [d][g*d_g] bf16, mid [T][g*d_g] bf16 scratch,
+    out [T][d] f32 / bf16."""
+    T, H, c = o.shape
+    d_g, d = wg.shape[1], wo.shape[0]
+    _check(lib().lca_grouped_out_proj(_ptr(o), int(T), int(H), int(c), int(g), _ptr(wg), int(d_g), _ptr(wo),
+                                      int(d), _ptr(mid), _ptr(out), _dtype(out), _stream(stream)))

@@ -5,6 +5,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <climits>
 #include <cmath>
 #include <cstring>
 
@@ -475,6 +476,57 @@ int lca_hca_attn(const void* q, int32_t q_dtype, int32_t H, int32_t B, int32_t T
     g_err[0] = 0;
     return attn_common(q, q_dtype, H, B, T, q_pos, comp, m, nullptr, 0, win, n_win, sink, sm_scale,
                        rope_theta, out, out_dtype, lse, ws, ws_bytes, stream);
+}
+
+int lca_linear(const void* x, int64_t ldx, int64_t sx, const void* w, int64_t ldw, int64_t sw, void* y,
+               int32_t y_dtype, int64_t ldy, int64_t sy, int32_t M, int32_t N, int32_t K, int32_t batch,
+               void* stream) {
+    g_err[0] = 0;
+    if (!x || !w || !y) return fail(LCA_EINVAL, "x, w and y must be non-NULL");
+    if (y_dtype != LCA_F32 && y_dtype != LCA_BF16) return fail(LCA_EDTYPE, "y_dtype must be f32 or bf16");
+    if (M < 0 || N < 1 || batch < 1) return fail(LCA_ESHAPE, "bad M / N / batch");
+    if (K < 8 || K % 8) return fail(LCA_ESHAPE, "K must be a positive multiple of 8 (got %d)", K);
+    if (ldx < K || ldw < K || ldy < N || sx < 0 || sw < 0 || sy < 0)
+        return fail(LCA_ESHAPE, "row strides must cover the rows (ldx, ldw >= K, ldy >= N)");
+    if (ldx % 8 || ldw % 8 || sx % 8 || sw % 8)
+        return fail(LCA_EALIGN, "x and w strides must be multiples of 8 elements (16-byte rows)");
+    if (!aligned16(x) || !aligned16(w) || ((uintptr_t)y & (y_dtype == LCA_F32 ? 3u : 1u)))
+        return fail(LCA_EALIGN, "x and w must be 16-byte aligned, y aligned to its element");
+    lca::GemmArgs a;
+    memset(&a, 0, sizeof a);
+    a.x = x; a.w = w; a.y = y; a.ldx = ldx; a.sx = sx; a.ldw = ldw; a.sw = sw; a.ldy = ldy; a.sy = sy;
+    a.M = M; a.N = N; a.K = K; a.batch = batch; a.y_dtype = y_dtype;
+    return hip_status(lca::launch_gemm(a, (hipStream_t)stream));
+}
+
+int lca_grouped_out_proj(const void* o, int32_t T, int32_t H, int32_t c, int32_t g, const void* wg, int32_t d_g,
+                         const void* wo, int32_t d, void* mid, void* out, int32_t out_dtype, void* stream) {
+    g_err[0] = 0;
+    if (!o || !wg || !wo || !mid || !out) return fail(LCA_EINVAL, "o, wg, wo, mid and out must be non-NULL");
+    if (out_dtype != LCA_F32 && out_dtype != LCA_BF16) return fail(LCA_EDTYPE, "out_dtype must be f32 or bf16");
+    if (T < 0 || H < 1 || c < 1 || g < 1 || H % g || d_g < 1 || d < 1)
+        return fail(LCA_ESHAPE, "bad T / H / c / g / d_g / d (H must be a multiple of g)");
+    const int64_t kg = (int64_t)(H / g) * c;
+    if (kg % 8 || d_g % 8 || kg > INT32_MAX || (int64_t)g * d_g > INT32_MAX)
+        return fail(LCA_ESHAPE, "(H / g) * c and d_g must be multiples of 8");
+    if (!aligned16(o) || !aligned16(wg) || !aligned16(wo) || !aligned16(mid) || !aligned16(out))
+        return fail(LCA_EALIGN, "pointers must be 16-byte aligned");
+    if (T == 0) return LCA_OK;
+    lca::GemmArgs a;
+    memset(&a, 0, sizeof a);
+    // the g group projections: one batch entry per group
+    a.x = o; a.ldx = (int64_t)H * c; a.sx = kg;
+    a.w = wg; a.ldw = kg; a.sw = (int64_t)d_g * kg;
+    a.y = mid; a.y_dtype = LCA_BF16; a.ldy = (int64_t)g * d_g; a.sy = d_g;
+    a.M = T; a.N = d_g; a.K = (int32_t)kg; a.batch = g;
+    hipError_t e = lca::launch_gemm(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e);
+    // the dense projection of the concatenated intermediate
+    a.x = mid; a.ldx = (int64_t)g * d_g; a.sx = 0;
+    a.w = wo; a.ldw = (int64_t)g * d_g; a.sw = 0;
+    a.y = out; a.y_dtype = out_dtype; a.ldy = d; a.sy = 0;
+    a.M = T; a.N = d; a.K = g * d_g; a.batch = 1;
+    return hip_status(lca::launch_gemm(a, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -121,4 +121,17 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
 // stores first)
 bool attn_fuses_store(const AttnArgs& a);
 
+// Linear map Y[b][m][n] = sum_k X[b][m][k] W[b][n][k] (bf16 X, W; f32 accumulation).  Element
+// strides in elements: X (b, m, k) at x + b sx + m ldx + k, W (b, n, k) at w + b sw + n ldw + k,
+// Y (b, m, n) at y + b sy + m ldy + n.  K, ldx, ldw, sx, sw multiples of 8 (16-byte rows); K >= 8.
+struct GemmArgs {
+    const void* x;
+    const void* w;
+    void* y;
+    int64_t ldx, sx, ldw, sw, ldy, sy;
+    int32_t M, N, K, batch;
+    int32_t y_dtype;
+};
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
+
 }  // namespace lca

@@ -230,3 +230,16 @@ def test_attn_append_validation(L):
         assert call(csa, eps=-1.0) == 1
         assert call(csa, x=FAKE + 4) == 4
         assert call(csa, xs=-1) == 2
+
+
+def test_linear_validation(L):
+    def call(x=FAKE, ldx=64, sx=0, w=FAKE2, ldw=64, sw=0, ydt=lca.F32, ldy=32, M=4, N=32, K=64, bt=1):
+        return L.lca_linear(x, ldx, sx, w, ldw, sw, FAKE2, ydt, ldy, 0, M, N, K, bt, None)
+    assert call(x=None) == 1
+    assert call(ydt=lca.FP8) == 3
+    assert call(K=60) == 2 and call(K=0) == 2 and call(N=0) == 2 and call(bt=0) == 2
+    assert call(ldx=32) == 2 and call(ldy=16) == 2
+    assert call(ldx=68) == 4 and call(sx=4, bt=2) == 4
+    assert call(x=FAKE + 8) == 4
+    assert L.lca_grouped_out_proj(FAKE, 4, 6, 64, 4, FAKE2, 64, FAKE2, 96, FAKE2, FAKE2, lca.F32, None) == 2  # H % g
+    assert L.lca_grouped_out_proj(FAKE, 4, 8, 63, 4, FAKE2, 64, FAKE2, 96, FAKE2, FAKE2, lca.F32, None) == 2  # (H/g) c % 8

@@ -444,3 +444,64 @@ def test_attention_append(fmt, mode, B, T, xdt):
     err = np.abs(host(out) - o).max()
     assert err <= 2e-2, err
     np.testing.assert_allclose(host(lg), lse, atol=1e-3, rtol=1e-4)
+
+
+# --------------------------------------------------------------------------
+# linear maps around the path ("DeepSeek-V4 中文翻译" section 2.3.1)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K,bt", [(1, 300, 136, 1), (3, 77, 520, 2), (4, 64, 8, 1), (2, 33, 4104, 1),
+                                      (200, 130, 72, 1), (256, 256, 1024, 3), (129, 257, 200, 2)])
+@pytest.mark.parametrize("ydt", [orc.F32, orc.BF16])
+def test_linear(M, N, K, bt, ydt):
+    """Streaming (M <= 4) and tiled (larger M) maps against the oracle: f32 within 1e-5 of the sum of
+    |products| (f32 accumulation), bf16 within one step of the oracle's rounding or that bound."""
+    x = S.to_bf16(S.normal(91, "x", (bt, M, K)))
+    w = S.to_bf16(S.normal(92, "w", (bt, N, K)))
+    o = orc.linear(x, w, y_fmt=ydt)
+    y = torch.full((bt, M, N), 7.0, dtype=torch.float32 if ydt == orc.F32 else torch.bfloat16, device="cuda")
+    lca.linear(dev(x), dev(w), y)
+    g = host(y)
+    bound = 1e-5 * np.einsum("bmk,bnk->bmn", np.abs(S.from_bf16(x)).astype(np.float64),
+                             np.abs(S.from_bf16(w)).astype(np.float64)) + 1e-30
+    if ydt == orc.F32:
+        assert np.all(np.abs(g.astype(np.float64) - o) <= bound)
+    else:
+        gv, ov = S.from_bf16(g).astype(np.float64), S.from_bf16(o).astype(np.float64)
+        assert np.all((bf16_ulps(g, o) <= 1) | (np.abs(gv - ov) <= bound))
+
+
+def test_linear_strided_slices():
+    """Row / batch strides: a column slice of a wider activation and a shared weight (batch stride 0)."""
+    T, Kw, K, N, bt = 70, 200, 64, 48, 3
+    xf = S.to_bf16(S.normal(93, "xf", (T, Kw)))
+    w = S.to_bf16(S.normal(94, "w", (N, K)))
+    xs = dev(xf)
+    ys = torch.zeros(bt, T, N, dtype=torch.float32, device="cuda")
+    # batch b reads columns [64 b, 64 b + 64) of every row
+    x3 = torch.as_strided(xs, (bt, T, K), (K, Kw, 1))
+    lca.linear(x3, dev(w), ys)
+    g = host(ys)
+    for b in range(bt):
+        o = orc.linear(np.ascontiguousarray(xf[:, K * b:K * b + K]), w)
+        np.testing.assert_allclose(g[b], o, rtol=1e-5, atol=1e-4)
+
+
+@pytest.mark.parametrize("T", [1, 37, 300])
+def test_grouped_out_proj(T):
+    """Grouped output projection against the oracle's (bf16 intermediate): the intermediate may round
+    one bf16 step apart where the f32 and fp64 sums straddle a rounding boundary, so the bound is one
+    such step of every intermediate, weighted by |wo|, plus the f32 accumulation bound."""
+    H, c, g, d_g, d = 16, 64, 4, 64, 96
+    o = S.to_bf16(S.normal(95, "o", (T, H, c)))
+    wg = S.to_bf16(S.normal(96, "wg", (g, d_g, H // g * c), 0.05))
+    wo = S.to_bf16(S.normal(97, "wo", (d, g * d_g), 0.05))
+    ref = orc.grouped_out_proj(o, wg, wo, g=g, mid_fmt=orc.BF16)
+    mid_exact = np.concatenate([orc.linear(np.ascontiguousarray(o[:, j * (H // g):(j + 1) * (H // g)].reshape(T, -1)),
+                                           wg[j]) for j in range(g)], -1).astype(np.float64)
+    step = np.exp2(np.floor(np.log2(np.maximum(np.abs(mid_exact), 1e-30))) - 7)
+    bound = step @ np.abs(S.from_bf16(wo)).astype(np.float64).T + 1e-4 * np.abs(ref) + 1e-6
+    mid = torch.empty(T, g * d_g, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty(T, d, dtype=torch.float32, device="cuda")
+    lca.grouped_out_proj(dev(o), dev(wg), dev(wo), mid, out, g=g)
+    assert np.all(np.abs(host(out).astype(np.float64) - ref) <= bound)
