@@ -16,7 +16,9 @@ Also reported (key "extra"): the same 1M decode with the CSA indexer's QK
 path in MXFP4 and the top-2048 recall of bf16 and MXFP4-QK scores against
 f32 scores; the same stack's 4096-token chunked prefill at 1M context (with
 the chunk's MXFP4 indexer call timed beside the bf16 one); and CSA decode for
-32 sequences at 131,072 tokens.  "roofline"
+32 sequences at 131,072 tokens; and the linear maps around one attention
+layer (projections and the grouped output projection) for a 4096-token chunk
+and for one decode token.  "roofline"
 covers the dominant decode kernel (indexer_score, HBM-bound), timed with HIP
 events on its stream inside the timed graph.  "cpu_baseline" is the fp64
 oracle timed on host cores on a bounded sample (four decode steps of the
@@ -518,6 +520,58 @@ def bench_decode_c4(W: int, K: int, seed: int = 1004):
                 indexer=dict(launch_ms=ind_ms, gbs=gbs, frac=gbs / HBM_PEAK_GBS, bytes=nbytes))
 
 
+def bench_projections(reps: int = 5, seed: int = 1006):
+    """The linear maps around one attention layer (lca_linear / lca_grouped_out_proj), shaped as the
+    pages' smaller model ([R] 4.2.1: hidden 4096, query compression 1024, 64 heads, output projection in
+    8 groups of 1024) with this benchmark's heads of 512 + 64 and 16 x 128 indexer: a 4096-token
+    chunk (MFMA tiles) and one decode token (weights streamed once).  Weights N(0, 1/fan_in), bf16."""
+    d, dq, H, c, HI, dI, g, dg = 4096, 1024, 64, C, 16, 128, 8, 1024
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+
+    def wt(n, k):
+        return (torch.randn(n, k, device="cuda", generator=gen) * k ** -0.5).to(torch.bfloat16)
+
+    maps = [("q_down", d, dq), ("q_up", dq, H * c), ("kv_ca_za_cb_zb", d, 4 * c), ("idx_keys_4x128", d, 4 * dI),
+            ("idx_q", dq, HI * dI), ("idx_w", d, HI)]
+    ws = {nm: wt(n, k) for nm, k, n in maps}
+    wg = torch.stack([wt(dg, H // g * c) for _ in range(g)])
+    wo = wt(d, g * dg)
+    res = {}
+    for T in (4096, 1):
+        xs = {k: torch.randn(T, k, device="cuda", generator=gen).to(torch.bfloat16) for k in (d, dq)}
+        o = torch.randn(T, H, c, device="cuda", generator=gen).to(torch.bfloat16)
+        mid = torch.empty(T, g * dg, dtype=torch.bfloat16, device="cuda")
+        out = torch.empty(T, d, dtype=torch.bfloat16, device="cuda")
+        row = {}
+        tot_ms, tot_fl, tot_by = 0.0, 0.0, 0.0
+        for nm, k, n in maps + [("grouped_out_proj", H * c, d)]:
+            if nm == "grouped_out_proj":
+                fn = lambda: lca.grouped_out_proj(o, wg, wo, mid, out, g=g)
+                fl = 2.0 * T * (g * dg * (H // g) * c + d * g * dg)
+                by = 2.0 * (g * dg * (H // g) * c + d * g * dg + T * (H * c + 2 * g * dg + d))
+            else:
+                y = torch.empty(T, n, dtype=torch.bfloat16, device="cuda")
+                fn = (lambda x=xs[k], w=ws[nm], y=y: lca.linear(x, w, y))
+                fl = 2.0 * T * n * k
+                by = 2.0 * (n * k + T * (k + n))
+            fn()
+            torch.cuda.synchronize()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(reps):
+                fn()
+            e.record()
+            torch.cuda.synchronize()
+            ms = s.elapsed_time(e) / reps
+            tot_ms, tot_fl, tot_by = tot_ms + ms, tot_fl + fl, tot_by + by
+            row[nm] = dict(ms=ms, tflops=fl / (ms * 1e-3) / 1e12, gbs=by / (ms * 1e-3) / 1e9)
+        row["total"] = dict(ms=tot_ms, tflops=tot_fl / (tot_ms * 1e-3) / 1e12,
+                            mfma_frac=tot_fl / (tot_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                            gbs=tot_by / (tot_ms * 1e-3) / 1e9, hbm_frac=tot_by / (tot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+        res[f"T{T}"] = row
+    return res
+
+
 # ----------------------------------------------------------------------------
 # CPU baseline: the fp64 oracle on a bounded sample of the 1M decode workload
 # ----------------------------------------------------------------------------
@@ -632,6 +686,12 @@ def main():
         c4 = bench_decode_c4(W, min(K, 64))
         log(f"32 x 128K decode: {c4['ms_per_step'] * 1e3:.1f} us/step, {c4['tokens_per_s']:.0f} tok/s")
         extra["decode_csa_b32_128k"] = c4
+        torch.cuda.empty_cache()
+        pj = bench_projections()
+        log(f"layer projections: 4096-token chunk {pj['T4096']['total']['ms']:.2f} ms "
+            f"({pj['T4096']['total']['tflops']:.0f} TFLOP/s), one decode token {pj['T1']['total']['ms'] * 1e3:.1f} us "
+            f"({pj['T1']['total']['gbs']:.0f} GB/s)")
+        extra["layer_projections"] = pj
     else:
         del stacks
     cpu = None if args.no_cpu else cpu_baseline()

@@ -6,18 +6,19 @@
 // Many rows: MFMA tiles.  A 256-thread workgroup computes a 128 x 128 tile of Y, each wave a
 // 64 x 64 quarter as 4 x 4 blocks of v_mfma_f32_16x16x32_bf16 (both operands K-contiguous: lane l
 // reads 8 consecutive k of row l mod 16 with one ds_read_b128).  K advances 64 at a time through
-// two LDS buffers whose rows are padded to 72 elements (144 bytes: the sixteen rows one block read
-// touches start 36 banks apart, so they fall in distinct banks); the next slice's global loads are
-// issued before the current slice's MFMAs, one barrier per slice.
-// Few rows (decode, M <= 4): the map is bound by reading W once.  Each wave produces 4 outputs for
-// every row of X: lane l reads 16 bytes of each of its 4 weight rows per 512-element step, four
-// steps in flight, and the 64 partial sums of an output meet in one wave reduction.
+// two LDS buffers whose rows are padded to 80 elements (160 bytes; measured against 64, 72, 88 and
+// 96: the fewest bank conflicts); the global loads run two slices ahead (two register sets), one
+// barrier per slice.
+// Few rows (decode, M <= 4): the map is bound by reading W once.  Lane l reads 16 bytes of each of a
+// wave's 4 weight rows per 512-element step of K, four steps in flight, and an output's 64 lane sums
+// meet in a wave reduction.  With few outputs the four waves of a workgroup split K over the same 4
+// outputs (their sums meet in LDS, added in a fixed order); with many, each wave has 4 of its own.
 #include "device.h"
 #include "kernels.h"
 
 namespace lca {
 
-constexpr int kGT = 128, kGK = 64, kGS = 72;  // tile rows / columns, K slice, LDS row stride
+constexpr int kGT = 128, kGK = 64, kGS = 80;  // tile rows / columns, K slice, LDS row stride
 constexpr int kGemvRows = 4;                  // M at most this: the streaming kernel
 
 template <typename TY>
@@ -46,33 +47,35 @@ __global__ void __launch_bounds__(256) gemm_mfma(GemmArgs a) {
     // This thread's four 16-byte chunks of each operand's slice: chunk q = tid + 256 i is row q / 8,
     // elements 8 (q mod 8) .. of the slice.  Rows past M / N re-read the last row (their results are
     // not stored); chunks past K (K is a multiple of 8) read the last chunk and are zeroed.
-    const uint16_t* xp[4];
-    const uint16_t* wp[4];
+    // (32-bit element offsets from the operands' bases: loads then take the scalar-base form)
+    uint32_t xo[4], wo[4];
     int kk[4], lo[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int q = tid + 256 * i, r = q >> 3;
         kk[i] = 8 * (q & 7);
         lo[i] = r * kGS + kk[i];
-        xp[i] = X + (int64_t)min(m0 + r, M - 1) * a.ldx;
-        wp[i] = W + (int64_t)min(n0 + r, N - 1) * a.ldw;
+        xo[i] = (uint32_t)((int64_t)min(m0 + r, M - 1) * a.ldx);
+        wo[i] = (uint32_t)((int64_t)min(n0 + r, N - 1) * a.ldw);
     }
-    u32x4 rx[4], rw[4];
-    auto load = [&](int k0) {
+    // two register sets: the slice after next is loaded while the next one waits for its LDS buffer
+    u32x4 rx[2][4], rw[2][4];
+    // (chunks past K are zeroed when stored, not when loaded: a use right after the load would make
+    // the wave wait for it)
+    auto load = [&](int st, int k0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int k = k0 + kk[i];
-            const int kc = min(k, K - 8);
-            const u32x4 vx = *(const u32x4*)(xp[i] + kc), vw = *(const u32x4*)(wp[i] + kc);
-            rx[i] = k < K ? vx : u32x4{0u, 0u, 0u, 0u};
-            rw[i] = k < K ? vw : u32x4{0u, 0u, 0u, 0u};
+            const uint32_t kc = (uint32_t)min(k0 + kk[i], K - 8);
+            rx[st][i] = *(const u32x4*)(X + (xo[i] + kc));
+            rw[st][i] = *(const u32x4*)(W + (wo[i] + kc));
         }
     };
-    auto store = [&](int buf) {
+    auto store = [&](int st, int buf, int k0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            *(u32x4*)&As[buf][lo[i]] = rx[i];
-            *(u32x4*)&Bs[buf][lo[i]] = rw[i];
+            const bool ok = k0 + kk[i] < K;
+            *(u32x4*)&As[buf][lo[i]] = ok ? rx[st][i] : u32x4{0u, 0u, 0u, 0u};
+            *(u32x4*)&Bs[buf][lo[i]] = ok ? rw[st][i] : u32x4{0u, 0u, 0u, 0u};
         }
     };
 
@@ -82,14 +85,8 @@ __global__ void __launch_bounds__(256) gemm_mfma(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int nk = (K + kGK - 1) / kGK;
-    load(0);
-    store(0);
-    __syncthreads();
     const int fr = (lane & 15) * kGS + 8 * (lane >> 4);  // this lane's fragment offset in a block
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) load((kt + 1) * kGK);
+    auto compute = [&](int buf) {
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             bf16x8 af[4], bw[4];
@@ -102,9 +99,31 @@ __global__ void __launch_bounds__(256) gemm_mfma(GemmArgs a) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bw[j], acc[i][j], 0, 0, 0);
         }
-        if (kt + 1 < nk) store(buf ^ 1);
+    };
+    // slice kt is in LDS buffer kt mod 2, slice kt + 1 in register set (kt + 1) mod 2
+    // (no branches in the loop body: slices past the end are loaded again from the last slice and
+    // stored into the free buffer, so the compiler counts the loads in flight exactly)
+    const int nk = (K + kGK - 1) / kGK, klast = (nk - 1) * kGK;
+    // (compiler barriers keep the phases in this order: the stores of the next slice must not move
+    // up, where they would wait for its loads)
+    auto step = [&](int kt, int cur, int nxt) {
+        load(cur, min((kt + 2) * kGK, klast));
+        asm volatile("" ::: "memory");
+        compute(cur);
+        asm volatile("" ::: "memory");
+        store(nxt, nxt, (kt + 1) * kGK);
         __syncthreads();
+    };
+    load(0, 0);
+    store(0, 0, 0);
+    load(1, min(kGK, klast));
+    __syncthreads();
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+        step(kt, 0, 1);
+        step(kt + 1, 1, 0);
     }
+    if (kt < nk) compute(0);  // an odd slice count: the last slice is in buffer 0
 
     // lane holds rows 4 (lane / 16) + r of each block, column lane mod 16
     TY* Y = (TY*)a.y + (int64_t)b * a.sy;
@@ -121,11 +140,16 @@ __global__ void __launch_bounds__(256) gemm_mfma(GemmArgs a) {
         }
 }
 
-template <int MR, typename TY>
+// KS: the four waves split K over the workgroup's 4 outputs (few outputs: more workgroups); else
+// each wave takes 4 outputs of its own over all of K (16 per workgroup).
+template <int MR, typename TY, bool KS>
 __global__ void __launch_bounds__(256) gemv_stream(GemmArgs a) {
+    __shared__ float red[4][MR][4];
     const int b = blockIdx.z, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int M = a.M, N = a.N, K = a.K;
-    const int n0 = blockIdx.x * 16 + 4 * wv;  // this wave's 4 outputs (rows of W)
+    // KS: wave wv takes every fourth 512-element step of K, k = 2048 i + 512 wv + 8 lane
+    const int n0 = KS ? blockIdx.x * 4 : blockIdx.x * 16 + 4 * wv;
+    const int kstep = KS ? 2048 : 512, kfirst = KS ? 512 * wv : 0;
     const uint16_t* X = (const uint16_t*)a.x + (int64_t)b * a.sx;
     const uint16_t* W = (const uint16_t*)a.w + (int64_t)b * a.sw;
     const uint16_t* wr[4];
@@ -136,14 +160,14 @@ __global__ void __launch_bounds__(256) gemv_stream(GemmArgs a) {
     for (int m = 0; m < MR; ++m)
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[m][r] = 0.0f;
-    // four 512-element steps per round, loads first (branch-free: chunks past K read the last chunk
+    // four steps of this wave per round, loads first (branch-free: chunks past K read the last chunk
     // and count zero)
-    for (int kb = 0; kb < K; kb += 2048) {
+    for (int kb = kfirst; kb < K; kb += 4 * kstep) {
         u32x4 wv_[4][4], xv[4][MR];
         bool ok[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int k = kb + 512 * u + 8 * lane;
+            const int k = kb + kstep * u + 8 * lane;
             ok[u] = k < K;
             const int kc = min(k, K - 8);
 #pragma unroll
@@ -173,22 +197,49 @@ __global__ void __launch_bounds__(256) gemv_stream(GemmArgs a) {
         }
     }
     TY* Y = (TY*)a.y + (int64_t)b * a.sy;
+    if constexpr (!KS) {
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float s = wave_sum_dpp(acc[m][r]);
+                if (lane == 0 && m < M && n0 + r < N) put_y<TY>(Y + (int64_t)m * a.ldy + n0 + r, s);
+            }
+        return;
+    }
 #pragma unroll
     for (int m = 0; m < MR; ++m)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const float s = wave_sum_dpp(acc[m][r]);
-            if (lane == 0 && m < M && n0 + r < N) put_y<TY>(Y + (int64_t)m * a.ldy + n0 + r, s);
+            if (lane == 0) red[wv][m][r] = s;
         }
+    __syncthreads();
+    // the four waves' partial sums in a fixed order
+    const int t = threadIdx.x;
+    if (t < MR * 4) {
+        const int m = t >> 2, r = t & 3;
+        const float s = (red[0][m][r] + red[1][m][r]) + (red[2][m][r] + red[3][m][r]);
+        if (m < M && n0 + r < N) put_y<TY>(Y + (int64_t)m * a.ldy + n0 + r, s);
+    }
 }
 
 template <typename TY>
 static void launch_gemm_t(const GemmArgs& a, hipStream_t st) {
     if (a.M <= kGemvRows) {
-        dim3 grid((unsigned)((a.N + 15) / 16), 1, (unsigned)a.batch);
-        if (a.M == 1) hipLaunchKernelGGL((gemv_stream<1, TY>), grid, dim3(256), 0, st, a);
-        else if (a.M == 2) hipLaunchKernelGGL((gemv_stream<2, TY>), grid, dim3(256), 0, st, a);
-        else hipLaunchKernelGGL((gemv_stream<4, TY>), grid, dim3(256), 0, st, a);
+        // outputs per workgroup: 4 (K split over the waves) while that leaves fewer than ~2048
+        // workgroups, else 16
+        const bool ks = (int64_t)a.N * a.batch < 8192;
+        dim3 grid((unsigned)(ks ? (a.N + 3) / 4 : (a.N + 15) / 16), 1, (unsigned)a.batch);
+        if (ks) {
+            if (a.M == 1) hipLaunchKernelGGL((gemv_stream<1, TY, true>), grid, dim3(256), 0, st, a);
+            else if (a.M == 2) hipLaunchKernelGGL((gemv_stream<2, TY, true>), grid, dim3(256), 0, st, a);
+            else hipLaunchKernelGGL((gemv_stream<4, TY, true>), grid, dim3(256), 0, st, a);
+        } else {
+            if (a.M == 1) hipLaunchKernelGGL((gemv_stream<1, TY, false>), grid, dim3(256), 0, st, a);
+            else if (a.M == 2) hipLaunchKernelGGL((gemv_stream<2, TY, false>), grid, dim3(256), 0, st, a);
+            else hipLaunchKernelGGL((gemv_stream<4, TY, false>), grid, dim3(256), 0, st, a);
+        }
         return;
     }
     dim3 grid((unsigned)((a.N + kGT - 1) / kGT), (unsigned)((a.M + kGT - 1) / kGT), (unsigned)a.batch);
