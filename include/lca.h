@@ -66,6 +66,7 @@ extern "C" {
 #define LCA_EALIGN 4      /* pointer not 16-byte aligned                   */
 #define LCA_EWORKSPACE 5  /* workspace missing or too small                */
 #define LCA_EHIP 6        /* the HIP runtime refused a launch              */
+#define LCA_ENOMEM 7      /* the paged cache has no free page or slot      */
 
 /* dtypes / storage formats */
 #define LCA_F32 0

@@ -7,7 +7,8 @@ fallback: when the built library is missing every call raises.
 Calls (same names as the C ABI):
     kv_compress, indexer_score, indexer_score_mxfp4, topk_select, csa_attn, hca_attn,
     csa_attn_append, hca_attn_append, linear, grouped_out_proj
-and helpers KV (the lca_kv storage planes), attn_workspace_size.
+and helpers KV (the lca_kv storage planes), attn_workspace_size.  The paged cache
+(include/lca_cache.h) is bound in the cache module (PagedCache).
 """
 from __future__ import annotations
 
@@ -18,6 +19,8 @@ from dataclasses import dataclass
 import torch
 
 F32, BF16, FP8, MXFP4 = 0, 1, 2, 3
+# status codes (LcaError.code)
+OK, EINVAL, ESHAPE, EDTYPE, EALIGN, EWORKSPACE, EHIP, ENOMEM = range(8)
 MAX_BATCH = 64
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblca.so")

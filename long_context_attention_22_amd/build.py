@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liblca.so")
 OBJ = os.path.join(ROOT, "_build", "lca")
 
-SOURCES = ["kv_compress.hip", "indexer.hip", "topk.hip", "attn.hip", "gemm.hip", "capi.cpp"]
+SOURCES = ["kv_compress.hip", "indexer.hip", "topk.hip", "attn.hip", "gemm.hip", "cache.hip", "capi.cpp"]
 # MFMA accumulators stay in VGPRs (-amdgpu-mfma-vgpr-form): the kernels keep their accumulators
 # within 256 VGPRs, and AGPR accumulators made the compiler copy them back and forth around the
 # attention loop's conditional rescale.

@@ -11,6 +11,7 @@
 
 #include "../../include/lca.h"
 #include "kernels.h"
+#include "status.h"
 
 namespace {
 
@@ -77,6 +78,17 @@ lca::Pos to_pos(const int64_t* p, int32_t B) {
 }
 
 }  // namespace
+
+namespace lca {
+int set_error(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+void clear_error() { g_err[0] = 0; }
+}  // namespace lca
 
 extern "C" {
 

@@ -96,11 +96,16 @@ class Params:
 
 class Layer:
     def __init__(self, spec: LayerSpec, B: int, comp_cap: int, win_cap: int, t_max: int, params: Params,
-                 device="cuda"):
+                 device="cuda", kvs: dict | None = None):
+        """kvs: the layer's storage from elsewhere (e.g. a PagedCache): {"comp", "win", "keys" (CSA)} KVs of
+        B sequences; default: fresh contiguous planes of comp_cap / win_cap rows."""
         self.spec, self.B, self.params = spec, B, params
-        self.comp = KV.empty(spec.fmt, B, comp_cap, spec.d_nope, spec.d_rope, device)
-        self.win = KV.empty(spec.fmt, B, win_cap, spec.d_nope, spec.d_rope, device)
-        self.keys = KV.empty(spec.key_fmt, B, comp_cap, spec.d_I, 0, device) if spec.kind == "csa" else None
+        if kvs is not None:
+            self.comp, self.win, self.keys = kvs["comp"], kvs["win"], kvs.get("keys")
+        else:
+            self.comp = KV.empty(spec.fmt, B, comp_cap, spec.d_nope, spec.d_rope, device)
+            self.win = KV.empty(spec.fmt, B, win_cap, spec.d_nope, spec.d_rope, device)
+            self.keys = KV.empty(spec.key_fmt, B, comp_cap, spec.d_I, 0, device) if spec.kind == "csa" else None
         self.t_max = t_max
         if spec.kind == "csa":
             sdt = torch.bfloat16 if spec.score_fmt == BF16 else torch.float32
@@ -171,3 +176,28 @@ class Layer:
         run = record or (lambda name, fn: fn())
         run("kv_compress", lambda: self.compress(raw, t0, T))
         self.attend(t0, q, out, q_idx, w, lse, record, x_win=raw.rows("c_a", t0, T))
+
+
+def cache_streams(specs: list[LayerSpec], comp_rows: list[int], win_cap: int):
+    """The CacheStreams of a stack of layers for a PagedCache: per layer i the compressed entries
+    ("i/comp", paged, ratio m), the window ring ("i/win", state cache) and for CSA the indexer keys
+    ("i/keys", paged)."""
+    from .cache import CacheStream
+    out = []
+    for i, (s, rows) in enumerate(zip(specs, comp_rows)):
+        out.append(CacheStream(f"{i}/comp", s.fmt, s.d_nope, s.d_rope, s.m, rows))
+        out.append(CacheStream(f"{i}/win", s.fmt, s.d_nope, s.d_rope, 0, win_cap))
+        if s.kind == "csa":
+            out.append(CacheStream(f"{i}/keys", s.key_fmt, s.d_I, 0, s.m, rows))
+    return out
+
+
+def slot_kvs(cache, i: int, b0: int, B: int) -> dict:
+    """Layer i's KVs for the B sequences in slots b0 .. b0+B-1 of a PagedCache."""
+    def sl(kv):
+        cut = lambda t: None if t is None else t[b0:b0 + B]
+        return KV(cut(kv.nope), cut(kv.rope), cut(kv.scale), kv.fmt, kv.d_nope, kv.d_rope, kv.cap)
+    out = {"comp": sl(cache.kv(f"{i}/comp")), "win": sl(cache.kv(f"{i}/win"))}
+    if f"{i}/keys" in cache.streams:
+        out["keys"] = sl(cache.kv(f"{i}/keys"))
+    return out

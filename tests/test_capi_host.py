@@ -36,7 +36,8 @@ def no_gpu():
 
 
 def _declared():
-    txt = open(os.path.join(ROOT, "include", "lca.h")).read()
+    txt = "".join(open(os.path.join(ROOT, "include", f)).read() for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+                  if f.endswith(".h"))
     return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(lca_\w+)\s*\(", txt, re.M)))
 
 
@@ -44,7 +45,7 @@ def test_exports_every_declared_symbol(L):
     names = _declared()
     assert set(names) >= {"lca_kv_compress", "lca_indexer_score", "lca_topk_select", "lca_csa_attn",
                           "lca_hca_attn", "lca_attn_workspace_size", "lca_topk_workspace_size",
-                          "lca_last_error", "lca_version"}
+                          "lca_last_error", "lca_version", "lca_cache_create", "lca_cache_fork"}
     for n in names:
         assert hasattr(L, n), n
     assert L.lca_version() == 1
@@ -243,3 +244,29 @@ def test_linear_validation(L):
     assert call(x=FAKE + 8) == 4
     assert L.lca_grouped_out_proj(FAKE, 4, 6, 64, 4, FAKE2, 64, FAKE2, 96, FAKE2, FAKE2, lca.F32, None) == 2  # H % g
     assert L.lca_grouped_out_proj(FAKE, 4, 8, 63, 4, FAKE2, 64, FAKE2, 96, FAKE2, FAKE2, lca.F32, None) == 2  # (H/g) c % 8
+
+
+def test_cache_validation(L):
+    """Plane rules of lca_cache_create, checked before the runtime is asked for anything."""
+    from long_context_attention_22_amd import cache as pc
+    Lc = pc._lib()
+
+    def create(planes, max_seqs=2, page=65536, pool=4):
+        arr = (pc._Plane * len(planes))(*[pc._Plane(*p) for p in planes])
+        h = C.c_void_p()
+        return Lc.lca_cache_create(arr, len(planes), max_seqs, page, pool, C.byref(h))
+
+    csa = (512, 1024, 4, 0)                            # fp8 nope rows of a CSA stream
+    assert create([csa], max_seqs=0) == lca.EINVAL
+    assert create([csa], max_seqs=lca.MAX_BATCH + 1) == lca.EINVAL
+    assert create([(512, 1024, -1, 0)]) == lca.EINVAL
+    assert create([(512, 1024, 4, 1)]) == lca.EINVAL  # reserved field
+    assert create([csa], page=0) == lca.ESHAPE
+    assert create([(768, 1024, 4, 0)]) == lca.ESHAPE  # rows do not tile the page
+    assert create([(512, 1000, 4, 0)]) == lca.ESHAPE  # a slot is not whole pages
+    # a page must cover a multiple of lcm(m) raw tokens: 4096 B of 512 B rows at m = 4 is 32 tokens,
+    # not a multiple of lcm(4, 128)
+    assert create([csa, (512, 1024, 128, 0)], page=4096) == lca.ESHAPE
+    assert b"lcm" in L.lca_last_error()
+    assert create([(4, 9, 0, 0)]) == lca.ESHAPE        # state plane of 36 bytes per slot
+    assert Lc.lca_cache_destroy(None) == lca.OK

@@ -6,7 +6,7 @@ the same seeded inputs.  Large workloads are compared on sampled rows, which
 the oracle computes one by one.  Configs 4 and 5 build their GPU state with
 bench.py's own builder, i.e. in the launch configuration the benchmark times.
 
-Bars (the benchmark spec): selected-entry sets equal on every decided row (the
+Bars: selected-entry sets equal on every decided row (the
 oracle's k-th and (k+1)-th candidates are separated: fp32 gap > 1e-3
 relative and no candidate near the boundary sits within 1e-5 of a bf16
 rounding midpoint), recall >= 99.9% overall; outputs max-abs <= 1e-4 (fp32

@@ -1,0 +1,243 @@
+"""The paged heterogeneous cache (include/lca_cache.h) under the whole layer path.
+
+Three sequences of different lengths are prefilled in chunks (ragged last chunk) and decoded
+through a CSA layer (m = 4, indexer, top-k 64) and an HCA layer (m' = 128) whose caches live in a
+PagedCache; the same steps run on contiguous caches.  Every output must be bit-identical (the
+kernels do not know about pages: the cache changes where rows live, not what is computed).  Then
+a sequence is forked at its current length (prefix reuse) and parent and child continue with
+different tokens, checked against contiguous copies; the parent is closed half way and the child
+must keep its shared pages.  The child's last outputs are also checked against the oracle
+computed from the raw inputs (the bars of the other parity tests: equal selections on decided
+rows, bf16 outputs within one bf16 step plus 2e-2).
+"""
+import numpy as np
+import pytest
+import torch
+
+import lca_synth as S
+import long_context_attention_22_amd as lca
+import oracle as orc
+from gpu_util import host
+from long_context_attention_22_amd.cache import CacheStream, PagedCache
+from long_context_attention_22_amd.stack import Layer, LayerSpec, RawStream, cache_streams, slot_kvs
+
+pytestmark = pytest.mark.gpu
+C = 576
+LENS = [1500, 2930, 700]
+CHUNK, WIN, DEC = 256, 384, 6
+PAGE = 16384
+SPAN = 3200                 # raw positions generated per sequence
+
+
+def _specs(key_fmt):
+    return [LayerSpec("csa", 4, H=16, k=64, key_fmt=key_fmt), LayerSpec("hca", 128, H=16)]
+
+
+def _raw(seed, spec, tag, n):
+    import bench
+    return bench.make_raw(seed, spec, tag, 1, 0, n)
+
+
+def _queries(seed, tag, spec, t0, T):
+    q = S.to_bf16(S.normal(seed, f"{tag}/q/{t0}", (1, T, spec.H, C)))
+    if spec.kind != "csa":
+        return q, None, None
+    qi = S.to_bf16(S.normal(seed, f"{tag}/qi/{t0}", (1, T, spec.H_I, spec.d_I)))
+    w = S.normal(seed, f"{tag}/w/{t0}", (1, T, spec.H_I), 0.25)
+    return q, qi, w
+
+
+def _dev(a):
+    from gpu_util import dev
+    return None if a is None else dev(a)
+
+
+class Seq:
+    """One sequence's layers (B = 1) over given storage, with its raw streams."""
+
+    def __init__(self, specs, params, comp_rows, raws, kvs=None):
+        self.layers = [Layer(sp, 1, comp_rows[i], WIN, CHUNK, params[i], kvs=None if kvs is None else kvs[i])
+                       for i, sp in enumerate(specs)]
+        self.raws = raws
+
+    def step(self, seed, tags, t0, T):
+        outs = []
+        for i, ly in enumerate(self.layers):
+            q, qi, w = _queries(seed, tags[i], ly.spec, t0, T)
+            out = torch.zeros(1, T, ly.spec.H, C, dtype=torch.bfloat16, device="cuda")
+            ly.step(self.raws[i], t0, _dev(q), out, q_idx=_dev(qi), w=_dev(w))
+            outs.append(out)
+        return outs
+
+
+def _clone_kv(kv):
+    cl = lambda t: None if t is None else t.clone()
+    return lca.KV(cl(kv.nope), cl(kv.rope), cl(kv.scale), kv.fmt, kv.d_nope, kv.d_rope, kv.cap)
+
+
+def _fork_raw(raw: RawStream, at: int, seed: int, tag: str) -> RawStream:
+    """The parent's raw rows before position `at`, fresh rows from there on."""
+    def f(name, t):
+        if t is None:
+            return None
+        new = S.to_bf16(S.activations(seed, f"{tag}/child/{name}", tuple(t.shape)))
+        from gpu_util import dev
+        out = t.clone()
+        out[:, at:] = dev(new)[:, at:]
+        return out
+    return RawStream(raw.base, *(f(n, getattr(raw, n)) for n in ("c_a", "z_a", "c_b", "z_b", "i_ca", "i_za",
+                                                                  "i_cb", "i_zb")))
+
+
+def _same(a, b, what):
+    for i, (x, y) in enumerate(zip(a, b)):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16)), f"{what}: layer {i} outputs differ"
+
+
+@pytest.mark.parametrize("key_fmt", [lca.BF16, lca.MXFP4])
+def test_paged_stack_matches_contiguous_and_forks(key_fmt):
+    import bench
+    seed = 4400 + key_fmt
+    specs = _specs(key_fmt)
+    tags = [f"pg{key_fmt}_csa", f"pg{key_fmt}_hca"]
+    params = [bench.make_params(seed, sp, tg) for sp, tg in zip(specs, tags)]
+    comp_rows = [SPAN // sp.m + 2 for sp in specs]
+    cache = PagedCache(cache_streams(specs, comp_rows, WIN), max_seqs=4, page_bytes=PAGE, pool_pages=400)
+    raws = [[_raw(seed + 17 * b, sp, tg, SPAN) for sp, tg in zip(specs, tags)] for b in range(len(LENS))]
+    paged, contig = [], []
+    for b in range(len(LENS)):
+        slot = cache.open()
+        assert slot == b
+        paged.append(Seq(specs, params, comp_rows, raws[b], [slot_kvs(cache, i, slot, 1) for i in range(2)]))
+        contig.append(Seq(specs, params, comp_rows, raws[b]))
+    # chunked prefill (ragged last chunk) and decode, sequence by sequence, reserving as they grow
+    for b, L in enumerate(LENS):
+        for t0 in list(range(0, L, CHUNK)) + list(range(L, L + DEC)):
+            T = min(CHUNK, L - t0) if t0 < L else 1
+            cache.reserve(b, t0 + T)
+            _same(paged[b].step(seed + b, tags, t0, T), contig[b].step(seed + b, tags, t0, T), f"seq {b} t0 {t0}")
+    st = cache.stats()
+    assert st["open_slots"] == 3 and st["shared_pages"] == 0 and st["mapped_pages"] > 0
+    torch.cuda.synchronize()
+
+    # prefix reuse: fork sequence 1 at its current length; both continue with different tokens
+    n = LENS[1] + DEC
+    child = cache.fork(1, n)
+    assert child == 3 and cache.tokens(child) == n
+    st = cache.stats()
+    assert st["shared_pages"] > 0, st
+    craw = [_fork_raw(r, n, seed, tg) for r, tg in zip(raws[1], tags)]
+    kid_p = Seq(specs, params, comp_rows, craw, [slot_kvs(cache, i, child, 1) for i in range(2)])
+    kid_c = Seq(specs, params, comp_rows, craw)
+    for i in range(2):
+        src, dst = contig[1].layers[i], kid_c.layers[i]
+        dst.comp, dst.win = _clone_kv(src.comp), _clone_kv(src.win)
+        if src.keys is not None:
+            dst.keys = _clone_kv(src.keys)
+    last = None
+    for j in range(16):                      # the child crosses an HCA entry boundary at 2944
+        t = n + j
+        if j < 4:                            # the parent goes on a little, then ends
+            cache.reserve(1, t + 1)
+            _same(paged[1].step(seed + 1, tags, t, 1), contig[1].step(seed + 1, tags, t, 1), f"parent t {t}")
+        elif j == 4:
+            cache.close(1)
+            assert cache.stats()["shared_pages"] == 0
+        cache.reserve(child, t + 1)
+        last = kid_p.step(seed + 99, tags, t, 1)
+        _same(last, kid_c.step(seed + 99, tags, t, 1), f"child t {t}")
+    torch.cuda.synchronize()
+
+    if key_fmt == lca.BF16:  # the child's last step against the oracle, from the raw inputs
+        _oracle_check(specs, tags, params, craw, n + 15, seed + 99, last, kid_p)
+    for s in (0, 2, child):
+        cache.close(s)
+    st = cache.stats()
+    assert st["free_pages"] == st["pool_pages"] and st["open_slots"] == 0
+    cache.destroy()
+
+
+def _oracle_check(specs, tags, params, craw, t, qseed, gout, kid):
+    from test_gpu_configs import _check_rows
+    n = t + 1
+    for i, (sp, tg) in enumerate(zip(specs, tags)):
+        r = {k: host(getattr(craw[i], k))[:, :n] for k in ("c_a", "z_a", "c_b", "z_b", "i_ca", "i_za", "i_cb", "i_zb")
+             if getattr(craw[i], k) is not None}
+        pr = params[i]
+        ph = lambda x: None if x is None else x.cpu().numpy()
+        cap = n // sp.m + 1
+        comp = orc.KV.empty(orc.FP8, 1, cap, 512, 64)
+        ov = sp.overlap
+        orc.kv_compress(r["c_a"], r["z_a"], r["c_b"] if ov else None, r["z_b"] if ov else None, comp, m=sp.m,
+                        overlap=ov, first_pos=[0], bias_a=ph(pr.bias_a), bias_b=ph(pr.bias_b) if ov else None,
+                        gamma=ph(pr.gamma), rope_theta=1e4)
+        win = orc.KV.empty(orc.FP8, 1, WIN, 512, 64)
+        lo = max(0, n - WIN)
+        orc.kv_compress(r["c_a"][:, lo:], r["z_a"][:, lo:], None, None, win, m=1, overlap=0, first_pos=[lo],
+                        gamma=ph(pr.gamma), rope_theta=1e4, ring=1)
+        q, qi, w = _queries(qseed, tg, sp, t, 1)
+        if sp.kind == "csa":
+            keys = orc.KV(np.zeros((1, cap, 128), np.uint16), np.zeros((1, cap, 0), np.uint16), None, orc.BF16, 128,
+                          0, cap)
+            orc.kv_compress(r["i_ca"], r["i_za"], r["i_cb"], r["i_zb"], keys, m=sp.m, overlap=1, first_pos=[0],
+                            bias_a=ph(pr.i_bias_a), bias_b=ph(pr.i_bias_b))
+            s32 = orc.indexer_score(qi, w, keys.nope, q_pos=[t], m=sp.m, score_fmt=orc.F32)
+            s16 = orc.indexer_score(qi, w, keys.nope, q_pos=[t], m=sp.m, score_fmt=orc.BF16)
+            ix = orc.topk_select(s16, q_pos=[t], m=sp.m, k=sp.k)
+            o, _ = orc.attention(q, q_pos=[t], comp=comp, m=sp.m, idx=ix, win=win, n_win=sp.n_win,
+                                 sink=ph(pr.sink), sm_scale=C ** -0.5, rope_theta=1e4)
+            gi, oi, os32 = [host(kid.layers[i].idx)[0, 0]], [ix[0, 0]], [s32[0, 0]]
+        else:
+            o, _ = orc.attention(q, q_pos=[t], comp=comp, m=sp.m, win=win, n_win=sp.n_win, sink=ph(pr.sink),
+                                 sm_scale=C ** -0.5, rope_theta=1e4)
+            gi, oi, os32 = [], [], []
+        _check_rows(f"paged child layer {i} ({sp.kind})", gi, oi, os32, [host(gout[i])[0, 0]], [o[0, 0]],
+                    lambda _: (t + 1) // sp.m, sp.k)
+
+
+def test_paged_cache_accounting_and_errors():
+    # one classical stream (bf16 rows of 512 + 64: two planes) and one state ring
+    streams = [CacheStream("c", lca.BF16, 512, 64, 4, 1000), CacheStream("w", lca.BF16, 512, 64, 0, 256)]
+    cache = PagedCache(streams, max_seqs=2, page_bytes=65536, pool_pages=6)
+    comp = cache.kv("c")
+    assert comp.cap % 64 == 0 and comp.cap >= 1000 and cache.kv("w").cap == 256
+    a = cache.open()
+    b = cache.open()
+    with pytest.raises(lca.LcaError) as e:
+        cache.open()
+    assert e.value.code == lca.ENOMEM
+    # 400 tokens: nope rows [0, 101) of 64 per page -> pages 0, 1; rope 512 per page -> page 0
+    cache.reserve(a, 400)
+    assert cache.stats()["free_pages"] == 5
+    comp.nope[a, :101] = 1.5
+    comp.rope[a, :101] = -2.0
+    # too many pages for the pool: refused, nothing mapped
+    with pytest.raises(lca.LcaError) as e:
+        cache.reserve(b, 4000)
+    assert e.value.code == lca.ENOMEM
+    assert cache.stats()["free_pages"] == 5 and cache.tokens(b) == 0
+    with pytest.raises(lca.LcaError) as e:
+        cache.reserve(a, 4 * comp.cap + 4)
+    assert e.value.code == lca.ESHAPE
+    cache.close(b)
+    with pytest.raises(lca.LcaError):
+        cache.fork(b, 0)                 # closed parent
+    kid = cache.fork(a, 400)             # 100 complete rows: page 1 holds rows 64..99 -> copied
+    assert kid == b and cache.stats()["shared_pages"] == 0 and cache.stats()["free_pages"] == 4
+    torch.cuda.synchronize()
+    assert torch.all(comp.nope[kid, :100] == 1.5) and torch.all(comp.rope[kid, :100] == -2.0)
+    comp.nope[kid, 100] = 7.0            # the child's own row: the parent keeps its value
+    torch.cuda.synchronize()
+    assert float(comp.nope[a, 100, 0]) == 1.5
+    cache.reserve(a, 600)                # parent: pages 2 (rows 128..150)
+    kid2_err = None
+    try:
+        cache.fork(a, 600)               # no free slot
+    except lca.LcaError as ex:
+        kid2_err = ex.code
+    assert kid2_err == lca.ENOMEM
+    cache.close(a)
+    cache.close(kid)
+    st = cache.stats()
+    assert st["free_pages"] == st["pool_pages"] == 6 and st["open_slots"] == 0
+    cache.destroy()
