@@ -18,7 +18,9 @@ f32 scores; the same stack's 4096-token chunked prefill at 1M context (with
 the chunk's MXFP4 indexer call timed beside the bf16 one); and CSA decode for
 32 sequences at 131,072 tokens; and the linear maps around one attention
 layer (projections and the grouped output projection) for a 4096-token chunk
-and for one decode token.  "roofline"
+and for one decode token; the 1M decode again with every cache in the paged
+cache (one slot per replica, 64 KiB and 2 MiB pages) and the cost of forking
+the 1M-token sequence (prefix reuse).  "roofline"
 covers the dominant decode kernel (indexer_score, HBM-bound), timed with HIP
 events on its stream inside the timed graph.  "cpu_baseline" is the fp64
 oracle timed on host cores on a bounded sample (four decode steps of the
@@ -45,7 +47,8 @@ if ROOT not in sys.path:
 
 import lca_synth as S  # noqa: E402
 import long_context_attention_22_amd as lca  # noqa: E402
-from long_context_attention_22_amd.stack import Layer, LayerSpec, Params, RawStream  # noqa: E402
+from long_context_attention_22_amd.stack import (Layer, LayerSpec, Params, RawStream, cache_streams,  # noqa: E402
+                                                 slot_kvs)
 
 METRIC = "CSA/HCA decode tokens/s at 128K–1M ctx (HBM GB/s %) + prefill tokens/s"
 # HBM traffic of the decode indexer launch from rocprofv3 FETCH_SIZE / WRITE_SIZE passes, scaled by
@@ -351,6 +354,102 @@ def bench_decode_1m(W: int, K: int, R: int, seed: int = 1005):
                               bytes_per_launch=nbytes, launch_ms=ind_ms, timing=timing)), stacks
 
 
+def _per_slot_pages(streams, n_tokens: int, page: int) -> int:
+    from long_context_attention_22_amd.cache import _planes_of, _row_bytes
+    total = 0
+    for st in streams:
+        if st.m > 0:
+            for _, dt, n in _planes_of(st):
+                total += -(-((n_tokens // st.m + 1) * _row_bytes(dt, n)) // page)
+    return total
+
+
+def paged_stack(base: Stack, cache, slot: int, n_tokens: int) -> Stack:
+    """The stack state of `base` (one sequence) copied into slot `slot` of a PagedCache."""
+    cache.reserve(slot, n_tokens)
+    st = Stack.__new__(Stack)
+    st.__dict__.update(base.__dict__)
+    st.layers = []
+    for i, src in enumerate(base.layers):
+        kv = slot_kvs(cache, i, slot, 1)
+        vis = min((n_tokens // src.spec.m) + 1, src.comp.cap)
+        for name in ("comp", "keys"):
+            a, b = getattr(src, name), kv.get(name)
+            if a is None:
+                continue
+            for pl in ("nope", "rope", "scale"):
+                if getattr(a, pl) is not None:
+                    getattr(b, pl)[:, :vis].copy_(getattr(a, pl)[:, :vis])
+        for pl in ("nope", "rope", "scale"):
+            if getattr(src.win, pl) is not None:
+                getattr(kv["win"], pl).copy_(getattr(src.win, pl))
+        dst = Layer.__new__(Layer)
+        dst.__dict__.update(src.__dict__)
+        dst.comp, dst.win, dst.keys = kv["comp"], kv["win"], kv.get("keys")
+        if src.keys is not None:
+            dst.scores, dst.idx = torch.empty_like(src.scores), torch.empty_like(src.idx)
+            dst.topk_ws = torch.empty_like(src.topk_ws)
+        dst.ws = torch.empty_like(src.ws)
+        st.layers.append(dst)
+    st.out = [torch.empty_like(o) for o in base.out]
+    return st
+
+
+def bench_paged(stacks, W: int, K: int, contiguous_ms: float, prefill_chunk_ms: float | None,
+                pages=(64 << 10, 2 << 20)):
+    """The 1M decode with every cache (compressed entries, indexer keys, window rings) in a PagedCache:
+    one slot per replica, filled with the contiguous stacks' state; then a fork of the 1M-token sequence."""
+    from long_context_attention_22_amd.cache import PagedCache
+    R = len(stacks)
+    base = stacks[0]
+    n_pos = (W + K + R - 1) // R + 2
+    n_tokens = T0_1M + n_pos + 1
+    rows = [ly.comp.cap for ly in base.layers]
+    streams = cache_streams(STACK_SPECS, rows, base.layers[0].win.cap)
+    out = {}
+    for page in pages:
+        per = _per_slot_pages(streams, n_tokens, page)
+        t = time.perf_counter()
+        cache = PagedCache(streams, max_seqs=R + 1, page_bytes=page, pool_pages=R * per + 64)
+        t_create = time.perf_counter() - t
+        t = time.perf_counter()
+        for r in range(R):
+            cache.open()
+            cache.reserve(r, n_tokens)
+        t_map = time.perf_counter() - t
+        mapped = cache.stats()["mapped_pages"]
+        pst = [paged_stack(base, cache, r, n_tokens) for r in range(R)]
+        torch.cuda.synchronize()
+        ms, g = timed_graph_decode(pst, W, K, None)
+        del g
+        torch.cuda.synchronize()
+        # prefix reuse: the 1M-token sequence forked at its current length
+        t = time.perf_counter()
+        child = cache.fork(0, n_tokens)
+        torch.cuda.synchronize()
+        t_fork = time.perf_counter() - t
+        stf = cache.stats()
+        t = time.perf_counter()
+        cache.close(child)
+        t_close = time.perf_counter() - t
+        st = cache.stats()
+        res = dict(ms_per_step=ms / K, tokens_per_s=K / (ms * 1e-3), vs_contiguous=(ms / K) / contiguous_ms,
+                   create_s=t_create, map_s=t_map, pages_mapped=mapped, map_us_per_page=t_map / mapped * 1e6,
+                   pool_pages=st["pool_pages"], device_bytes=st["device_bytes"],
+                   fork=dict(tokens=n_tokens, ms=t_fork * 1e3, shared_pages=stf["shared_pages"],
+                             fresh_pages=st["free_pages"] - stf["free_pages"], close_ms=t_close * 1e3))
+        if prefill_chunk_ms:
+            res["fork"]["prefill_estimate_ms"] = prefill_chunk_ms * n_tokens / 4096
+        out[f"page_{page // 1024}k"] = res
+        log(f"paged cache, {page // 1024} KiB pages: {res['ms_per_step'] * 1e3:.1f} us/step "
+            f"({res['vs_contiguous']:.3f} x contiguous); create {t_create:.2f} s, {mapped} pages mapped in "
+            f"{t_map:.2f} s; fork of {n_tokens} tokens {t_fork * 1e3:.1f} ms ({stf['shared_pages']} pages shared)")
+        del pst
+        cache.destroy()
+        torch.cuda.empty_cache()
+    return out
+
+
 def mxfp4_copy(src: lca.KV) -> lca.KV:
     """bf16 indexer keys re-stored as MXFP4 through the library's compressor (m = 1, no norm, no RoPE:
     each row is quantised as it is)."""
@@ -650,6 +749,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the prefill and the 32 x 128K decode")
     ap.add_argument("--mxfp4", action="store_true",
                     help="with --no-extra: still time the 1M decode with the MXFP4 indexer (no recall)")
+    ap.add_argument("--paged", action="store_true", help="with --no-extra: still time the paged-cache decode")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB device copy (reference for rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -677,10 +777,14 @@ def main():
             log(f"top-2048 recall vs f32 scores: bf16 {f4['recall_top2048']['bf16_scores_vs_f32']:.4f}, MXFP4 QK "
                 f"{f4['recall_top2048']['mxfp4_qk_vs_f32']:.4f}")
         extra["decode_1m_mxfp4_indexer"] = f4
+    if not args.no_extra or args.paged:
+        pf = None
+        if not args.no_extra:
+            pf = bench_prefill_1m(stacks[0])
+            log(f"1M prefill chunk: {pf['ms']:.2f} ms, {pf['tokens_per_s']:.0f} tok/s, {pf['tflops']:.0f} TFLOP/s")
+            extra["prefill_1m_chunk4096"] = pf
+        extra["decode_1m_paged_cache"] = bench_paged(stacks, W, K, res["ms_per_step"], pf and pf["ms"])
     if not args.no_extra:
-        pf = bench_prefill_1m(stacks[0])
-        log(f"1M prefill chunk: {pf['ms']:.2f} ms, {pf['tokens_per_s']:.0f} tok/s, {pf['tflops']:.0f} TFLOP/s")
-        extra["prefill_1m_chunk4096"] = pf
         del stacks
         torch.cuda.empty_cache()
         c4 = bench_decode_c4(W, min(K, 64))
