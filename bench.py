@@ -454,9 +454,7 @@ def mxfp4_copy(src: lca.KV) -> lca.KV:
     """bf16 indexer keys re-stored as MXFP4 through the library's compressor (m = 1, no norm, no RoPE:
     each row is quantised as it is)."""
     k4 = lca.KV.empty(lca.MXFP4, src.nope.shape[0], src.cap, src.d_nope, 0)
-    for b in range(src.nope.shape[0]):
-        x = src.nope[b:b + 1]
-        lca.kv_compress(x, torch.zeros_like(x), None, None, _seq_view(k4, b), m=1, overlap=0, first_pos=0)
+    lca.kv_compress(src.nope, torch.zeros_like(src.nope), None, None, k4, m=1, overlap=0, first_pos=0)
     return k4
 
 
@@ -614,9 +612,18 @@ def bench_decode_c4(W: int, K: int, seed: int = 1004):
     nbytes = indexer_bytes(vis, B)
     gbs = nbytes / (ind_ms * 1e-3) / 1e9
     step_bytes = nbytes + B * (1024 + 128) * 656 + B * 64 * C * 2 * 2
+    # the same decode with the indexer's QK path in MXFP4 (keys re-stored as MXFP4 by the compressor)
+    keys_to_mxfp4(st.layers[0])
+    torch.cuda.synchronize()
+    ms4, g = timed_graph_decode([st], W, K, None)
+    ind4 = graph_kernel_ms([st], W, K, "indexer_score")
+    del g
+    b4 = B * (vis * (64 + 4 + 2) + 16 * 128 * 2 + 16 * 4)
     return dict(batch=B, ctx=t0, ms_per_step=ms / K, tokens_per_s=B * K / (ms * 1e-3),
                 step_hbm_gbs=step_bytes / (ms / K * 1e-3) / 1e9,
-                indexer=dict(launch_ms=ind_ms, gbs=gbs, frac=gbs / HBM_PEAK_GBS, bytes=nbytes))
+                indexer=dict(launch_ms=ind_ms, gbs=gbs, frac=gbs / HBM_PEAK_GBS, bytes=nbytes),
+                mxfp4_indexer=dict(ms_per_step=ms4 / K, tokens_per_s=B * K / (ms4 * 1e-3), launch_ms=ind4,
+                                   bytes=b4, gbs=b4 / (ind4 * 1e-3) / 1e9))
 
 
 def bench_projections(reps: int = 5, seed: int = 1006):
@@ -788,7 +795,8 @@ def main():
         del stacks
         torch.cuda.empty_cache()
         c4 = bench_decode_c4(W, min(K, 64))
-        log(f"32 x 128K decode: {c4['ms_per_step'] * 1e3:.1f} us/step, {c4['tokens_per_s']:.0f} tok/s")
+        log(f"32 x 128K decode: {c4['ms_per_step'] * 1e3:.1f} us/step, {c4['tokens_per_s']:.0f} tok/s; with the MXFP4 "
+            f"indexer {c4['mxfp4_indexer']['ms_per_step'] * 1e3:.1f} us/step, {c4['mxfp4_indexer']['tokens_per_s']:.0f} tok/s")
         extra["decode_csa_b32_128k"] = c4
         torch.cuda.empty_cache()
         pj = bench_projections()
