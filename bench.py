@@ -364,8 +364,9 @@ def _per_slot_pages(streams, n_tokens: int, page: int) -> int:
     return total
 
 
-def paged_stack(base: Stack, cache, slot: int, n_tokens: int) -> Stack:
-    """The stack state of `base` (one sequence) copied into slot `slot` of a PagedCache."""
+def paged_stack(base: Stack, cache, slot: int, n_tokens: int, copy: bool = True) -> Stack:
+    """The stack state of `base` (one sequence) copied into slot `slot` of a PagedCache (copy=False: only
+    the stack's layers over that slot, e.g. for a slot filled by a fork)."""
     cache.reserve(slot, n_tokens)
     st = Stack.__new__(Stack)
     st.__dict__.update(base.__dict__)
@@ -373,14 +374,14 @@ def paged_stack(base: Stack, cache, slot: int, n_tokens: int) -> Stack:
     for i, src in enumerate(base.layers):
         kv = slot_kvs(cache, i, slot, 1)
         vis = min((n_tokens // src.spec.m) + 1, src.comp.cap)
-        for name in ("comp", "keys"):
+        for name in ("comp", "keys") if copy else ():
             a, b = getattr(src, name), kv.get(name)
             if a is None:
                 continue
             for pl in ("nope", "rope", "scale"):
                 if getattr(a, pl) is not None:
                     getattr(b, pl)[:, :vis].copy_(getattr(a, pl)[:, :vis])
-        for pl in ("nope", "rope", "scale"):
+        for pl in ("nope", "rope", "scale") if copy else ():
             if getattr(src.win, pl) is not None:
                 getattr(kv["win"], pl).copy_(getattr(src.win, pl))
         dst = Layer.__new__(Layer)

@@ -241,3 +241,35 @@ def test_paged_cache_accounting_and_errors():
     st = cache.stats()
     assert st["free_pages"] == st["pool_pages"] == 6 and st["open_slots"] == 0
     cache.destroy()
+
+
+def test_paged_1m_stack_and_fork():
+    """The benchmark's 1M-context 4-layer stack in the launch configuration bench.py times, on 2 MiB pages:
+    decode outputs bit-identical to the contiguous caches, and a fork of the 1M-token sequence decoding
+    on bit-identical to the contiguous sequence it was forked from."""
+    import bench
+    seed, t0, n_pos = 1005, bench.T0_1M, 12
+    base = bench.Stack(bench.STACK_SPECS, bench.STACK_TAGS, 1, t0, n_pos, 1, seed, win_cap=8192)
+    n_tokens = t0 + n_pos + 1
+    streams = cache_streams(bench.STACK_SPECS, [ly.comp.cap for ly in base.layers], 8192)
+    per = bench._per_slot_pages(streams, n_tokens, 2 << 20)
+    cache = PagedCache(streams, max_seqs=2, page_bytes=2 << 20, pool_pages=per + 64)
+    cache.open()
+    pst = bench.paged_stack(base, cache, 0, n_tokens)
+    for j in range(8):
+        base.decode(j)
+        pst.decode(j)
+        _same(pst.out, base.out, f"1M decode step {j}")
+    torch.cuda.synchronize()
+    kid = cache.fork(0, t0 + 8)
+    st = cache.stats()
+    assert kid == 1 and st["shared_pages"] > 0, st
+    kst = bench.paged_stack(base, cache, kid, n_tokens, copy=False)
+    for j in range(8, 12):
+        base.decode(j)
+        kst.decode(j)
+        _same(kst.out, base.out, f"1M forked decode step {j}")
+    torch.cuda.synchronize()
+    print(f"1M paged: 8 steps + 4 forked steps bit-identical; {st['shared_pages']} pages shared by the fork")
+    del pst, kst
+    cache.destroy()
