@@ -143,6 +143,7 @@ def clone_layer(src: Layer) -> Layer:
         dst.scores = torch.empty_like(src.scores)
         dst.idx = torch.empty_like(src.idx)
         dst.topk_ws = torch.empty_like(src.topk_ws)
+        dst.itk_ws = torch.zeros_like(src.itk_ws)
     dst.ws = torch.empty_like(src.ws)
     return dst
 
@@ -209,7 +210,9 @@ class KernelTimer:
 
 
 def graph_kernel_ms(stacks, W: int, K: int, name: str) -> float:
-    """Mean duration of one kernel's launches of the timed steps, replayed back to back in a graph."""
+    """Mean duration of one kernel's launches of the timed steps, replayed back to back in a graph.
+    (indexer_score: the decode step runs the indexer inside indexer_topk; its launches are collected
+    here as plain indexer_score calls with the same arguments.)"""
     R = len(stacks)
     launches = []
 
@@ -217,8 +220,13 @@ def graph_kernel_ms(stacks, W: int, K: int, name: str) -> float:
         if n == name:
             launches.append(fn)
 
+    fused = [(ly, ly.fuse_topk) for st in stacks for ly in st.layers]
+    for ly, _ in fused:
+        ly.fuse_topk = False
     for i in range(W, W + K):  # collect the launches (nothing runs: only the named one is kept)
         stacks[i % R].decode(i // R, record=lambda n, fn: grab(n, fn) if n == name else None)
+    for ly, f in fused:
+        ly.fuse_topk = f
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for fn in launches:
@@ -390,6 +398,7 @@ def paged_stack(base: Stack, cache, slot: int, n_tokens: int, copy: bool = True)
         if src.keys is not None:
             dst.scores, dst.idx = torch.empty_like(src.scores), torch.empty_like(src.idx)
             dst.topk_ws = torch.empty_like(src.topk_ws)
+            dst.itk_ws = torch.zeros_like(src.itk_ws)
         dst.ws = torch.empty_like(src.ws)
         st.layers.append(dst)
     st.out = [torch.empty_like(o) for o in base.out]

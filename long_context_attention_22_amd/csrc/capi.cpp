@@ -248,6 +248,63 @@ int lca_topk_select(const void* scores, int32_t score_dtype, int64_t s_stride, i
     return hip_status(lca::launch_topk(a, (hipStream_t)stream));
 }
 
+// Workspace of lca_indexer_topk: the split top-k's histograms, then one arrival counter per row.
+static size_t itk_counter_offset(int32_t B, int64_t s_stride) {
+    return (lca::topk_ws_bytes(B, 1, s_stride, LCA_BF16) + 15) / 16 * 16;
+}
+
+size_t lca_indexer_topk_workspace_size(int32_t B, int64_t s_stride, int32_t k) {
+    if (B < 1 || s_stride < 1 || k < 1) return 0;
+    if (lca::topk_split_chunks(B, s_stride, s_stride, LCA_BF16) == 0) return 0;
+    return itk_counter_offset(B, s_stride) + ((size_t)B * sizeof(uint32_t) + 15) / 16 * 16;
+}
+
+int lca_indexer_topk(const void* q, const float* w, const void* k, int64_t k_cap, int32_t H_I, int32_t d_I,
+                     int32_t B, const int64_t* q_pos, int32_t m, void* scores, int64_t s_stride, int32_t topk,
+                     int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    if (!q || !k || !scores || !idx) return fail(LCA_EINVAL, "q, k, scores and idx must be non-NULL");
+    if (m < 1) return fail(LCA_EINVAL, "m must be >= 1");
+    if (topk < 1) return fail(LCA_EINVAL, "k must be >= 1");
+    if (k_cap < 1 || s_stride < 1) return fail(LCA_ESHAPE, "bad k_cap / s_stride");
+    if (H_I != 16 || d_I != 128)
+        return fail(LCA_ESHAPE, "the indexer supports H_I = 16, d_I = 128 (got %d x %d)", H_I, d_I);
+    int rc = check_batch(B, q_pos, "q_pos");
+    if (rc) return rc;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(w) || !aligned16(scores) || !aligned16(idx) || !aligned16(ws))
+        return fail(LCA_EALIGN, "pointers must be 16-byte aligned");
+    int64_t max_vis = 0;
+    for (int b = 0; b < B; ++b) {
+        const int64_t vis = (q_pos[b] + 1) / m;
+        if (vis > k_cap || vis > s_stride)
+            return fail(LCA_ESHAPE, "sequence %d sees %lld entries: more than k_cap %lld or s_stride %lld", b,
+                        (long long)vis, (long long)k_cap, (long long)s_stride);
+        if (vis > max_vis) max_vis = vis;
+    }
+    const int G = lca::topk_split_chunks(B, max_vis, s_stride, LCA_BF16);
+    const size_t need = G ? lca_indexer_topk_workspace_size(B, s_stride, topk) : 0;
+    if (need > 0 && (!ws || ws_bytes < need))
+        return fail(LCA_EWORKSPACE, "indexer + top-k workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+    lca::IndexerArgs ia;
+    memset(&ia, 0, sizeof ia);
+    ia.q = q; ia.w = w; ia.k = k; ia.in_dtype = LCA_BF16; ia.k_cap = k_cap; ia.H_I = H_I; ia.d_I = d_I;
+    ia.B = B; ia.T = 1; ia.m = m; ia.scores = scores; ia.score_dtype = LCA_BF16; ia.s_stride = s_stride;
+    ia.q_pos = to_pos(q_pos, B);
+    ia.max_vis = max_vis;
+    lca::TopkArgs ta;
+    memset(&ta, 0, sizeof ta);
+    ta.scores = scores; ta.score_dtype = LCA_BF16; ta.s_stride = s_stride; ta.B = B; ta.T = 1; ta.m = m;
+    ta.k = topk; ta.idx = idx; ta.ws = ws; ta.max_n = max_vis; ta.q_pos = ia.q_pos;
+    if (G > 0) {  // fused: the indexer makes the top-k's first histograms
+        ia.th_h1 = (uint32_t*)ws;
+        ia.th_row = (int64_t)G * 512;
+        ta.th_cnt = (uint32_t*)((char*)ws + itk_counter_offset(B, s_stride));
+    }
+    hipError_t e = lca::launch_indexer(ia, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(lca::launch_topk(ta, (hipStream_t)stream));
+}
+
 // Bytes of one expanded (bf16) row, and the expansion's bound: at most max_keys compressed rows
 // plus a window ring of at most max_keys + T - 1 rows per sequence.
 static constexpr size_t kExpandRowBytes = (512 + 64) * sizeof(uint16_t);

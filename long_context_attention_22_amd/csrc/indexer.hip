@@ -23,6 +23,8 @@
 // Same grid, epilogue and causal skip as the bf16 path.
 //
 // f32 path: one thread per (token, key), f32 FMA (used for fp32 workloads).
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -39,6 +41,15 @@ __device__ __forceinline__ void store_score<float>(float* p, float v) {
 template <>
 __device__ __forceinline__ void store_score<uint16_t>(uint16_t* p, float v) {
     *p = f2bf(v == 0.0f ? 0.0f : v);
+}
+
+// High byte of the top-k's monotone key of a stored bf16 score (the bits store_score writes; -0 as +0):
+// positive scores map to 0x80.. and up, negative ones below.
+__device__ __forceinline__ uint32_t score_key_high(float v) {
+    uint32_t h = f2bf(v == 0.0f ? 0.0f : v);
+    if (h == 0x8000u) h = 0u;
+    const uint32_t key = (h & 0x8000u) ? (~h & 0xffffu) : (h | 0x8000u);
+    return key >> 8;
 }
 
 // (visible count (t + 1) / m: a shift when m is a power of two)
@@ -69,13 +80,24 @@ __global__ void __launch_bounds__(256) indexer_mfma(IndexerArgs a, int64_t keys_
     const int64_t p0 = a.q_pos.v[b], k_cap = a.k_cap, s_stride = a.s_stride;
     const void *pq = a.q, *pk = a.k, *psc = a.scores;
     const float* pw = a.w;
-    asm volatile("" ::"s"(T), "s"(m), "s"(p0), "s"(k_cap), "s"(s_stride), "s"(pq), "s"(pk), "s"(psc), "s"(pw));
+    uint32_t* th_h1 = a.th_h1;
+    const int64_t th_row = a.th_row;
+    asm volatile("" ::"s"(T), "s"(m), "s"(p0), "s"(k_cap), "s"(s_stride), "s"(pq), "s"(pk), "s"(psc), "s"(pw),
+                 "s"(th_h1), "s"(th_row));
     const int ntok = min(TOK, T - i0);
     const int64_t pos0 = p0 + i0;
     const int64_t vis_last = min(vis_of(pos0 + ntok, m), k_cap);
     const int64_t key_lo = (int64_t)blockIdx.x * keys_per_wg;
     const int64_t key_hi = min(key_lo + keys_per_wg, vis_last);
     if (key_lo >= key_hi) return;
+    // fused top-k pass: high-byte histogram of this workgroup's stored scores (wave-uniform flag)
+    constexpr bool kCanHist = TOK == 1 && std::is_same<TS, uint16_t>::value;
+    __shared__ uint32_t th_hist[kCanHist ? 256 : 1];
+    const bool hist = kCanHist && th_h1 != nullptr;
+    if (hist) {
+        th_hist[threadIdx.x] = 0u;
+        __syncthreads();
+    }
 
     const int hrow = lane & 15, kgrp = lane >> 4;
     bf16x8 qa[TOK][4];
@@ -134,7 +156,10 @@ __global__ void __launch_bounds__(256) indexer_mfma(IndexerArgs a, int64_t keys_
             // the four head quartets of each key: lane l gets key 16 (l >> 4) + (l & 15) = l
             const float mine = sum4g_scatter(part[0], part[1], part[2], part[3]);
             if (TOK == 1) {
-                if (mykey < vis_tk[tk]) store_score<TS>(sbase + (int64_t)tk * a.s_stride + mykey, mine);
+                if (mykey < vis_tk[tk]) {
+                    store_score<TS>(sbase + (int64_t)tk * a.s_stride + mykey, mine);
+                    if (hist) atomicAdd(&th_hist[score_key_high(mine)], 1u);
+                }
             }
             mine_all[tk] = mine;
         }
@@ -148,6 +173,11 @@ __global__ void __launch_bounds__(256) indexer_mfma(IndexerArgs a, int64_t keys_
                     if (tk < ntok) store_score<TS>(sbase + (int64_t)tk * a.s_stride + mykey, mine_all[tk]);
             }
         }
+    }
+    if (hist) {  // into the histogram of the 16384-key chunk holding this workgroup's keys
+        __syncthreads();
+        const uint32_t c = th_hist[threadIdx.x];
+        if (c) atomicAdd(th_h1 + b * th_row + (key_lo >> 14) * 256 + threadIdx.x, c);
     }
 }
 
@@ -328,6 +358,11 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t st) {
     // MXFP4 keys are 68 bytes: a single-token launch gives each workgroup twice the keys
     if (fp4 && tok == 1) kpw *= 2;
     if (kpw < 256) kpw = 256;
+    if (a.th_h1) {  // a workgroup's keys must lie in one 16384-key chunk of the top-k
+        int64_t p = 256;
+        while (p < kpw && p < 16384) p <<= 1;
+        kpw = p;
+    }
     const int64_t nsplit = (a.max_vis + kpw - 1) / kpw;
     dim3 grid((unsigned)nsplit, (unsigned)groups, (unsigned)a.B);
     if (fp4) {

@@ -55,6 +55,11 @@ struct IndexerArgs {
     int64_t s_stride;
     Pos q_pos;
     int64_t max_vis;
+    // Fused first pass of the split top-k (single-token rows, bf16 scores, bf16 keys): the high-byte
+    // histograms of each row's 16384-key chunks, added with device atomics into th_h1 (row r at
+    // th_h1 + r * th_row, chunk g at + 256 g; zero on entry).  NULL = off.
+    uint32_t* th_h1;
+    int64_t th_row;
 };
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t st);
 
@@ -67,8 +72,14 @@ struct TopkArgs {
     void* ws;
     int64_t max_n;   // largest candidate count over the rows
     Pos q_pos;
+    // The split schedule's high-byte histograms were made by the indexer (IndexerArgs::th_h1): only
+    // the last two launches run, and the last workgroup of each row (arrivals counted in th_cnt[row],
+    // zero on entry) clears the row's histograms and its counter for the next call.  NULL = off.
+    uint32_t* th_cnt;
 };
 size_t topk_ws_bytes(int32_t B, int32_t T, int64_t s_stride, int32_t score_dtype);
+// chunks per row of the split schedule for these rows, 0 when the rows take the row schedule
+int topk_split_chunks(int32_t rows, int64_t max_n, int64_t s_stride, int32_t score_dtype);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 
 struct AttnArgs {

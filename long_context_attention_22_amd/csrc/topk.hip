@@ -376,12 +376,30 @@ __global__ void __launch_bounds__(kSplitThreads) topk_split_h2(TopkArgs a, int G
     if (tid < 256) r.h2[g * 256 + tid] = hs[tid];
 }
 
+// Fused schedule (a.th_cnt): this workgroup has read the row's histograms for the last time; the
+// last of the row's G workgroups to get here clears both (and the arrival counter), so the next
+// call's indexer adds into zeros and the workspace is left as it came.  Every workgroup of the row
+// comes here exactly once.
+__device__ __forceinline__ void th_arrive(const TopkArgs& a, const SplitRow& r, int G, uint32_t* last) {
+    if (!a.th_cnt) return;
+    const int64_t rowid = (int64_t)blockIdx.z * gridDim.y + blockIdx.y;
+    __syncthreads();  // (every histogram value this workgroup loaded has been used)
+    if (threadIdx.x == 0) *last = atomicAdd(&a.th_cnt[rowid], 1u) == (uint32_t)G - 1u;
+    __syncthreads();
+    if (*last) {
+        for (int j = threadIdx.x; j < G * 512; j += kSplitThreads) r.h1[j] = 0u;  // h1, then h2
+        if (threadIdx.x == 0) a.th_cnt[rowid] = 0u;
+    }
+}
+
 __global__ void __launch_bounds__(kSplitThreads) topk_split_emit(TopkArgs a, int G) {
     const SplitRow r = split_row(a, G);
     const int g = blockIdx.x, tid = threadIdx.x;
     const int64_t lo = (int64_t)g * kChunk, hi = min(lo + kChunk, r.n);
     const int kk = a.k;
+    __shared__ uint32_t th_last;
     if (r.n <= r.K) {  // fewer candidates than k: all of them, in order
+        th_arrive(a, r, G, &th_last);
         for (int64_t j = lo + tid; j < lo + kChunk && j < kk; j += kSplitThreads)
             r.out[j] = j < r.n ? (int32_t)j : -1;
         if (g == G - 1)
@@ -403,6 +421,7 @@ __global__ void __launch_bounds__(kSplitThreads) topk_split_emit(TopkArgs a, int
         tot2[tid] = t2;
     }
     __syncthreads();
+    th_arrive(a, r, G, &th_last);
     if (tid < 64) pick_digit(tot1, (uint32_t)r.K, &d1, &rem1);
     __syncthreads();
     if (tid < 64) pick_digit(tot2, rem1, &d2, &rem2);
@@ -473,12 +492,20 @@ size_t topk_ws_bytes(int32_t B, int32_t T, int64_t s_stride, int32_t score_dtype
     return (size_t)B * T * split_chunks(s_stride) * 512 * sizeof(uint32_t);
 }
 
+int topk_split_chunks(int32_t rows, int64_t max_n, int64_t s_stride, int32_t score_dtype) {
+    TopkArgs a;
+    a.B = rows;
+    a.T = 1;
+    a.score_dtype = score_dtype;
+    return use_split(a, max_n) ? split_chunks(s_stride) : 0;
+}
+
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
     if (use_split(a, a.max_n)) {
         const int G = split_chunks(a.s_stride);
         dim3 grid((unsigned)G, (unsigned)a.T, (unsigned)a.B);
-        hipLaunchKernelGGL(topk_split_h1, grid, dim3(kSplitThreads), 0, st, a, G);
+        if (!a.th_cnt) hipLaunchKernelGGL(topk_split_h1, grid, dim3(kSplitThreads), 0, st, a, G);
         hipLaunchKernelGGL(topk_split_h2, grid, dim3(kSplitThreads), 0, st, a, G);
         hipLaunchKernelGGL(topk_split_emit, grid, dim3(kSplitThreads), 0, st, a, G);
         return hipGetLastError();

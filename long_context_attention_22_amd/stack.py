@@ -12,6 +12,8 @@ at positions t0 .. t0+T-1 of every sequence, Layer.step() issues:
     indexer keys      kv_compress(m, overlap, d_I)      (CSA; bf16 or MXFP4 keys)
     scores            indexer_score / _mxfp4            (CSA)
     selection         topk_select                       (CSA)
+                      (decode rows with bf16 keys: one indexer_topk call, the top-k's first
+                      histogram pass fused into the indexer)
     attention         csa_attn / hca_attn
 
 Decode is T = 1; chunked prefill is T > 1.  Nothing here computes: every step
@@ -28,7 +30,8 @@ from dataclasses import dataclass
 import torch
 
 from . import (BF16, FP8, MXFP4, KV, attn_workspace_size, csa_attn, csa_attn_append, hca_attn, hca_attn_append,
-               indexer_score, indexer_score_mxfp4, kv_compress, topk_select, topk_workspace_size)
+               indexer_score, indexer_score_mxfp4, indexer_topk, indexer_topk_workspace_size, kv_compress,
+               topk_select, topk_workspace_size)
 
 
 @dataclass
@@ -113,9 +116,14 @@ class Layer:
             self.idx = torch.zeros(B, t_max, spec.k, dtype=torch.int32, device=device)
             tws = max(topk_workspace_size(B, T, comp_cap, spec.k) for T in range(1, min(t_max, 128) + 1))
             self.topk_ws = torch.zeros(max(16, tws), dtype=torch.uint8, device=device)
+            # decode rows with bf16 keys and scores: indexer_topk (its own workspace, zeroed once)
+            self.itk_ws = torch.zeros(max(16, indexer_topk_workspace_size(B, comp_cap, spec.k)), dtype=torch.uint8,
+                                      device=device)
+            self.fuse_topk = True
             max_keys = spec.k + spec.n_win
         else:
-            self.scores = self.idx = self.topk_ws = None
+            self.scores = self.idx = self.topk_ws = self.itk_ws = None
+            self.fuse_topk = False
             max_keys = comp_cap + spec.n_win
         # split partials are needed only for short launches (few query rows); size for the largest
         ws = max(attn_workspace_size(B, T, spec.H, spec.c, max_keys) for T in range(1, min(t_max, 128) + 1))
@@ -151,11 +159,15 @@ class Layer:
         if s.kind == "csa":
             sc = self.scores[:, :T]
             ix = self.idx[:, :T]
-            if self.keys.fmt == MXFP4:
-                run("indexer_score", lambda: indexer_score_mxfp4(q_idx, w, self.keys, sc, q_pos=t0, m=s.m))
+            if T == 1 and self.fuse_topk and self.keys.fmt == BF16 and s.score_fmt == BF16:
+                run("indexer_topk", lambda: indexer_topk(q_idx, w, self.keys.nope, sc, ix, q_pos=t0, m=s.m,
+                                                         ws=self.itk_ws))
             else:
-                run("indexer_score", lambda: indexer_score(q_idx, w, self.keys.nope, sc, q_pos=t0, m=s.m))
-            run("topk_select", lambda: topk_select(sc, ix, q_pos=t0, m=s.m, ws=self.topk_ws))
+                if self.keys.fmt == MXFP4:
+                    run("indexer_score", lambda: indexer_score_mxfp4(q_idx, w, self.keys, sc, q_pos=t0, m=s.m))
+                else:
+                    run("indexer_score", lambda: indexer_score(q_idx, w, self.keys.nope, sc, q_pos=t0, m=s.m))
+                run("topk_select", lambda: topk_select(sc, ix, q_pos=t0, m=s.m, ws=self.topk_ws))
             kw = dict(q_pos=t0, comp=self.comp, m=s.m, idx=ix, win=self.win, n_win=s.n_win, sink=p.sink,
                       sm_scale=s.sm_scale, rope_theta=s.rope_theta, lse=lse, ws=self.ws, **app)
             if x_win is None:

@@ -270,3 +270,32 @@ def test_cache_validation(L):
     assert b"lcm" in L.lca_last_error()
     assert create([(4, 9, 0, 0)]) == lca.ESHAPE        # state plane of 36 bytes per slot
     assert Lc.lca_cache_destroy(None) == lca.OK
+
+
+def test_indexer_topk_validation(L):
+    """lca_indexer_topk rejects bad arguments before launching (the two calls' rules plus its workspace)."""
+    L.lca_indexer_topk.restype = C.c_int
+    vp = C.c_void_p
+
+    def call(**kw):
+        a = dict(q=FAKE, w=None, k=FAKE2, k_cap=300000, H_I=16, d_I=128, B=1, q_pos=pos(1 << 20), m=4,
+                 scores=FAKE, s_stride=300000, topk=2048, idx=FAKE2, ws=FAKE, ws_bytes=1 << 20)
+        a.update(kw)
+        return L.lca_indexer_topk(vp(a["q"]), vp(a["w"]) if a["w"] else None, vp(a["k"]), C.c_int64(a["k_cap"]),
+                                  C.c_int32(a["H_I"]), C.c_int32(a["d_I"]), C.c_int32(a["B"]), a["q_pos"],
+                                  C.c_int32(a["m"]), vp(a["scores"]), C.c_int64(a["s_stride"]), C.c_int32(a["topk"]),
+                                  vp(a["idx"]), vp(a["ws"]) if a["ws"] else None, C.c_size_t(a["ws_bytes"]), None)
+
+    assert call(q=0) == lca.EINVAL
+    assert call(idx=0) == lca.EINVAL
+    assert call(m=0) == lca.EINVAL
+    assert call(topk=0) == lca.EINVAL
+    assert call(H_I=8) == lca.ESHAPE
+    assert call(B=0, q_pos=pos(0)) == lca.ESHAPE
+    assert call(k_cap=1000) == lca.ESHAPE            # 262,144 visible entries do not fit
+    assert call(idx=FAKE2 + 4) == lca.EALIGN
+    need = L.lca_indexer_topk_workspace_size(1, 300000, 2048)
+    assert need > 0
+    assert call(ws=0, ws_bytes=0) == lca.EWORKSPACE
+    assert call(ws_bytes=need - 1) == lca.EWORKSPACE
+    assert L.lca_indexer_topk_workspace_size(1, 10000, 2048) == 0   # short rows: the row schedule
