@@ -200,6 +200,15 @@ int lca_indexer_topk(const void* q, const float* w, const void* k, int64_t k_cap
 size_t lca_indexer_topk_workspace_size(int32_t B, int64_t s_stride, int32_t k);
 
 /*
+ * lca_indexer_topk_mxfp4 -- the same fused call with the QK path in MXFP4 ([R] 5.2.1): the scores
+ * of lca_indexer_score_mxfp4 (k: MXFP4 key rows, k.cap rows per sequence) and the selection of
+ * lca_topk_select on them, with the same workspace (lca_indexer_topk_workspace_size) and rules.
+ */
+int lca_indexer_topk_mxfp4(const void* q, const float* w, lca_kv k, int32_t H_I, int32_t d_I, int32_t B,
+                           const int64_t* q_pos, int32_t m, void* scores, int64_t s_stride, int32_t topk,
+                           int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * lca_csa_attn -- CSA core attention, [R] 2.3.1 (shared-KV MQA: each stored
  * row is both key and value, one KV head for all H query heads) and 2.3.3
  * (sliding-window branch, attention sink, output RoPE).  For query row

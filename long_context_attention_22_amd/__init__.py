@@ -5,7 +5,8 @@ kernels.  torch supplies device memory and the current stream.  There is no
 fallback: when the built library is missing every call raises.
 
 Calls (same names as the C ABI):
-    kv_compress, indexer_score, indexer_score_mxfp4, topk_select, indexer_topk, csa_attn, hca_attn,
+    kv_compress, indexer_score, indexer_score_mxfp4, topk_select, indexer_topk, indexer_topk_mxfp4,
+    csa_attn, hca_attn,
     csa_attn_append, hca_attn_append, linear, grouped_out_proj
 and helpers KV (the lca_kv storage planes), attn_workspace_size.  The paged cache
 (include/lca_cache.h) is bound in the cache module (PagedCache).
@@ -69,13 +70,14 @@ def lib():
         L.lca_linear.argtypes = [vp, i64, i64, vp, i64, i64, vp, i32, i64, i64, i32, i32, i32, i32, vp]
         L.lca_grouped_out_proj.argtypes = [vp, i32, i32, i32, i32, vp, i32, vp, i32, vp, vp, i32, vp]
         L.lca_indexer_topk.argtypes = [vp, vp, vp, i64, i32, i32, i32, vp, i32, vp, i64, i32, vp, vp, sz, vp]
+        L.lca_indexer_topk_mxfp4.argtypes = [vp, vp, _KV, i32, i32, i32, vp, i32, vp, i64, i32, vp, vp, sz, vp]
         L.lca_indexer_topk_workspace_size.argtypes = [i32, i64, i32]
         L.lca_indexer_topk_workspace_size.restype = sz
         L.lca_attn_workspace_size.argtypes = [i32, i32, i32, i32, i64]
         L.lca_attn_workspace_size.restype = sz
         for name in ("lca_kv_compress", "lca_indexer_score", "lca_indexer_score_mxfp4", "lca_topk_select",
                      "lca_csa_attn", "lca_hca_attn", "lca_csa_attn_append", "lca_hca_attn_append", "lca_linear",
-                     "lca_grouped_out_proj", "lca_indexer_topk"):
+                     "lca_grouped_out_proj", "lca_indexer_topk", "lca_indexer_topk_mxfp4"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -207,6 +209,15 @@ def indexer_topk(q, w, k, scores, idx, *, q_pos, m: int, ws=None, stream=None):
     _check(lib().lca_indexer_topk(_ptr(q), _ptr(w), _ptr(k), int(k.shape[1]), int(q.shape[2]), int(q.shape[3]),
                                   int(B), _pos(q_pos, B), int(m), _ptr(scores), int(scores.shape[2]),
                                   int(idx.shape[2]), _ptr(idx), _ptr(ws), nbytes, _stream(stream)))
+
+
+def indexer_topk_mxfp4(q, w, k: KV, scores, idx, *, q_pos, m: int, ws=None, stream=None):
+    """indexer_topk with MXFP4 keys (k: KV with fmt MXFP4; q bf16, quantised in the call)."""
+    B = q.shape[0]
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().lca_indexer_topk_mxfp4(_ptr(q), _ptr(w), k.c(), int(q.shape[2]), int(q.shape[3]), int(B),
+                                        _pos(q_pos, B), int(m), _ptr(scores), int(scores.shape[2]), int(idx.shape[2]),
+                                        _ptr(idx), _ptr(ws), nbytes, _stream(stream)))
 
 
 def indexer_topk_workspace_size(B: int, s_stride: int, k: int) -> int:

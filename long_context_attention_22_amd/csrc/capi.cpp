@@ -253,6 +253,9 @@ static size_t itk_counter_offset(int32_t B, int64_t s_stride) {
     return (lca::topk_ws_bytes(B, 1, s_stride, LCA_BF16) + 15) / 16 * 16;
 }
 
+static int indexer_topk_launch(lca::IndexerArgs ia, int32_t topk, int32_t* idx, void* ws, size_t ws_bytes,
+                               void* stream);
+
 size_t lca_indexer_topk_workspace_size(int32_t B, int64_t s_stride, int32_t k) {
     if (B < 1 || s_stride < 1 || k < 1) return 0;
     if (lca::topk_split_chunks(B, s_stride, s_stride, LCA_BF16) == 0) return 0;
@@ -281,16 +284,26 @@ int lca_indexer_topk(const void* q, const float* w, const void* k, int64_t k_cap
                         (long long)vis, (long long)k_cap, (long long)s_stride);
         if (vis > max_vis) max_vis = vis;
     }
-    const int G = lca::topk_split_chunks(B, max_vis, s_stride, LCA_BF16);
-    const size_t need = G ? lca_indexer_topk_workspace_size(B, s_stride, topk) : 0;
-    if (need > 0 && (!ws || ws_bytes < need))
-        return fail(LCA_EWORKSPACE, "indexer + top-k workspace of %zu bytes needed (got %zu)", need, ws_bytes);
     lca::IndexerArgs ia;
     memset(&ia, 0, sizeof ia);
     ia.q = q; ia.w = w; ia.k = k; ia.in_dtype = LCA_BF16; ia.k_cap = k_cap; ia.H_I = H_I; ia.d_I = d_I;
     ia.B = B; ia.T = 1; ia.m = m; ia.scores = scores; ia.score_dtype = LCA_BF16; ia.s_stride = s_stride;
     ia.q_pos = to_pos(q_pos, B);
     ia.max_vis = max_vis;
+    return indexer_topk_launch(ia, topk, idx, ws, ws_bytes, stream);
+}
+
+// the shared part of lca_indexer_topk(_mxfp4): the workspace check and the two launches
+static int indexer_topk_launch(lca::IndexerArgs ia, int32_t topk, int32_t* idx, void* ws, size_t ws_bytes,
+                               void* stream) {
+    const int32_t B = ia.B;
+    const int64_t s_stride = ia.s_stride, max_vis = ia.max_vis;
+    const int G = lca::topk_split_chunks(B, max_vis, s_stride, LCA_BF16);
+    const size_t need = G ? lca_indexer_topk_workspace_size(B, s_stride, topk) : 0;
+    if (need > 0 && (!ws || ws_bytes < need))
+        return fail(LCA_EWORKSPACE, "indexer + top-k workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+    void* scores = ia.scores;
+    const int32_t m = ia.m;
     lca::TopkArgs ta;
     memset(&ta, 0, sizeof ta);
     ta.scores = scores; ta.score_dtype = LCA_BF16; ta.s_stride = s_stride; ta.B = B; ta.T = 1; ta.m = m;
@@ -303,6 +316,39 @@ int lca_indexer_topk(const void* q, const float* w, const void* k, int64_t k_cap
     hipError_t e = lca::launch_indexer(ia, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e);
     return hip_status(lca::launch_topk(ta, (hipStream_t)stream));
+}
+
+int lca_indexer_topk_mxfp4(const void* q, const float* w, lca_kv k, int32_t H_I, int32_t d_I, int32_t B,
+                           const int64_t* q_pos, int32_t m, void* scores, int64_t s_stride, int32_t topk,
+                           int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    if (!q || !scores || !idx) return fail(LCA_EINVAL, "q, scores and idx must be non-NULL");
+    if (m < 1) return fail(LCA_EINVAL, "m must be >= 1");
+    if (topk < 1) return fail(LCA_EINVAL, "k must be >= 1");
+    if (k.fmt != LCA_MXFP4) return fail(LCA_EDTYPE, "keys must be stored MXFP4 (fmt %d)", LCA_MXFP4);
+    int rc = check_kv(k, "k", true, true);
+    if (rc) return rc;
+    if (H_I != 16 || d_I != 128 || k.d_nope != d_I)
+        return fail(LCA_ESHAPE, "MXFP4 indexer supports H_I = 16, d_I = k.d_nope = 128 (got %d x %d, keys %d)", H_I,
+                    d_I, k.d_nope);
+    if (s_stride < 1) return fail(LCA_ESHAPE, "bad s_stride");
+    if ((rc = check_batch(B, q_pos, "q_pos"))) return rc;
+    if (!aligned16(q) || !aligned16(w) || !aligned16(scores) || !aligned16(idx) || !aligned16(ws))
+        return fail(LCA_EALIGN, "pointers must be 16-byte aligned");
+    int64_t max_vis = 0;
+    for (int b = 0; b < B; ++b) {
+        const int64_t vis = (q_pos[b] + 1) / m;
+        if (vis > k.cap || vis > s_stride)
+            return fail(LCA_ESHAPE, "sequence %d sees %lld entries: more than k.cap %lld or s_stride %lld", b,
+                        (long long)vis, (long long)k.cap, (long long)s_stride);
+        if (vis > max_vis) max_vis = vis;
+    }
+    lca::IndexerArgs ia;
+    memset(&ia, 0, sizeof ia);
+    ia.q = q; ia.w = w; ia.k = k.nope; ia.k_scale = k.scale; ia.in_dtype = LCA_MXFP4; ia.k_cap = k.cap;
+    ia.H_I = H_I; ia.d_I = d_I; ia.B = B; ia.T = 1; ia.m = m; ia.scores = scores; ia.score_dtype = LCA_BF16;
+    ia.s_stride = s_stride; ia.q_pos = to_pos(q_pos, B); ia.max_vis = max_vis;
+    return indexer_topk_launch(ia, topk, idx, ws, ws_bytes, stream);
 }
 
 // Bytes of one expanded (bf16) row, and the expansion's bound: at most max_keys compressed rows

@@ -197,14 +197,24 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
     const int64_t p0 = a.q_pos.v[b], k_cap = a.k_cap, s_stride = a.s_stride;
     const void *pq = a.q, *pk = a.k, *pks = a.k_scale, *psc = a.scores;
     const float* pw = a.w;
+    uint32_t* th_h1 = a.th_h1;
+    const int64_t th_row = a.th_row;
     asm volatile("" ::"s"(T), "s"(m), "s"(p0), "s"(k_cap), "s"(s_stride), "s"(pq), "s"(pk), "s"(pks), "s"(psc),
-                 "s"(pw));
+                 "s"(pw), "s"(th_h1), "s"(th_row));
     const int ntok = min(TOK, T - i0);
     const int64_t pos0 = p0 + i0;
     const int64_t vis_last = min(vis_of(pos0 + ntok, m), k_cap);
     const int64_t key_lo = (int64_t)blockIdx.x * keys_per_wg;
     const int64_t key_hi = min(key_lo + keys_per_wg, vis_last);
     if (key_lo >= key_hi) return;
+    // fused top-k pass (as in indexer_mfma)
+    constexpr bool kCanHist = TOK == 1 && std::is_same<TS, uint16_t>::value;
+    __shared__ uint32_t th_hist[kCanHist ? 256 : 1];
+    const bool hist = kCanHist && th_h1 != nullptr;
+    if (hist) {
+        th_hist[threadIdx.x] = 0u;
+        __syncthreads();
+    }
 
     const int hrow = lane & 15, kgrp = lane >> 4;
     // this lane's head and 32-element block of each token's q (bf16), and the head weights.  All
@@ -298,7 +308,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
             }
             const float mine = sum4g_scatter(part[0], part[1], part[2], part[3]);  // key c0 + lane
             if (TOK == 1) {
-                if (mykey < vis_tk[tk]) store_score<TS>(sbase + (int64_t)tk * s_stride + mykey, mine);
+                if (mykey < vis_tk[tk]) {
+                    store_score<TS>(sbase + (int64_t)tk * s_stride + mykey, mine);
+                    if (hist) atomicAdd(&th_hist[score_key_high(mine)], 1u);
+                }
             }
             mine_all[tk] = mine;
         }
@@ -317,6 +330,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
             kc[bl] = *(const u32x4*)(kbase + key * (kIdxD / 2) + 16 * kgrp);
             ks[bl] = ksbase[key];
         }
+    }
+    if (hist) {
+        __syncthreads();
+        const uint32_t c = th_hist[threadIdx.x];
+        if (c) atomicAdd(th_h1 + b * th_row + (key_lo >> 14) * 256 + threadIdx.x, c);
     }
 }
 

@@ -12,8 +12,8 @@ at positions t0 .. t0+T-1 of every sequence, Layer.step() issues:
     indexer keys      kv_compress(m, overlap, d_I)      (CSA; bf16 or MXFP4 keys)
     scores            indexer_score / _mxfp4            (CSA)
     selection         topk_select                       (CSA)
-                      (decode rows with bf16 keys: one indexer_topk call, the top-k's first
-                      histogram pass fused into the indexer)
+                      (decode rows: one indexer_topk / indexer_topk_mxfp4 call, the top-k's
+                      first histogram pass fused into the indexer)
     attention         csa_attn / hca_attn
 
 Decode is T = 1; chunked prefill is T > 1.  Nothing here computes: every step
@@ -30,7 +30,8 @@ from dataclasses import dataclass
 import torch
 
 from . import (BF16, FP8, MXFP4, KV, attn_workspace_size, csa_attn, csa_attn_append, hca_attn, hca_attn_append,
-               indexer_score, indexer_score_mxfp4, indexer_topk, indexer_topk_workspace_size, kv_compress,
+               indexer_score, indexer_score_mxfp4, indexer_topk, indexer_topk_mxfp4, indexer_topk_workspace_size,
+               kv_compress,
                topk_select, topk_workspace_size)
 
 
@@ -159,9 +160,13 @@ class Layer:
         if s.kind == "csa":
             sc = self.scores[:, :T]
             ix = self.idx[:, :T]
-            if T == 1 and self.fuse_topk and self.keys.fmt == BF16 and s.score_fmt == BF16:
-                run("indexer_topk", lambda: indexer_topk(q_idx, w, self.keys.nope, sc, ix, q_pos=t0, m=s.m,
-                                                         ws=self.itk_ws))
+            if T == 1 and self.fuse_topk and s.score_fmt == BF16 and self.keys.fmt in (BF16, MXFP4):
+                if self.keys.fmt == MXFP4:
+                    run("indexer_topk", lambda: indexer_topk_mxfp4(q_idx, w, self.keys, sc, ix, q_pos=t0, m=s.m,
+                                                                   ws=self.itk_ws))
+                else:
+                    run("indexer_topk", lambda: indexer_topk(q_idx, w, self.keys.nope, sc, ix, q_pos=t0, m=s.m,
+                                                             ws=self.itk_ws))
             else:
                 if self.keys.fmt == MXFP4:
                     run("indexer_score", lambda: indexer_score_mxfp4(q_idx, w, self.keys, sc, q_pos=t0, m=s.m))

@@ -98,3 +98,36 @@ def test_indexer_topk_graph_replays():
         _separate(q, w, k, [pos[rep]], m, s_stride, topk)  # eager work between replays
         torch.cuda.synchronize()
     assert int(ws.count_nonzero()) == 0
+
+
+def _mxfp4_keys(seed, B, cap):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    kv = lca.KV.empty(lca.MXFP4, B, cap, 128, 0)
+    kv.nope.copy_(torch.randint(0, 256, kv.nope.shape, dtype=torch.uint8, device="cuda", generator=g))
+    kv.scale.copy_(torch.randint(118, 128, kv.scale.shape, dtype=torch.uint8, device="cuda", generator=g))
+    return kv
+
+
+@pytest.mark.parametrize("B,cap,topk,pos_list", [
+    (1, 262160, 2048, [[(1 << 20) + 3], [(1 << 20) + 7]]),
+    (32, 32800, 1024, [[131071 + 4 * b for b in range(32)]]),
+])
+def test_indexer_topk_mxfp4_matches_separate_calls(B, cap, topk, pos_list):
+    m, s_stride = 4, cap
+    ws = torch.zeros(lca.indexer_topk_workspace_size(B, s_stride, topk), dtype=torch.uint8, device="cuda")
+    k = _mxfp4_keys(5, B, cap)
+    tws = torch.zeros(max(16, lca.topk_workspace_size(B, 1, s_stride, topk)), dtype=torch.uint8, device="cuda")
+    for call, q_pos in enumerate(pos_list):
+        q, w, _ = _inputs(200 + call, B, 16)
+        sc = torch.zeros(B, 1, s_stride, dtype=torch.bfloat16, device="cuda")
+        ix = torch.empty(B, 1, topk, dtype=torch.int32, device="cuda")
+        lca.indexer_topk_mxfp4(q, w, k, sc, ix, q_pos=q_pos, m=m, ws=ws)
+        sc_ref = torch.zeros_like(sc)
+        ix_ref = torch.empty_like(ix)
+        lca.indexer_score_mxfp4(q, w, k, sc_ref, q_pos=q_pos, m=m)
+        lca.topk_select(sc_ref, ix_ref, q_pos=q_pos, m=m, ws=tws)
+        torch.cuda.synchronize()
+        for b, (a, r) in enumerate(zip(_vis_cols(sc, q_pos, m), _vis_cols(sc_ref, q_pos, m))):
+            assert np.array_equal(a, r), (call, b)
+        assert torch.equal(ix, ix_ref), call
+    assert int(ws.count_nonzero()) == 0
