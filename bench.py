@@ -18,7 +18,8 @@ f32 scores; the same stack's 4096-token chunked prefill at 1M context (with
 the chunk's MXFP4 indexer call timed beside the bf16 one); and CSA decode for
 32 sequences at 131,072 tokens; and the linear maps around one attention
 layer (projections and the grouped output projection) for a 4096-token chunk
-and for one decode token; the 1M decode again with every cache in the paged
+and for one decode token; a whole single-layer prefill from position 0 (CSA at 8,192 tokens,
+HCA at 65,536, bf16 storage); the 1M decode again with every cache in the paged
 cache (one slot per replica, 64 KiB and 2 MiB pages) and the cost of forking
 the 1M-token sequence (prefix reuse).  "roofline"
 covers the dominant decode kernel (indexer_score, HBM-bound), timed with HIP
@@ -532,7 +533,7 @@ def attn_flops(T: int, t0: int, m: int, H: int, n_win: int, k: int | None) -> fl
     tot = 0
     for i in range(T):
         t = t0 + i
-        keys = (k if k is not None else (t + 1) // m) + min(n_win, t + 1)
+        keys = (min(k, (t + 1) // m) if k is not None else (t + 1) // m) + min(n_win, t + 1)
         tot += keys
     return 4.0 * tot * H * C
 
@@ -614,6 +615,82 @@ def bench_prefill_1m(stack: Stack, reps: int = 20, T: int = 4096, seed: int = 10
                 indexer_mxfp4=dict(ms=kt["indexer_mxfp4"], tflops=idx_fl / (kt["indexer_mxfp4"] * 1e-3) / 1e12,
                                    frac=idx_fl / (kt["indexer_mxfp4"] * 1e-3) / 1e12 / FP4_PEAK_TFLOPS),
                 csa_attn=dict(flops=csa_fl, tflops=csa_fl / (kt["csa_attn"] * 1e-3) / 1e12))
+
+
+def bench_prefill_single(kind: str, T: int, reps: int = 10, seed: int = 0):
+    """A whole single-layer prefill from position 0 with bf16 storage: CSA at 8,192 tokens (window store,
+    compressor, indexer keys, indexer, top-512, attention) or HCA at 65,536 tokens (window store,
+    compressor, attention).  Inputs drawn on the GPU (N(0,1), 1 % of channels x20 in the compressor
+    streams; w N(0,1)/4); median of reps, each after a cache-evicting write."""
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    H, m = 64, (4 if kind == "csa" else 128)
+    k, n_win = 512, 128
+    out_ch = torch.randperm(C, generator=g, device="cuda")[: C // 100]
+
+    def acts(c, oc=None):
+        x = torch.randn(1, T, c, device="cuda", generator=g)
+        if oc is not None:
+            x[..., oc] *= 20.0
+        return x.to(torch.bfloat16)
+
+    ca, za, cb, zb = (acts(C, out_ch) for _ in range(4))
+    ba = torch.randn(m, C, device="cuda", generator=g) * 0.5
+    bb = torch.randn(m, C, device="cuda", generator=g) * 0.5
+    gamma = 1.0 + 0.1 * torch.randn(C, device="cuda", generator=g)
+    sink = torch.randn(H, device="cuda", generator=g)
+    q = torch.randn(1, T, H, C, device="cuda", generator=g).to(torch.bfloat16)
+    out = torch.empty(1, T, H, C, dtype=torch.bfloat16, device="cuda")
+    ncap = T // m
+    win = lca.KV.empty(lca.BF16, 1, T, 512, 64)
+    comp = lca.KV.empty(lca.BF16, 1, ncap, 512, 64)
+    if kind == "csa":
+        ich = torch.randperm(128, generator=g, device="cuda")[:2]
+        ica, iza, icb, izb = (acts(128, ich) for _ in range(4))
+        iba = torch.randn(m, 128, device="cuda", generator=g) * 0.5
+        ibb = torch.randn(m, 128, device="cuda", generator=g) * 0.5
+        keys = lca.KV.empty(lca.BF16, 1, ncap, 128, 0)
+        qi = torch.randn(1, T, 16, 128, device="cuda", generator=g).to(torch.bfloat16)
+        w = torch.randn(1, T, 16, device="cuda", generator=g) * 0.25
+        sc = torch.empty(1, T, ncap, dtype=torch.bfloat16, device="cuda")
+        idx = torch.empty(1, T, k, dtype=torch.int32, device="cuda")
+        tws = torch.empty(max(16, lca.topk_workspace_size(1, T, ncap, k)), dtype=torch.uint8, device="cuda")
+    aws = torch.empty(max(16, lca.attn_workspace_size(1, T, H, C, (k if kind == "csa" else ncap) + n_win)),
+                      dtype=torch.uint8, device="cuda")
+
+    def run():
+        lca.kv_compress(ca, za, None, None, win, m=1, overlap=0, first_pos=0, gamma=gamma, rope_theta=1e4)
+        if kind == "csa":
+            lca.kv_compress(ca, za, cb, zb, comp, m=m, overlap=1, first_pos=0, bias_a=ba, bias_b=bb, gamma=gamma,
+                            rope_theta=1e4)
+            lca.kv_compress(ica, iza, icb, izb, keys, m=m, overlap=1, first_pos=0, bias_a=iba, bias_b=ibb)
+            lca.indexer_score(qi, w, keys.nope, sc, q_pos=0, m=m)
+            lca.topk_select(sc, idx, q_pos=0, m=m, ws=tws)
+            lca.csa_attn(q, out, q_pos=0, comp=comp, m=m, idx=idx, win=win, n_win=n_win, sink=sink,
+                         sm_scale=C ** -0.5, rope_theta=1e4, ws=aws)
+        else:
+            lca.kv_compress(ca, za, None, None, comp, m=m, overlap=0, first_pos=0, bias_a=ba, gamma=gamma,
+                            rope_theta=1e4)
+            lca.hca_attn(q, out, q_pos=0, comp=comp, m=m, win=win, n_win=n_win, sink=sink, sm_scale=C ** -0.5,
+                         rope_theta=1e4, ws=aws)
+
+    run()
+    torch.cuda.synchronize()
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    times = []
+    for r in range(reps):
+        flush.fill_(r & 255)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        run()
+        e.record()
+        torch.cuda.synchronize()
+        times.append(s.elapsed_time(e))
+    ms = float(np.median(times))
+    att = attn_flops(T, 0, m, H, n_win, k if kind == "csa" else None)
+    idx_fl = 2.0 * 16 * 128 * sum((i + 1) // m for i in range(T)) if kind == "csa" else 0.0
+    tf = (att + idx_fl) / (ms * 1e-3) / 1e12
+    return dict(tokens=T, ms=ms, tokens_per_s=T / (ms * 1e-3), attn_flops=att, indexer_flops=idx_fl, tflops=tf,
+                mfma_frac=tf / BF16_PEAK_TFLOPS, storage="bf16", top_k=k if kind == "csa" else None, reps=reps)
 
 
 def bench_decode_c4(W: int, K: int, seed: int = 1004):
@@ -817,6 +894,12 @@ def main():
             f"indexer {c4['mxfp4_indexer']['ms_per_step'] * 1e3:.1f} us/step, {c4['mxfp4_indexer']['tokens_per_s']:.0f} tok/s")
         extra["decode_csa_b32_128k"] = c4
         torch.cuda.empty_cache()
+        for kind, T in (("csa", 8192), ("hca", 65536)):
+            r = bench_prefill_single(kind, T)
+            log(f"{kind.upper()} prefill of {T} tokens: {r['ms']:.2f} ms, {r['tokens_per_s']:.0f} tok/s, "
+                f"{r['tflops']:.0f} TFLOP/s ({100 * r['mfma_frac']:.1f} % of the bf16 MFMA peak)")
+            extra[f"prefill_{kind}_{T}"] = r
+            torch.cuda.empty_cache()
         pj = bench_projections()
         log(f"layer projections: 4096-token chunk {pj['T4096']['total']['ms']:.2f} ms "
             f"({pj['T4096']['total']['tflops']:.0f} TFLOP/s), one decode token {pj['T1']['total']['ms'] * 1e3:.1f} us "
