@@ -141,6 +141,109 @@ __device__ __forceinline__ void pick_digit(const uint32_t* hsum, uint32_t rem, u
 // ---------------------------------------------------------------------------
 // row schedule
 // ---------------------------------------------------------------------------
+constexpr int kCand = 10240;  // keys sharing the chosen high byte that the two-pass tail takes
+constexpr int kDef = 4096;   // keys above it (at most K)
+
+// Two-pass end of a 16-bit row (the high byte d1 chosen, rem keys to take from its bucket): one
+// pass lists, in index order, the keys above bucket d1 (all selected) and the bucket's keys with
+// their low bytes in LDS; the low byte and the tie rule are resolved on that list, and the two
+// ascending lists are merged into the output by binary search.  Same result as the low-byte
+// histogram pass followed by the emission pass.
+template <typename TS>
+__device__ __forceinline__ void row_tail16(const TS* row, int64_t n, int32_t* out, uint32_t d1, uint32_t rem,
+                                        uint32_t K, uint32_t* hist, uint32_t* hsum, uint32_t* wsum,
+                                        uint32_t* sel_digit, uint32_t* sel_rem) {
+    __shared__ uint32_t cand[kCand];  // (index << 8) | low byte, ascending index
+    __shared__ int32_t defl[kDef];    // indices above bucket d1, ascending
+    __shared__ int32_t chosen[kDef];  // the bucket's selected indices, ascending
+    const int tid = threadIdx.x, lane = tid & 63;
+    uint32_t def_base = 0, cand_base = 0;
+    for (int64_t base = 0; base < n; base += 8 * kTopkThreads) {
+        const int64_t e0 = base + 8 * (int64_t)tid;
+        uint32_t keys[8];
+        uint32_t nd = 0, nc = 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const bool valid = e0 + u < n;
+            keys[u] = valid ? mono_key(row[e0 + u]) : 0u;
+            nd += (valid && (keys[u] >> 8) > d1) ? 1u : 0u;
+            nc += (valid && (keys[u] >> 8) == d1) ? 1u : 0u;
+        }
+        uint32_t tot;
+        const uint32_t packed = nd | (nc << 16);
+        const uint32_t excl = block_incl_scan<kTopkWaves>(packed, wsum, &tot) - packed;
+        uint32_t dp = def_base + (excl & 0xffffu), cp = cand_base + (excl >> 16);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (e0 + u >= n) break;
+            const uint32_t hb = keys[u] >> 8;
+            if (hb > d1) defl[dp++] = (int32_t)(e0 + u);
+            else if (hb == d1) cand[cp++] = ((uint32_t)(e0 + u) << 8) | (keys[u] & 255u);
+        }
+        def_base += tot & 0xffffu;
+        cand_base += tot >> 16;
+    }
+    const uint32_t D = def_base, C = cand_base;  // D = K - rem, C = the bucket's size
+    // low byte: histogram of the bucket
+    for (int j = tid; j < 256 * 16; j += kTopkThreads) hist[j] = 0;
+    __syncthreads();
+    for (uint32_t j = tid; j < C; j += kTopkThreads) atomicAdd(&hist[(cand[j] & 255u) * 16 + (lane & 15)], 1u);
+    __syncthreads();
+    if (tid < 256) {
+        uint32_t s = 0;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) s += hist[tid * 16 + ((c + tid) & 15)];
+        hsum[tid] = s;
+    }
+    __syncthreads();
+    if (tid < 64) pick_digit(hsum, rem, sel_digit, sel_rem);
+    __syncthreads();
+    const uint32_t d2 = *sel_digit, rem2 = *sel_rem;
+    // the bucket's selected keys: low byte above d2, and the first rem2 (in index order) equal to it
+    const uint32_t per = (C + kTopkThreads - 1) / kTopkThreads;
+    const uint32_t c0 = min(C, tid * per), c1 = min(C, c0 + per);
+    uint32_t neq = 0;
+    for (uint32_t j = c0; j < c1; ++j) neq += (cand[j] & 255u) == d2 ? 1u : 0u;
+    uint32_t tot;
+    uint32_t eq_before = block_incl_scan<kTopkWaves>(neq, wsum, &tot) - neq;
+    uint32_t nsel = 0;
+    for (uint32_t j = c0; j < c1; ++j) {
+        const uint32_t lo = cand[j] & 255u;
+        if (lo > d2) ++nsel;
+        else if (lo == d2 && eq_before++ < rem2) ++nsel;
+    }
+    uint32_t sel_pos = block_incl_scan<kTopkWaves>(nsel, wsum, &tot) - nsel;
+    eq_before = block_incl_scan<kTopkWaves>(neq, wsum, &tot) - neq;  // (restart this thread's count)
+    for (uint32_t j = c0; j < c1; ++j) {
+        const uint32_t lo = cand[j] & 255u;
+        const bool take = lo > d2 || (lo == d2 && eq_before++ < rem2);
+        if (take) chosen[sel_pos++] = (int32_t)(cand[j] >> 8);
+    }
+    __syncthreads();
+    // merge: each entry's place is its rank in its own list plus the entries of the other list below it
+    for (uint32_t j = tid; j < D; j += kTopkThreads) {
+        const int32_t v = defl[j];
+        uint32_t lo = 0, hi = rem;
+        while (lo < hi) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if (chosen[mid] < v) lo = mid + 1;
+            else hi = mid;
+        }
+        out[j + lo] = v;
+    }
+    for (uint32_t j = tid; j < rem; j += kTopkThreads) {
+        const int32_t v = chosen[j];
+        uint32_t lo = 0, hi = D;
+        while (lo < hi) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if (defl[mid] < v) lo = mid + 1;
+            else hi = mid;
+        }
+        out[j + lo] = v;
+    }
+    (void)K;
+}
+
 template <typename TS, int BITS>
 __global__ void __launch_bounds__(kTopkThreads) topk_row(TopkArgs a) {
     const int b = blockIdx.y, i = blockIdx.x;
@@ -186,6 +289,13 @@ __global__ void __launch_bounds__(kTopkThreads) topk_row(TopkArgs a) {
         __syncthreads();
         prefix |= sel_digit << shift;
         rem = sel_rem;
+        if constexpr (BITS == 16) {
+            // few keys share the chosen high byte: one more pass over the row instead of two
+            if (shift == 8 && hsum[sel_digit] <= kCand && K <= kDef && n < (int64_t)1 << 24) {
+                row_tail16<TS>(row, n, out, prefix >> 8, rem, (uint32_t)K, hist, hsum, wsum, &sel_digit, &sel_rem);
+                return;
+            }
+        }
         __syncthreads();
     }
     const uint32_t tau = prefix;
