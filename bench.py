@@ -852,6 +852,8 @@ def main():
     ap.add_argument("--mxfp4", action="store_true",
                     help="with --no-extra: still time the 1M decode with the MXFP4 indexer (no recall)")
     ap.add_argument("--paged", action="store_true", help="with --no-extra: still time the paged-cache decode")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="profiling mode: build the 1M stack, run its 4096-token chunk (3 reps), print nothing else")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB device copy (reference for rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -864,6 +866,11 @@ def main():
     K, W, R = args.steps, args.warmup, args.replicas
     if args.calibrate_copy:
         calibrate_copy()
+    if args.prefill_only:
+        base = Stack(STACK_SPECS, STACK_TAGS, 1, T0_1M, 4, 1, 1005, win_cap=8192, raw_span=4096)
+        pf = bench_prefill_1m(base, reps=3)
+        log(f"1M prefill chunk: {pf['ms']:.2f} ms ({pf['tokens_per_s']:.0f} tok/s)")
+        return
 
     d = bench_decode_1m(W, K, R)
     res, stacks = d
