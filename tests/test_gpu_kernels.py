@@ -505,3 +505,47 @@ def test_grouped_out_proj(T):
     out = torch.empty(T, d, dtype=torch.float32, device="cuda")
     lca.grouped_out_proj(dev(o), dev(wg), dev(wo), mid, out, g=g)
     assert np.all(np.abs(host(out).astype(np.float64) - ref) <= bound)
+
+
+@pytest.mark.parametrize("T", [4096, 1])
+def test_linear_full_size_sampled(T):
+    """The maps bench.py times, at their full shapes (d = 4096, 64 heads of 576, indexer 16 x 128, 8 groups of
+    1024), in the same launch configuration: sampled outputs against the oracle on the sampled rows and
+    columns (bf16 outputs within one bf16 step of the oracle's rounding or 1e-5 of the sum of |products|)."""
+    d, dq, H, c, dg, g = 4096, 1024, 64, 576, 1024, 8
+    maps = [(d, dq), (dq, H * c), (d, 4 * c), (d, 4 * 128), (dq, 16 * 128), (d, 16)]
+    gen = torch.Generator(device="cuda").manual_seed(77)
+    rng = np.random.default_rng(77)
+    for k, n in maps:
+        x = torch.randn(T, k, device="cuda", generator=gen).to(torch.bfloat16)
+        w = (torch.randn(n, k, device="cuda", generator=gen) * k ** -0.5).to(torch.bfloat16)
+        y = torch.empty(T, n, dtype=torch.bfloat16, device="cuda")
+        lca.linear(x, w, y)
+        torch.cuda.synchronize()
+        rows = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, 14)]))
+        cols = np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, 30)]))
+        xs, ws = host(x)[rows][None], host(w)[cols][None]
+        o = orc.linear(xs, ws, y_fmt=orc.BF16)[0]
+        gsel = host(y)[rows][:, cols]
+        bound = 1e-5 * (np.abs(S.from_bf16(xs[0])).astype(np.float64) @ np.abs(S.from_bf16(ws[0])).astype(np.float64).T)
+        ok = (bf16_ulps(gsel, o) <= 1) | (np.abs(S.from_bf16(gsel) - S.from_bf16(o)) <= bound)
+        assert ok.all(), (k, n, T)
+    # the grouped output projection: sampled tokens, every output column
+    o_in = torch.randn(T, H, c, device="cuda", generator=gen).to(torch.bfloat16)
+    wg = torch.stack([(torch.randn(dg, H // g * c, device="cuda", generator=gen) * (H // g * c) ** -0.5)
+                      .to(torch.bfloat16) for _ in range(g)])
+    wo = (torch.randn(d, g * dg, device="cuda", generator=gen) * (g * dg) ** -0.5).to(torch.bfloat16)
+    mid = torch.empty(T, g * dg, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty(T, d, dtype=torch.float32, device="cuda")
+    lca.grouped_out_proj(o_in, wg, wo, mid, out, g=g)
+    torch.cuda.synchronize()
+    toks = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, 6)]))
+    oh, wgh, woh = host(o_in)[toks], host(wg), host(wo)
+    ref = orc.grouped_out_proj(oh, wgh, woh, g=g, mid_fmt=orc.BF16, out_fmt=orc.F32)
+    # (the bound of test_grouped_out_proj: one bf16 step of every intermediate, weighted by |wo|)
+    nt = len(toks)
+    mid_exact = np.concatenate([orc.linear(np.ascontiguousarray(oh[:, j * (H // g):(j + 1) * (H // g)].reshape(nt, -1)),
+                                           wgh[j]) for j in range(g)], -1).astype(np.float64)
+    step = np.exp2(np.floor(np.log2(np.maximum(np.abs(mid_exact), 1e-30))) - 7)
+    bound = step @ np.abs(S.from_bf16(woh)).astype(np.float64).T + 1e-4 * np.abs(ref) + 1e-6
+    assert np.all(np.abs(host(out)[toks].astype(np.float64) - ref) <= bound), T
