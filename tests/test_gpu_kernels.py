@@ -549,3 +549,25 @@ def test_linear_full_size_sampled(T):
     step = np.exp2(np.floor(np.log2(np.maximum(np.abs(mid_exact), 1e-30))) - 7)
     bound = step @ np.abs(S.from_bf16(woh)).astype(np.float64).T + 1e-4 * np.abs(ref) + 1e-6
     assert np.all(np.abs(host(out)[toks].astype(np.float64) - ref) <= bound), T
+
+
+def test_indexer_mxfp4_full_size_sampled():
+    """The 1M decode launch of the MXFP4 indexer (262,147 visible keys, the configuration bench.py times):
+    f32 scores of 1,024 sampled keys (plus the first and last) against the oracle on those key rows."""
+    B, N, t = 1, 262160, (1 << 20) + 7
+    k = _mxfp4_keys(123, B, N)
+    q = S.to_bf16(S.normal(124, "q4full", (B, 1, 16, 128)))
+    w = S.normal(125, "w4full", (B, 1, 16), 0.25)
+    sc = torch.full((B, 1, N), 7.0, dtype=torch.float32, device="cuda")
+    lca.indexer_score_mxfp4(dev(q), dev(w), kv_dev(k), sc, q_pos=t, m=4)
+    torch.cuda.synchronize()
+    vis = (t + 1) // 4
+    cols = np.unique(np.concatenate([[0, vis - 1], S.stream(126, "cols").integers(0, vis, 1024)]))
+    sub = orc.KV(np.ascontiguousarray(k.nope[:, cols]), np.zeros((B, len(cols), 0), np.uint16),
+                 np.ascontiguousarray(k.scale[:, cols]), orc.MXFP4, 128, 0, len(cols))
+    # every sampled key visible to a query at position 4 * len(cols)
+    o = orc.indexer_score_mxfp4(q, w, sub, q_pos=[4 * len(cols)], m=4, score_fmt=orc.F32)
+    gv, ov = host(sc)[0, 0, cols].astype(np.float64), o[0, 0, :len(cols)].astype(np.float64)
+    tol = 1e-5 * np.abs(ov) + 1e-5 * np.abs(ov).max()
+    assert np.all(np.abs(gv - ov) <= tol)
+    assert np.all(host(sc)[0, 0, vis:] == 7.0)
