@@ -869,7 +869,8 @@ def main():
     if args.prefill_only:
         base = Stack(STACK_SPECS, STACK_TAGS, 1, T0_1M, 4, 1, 1005, win_cap=8192, raw_span=4096)
         pf = bench_prefill_1m(base, reps=3)
-        log(f"1M prefill chunk: {pf['ms']:.2f} ms ({pf['tokens_per_s']:.0f} tok/s)")
+        log(f"1M prefill chunk: {pf['ms']:.2f} ms ({pf['tokens_per_s']:.0f} tok/s); kernels (ms): "
+            + ", ".join(f"{k} {v:.3f}" for k, v in pf['kernel_ms'].items()))
         return
 
     d = bench_decode_1m(W, K, R)
