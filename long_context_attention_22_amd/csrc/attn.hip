@@ -582,9 +582,14 @@ __global__ void __launch_bounds__(512) attn_mfma(AttnArgs a, int64_t split_len, 
 constexpr int kCombGroups = 8, kCombQuarters = 4, kCombPer = kC / 4 / kCombQuarters;  // 36 threads x 4 dims
 constexpr int kCombThreads = kCombGroups * kCombPer;
 static int comb_groups(int nsplit) { return nsplit > 32 ? 8 : nsplit > 16 ? 4 : nsplit > 8 ? 2 : 1; }
-__global__ void __launch_bounds__(kCombThreads) attn_combine(AttnArgs a, int nsplit) {
-    const int ng = blockDim.x / kCombPer;  // blockDim.x = max(64, ng x 36): wave 0 is whole
-    const int ri = blockIdx.x, h = blockIdx.y >> 2, qz = blockIdx.y & 3, b = blockIdx.z;
+// quad = 0: one workgroup per (row, head, dim quarter), ng groups of 36 threads splitting the splits;
+// quad = 1 (few splits): one workgroup per (row, head), its four groups of 36 threads the four dim
+// quarters, so the head's split weights are formed once and there are four times fewer workgroups.
+__global__ void __launch_bounds__(kCombThreads) attn_combine(AttnArgs a, int nsplit, int quad) {
+    const int ng = quad ? 1 : blockDim.x / kCombPer;  // blockDim.x = max(64, ng x 36): wave 0 is whole
+    const int ri = blockIdx.x, b = blockIdx.z;
+    const int h = quad ? (int)blockIdx.y : (int)(blockIdx.y >> 2);
+    const int qz = quad ? (int)threadIdx.x / kCombPer : (int)(blockIdx.y & 3);
     const int64_t nrows = (int64_t)gridDim.x * gridDim.z;
     const int64_t rowid = (int64_t)b * gridDim.x + ri;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -598,8 +603,8 @@ __global__ void __launch_bounds__(kCombThreads) attn_combine(AttnArgs a, int nsp
     __shared__ float s_mu, s_den;
     __shared__ f32x4 part[kCombGroups - 1][kCombPer][2];
     const int el = tid % kCombPer;  // this thread's slot in the group exchange
-    const int q = tid / kCombPer;
-    const int e = qz * kCombPer + (tid - q * kCombPer);  // float4 index in the row
+    const int q = quad ? 0 : tid / kCombPer;
+    const int e = qz * kCombPer + el;  // float4 index in the row
     const int d = 4 * e;
     // RoPE dims 512 + j pair with 544 + j (j < 32)
     const bool rot = a.rope_theta != 0.0 && d >= kDN;
@@ -1378,9 +1383,15 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns <= 1) return e;
-    const int ct = comb_groups(ns) * kCombPer;
-    hipLaunchKernelGGL(attn_combine, dim3((unsigned)a.T, (unsigned)(a.H * kCombQuarters), (unsigned)a.B),
-                       dim3(ct < 64 ? 64 : ct), 0, st, a, ns);
+    const int groups = comb_groups(ns);
+    if (groups == 1) {
+        hipLaunchKernelGGL(attn_combine, dim3((unsigned)a.T, (unsigned)a.H, (unsigned)a.B),
+                           dim3(kCombQuarters * kCombPer), 0, st, a, ns, 1);
+    } else {
+        const int ct = groups * kCombPer;
+        hipLaunchKernelGGL(attn_combine, dim3((unsigned)a.T, (unsigned)(a.H * kCombQuarters), (unsigned)a.B),
+                           dim3(ct < 64 ? 64 : ct), 0, st, a, ns, 0);
+    }
     return hipGetLastError();
 }
 
