@@ -213,8 +213,9 @@ int lca_indexer_topk_mxfp4(const void* q, const float* w, lca_kv k, int32_t H_I,
  * row is both key and value, one KV head for all H query heads) and 2.3.3
  * (sliding-window branch, attention sink, output RoPE).  For query row
  * (b, i), t = q_pos[b] + i, head h, the attended rows are
- *   comp rows idx[b][i][j] >= 0 (j < k)  and  window rows p in
- *   [max(0, t - n_win + 1), t], stored at win row p mod win.cap,
+ *   comp rows e = idx[b][i][j] (j < k) with 0 <= e < vis(t) = min(floor((t + 1) / m),
+ *   comp.cap)  and  window rows p in [max(0, t - n_win + 1), t], stored at win
+ *   row p mod win.cap,
  * under one softmax with logits sm_scale * <q[b][i][h], row> and an optional
  * sink logit sink[h] that adds e^sink[h] to the denominator only:
  *   o = sum_j e^(l_j - mu) row_j / (e^(sink - mu) + sum_j e^(l_j - mu)).
@@ -225,8 +226,10 @@ int lca_indexer_topk_mxfp4(const void* q, const float* w, lca_kv k, int32_t H_I,
  * of out_dtype (LCA_F32 or LCA_BF16).  comp and win share d_nope / d_rope;
  * supported shapes: (d_nope, d_rope) = (512, 64) with H % 16 == 0 for
  * bf16/fp8 caches, any c <= 1024 for f32.  The window ring must hold every
- * needed row: min(n_win - 1, q_pos[b]) + T <= win.cap (n_win = 0: no window).  Every
- * idx value must be < comp.cap.  ws: device workspace of at least
+ * needed row: min(n_win - 1, q_pos[b]) + T <= win.cap (n_win = 0: no window).  idx
+ * values that are negative (padding) or not visible (e >= vis(t): a block
+ * ending after t, or a row past the cache) are skipped, never read: block-level
+ * causality holds whatever the list names.  ws: device workspace of at least
  * lca_attn_workspace_size(B, T, H, c, max keys per query) bytes.
  */
 int lca_csa_attn(const void* q, int32_t q_dtype, int32_t H, int32_t B, int32_t T,

@@ -174,6 +174,7 @@ def kv_compress(c_a, z_a, c_b, z_b, out: KV, *, m: int, overlap: int, first_pos,
 
 def indexer_score(q, w, k, scores, *, q_pos, m: int, stream=None):
     """q [B][T][H_I][d_I], w [B][T][H_I] f32 or None, k [B][k_cap][d_I], scores [B][T][s_stride]."""
+    _dense(("q", q), ("w", w), ("scores", scores))
     B, T, H_I, d_I = q.shape
     _check(lib().lca_indexer_score(_ptr(q), _ptr(w), _ptr(k), _dtype(q), int(k.shape[1]), int(H_I),
                                    int(d_I), int(B), int(T), _pos(q_pos, B), int(m), _ptr(scores),
@@ -183,6 +184,7 @@ def indexer_score(q, w, k, scores, *, q_pos, m: int, stream=None):
 def indexer_score_mxfp4(q, w, k: KV, scores, *, q_pos, m: int, stream=None):
     """q [B][T][H_I][d_I] bf16 (quantised to MXFP4 in the call), w [B][T][H_I] f32 or None, k MXFP4 key
     rows (KV with fmt MXFP4), scores [B][T][s_stride]."""
+    _dense(("q", q), ("w", w), ("scores", scores))
     B, T, H_I, d_I = q.shape
     _check(lib().lca_indexer_score_mxfp4(_ptr(q), _ptr(w), k.c(), int(H_I), int(d_I), int(B), int(T),
                                          _pos(q_pos, B), int(m), _ptr(scores), _dtype(scores),
@@ -191,6 +193,7 @@ def indexer_score_mxfp4(q, w, k: KV, scores, *, q_pos, m: int, stream=None):
 
 def topk_select(scores, idx, *, q_pos, m: int, ws=None, stream=None):
     """scores [B][T][s_stride] -> idx [B][T][k] int32."""
+    _dense(("scores", scores), ("idx", idx))
     B, T, s_stride = scores.shape
     k = idx.shape[2]
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
@@ -204,6 +207,7 @@ def indexer_topk(q, w, k, scores, idx, *, q_pos, m: int, ws=None, stream=None):
     q [B][1][16][128] bf16, w [B][1][16] f32 or None, k [B][k_cap][128] bf16, scores [B][1][s_stride] bf16,
     idx [B][1][k] int32; ws: indexer_topk_workspace_size bytes, zeroed before its first use and kept for
     this call only (every call leaves it zeroed)."""
+    _dense(("q", q), ("w", w), ("scores", scores), ("idx", idx))
     B = q.shape[0]
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().lca_indexer_topk(_ptr(q), _ptr(w), _ptr(k), int(k.shape[1]), int(q.shape[2]), int(q.shape[3]),
@@ -213,6 +217,7 @@ def indexer_topk(q, w, k, scores, idx, *, q_pos, m: int, ws=None, stream=None):
 
 def indexer_topk_mxfp4(q, w, k: KV, scores, idx, *, q_pos, m: int, ws=None, stream=None):
     """indexer_topk with MXFP4 keys (k: KV with fmt MXFP4; q bf16, quantised in the call)."""
+    _dense(("q", q), ("w", w), ("scores", scores), ("idx", idx))
     B = q.shape[0]
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().lca_indexer_topk_mxfp4(_ptr(q), _ptr(w), k.c(), int(q.shape[2]), int(q.shape[3]), int(B),
@@ -236,8 +241,18 @@ def _empty_kv():
     return _KV(0, 0, 0, 0, 0, 0, 0)
 
 
+def _dense(*named):
+    """The calls take q, w, scores, idx, out and lse as dense row-major arrays ([B][T][...], the last
+    dims contiguous): a strided view (e.g. a row slice of a larger buffer with B > 1) would be
+    addressed as if it were dense, so it is refused."""
+    for name, t in named:
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous (got strides {tuple(t.stride())})")
+
+
 def csa_attn(q, out, *, q_pos, comp: KV, m: int, idx, win: KV | None, n_win: int, sink=None,
              sm_scale: float, rope_theta: float = 0.0, lse=None, ws=None, stream=None):
+    _dense(("q", q), ("out", out), ("lse", lse), ("idx", idx))
     B, T, H, _ = q.shape
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().lca_csa_attn(_ptr(q), _dtype(q), int(H), int(B), int(T), _pos(q_pos, B), comp.c(),
@@ -249,6 +264,7 @@ def csa_attn(q, out, *, q_pos, comp: KV, m: int, idx, win: KV | None, n_win: int
 
 def hca_attn(q, out, *, q_pos, comp: KV, m: int, win: KV | None, n_win: int, sink=None,
              sm_scale: float, rope_theta: float = 0.0, lse=None, ws=None, stream=None):
+    _dense(("q", q), ("out", out), ("lse", lse))
     B, T, H, _ = q.shape
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().lca_hca_attn(_ptr(q), _dtype(q), int(H), int(B), int(T), _pos(q_pos, B), comp.c(),
@@ -270,6 +286,7 @@ def csa_attn_append(q, out, x_win, *, q_pos, comp: KV, m: int, idx, win: KV, n_w
                     stream=None):
     """Window store of rows q_pos .. q_pos+T-1 from x_win [B][T][c] (may be a row window of a longer
     per-sequence stream), then csa_attn."""
+    _dense(("q", q), ("out", out), ("lse", lse), ("idx", idx))
     B, T, H, _ = q.shape
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().lca_csa_attn_append(_ptr(q), _dtype(q), int(H), int(B), int(T), _pos(q_pos, B), comp.c(),
@@ -284,6 +301,7 @@ def hca_attn_append(q, out, x_win, *, q_pos, comp: KV, m: int, win: KV, n_win: i
                     stream=None):
     """Window store of rows q_pos .. q_pos+T-1 from x_win [B][T][c] (may be a row window of a longer
     per-sequence stream), then hca_attn."""
+    _dense(("q", q), ("out", out), ("lse", lse))
     B, T, H, _ = q.shape
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().lca_hca_attn_append(_ptr(q), _dtype(q), int(H), int(B), int(T), _pos(q_pos, B), comp.c(),

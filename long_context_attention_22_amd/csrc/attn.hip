@@ -43,6 +43,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 struct SlotMap {
+    int64_t vis;     // visible compressed entries, min(floor((t + 1) / m), comp.cap)
     int64_t ncs;     // compressed slots
     int64_t w_lo;    // first window position
     int64_t w_row;   // its ring row, w_lo mod win.cap
@@ -58,6 +59,7 @@ __device__ __forceinline__ SlotMap slot_map(const AttnArgs& a, int b, int i, int
     *tp = t;
     const int64_t q1 = a.m_shift >= 0 ? (t + 1) >> a.m_shift : (t + 1) / a.m;
     const int64_t vis = min(q1, a.comp.cap);
+    s.vis = vis;
     s.ncs = a.idx ? (int64_t)a.k : vis;
     const int64_t d = a.q_pos.v[b] - a.n_win + 1;  // first window position of row 0
     const int64_t wl = d + i;
@@ -83,14 +85,16 @@ __device__ __forceinline__ void row_coords(const AttnArgs& a, int64_t rowid, int
     *i = (int)(r - (uint32_t)*b * T);
 }
 
-// source row of a slot: 0 = invalid, 1 = compressed row, 2 = window row.  Window slots are
-// consecutive positions, fewer than win.cap of them, so their ring rows wrap at most once.
+// source row of a slot: 0 = invalid, 1 = compressed row, 2 = window row.  A listed entry id is
+// attended only when it is visible, 0 <= e < vis(t): an entry whose block ends after t never is
+// (block-level causality), whatever the index list says.  Window slots are consecutive positions,
+// fewer than win.cap of them, so their ring rows wrap at most once.
 __device__ __forceinline__ int slot_row(const AttnArgs& a, const SlotMap& sm, int64_t rowid, int b,
                                         int64_t slot, int64_t s_end, int64_t* row) {
     if (slot >= s_end) return 0;
     if (slot < sm.ncs) {
         int64_t e = a.idx ? (int64_t)a.idx[rowid * a.k + slot] : slot;
-        if (e < 0 || e >= a.comp.cap) return 0;
+        if (e < 0 || e >= sm.vis) return 0;
         *row = (int64_t)b * a.comp.cap + e;
         return 1;
     }
@@ -159,7 +163,7 @@ struct Gather {
     // Common case, decided per tile (wave-uniform): every slot of the tile is a compressed slot.
     // Rows are addressed from a per-tile scalar base (dense) or from 32-bit row offsets (CSA;
     // off32: the sequence's rows span less than 4 GiB).
-    __device__ __forceinline__ void load_comp(const AttnArgs& a, const KvPtrs& P, int64_t s0) {
+    __device__ __forceinline__ void load_comp(const SlotMap& sm, const KvPtrs& P, int64_t s0) {
         if constexpr (DENSE) {
             const GMEM uint8_t* bn = P.nope[0] + s0 * kRow;
             const GMEM uint8_t* bs = (const GMEM uint8_t*)P.scale[0] + s0 * 16;
@@ -175,7 +179,7 @@ struct Gather {
         } else {
             bool ok[2];
 #pragma unroll
-            for (int u = 0; u < 2; ++u) ok[u] = ent[u] >= 0 && ent[u] < a.comp.cap;
+            for (int u = 0; u < 2; ++u) ok[u] = ent[u] >= 0 && ent[u] < sm.vis;  // visible entries only
             const bool all = !__builtin_amdgcn_ballot_w64(!(ok[0] && ok[1]));  // wave-uniform
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
@@ -199,7 +203,7 @@ struct Gather {
     __device__ __forceinline__ void load(const AttnArgs& a, const SlotMap& sm, const KvPtrs& P, bool off32,
                                          int64_t s0, int64_t s_end) {
         if (off32 && s0 + kKT <= min(sm.ncs, s_end)) {  // wave-uniform
-            load_comp(a, P, s0);
+            load_comp(sm, P, s0);
             return;
         }
 #pragma unroll
@@ -212,7 +216,7 @@ struct Gather {
             if (slot < s_end) {
                 if (slot < sm.ncs) {
                     const int64_t e = DENSE ? slot : (int64_t)ent[u];
-                    if (e >= 0 && e < a.comp.cap) {
+                    if (e >= 0 && e < sm.vis) {
                         row = e;
                         sr = 1;
                     }
@@ -753,7 +757,7 @@ struct DecRegs {  // one tile's raw rows for this thread
 // each tile waits only for its own rows.  Offsets are 32-bit (the caller checks that every plane
 // of one sequence spans less than 4 GiB).
 template <int FMT, bool DENSE>
-__device__ __forceinline__ void dec_load(DecRegs<FMT>& R, int ncs, int w_row, int s_end, int comp_cap, int win_cap,
+__device__ __forceinline__ void dec_load(DecRegs<FMT>& R, int ncs, int w_row, int s_end, int vis, int win_cap,
                                          const KvPtrs& P, const int32_t* ent, int s_begin, int s0, int hw,
                                          int c) {
     constexpr uint32_t kRow = FMT == LCA_FP8 ? kDN : 2 * kDN;
@@ -768,7 +772,7 @@ __device__ __forceinline__ void dec_load(DecRegs<FMT>& R, int ncs, int w_row, in
         if (r >= win_cap) r -= win_cap;
         // (entry ids are read only for slots of this split: the index is clamped for the rest)
         const int e = DENSE ? slot : ent[min(slot - s_begin, kDecMaxLen - 1)];
-        const bool ok = slot < s_end && (wnd || (uint32_t)e < (uint32_t)comp_cap);
+        const bool ok = slot < s_end && (wnd || (uint32_t)e < (uint32_t)vis);
         const uint32_t row = !ok ? 0u : (uint32_t)(wnd ? r : e);
         const bool w = ok && wnd;
         R.ok |= (uint32_t)ok << u;
@@ -887,7 +891,7 @@ __global__ void __launch_bounds__(256) attn_dec(AttnArgs a, int64_t split_len, i
     const int s_end = (int)min(sm.nslots, (int64_t)s_begin + split_len);
     const int ntile = s_end > s_begin ? (s_end - s_begin + kKT - 1) / kKT : 0;
     const int ncs = (int)sm.ncs, w_row = (int)sm.w_row;
-    const int comp_cap = (int)a.comp.cap, win_cap = (int)a.win.cap;
+    const int vis = (int)sm.vis, win_cap = (int)a.win.cap;
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int n = lane & 15, g4 = lane >> 4;  // MFMA lane coordinates
@@ -948,7 +952,7 @@ __global__ void __launch_bounds__(256) attn_dec(AttnArgs a, int64_t split_len, i
     DecRegs<FMT> R[NP];
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
-        dec_load<FMT, DENSE>(R[j], ncs, w_row, s_end, comp_cap, win_cap, P, ent, s_begin, s_begin + j * kKT, hw, c);
+        dec_load<FMT, DENSE>(R[j], ncs, w_row, s_end, vis, win_cap, P, ent, s_begin, s_begin + j * kKT, hw, c);
         // (tile by tile, in the order the loop consumes them: the loop's waits count on it)
         asm volatile("" ::: "memory");
     }
@@ -973,7 +977,7 @@ __global__ void __launch_bounds__(256) attn_dec(AttnArgs a, int64_t split_len, i
     dec_store<FMT>(R[0], &Kt[0][0], (uint8_t*)vflag[0], hw, c);
     if (app) dec_fix_row<FMT>(&Kt[0][0], hw, c, rowt, tl);
     if (NP < kDecMaxTiles)
-        dec_load<FMT, DENSE>(R[0], ncs, w_row, s_end, comp_cap, win_cap, P, ent, s_begin, s_begin + NP * kKT, hw, c);
+        dec_load<FMT, DENSE>(R[0], ncs, w_row, s_end, vis, win_cap, P, ent, s_begin, s_begin + NP * kKT, hw, c);
 #pragma unroll
     for (int ks = 0; ks < 5; ++ks) asm volatile("" ::"v"(qf[ks]));
     __syncthreads();
@@ -1016,7 +1020,7 @@ __global__ void __launch_bounds__(256) attn_dec(AttnArgs a, int64_t split_len, i
                 dec_store<FMT>(Rn, (uint16_t*)((char*)&Kt[0][0] + bn), (uint8_t*)vflag[fn], hw, c);
                 if (app) dec_fix_row<FMT>((uint16_t*)((char*)&Kt[0][0] + bn), hw, c, rowt, tl - (t + 1) * kKT);
                 if (t + 1 + NP < kDecMaxTiles)
-                    dec_load<FMT, DENSE>(Rn, ncs, w_row, s_end, comp_cap, win_cap, P, ent, s_begin,
+                    dec_load<FMT, DENSE>(Rn, ncs, w_row, s_end, vis, win_cap, P, ent, s_begin,
                                          s_begin + (t + 1 + NP) * kKT, hw, c);
             }
             __syncthreads();

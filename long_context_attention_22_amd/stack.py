@@ -98,6 +98,13 @@ class Params:
     i_bias_b: torch.Tensor | None = None
 
 
+def _rows(buf: torch.Tensor, T: int) -> torch.Tensor:
+    """The first B x T rows of a [B][t_max][n] buffer as a dense [B][T][n] array (its leading
+    elements: the calls take dense arrays, and a [:, :T] slice is strided when B > 1)."""
+    B, _, n = buf.shape
+    return buf.view(-1)[:B * T * n].view(B, T, n)
+
+
 class Layer:
     def __init__(self, spec: LayerSpec, B: int, comp_cap: int, win_cap: int, t_max: int, params: Params,
                  device="cuda", kvs: dict | None = None):
@@ -158,8 +165,8 @@ class Layer:
         run = record or (lambda name, fn: fn())
         app = {} if x_win is None else dict(gamma=p.gamma, eps=s.eps)
         if s.kind == "csa":
-            sc = self.scores[:, :T]
-            ix = self.idx[:, :T]
+            sc = _rows(self.scores, T)
+            ix = _rows(self.idx, T)
             if T == 1 and self.fuse_topk and s.score_fmt == BF16 and self.keys.fmt in (BF16, MXFP4):
                 if self.keys.fmt == MXFP4:
                     run("indexer_topk", lambda: indexer_topk_mxfp4(q_idx, w, self.keys, sc, ix, q_pos=t0, m=s.m,

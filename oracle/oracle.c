@@ -455,8 +455,11 @@ int orc_topk_select(const void* scores, int32_t score_fmt, int64_t s_stride, int
 /* ------------------------------------------------------------------------- */
 /*
  * For query position t and head h the attended set is the union of
- *   - compressed entries: CSA the entries listed in idx (>= 0); HCA every
- *     visible entry s < vis(t) (dense attention over the compressed stream);
+ *   - compressed entries: CSA the entries listed in idx that are visible,
+ *     0 <= s < vis(t) (block-level causality: an entry whose block ends after
+ *     t is never attended, whatever the selection lists; negative ids are
+ *     padding); HCA every visible entry s < vis(t) (dense attention over the
+ *     compressed stream);
  *   - window rows: the n_win most recent raw positions ending at t itself,
  *     p in [max(0, t - n_win + 1), t], stored at ring row p mod win.cap.
  * Each stored vector is both key and value (shared-KV MQA: one KV head for all
@@ -486,8 +489,10 @@ int orc_attention(const void* q, int32_t q_fmt, int32_t H, int32_t B, int32_t T,
             if (vis > comp.cap) vis = comp.cap;
             int64_t ncomp = 0;
             if (idx) {
-                for (int j = 0; j < k; ++j)
-                    if (idx[((int64_t)b * T + i) * k + j] >= 0) ++ncomp;
+                for (int j = 0; j < k; ++j) {
+                    const int32_t s = idx[((int64_t)b * T + i) * k + j];
+                    if (s >= 0 && s < vis) ++ncomp;
+                }
             } else {
                 ncomp = vis;
             }
@@ -500,7 +505,7 @@ int orc_attention(const void* q, int32_t q_fmt, int32_t H, int32_t B, int32_t T,
             if (idx) {
                 for (int j = 0; j < k; ++j) {
                     int32_t s = idx[((int64_t)b * T + i) * k + j];
-                    if (s >= 0) orc_kv_decode(comp, b, s, 1, kv + (r++) * c);
+                    if (s >= 0 && s < vis) orc_kv_decode(comp, b, s, 1, kv + (r++) * c);
                 }
             } else {
                 for (int64_t s = 0; s < vis; ++s) orc_kv_decode(comp, b, s, 1, kv + (r++) * c);

@@ -343,8 +343,8 @@ def _oracle_step(L, spec, t0, T):
                     L["comp"], m=m, overlap=ov, first_pos=[lo] * B, bias_a=prm["ba"], bias_b=prm["bb"] if ov else None,
                     gamma=prm["gamma"], rope_theta=1e4)
     if spec.kind == "csa":
-        kv = orc.KV(L["keys"], np.zeros((B, L["keys"].shape[1], 0), np.uint16), None, orc.BF16, 128, 0,
-                    L["keys"].shape[1])
+        kv = L.get("k4") or orc.KV(L["keys"], np.zeros((B, L["keys"].shape[1], 0), np.uint16), None, orc.BF16,
+                                   128, 0, L["keys"].shape[1])
         orc.kv_compress(r("ica", lo, n), r("iza", lo, n), r("icb", lo, n), r("izb", lo, n), kv, m=m, overlap=1,
                         first_pos=[lo] * B, bias_a=prm["iba"], bias_b=prm["ibb"])
 
@@ -352,8 +352,12 @@ def _oracle_step(L, spec, t0, T):
 def _oracle_attend(L, spec, t, q, qI=None, w=None):
     """One query row per sequence at position t: (idx or None, fp32 scores or None, out)."""
     if spec.kind == "csa":
-        s32 = orc.indexer_score(qI, w, L["keys"], q_pos=[t] * q.shape[0], m=spec.m, score_fmt=orc.F32)
-        s16 = orc.indexer_score(qI, w, L["keys"], q_pos=[t] * q.shape[0], m=spec.m, score_fmt=orc.BF16)
+        if L.get("k4") is not None:  # MXFP4 indexer keys: the QK path in MXFP4
+            s32 = orc.indexer_score_mxfp4(qI, w, L["k4"], q_pos=[t] * q.shape[0], m=spec.m, score_fmt=orc.F32)
+            s16 = orc.indexer_score_mxfp4(qI, w, L["k4"], q_pos=[t] * q.shape[0], m=spec.m, score_fmt=orc.BF16)
+        else:
+            s32 = orc.indexer_score(qI, w, L["keys"], q_pos=[t] * q.shape[0], m=spec.m, score_fmt=orc.F32)
+            s16 = orc.indexer_score(qI, w, L["keys"], q_pos=[t] * q.shape[0], m=spec.m, score_fmt=orc.BF16)
         ix = orc.topk_select(s16, q_pos=[t] * q.shape[0], m=spec.m, k=spec.k)
         o, _ = orc.attention(q, q_pos=[t] * q.shape[0], comp=L["comp"], m=spec.m, idx=ix, win=L["win"], n_win=128,
                              sink=L["prm"]["sink"], sm_scale=C ** -0.5, rope_theta=1e4)

@@ -148,8 +148,9 @@ def test_paged_stack_matches_contiguous_and_forks(key_fmt):
         _same(last, kid_c.step(seed + 99, tags, t, 1), f"child t {t}")
     torch.cuda.synchronize()
 
-    if key_fmt == lca.BF16:  # the child's last step against the oracle, from the raw inputs
-        _oracle_check(specs, tags, params, craw, n + 15, seed + 99, last, kid_p)
+    # the child's last step against the oracle, from the raw inputs (MXFP4 keys: the oracle's MXFP4
+    # storage and scores)
+    _oracle_check(specs, tags, params, craw, n + 15, seed + 99, last, kid_p)
     for s in (0, 2, child):
         cache.close(s)
     st = cache.stats()
@@ -177,12 +178,16 @@ def _oracle_check(specs, tags, params, craw, t, qseed, gout, kid):
                         gamma=ph(pr.gamma), rope_theta=1e4, ring=1)
         q, qi, w = _queries(qseed, tg, sp, t, 1)
         if sp.kind == "csa":
-            keys = orc.KV(np.zeros((1, cap, 128), np.uint16), np.zeros((1, cap, 0), np.uint16), None, orc.BF16, 128,
-                          0, cap)
+            fp4 = sp.key_fmt == lca.MXFP4
+            keys = orc.KV.empty(orc.MXFP4 if fp4 else orc.BF16, 1, cap, 128, 0)
             orc.kv_compress(r["i_ca"], r["i_za"], r["i_cb"], r["i_zb"], keys, m=sp.m, overlap=1, first_pos=[0],
                             bias_a=ph(pr.i_bias_a), bias_b=ph(pr.i_bias_b))
-            s32 = orc.indexer_score(qi, w, keys.nope, q_pos=[t], m=sp.m, score_fmt=orc.F32)
-            s16 = orc.indexer_score(qi, w, keys.nope, q_pos=[t], m=sp.m, score_fmt=orc.BF16)
+            if fp4:
+                s32 = orc.indexer_score_mxfp4(qi, w, keys, q_pos=[t], m=sp.m, score_fmt=orc.F32)
+                s16 = orc.indexer_score_mxfp4(qi, w, keys, q_pos=[t], m=sp.m, score_fmt=orc.BF16)
+            else:
+                s32 = orc.indexer_score(qi, w, keys.nope, q_pos=[t], m=sp.m, score_fmt=orc.F32)
+                s16 = orc.indexer_score(qi, w, keys.nope, q_pos=[t], m=sp.m, score_fmt=orc.BF16)
             ix = orc.topk_select(s16, q_pos=[t], m=sp.m, k=sp.k)
             o, _ = orc.attention(q, q_pos=[t], comp=comp, m=sp.m, idx=ix, win=win, n_win=sp.n_win,
                                  sink=ph(pr.sink), sm_scale=C ** -0.5, rope_theta=1e4)

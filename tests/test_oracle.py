@@ -206,6 +206,21 @@ def test_compress_rmsnorm_and_rope(orc):
                 math.hypot(out.rope[0, s, i], out.rope[0, s, i + dr // 2]), rel=1e-6)
 
 
+def test_compress_rmsnorm_epsilon(orc):
+    """epsilon joins the mean square under the root: a row of ones with eps = 3 becomes 1 / sqrt(1 + 3)
+    = 0.5 in every dim, a row of twos 2 / sqrt(4 + 3); an all-zero row stays zero (no division by 0)."""
+    dn = 16
+    x = np.ones((1, 3, dn), np.float32)
+    x[0, 1] = 2.0
+    x[0, 2] = 0.0
+    out = orc.KV.empty(orc.F32, 1, 3, dn, 0)
+    orc.kv_compress(x, np.zeros_like(x), None, None, out, m=1, overlap=0, first_pos=[0],
+                    gamma=np.ones(dn, np.float32), eps=3.0)
+    np.testing.assert_array_equal(out.nope[0, 0], np.full(dn, 0.5, np.float32))
+    np.testing.assert_allclose(out.nope[0, 1], 2.0 / math.sqrt(7.0), rtol=1e-7)
+    np.testing.assert_array_equal(out.nope[0, 2], np.zeros(dn, np.float32))
+
+
 def test_compress_store_formats(orc):
     m, dn, dr = 1, 256, 64
     x = S.block_scaled(3, "x", 0, 40, dn + dr)[None]
@@ -419,6 +434,52 @@ def test_invisible_and_future_rows_never_read(orc):
         b_, _ = orc.attention(qt, q_pos=[t], comp=e3, m=m, idx=idx[:, t:t + 1], win=w2, n_win=n_win,
                               sm_scale=0.2)
         np.testing.assert_array_equal(b_[0, 0], o_c[0, t])
+
+
+def _windowed_mqa(q, kv, scale, n_win):
+    """Textbook sliding-window softmax attention: query t attends keys p in [t - n_win + 1, t]."""
+    T, H, c = q.shape
+    lg = np.einsum("thd,sd->ths", q.astype(np.float64), kv.astype(np.float64)) * scale
+    t, p = np.arange(T)[:, None], np.arange(T)[None, :]
+    mask = (p <= t) & (p > t - n_win)
+    lg = np.where(mask[:, None, :], lg, -np.inf)
+    lg -= lg.max(-1, keepdims=True)
+    w = np.exp(lg)
+    w /= w.sum(-1, keepdims=True)
+    return np.einsum("ths,sd->thd", w, kv.astype(np.float64))
+
+
+def test_window_ring_wrap_is_sliding_window_mqa(orc):
+    """A window ring smaller than the sequence (cap 7 < T = 30), written by the compressor's ring rule
+    (row p mod cap) one chunk at a time, read at row p mod cap: each query's output equals the textbook
+    sliding-window attention over the raw rows."""
+    T, H, c, n_win, cap = 30, 2, 24, 5, 7
+    x, q = _f32(1, T, c, seed=84), _f32(1, T, H, c, seed=85)
+    ref = _windowed_mqa(q[0], x[0], 0.3, n_win)
+    ring = orc.KV.empty(orc.F32, 1, cap, c - 8, 8)
+    comp = orc.KV.empty(orc.F32, 1, 1, c - 8, 8)   # m larger than the sequence: nothing visible
+    z = np.zeros_like(x)
+    for t in range(T):                              # store row t, then attend from t (decode order)
+        orc.kv_compress(x[:, t:t + 1], z[:, t:t + 1], None, None, ring, m=1, overlap=0, first_pos=[t], ring=1)
+        o, _ = orc.attention(q[:, t:t + 1], q_pos=[t], comp=comp, m=64, idx=None, win=ring, n_win=n_win,
+                             sm_scale=0.3)
+        np.testing.assert_allclose(o[0, 0], ref[t], rtol=1e-5, atol=1e-6)
+
+
+def test_csa_listed_future_entries_not_attended(orc):
+    """Block-level causality holds at the attention step: an index list naming every entry, future ones
+    included (their rows NaN), and ids past the cache still gives textbook causal attention
+    (identity compressor, m = 1)."""
+    T, H, c = 14, 2, 24
+    x, q = _f32(1, T, c, seed=86), _f32(1, T, H, c, seed=87)
+    comp = _rows_kv(orc, x)
+    ref = _causal_mqa(q[0], x[0], 0.25)
+    idx = np.tile(np.arange(T + 2, dtype=np.int32), (1, T, 1))   # ids T, T + 1 lie past the cache
+    for t in range(T):
+        poisoned = orc.KV(comp.nope.copy(), comp.rope.copy(), None, comp.fmt, comp.d_nope, comp.d_rope, comp.cap)
+        poisoned.nope[0, t + 1:] = np.nan
+        o, _ = orc.attention(q[:, t:t + 1], q_pos=[t], comp=poisoned, m=1, idx=idx[:, t:t + 1], sm_scale=0.25)
+        np.testing.assert_allclose(o[0, 0], ref[t], rtol=1e-5, atol=1e-6)
 
 
 def test_output_rope_makes_position_relative(orc):
