@@ -250,6 +250,30 @@ int lca_hca_attn(const void* q, int32_t q_dtype, int32_t H, int32_t B, int32_t T
                  int32_t out_dtype, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * lca_hca_attn_noalloc -- lca_hca_attn for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc): the same arguments without the workspace, the same
+ * kernels and results.  Its scratch (the split partials of decode-sized
+ * launches, and the once-per-launch fp8 expansion of long ones when it fits)
+ * is one static device array of LCA_NOALLOC_SCRATCH_BYTES per GPU, held from
+ * the library's load on that device until the process ends; the call never
+ * allocates or frees.  A launch whose split partials need more than that
+ * (lca_attn_workspace_size's split part, e.g. more rows x longer contexts
+ * than one 1M-token decode row) fails with LCA_EWORKSPACE before anything
+ * runs; a long launch whose expansion does not fit expands per tile as
+ * lca_hca_attn does with a small workspace.  Every call on one GPU shares
+ * that GPU's array: calls that overlap in time on one GPU (two streams, two
+ * threads) race and must be serialised by the caller.  The first call on a
+ * device looks up the array's device address (hipGetSymbolAddress) with that
+ * device current; errors as lca_hca_attn, plus LCA_EHIP if that lookup fails.
+ */
+#define LCA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int lca_hca_attn_noalloc(const void* q, int32_t q_dtype, int32_t H, int32_t B, int32_t T,
+                         const int64_t* q_pos, lca_kv comp, int32_t m, lca_kv win, int32_t n_win,
+                         const float* sink, float sm_scale, double rope_theta, void* out,
+                         int32_t out_dtype, float* lse, void* stream);
+
+/*
  * lca_csa_attn_append / lca_hca_attn_append -- the window store of the call's
  * own rows, then the attention: first rows q_pos[b] .. q_pos[b] + T - 1 of
  * x_win (x_dtype LCA_F32 or LCA_BF16; the raw rows of those positions: T

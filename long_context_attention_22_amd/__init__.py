@@ -63,6 +63,8 @@ def lib():
                                    vp, i32, vp, vp, sz, vp]
         L.lca_hca_attn.argtypes = [vp, i32, i32, i32, i32, vp, _KV, i32, _KV, i32, vp, f32, f64, vp, i32,
                                    vp, vp, sz, vp]
+        L.lca_hca_attn_noalloc.argtypes = [vp, i32, i32, i32, i32, vp, _KV, i32, _KV, i32, vp, f32, f64, vp, i32,
+                                           vp, vp]
         L.lca_csa_attn_append.argtypes = [vp, i32, i32, i32, i32, vp, _KV, i32, vp, i32, _KV, i32, vp, i32, i64,
                                           vp, f32, vp, f32, f64, vp, i32, vp, vp, sz, vp]
         L.lca_hca_attn_append.argtypes = [vp, i32, i32, i32, i32, vp, _KV, i32, _KV, i32, vp, i32, i64, vp, f32,
@@ -76,8 +78,9 @@ def lib():
         L.lca_attn_workspace_size.argtypes = [i32, i32, i32, i32, i64]
         L.lca_attn_workspace_size.restype = sz
         for name in ("lca_kv_compress", "lca_indexer_score", "lca_indexer_score_mxfp4", "lca_topk_select",
-                     "lca_csa_attn", "lca_hca_attn", "lca_csa_attn_append", "lca_hca_attn_append", "lca_linear",
-                     "lca_grouped_out_proj", "lca_indexer_topk", "lca_indexer_topk_mxfp4"):
+                     "lca_csa_attn", "lca_hca_attn", "lca_hca_attn_noalloc", "lca_csa_attn_append",
+                     "lca_hca_attn_append", "lca_linear", "lca_grouped_out_proj", "lca_indexer_topk",
+                     "lca_indexer_topk_mxfp4"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -271,6 +274,20 @@ def hca_attn(q, out, *, q_pos, comp: KV, m: int, win: KV | None, n_win: int, sin
                               int(m), win.c() if win is not None else _empty_kv(), int(n_win),
                               _ptr(sink), float(sm_scale), float(rope_theta), _ptr(out), _dtype(out),
                               _ptr(lse), _ptr(ws), nbytes, _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # LCA_NOALLOC_SCRATCH_BYTES
+
+
+def hca_attn_noalloc(q, out, *, q_pos, comp: KV, m: int, win: KV | None, n_win: int, sink=None,
+                     sm_scale: float, rope_theta: float = 0.0, lse=None, stream=None):
+    """hca_attn without a workspace: the library's static per-GPU scratch (calls on one GPU must not overlap)."""
+    _dense(("q", q), ("out", out), ("lse", lse))
+    B, T, H, _ = q.shape
+    _check(lib().lca_hca_attn_noalloc(_ptr(q), _dtype(q), int(H), int(B), int(T), _pos(q_pos, B), comp.c(),
+                                      int(m), win.c() if win is not None else _empty_kv(), int(n_win),
+                                      _ptr(sink), float(sm_scale), float(rope_theta), _ptr(out), _dtype(out),
+                                      _ptr(lse), _stream(stream)))
 
 
 def _rows_stride(x, T: int) -> int:

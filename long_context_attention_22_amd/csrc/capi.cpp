@@ -8,6 +8,7 @@
 #include <climits>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/lca.h"
 #include "kernels.h"
@@ -591,6 +592,46 @@ int lca_hca_attn(const void* q, int32_t q_dtype, int32_t H, int32_t B, int32_t T
     g_err[0] = 0;
     return attn_common(q, q_dtype, H, B, T, q_pos, comp, m, nullptr, 0, win, n_win, sink, sm_scale,
                        rope_theta, out, out_dtype, lse, ws, ws_bytes, stream);
+}
+
+// Scratch of lca_hca_attn_noalloc: one static array per GPU (each device that loads the library holds its own
+// copy until the process ends).  In host code `scratch` names a host-side stand-in, not device memory: every
+// use goes through the device address hipGetSymbolAddress returns, looked up once per device with that device
+// current and kept in g_scratch_ptr.
+static __device__ __align__(256) uint8_t scratch[LCA_NOALLOC_SCRATCH_BYTES];
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_for_current_device(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(LCA_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(LCA_EINVAL, "device %d beyond the %d supported", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(LCA_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return LCA_OK;
+}
+}  // namespace
+
+int lca_hca_attn_noalloc(const void* q, int32_t q_dtype, int32_t H, int32_t B, int32_t T, const int64_t* q_pos,
+                         lca_kv comp, int32_t m, lca_kv win, int32_t n_win, const float* sink, float sm_scale,
+                         double rope_theta, void* out, int32_t out_dtype, float* lse, void* stream) {
+    g_err[0] = 0;
+    void* ws = nullptr;
+    const int rc = scratch_for_current_device(&ws);
+    if (rc) return rc;
+    // (attn_common checks the launch's split partials against the array's size: LCA_EWORKSPACE beyond it)
+    return attn_common(q, q_dtype, H, B, T, q_pos, comp, m, nullptr, 0, win, n_win, sink, sm_scale, rope_theta,
+                       out, out_dtype, lse, ws, LCA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int lca_linear(const void* x, int64_t ldx, int64_t sx, const void* w, int64_t ldw, int64_t sw, void* y,
