@@ -764,6 +764,43 @@ __device__ __forceinline__ void dec_load(DecRegs<FMT>& R, int ncs, int w_row, in
     R.ok = 0;
     uint32_t rrow = 0;
     bool rw = false;
+    if (s0 + kKT <= min(ncs, s_end)) {
+        // (wave-uniform) every slot of the tile is a compressed slot: no window rows, no wrap, no
+        // per-row choice of plane.  Dense: the tile's rows are consecutive entries, addressed from one
+        // scalar base per tile plus loop-invariant lane offsets.  Selected: 32-bit row offsets of the
+        // entry ids.  The same loads as the general path below, so the waits count alike.
+        const uint32_t lane_off = (uint32_t)hw * kRow + 16u * c;
+        const GMEM uint8_t* nb = P.nope[0];
+        const GMEM uint8_t* sb = (const GMEM uint8_t*)P.scale[0];
+        const GMEM uint8_t* rb = (const GMEM uint8_t*)P.rope[0];
+        if constexpr (DENSE) {
+            nb += (uint64_t)(uint32_t)s0 * kRow;
+            if constexpr (FMT == LCA_FP8) sb += (uint64_t)(uint32_t)s0 * 16u;
+            rb += (uint64_t)(uint32_t)s0 * 128u;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            uint32_t noff, soff, row;
+            if constexpr (DENSE) {
+                row = (uint32_t)(hw + 8 * u);  // (relative to s0)
+                noff = lane_off + (uint32_t)(8 * u) * kRow;
+            } else {
+                const int e = ent[s0 + hw + 8 * u - s_begin];
+                const bool ok = (uint32_t)e < (uint32_t)vis;
+                R.ok |= (uint32_t)ok << u;
+                row = ok ? (uint32_t)e : 0u;
+                noff = row * kRow + 16u * c;
+            }
+            soff = row * 16u + 4u * (c >> 3);
+            if (u == (c >> 3)) rrow = row;
+            R.v[u][0] = *(const GMEM u32x4*)(nb + noff);
+            if constexpr (FMT == LCA_FP8) R.sc[u] = *(const GMEM float*)(sb + soff);
+            else R.v[u][1] = *(const GMEM u32x4*)(nb + (noff + 512u));
+        }
+        if constexpr (DENSE) R.ok = 0xfu;
+        R.rp = *(const GMEM u32x4*)(rb + (rrow * 128u + 16u * (c & 7)));
+        return;
+    }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int slot = s0 + hw + 8 * u;

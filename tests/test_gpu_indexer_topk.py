@@ -18,12 +18,20 @@ from gpu_util import host
 pytestmark = pytest.mark.gpu
 
 
-def _inputs(seed, B, cap):
+def _inputs(seed, B, cap, ties=False):
     g = torch.Generator(device="cuda").manual_seed(seed)
     q = torch.randn(B, 1, 16, 128, device="cuda", generator=g).to(torch.bfloat16)
     w = torch.randn(B, 1, 16, device="cuda", generator=g) * 0.25
+    if ties:  # every score 0: the whole row ties, the first k indices win
+        w.zero_()
     k = torch.randn(B, cap, 128, device="cuda", generator=g).to(torch.bfloat16)
     return q, w, k
+
+
+def _check_ws(ws, nbytes):
+    """Every call leaves the workspace zeroed (histograms and arrival counters)."""
+    if nbytes:
+        assert int(ws.count_nonzero()) == 0
 
 
 def _separate(q, w, k, q_pos, m, s_stride, topk):
@@ -41,19 +49,21 @@ def _vis_cols(sc, q_pos, m):
     return [host(sc[b, 0, :(p + 1) // m]) for b, p in enumerate(q_pos)]
 
 
-@pytest.mark.parametrize("B,cap,topk,pos_list", [
-    (1, 262160, 2048, [[(1 << 20) + 3], [(1 << 20) + 7], [(1 << 20) + 11]]),       # 1M decode, three calls
-    (32, 32800, 1024, [[131071 + 4 * b for b in range(32)], [131075] * 32]),      # 32 x 128K
-    (3, 300016, 2048, [[1199995, 20003, 6000], [1200003, 65539, 8191]]),          # mixed lengths, trivial rows
-    (2, 12000, 512, [[40000, 47000]]),                                             # the row schedule
+@pytest.mark.parametrize("B,cap,topk,pos_list,ties", [
+    (1, 262160, 2048, [[(1 << 20) + 3], [(1 << 20) + 7], [(1 << 20) + 11]], False),  # 1M decode, three calls
+    (32, 32800, 1024, [[131071 + 4 * b for b in range(32)], [131075] * 32], False),  # 32 x 128K
+    (3, 300016, 2048, [[1199995, 20003, 6000], [1200003, 65539, 8191]], False),      # mixed lengths, trivial rows
+    (2, 12000, 512, [[40000, 47000]], False),                                         # the row schedule
+    (1, 262160, 2048, [[(1 << 20) + 3], [(1 << 20) + 7]], True),                      # a row of equal scores
+    (1, 1048600, 2048, [[(1 << 22) + 3]], False),                                     # a 4M-token row, 65 chunks
 ])
-def test_indexer_topk_matches_separate_calls(B, cap, topk, pos_list):
+def test_indexer_topk_matches_separate_calls(B, cap, topk, pos_list, ties):
     m = 4
     s_stride = cap
     nbytes = lca.indexer_topk_workspace_size(B, s_stride, topk)
     ws = torch.zeros(max(16, nbytes), dtype=torch.uint8, device="cuda")
     for call, q_pos in enumerate(pos_list):
-        q, w, k = _inputs(100 + call, B, cap)
+        q, w, k = _inputs(100 + call, B, cap, ties)
         sc = torch.zeros(B, 1, s_stride, dtype=torch.bfloat16, device="cuda")
         ix = torch.empty(B, 1, topk, dtype=torch.int32, device="cuda")
         lca.indexer_topk(q, w, k, sc, ix, q_pos=q_pos, m=m, ws=ws)
@@ -69,8 +79,7 @@ def test_indexer_topk_matches_separate_calls(B, cap, topk, pos_list):
             row[0, 0, :n] = host(sc[b, 0, :n])
             o_ix = orc.topk_select(row, q_pos=[p], m=m, k=topk)
             assert np.array_equal(o_ix[0, 0], host(ix[b, 0])), (call, b)
-    if nbytes:  # every call leaves its workspace zeroed
-        assert int(ws.count_nonzero()) == 0
+        _check_ws(ws, nbytes)
 
 
 def test_indexer_topk_graph_replays():
@@ -97,7 +106,7 @@ def test_indexer_topk_graph_replays():
             assert torch.equal(ix, ix_ref), rep
         _separate(q, w, k, [pos[rep]], m, s_stride, topk)  # eager work between replays
         torch.cuda.synchronize()
-    assert int(ws.count_nonzero()) == 0
+        _check_ws(ws, ws.numel())
 
 
 def _mxfp4_keys(seed, B, cap):
@@ -130,4 +139,4 @@ def test_indexer_topk_mxfp4_matches_separate_calls(B, cap, topk, pos_list):
         for b, (a, r) in enumerate(zip(_vis_cols(sc, q_pos, m), _vis_cols(sc_ref, q_pos, m))):
             assert np.array_equal(a, r), (call, b)
         assert torch.equal(ix, ix_ref), call
-    assert int(ws.count_nonzero()) == 0
+        _check_ws(ws, ws.numel())
