@@ -22,10 +22,11 @@ and for one decode token; a whole single-layer prefill from position 0 (CSA at 8
 HCA at 65,536, bf16 storage); the 1M decode again with every cache in the paged
 cache (one slot per replica, 64 KiB and 2 MiB pages) and the cost of forking
 the 1M-token sequence (prefix reuse).  "roofline"
-covers the dominant decode kernel (indexer_score, HBM-bound), timed with HIP
-events on its stream inside the timed graph.  "cpu_baseline" is the fp64
-oracle timed on host cores on a bounded sample (four decode steps of the
-stack).
+covers the dominant decode call, the CSA layer's fused indexer + top-k
+(HBM-bound: 67 MB of keys per token), timed with HIP events around a graph of
+the step's own calls; "step_hbm" is the whole step's algorithmic bytes over
+its time.  "cpu_baseline" is the fp64 oracle on the host cores, a bounded
+sample (one copy of the stack per core, four decode steps each).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -52,12 +53,13 @@ from long_context_attention_22_amd.stack import (Layer, LayerSpec, Params, RawSt
                                                  slot_kvs)
 
 METRIC = "CSA/HCA decode tokens/s at 128K–1M ctx (HBM GB/s %) + prefill tokens/s"
-# HBM traffic of the decode indexer launch from rocprofv3 FETCH_SIZE / WRITE_SIZE passes, scaled by
-# the same counters on a plain copy; used only while the indexer source is unchanged since then.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_decode_1m_traffic.json")
+# HBM traffic of the decode indexer + top-k call (its three kernels) from rocprofv3 FETCH_SIZE /
+# WRITE_SIZE passes, scaled by the same counters on a plain copy; used only while the sources of those
+# kernels are unchanged since then.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_topk_decode_1m_traffic.json")
 MXFP4_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_mxfp4_decode_1m_traffic.json")
-INDEXER_SOURCES = ["long_context_attention_22_amd/csrc/indexer.hip", "long_context_attention_22_amd/csrc/device.h",
-                   "long_context_attention_22_amd/csrc/kernels.h"]
+INDEXER_SOURCES = ["long_context_attention_22_amd/csrc/indexer.hip", "long_context_attention_22_amd/csrc/topk.hip",
+                   "long_context_attention_22_amd/csrc/device.h", "long_context_attention_22_amd/csrc/kernels.h"]
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 FP4_PEAK_TFLOPS = 10100.0   # dense MXFP4 MFMA
@@ -210,10 +212,11 @@ class KernelTimer:
         return float(np.mean([a.elapsed_time(b) for a, b in self.pairs]))
 
 
-def graph_kernel_ms(stacks, W: int, K: int, name: str) -> float:
-    """Mean duration of one kernel's launches of the timed steps, replayed back to back in a graph.
-    (indexer_score: the decode step runs the indexer inside indexer_topk; its launches are collected
-    here as plain indexer_score calls with the same arguments.)"""
+def graph_kernel_ms(stacks, W: int, K: int, name: str, unfuse: bool = False) -> float:
+    """Mean duration of one library call's launches of the timed steps (the same calls with the same
+    arguments and caches), replayed back to back in a graph; HIP events on the launch stream around the
+    replay, divided by the call count.  unfuse: collect the CSA layers' selection as a plain
+    indexer_score call instead of the fused indexer_topk (for the separate-call figures)."""
     R = len(stacks)
     launches = []
 
@@ -222,8 +225,9 @@ def graph_kernel_ms(stacks, W: int, K: int, name: str) -> float:
             launches.append(fn)
 
     fused = [(ly, ly.fuse_topk) for st in stacks for ly in st.layers]
-    for ly, _ in fused:
-        ly.fuse_topk = False
+    if unfuse:
+        for ly, _ in fused:
+            ly.fuse_topk = False
     for i in range(W, W + K):  # collect the launches (nothing runs: only the named one is kept)
         stacks[i % R].decode(i // R, record=lambda n, fn: grab(n, fn) if n == name else None)
     for ly, f in fused:
@@ -341,6 +345,38 @@ def indexer_bytes(vis: int, B: int, d_I: int = 128, H_I: int = 16) -> int:
     return B * (vis * d_I * 2 + vis * 2 + H_I * d_I * 2 + H_I * 4)
 
 
+def indexer_topk_bytes(vis: int, B: int, k: int, key_bytes: int = 256, d_I: int = 128, H_I: int = 16) -> int:
+    """Algorithmic bytes of one decode indexer + top-k call: keys read once, q and w read, the k selected
+    indices written.  The score row between the two (written once, read by the top-k's passes) is staged,
+    not algorithmic: staged_score_bytes."""
+    return B * (vis * key_bytes + H_I * d_I * 2 + H_I * 4 + k * 4)
+
+
+def staged_score_bytes(vis: int, B: int, reads: int = 2) -> int:
+    """The bf16 score row of a fused decode call: written by the indexer, read by the top-k's two launches."""
+    return B * vis * 2 * (1 + reads)
+
+
+def decode_step_bytes(specs, t: int, B: int = 1) -> int:
+    """Algorithmic HBM bytes of one decode token through the stack at position t: per layer the attended
+    stored rows (fp8 entries of 656 bytes: CSA the top-k selected, HCA every visible one, plus the window),
+    q and o (bf16), the raw row of the window store and its stored row; CSA adds the indexer keys, its
+    queries and head weights.  The amortised compression of a completed block (< 0.1 %) is left out."""
+    row = 512 + 128 + 16
+    tot = 0
+    for sp in specs:
+        vis = (t + 1) // sp.m
+        rows = (min(sp.k, vis) if sp.kind == "csa" else vis) + min(sp.n_win, t + 1)
+        tot += rows * row + 2 * sp.H * C * 2 + C * 2 + row
+        if sp.kind == "csa":
+            tot += vis * sp.d_I * 2 + sp.H_I * sp.d_I * 2 + sp.H_I * 4
+    return B * tot
+
+
+ROOFLINE_KERNELS = ("indexer_mfma<1, unsigned short> (1025 workgroups, with the top-k's chunk histograms), "
+                    "topk_split_h2, topk_split_emit")
+
+
 def bench_decode_1m(W: int, K: int, R: int, seed: int = 1005):
     n_pos = (W + K + R - 1) // R + 2
     log(f"building the 1M-context stack ({R} replicas, {n_pos} positions each)")
@@ -350,17 +386,23 @@ def bench_decode_1m(W: int, K: int, R: int, seed: int = 1005):
     torch.cuda.synchronize()
     log(f"built in {time.time() - t_build:.1f} s")
     ms, g = timed_graph_decode(stacks, W, K, None)
-    ind_ms = graph_kernel_ms(stacks, W, K, "indexer_score")
-    timing = ("HIP events on the launch stream around one graph replay of the timed steps' indexer launches "
-              "(back to back, same arguments and caches), divided by the launch count")
-    vis = (T0_1M + 1) // 4
-    nbytes = indexer_bytes(vis, 1)
-    achieved = nbytes / (ind_ms * 1e-3) / 1e9
     del g
-    return dict(ms=ms, ms_per_step=ms / K, tokens_per_s=K / (ms * 1e-3), indexer_ms=ind_ms,
-                roofline=dict(kernel="indexer_score", bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS,
-                              unit="GB/s", frac=achieved / HBM_PEAK_GBS, traffic=measured_traffic(),
-                              bytes_per_launch=nbytes, launch_ms=ind_ms, timing=timing)), stacks
+    # the dominant decode call, as the step runs it: the CSA layer's fused indexer + top-k
+    call_ms = graph_kernel_ms(stacks, W, K, "indexer_topk")
+    timing = ("HIP events on the launch stream around one graph replay of the timed steps' indexer_topk calls "
+              "(the step's own arguments and caches, replicas rotating, back to back), divided by the call count")
+    vis = (T0_1M + 1) // 4
+    nbytes = indexer_topk_bytes(vis, 1, 2048)
+    achieved = nbytes / (call_ms * 1e-3) / 1e9
+    step_bytes = decode_step_bytes(STACK_SPECS, T0_1M)
+    step_gbs = step_bytes / (ms / K * 1e-3) / 1e9
+    return dict(ms=ms, ms_per_step=ms / K, tokens_per_s=K / (ms * 1e-3), indexer_ms=call_ms,
+                step_hbm=dict(bytes_per_step=step_bytes, gbs=step_gbs, frac=step_gbs / HBM_PEAK_GBS),
+                roofline=dict(kernel="indexer_topk", kernels=ROOFLINE_KERNELS, bound="hbm", achieved=achieved,
+                              peak=HBM_PEAK_GBS, unit="GB/s", frac=achieved / HBM_PEAK_GBS,
+                              traffic=measured_traffic(), bytes_per_launch=nbytes,
+                              staged_bytes_per_launch=staged_score_bytes(vis, 1), launch_ms=call_ms,
+                              timing=timing)), stacks
 
 
 def _per_slot_pages(streams, n_tokens: int, page: int) -> int:
@@ -500,6 +542,54 @@ def score_recall(stack: Stack, keys_bf16: lca.KV, keys_fp4: lca.KV, rows: int, k
     return float(np.mean(r16)), float(np.mean(r4))
 
 
+def bench_topk_precision(stack: Stack, rows: int = 8, k: int = 2048, reps: int = 5):
+    """The selector on f32 against bf16 index scores of the same 1M decode rows ("DeepSeek-V4 中文翻译"
+    section 5.2.1 reports BF16 scores making the top-k selector 2x faster at 99.7 % recall): the
+    library's topk_select on each, timed over a graph of the rows' calls; recall of the bf16 selections
+    against the f32 ones."""
+    li = [i for i, sp in enumerate(stack.specs) if sp.kind == "csa"][0]
+    layer = stack.layers[li]
+    cap = layer.keys.cap
+    ts = [stack.t0 + j for j in range(rows)]
+    s32 = [torch.empty(1, 1, cap, dtype=torch.float32, device="cuda") for _ in ts]
+    s16 = [torch.empty(1, 1, cap, dtype=torch.bfloat16, device="cuda") for _ in ts]
+    i32 = [torch.empty(1, 1, k, dtype=torch.int32, device="cuda") for _ in ts]
+    i16 = [torch.empty(1, 1, k, dtype=torch.int32, device="cuda") for _ in ts]
+    ws = torch.zeros(max(16, lca.topk_workspace_size(1, 1, cap, k)), dtype=torch.uint8, device="cuda")
+    for j, t in enumerate(ts):
+        qi, w = stack.qi[li][j], stack.w[li][j]
+        lca.indexer_score(qi, w, layer.keys.nope, s32[j], q_pos=t, m=4)
+        lca.indexer_score(qi, w, layer.keys.nope, s16[j], q_pos=t, m=4)
+    out = {}
+    for name, sc, ix in (("f32", s32, i32), ("bf16", s16, i16)):
+        calls = [lambda j=j, t=t: lca.topk_select(sc[j], ix[j], q_pos=t, m=4, ws=ws) for j, t in enumerate(ts)]
+        for fn in calls:
+            fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                for fn in calls:
+                    fn()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        out[f"{name}_ms"] = e0.elapsed_time(e1) / (reps * len(calls))
+        del g
+    rec = np.mean([len(set(host_list(a)) & set(host_list(b))) / k for a, b in zip(i32, i16)])
+    out.update(speedup=out["f32_ms"] / out["bf16_ms"], recall_bf16_vs_f32=float(rec), rows=rows, keys=cap,
+               schedules="bf16: three launches over 16,384-key chunks; f32: one 1,024-thread workgroup per row")
+    return out
+
+
+def host_list(t: torch.Tensor) -> list:
+    return [int(x) for x in t.flatten().tolist() if x >= 0]
+
+
 def bench_decode_1m_mxfp4(stacks, W: int, K: int, recall: bool = True):
     """The same 1M decode with the CSA layer's indexer QK path in MXFP4 (keys stored MXFP4, each query
     head quantised in the indexer call); top-k recall against f32 scores on the benchmark's inputs."""
@@ -510,9 +600,11 @@ def bench_decode_1m_mxfp4(stacks, W: int, K: int, recall: bool = True):
     torch.cuda.synchronize()
     ms, g = timed_graph_decode(stacks, W, K, None)
     del g
-    ind_ms = graph_kernel_ms(stacks, W, K, "indexer_score")
+    call_ms = graph_kernel_ms(stacks, W, K, "indexer_topk")            # as the step runs it
+    ind_ms = graph_kernel_ms(stacks, W, K, "indexer_score", unfuse=True)  # the plain indexer kernel
     vis = (T0_1M + 1) // 4
     nbytes = vis * (64 + 4 + 2) + 16 * 128 * 2 + 16 * 4
+    call_bytes = indexer_topk_bytes(vis, 1, 2048, key_bytes=64 + 4)
     rows = min(16, len(stacks[0].qi[li]))
     rec = None
     if recall:
@@ -523,8 +615,11 @@ def bench_decode_1m_mxfp4(stacks, W: int, K: int, recall: bool = True):
         st.layers[li].keys, st.layers[li].spec = keys, spec
     gbs = nbytes / (ind_ms * 1e-3) / 1e9
     return dict(ms_per_step=ms / K, tokens_per_s=K / (ms * 1e-3),
+                indexer_topk=dict(launch_ms=call_ms, bytes=call_bytes, gbs=call_bytes / (call_ms * 1e-3) / 1e9,
+                                  frac=call_bytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS),
                 indexer=dict(launch_ms=ind_ms, bytes=nbytes, gbs=gbs, frac=gbs / HBM_PEAK_GBS,
-                             traffic=measured_traffic(MXFP4_TRAFFIC_FILE)),
+                             traffic=measured_traffic(MXFP4_TRAFFIC_FILE),
+                             note="the plain indexer kernel (indexer_score_mxfp4) on the step's arguments"),
                 recall_top2048=rec)
 
 
@@ -701,24 +796,94 @@ def bench_decode_c4(W: int, K: int, seed: int = 1004):
     log("building the 32 x 128K CSA decode state")
     st = Stack([spec], ["c4_csa"], B, t0, n_pos, 1, seed, win_cap=256)
     ms, g = timed_graph_decode([st], W, K, None)
-    ind_ms = graph_kernel_ms([st], W, K, "indexer_score")
     del g
+    call_ms = graph_kernel_ms([st], W, K, "indexer_topk")
+    ind_ms = graph_kernel_ms([st], W, K, "indexer_score", unfuse=True)
     vis = (t0 + 1) // 4
     nbytes = indexer_bytes(vis, B)
+    call_bytes = indexer_topk_bytes(vis, B, 1024)
     gbs = nbytes / (ind_ms * 1e-3) / 1e9
-    step_bytes = nbytes + B * (1024 + 128) * 656 + B * 64 * C * 2 * 2
+    step_bytes = decode_step_bytes([spec], t0, B)
+    step_gbs = step_bytes / (ms / K * 1e-3) / 1e9
     # the same decode with the indexer's QK path in MXFP4 (keys re-stored as MXFP4 by the compressor)
     keys_to_mxfp4(st.layers[0])
     torch.cuda.synchronize()
     ms4, g = timed_graph_decode([st], W, K, None)
-    ind4 = graph_kernel_ms([st], W, K, "indexer_score")
     del g
+    call4 = graph_kernel_ms([st], W, K, "indexer_topk")
+    ind4 = graph_kernel_ms([st], W, K, "indexer_score", unfuse=True)
     b4 = B * (vis * (64 + 4 + 2) + 16 * 128 * 2 + 16 * 4)
     return dict(batch=B, ctx=t0, ms_per_step=ms / K, tokens_per_s=B * K / (ms * 1e-3),
-                step_hbm_gbs=step_bytes / (ms / K * 1e-3) / 1e9,
-                indexer=dict(launch_ms=ind_ms, gbs=gbs, frac=gbs / HBM_PEAK_GBS, bytes=nbytes),
-                mxfp4_indexer=dict(ms_per_step=ms4 / K, tokens_per_s=B * K / (ms4 * 1e-3), launch_ms=ind4,
-                                   bytes=b4, gbs=b4 / (ind4 * 1e-3) / 1e9))
+                step_hbm=dict(bytes_per_step=step_bytes, gbs=step_gbs, frac=step_gbs / HBM_PEAK_GBS),
+                indexer_topk=dict(launch_ms=call_ms, bytes=call_bytes, gbs=call_bytes / (call_ms * 1e-3) / 1e9,
+                                  frac=call_bytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS),
+                indexer=dict(launch_ms=ind_ms, gbs=gbs, frac=gbs / HBM_PEAK_GBS, bytes=nbytes,
+                             note="the plain indexer kernel (indexer_score) on the step's arguments"),
+                mxfp4_indexer=dict(ms_per_step=ms4 / K, tokens_per_s=B * K / (ms4 * 1e-3), indexer_topk_ms=call4,
+                                   launch_ms=ind4, bytes=b4, gbs=b4 / (ind4 * 1e-3) / 1e9))
+
+
+def compress_bytes(n_rows: int, m: int, overlap: int, c: int, fmt: int, in_b: int = 2) -> tuple[int, int]:
+    """(algorithmic bytes, entries) of one compressor launch over n_rows raw rows (plus the m rows of the
+    previous block when overlapping): C and Z of each row read once (and C_b, Z_b), the bias rows and
+    gamma, each entry written once."""
+    n_in = n_rows + (m if overlap else 0)
+    entries = n_rows // m
+    row_out = {lca.FP8: 512 + 128 + 16, lca.BF16: 2 * c, lca.F32: 4 * c}[fmt]
+    streams = 4 if overlap else 2
+    return streams * n_in * c * in_b + (2 if overlap else 1) * m * c * 4 + c * 4 + entries * row_out, entries
+
+
+def bench_compressor(seed: int = 1007):
+    """The compressor's launches timed alone (rows from HBM): an HCA layer's 65,536-token prefill (m' = 128,
+    512 entries, bf16 storage), and the 4096-token chunk at 1M of a CSA layer (m = 4 with overlap, 1,024 fp8
+    entries) and of an HCA layer (32 fp8 entries).  Each launch reads its own copy of the inputs, the copies
+    rotating through more than the 256 MB Infinity Cache; HIP events around a graph of the launches."""
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    out = {}
+    cases = [("hca_prefill_65536", 65536, 128, 0, lca.BF16, 0),
+             ("csa_chunk_4096", 4096, 4, 1, lca.FP8, T0_1M),
+             ("hca_chunk_4096", 4096, 128, 0, lca.FP8, T0_1M)]
+    for name, n, m, ov, fmt, p0 in cases:
+        nbytes, entries = compress_bytes(n, m, ov, C, fmt)
+        n_in = n + (m if ov else 0)
+        copies = max(3, -(-(320 << 20) // max(1, nbytes)))
+        streams = []
+        for _ in range(copies):
+            x = (torch.randn(4 if ov else 2, 1, n_in, C, device="cuda", generator=gen)).to(torch.bfloat16)
+            streams.append(x)
+        ba = torch.randn(m, C, device="cuda", generator=gen) * 0.5
+        bb = torch.randn(m, C, device="cuda", generator=gen) * 0.5
+        gamma = 1.0 + 0.1 * torch.randn(C, device="cuda", generator=gen)
+        cap = (p0 + n) // m + 2
+        kv = lca.KV.empty(fmt, 1, cap, 512, 64)
+        first = p0 - (m if ov else 0)
+
+        def launch(x):
+            lca.kv_compress(x[0], x[1], x[2] if ov else None, x[3] if ov else None, kv, m=m, overlap=ov,
+                            first_pos=first, bias_a=ba, bias_b=bb if ov else None, gamma=gamma, rope_theta=1e4)
+
+        for x in streams[:2]:
+            launch(x)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for x in streams:
+                launch(x)
+        g.replay()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        g.replay()
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / len(streams)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = dict(rows=n, m=m, overlap=ov, entries=entries, storage={lca.FP8: "fp8", lca.BF16: "bf16"}[fmt],
+                         bytes=nbytes, launch_ms=ms, gbs=gbs, hbm_frac=gbs / HBM_PEAK_GBS, copies=len(streams))
+        del g, streams, kv
+        torch.cuda.empty_cache()
+    return out
 
 
 def bench_projections(reps: int = 5, seed: int = 1006):
@@ -777,9 +942,10 @@ def bench_projections(reps: int = 5, seed: int = 1006):
 # CPU baseline: the fp64 oracle on a bounded sample of the 1M decode workload
 # ----------------------------------------------------------------------------
 
-def cpu_baseline(n_steps: int = 4, seed: int = 1005):
+def _cpu_sample(seed: int, n_steps: int, start_barrier=None):
+    """One oracle copy of the 1M stack (random stored cache bytes of the benchmark's shapes) decoding n_steps
+    tokens; returns the seconds of the decode steps alone."""
     import oracle as orc
-    log(f"cpu baseline: oracle, {n_steps} decode steps of the 1M stack")
     t0 = T0_1M
     g = S.stream(seed, "cpu/bytes")
 
@@ -800,14 +966,15 @@ def cpu_baseline(n_steps: int = 4, seed: int = 1005):
             d["keys"] = S.to_bf16(g.standard_normal((1, cap, 128)).astype(np.float32))
         d["raw"] = [S.to_bf16(S.activations(seed, f"cpu/{tag}/{n}", (1, 2 * spec.m + n_steps, C)))
                     for n in ("ca", "za", "cb", "zb")]
-        d["iraw"] = [S.to_bf16(S.activations(seed, f"cpu/{tag}/i{n}", (1, 2 * spec.m + n_steps, 128)))
-                     for n in ("ca", "za", "cb", "zb")]
         layers.append(d)
     q = S.to_bf16(S.normal(seed, "cpu/q", (1, 1, 64, C)))
     qi = S.to_bf16(S.normal(seed, "cpu/qi", (1, 1, 16, 128)))
     w = S.normal(seed, "cpu/w", (1, 1, 16), 0.25)
     sink = S.normal(seed, "cpu/sink", (64,))
     gamma = np.ones(C, np.float32)
+    orc.lib()
+    if start_barrier is not None:
+        start_barrier.wait()
     start = time.perf_counter()
     for j in range(n_steps):
         t = t0 + j
@@ -831,12 +998,52 @@ def cpu_baseline(n_steps: int = 4, seed: int = 1005):
             else:
                 orc.attention(q, q_pos=[t], comp=d["comp"], m=128, idx=None, win=d["win"], n_win=128, sink=sink,
                               sm_scale=C ** -0.5, rope_theta=1e4, out_fmt=orc.BF16)
-    el = time.perf_counter() - start
-    return dict(value=n_steps / el, unit="tokens/s", cores=1, kind="oracle",
+    return time.perf_counter() - start
+
+
+def _cpu_proc(seed: int, n_steps: int, barrier, results):
+    try:
+        results.put((seed, _cpu_sample(seed, n_steps, barrier)))
+    except BaseException as e:  # (reported by the parent; the barrier is broken so no copy waits forever)
+        barrier.abort()
+        results.put((seed, repr(e)))
+
+
+def cpu_baseline(n_steps: int = 4, seed: int = 1005, max_workers: int = 16):
+    """The fp64 oracle on the host: one copy of the 1M stack per host core (at most max_workers), each
+    decoding n_steps tokens in its own process (the oracle works one query row at a time, so a decode row
+    keeps one core busy); tokens/s = copies x n_steps / the slowest copy's decode time.  The copies start
+    their decode steps together (a barrier after building their caches)."""
+    import multiprocessing as mp
+    n = max(1, min(max_workers, os.cpu_count() or 1))
+    log(f"cpu baseline: oracle, {n} copies x {n_steps} decode steps of the 1M stack")
+    ctx = mp.get_context("spawn")
+    env_prev = os.environ.get("OMP_NUM_THREADS")
+    os.environ["OMP_NUM_THREADS"] = "1"          # (one row per oracle call: one thread each)
+    try:
+        barrier = ctx.Barrier(n, timeout=900)
+        results = ctx.Queue()
+        procs = [ctx.Process(target=_cpu_proc, args=(seed + i, n_steps, barrier, results)) for i in range(n)]
+        for pr in procs:
+            pr.start()
+        got = [results.get(timeout=1800) for _ in procs]
+        for pr in procs:
+            pr.join()
+    finally:
+        if env_prev is None:
+            os.environ.pop("OMP_NUM_THREADS", None)
+        else:
+            os.environ["OMP_NUM_THREADS"] = env_prev
+    bad = [v for _, v in got if isinstance(v, str)]
+    if bad:
+        raise RuntimeError(f"cpu baseline copy failed: {bad[0]}")
+    els = [v for _, v in got]
+    el = max(els)
+    return dict(value=n * n_steps / el, unit="tokens/s", cores=n, kind="oracle",
                 host=dict(cpu=host_cpu(), nproc=os.cpu_count()),
-                sample=f"{n_steps} decode steps of the 1M-context 4-layer stack (fp64 oracle; one query row "
-                       f"per call, so one host thread does the work); {el:.1f} s; random stored cache bytes of "
-                       f"the benchmark's shapes")
+                sample=f"{n} oracle copies of the 1M-context 4-layer stack, one per host core, each decoding "
+                       f"{n_steps} tokens (fp64; random stored cache bytes of the benchmark's shapes); slowest "
+                       f"copy {el:.1f} s, fastest {min(els):.1f} s")
 
 
 # ----------------------------------------------------------------------------
@@ -876,8 +1083,9 @@ def main():
     d = bench_decode_1m(W, K, R)
     res, stacks = d
     res["roofline"]["copy_ceiling_gbs"] = copy_ceiling_gbs()
-    log(f"1M decode: {res['ms_per_step'] * 1e3:.1f} us/step, {res['tokens_per_s']:.0f} tok/s; indexer "
-        f"{res['indexer_ms'] * 1e3:.1f} us = {res['roofline']['achieved']:.0f} GB/s")
+    log(f"1M decode: {res['ms_per_step'] * 1e3:.1f} us/step, {res['tokens_per_s']:.0f} tok/s, "
+        f"{res['step_hbm']['gbs']:.0f} GB/s over the step ({100 * res['step_hbm']['frac']:.1f} % of HBM peak); "
+        f"indexer + top-k {res['indexer_ms'] * 1e3:.1f} us = {res['roofline']['achieved']:.0f} GB/s")
     extra = {}
     if not args.no_extra or args.mxfp4:
         f4 = bench_decode_1m_mxfp4(stacks, W, K, recall=not args.no_extra)
@@ -887,6 +1095,11 @@ def main():
             log(f"top-2048 recall vs f32 scores: bf16 {f4['recall_top2048']['bf16_scores_vs_f32']:.4f}, MXFP4 QK "
                 f"{f4['recall_top2048']['mxfp4_qk_vs_f32']:.4f}")
         extra["decode_1m_mxfp4_indexer"] = f4
+    if not args.no_extra:
+        tp = bench_topk_precision(stacks[0])
+        log(f"top-2048 selector on the same 1M rows: f32 scores {tp['f32_ms'] * 1e3:.1f} us, bf16 "
+            f"{tp['bf16_ms'] * 1e3:.1f} us ({tp['speedup']:.1f}x), recall {tp['recall_bf16_vs_f32']:.4f}")
+        extra["topk_bf16_vs_f32_scores"] = tp
     if not args.no_extra or args.paged:
         pf = None
         if not args.no_extra:
@@ -908,6 +1121,10 @@ def main():
                 f"{r['tflops']:.0f} TFLOP/s ({100 * r['mfma_frac']:.1f} % of the bf16 MFMA peak)")
             extra[f"prefill_{kind}_{T}"] = r
             torch.cuda.empty_cache()
+        cp = bench_compressor()
+        log("compressor: " + ", ".join(f"{k} {v['launch_ms'] * 1e3:.1f} us = {v['gbs']:.0f} GB/s" for k, v in cp.items()))
+        extra["compressor"] = cp
+        torch.cuda.empty_cache()
         pj = bench_projections()
         log(f"layer projections: 4096-token chunk {pj['T4096']['total']['ms']:.2f} ms "
             f"({pj['T4096']['total']['tflops']:.0f} TFLOP/s), one decode token {pj['T1']['total']['ms'] * 1e3:.1f} us "
@@ -926,6 +1143,7 @@ def main():
                    "kv": "fp8-e4m3 (pow2 scale / 128 dims) + bf16 rope", "indexer": "16x128 bf16, bf16 scores",
                    "replicas": R, "parallelism": "single GPU"},
         "roofline": res["roofline"],
+        "step_hbm": res["step_hbm"],
         "cpu_baseline": cpu,
         "extra": extra,
     }

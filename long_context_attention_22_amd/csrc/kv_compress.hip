@@ -6,11 +6,12 @@
 // per 32 dims).
 //
 // HBM-bound: every input element is read exactly once.  One workgroup per
-// (entry, sequence); thread j owns channel j, so each wave reads 64
-// consecutive channels of a row (one 128-byte line for bf16).  Pooling is an
-// online softmax over the block's rows, eight rows in flight at a time.  The
-// per-entry reductions (RMS, fp8 group max) and the RoPE pair exchange go
-// through LDS.
+// (entry, sequence).  bf16 inputs: each lane reads 16 bytes (8 channels) of a
+// row, eight row slots side by side, each an online softmax over its share of
+// the block's rows, merged through LDS (kv_pool_wide); other inputs: thread j
+// owns channel j and walks the rows (kv_compress_kernel).  Then thread j owns
+// channel j: the per-entry reductions (RMS, fp8 group max) and the RoPE pair
+// exchange go through LDS.
 #include "device.h"
 #include "kernels.h"
 #include "rowstore.h"
@@ -52,36 +53,15 @@ __device__ __forceinline__ void pool_rows(const T* zp, const T* cp, const float*
     }
 }
 
-template <typename T, int FMT>
-__global__ void __launch_bounds__(1024) kv_compress_kernel(CompressArgs a) {
-    const int b = blockIdx.y;
+// The rest of an entry once its pooled value y of channel j (thread j < c) is known: RMSNorm over all
+// c dims, RoPE at position s m, the store.  red: 16 floats of LDS, ys: 1024.
+template <int FMT>
+__device__ __forceinline__ void finish_entry(const CompressArgs& a, float y, int b, int64_t s, float* red, float* ys) {
     const int m = a.m;
-    const int64_t p0 = a.first_pos.v[b];
-    const int64_t s = a.s_lo.v[b] + blockIdx.x;
-    const int64_t s_hi = (p0 + a.n_rows) / m;
-    if (s >= s_hi) return;  // uniform over the workgroup
-
     const int d_nope = a.out.d_nope, d_rope = a.out.d_rope;
     const int c = d_nope + d_rope;
     const int j = threadIdx.x;
     const int lane = j & 63, wv = j >> 6;
-    __shared__ float red[16];
-    __shared__ float ys[1024];
-
-    float y = 0.0f;
-    if (j < c) {
-        float mx = -INFINITY, den = 0.0f, num = 0.0f;
-        const int64_t ra = (int64_t)b * a.in_stride + (s * m - p0);
-        pool_rows<T>((const T*)a.z_a + ra * c + j, (const T*)a.c_a + ra * c + j,
-                     a.bias_a ? a.bias_a + j : nullptr, m, c, mx, den, num);
-        if (a.overlap && s >= 1) {
-            const int64_t rb = ra - m;
-            pool_rows<T>((const T*)a.z_b + rb * c + j, (const T*)a.c_b + rb * c + j,
-                         a.bias_b ? a.bias_b + j : nullptr, m, c, mx, den, num);
-        }
-        y = num / den;
-    }
-
     if (a.gamma) {  // RMSNorm over all c dims
         float ss = wave_sum(y * y);
         if (lane == 0) red[wv] = ss;
@@ -138,6 +118,144 @@ __global__ void __launch_bounds__(1024) kv_compress_kernel(CompressArgs a) {
         if (j < d_nope) ((float*)a.out.nope)[row * d_nope + j] = y;
         else if (j < c) ((float*)a.out.rope)[row * d_rope + (j - d_nope)] = y;
     }
+}
+
+// One workgroup per (entry, sequence), thread j = channel j: the pooling walks the block's rows one
+// channel per thread (any input type and width).
+template <typename T, int FMT>
+__global__ void __launch_bounds__(1024) kv_compress_kernel(CompressArgs a) {
+    const int b = blockIdx.y;
+    const int m = a.m;
+    const int64_t p0 = a.first_pos.v[b];
+    const int64_t s = a.s_lo.v[b] + blockIdx.x;
+    const int64_t s_hi = (p0 + a.n_rows) / m;
+    if (s >= s_hi) return;  // uniform over the workgroup
+    const int c = a.out.d_nope + a.out.d_rope;
+    const int j = threadIdx.x;
+    __shared__ float red[16];
+    __shared__ float ys[1024];
+    float y = 0.0f;
+    if (j < c) {
+        float mx = -INFINITY, den = 0.0f, num = 0.0f;
+        const int64_t ra = (int64_t)b * a.in_stride + (s * m - p0);
+        pool_rows<T>((const T*)a.z_a + ra * c + j, (const T*)a.c_a + ra * c + j,
+                     a.bias_a ? a.bias_a + j : nullptr, m, c, mx, den, num);
+        if (a.overlap && s >= 1) {
+            const int64_t rb = ra - m;
+            pool_rows<T>((const T*)a.z_b + rb * c + j, (const T*)a.c_b + rb * c + j,
+                         a.bias_b ? a.bias_b + j : nullptr, m, c, mx, den, num);
+        }
+        y = num / den;
+    }
+    finish_entry<FMT>(a, y, b, s, red, ys);
+}
+
+// bf16 inputs, c a multiple of 8 (at most kPoolMaxC): the block's rows are read 16 bytes (8 channels) per
+// lane.  Thread t = (row slot rs = t / (c / 8), chunk ch = t % (c / 8)) pools channels 8 ch .. 8 ch + 7
+// over the rows rs, rs + kPoolSlots, ... of the entry's row list (the a-block's m rows, then the
+// b-block's m rows when overlapping), kPoolRows rows' loads (C, Z and the bias rows) in flight at a time,
+// as an online softmax per channel; the kPoolSlots partial states (max, sum, weighted sum) of a
+// channel are merged through LDS in slot order, then thread j < c finishes channel j as above.  Each
+// wave moves 1 KB per load instruction instead of 128 bytes, and a row is read by c / 8 lanes side by
+// side.
+constexpr int kPoolSlots = 8;
+constexpr int kPoolRows = 6;    // rows whose loads a thread has in flight at once (registers: 16 each)
+constexpr int kPoolMaxC = 576;  // (the merge's LDS: 3 x 8 x 576 floats, so two workgroups fit a CU)
+template <int FMT>
+__global__ void __launch_bounds__(kPoolMaxC) kv_pool_wide(CompressArgs a) {
+    const int b = blockIdx.y;
+    const int m = a.m;
+    const int64_t p0 = a.first_pos.v[b];
+    const int64_t s = a.s_lo.v[b] + blockIdx.x;
+    const int64_t s_hi = (p0 + a.n_rows) / m;
+    if (s >= s_hi) return;  // uniform over the workgroup
+    const int c = a.out.d_nope + a.out.d_rope;
+    const int nch = c >> 3;
+    const int t = threadIdx.x;
+    const int rs = t / nch, ch = t - rs * nch;
+    __shared__ float red[16];
+    __shared__ float ys[1024];
+    __shared__ float st[3][kPoolSlots][kPoolMaxC];  // reference, sum, weighted sum of (slot, channel)
+    const int L = (a.overlap && s >= 1) ? 2 * m : m;  // rows of the entry's list
+    const int64_t ra = (int64_t)b * a.in_stride + (s * m - p0);  // the a-block's first row
+    float mx[8], den[8], num[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        mx[i] = -INFINITY;
+        den[i] = 0.0f;
+        num[i] = 0.0f;
+    }
+    for (int k0 = rs; k0 < L; k0 += kPoolRows * kPoolSlots) {
+        u32x4 zc[kPoolRows][2];
+        f32x4 bs[kPoolRows][2];
+        bool ok[kPoolRows];
+#pragma unroll
+        for (int u = 0; u < kPoolRows; ++u) {
+            const int k = k0 + u * kPoolSlots;
+            ok[u] = k < L;
+            // b-block row k - m (block s - 1); a slot past the list reads the a-block's first row (in
+            // range, dropped below)
+            const bool bb = ok[u] && k >= m;
+            const int i = ok[u] ? (bb ? k - m : k) : 0;
+            const int64_t row = ra + (bb ? i - m : i);
+            const uint16_t* zp = (const uint16_t*)(bb ? a.z_b : a.z_a) + row * c + 8 * ch;
+            const uint16_t* cp = (const uint16_t*)(bb ? a.c_b : a.c_a) + row * c + 8 * ch;
+            const float* bp = bb ? a.bias_b : a.bias_a;
+            zc[u][0] = *(const u32x4*)zp;
+            zc[u][1] = *(const u32x4*)cp;
+            if (bp) {
+                bs[u][0] = *(const f32x4*)(bp + (int64_t)i * c + 8 * ch);
+                bs[u][1] = *(const f32x4*)(bp + (int64_t)i * c + 8 * ch + 4);
+            } else {
+                bs[u][0] = bs[u][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kPoolRows; ++u) {
+            if (!ok[u]) continue;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t zw = zc[u][0][i >> 1], cw = zc[u][1][i >> 1];
+                const float z = __uint_as_float((i & 1) ? (zw & 0xffff0000u) : (zw << 16)) + bs[u][i >> 2][i & 3];
+                const float cv = __uint_as_float((i & 1) ? (cw & 0xffff0000u) : (cw << 16));
+                // lazy rescaling: the reference moves only when a logit exceeds it by more than 16
+                // (weights stay <= e^16), so most rows cost one exponential instead of two
+                if (z > mx[i] + 16.0f) {
+                    const float corr = __expf(mx[i] - z);  // (reference -inf: 0)
+                    den[i] *= corr;
+                    num[i] *= corr;
+                    mx[i] = z;
+                }
+                const float e = __expf(z - mx[i]);
+                den[i] += e;
+                num[i] = fmaf(e, cv, num[i]);
+            }
+        }
+    }
+    if (rs < kPoolSlots) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            st[0][rs][8 * ch + i] = mx[i];
+            st[1][rs][8 * ch + i] = den[i];
+            st[2][rs][8 * ch + i] = num[i];
+        }
+    }
+    __syncthreads();
+    float y = 0.0f;
+    if (t < c) {  // merge the slots of channel t, in slot order
+        float M = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < kPoolSlots; ++r) M = fmaxf(M, st[0][r][t]);
+        float dn = 0.0f, nu = 0.0f;
+#pragma unroll
+        for (int r = 0; r < kPoolSlots; ++r) {
+            const float w = st[0][r][t] == -INFINITY ? 0.0f : __expf(st[0][r][t] - M);
+            dn = fmaf(st[1][r][t], w, dn);
+            nu = fmaf(st[2][r][t], w, nu);
+        }
+        y = nu / dn;
+    }
+    finish_entry<FMT>(a, y, b, s, red, ys);
 }
 
 // m = 1 (the window / state-cache store, [R] 2.3.3 and 3.5.1): the softmax over one position is 1,
@@ -211,6 +329,16 @@ hipError_t launch_kv_compress(const CompressArgs& a, hipStream_t st) {
                 if (bf) launch_store_rows<uint16_t, LCA_FP8>(a, c, grid, st);
                 else launch_store_rows<float, LCA_FP8>(a, c, grid, st);
                 break;
+        }
+        return hipGetLastError();
+    }
+    if (bf && c % 8 == 0 && c <= kPoolMaxC) {
+        const dim3 wblock((unsigned)(c / 8 * kPoolSlots));
+        switch (a.out.fmt) {
+            case LCA_F32: hipLaunchKernelGGL((kv_pool_wide<LCA_F32>), grid, wblock, 0, st, a); break;
+            case LCA_BF16: hipLaunchKernelGGL((kv_pool_wide<LCA_BF16>), grid, wblock, 0, st, a); break;
+            case LCA_MXFP4: hipLaunchKernelGGL((kv_pool_wide<LCA_MXFP4>), grid, wblock, 0, st, a); break;
+            default: hipLaunchKernelGGL((kv_pool_wide<LCA_FP8>), grid, wblock, 0, st, a); break;
         }
         return hipGetLastError();
     }
