@@ -24,7 +24,8 @@ F32, BF16, FP8, MXFP4 = 0, 1, 2, 3
 OK, EINVAL, ESHAPE, EDTYPE, EALIGN, EWORKSPACE, EHIP, ENOMEM = range(8)
 MAX_BATCH = 64
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblca.so")
+# (LCA_LIB names another build of the same sources, e.g. the host-sanitizer build the tests make)
+LIB_PATH = os.environ.get("LCA_LIB", os.path.join(_HERE, "liblca.so"))
 _lib = None
 
 

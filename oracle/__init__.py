@@ -23,11 +23,13 @@ _lib = None
 
 
 def lib():
+    """The built oracle library; LCA_ORACLE_LIB names another build of oracle.c (the sanitizer test)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB):
+        path = os.environ.get("LCA_ORACLE_LIB", _build.LIB)
+        if path == _build.LIB and not os.path.exists(path):
             _build.build()
-        _lib = C.CDLL(_build.LIB)
+        _lib = C.CDLL(path)
         _declare(_lib)
     return _lib
 
