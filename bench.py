@@ -646,17 +646,11 @@ def bench_prefill_1m(stack: Stack, reps: int = 20, T: int = 4096, seed: int = 10
         else:
             qis.append(None)
             ws.append(None)
-    # the chunk needs T rows of scores / idx and prefill-sized scratch
+    # the chunk needs T rows of scores / idx and prefill-sized workspaces
     for layer in stack.layers:
-        if layer.spec.kind == "csa" and layer.scores.shape[1] < T:
-            layer.scores = torch.empty(1, T, layer.comp.cap, dtype=torch.bfloat16, device="cuda")
-            layer.idx = torch.empty(1, T, layer.spec.k, dtype=torch.int32, device="cuda")
-        keys = (layer.spec.k if layer.spec.kind == "csa" else layer.comp.cap) + layer.spec.n_win
-        need = lca.attn_workspace_size(1, T, layer.spec.H, C, keys)
-        if need > layer.ws.numel():
-            layer.ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        layer.reserve_rows(T)
     outs = [torch.empty(1, T, s.H, C, dtype=torch.bfloat16, device="cuda") for s in stack.specs]
-    timers = {n: KernelTimer(n) for n in ("indexer_score", "topk_select", "csa_attn", "hca_attn")}
+    timers = {n: KernelTimer(n) for n in ("indexer_topk", "csa_attn", "hca_attn")}
 
     def rec(name, fn):
         if name in timers:
@@ -685,9 +679,19 @@ def bench_prefill_1m(stack: Stack, reps: int = 20, T: int = 4096, seed: int = 10
     chunk(record=rec)
     torch.cuda.synchronize()
     kt = {n: t.mean_ms() for n, t in timers.items() if t.pairs}
-    # the chunk's indexer call with the QK path in MXFP4 (same queries, keys re-stored as MXFP4)
+    # the chunk's CSA selection as separate calls (the indexer kernel alone: its MFMA fraction; the
+    # top-k with all its passes), on the same queries and keys
     li = [i for i, sp in enumerate(stack.specs) if sp.kind == "csa"][0]
     layer = stack.layers[li]
+    sep = {n: KernelTimer(n) for n in ("indexer_score", "topk_select")}
+    for _ in range(3):
+        sep["indexer_score"]("indexer_score", lambda: lca.indexer_score(qis[li], ws[li], layer.keys.nope,
+                                                                        layer.scores[:, :T], q_pos=stack.t0, m=4))
+        sep["topk_select"]("topk_select", lambda: lca.topk_select(layer.scores[:, :T], layer.idx[:, :T],
+                                                                  q_pos=stack.t0, m=4, ws=layer.topk_ws))
+    torch.cuda.synchronize()
+    kt.update({n: t.mean_ms() for n, t in sep.items()})
+    # the chunk's indexer call with the QK path in MXFP4 (same queries, keys re-stored as MXFP4)
     k4 = mxfp4_copy(layer.keys)
     f4 = KernelTimer("indexer_mxfp4")
     for _ in range(reps):
@@ -714,7 +718,7 @@ def bench_prefill_1m(stack: Stack, reps: int = 20, T: int = 4096, seed: int = 10
 
 def bench_prefill_single(kind: str, T: int, reps: int = 10, seed: int = 0):
     """A whole single-layer prefill from position 0 with bf16 storage: CSA at 8,192 tokens (window store,
-    compressor, indexer keys, indexer, top-512, attention) or HCA at 65,536 tokens (window store,
+    compressor, indexer keys, indexer + top-512 (one fused call), attention) or HCA at 65,536 tokens (window store,
     compressor, attention).  Inputs drawn on the GPU (N(0,1), 1 % of channels x20 in the compressor
     streams; w N(0,1)/4); median of reps, each after a cache-evicting write."""
     g = torch.Generator(device="cuda").manual_seed(seed)
@@ -748,7 +752,7 @@ def bench_prefill_single(kind: str, T: int, reps: int = 10, seed: int = 0):
         w = torch.randn(1, T, 16, device="cuda", generator=g) * 0.25
         sc = torch.empty(1, T, ncap, dtype=torch.bfloat16, device="cuda")
         idx = torch.empty(1, T, k, dtype=torch.int32, device="cuda")
-        tws = torch.empty(max(16, lca.topk_workspace_size(1, T, ncap, k)), dtype=torch.uint8, device="cuda")
+        tws = torch.zeros(max(16, lca.indexer_topk_workspace_size(1, T, ncap, k)), dtype=torch.uint8, device="cuda")
     aws = torch.empty(max(16, lca.attn_workspace_size(1, T, H, C, (k if kind == "csa" else ncap) + n_win)),
                       dtype=torch.uint8, device="cuda")
 
@@ -758,8 +762,7 @@ def bench_prefill_single(kind: str, T: int, reps: int = 10, seed: int = 0):
             lca.kv_compress(ca, za, cb, zb, comp, m=m, overlap=1, first_pos=0, bias_a=ba, bias_b=bb, gamma=gamma,
                             rope_theta=1e4)
             lca.kv_compress(ica, iza, icb, izb, keys, m=m, overlap=1, first_pos=0, bias_a=iba, bias_b=ibb)
-            lca.indexer_score(qi, w, keys.nope, sc, q_pos=0, m=m)
-            lca.topk_select(sc, idx, q_pos=0, m=m, ws=tws)
+            lca.indexer_topk(qi, w, keys.nope, sc, idx, q_pos=0, m=m, ws=tws)
             lca.csa_attn(q, out, q_pos=0, comp=comp, m=m, idx=idx, win=win, n_win=n_win, sink=sink,
                          sm_scale=C ** -0.5, rope_theta=1e4, ws=aws)
         else:

@@ -180,24 +180,25 @@ int lca_topk_select(const void* scores, int32_t score_dtype, int64_t s_stride, i
 size_t lca_topk_workspace_size(int32_t B, int32_t T, int64_t s_stride, int32_t k);
 
 /*
- * lca_indexer_topk -- lca_indexer_score followed by lca_topk_select for single-token rows (decode),
- * with the first pass of the top-k fused into the indexer.  [R] 2.3.1 (indexer, then top-k) and
- * 5.2.1 (bf16 scores).  For each sequence b the query row is position q_pos[b] (T = 1): scores
- * [B][1][s_stride] bf16 get the scores of lca_indexer_score (q, w, k bf16 as there; H_I = 16,
- * d_I = 128) and idx [B][1][k] int32 the selection of lca_topk_select on those scores, bit for bit.
- * When the rows are few and long (the top-k's split schedule) the indexer also builds the
- * high-byte histograms of each 16384-key chunk of the row, with device atomics, so the top-k
- * runs two launches instead of three and reads the scores once less.
- * ws: device workspace of lca_indexer_topk_workspace_size(B, s_stride, k) bytes (may be NULL when
- * that is 0).  It must be ZEROED BEFORE ITS FIRST USE and must not be shared with other calls
- * (lca_topk_select writes the same histograms without clearing them): every call leaves it zeroed
- * again, also inside a captured graph.  Errors as lca_indexer_score and lca_topk_select;
- * LCA_EWORKSPACE when ws is too small.
+ * lca_indexer_topk -- lca_indexer_score followed by lca_topk_select, with the top-k's first pass
+ * fused into the indexer.  [R] 2.3.1 (indexer, then top-k) and 5.2.1 (bf16 scores).  For each
+ * sequence b the query rows are positions q_pos[b] .. q_pos[b] + T - 1: scores [B][T][s_stride]
+ * bf16 get the scores of lca_indexer_score (q, w, k bf16 as there; H_I = 16, d_I = 128) and idx
+ * [B][T][k] int32 the selection of lca_topk_select on those scores, bit for bit.  While it stores
+ * the scores, the indexer also counts their high bytes (the top-k's first radix digit) with LDS and
+ * device atomics: per row and 16384-key chunk when the rows are few and long (the top-k's split
+ * schedule: its last two launches run), else per row (its row schedule: each row's workgroup skips
+ * the first of its passes over the scores).
+ * ws: device workspace of lca_indexer_topk_workspace_size(B, T, s_stride, k) bytes.  It must be
+ * ZEROED BEFORE ITS FIRST USE and must not be shared with other calls (lca_topk_select writes the
+ * same histograms without clearing them): every call leaves it zeroed again, also inside a captured
+ * graph.  Errors as lca_indexer_score and lca_topk_select; LCA_EWORKSPACE when ws is NULL or too
+ * small.
  */
 int lca_indexer_topk(const void* q, const float* w, const void* k, int64_t k_cap, int32_t H_I, int32_t d_I,
-                     int32_t B, const int64_t* q_pos, int32_t m, void* scores, int64_t s_stride, int32_t topk,
-                     int32_t* idx, void* ws, size_t ws_bytes, void* stream);
-size_t lca_indexer_topk_workspace_size(int32_t B, int64_t s_stride, int32_t k);
+                     int32_t B, int32_t T, const int64_t* q_pos, int32_t m, void* scores, int64_t s_stride,
+                     int32_t topk, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+size_t lca_indexer_topk_workspace_size(int32_t B, int32_t T, int64_t s_stride, int32_t k);
 
 /*
  * lca_indexer_topk_mxfp4 -- the same fused call with the QK path in MXFP4 ([R] 5.2.1): the scores
@@ -205,7 +206,7 @@ size_t lca_indexer_topk_workspace_size(int32_t B, int64_t s_stride, int32_t k);
  * lca_topk_select on them, with the same workspace (lca_indexer_topk_workspace_size) and rules.
  */
 int lca_indexer_topk_mxfp4(const void* q, const float* w, lca_kv k, int32_t H_I, int32_t d_I, int32_t B,
-                           const int64_t* q_pos, int32_t m, void* scores, int64_t s_stride, int32_t topk,
+                           int32_t T, const int64_t* q_pos, int32_t m, void* scores, int64_t s_stride, int32_t topk,
                            int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
 /*

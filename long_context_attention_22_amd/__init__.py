@@ -72,9 +72,9 @@ def lib():
                                           vp, f32, f64, vp, i32, vp, vp, sz, vp]
         L.lca_linear.argtypes = [vp, i64, i64, vp, i64, i64, vp, i32, i64, i64, i32, i32, i32, i32, vp]
         L.lca_grouped_out_proj.argtypes = [vp, i32, i32, i32, i32, vp, i32, vp, i32, vp, vp, i32, vp]
-        L.lca_indexer_topk.argtypes = [vp, vp, vp, i64, i32, i32, i32, vp, i32, vp, i64, i32, vp, vp, sz, vp]
-        L.lca_indexer_topk_mxfp4.argtypes = [vp, vp, _KV, i32, i32, i32, vp, i32, vp, i64, i32, vp, vp, sz, vp]
-        L.lca_indexer_topk_workspace_size.argtypes = [i32, i64, i32]
+        L.lca_indexer_topk.argtypes = [vp, vp, vp, i64, i32, i32, i32, i32, vp, i32, vp, i64, i32, vp, vp, sz, vp]
+        L.lca_indexer_topk_mxfp4.argtypes = [vp, vp, _KV, i32, i32, i32, i32, vp, i32, vp, i64, i32, vp, vp, sz, vp]
+        L.lca_indexer_topk_workspace_size.argtypes = [i32, i32, i64, i32]
         L.lca_indexer_topk_workspace_size.restype = sz
         L.lca_attn_workspace_size.argtypes = [i32, i32, i32, i32, i64]
         L.lca_attn_workspace_size.restype = sz
@@ -207,30 +207,30 @@ def topk_select(scores, idx, *, q_pos, m: int, ws=None, stream=None):
 
 
 def indexer_topk(q, w, k, scores, idx, *, q_pos, m: int, ws=None, stream=None):
-    """Decode rows (T = 1): indexer_score then topk_select, the top-k's first pass fused into the indexer.
-    q [B][1][16][128] bf16, w [B][1][16] f32 or None, k [B][k_cap][128] bf16, scores [B][1][s_stride] bf16,
-    idx [B][1][k] int32; ws: indexer_topk_workspace_size bytes, zeroed before its first use and kept for
-    this call only (every call leaves it zeroed)."""
+    """indexer_score then topk_select, the top-k's first pass fused into the indexer.  q [B][T][16][128]
+    bf16, w [B][T][16] f32 or None, k [B][k_cap][128] bf16, scores [B][T][s_stride] bf16, idx [B][T][k]
+    int32; ws: indexer_topk_workspace_size(B, T, s_stride, k) bytes, zeroed before its first use and kept
+    for this call only (every call leaves it zeroed)."""
     _dense(("q", q), ("w", w), ("scores", scores), ("idx", idx))
-    B = q.shape[0]
+    B, T = q.shape[0], q.shape[1]
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().lca_indexer_topk(_ptr(q), _ptr(w), _ptr(k), int(k.shape[1]), int(q.shape[2]), int(q.shape[3]),
-                                  int(B), _pos(q_pos, B), int(m), _ptr(scores), int(scores.shape[2]),
+                                  int(B), int(T), _pos(q_pos, B), int(m), _ptr(scores), int(scores.shape[2]),
                                   int(idx.shape[2]), _ptr(idx), _ptr(ws), nbytes, _stream(stream)))
 
 
 def indexer_topk_mxfp4(q, w, k: KV, scores, idx, *, q_pos, m: int, ws=None, stream=None):
     """indexer_topk with MXFP4 keys (k: KV with fmt MXFP4; q bf16, quantised in the call)."""
     _dense(("q", q), ("w", w), ("scores", scores), ("idx", idx))
-    B = q.shape[0]
+    B, T = q.shape[0], q.shape[1]
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib().lca_indexer_topk_mxfp4(_ptr(q), _ptr(w), k.c(), int(q.shape[2]), int(q.shape[3]), int(B),
+    _check(lib().lca_indexer_topk_mxfp4(_ptr(q), _ptr(w), k.c(), int(q.shape[2]), int(q.shape[3]), int(B), int(T),
                                         _pos(q_pos, B), int(m), _ptr(scores), int(scores.shape[2]), int(idx.shape[2]),
                                         _ptr(idx), _ptr(ws), nbytes, _stream(stream)))
 
 
-def indexer_topk_workspace_size(B: int, s_stride: int, k: int) -> int:
-    return int(lib().lca_indexer_topk_workspace_size(int(B), int(s_stride), int(k)))
+def indexer_topk_workspace_size(B: int, T: int, s_stride: int, k: int) -> int:
+    return int(lib().lca_indexer_topk_workspace_size(int(B), int(T), int(s_stride), int(k)))
 
 
 def topk_workspace_size(B: int, T: int, s_stride: int, k: int) -> int:

@@ -249,105 +249,119 @@ int lca_topk_select(const void* scores, int32_t score_dtype, int64_t s_stride, i
     return hip_status(lca::launch_topk(a, (hipStream_t)stream));
 }
 
-// Workspace of lca_indexer_topk: the split top-k's histograms, then one arrival counter per row.
-static size_t itk_counter_offset(int32_t B, int64_t s_stride) {
-    return (lca::topk_ws_bytes(B, 1, s_stride, LCA_BF16) + 15) / 16 * 16;
+// Workspace of lca_indexer_topk for B x T query rows: the top-k's first-pass histograms as the indexer
+// builds them.  Split schedule (few long rows): per row its 16384-key chunks' histograms (and the
+// second pass's), then one arrival counter per row.  Row schedule: one histogram per row.  Both start
+// at the workspace's first byte; a call leaves what it used zero.
+static size_t itk_counter_offset(int32_t rows, int64_t s_stride) {
+    return (lca::topk_ws_bytes(rows, 1, s_stride, LCA_BF16) + 15) / 16 * 16;
 }
 
 static int indexer_topk_launch(lca::IndexerArgs ia, int32_t topk, int32_t* idx, void* ws, size_t ws_bytes,
                                void* stream);
 
-size_t lca_indexer_topk_workspace_size(int32_t B, int64_t s_stride, int32_t k) {
-    if (B < 1 || s_stride < 1 || k < 1) return 0;
-    if (lca::topk_split_chunks(B, s_stride, s_stride, LCA_BF16) == 0) return 0;
-    return itk_counter_offset(B, s_stride) + ((size_t)B * sizeof(uint32_t) + 15) / 16 * 16;
+size_t lca_indexer_topk_workspace_size(int32_t B, int32_t T, int64_t s_stride, int32_t k) {
+    if (B < 1 || T < 1 || s_stride < 1 || k < 1) return 0;
+    const int32_t rows = B * T;
+    size_t split = 0;
+    if (lca::topk_split_chunks(rows, s_stride, s_stride, LCA_BF16) > 0)
+        split = itk_counter_offset(rows, s_stride) + ((size_t)rows * sizeof(uint32_t) + 15) / 16 * 16;
+    const size_t row = (size_t)rows * 256 * sizeof(uint32_t);
+    return split > row ? split : row;
 }
 
-int lca_indexer_topk(const void* q, const float* w, const void* k, int64_t k_cap, int32_t H_I, int32_t d_I,
-                     int32_t B, const int64_t* q_pos, int32_t m, void* scores, int64_t s_stride, int32_t topk,
-                     int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
-    g_err[0] = 0;
-    if (!q || !k || !scores || !idx) return fail(LCA_EINVAL, "q, k, scores and idx must be non-NULL");
+// the validation both forms share: shapes, positions, alignment; fills max_vis
+static int indexer_topk_check(const void* q, const void* scores, const int32_t* idx, const float* w, const void* ws,
+                              int32_t m, int32_t topk, int32_t B, int32_t T, const int64_t* q_pos, int64_t k_cap,
+                              int64_t s_stride, int64_t* max_vis) {
+    if (!q || !scores || !idx) return fail(LCA_EINVAL, "q, scores and idx must be non-NULL");
     if (m < 1) return fail(LCA_EINVAL, "m must be >= 1");
     if (topk < 1) return fail(LCA_EINVAL, "k must be >= 1");
+    if (T < 0) return fail(LCA_ESHAPE, "T < 0");
     if (k_cap < 1 || s_stride < 1) return fail(LCA_ESHAPE, "bad k_cap / s_stride");
-    if (H_I != 16 || d_I != 128)
-        return fail(LCA_ESHAPE, "the indexer supports H_I = 16, d_I = 128 (got %d x %d)", H_I, d_I);
     int rc = check_batch(B, q_pos, "q_pos");
     if (rc) return rc;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(w) || !aligned16(scores) || !aligned16(idx) || !aligned16(ws))
+    if (!aligned16(q) || !aligned16(w) || !aligned16(scores) || !aligned16(idx) || !aligned16(ws))
         return fail(LCA_EALIGN, "pointers must be 16-byte aligned");
-    int64_t max_vis = 0;
-    for (int b = 0; b < B; ++b) {
-        const int64_t vis = (q_pos[b] + 1) / m;
+    *max_vis = 0;
+    for (int b = 0; b < B && T > 0; ++b) {
+        const int64_t vis = (q_pos[b] + T) / m;
         if (vis > k_cap || vis > s_stride)
             return fail(LCA_ESHAPE, "sequence %d sees %lld entries: more than k_cap %lld or s_stride %lld", b,
                         (long long)vis, (long long)k_cap, (long long)s_stride);
-        if (vis > max_vis) max_vis = vis;
+        if (vis > *max_vis) *max_vis = vis;
     }
+    return LCA_OK;
+}
+
+int lca_indexer_topk(const void* q, const float* w, const void* k, int64_t k_cap, int32_t H_I, int32_t d_I,
+                     int32_t B, int32_t T, const int64_t* q_pos, int32_t m, void* scores, int64_t s_stride,
+                     int32_t topk, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    if (!k) return fail(LCA_EINVAL, "k must be non-NULL");
+    if (H_I != 16 || d_I != 128)
+        return fail(LCA_ESHAPE, "the indexer supports H_I = 16, d_I = 128 (got %d x %d)", H_I, d_I);
+    int64_t max_vis = 0;
+    int rc = indexer_topk_check(q, scores, idx, w, ws, m, topk, B, T, q_pos, k_cap, s_stride, &max_vis);
+    if (rc) return rc;
+    if (!aligned16(k)) return fail(LCA_EALIGN, "pointers must be 16-byte aligned");
+    if (T == 0) return LCA_OK;
     lca::IndexerArgs ia;
     memset(&ia, 0, sizeof ia);
     ia.q = q; ia.w = w; ia.k = k; ia.in_dtype = LCA_BF16; ia.k_cap = k_cap; ia.H_I = H_I; ia.d_I = d_I;
-    ia.B = B; ia.T = 1; ia.m = m; ia.scores = scores; ia.score_dtype = LCA_BF16; ia.s_stride = s_stride;
+    ia.B = B; ia.T = T; ia.m = m; ia.scores = scores; ia.score_dtype = LCA_BF16; ia.s_stride = s_stride;
     ia.q_pos = to_pos(q_pos, B);
     ia.max_vis = max_vis;
     return indexer_topk_launch(ia, topk, idx, ws, ws_bytes, stream);
 }
 
-// the shared part of lca_indexer_topk(_mxfp4): the workspace check and the two launches
+// the shared part of lca_indexer_topk(_mxfp4): the workspace check and the launches
 static int indexer_topk_launch(lca::IndexerArgs ia, int32_t topk, int32_t* idx, void* ws, size_t ws_bytes,
                                void* stream) {
-    const int32_t B = ia.B;
+    const int32_t B = ia.B, T = ia.T, rows = B * T;
     const int64_t s_stride = ia.s_stride, max_vis = ia.max_vis;
-    const int G = lca::topk_split_chunks(B, max_vis, s_stride, LCA_BF16);
-    const size_t need = G ? lca_indexer_topk_workspace_size(B, s_stride, topk) : 0;
-    if (need > 0 && (!ws || ws_bytes < need))
+    const size_t need = lca_indexer_topk_workspace_size(B, T, s_stride, topk);
+    if (!ws || ws_bytes < need)
         return fail(LCA_EWORKSPACE, "indexer + top-k workspace of %zu bytes needed (got %zu)", need, ws_bytes);
-    void* scores = ia.scores;
-    const int32_t m = ia.m;
     lca::TopkArgs ta;
     memset(&ta, 0, sizeof ta);
-    ta.scores = scores; ta.score_dtype = LCA_BF16; ta.s_stride = s_stride; ta.B = B; ta.T = 1; ta.m = m;
+    ta.scores = ia.scores; ta.score_dtype = LCA_BF16; ta.s_stride = s_stride; ta.B = B; ta.T = T; ta.m = ia.m;
     ta.k = topk; ta.idx = idx; ta.ws = ws; ta.max_n = max_vis; ta.q_pos = ia.q_pos;
-    if (G > 0) {  // fused: the indexer makes the top-k's first histograms
-        ia.th_h1 = (uint32_t*)ws;
+    ia.th_h1 = (uint32_t*)ws;
+    const int G = lca::topk_split_chunks(rows, max_vis, s_stride, LCA_BF16);
+    if (G > 0) {  // split schedule: the chunks' histograms; the top-k runs its last two launches
         ia.th_row = (int64_t)G * 512;
-        ta.th_cnt = (uint32_t*)((char*)ws + itk_counter_offset(B, s_stride));
+        ia.th_chunked = 1;
+        ta.th_cnt = (uint32_t*)((char*)ws + itk_counter_offset(rows, s_stride));
+    } else {      // row schedule: one histogram per row; the top-k skips its first pass
+        ia.th_row = 256;
+        ia.th_chunked = 0;
+        ta.row_h1 = (uint32_t*)ws;
     }
-    hipError_t e = lca::launch_indexer(ia, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_status(e);
+    if (max_vis > 0) {
+        hipError_t e = lca::launch_indexer(ia, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_status(e);
+    }
     return hip_status(lca::launch_topk(ta, (hipStream_t)stream));
 }
 
 int lca_indexer_topk_mxfp4(const void* q, const float* w, lca_kv k, int32_t H_I, int32_t d_I, int32_t B,
-                           const int64_t* q_pos, int32_t m, void* scores, int64_t s_stride, int32_t topk,
+                           int32_t T, const int64_t* q_pos, int32_t m, void* scores, int64_t s_stride, int32_t topk,
                            int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
     g_err[0] = 0;
-    if (!q || !scores || !idx) return fail(LCA_EINVAL, "q, scores and idx must be non-NULL");
-    if (m < 1) return fail(LCA_EINVAL, "m must be >= 1");
-    if (topk < 1) return fail(LCA_EINVAL, "k must be >= 1");
     if (k.fmt != LCA_MXFP4) return fail(LCA_EDTYPE, "keys must be stored MXFP4 (fmt %d)", LCA_MXFP4);
     int rc = check_kv(k, "k", true, true);
     if (rc) return rc;
     if (H_I != 16 || d_I != 128 || k.d_nope != d_I)
         return fail(LCA_ESHAPE, "MXFP4 indexer supports H_I = 16, d_I = k.d_nope = 128 (got %d x %d, keys %d)", H_I,
                     d_I, k.d_nope);
-    if (s_stride < 1) return fail(LCA_ESHAPE, "bad s_stride");
-    if ((rc = check_batch(B, q_pos, "q_pos"))) return rc;
-    if (!aligned16(q) || !aligned16(w) || !aligned16(scores) || !aligned16(idx) || !aligned16(ws))
-        return fail(LCA_EALIGN, "pointers must be 16-byte aligned");
     int64_t max_vis = 0;
-    for (int b = 0; b < B; ++b) {
-        const int64_t vis = (q_pos[b] + 1) / m;
-        if (vis > k.cap || vis > s_stride)
-            return fail(LCA_ESHAPE, "sequence %d sees %lld entries: more than k.cap %lld or s_stride %lld", b,
-                        (long long)vis, (long long)k.cap, (long long)s_stride);
-        if (vis > max_vis) max_vis = vis;
-    }
+    if ((rc = indexer_topk_check(q, scores, idx, w, ws, m, topk, B, T, q_pos, k.cap, s_stride, &max_vis))) return rc;
+    if (T == 0) return LCA_OK;
     lca::IndexerArgs ia;
     memset(&ia, 0, sizeof ia);
     ia.q = q; ia.w = w; ia.k = k.nope; ia.k_scale = k.scale; ia.in_dtype = LCA_MXFP4; ia.k_cap = k.cap;
-    ia.H_I = H_I; ia.d_I = d_I; ia.B = B; ia.T = 1; ia.m = m; ia.scores = scores; ia.score_dtype = LCA_BF16;
+    ia.H_I = H_I; ia.d_I = d_I; ia.B = B; ia.T = T; ia.m = m; ia.scores = scores; ia.score_dtype = LCA_BF16;
     ia.s_stride = s_stride; ia.q_pos = to_pos(q_pos, B); ia.max_vis = max_vis;
     return indexer_topk_launch(ia, topk, idx, ws, ws_bytes, stream);
 }

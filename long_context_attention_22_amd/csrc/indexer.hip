@@ -43,13 +43,38 @@ __device__ __forceinline__ void store_score<uint16_t>(uint16_t* p, float v) {
     *p = f2bf(v == 0.0f ? 0.0f : v);
 }
 
-// High byte of the top-k's monotone key of a stored bf16 score (the bits store_score writes; -0 as +0):
-// positive scores map to 0x80.. and up, negative ones below.
-__device__ __forceinline__ uint32_t score_key_high(float v) {
-    uint32_t h = f2bf(v == 0.0f ? 0.0f : v);
-    if (h == 0x8000u) h = 0u;
+// High byte of the top-k's monotone key of a stored bf16 score h (the bits store_score writes, -0
+// stored as +0): positive scores map to 0x80.. and up, negative ones below.
+__device__ __forceinline__ uint32_t key_high_of_bits(uint32_t h) {
     const uint32_t key = (h & 0x8000u) ? (~h & 0xffffu) : (h | 0x8000u);
     return key >> 8;
+}
+
+// A score's store and, with the fused top-k pass on, its count in the LDS histogram hist (bf16 scores).
+template <typename TS>
+__device__ __forceinline__ void store_count(TS* p, float v, uint32_t* hist, bool count) {
+    if constexpr (std::is_same<TS, uint16_t>::value) {
+        const uint32_t h = f2bf(v == 0.0f ? 0.0f : v);
+        *p = (uint16_t)h;
+        if (count) atomicAdd(&hist[key_high_of_bits(h)], 1u);
+    } else {
+        store_score<TS>(p, v);
+    }
+}
+
+// The fused top-k pass's LDS histograms (one per token of the workgroup) into the top-k's workspace:
+// row (b, i) at th_h1 + (b T + i) th_row, plus (key_lo / 16384) 256 when the top-k takes its chunked
+// (split) schedule.  Only nonzero bins cost a device atomic.
+template <int TOK>
+__device__ __forceinline__ void flush_hist(const uint32_t* hist, uint32_t* th_h1, int64_t th_row, int th_chunked,
+                                           int64_t row0, int ntok, int64_t key_lo) {
+    __syncthreads();
+    const int64_t coff = th_chunked ? (key_lo >> 14) * 256 : 0;
+#pragma unroll
+    for (int tk = 0; tk < TOK; ++tk) {
+        const uint32_t c = hist[tk * 256 + threadIdx.x];
+        if (tk < ntok && c) atomicAdd(th_h1 + (row0 + tk) * th_row + coff + threadIdx.x, c);
+    }
 }
 
 // (visible count (t + 1) / m: a shift when m is a power of two)
@@ -82,20 +107,23 @@ __global__ void __launch_bounds__(256) indexer_mfma(IndexerArgs a, int64_t keys_
     const float* pw = a.w;
     uint32_t* th_h1 = a.th_h1;
     const int64_t th_row = a.th_row;
+    const int th_chunked = a.th_chunked;
     asm volatile("" ::"s"(T), "s"(m), "s"(p0), "s"(k_cap), "s"(s_stride), "s"(pq), "s"(pk), "s"(psc), "s"(pw),
-                 "s"(th_h1), "s"(th_row));
+                 "s"(th_h1), "s"(th_row), "s"(th_chunked));
     const int ntok = min(TOK, T - i0);
     const int64_t pos0 = p0 + i0;
     const int64_t vis_last = min(vis_of(pos0 + ntok, m), k_cap);
     const int64_t key_lo = (int64_t)blockIdx.x * keys_per_wg;
     const int64_t key_hi = min(key_lo + keys_per_wg, vis_last);
     if (key_lo >= key_hi) return;
-    // fused top-k pass: high-byte histogram of this workgroup's stored scores (wave-uniform flag)
-    constexpr bool kCanHist = TOK == 1 && std::is_same<TS, uint16_t>::value;
-    __shared__ uint32_t th_hist[kCanHist ? 256 : 1];
+    // fused top-k pass: high-byte histograms of this workgroup's stored scores, one per token
+    // (wave-uniform flag)
+    constexpr bool kCanHist = std::is_same<TS, uint16_t>::value;
+    __shared__ uint32_t th_hist[kCanHist ? TOK * 256 : 1];
     const bool hist = kCanHist && th_h1 != nullptr;
     if (hist) {
-        th_hist[threadIdx.x] = 0u;
+#pragma unroll
+        for (int tk = 0; tk < TOK; ++tk) th_hist[tk * 256 + threadIdx.x] = 0u;
         __syncthreads();
     }
 
@@ -156,29 +184,25 @@ __global__ void __launch_bounds__(256) indexer_mfma(IndexerArgs a, int64_t keys_
             // the four head quartets of each key: lane l gets key 16 (l >> 4) + (l & 15) = l
             const float mine = sum4g_scatter(part[0], part[1], part[2], part[3]);
             if (TOK == 1) {
-                if (mykey < vis_tk[tk]) {
-                    store_score<TS>(sbase + (int64_t)tk * a.s_stride + mykey, mine);
-                    if (hist) atomicAdd(&th_hist[score_key_high(mine)], 1u);
-                }
+                if (mykey < vis_tk[tk]) store_count<TS>(sbase + (int64_t)tk * a.s_stride + mykey, mine, th_hist, hist);
             }
             mine_all[tk] = mine;
         }
         // Several tokens: every key of the workgroup's range is stored for every token, after the
         // whole chunk (one masked region instead of one per token); a token's columns in
-        // [vis(t), key_hi) hold scores of keys it cannot see, which the contract leaves unspecified.
+        // [vis(t), key_hi) hold scores of keys it cannot see, which the contract leaves unspecified
+        // (and which the histograms do not count).
         if constexpr (TOK > 1) {
             if (mykey < key_hi) {
 #pragma unroll
                 for (int tk = 0; tk < TOK; ++tk)
-                    if (tk < ntok) store_score<TS>(sbase + (int64_t)tk * a.s_stride + mykey, mine_all[tk]);
+                    if (tk < ntok)
+                        store_count<TS>(sbase + (int64_t)tk * a.s_stride + mykey, mine_all[tk], th_hist + tk * 256,
+                                        hist && mykey < vis_tk[tk]);
             }
         }
     }
-    if (hist) {  // into the histogram of the 16384-key chunk holding this workgroup's keys
-        __syncthreads();
-        const uint32_t c = th_hist[threadIdx.x];
-        if (c) atomicAdd(th_h1 + b * th_row + (key_lo >> 14) * 256 + threadIdx.x, c);
-    }
+    if (hist) flush_hist<TOK>(th_hist, th_h1, th_row, th_chunked, (int64_t)b * T + i0, ntok, key_lo);
 }
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -199,8 +223,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
     const float* pw = a.w;
     uint32_t* th_h1 = a.th_h1;
     const int64_t th_row = a.th_row;
+    const int th_chunked = a.th_chunked;
     asm volatile("" ::"s"(T), "s"(m), "s"(p0), "s"(k_cap), "s"(s_stride), "s"(pq), "s"(pk), "s"(pks), "s"(psc),
-                 "s"(pw), "s"(th_h1), "s"(th_row));
+                 "s"(pw), "s"(th_h1), "s"(th_row), "s"(th_chunked));
     const int ntok = min(TOK, T - i0);
     const int64_t pos0 = p0 + i0;
     const int64_t vis_last = min(vis_of(pos0 + ntok, m), k_cap);
@@ -208,11 +233,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
     const int64_t key_hi = min(key_lo + keys_per_wg, vis_last);
     if (key_lo >= key_hi) return;
     // fused top-k pass (as in indexer_mfma)
-    constexpr bool kCanHist = TOK == 1 && std::is_same<TS, uint16_t>::value;
-    __shared__ uint32_t th_hist[kCanHist ? 256 : 1];
+    constexpr bool kCanHist = std::is_same<TS, uint16_t>::value;
+    __shared__ uint32_t th_hist[kCanHist ? TOK * 256 : 1];
     const bool hist = kCanHist && th_h1 != nullptr;
     if (hist) {
-        th_hist[threadIdx.x] = 0u;
+#pragma unroll
+        for (int tk = 0; tk < TOK; ++tk) th_hist[tk * 256 + threadIdx.x] = 0u;
         __syncthreads();
     }
 
@@ -308,10 +334,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
             }
             const float mine = sum4g_scatter(part[0], part[1], part[2], part[3]);  // key c0 + lane
             if (TOK == 1) {
-                if (mykey < vis_tk[tk]) {
-                    store_score<TS>(sbase + (int64_t)tk * s_stride + mykey, mine);
-                    if (hist) atomicAdd(&th_hist[score_key_high(mine)], 1u);
-                }
+                if (mykey < vis_tk[tk]) store_count<TS>(sbase + (int64_t)tk * s_stride + mykey, mine, th_hist, hist);
             }
             mine_all[tk] = mine;
         }
@@ -320,7 +343,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
             if (mykey < key_hi) {
 #pragma unroll
                 for (int tk = 0; tk < TOK; ++tk)
-                    if (tk < ntok) store_score<TS>(sbase + (int64_t)tk * s_stride + mykey, mine_all[tk]);
+                    if (tk < ntok)
+                        store_count<TS>(sbase + (int64_t)tk * s_stride + mykey, mine_all[tk], th_hist + tk * 256,
+                                        hist && mykey < vis_tk[tk]);
             }
         }
         c0 += 256;
@@ -331,11 +356,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
             ks[bl] = ksbase[key];
         }
     }
-    if (hist) {
-        __syncthreads();
-        const uint32_t c = th_hist[threadIdx.x];
-        if (c) atomicAdd(th_h1 + b * th_row + (key_lo >> 14) * 256 + threadIdx.x, c);
-    }
+    if (hist) flush_hist<TOK>(th_hist, th_h1, th_row, th_chunked, (int64_t)b * T + i0, ntok, key_lo);
 }
 
 template <typename TIn, typename TS>
@@ -376,7 +397,7 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t st) {
     // MXFP4 keys are 68 bytes: a single-token launch gives each workgroup twice the keys
     if (fp4 && tok == 1) kpw *= 2;
     if (kpw < 256) kpw = 256;
-    if (a.th_h1) {  // a workgroup's keys must lie in one 16384-key chunk of the top-k
+    if (a.th_h1 && a.th_chunked) {  // a workgroup's keys must lie in one 16384-key chunk of the top-k
         int64_t p = 256;
         while (p < kpw && p < 16384) p <<= 1;
         kpw = p;

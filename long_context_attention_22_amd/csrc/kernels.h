@@ -55,11 +55,13 @@ struct IndexerArgs {
     int64_t s_stride;
     Pos q_pos;
     int64_t max_vis;
-    // Fused first pass of the split top-k (single-token rows, bf16 scores, bf16 keys): the high-byte
-    // histograms of each row's 16384-key chunks, added with device atomics into th_h1 (row r at
-    // th_h1 + r * th_row, chunk g at + 256 g; zero on entry).  NULL = off.
+    // Fused first pass of the top-k (bf16 scores): the high-byte histograms of each query row's visible
+    // scores, added with device atomics into th_h1 (row r = b T + i at th_h1 + r * th_row; zero on
+    // entry) -- per 16384-key chunk (chunk g at + 256 g) when th_chunked (the top-k's split schedule),
+    // else one per row (its row schedule).  NULL = off.
     uint32_t* th_h1;
     int64_t th_row;
+    int32_t th_chunked;
 };
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t st);
 
@@ -76,6 +78,9 @@ struct TopkArgs {
     // the last two launches run, and the last workgroup of each row (arrivals counted in th_cnt[row],
     // zero on entry) clears the row's histograms and its counter for the next call.  NULL = off.
     uint32_t* th_cnt;
+    // The row schedule's first pass was made by the indexer: row r's high-byte histogram at
+    // row_h1 + 256 r (zero on entry); the row's workgroup reads it instead of the pass and zeroes it.
+    uint32_t* row_h1;
 };
 size_t topk_ws_bytes(int32_t B, int32_t T, int64_t s_stride, int32_t score_dtype);
 // chunks per row of the split schedule for these rows, 0 when the rows take the row schedule

@@ -253,6 +253,15 @@ __global__ void __launch_bounds__(kTopkThreads) topk_row(TopkArgs a) {
     int32_t* out = a.idx + ((int64_t)b * a.T + i) * a.k;
     const int tid = threadIdx.x, lane = tid & 63;
     const int64_t K = min((int64_t)a.k, n);
+    // The first pass made by the indexer (a.row_h1, bf16 rows): this row's high-byte histogram, read
+    // and zeroed for the next call (also for the rows that need no selection).
+    const bool pre = BITS == 16 && a.row_h1 != nullptr;
+    uint32_t h1 = 0;
+    if (pre && tid < 256) {
+        uint32_t* hp = a.row_h1 + ((int64_t)b * a.T + i) * 256 + tid;
+        h1 = *hp;
+        *hp = 0u;
+    }
 
     for (int64_t j = K + tid; j < a.k; j += kTopkThreads) out[j] = -1;
     if (n <= a.k) {
@@ -269,20 +278,24 @@ __global__ void __launch_bounds__(kTopkThreads) topk_row(TopkArgs a) {
     uint32_t rem = (uint32_t)K;
 #pragma unroll 1
     for (int shift = BITS - 8; shift >= 0; shift -= 8) {
-        for (int j = tid; j < 256 * 16; j += kTopkThreads) hist[j] = 0;
-        __syncthreads();
-        const uint32_t hmask = (shift + 8 >= 32) ? 0u : (0xffffffffu << (shift + 8));
-        const uint32_t want = prefix & hmask;
-        const int sub = lane & 15;
-        for_each_key<TS, kTopkThreads>(row, 0, n, [&](int64_t, uint32_t key) {
-            if ((key & hmask) == want) atomicAdd(&hist[((key >> shift) & 255u) * 16 + sub], 1u);
-        });
-        __syncthreads();
-        if (tid < 256) {
-            uint32_t s = 0;
+        if (pre && shift == BITS - 8) {
+            if (tid < 256) hsum[tid] = h1;
+        } else {
+            for (int j = tid; j < 256 * 16; j += kTopkThreads) hist[j] = 0;
+            __syncthreads();
+            const uint32_t hmask = (shift + 8 >= 32) ? 0u : (0xffffffffu << (shift + 8));
+            const uint32_t want = prefix & hmask;
+            const int sub = lane & 15;
+            for_each_key<TS, kTopkThreads>(row, 0, n, [&](int64_t, uint32_t key) {
+                if ((key & hmask) == want) atomicAdd(&hist[((key >> shift) & 255u) * 16 + sub], 1u);
+            });
+            __syncthreads();
+            if (tid < 256) {
+                uint32_t s = 0;
 #pragma unroll
-            for (int c = 0; c < 16; ++c) s += hist[tid * 16 + ((c + tid) & 15)];
-            hsum[tid] = s;
+                for (int c = 0; c < 16; ++c) s += hist[tid * 16 + ((c + tid) & 15)];
+                hsum[tid] = s;
+            }
         }
         __syncthreads();
         if (tid < 64) pick_digit(hsum, rem, &sel_digit, &sel_rem);

@@ -12,7 +12,7 @@ at positions t0 .. t0+T-1 of every sequence, Layer.step() issues:
     indexer keys      kv_compress(m, overlap, d_I)      (CSA; bf16 or MXFP4 keys)
     scores            indexer_score / _mxfp4            (CSA)
     selection         topk_select                       (CSA)
-                      (decode rows: one indexer_topk / indexer_topk_mxfp4 call, the top-k's
+                      (bf16 scores: one indexer_topk / indexer_topk_mxfp4 call, the top-k's
                       first histogram pass fused into the indexer)
     attention         csa_attn / hca_attn
 
@@ -124,9 +124,9 @@ class Layer:
             self.idx = torch.zeros(B, t_max, spec.k, dtype=torch.int32, device=device)
             tws = max(topk_workspace_size(B, T, comp_cap, spec.k) for T in range(1, min(t_max, 128) + 1))
             self.topk_ws = torch.zeros(max(16, tws), dtype=torch.uint8, device=device)
-            # decode rows with bf16 keys and scores: indexer_topk (its own workspace, zeroed once)
-            self.itk_ws = torch.zeros(max(16, indexer_topk_workspace_size(B, comp_cap, spec.k)), dtype=torch.uint8,
-                                      device=device)
+            # bf16 scores: indexer_topk (its own workspace, zeroed once; sized for the largest row count)
+            itk = max(indexer_topk_workspace_size(B, T, comp_cap, spec.k) for T in sorted({1, min(t_max, 127), t_max}))
+            self.itk_ws = torch.zeros(max(16, itk), dtype=torch.uint8, device=device)
             self.fuse_topk = True
             max_keys = spec.k + spec.n_win
         else:
@@ -136,6 +136,29 @@ class Layer:
         # split partials are needed only for short launches (few query rows); size for the largest
         ws = max(attn_workspace_size(B, T, spec.H, spec.c, max_keys) for T in range(1, min(t_max, 128) + 1))
         self.ws = torch.zeros(max(16, ws), dtype=torch.uint8, device=device)
+
+    def reserve_rows(self, T: int):
+        """Buffers and workspaces for calls of T query rows per sequence (a prefill chunk on a layer built
+        for decode): scores, idx, the fused indexer + top-k workspace (zeroed) and the attention's."""
+        s, B = self.spec, self.B
+        if s.kind == "csa":
+            cap = self.keys.cap
+            if self.scores.shape[1] < T:
+                self.scores = torch.zeros(B, T, cap, dtype=self.scores.dtype, device=self.scores.device)
+                self.idx = torch.zeros(B, T, s.k, dtype=torch.int32, device=self.idx.device)
+            need = indexer_topk_workspace_size(B, T, cap, s.k)
+            if need > self.itk_ws.numel():
+                self.itk_ws = torch.zeros(need, dtype=torch.uint8, device=self.itk_ws.device)
+            need = topk_workspace_size(B, T, cap, s.k)
+            if need > self.topk_ws.numel():
+                self.topk_ws = torch.zeros(need, dtype=torch.uint8, device=self.topk_ws.device)
+            keys = s.k + s.n_win
+        else:
+            keys = self.comp.cap + s.n_win
+        need = attn_workspace_size(B, T, s.H, s.c, keys)
+        if need > self.ws.numel():
+            self.ws = torch.zeros(need, dtype=torch.uint8, device=self.ws.device)
+        self.t_max = max(self.t_max, T)
 
     # ------------------------------------------------------------------
     def compress(self, raw: RawStream, t0: int, T: int):
@@ -167,7 +190,7 @@ class Layer:
         if s.kind == "csa":
             sc = _rows(self.scores, T)
             ix = _rows(self.idx, T)
-            if T == 1 and self.fuse_topk and s.score_fmt == BF16 and self.keys.fmt in (BF16, MXFP4):
+            if self.fuse_topk and s.score_fmt == BF16 and self.keys.fmt in (BF16, MXFP4):
                 if self.keys.fmt == MXFP4:
                     run("indexer_topk", lambda: indexer_topk_mxfp4(q_idx, w, self.keys, sc, ix, q_pos=t0, m=s.m,
                                                                    ws=self.itk_ws))

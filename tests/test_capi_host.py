@@ -278,11 +278,12 @@ def test_indexer_topk_validation(L):
     vp = C.c_void_p
 
     def call(**kw):
-        a = dict(q=FAKE, w=None, k=FAKE2, k_cap=300000, H_I=16, d_I=128, B=1, q_pos=pos(1 << 20), m=4,
+        a = dict(q=FAKE, w=None, k=FAKE2, k_cap=300000, H_I=16, d_I=128, B=1, T=1, q_pos=pos(1 << 20), m=4,
                  scores=FAKE, s_stride=300000, topk=2048, idx=FAKE2, ws=FAKE, ws_bytes=1 << 20)
         a.update(kw)
         return L.lca_indexer_topk(vp(a["q"]), vp(a["w"]) if a["w"] else None, vp(a["k"]), C.c_int64(a["k_cap"]),
-                                  C.c_int32(a["H_I"]), C.c_int32(a["d_I"]), C.c_int32(a["B"]), a["q_pos"],
+                                  C.c_int32(a["H_I"]), C.c_int32(a["d_I"]), C.c_int32(a["B"]), C.c_int32(a["T"]),
+                                  a["q_pos"],
                                   C.c_int32(a["m"]), vp(a["scores"]), C.c_int64(a["s_stride"]), C.c_int32(a["topk"]),
                                   vp(a["idx"]), vp(a["ws"]) if a["ws"] else None, C.c_size_t(a["ws_bytes"]), None)
 
@@ -294,8 +295,14 @@ def test_indexer_topk_validation(L):
     assert call(B=0, q_pos=pos(0)) == lca.ESHAPE
     assert call(k_cap=1000) == lca.ESHAPE            # 262,144 visible entries do not fit
     assert call(idx=FAKE2 + 4) == lca.EALIGN
-    need = L.lca_indexer_topk_workspace_size(1, 300000, 2048)
+    assert call(T=-1) == lca.ESHAPE
+    assert call(T=40000, k_cap=262200, s_stride=262200) == lca.ESHAPE   # the last row sees past the cache
+    need = L.lca_indexer_topk_workspace_size(1, 1, 300000, 2048)
     assert need > 0
     assert call(ws=0, ws_bytes=0) == lca.EWORKSPACE
     assert call(ws_bytes=need - 1) == lca.EWORKSPACE
-    assert L.lca_indexer_topk_workspace_size(1, 10000, 2048) == 0   # short rows: the row schedule
+    # short rows (the row schedule): one 256-bin histogram per row; many rows: likewise
+    assert L.lca_indexer_topk_workspace_size(1, 1, 10000, 2048) == 1024
+    assert L.lca_indexer_topk_workspace_size(2, 4096, 300000, 2048) == 2 * 4096 * 1024
+    rows_need = L.lca_indexer_topk_workspace_size(1, 4096, 300000, 2048)
+    assert call(T=4096, ws_bytes=rows_need - 1) == lca.EWORKSPACE

@@ -476,8 +476,7 @@ def test_config5_stack_1m_decode_and_chunk():
         if sp.kind == "csa":
             qi = S.to_bf16(S.normal(seed, f"{tg}/qip", (1, T, sp.H_I, sp.d_I)))
             w = S.normal(seed, f"{tg}/wp", (1, T, sp.H_I), 0.25)
-            ly.scores = torch.zeros(1, T, ly.comp.cap, dtype=torch.bfloat16, device="cuda")
-            ly.idx = torch.zeros(1, T, sp.k, dtype=torch.int32, device="cuda")
+        ly.reserve_rows(T)  # (the chunk takes the fused indexer + top-k: the first top-k pass in the indexer)
         out = torch.zeros(1, T, sp.H, C, dtype=torch.bfloat16, device="cuda")
         ly.step(st.raws[i], t0, dev(q), out, q_idx=None if qi is None else dev(qi), w=None if w is None else dev(w))
         torch.cuda.synchronize()

@@ -187,7 +187,7 @@ def _select(c, keys_dev, decode):
     sc = torch.zeros(B, T, cap, dtype=torch.bfloat16, device="cuda")
     idx = torch.zeros(B, T, k, dtype=torch.int32, device="cuda")
     if decode:
-        ws = torch.zeros(max(16, lca.indexer_topk_workspace_size(B, cap, k)), dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(max(16, lca.indexer_topk_workspace_size(B, 1, cap, k)), dtype=torch.uint8, device="cuda")
         if keys_dev.fmt == lca.MXFP4:
             lca.indexer_topk_mxfp4(dev(c["qi"]), dev(c["w"]), keys_dev, sc, idx, q_pos=c["q_pos"], m=c["m"], ws=ws)
         else:

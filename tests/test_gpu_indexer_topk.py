@@ -60,7 +60,7 @@ def _vis_cols(sc, q_pos, m):
 def test_indexer_topk_matches_separate_calls(B, cap, topk, pos_list, ties):
     m = 4
     s_stride = cap
-    nbytes = lca.indexer_topk_workspace_size(B, s_stride, topk)
+    nbytes = lca.indexer_topk_workspace_size(B, 1, s_stride, topk)
     ws = torch.zeros(max(16, nbytes), dtype=torch.uint8, device="cuda")
     for call, q_pos in enumerate(pos_list):
         q, w, k = _inputs(100 + call, B, cap, ties)
@@ -82,10 +82,79 @@ def test_indexer_topk_matches_separate_calls(B, cap, topk, pos_list, ties):
         _check_ws(ws, nbytes)
 
 
+def _inputs_rows(seed, B, T, cap):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    q = torch.randn(B, T, 16, 128, device="cuda", generator=g).to(torch.bfloat16)
+    w = torch.randn(B, T, 16, device="cuda", generator=g) * 0.25
+    k = torch.randn(B, cap, 128, device="cuda", generator=g).to(torch.bfloat16)
+    return q, w, k
+
+
+@pytest.mark.parametrize("B,T,cap,topk,q_pos,sample", [
+    (1, 4096, 263200, 2048, [1 << 20], [0, 1, 2, 1365, 4094, 4095]),   # the 1M prefill chunk: row schedule
+    (1, 100, 262300, 2048, [(1 << 20) - 50], [0, 49, 50, 99]),        # few long rows, 8 per workgroup: split
+    (2, 37, 300100, 1024, [1200003, 65539], [0, 36, 37, 73]),         # few long rows, one per workgroup: split
+    (1, 300, 9000, 512, [30000], [0, 1, 150, 299]),                   # short rows: row schedule
+])
+def test_indexer_topk_prefill_rows(B, T, cap, topk, q_pos, sample):
+    """Several query rows per sequence: the indexer counts every row's first radix digit while it stores
+    the scores (per chunk for the split schedule, per row for the row schedule); scores and selections
+    equal the separate calls bit for bit, the selections of sampled rows equal the oracle's top-k of the
+    same scores, and the workspace is zero again after two calls."""
+    m = 4
+    nbytes = lca.indexer_topk_workspace_size(B, T, cap, topk)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    for call in range(2):
+        q, w, k = _inputs_rows(300 + call, B, T, cap)
+        sc = torch.zeros(B, T, cap, dtype=torch.bfloat16, device="cuda")
+        ix = torch.empty(B, T, topk, dtype=torch.int32, device="cuda")
+        lca.indexer_topk(q, w, k, sc, ix, q_pos=q_pos, m=m, ws=ws)
+        sc_ref = torch.zeros_like(sc)
+        ix_ref = torch.empty_like(ix)
+        tws = torch.zeros(max(16, lca.topk_workspace_size(B, T, cap, topk)), dtype=torch.uint8, device="cuda")
+        lca.indexer_score(q, w, k, sc_ref, q_pos=q_pos, m=m)
+        lca.topk_select(sc_ref, ix_ref, q_pos=q_pos, m=m, ws=tws)
+        torch.cuda.synchronize()
+        assert torch.equal(ix, ix_ref), call
+        for r in sample:
+            b, i = divmod(r, T)
+            n = (q_pos[b] + i + 1) // m
+            a_, r_ = host(sc[b, i, :n]), host(sc_ref[b, i, :n])
+            assert np.array_equal(a_, r_), (call, r)
+            row = np.zeros((1, 1, cap), np.uint16)
+            row[0, 0, :n] = a_
+            o_ix = orc.topk_select(row, q_pos=[q_pos[b] + i], m=m, k=topk)
+            assert np.array_equal(o_ix[0, 0], host(ix[b, i])), (call, r)
+        del sc, sc_ref
+        _check_ws(ws, nbytes)
+
+
+def test_indexer_topk_mxfp4_prefill_rows():
+    B, T, cap, topk, m = 1, 200, 262300, 2048, 4
+    q_pos = [(1 << 20) - 150]
+    k = _mxfp4_keys(11, B, cap)
+    nbytes = lca.indexer_topk_workspace_size(B, T, cap, topk)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    q, w, _ = _inputs_rows(12, B, T, 16)
+    sc = torch.zeros(B, T, cap, dtype=torch.bfloat16, device="cuda")
+    ix = torch.empty(B, T, topk, dtype=torch.int32, device="cuda")
+    lca.indexer_topk_mxfp4(q, w, k, sc, ix, q_pos=q_pos, m=m, ws=ws)
+    sc_ref, ix_ref = torch.zeros_like(sc), torch.empty_like(ix)
+    tws = torch.zeros(max(16, lca.topk_workspace_size(B, T, cap, topk)), dtype=torch.uint8, device="cuda")
+    lca.indexer_score_mxfp4(q, w, k, sc_ref, q_pos=q_pos, m=m)
+    lca.topk_select(sc_ref, ix_ref, q_pos=q_pos, m=m, ws=tws)
+    torch.cuda.synchronize()
+    assert torch.equal(ix, ix_ref)
+    for i in (0, 99, 199):
+        n = (q_pos[0] + i + 1) // m
+        assert np.array_equal(host(sc[0, i, :n]), host(sc_ref[0, i, :n])), i
+    _check_ws(ws, nbytes)
+
+
 def test_indexer_topk_graph_replays():
     B, cap, topk, m = 1, 262160, 2048, 4
     s_stride = cap
-    ws = torch.zeros(lca.indexer_topk_workspace_size(B, s_stride, topk), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(lca.indexer_topk_workspace_size(B, 1, s_stride, topk), dtype=torch.uint8, device="cuda")
     q, w, k = _inputs(7, B, cap)
     pos = [(1 << 20) + 1, (1 << 20) + 2, (1 << 20) + 3]
     outs = [(torch.zeros(B, 1, s_stride, dtype=torch.bfloat16, device="cuda"),
@@ -123,7 +192,7 @@ def _mxfp4_keys(seed, B, cap):
 ])
 def test_indexer_topk_mxfp4_matches_separate_calls(B, cap, topk, pos_list):
     m, s_stride = 4, cap
-    ws = torch.zeros(lca.indexer_topk_workspace_size(B, s_stride, topk), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(lca.indexer_topk_workspace_size(B, 1, s_stride, topk), dtype=torch.uint8, device="cuda")
     k = _mxfp4_keys(5, B, cap)
     tws = torch.zeros(max(16, lca.topk_workspace_size(B, 1, s_stride, topk)), dtype=torch.uint8, device="cuda")
     for call, q_pos in enumerate(pos_list):
