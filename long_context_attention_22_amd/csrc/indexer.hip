@@ -95,8 +95,11 @@ __device__ __forceinline__ void token_vis(int64_t (&vis)[TOK], int64_t pos0, int
     }
 }
 
-template <int TOK, typename TS>
-__global__ void __launch_bounds__(256) indexer_mfma(IndexerArgs a, int64_t keys_per_wg) {
+// HIST: the fused top-k pass is on (bf16 scores; a.th_h1 set).  (Two waves per SIMD: the register budget
+// the 8-token form has to fit, 256 per lane.)
+template <int TOK, typename TS, bool HIST>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) indexer_mfma(IndexerArgs a,
+                                                                                           int64_t keys_per_wg) {
     const int b = blockIdx.z;
     const int i0 = blockIdx.y * TOK;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -117,10 +120,9 @@ __global__ void __launch_bounds__(256) indexer_mfma(IndexerArgs a, int64_t keys_
     const int64_t key_hi = min(key_lo + keys_per_wg, vis_last);
     if (key_lo >= key_hi) return;
     // fused top-k pass: high-byte histograms of this workgroup's stored scores, one per token
-    // (wave-uniform flag)
-    constexpr bool kCanHist = std::is_same<TS, uint16_t>::value;
-    __shared__ uint32_t th_hist[kCanHist ? TOK * 256 : 1];
-    const bool hist = kCanHist && th_h1 != nullptr;
+    static_assert(!HIST || std::is_same<TS, uint16_t>::value, "the fused top-k pass needs bf16 scores");
+    __shared__ uint32_t th_hist[HIST ? TOK * 256 : 1];
+    constexpr bool hist = HIST;
     if (hist) {
 #pragma unroll
         for (int tk = 0; tk < TOK; ++tk) th_hist[tk * 256 + threadIdx.x] = 0u;
@@ -212,8 +214,10 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t x) { return __builtin_bit_cast(bf16x2, x); }
 
 // (at most 128 VGPRs: four waves per SIMD hide the key loads better than wider token pipelining)
-template <int TOK, typename TS>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) indexer_fp4(IndexerArgs a, int64_t keys_per_wg) {
+// (the fused top-k pass's per-token histograms need more registers than the four-wave budget holds)
+template <int TOK, typename TS, bool HIST>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HIST && TOK > 1 ? 2 : 4, 8)))
+indexer_fp4(IndexerArgs a, int64_t keys_per_wg) {
     const int b = blockIdx.z;
     const int i0 = blockIdx.y * TOK;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -233,9 +237,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
     const int64_t key_hi = min(key_lo + keys_per_wg, vis_last);
     if (key_lo >= key_hi) return;
     // fused top-k pass (as in indexer_mfma)
-    constexpr bool kCanHist = std::is_same<TS, uint16_t>::value;
-    __shared__ uint32_t th_hist[kCanHist ? TOK * 256 : 1];
-    const bool hist = kCanHist && th_h1 != nullptr;
+    static_assert(!HIST || std::is_same<TS, uint16_t>::value, "the fused top-k pass needs bf16 scores");
+    __shared__ uint32_t th_hist[HIST ? TOK * 256 : 1];
+    constexpr bool hist = HIST;
     if (hist) {
 #pragma unroll
         for (int tk = 0; tk < TOK; ++tk) th_hist[tk * 256 + threadIdx.x] = 0u;
@@ -404,21 +408,23 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t st) {
     }
     const int64_t nsplit = (a.max_vis + kpw - 1) / kpw;
     dim3 grid((unsigned)nsplit, (unsigned)groups, (unsigned)a.B);
+    const bool hist = a.th_h1 != nullptr && bf_scores;
+#define LCA_IDX_LAUNCH(K, TOKN, TS, H) hipLaunchKernelGGL((K<TOKN, TS, H>), grid, dim3(256), 0, st, a, kpw)
+#define LCA_IDX_PICK(K, TOKN)                                                         \
+    do {                                                                              \
+        if (!bf_scores) LCA_IDX_LAUNCH(K, TOKN, float, false);                        \
+        else if (hist) LCA_IDX_LAUNCH(K, TOKN, uint16_t, true);                       \
+        else LCA_IDX_LAUNCH(K, TOKN, uint16_t, false);                                \
+    } while (0)
     if (fp4) {
-        if (tok == 8) {
-            if (bf_scores) hipLaunchKernelGGL((indexer_fp4<8, uint16_t>), grid, dim3(256), 0, st, a, kpw);
-            else hipLaunchKernelGGL((indexer_fp4<8, float>), grid, dim3(256), 0, st, a, kpw);
-        } else {
-            if (bf_scores) hipLaunchKernelGGL((indexer_fp4<1, uint16_t>), grid, dim3(256), 0, st, a, kpw);
-            else hipLaunchKernelGGL((indexer_fp4<1, float>), grid, dim3(256), 0, st, a, kpw);
-        }
-    } else if (tok == 8) {
-        if (bf_scores) hipLaunchKernelGGL((indexer_mfma<8, uint16_t>), grid, dim3(256), 0, st, a, kpw);
-        else hipLaunchKernelGGL((indexer_mfma<8, float>), grid, dim3(256), 0, st, a, kpw);
+        if (tok == 8) LCA_IDX_PICK(indexer_fp4, 8);
+        else LCA_IDX_PICK(indexer_fp4, 1);
     } else {
-        if (bf_scores) hipLaunchKernelGGL((indexer_mfma<1, uint16_t>), grid, dim3(256), 0, st, a, kpw);
-        else hipLaunchKernelGGL((indexer_mfma<1, float>), grid, dim3(256), 0, st, a, kpw);
+        if (tok == 8) LCA_IDX_PICK(indexer_mfma, 8);
+        else LCA_IDX_PICK(indexer_mfma, 1);
     }
+#undef LCA_IDX_PICK
+#undef LCA_IDX_LAUNCH
     return hipGetLastError();
 }
 
