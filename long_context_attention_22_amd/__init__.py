@@ -210,7 +210,7 @@ def indexer_topk(q, w, k, scores, idx, *, q_pos, m: int, ws=None, stream=None):
     """indexer_score then topk_select, the top-k's first pass fused into the indexer.  q [B][T][16][128]
     bf16, w [B][T][16] f32 or None, k [B][k_cap][128] bf16, scores [B][T][s_stride] bf16, idx [B][T][k]
     int32; ws: indexer_topk_workspace_size(B, T, s_stride, k) bytes, zeroed before its first use and kept
-    for this call only (every call leaves it zeroed)."""
+    for this call only (every call leaves it ready for the next: what must start at zero is zeroed again)."""
     _dense(("q", q), ("w", w), ("scores", scores), ("idx", idx))
     B, T = q.shape[0], q.shape[1]
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()

@@ -250,12 +250,9 @@ int lca_topk_select(const void* scores, int32_t score_dtype, int64_t s_stride, i
 }
 
 // Workspace of lca_indexer_topk for B x T query rows: the top-k's first-pass histograms as the indexer
-// builds them.  Split schedule (few long rows): per row its 16384-key chunks' histograms (and the
-// second pass's), then one arrival counter per row.  Row schedule: one histogram per row.  Both start
-// at the workspace's first byte; a call leaves what it used zero.
-static size_t itk_counter_offset(int32_t rows, int64_t s_stride) {
-    return (lca::topk_ws_bytes(rows, 1, s_stride, LCA_BF16) + 15) / 16 * 16;
-}
+// builds them, from the workspace's first byte.  Split schedule (few long rows): per row its
+// 16384-key chunks' histograms, then the top-k's own second-pass histograms and figures (which need
+// no zeros).  Row schedule: one histogram per row.  A call clears the first-pass histograms again.
 
 static int indexer_topk_launch(lca::IndexerArgs ia, int32_t topk, int32_t* idx, void* ws, size_t ws_bytes,
                                void* stream);
@@ -265,7 +262,7 @@ size_t lca_indexer_topk_workspace_size(int32_t B, int32_t T, int64_t s_stride, i
     const int32_t rows = B * T;
     size_t split = 0;
     if (lca::topk_split_chunks(rows, s_stride, s_stride, LCA_BF16) > 0)
-        split = itk_counter_offset(rows, s_stride) + ((size_t)rows * sizeof(uint32_t) + 15) / 16 * 16;
+        split = lca::topk_ws_bytes(rows, 1, s_stride, LCA_BF16);
     const size_t row = (size_t)rows * 256 * sizeof(uint32_t);
     return split > row ? split : row;
 }
@@ -330,9 +327,9 @@ static int indexer_topk_launch(lca::IndexerArgs ia, int32_t topk, int32_t* idx, 
     ia.th_h1 = (uint32_t*)ws;
     const int G = lca::topk_split_chunks(rows, max_vis, s_stride, LCA_BF16);
     if (G > 0) {  // split schedule: the chunks' histograms; the top-k runs its last two launches
-        ia.th_row = (int64_t)G * 512;
+        ia.th_row = (int64_t)G * 256;
         ia.th_chunked = 1;
-        ta.th_cnt = (uint32_t*)((char*)ws + itk_counter_offset(rows, s_stride));
+        ta.split_fused = 1;
     } else {      // row schedule: one histogram per row; the top-k skips its first pass
         ia.th_row = 256;
         ia.th_chunked = 0;

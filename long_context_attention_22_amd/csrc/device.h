@@ -163,6 +163,23 @@ __device__ __forceinline__ float sum4g_scatter(float v0, float v1, float v2, flo
 // over the four 16-lane groups: every lane gets the same value, summed in the same order
 __device__ __forceinline__ float max4g(float v) { return xlane32(xlane16(v, true), true); }
 __device__ __forceinline__ float sum4g(float v) { return xlane32(xlane16(v, false), false); }
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS traffic): shifts by 1, 2,
+// 4 and 8 lanes scan each 16-lane row, then gfx9's row broadcasts carry lane 15 of rows 0 and 2 into
+// rows 1 and 3 and lane 31 into rows 2 and 3.  Lanes whose source lies outside the row, or whose row
+// the row mask leaves out, add the old value 0.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return v;
+}
+__device__ __forceinline__ uint32_t wave_lane63(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // bitwise OR over the eight lanes of each aligned group of 8 (quad swaps, then the half-row mirror)
 __device__ __forceinline__ uint32_t or8(uint32_t v) {
     v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xb1, 0xf, 0xf, false);   // quad_perm [1,0,3,2]

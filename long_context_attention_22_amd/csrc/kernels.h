@@ -57,8 +57,8 @@ struct IndexerArgs {
     int64_t max_vis;
     // Fused first pass of the top-k (bf16 scores): the high-byte histograms of each query row's visible
     // scores, added with device atomics into th_h1 (row r = b T + i at th_h1 + r * th_row; zero on
-    // entry) -- per 16384-key chunk (chunk g at + 256 g) when th_chunked (the top-k's split schedule),
-    // else one per row (its row schedule).  NULL = off.
+    // entry) -- per 16384-key chunk (chunk g at + 256 g, th_row = 256 G) when th_chunked (the top-k's
+    // split schedule), else one per row (its row schedule, th_row = 256).  NULL = off.
     uint32_t* th_h1;
     int64_t th_row;
     int32_t th_chunked;
@@ -74,10 +74,10 @@ struct TopkArgs {
     void* ws;
     int64_t max_n;   // largest candidate count over the rows
     Pos q_pos;
-    // The split schedule's high-byte histograms were made by the indexer (IndexerArgs::th_h1): only
-    // the last two launches run, and the last workgroup of each row (arrivals counted in th_cnt[row],
-    // zero on entry) clears the row's histograms and its counter for the next call.  NULL = off.
-    uint32_t* th_cnt;
+    // The split schedule's high-byte histograms were made by the indexer (IndexerArgs::th_h1, at the
+    // workspace's start): only the last two launches run, and the last one clears those histograms
+    // for the next call.
+    int32_t split_fused;
     // The row schedule's first pass was made by the indexer: row r's high-byte histogram at
     // row_h1 + 256 r (zero on entry); the row's workgroup reads it instead of the pass and zeroes it.
     uint32_t* row_h1;

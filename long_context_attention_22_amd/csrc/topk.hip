@@ -90,11 +90,7 @@ __device__ __forceinline__ void for_each_key(const TS* row, int64_t lo, int64_t 
 template <int NW>
 __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        uint32_t n = __shfl_up(v, o, kWave);
-        if (lane >= o) v += n;
-    }
+    v = wave_incl_scan(v);
     if (lane == 63) wsum[wv] = v;
     __syncthreads();
     uint32_t off = 0, tot = 0;
@@ -117,13 +113,9 @@ __device__ __forceinline__ void pick_digit(const uint32_t* hsum, uint32_t rem, u
     const uint32_t h0 = hsum[4 * lane], h1 = hsum[4 * lane + 1], h2 = hsum[4 * lane + 2],
                    h3 = hsum[4 * lane + 3];
     const uint32_t loc = h0 + h1 + h2 + h3;
-    uint32_t suf = loc;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        uint32_t nb = __shfl_down(suf, o, kWave);
-        if (lane + o < 64) suf += nb;
-    }
-    const uint32_t above = suf - loc;
+    // keys in digits above this lane's four: the total less the inclusive prefix
+    const uint32_t incl = wave_incl_scan(loc);
+    const uint32_t above = wave_lane63(incl) - incl, suf = above + loc;
     if (above < rem && suf >= rem) {
         uint32_t acc = above;
         const uint32_t hs[4] = {h0, h1, h2, h3};
@@ -229,7 +221,7 @@ __device__ __forceinline__ void row_tail16(const TS* row, int64_t n, int32_t* ou
             if (chosen[mid] < v) lo = mid + 1;
             else hi = mid;
         }
-        out[j + lo] = v;
+        if (j + lo < K) out[j + lo] = v;  // (always: D + rem = K; a guard on the global store)
     }
     for (uint32_t j = tid; j < rem; j += kTopkThreads) {
         const int32_t v = chosen[j];
@@ -239,9 +231,8 @@ __device__ __forceinline__ void row_tail16(const TS* row, int64_t n, int32_t* ou
             if (defl[mid] < v) lo = mid + 1;
             else hi = mid;
         }
-        out[j + lo] = v;
+        if (j + lo < K) out[j + lo] = v;  // (always: D + rem = K; a guard on the global store)
     }
-    (void)K;
 }
 
 template <typename TS, int BITS>
@@ -333,12 +324,12 @@ __global__ void __launch_bounds__(kTopkThreads) topk_row(TopkArgs a) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             if (e0 + u >= n) break;
-            const uint32_t pos = gt_before + min(eq_before, rem);
+            const uint32_t pos = gt_before + min(eq_before, rem);  // < K for every kept key
             if (keys[u] > tau) {
-                out[pos] = (int32_t)(e0 + u);
+                if (pos < (uint32_t)K) out[pos] = (int32_t)(e0 + u);
                 ++gt_before;
             } else if (keys[u] == tau) {
-                if (eq_before < rem) out[pos] = (int32_t)(e0 + u);
+                if (eq_before < rem && pos < (uint32_t)K) out[pos] = (int32_t)(e0 + u);
                 ++eq_before;
             }
         }
@@ -354,13 +345,20 @@ __global__ void __launch_bounds__(kTopkThreads) topk_row(TopkArgs a) {
 // Grid (G, T, B): chunk g = blockIdx.x of row i = blockIdx.y of sequence b = blockIdx.z.  Each
 // launch is short and bound by latency, so every kernel reads its arguments, its 32 keys per
 // thread and every histogram column it needs in one round of loads before any of them is used.
+//   Workspace of R = B T rows: the rows' high-byte histograms h1 [R][G][256], then their low-byte
+// histograms h2 [R][G][256] (keys with the chosen high byte), then per row and chunk g the word
+// quadruple (keys above the chosen high byte in the chunks before g, that byte, the keys still to
+// take from its bucket, 0) that the second launch leaves for the third.  Only h1 may need zeros:
+// where the indexer adds it up (TopkArgs::split_fused) the third launch clears it again, each
+// workgroup its own chunk, since by then the second launch -- its last reader -- has ended.
 constexpr int kPer = kChunk / kSplitThreads;  // 32 keys per thread
 struct SplitRow {
     const uint16_t* row;
     int32_t* out;
     int64_t n, K, stride;
-    uint32_t* h1;   // [G][256] high-byte histograms of this row
-    uint32_t* h2;   // [G][256] low-byte histograms (keys with the chosen high byte)
+    uint32_t* h1;    // [G][256] high-byte histograms of this row
+    uint32_t* h2;    // [G][256] low-byte histograms (keys with the chosen high byte)
+    uint32_t* meta;  // [G][4] (above d1 before chunk g, d1, rem1, 0)
 };
 
 __device__ __forceinline__ SplitRow split_row(const TopkArgs& a, int G) {
@@ -381,8 +379,10 @@ __device__ __forceinline__ SplitRow split_row(const TopkArgs& a, int G) {
     r.stride = stride;
     r.row = (const uint16_t*)sc + rowid * stride;
     r.out = idx + rowid * k;
-    r.h1 = (uint32_t*)ws + rowid * (int64_t)G * 512;
-    r.h2 = r.h1 + (int64_t)G * 256;
+    const int64_t rows = (int64_t)gridDim.y * gridDim.z;
+    r.h1 = (uint32_t*)ws + rowid * (int64_t)G * 256;
+    r.h2 = (uint32_t*)ws + (rows + rowid) * (int64_t)G * 256;
+    r.meta = (uint32_t*)ws + 2 * rows * (int64_t)G * 256 + rowid * (int64_t)G * 4;
     return r;
 }
 
@@ -439,29 +439,25 @@ __device__ __forceinline__ void keys_hist(const uint32_t* raw, int64_t e0, int64
     __syncthreads();
 }
 
-// Column sums of bin `bin` over the G chunk histograms h[g][256] of NH histograms (h2 = h1 + 256 G):
-// the totals and the sums over the chunks before g_me.  All loads of a batch of 24 chunks go out
-// before any sum (one round for G <= 24).
-template <int NH>
-__device__ __forceinline__ void col_sums(const uint32_t* h1, int G, int g_me, int bin, uint32_t* tot, uint32_t* pre) {
+// Column sums of bin `bin` over the G chunk histograms h[g][256]: the total and the sum over the
+// chunks before g_me.  All loads of a batch of 24 chunks go out before any sum (one round for
+// G <= 24).
+__device__ __forceinline__ void col_sums(const uint32_t* h, int G, int g_me, int bin, uint32_t* tot, uint32_t* pre) {
     constexpr int kB = 24;
-#pragma unroll
-    for (int k = 0; k < NH; ++k) tot[k] = pre[k] = 0;
+    uint32_t t = 0, p = 0;
     for (int g0 = 0; g0 < G; g0 += kB) {
-        uint32_t v[NH][kB];
+        uint32_t v[kB];
 #pragma unroll
-        for (int k = 0; k < NH; ++k)
+        for (int u = 0; u < kB; ++u) v[u] = h[(g0 + u < G ? g0 + u : 0) * 256 + bin];
 #pragma unroll
-            for (int u = 0; u < kB; ++u) v[k][u] = h1[(int64_t)k * G * 256 + (g0 + u < G ? g0 + u : 0) * 256 + bin];
-#pragma unroll
-        for (int k = 0; k < NH; ++k)
-#pragma unroll
-            for (int u = 0; u < kB; ++u) {
-                const uint32_t x = g0 + u < G ? v[k][u] : 0u;
-                tot[k] += x;
-                pre[k] += g0 + u < g_me ? x : 0u;
-            }
+        for (int u = 0; u < kB; ++u) {
+            const uint32_t x = g0 + u < G ? v[u] : 0u;
+            t += x;
+            p += g0 + u < g_me ? x : 0u;
+        }
     }
+    *tot = t;
+    *pre = p;
 }
 
 __global__ void __launch_bounds__(kSplitThreads) topk_split_h1(TopkArgs a, int G) {
@@ -477,6 +473,9 @@ __global__ void __launch_bounds__(kSplitThreads) topk_split_h1(TopkArgs a, int G
     if (threadIdx.x < 256) r.h1[g * 256 + threadIdx.x] = hs[threadIdx.x];
 }
 
+// Second digit: every chunk finds the high byte d1 from the column totals of h1 and counts the low
+// bytes of its keys in bucket d1; it also leaves, for the third launch, the number of keys above
+// d1 in the chunks before it.
 __global__ void __launch_bounds__(kSplitThreads) topk_split_h2(TopkArgs a, int G) {
     const SplitRow r = split_row(a, G);
     const int g = blockIdx.x, tid = threadIdx.x;
@@ -484,86 +483,68 @@ __global__ void __launch_bounds__(kSplitThreads) topk_split_h2(TopkArgs a, int G
     __shared__ uint32_t hist[256 * 16];
     __shared__ uint32_t hs[256];
     __shared__ uint32_t d1, rem1;
+    __shared__ uint32_t wsum[kSplitThreads / 64];
     if (r.n <= r.K) return;
     uint32_t raw[kPer / 2];
     load_keys(r, lo, hi, raw);
-    uint32_t t1[1] = {0}, p1[1] = {0};
-    if (tid < 256) col_sums<1>(r.h1, G, 0, tid, t1, p1);
-    if (tid < 256) hs[tid] = t1[0];
+    uint32_t t1 = 0, p1 = 0;
+    if (tid < 256) col_sums(r.h1, G, g, tid, &t1, &p1);
+    if (tid < 256) hs[tid] = t1;
     __syncthreads();
     if (tid < 64) pick_digit(hs, (uint32_t)r.K, &d1, &rem1);
     __syncthreads();
     const uint32_t hb = d1;
+    uint32_t above;
+    block_incl_scan<kSplitThreads / 64>(tid < 256 && (uint32_t)tid > hb ? p1 : 0u, wsum, &above);
+    if (tid == 0) *(u32x4*)(r.meta + 4 * g) = u32x4{above, hb, rem1, 0u};
     keys_hist(raw, lo + (int64_t)kPer * tid, hi, hist, hs,
               [hb](uint32_t key) { return (key >> 8) == hb ? (int)(key & 255u) : -1; });
     if (tid < 256) r.h2[g * 256 + tid] = hs[tid];
 }
 
-// Fused schedule (a.th_cnt): this workgroup has read the row's histograms for the last time; the
-// last of the row's G workgroups to get here clears both (and the arrival counter), so the next
-// call's indexer adds into zeros and the workspace is left as it came.  Every workgroup of the row
-// comes here exactly once.
-__device__ __forceinline__ void th_arrive(const TopkArgs& a, const SplitRow& r, int G, uint32_t* last) {
-    if (!a.th_cnt) return;
-    const int64_t rowid = (int64_t)blockIdx.z * gridDim.y + blockIdx.y;
-    __syncthreads();  // (every histogram value this workgroup loaded has been used)
-    if (threadIdx.x == 0) *last = atomicAdd(&a.th_cnt[rowid], 1u) == (uint32_t)G - 1u;
-    __syncthreads();
-    if (*last) {
-        for (int j = threadIdx.x; j < G * 512; j += kSplitThreads) r.h1[j] = 0u;  // h1, then h2
-        if (threadIdx.x == 0) a.th_cnt[rowid] = 0u;
-    }
-}
-
+// Emission: the threshold key tau = (d1, d2) and the number rem of keys equal to it to keep; keys
+// above tau are kept, keys equal to it in index order until rem are taken.  Where the indexer made
+// h1, the workgroup clears its chunk of it for the next call.
 __global__ void __launch_bounds__(kSplitThreads) topk_split_emit(TopkArgs a, int G) {
     const SplitRow r = split_row(a, G);
     const int g = blockIdx.x, tid = threadIdx.x;
     const int64_t lo = (int64_t)g * kChunk, hi = min(lo + kChunk, r.n);
     const int kk = a.k;
-    __shared__ uint32_t th_last;
+    if (a.split_fused && tid < 256) r.h1[g * 256 + tid] = 0u;
     if (r.n <= r.K) {  // fewer candidates than k: all of them, in order
-        th_arrive(a, r, G, &th_last);
         for (int64_t j = lo + tid; j < lo + kChunk && j < kk; j += kSplitThreads)
             r.out[j] = j < r.n ? (int32_t)j : -1;
         if (g == G - 1)
             for (int64_t j = (int64_t)G * kChunk + tid; j < kk; j += kSplitThreads) r.out[j] = j < r.n ? (int32_t)j : -1;
         return;
     }
-    // one round: this thread's keys and (thread = bin) both histograms' columns
+    // one round: this thread's keys, the second launch's figures and (thread = bin) h2's column
     uint32_t raw[kPer / 2];
     load_keys(r, lo, hi, raw);
-    uint32_t tt[2] = {0, 0}, pp[2] = {0, 0};
-    if (tid < 256) col_sums<2>(r.h1, G, g, tid, tt, pp);
-    const uint32_t t1 = tt[0], p1 = pp[0], t2 = tt[1], p2 = pp[1];
-    __shared__ uint32_t tot1[256], tot2[256];
-    __shared__ uint32_t d1, rem1, d2, rem2;
+    const u32x4 mt = *(const u32x4*)(r.meta + 4 * g);
+    uint32_t t2 = 0, p2 = 0;
+    if (tid < 256) col_sums(r.h2, G, g, tid, &t2, &p2);
+    __shared__ uint32_t tot2[256];
+    __shared__ uint32_t d2, rem2;
     __shared__ uint32_t wsum[kSplitThreads / 64];
     __shared__ uint32_t base_gt, base_eq;
-    if (tid < 256) {
-        tot1[tid] = t1;
-        tot2[tid] = t2;
-    }
+    if (tid < 256) tot2[tid] = t2;
     __syncthreads();
-    th_arrive(a, r, G, &th_last);
-    if (tid < 64) pick_digit(tot1, (uint32_t)r.K, &d1, &rem1);
-    __syncthreads();
+    const uint32_t above1 = mt[0], d1 = mt[1], rem1 = mt[2];
     if (tid < 64) pick_digit(tot2, rem1, &d2, &rem2);
     __syncthreads();
     const uint32_t tau = (d1 << 8) | d2, rem = rem2;
     if (g == 0)
         for (int64_t j = r.K + tid; j < kk; j += kSplitThreads) r.out[j] = -1;
-    // keys above tau and equal to tau in the chunks before this one: thread = bin
+    // keys above tau and equal to tau in the chunks before this one: thread = low byte
     {
-        uint32_t gt = 0, eq = 0;
-        if (tid < 256) {
-            gt = ((uint32_t)tid > d1 ? p1 : 0u) + ((uint32_t)tid > d2 ? p2 : 0u);
-            eq = (uint32_t)tid == d2 ? p2 : 0u;
-        }
+        const uint32_t gt = tid < 256 && (uint32_t)tid > d2 ? p2 : 0u;
+        const uint32_t eq = tid < 256 && (uint32_t)tid == d2 ? p2 : 0u;
         uint32_t s1, s2;
         block_incl_scan<kSplitThreads / 64>(gt, wsum, &s1);
         block_incl_scan<kSplitThreads / 64>(eq, wsum, &s2);
         if (tid == 0) {
-            base_gt = s1;
+            base_gt = above1 + s1;
             base_eq = s2;
         }
         __syncthreads();
@@ -587,12 +568,12 @@ __global__ void __launch_bounds__(kSplitThreads) topk_split_emit(TopkArgs a, int
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
         if (e0 + u >= hi) break;
-        const uint32_t pos = gt_before + min(eq_before, rem);
+        const uint32_t pos = gt_before + min(eq_before, rem);  // < K for every kept key
         if (keys[u] > tau) {
-            r.out[pos] = (int32_t)(e0 + u);
+            if (pos < (uint32_t)r.K) r.out[pos] = (int32_t)(e0 + u);
             ++gt_before;
         } else if (keys[u] == tau) {
-            if (eq_before < rem) r.out[pos] = (int32_t)(e0 + u);
+            if (eq_before < rem && pos < (uint32_t)r.K) r.out[pos] = (int32_t)(e0 + u);
             ++eq_before;
         }
     }
@@ -612,7 +593,7 @@ size_t topk_ws_bytes(int32_t B, int32_t T, int64_t s_stride, int32_t score_dtype
     a.T = T;
     a.score_dtype = score_dtype;
     if (!use_split(a, s_stride)) return 0;
-    return (size_t)B * T * split_chunks(s_stride) * 512 * sizeof(uint32_t);
+    return (size_t)B * T * split_chunks(s_stride) * (512 + 4) * sizeof(uint32_t);
 }
 
 int topk_split_chunks(int32_t rows, int64_t max_n, int64_t s_stride, int32_t score_dtype) {
@@ -628,7 +609,7 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
     if (use_split(a, a.max_n)) {
         const int G = split_chunks(a.s_stride);
         dim3 grid((unsigned)G, (unsigned)a.T, (unsigned)a.B);
-        if (!a.th_cnt) hipLaunchKernelGGL(topk_split_h1, grid, dim3(kSplitThreads), 0, st, a, G);
+        if (!a.split_fused) hipLaunchKernelGGL(topk_split_h1, grid, dim3(kSplitThreads), 0, st, a, G);
         hipLaunchKernelGGL(topk_split_h2, grid, dim3(kSplitThreads), 0, st, a, G);
         hipLaunchKernelGGL(topk_split_emit, grid, dim3(kSplitThreads), 0, st, a, G);
         return hipGetLastError();
