@@ -893,7 +893,8 @@ def bench_projections(reps: int = 5, seed: int = 1006):
     """The linear maps around one attention layer (lca_linear / lca_grouped_out_proj), shaped as the
     pages' smaller model ([R] 4.2.1: hidden 4096, query compression 1024, 64 heads, output projection in
     8 groups of 1024) with this benchmark's heads of 512 + 64 and 16 x 128 indexer: a 4096-token
-    chunk (MFMA tiles) and one decode token (weights streamed once).  Weights N(0, 1/fan_in), bf16."""
+    chunk (MFMA tiles) and one decode token (weights streamed once).  Weights N(0, 1/fan_in), bf16.  Each
+    map is timed as `reps` launches replayed from one captured graph (HIP events around the replay)."""
     d, dq, H, c, HI, dI, g, dg = 4096, 1024, 64, C, 16, 128, 8, 1024
     gen = torch.Generator(device="cuda").manual_seed(seed)
 
@@ -913,24 +914,38 @@ def bench_projections(reps: int = 5, seed: int = 1006):
         out = torch.empty(T, d, dtype=torch.bfloat16, device="cuda")
         row = {}
         tot_ms, tot_fl, tot_by = 0.0, 0.0, 0.0
+        # one decode token streams each weight once: its reps read distinct copies (the replay touches more
+        # than the 256 MB memory-side cache for the large maps)
+        ncp = reps if T == 1 else 1
         for nm, k, n in maps + [("grouped_out_proj", H * c, d)]:
             if nm == "grouped_out_proj":
-                fn = lambda: lca.grouped_out_proj(o, wg, wo, mid, out, g=g)
+                cps = [(wg, wo)] + [(wg.clone(), wo.clone()) for _ in range(ncp - 1)]
+                fns = [lambda a=a, b=b: lca.grouped_out_proj(o, a, b, mid, out, g=g) for a, b in cps]
                 fl = 2.0 * T * (g * dg * (H // g) * c + d * g * dg)
                 by = 2.0 * (g * dg * (H // g) * c + d * g * dg + T * (H * c + 2 * g * dg + d))
             else:
                 y = torch.empty(T, n, dtype=torch.bfloat16, device="cuda")
-                fn = (lambda x=xs[k], w=ws[nm], y=y: lca.linear(x, w, y))
+                cps = [ws[nm]] + [ws[nm].clone() for _ in range(ncp - 1)]
+                fns = [lambda x=xs[k], w=w, y=y: lca.linear(x, w, y) for w in cps]
                 fl = 2.0 * T * n * k
                 by = 2.0 * (n * k + T * (k + n))
-            fn()
+            for fn in fns:
+                fn()
+            torch.cuda.synchronize()
+            # the reps as one captured graph: a decode token's launches are a few microseconds each, below
+            # the host's cost of an eager launch from Python
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                for r in range(reps):
+                    fns[r % len(fns)]()
+            gr.replay()
             torch.cuda.synchronize()
             s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             s.record()
-            for _ in range(reps):
-                fn()
+            gr.replay()
             e.record()
             torch.cuda.synchronize()
+            del gr, cps, fns
             ms = s.elapsed_time(e) / reps
             tot_ms, tot_fl, tot_by = tot_ms + ms, tot_fl + fl, tot_by + by
             row[nm] = dict(ms=ms, tflops=fl / (ms * 1e-3) / 1e12, gbs=by / (ms * 1e-3) / 1e9)
