@@ -34,6 +34,7 @@
 #include "device.h"
 #include "kernels.h"
 #include "rowstore.h"
+#include "trace.h"
 
 namespace lca {
 
@@ -1373,6 +1374,7 @@ __global__ void __launch_bounds__(256) kv_expand(ExpandArgs a) {
 
 hipError_t launch_kv_expand(const ExpandArgs& a, hipStream_t st) {
     if (a.max_count <= 0) return hipSuccess;
+    if (trace_on()) trace("  kv_expand: grid (%lld, %d) x 256, fp8 rows -> bf16", (long long)((a.max_count + 7) / 8), a.B);
     hipLaunchKernelGGL(kv_expand, dim3((unsigned)((a.max_count + 7) / 8), (unsigned)a.B), dim3(256), 0, st, a);
     return hipGetLastError();
 }
@@ -1395,6 +1397,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     if (rows <= 0) return hipSuccess;
     const int c = a.comp.d_nope + a.comp.d_rope;
     if (a.comp.fmt == LCA_F32) {
+        if (trace_on()) trace("  attn_f32: grid (%lld, %d) x 64", (long long)rows, a.H);
         hipLaunchKernelGGL(attn_f32, dim3((unsigned)rows, (unsigned)a.H), dim3(64), 0, st, a);
         return hipGetLastError();
     }
@@ -1405,6 +1408,10 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     // (same splits, same workspace layout)
     if (dec_launch(a, p)) {
         dim3 grid((unsigned)((ns + 7) / 8 * 8 * (a.H / 16)), (unsigned)a.T, (unsigned)a.B);
+        if (trace_on())
+            trace("  attn_dec<%s, %s>: grid (%u, %u, %u) x 256, %d split(s) of %lld slots%s", a.comp.fmt == LCA_FP8 ? "fp8" : "bf16",
+                  dense ? "dense" : "selected", grid.x, grid.y, grid.z, ns, (long long)p.len,
+                  a.app_x ? ", window store fused" : "");
         if (a.comp.fmt == LCA_FP8) {
             if (dense) hipLaunchKernelGGL((attn_dec<LCA_FP8, true, 4>), grid, dim3(256), 0, st, a, p.len, ns);
             else hipLaunchKernelGGL((attn_dec<LCA_FP8, false, 4>), grid, dim3(256), 0, st, a, p.len, ns);
@@ -1414,6 +1421,9 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
         }
     } else {
         dim3 grid((unsigned)rows, (unsigned)ns);
+        if (trace_on())
+            trace("  attn_mfma<%s, %s>: grid (%u, %u) x 512, %d split(s) of %lld slots", a.comp.fmt == LCA_FP8 ? "fp8" : "bf16",
+                  dense ? "dense" : "selected", grid.x, grid.y, ns, (long long)p.len);
         if (a.comp.fmt == LCA_FP8) {
             if (dense) hipLaunchKernelGGL((attn_mfma<LCA_FP8, true>), grid, dim3(512), 0, st, a, p.len, ns);
             else hipLaunchKernelGGL((attn_mfma<LCA_FP8, false>), grid, dim3(512), 0, st, a, p.len, ns);
@@ -1425,6 +1435,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ns <= 1) return e;
     const int groups = comb_groups(ns);
+    if (trace_on()) trace("  attn_combine: %d split(s), %d group(s)", ns, groups);
     if (groups == 1) {
         hipLaunchKernelGGL(attn_combine, dim3((unsigned)a.T, (unsigned)a.H, (unsigned)a.B),
                            dim3(kCombQuarters * kCombPer), 0, st, a, ns, 1);

@@ -7,12 +7,14 @@
 #include <cstdio>
 #include <climits>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
 #include "../../include/lca.h"
 #include "kernels.h"
 #include "status.h"
+#include "trace.h"
 
 namespace {
 
@@ -23,10 +25,19 @@ int fail(int code, const char* fmt, ...) {
     va_start(ap, fmt);
     vsnprintf(g_err, sizeof g_err, fmt, ap);
     va_end(ap);
+    if (lca::trace_on()) lca::trace("  -> error %d: %s", code, g_err);
     return code;
 }
 
+// one trace line per call (LCA_TRACE)
+#define LCA_TRACE_CALL(...)                         \
+    do {                                            \
+        if (lca::trace_on()) lca::trace(__VA_ARGS__); \
+    } while (0)
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+long long pos0(const int64_t* p) { return p ? (long long)p[0] : -1; }  // (traces only)
 
 int check_kv(const lca_kv& kv, const char* name, bool need_rows, bool allow_fp4) {
     if (kv.fmt == LCA_MXFP4 && !allow_fp4)
@@ -86,7 +97,23 @@ int set_error(int code, const char* fmt, ...) {
     va_start(ap, fmt);
     vsnprintf(g_err, sizeof g_err, fmt, ap);
     va_end(ap);
+    if (trace_on()) trace("  -> error %d: %s", code, g_err);
     return code;
+}
+bool trace_on() {
+    static const bool on = [] {
+        const char* e = getenv("LCA_TRACE");
+        return e && *e && strcmp(e, "0") != 0;
+    }();
+    return on;
+}
+void trace(const char* fmt, ...) {
+    char line[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(line, sizeof line, fmt, ap);
+    va_end(ap);
+    fprintf(stderr, "[lca] %s\n", line);
 }
 void clear_error() { g_err[0] = 0; }
 }  // namespace lca
@@ -102,6 +129,9 @@ int lca_kv_compress(const void* c_a, const void* z_a, const void* c_b, const voi
                     float eps, double rope_theta, int32_t m, int32_t overlap, int32_t B, int64_t n_rows,
                     int64_t in_stride, const int64_t* first_pos, lca_kv out, int32_t ring, void* stream) {
     g_err[0] = 0;
+    LCA_TRACE_CALL("lca_kv_compress B=%d rows=%lld in_dtype=%d m=%d overlap=%d out fmt=%d dims=%d+%d cap=%lld ring=%d "
+                   "first_pos[0]=%lld", B, (long long)n_rows, in_dtype, m, overlap, out.fmt, out.d_nope, out.d_rope,
+                   (long long)out.cap, ring, pos0(first_pos));
     if (!c_a || !z_a) return fail(LCA_EINVAL, "c_a / z_a is NULL");
     if (m < 1) return fail(LCA_EINVAL, "m must be >= 1 (got %d)", m);
     if (overlap != 0 && overlap != 1) return fail(LCA_EINVAL, "overlap must be 0 or 1");
@@ -154,6 +184,9 @@ int lca_indexer_score(const void* q, const float* w, const void* k, int32_t in_d
                       int32_t H_I, int32_t d_I, int32_t B, int32_t T, const int64_t* q_pos, int32_t m,
                       void* scores, int32_t score_dtype, int64_t s_stride, void* stream) {
     g_err[0] = 0;
+    LCA_TRACE_CALL("lca_indexer_score B=%d T=%d keys fmt=%d k_cap=%lld H_I=%d d_I=%d m=%d score_dtype=%d s_stride=%lld "
+                   "q_pos[0]=%lld", B, T, in_dtype, (long long)k_cap, H_I, d_I, m, score_dtype, (long long)s_stride,
+                   pos0(q_pos));
     if (!q || !k || !scores) return fail(LCA_EINVAL, "q, k and scores must be non-NULL");
     if (m < 1) return fail(LCA_EINVAL, "m must be >= 1");
     if (in_dtype != LCA_BF16 && in_dtype != LCA_F32) return fail(LCA_EDTYPE, "in_dtype must be bf16 or f32");
@@ -187,6 +220,8 @@ int lca_indexer_score_mxfp4(const void* q, const float* w, lca_kv k, int32_t H_I
                             int32_t T, const int64_t* q_pos, int32_t m, void* scores, int32_t score_dtype,
                             int64_t s_stride, void* stream) {
     g_err[0] = 0;
+    LCA_TRACE_CALL("lca_indexer_score_mxfp4 B=%d T=%d k_cap=%lld H_I=%d d_I=%d m=%d score_dtype=%d s_stride=%lld "
+                   "q_pos[0]=%lld", B, T, (long long)k.cap, H_I, d_I, m, score_dtype, (long long)s_stride, pos0(q_pos));
     if (!q || !scores) return fail(LCA_EINVAL, "q and scores must be non-NULL");
     if (m < 1) return fail(LCA_EINVAL, "m must be >= 1");
     if (k.fmt != LCA_MXFP4) return fail(LCA_EDTYPE, "keys must be stored MXFP4 (fmt %d)", LCA_MXFP4);
@@ -224,6 +259,8 @@ int lca_topk_select(const void* scores, int32_t score_dtype, int64_t s_stride, i
                     const int64_t* q_pos, int32_t m, int32_t k, int32_t* idx, void* ws, size_t ws_bytes,
                     void* stream) {
     g_err[0] = 0;
+    LCA_TRACE_CALL("lca_topk_select B=%d T=%d score_dtype=%d s_stride=%lld m=%d k=%d ws=%zu q_pos[0]=%lld", B, T,
+                   score_dtype, (long long)s_stride, m, k, ws_bytes, pos0(q_pos));
     if (!scores || !idx) return fail(LCA_EINVAL, "scores and idx must be non-NULL");
     if (m < 1) return fail(LCA_EINVAL, "m must be >= 1");
     if (k < 1) return fail(LCA_EINVAL, "k must be >= 1");
@@ -295,6 +332,8 @@ int lca_indexer_topk(const void* q, const float* w, const void* k, int64_t k_cap
                      int32_t B, int32_t T, const int64_t* q_pos, int32_t m, void* scores, int64_t s_stride,
                      int32_t topk, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
     g_err[0] = 0;
+    LCA_TRACE_CALL("lca_indexer_topk B=%d T=%d k_cap=%lld H_I=%d d_I=%d m=%d s_stride=%lld k=%d ws=%zu q_pos[0]=%lld",
+                   B, T, (long long)k_cap, H_I, d_I, m, (long long)s_stride, topk, ws_bytes, pos0(q_pos));
     if (!k) return fail(LCA_EINVAL, "k must be non-NULL");
     if (H_I != 16 || d_I != 128)
         return fail(LCA_ESHAPE, "the indexer supports H_I = 16, d_I = 128 (got %d x %d)", H_I, d_I);
@@ -326,6 +365,8 @@ static int indexer_topk_launch(lca::IndexerArgs ia, int32_t topk, int32_t* idx, 
     ta.k = topk; ta.idx = idx; ta.ws = ws; ta.max_n = max_vis; ta.q_pos = ia.q_pos;
     ia.th_h1 = (uint32_t*)ws;
     const int G = lca::topk_split_chunks(rows, max_vis, s_stride, LCA_BF16);
+    LCA_TRACE_CALL("  indexer_topk: %s schedule%s, %d chunk(s) of 16384 keys per row", G > 0 ? "split" : "row",
+                   G > 0 ? " (top-k: second-digit and emission launches)" : "", G > 0 ? G : 1);
     if (G > 0) {  // split schedule: the chunks' histograms; the top-k runs its last two launches
         ia.th_row = (int64_t)G * 256;
         ia.th_chunked = 1;
@@ -346,6 +387,8 @@ int lca_indexer_topk_mxfp4(const void* q, const float* w, lca_kv k, int32_t H_I,
                            int32_t T, const int64_t* q_pos, int32_t m, void* scores, int64_t s_stride, int32_t topk,
                            int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
     g_err[0] = 0;
+    LCA_TRACE_CALL("lca_indexer_topk_mxfp4 B=%d T=%d k_cap=%lld H_I=%d d_I=%d m=%d s_stride=%lld k=%d ws=%zu "
+                   "q_pos[0]=%lld", B, T, (long long)k.cap, H_I, d_I, m, (long long)s_stride, topk, ws_bytes, pos0(q_pos));
     if (k.fmt != LCA_MXFP4) return fail(LCA_EDTYPE, "keys must be stored MXFP4 (fmt %d)", LCA_MXFP4);
     int rc = check_kv(k, "k", true, true);
     if (rc) return rc;
@@ -566,6 +609,9 @@ int lca_csa_attn(const void* q, int32_t q_dtype, int32_t H, int32_t B, int32_t T
                  const float* sink, float sm_scale, double rope_theta, void* out, int32_t out_dtype,
                  float* lse, void* ws, size_t ws_bytes, void* stream) {
     g_err[0] = 0;
+    LCA_TRACE_CALL("lca_csa_attn B=%d T=%d H=%d q_dtype=%d comp fmt=%d cap=%lld m=%d k=%d win cap=%lld n_win=%d out_dtype=%d "
+                   "ws=%zu q_pos[0]=%lld", B, T, H, q_dtype, comp.fmt, (long long)comp.cap, m, k, (long long)win.cap, n_win,
+                   out_dtype, ws_bytes, pos0(q_pos));
     if (!idx) return fail(LCA_EINVAL, "idx is NULL");
     if (k < 1) return fail(LCA_EINVAL, "k must be >= 1");
     return attn_common(q, q_dtype, H, B, T, q_pos, comp, m, idx, k, win, n_win, sink, sm_scale, rope_theta,
@@ -578,6 +624,9 @@ int lca_csa_attn_append(const void* q, int32_t q_dtype, int32_t H, int32_t B, in
                         const float* sink, float sm_scale, double rope_theta, void* out, int32_t out_dtype,
                         float* lse, void* ws, size_t ws_bytes, void* stream) {
     g_err[0] = 0;
+    LCA_TRACE_CALL("lca_csa_attn_append B=%d T=%d H=%d q_dtype=%d comp fmt=%d cap=%lld m=%d k=%d win cap=%lld n_win=%d out_dtype=%d "
+                   "ws=%zu q_pos[0]=%lld", B, T, H, q_dtype, comp.fmt, (long long)comp.cap, m, k, (long long)win.cap, n_win,
+                   out_dtype, ws_bytes, pos0(q_pos));
     if (!idx) return fail(LCA_EINVAL, "idx is NULL");
     if (k < 1) return fail(LCA_EINVAL, "k must be >= 1");
     if (!x_win) return fail(LCA_EINVAL, "x_win is NULL");
@@ -591,6 +640,9 @@ int lca_hca_attn_append(const void* q, int32_t q_dtype, int32_t H, int32_t B, in
                         double rope_theta, void* out, int32_t out_dtype, float* lse, void* ws, size_t ws_bytes,
                         void* stream) {
     g_err[0] = 0;
+    LCA_TRACE_CALL("lca_hca_attn_append B=%d T=%d H=%d q_dtype=%d comp fmt=%d cap=%lld m=%d k=%d win cap=%lld n_win=%d out_dtype=%d "
+                   "ws=%zu q_pos[0]=%lld", B, T, H, q_dtype, comp.fmt, (long long)comp.cap, m, 0, (long long)win.cap, n_win,
+                   out_dtype, ws_bytes, pos0(q_pos));
     if (!x_win) return fail(LCA_EINVAL, "x_win is NULL");
     return attn_common(q, q_dtype, H, B, T, q_pos, comp, m, nullptr, 0, win, n_win, sink, sm_scale, rope_theta,
                        out, out_dtype, lse, ws, ws_bytes, stream, x_win, x_dtype, x_stride, gamma, eps);
@@ -601,6 +653,9 @@ int lca_hca_attn(const void* q, int32_t q_dtype, int32_t H, int32_t B, int32_t T
                  double rope_theta, void* out, int32_t out_dtype, float* lse, void* ws, size_t ws_bytes,
                  void* stream) {
     g_err[0] = 0;
+    LCA_TRACE_CALL("lca_hca_attn B=%d T=%d H=%d q_dtype=%d comp fmt=%d cap=%lld m=%d k=%d win cap=%lld n_win=%d out_dtype=%d "
+                   "ws=%zu q_pos[0]=%lld", B, T, H, q_dtype, comp.fmt, (long long)comp.cap, m, 0, (long long)win.cap, n_win,
+                   out_dtype, ws_bytes, pos0(q_pos));
     return attn_common(q, q_dtype, H, B, T, q_pos, comp, m, nullptr, 0, win, n_win, sink, sm_scale,
                        rope_theta, out, out_dtype, lse, ws, ws_bytes, stream);
 }
@@ -637,6 +692,9 @@ int lca_hca_attn_noalloc(const void* q, int32_t q_dtype, int32_t H, int32_t B, i
                          lca_kv comp, int32_t m, lca_kv win, int32_t n_win, const float* sink, float sm_scale,
                          double rope_theta, void* out, int32_t out_dtype, float* lse, void* stream) {
     g_err[0] = 0;
+    LCA_TRACE_CALL("lca_hca_attn_noalloc B=%d T=%d H=%d q_dtype=%d comp fmt=%d cap=%lld m=%d win cap=%lld n_win=%d "
+                   "out_dtype=%d q_pos[0]=%lld", B, T, H, q_dtype, comp.fmt, (long long)comp.cap, m, (long long)win.cap,
+                   n_win, out_dtype, pos0(q_pos));
     void* ws = nullptr;
     const int rc = scratch_for_current_device(&ws);
     if (rc) return rc;
@@ -649,6 +707,7 @@ int lca_linear(const void* x, int64_t ldx, int64_t sx, const void* w, int64_t ld
                int32_t y_dtype, int64_t ldy, int64_t sy, int32_t M, int32_t N, int32_t K, int32_t batch,
                void* stream) {
     g_err[0] = 0;
+    LCA_TRACE_CALL("lca_linear M=%d N=%d K=%d batch=%d y_dtype=%d", M, N, K, batch, y_dtype);
     if (!x || !w || !y) return fail(LCA_EINVAL, "x, w and y must be non-NULL");
     if (y_dtype != LCA_F32 && y_dtype != LCA_BF16) return fail(LCA_EDTYPE, "y_dtype must be f32 or bf16");
     if (M < 0 || N < 1 || batch < 1) return fail(LCA_ESHAPE, "bad M / N / batch");
@@ -669,6 +728,7 @@ int lca_linear(const void* x, int64_t ldx, int64_t sx, const void* w, int64_t ld
 int lca_grouped_out_proj(const void* o, int32_t T, int32_t H, int32_t c, int32_t g, const void* wg, int32_t d_g,
                          const void* wo, int32_t d, void* mid, void* out, int32_t out_dtype, void* stream) {
     g_err[0] = 0;
+    LCA_TRACE_CALL("lca_grouped_out_proj T=%d H=%d c=%d g=%d d_g=%d d=%d out_dtype=%d", T, H, c, g, d_g, d, out_dtype);
     if (!o || !wg || !wo || !mid || !out) return fail(LCA_EINVAL, "o, wg, wo, mid and out must be non-NULL");
     if (out_dtype != LCA_F32 && out_dtype != LCA_BF16) return fail(LCA_EDTYPE, "out_dtype must be f32 or bf16");
     if (T < 0 || H < 1 || c < 1 || g < 1 || H % g || d_g < 1 || d < 1)

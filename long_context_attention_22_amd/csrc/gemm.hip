@@ -15,6 +15,7 @@
 // outputs (their sums meet in LDS, added in a fixed order); with many, each wave has 4 of its own.
 #include "device.h"
 #include "kernels.h"
+#include "trace.h"
 
 namespace lca {
 
@@ -231,6 +232,7 @@ static void launch_gemm_t(const GemmArgs& a, hipStream_t st) {
         // workgroups, else 16
         const bool ks = (int64_t)a.N * a.batch < 8192;
         dim3 grid((unsigned)(ks ? (a.N + 3) / 4 : (a.N + 15) / 16), 1, (unsigned)a.batch);
+        if (trace_on()) trace("  gemv_stream<%d>: grid (%u, 1, %u) x 256%s", a.M, grid.x, grid.z, ks ? ", K split over waves" : "");
         if (ks) {
             if (a.M == 1) hipLaunchKernelGGL((gemv_stream<1, TY, true>), grid, dim3(256), 0, st, a);
             else if (a.M == 2) hipLaunchKernelGGL((gemv_stream<2, TY, true>), grid, dim3(256), 0, st, a);
@@ -243,6 +245,7 @@ static void launch_gemm_t(const GemmArgs& a, hipStream_t st) {
         return;
     }
     dim3 grid((unsigned)((a.N + kGT - 1) / kGT), (unsigned)((a.M + kGT - 1) / kGT), (unsigned)a.batch);
+    if (trace_on()) trace("  gemm_mfma: grid (%u, %u, %u) x 256, 128 x 128 tiles", grid.x, grid.y, grid.z);
     hipLaunchKernelGGL((gemm_mfma<TY>), grid, dim3(256), 0, st, a);
 }
 

@@ -15,6 +15,7 @@
 #include "device.h"
 #include "kernels.h"
 #include "rowstore.h"
+#include "trace.h"
 
 namespace lca {
 
@@ -311,6 +312,10 @@ hipError_t launch_kv_compress(const CompressArgs& a, hipStream_t st) {
     dim3 grid((unsigned)a.max_entries, (unsigned)a.B);
     dim3 block((unsigned)((c + 63) / 64 * 64));
     const bool bf = a.in_dtype == LCA_BF16;
+    if (trace_on())
+        trace("  compress: %s grid (%u, %u), %lld entr%s per sequence", a.m == 1 && !a.overlap && a.out.d_rope <= 64
+              ? "kv_store_rows" : bf && c % 8 == 0 && c <= kPoolMaxC ? "kv_pool_wide" : "kv_compress_kernel", grid.x, grid.y,
+              (long long)a.max_entries, a.max_entries == 1 ? "y" : "ies");
     if (a.m == 1 && !a.overlap && a.out.d_rope <= 64) {
         switch (a.out.fmt) {
             case LCA_F32:
