@@ -186,15 +186,16 @@ size_t lca_topk_workspace_size(int32_t B, int32_t T, int64_t s_stride, int32_t k
  * bf16 get the scores of lca_indexer_score (q, w, k bf16 as there; H_I = 16, d_I = 128) and idx
  * [B][T][k] int32 the selection of lca_topk_select on those scores, bit for bit.  While it stores
  * the scores, the indexer also counts their high bytes (the top-k's first radix digit) with LDS and
- * device atomics: per row and 16384-key chunk when the rows are few and long (the top-k's split
+ * device atomics: per row and 4096-key chunk when the rows are few and long (the top-k's split
  * schedule: its last two launches run), else per row (its row schedule: each row's workgroup skips
  * the first of its passes over the scores).
  * ws: device workspace of lca_indexer_topk_workspace_size(B, T, s_stride, k) bytes.  It must be
  * ZEROED BEFORE ITS FIRST USE and must not be shared with other calls (lca_topk_select writes the
  * same histograms without clearing them): every call leaves it ready for the next one, also inside
  * a captured graph -- the first-pass histograms, at the workspace's start, are zeroed again (per
- * row 256 words per 16384-key chunk in the split schedule, 256 words in the row schedule); what
- * follows them holds the top-k's own per-call figures, which need no initialisation.  Errors as
+ * row 128 words of 16-bit counts per 4096-key chunk in the split schedule, 256 words in the row
+ * schedule); what follows them holds the top-k's own per-call figures, which need no
+ * initialisation.  Errors as
  * lca_indexer_score and lca_topk_select; LCA_EWORKSPACE when ws is NULL or too small.
  */
 int lca_indexer_topk(const void* q, const float* w, const void* k, int64_t k_cap, int32_t H_I, int32_t d_I,

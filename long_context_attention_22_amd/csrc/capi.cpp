@@ -288,7 +288,7 @@ int lca_topk_select(const void* scores, int32_t score_dtype, int64_t s_stride, i
 
 // Workspace of lca_indexer_topk for B x T query rows: the top-k's first-pass histograms as the indexer
 // builds them, from the workspace's first byte.  Split schedule (few long rows): per row its
-// 16384-key chunks' histograms, then the top-k's own second-pass histograms and figures (which need
+// kTopkChunk-key chunks' histograms, then the top-k's own second-pass histograms and figures (which need
 // no zeros).  Row schedule: one histogram per row.  A call clears the first-pass histograms again.
 
 static int indexer_topk_launch(lca::IndexerArgs ia, int32_t topk, int32_t* idx, void* ws, size_t ws_bytes,
@@ -365,10 +365,11 @@ static int indexer_topk_launch(lca::IndexerArgs ia, int32_t topk, int32_t* idx, 
     ta.k = topk; ta.idx = idx; ta.ws = ws; ta.max_n = max_vis; ta.q_pos = ia.q_pos;
     ia.th_h1 = (uint32_t*)ws;
     const int G = lca::topk_split_chunks(rows, max_vis, s_stride, LCA_BF16);
-    LCA_TRACE_CALL("  indexer_topk: %s schedule%s, %d chunk(s) of 16384 keys per row", G > 0 ? "split" : "row",
-                   G > 0 ? " (top-k: second-digit and emission launches)" : "", G > 0 ? G : 1);
+    LCA_TRACE_CALL("  indexer_topk: %s schedule%s, %d chunk(s) of %d keys per row", G > 0 ? "split" : "row",
+                   G > 0 ? " (top-k: second-digit and emission launches)" : "", G > 0 ? G : 1,
+                   G > 0 ? lca::kTopkChunk : (int)s_stride);
     if (G > 0) {  // split schedule: the chunks' histograms; the top-k runs its last two launches
-        ia.th_row = (int64_t)G * 256;
+        ia.th_row = (int64_t)G * lca::kTopkHistWords;
         ia.th_chunked = 1;
         ta.split_fused = 1;
     } else {      // row schedule: one histogram per row; the top-k skips its first pass

@@ -63,17 +63,20 @@ __device__ __forceinline__ void store_count(TS* p, float v, uint32_t* hist, bool
 }
 
 // The fused top-k pass's LDS histograms (one per token of the workgroup) into the top-k's workspace:
-// row (b, i) at th_h1 + (b T + i) th_row, plus (key_lo / 16384) 256 when the top-k takes its chunked
-// (split) schedule.  Only nonzero bins cost a device atomic.
+// row (b, i) at th_h1 + (b T + i) th_row, plus (key_lo / kTopkChunk) kTopkHistWords in 16-bit counts
+// when the top-k takes its chunked (split) schedule, else 32-bit counts.  Only nonzero bins cost a
+// device atomic.
 template <int TOK>
 __device__ __forceinline__ void flush_hist(const uint32_t* hist, uint32_t* th_h1, int64_t th_row, int th_chunked,
                                            int64_t row0, int ntok, int64_t key_lo) {
     __syncthreads();
-    const int64_t coff = th_chunked ? (key_lo >> 14) * 256 : 0;
+    const int bin = threadIdx.x;
+    const int64_t off = th_chunked ? (key_lo >> kTopkChunkLog2) * kTopkHistWords + (bin >> 1) : bin;
+    const int sh = th_chunked ? 16 * (bin & 1) : 0;
 #pragma unroll
     for (int tk = 0; tk < TOK; ++tk) {
-        const uint32_t c = hist[tk * 256 + threadIdx.x];
-        if (tk < ntok && c) atomicAdd(th_h1 + (row0 + tk) * th_row + coff + threadIdx.x, c);
+        const uint32_t c = hist[tk * 256 + bin];
+        if (tk < ntok && c) atomicAdd(th_h1 + (row0 + tk) * th_row + off, c << sh);
     }
 }
 
@@ -401,9 +404,9 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t st) {
     // MXFP4 keys are 68 bytes: a single-token launch gives each workgroup twice the keys
     if (fp4 && tok == 1) kpw *= 2;
     if (kpw < 256) kpw = 256;
-    if (a.th_h1 && a.th_chunked) {  // a workgroup's keys must lie in one 16384-key chunk of the top-k
+    if (a.th_h1 && a.th_chunked) {  // a workgroup's keys must lie in one chunk of the top-k
         int64_t p = 256;
-        while (p < kpw && p < 16384) p <<= 1;
+        while (p < kpw && p < kTopkChunk) p <<= 1;
         kpw = p;
     }
     const int64_t nsplit = (a.max_vis + kpw - 1) / kpw;

@@ -57,13 +57,21 @@ struct IndexerArgs {
     int64_t max_vis;
     // Fused first pass of the top-k (bf16 scores): the high-byte histograms of each query row's visible
     // scores, added with device atomics into th_h1 (row r = b T + i at th_h1 + r * th_row; zero on
-    // entry) -- per 16384-key chunk (chunk g at + 256 g, th_row = 256 G) when th_chunked (the top-k's
-    // split schedule), else one per row (its row schedule, th_row = 256).  NULL = off.
+    // entry) -- per kTopkChunk-key chunk when th_chunked (the top-k's split schedule: chunk g at
+    // + kTopkHistWords g in 16-bit counts, th_row = kTopkHistWords G), else one per row in 32-bit
+    // counts (its row schedule, th_row = 256).  NULL = off.
     uint32_t* th_h1;
     int64_t th_row;
     int32_t th_chunked;
 };
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t st);
+
+// Keys per chunk of the top-k's split schedule (one workgroup each, a power of two).
+constexpr int kTopkChunkLog2 = 12;
+constexpr int kTopkChunk = 1 << kTopkChunkLog2;
+// A chunk's 256-bin histogram holds 16-bit counts (at most kTopkChunk per bin), two bins per word:
+// bin 2j in the low half of word j, bin 2j + 1 in the high half.
+constexpr int kTopkHistWords = 128;
 
 struct TopkArgs {
     const void* scores;

@@ -10,17 +10,19 @@
 // compacts the winners with a block-wide exclusive scan, which yields the
 // ascending output and the lower-index tie rule directly.  Histograms live
 // in LDS with 16 copies (one per lane mod 16) so that lanes sharing a bin
-// rarely hit the same LDS word; rows are read with 16-byte loads, four in
-// flight per thread.
+// rarely hit the same LDS word.
 //
 // Two schedules:
-//   row   -- one 1024-thread workgroup per row (many rows: prefill).
+//   row   -- one 1024-thread workgroup per row (many rows: prefill); rows are
+//            read with 16-byte loads, four in flight per thread.
 //   split -- bf16 rows that are few and long (decode): each row is cut into
-//            16384-key chunks, one workgroup per chunk, in three launches
+//            kTopkChunk-key chunks, one workgroup per chunk, in three launches
 //            (high-byte histograms, low-byte histograms of the chosen high
 //            byte, emit).  Every workgroup re-derives the digits and its
 //            output offset from the per-chunk histograms in the workspace,
-//            so no launch needs a grid-wide barrier or zeroed memory.
+//            so no launch needs a grid-wide barrier or zeroed memory.  Short
+//            chunks spread the per-key work of these latency-bound launches
+//            over many CUs; the price is more histogram columns to sum.
 #include "device.h"
 #include "kernels.h"
 
@@ -28,7 +30,8 @@ namespace lca {
 
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
-constexpr int kChunk = 16384;          // keys per workgroup in the split schedule
+constexpr int kChunk = kTopkChunk;     // keys per workgroup in the split schedule
+constexpr int kSplitMin = 16384;       // rows longer than this may take it
 constexpr int kSplitThreads = 512;
 
 __device__ __forceinline__ uint32_t mono_key(uint16_t h) {
@@ -103,6 +106,27 @@ __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* wsum, 
     __syncthreads();
     *total = tot;
     return v + off;
+}
+
+// sums of a and of b over the workgroup's NW waves, in every thread (wsum: 2 NW words)
+template <int NW>
+__device__ __forceinline__ void block_sum2(uint32_t a, uint32_t b, uint32_t* wsum, uint32_t* sa, uint32_t* sb) {
+    const int wv = threadIdx.x >> 6;
+    a = wave_lane63(wave_incl_scan(a));
+    b = wave_lane63(wave_incl_scan(b));
+    if ((threadIdx.x & 63) == 0) {
+        wsum[wv] = a;
+        wsum[NW + wv] = b;
+    }
+    __syncthreads();
+    uint32_t x = 0, y = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        x += wsum[w];
+        y += wsum[NW + w];
+    }
+    *sa = x;
+    *sb = y;
 }
 
 // Find the digit d with (count of digits > d) < rem <= (count of digits >= d).
@@ -343,21 +367,22 @@ __global__ void __launch_bounds__(kTopkThreads) topk_row(TopkArgs a) {
 // split schedule (bf16 scores)
 // ---------------------------------------------------------------------------
 // Grid (G, T, B): chunk g = blockIdx.x of row i = blockIdx.y of sequence b = blockIdx.z.  Each
-// launch is short and bound by latency, so every kernel reads its arguments, its 32 keys per
+// launch is short and bound by latency, so every kernel reads its arguments, its keys per
 // thread and every histogram column it needs in one round of loads before any of them is used.
-//   Workspace of R = B T rows: the rows' high-byte histograms h1 [R][G][256], then their low-byte
-// histograms h2 [R][G][256] (keys with the chosen high byte), then per row and chunk g the word
-// quadruple (keys above the chosen high byte in the chunks before g, that byte, the keys still to
-// take from its bucket, 0) that the second launch leaves for the third.  Only h1 may need zeros:
+//   Workspace of R = B T rows: the rows' high-byte histograms h1 [R][G][kTopkHistWords], then their
+// low-byte histograms h2 [R][G][kTopkHistWords] (keys with the chosen high byte; both in 16-bit
+// counts, two bins per word), then per row and chunk g the word quadruple (keys above the chosen
+// high byte in the chunks before g, that byte, the keys still to take from its bucket, 0) that the
+// second launch leaves for the third.  Only h1 may need zeros:
 // where the indexer adds it up (TopkArgs::split_fused) the third launch clears it again, each
 // workgroup its own chunk, since by then the second launch -- its last reader -- has ended.
-constexpr int kPer = kChunk / kSplitThreads;  // 32 keys per thread
+constexpr int kPer = kChunk / kSplitThreads;  // keys per thread
 struct SplitRow {
     const uint16_t* row;
     int32_t* out;
     int64_t n, K, stride;
-    uint32_t* h1;    // [G][256] high-byte histograms of this row
-    uint32_t* h2;    // [G][256] low-byte histograms (keys with the chosen high byte)
+    uint32_t* h1;    // [G][kTopkHistWords] high-byte histograms of this row
+    uint32_t* h2;    // [G][kTopkHistWords] low-byte histograms (keys with the chosen high byte)
     uint32_t* meta;  // [G][4] (above d1 before chunk g, d1, rem1, 0)
 };
 
@@ -380,15 +405,15 @@ __device__ __forceinline__ SplitRow split_row(const TopkArgs& a, int G) {
     r.row = (const uint16_t*)sc + rowid * stride;
     r.out = idx + rowid * k;
     const int64_t rows = (int64_t)gridDim.y * gridDim.z;
-    r.h1 = (uint32_t*)ws + rowid * (int64_t)G * 256;
-    r.h2 = (uint32_t*)ws + (rows + rowid) * (int64_t)G * 256;
-    r.meta = (uint32_t*)ws + 2 * rows * (int64_t)G * 256 + rowid * (int64_t)G * 4;
+    r.h1 = (uint32_t*)ws + rowid * (int64_t)G * kTopkHistWords;
+    r.h2 = (uint32_t*)ws + (rows + rowid) * (int64_t)G * kTopkHistWords;
+    r.meta = (uint32_t*)ws + 2 * rows * (int64_t)G * kTopkHistWords + rowid * (int64_t)G * 4;
     return r;
 }
 
-// This thread's 32 consecutive scores of chunk [lo, hi) as bf16 pairs (element lo + 32 tid + 2q in
-// the low half of raw[q]).  Elements at or past hi are never counted: a thread whose 32 keys lie
-// inside the row's s_stride reads them as two 16-byte pairs whatever their validity, the others
+// This thread's kPer consecutive scores of chunk [lo, hi) as bf16 pairs (element lo + kPer tid + 2q
+// in the low half of raw[q]).  Elements at or past hi are never counted: a thread whose keys lie
+// inside the row's s_stride reads them as 16-byte vectors whatever their validity, the others
 // element by element.
 __device__ __forceinline__ void load_keys(const SplitRow& r, int64_t lo, int64_t hi, uint32_t* raw) {
     const int64_t e0 = lo + (int64_t)kPer * threadIdx.x;
@@ -412,6 +437,62 @@ __device__ __forceinline__ void load_keys(const SplitRow& r, int64_t lo, int64_t
 
 __device__ __forceinline__ uint32_t raw_key(const uint32_t* raw, int u) {
     return mono_key((uint16_t)(raw[u >> 1] >> (16 * (u & 1))));
+}
+
+// Comparisons of mono_key(h) with a key tau done on the raw bf16 bits h: the key grows with h on the
+// non-negative half and falls with h on the negative half (-0 counts as +0), so the raw values whose
+// key is above tau form one interval, and those whose key equals tau are one value (two for tau =
+// +0: +0 and -0).  Raw values sit zero-extended in 32 bits; kNoKey, what a lane past the row holds,
+// passes neither test.
+constexpr uint32_t kNoKey = 0x10000u;
+struct KeyCut {
+    uint32_t gt_lo, gt_span;   // key(h) > tau  <=>  h - gt_lo < gt_span (unsigned)
+    uint32_t eq_mask, eq_raw;  // key(h) == tau <=>  (h & eq_mask) == eq_raw
+    __device__ __forceinline__ bool gt(uint32_t h) const { return h - gt_lo < gt_span; }
+    __device__ __forceinline__ bool eq(uint32_t h) const { return (h & eq_mask) == eq_raw; }
+};
+// tau in [-1, 0xffff]; -1 stands below every key
+__device__ __forceinline__ KeyCut key_cut(int tau) {
+    KeyCut c;
+    if (tau < 0) {
+        c = KeyCut{0u, 0x10000u, 0x1ffffu, 0x20000u};
+    } else if (tau >= 0x8000) {  // a non-negative value with raw bits rt
+        const uint32_t rt = (uint32_t)tau & 0x7fffu;
+        c = KeyCut{rt + 1u, 0x7fffu - rt, rt == 0u ? 0x17fffu : 0x1ffffu, rt};
+    } else {  // a negative value with raw bits rt (0x8000, -0, is no key: the interval then takes it in)
+        const uint32_t rt = ~(uint32_t)tau & 0xffffu;
+        c = KeyCut{0u, rt == 0x8000u ? 0x8001u : rt, 0x1ffffu, rt == 0x8000u ? 0x20000u : rt};
+    }
+    return c;
+}
+
+__device__ __forceinline__ uint32_t lane_count(bool p) {
+    return (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(p));
+}
+// lanes below this one in the mask
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// The second and third launches hold a chunk wave by wave: wave w has keys lo + kWaveKeys w + 64 u +
+// lane for u < kBlk, so each u is 64 consecutive keys across the wave, and counts and ranks in index
+// order come from lane masks (ballot, mbcnt) instead of per-thread loops.
+constexpr int kWaveKeys = kChunk / (kSplitThreads / 64);
+constexpr int kBlk = kWaveKeys / 64;  // = kPer
+__device__ __forceinline__ int64_t lane_first(int64_t lo) {
+    return lo + (int64_t)(threadIdx.x >> 6) * kWaveKeys + (threadIdx.x & 63);
+}
+// The loads take any key inside the row's s_stride, so that their addresses need no position; keys
+// at or past hi (visible count, chunk end) become kNoKey afterwards.
+__device__ __forceinline__ void load_lane_keys(const SplitRow& r, int64_t lo, uint32_t* h) {
+    const int64_t e = lane_first(lo);
+#pragma unroll
+    for (int u = 0; u < kBlk; ++u) h[u] = e + 64 * u < r.stride ? (uint32_t)r.row[e + 64 * u] : kNoKey;
+}
+__device__ __forceinline__ void mask_lane_keys(int64_t lo, int64_t hi, uint32_t* h) {
+    const int64_t e = lane_first(lo);
+#pragma unroll
+    for (int u = 0; u < kBlk; ++u) h[u] = e + 64 * u < hi ? h[u] : kNoKey;
 }
 
 // histogram (16 LDS copies, one per lane mod 16) of bin_of(key) over this thread's valid keys,
@@ -439,25 +520,48 @@ __device__ __forceinline__ void keys_hist(const uint32_t* raw, int64_t e0, int64
     __syncthreads();
 }
 
-// Column sums of bin `bin` over the G chunk histograms h[g][256]: the total and the sum over the
-// chunks before g_me.  All loads of a batch of 24 chunks go out before any sum (one round for
-// G <= 24).
-__device__ __forceinline__ void col_sums(const uint32_t* h, int G, int g_me, int bin, uint32_t* tot, uint32_t* pre) {
-    constexpr int kB = 24;
-    uint32_t t = 0, p = 0;
-    for (int g0 = 0; g0 < G; g0 += kB) {
+// Column sums over the G chunk histograms h[g][kTopkHistWords] (16-bit counts, two bins per word):
+// for bins 2t and 2t + 1 of thread t < 128, the totals over every chunk and the sums over the chunks
+// before g_me.  The 512 threads share the loads: thread (t = tid mod 128, c = tid / 128) takes the
+// chunks g = c mod 4, all of a batch of kB at once (one round for up to 4 kB chunks); the four parts
+// meet in LDS (red, 16 x 128 words).  Every thread of the workgroup must call it.
+__device__ __forceinline__ void col_sums(const uint32_t* h, int G, int g_me, uint32_t* red, uint32_t* tot,
+                                         uint32_t* pre) {
+    constexpr int kB = 18;
+    const int tid = threadIdx.x, t = tid & 127, cg = tid >> 7;  // (cg is uniform over a wave)
+    uint32_t tl = 0, th = 0, pl = 0, ph = 0;
+    for (int g0 = cg; g0 < G; g0 += 4 * kB) {
         uint32_t v[kB];
 #pragma unroll
-        for (int u = 0; u < kB; ++u) v[u] = h[(g0 + u < G ? g0 + u : 0) * 256 + bin];
+        for (int u = 0; u < kB; ++u) v[u] = g0 + 4 * u < G ? h[(g0 + 4 * u) * kTopkHistWords + t] : 0u;
 #pragma unroll
         for (int u = 0; u < kB; ++u) {
-            const uint32_t x = g0 + u < G ? v[u] : 0u;
-            t += x;
-            p += g0 + u < g_me ? x : 0u;
+            const uint32_t lo = v[u] & 0xffffu, hi = v[u] >> 16;
+            tl += lo;
+            th += hi;
+            pl += g0 + 4 * u < g_me ? lo : 0u;
+            ph += g0 + 4 * u < g_me ? hi : 0u;
         }
     }
-    *tot = t;
-    *pre = p;
+    red[(4 * cg + 0) * 128 + t] = tl;
+    red[(4 * cg + 1) * 128 + t] = th;
+    red[(4 * cg + 2) * 128 + t] = pl;
+    red[(4 * cg + 3) * 128 + t] = ph;
+    __syncthreads();
+    if (tid < 128) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            tot[j] = red[j * 128 + t] + red[(4 + j) * 128 + t] + red[(8 + j) * 128 + t] + red[(12 + j) * 128 + t];
+            pre[j] = red[(2 + j) * 128 + t] + red[(6 + j) * 128 + t] + red[(10 + j) * 128 + t] +
+                     red[(14 + j) * 128 + t];
+        }
+    }
+}
+
+// the reduced LDS histogram hs[256] as one chunk's packed column (16-bit counts)
+__device__ __forceinline__ void store_packed(const uint32_t* hs, uint32_t* col) {
+    const int t = threadIdx.x;
+    if (t < kTopkHistWords) col[t] = hs[2 * t] | (hs[2 * t + 1] << 16);
 }
 
 __global__ void __launch_bounds__(kSplitThreads) topk_split_h1(TopkArgs a, int G) {
@@ -470,7 +574,7 @@ __global__ void __launch_bounds__(kSplitThreads) topk_split_h1(TopkArgs a, int G
     uint32_t raw[kPer / 2];
     load_keys(r, lo, hi, raw);
     keys_hist(raw, lo + (int64_t)kPer * threadIdx.x, hi, hist, hs, [](uint32_t key) { return (int)(key >> 8); });
-    if (threadIdx.x < 256) r.h1[g * 256 + threadIdx.x] = hs[threadIdx.x];
+    store_packed(hs, r.h1 + g * kTopkHistWords);
 }
 
 // Second digit: every chunk finds the high byte d1 from the column totals of h1 and counts the low
@@ -479,27 +583,52 @@ __global__ void __launch_bounds__(kSplitThreads) topk_split_h1(TopkArgs a, int G
 __global__ void __launch_bounds__(kSplitThreads) topk_split_h2(TopkArgs a, int G) {
     const SplitRow r = split_row(a, G);
     const int g = blockIdx.x, tid = threadIdx.x;
-    const int64_t lo = (int64_t)g * kChunk, hi = min(lo + kChunk, r.n);
-    __shared__ uint32_t hist[256 * 16];
+    const int64_t lo = (int64_t)g * kChunk;
+    __shared__ uint32_t hist[256 * 16];  // (also the column sums' LDS)
     __shared__ uint32_t hs[256];
     __shared__ uint32_t d1, rem1;
-    __shared__ uint32_t wsum[kSplitThreads / 64];
-    if (r.n <= r.K) return;
-    uint32_t raw[kPer / 2];
-    load_keys(r, lo, hi, raw);
-    uint32_t t1 = 0, p1 = 0;
-    if (tid < 256) col_sums(r.h1, G, g, tid, &t1, &p1);
-    if (tid < 256) hs[tid] = t1;
+    __shared__ uint32_t wsum[2 * (kSplitThreads / 64)];
+    uint32_t h[kBlk];
+    load_lane_keys(r, lo, h);
+    uint32_t t1[2] = {0u, 0u}, p1[2] = {0u, 0u};
+    col_sums(r.h1, G, g, hist, t1, p1);
+    if (r.n <= r.K) return;  // (uniform) every candidate is kept: the emit launch lists them
+    mask_lane_keys(lo, min(lo + kChunk, r.n), h);
+    if (tid < 128) {
+        hs[2 * tid] = t1[0];
+        hs[2 * tid + 1] = t1[1];
+    }
     __syncthreads();
     if (tid < 64) pick_digit(hs, (uint32_t)r.K, &d1, &rem1);
     __syncthreads();
     const uint32_t hb = d1;
-    uint32_t above;
-    block_incl_scan<kSplitThreads / 64>(tid < 256 && (uint32_t)tid > hb ? p1 : 0u, wsum, &above);
+    uint32_t above, unused;
+    const uint32_t pa = tid < 128 ? ((uint32_t)(2 * tid) > hb ? p1[0] : 0u) + ((uint32_t)(2 * tid + 1) > hb ? p1[1] : 0u)
+                                  : 0u;
+    block_sum2<kSplitThreads / 64>(pa, 0u, wsum, &above, &unused);
     if (tid == 0) *(u32x4*)(r.meta + 4 * g) = u32x4{above, hb, rem1, 0u};
-    keys_hist(raw, lo + (int64_t)kPer * tid, hi, hist, hs,
-              [hb](uint32_t key) { return (key >> 8) == hb ? (int)(key & 255u) : -1; });
-    if (tid < 256) r.h2[g * 256 + tid] = hs[tid];
+    // low bytes of the keys in bucket hb: keys above (hb, 0) - 1 and not above (hb, 255); the bucket
+    // holds keys of one sign, so the low byte is the raw one, inverted for negatives
+    const KeyCut in_lo = key_cut((int)(hb << 8) - 1), in_hi = key_cut((int)((hb << 8) | 255u));
+    const uint32_t flip = hb >= 0x80u ? 0u : 255u;
+    for (int j = tid; j < 256 * 16; j += kSplitThreads) hist[j] = 0;
+    __syncthreads();
+    const int sub = tid & 15;
+#pragma unroll
+    for (int u = 0; u < kBlk; ++u) {
+        const bool in = in_lo.gt(h[u]) && !in_hi.gt(h[u]);
+        if (__builtin_amdgcn_ballot_w64(in) != 0 && in)
+            atomicAdd(&hist[(((h[u] & 255u) ^ flip) << 4) + sub], 1u);
+    }
+    __syncthreads();
+    if (tid < 256) {
+        uint32_t s = 0;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) s += hist[tid * 16 + ((c + tid) & 15)];
+        hs[tid] = s;
+    }
+    __syncthreads();
+    store_packed(hs, r.h2 + g * kTopkHistWords);
 }
 
 // Emission: the threshold key tau = (d1, d2) and the number rem of keys equal to it to keep; keys
@@ -508,27 +637,32 @@ __global__ void __launch_bounds__(kSplitThreads) topk_split_h2(TopkArgs a, int G
 __global__ void __launch_bounds__(kSplitThreads) topk_split_emit(TopkArgs a, int G) {
     const SplitRow r = split_row(a, G);
     const int g = blockIdx.x, tid = threadIdx.x;
-    const int64_t lo = (int64_t)g * kChunk, hi = min(lo + kChunk, r.n);
+    const int64_t lo = (int64_t)g * kChunk;
     const int kk = a.k;
-    if (a.split_fused && tid < 256) r.h1[g * 256 + tid] = 0u;
-    if (r.n <= r.K) {  // fewer candidates than k: all of them, in order
+    if (a.split_fused && tid < kTopkHistWords) r.h1[g * kTopkHistWords + tid] = 0u;
+    // one round: this lane's keys, the second launch's figures and h2's columns
+    uint32_t h[kBlk];
+    load_lane_keys(r, lo, h);
+    const u32x4 mt = *(const u32x4*)(r.meta + 4 * g);
+    __shared__ uint32_t red[16 * 128];
+    uint32_t t2[2] = {0u, 0u}, p2[2] = {0u, 0u};
+    col_sums(r.h2, G, g, red, t2, p2);
+    if (r.n <= r.K) {  // (uniform) fewer candidates than k: all of them, in order
         for (int64_t j = lo + tid; j < lo + kChunk && j < kk; j += kSplitThreads)
             r.out[j] = j < r.n ? (int32_t)j : -1;
         if (g == G - 1)
             for (int64_t j = (int64_t)G * kChunk + tid; j < kk; j += kSplitThreads) r.out[j] = j < r.n ? (int32_t)j : -1;
         return;
     }
-    // one round: this thread's keys, the second launch's figures and (thread = bin) h2's column
-    uint32_t raw[kPer / 2];
-    load_keys(r, lo, hi, raw);
-    const u32x4 mt = *(const u32x4*)(r.meta + 4 * g);
-    uint32_t t2 = 0, p2 = 0;
-    if (tid < 256) col_sums(r.h2, G, g, tid, &t2, &p2);
+    const int64_t hi = min(lo + kChunk, r.n);
+    mask_lane_keys(lo, hi, h);
     __shared__ uint32_t tot2[256];
     __shared__ uint32_t d2, rem2;
-    __shared__ uint32_t wsum[kSplitThreads / 64];
-    __shared__ uint32_t base_gt, base_eq;
-    if (tid < 256) tot2[tid] = t2;
+    __shared__ uint32_t wsum[2 * (kSplitThreads / 64)];
+    if (tid < 128) {
+        tot2[2 * tid] = t2[0];
+        tot2[2 * tid + 1] = t2[1];
+    }
     __syncthreads();
     const uint32_t above1 = mt[0], d1 = mt[1], rem1 = mt[2];
     if (tid < 64) pick_digit(tot2, rem1, &d2, &rem2);
@@ -536,53 +670,62 @@ __global__ void __launch_bounds__(kSplitThreads) topk_split_emit(TopkArgs a, int
     const uint32_t tau = (d1 << 8) | d2, rem = rem2;
     if (g == 0)
         for (int64_t j = r.K + tid; j < kk; j += kSplitThreads) r.out[j] = -1;
-    // keys above tau and equal to tau in the chunks before this one: thread = low byte
+    // keys above tau and equal to tau in the chunks before this one (threads t < 128: low bytes 2t, 2t + 1)
+    uint32_t base_gt, base_eq;
     {
-        const uint32_t gt = tid < 256 && (uint32_t)tid > d2 ? p2 : 0u;
-        const uint32_t eq = tid < 256 && (uint32_t)tid == d2 ? p2 : 0u;
-        uint32_t s1, s2;
-        block_incl_scan<kSplitThreads / 64>(gt, wsum, &s1);
-        block_incl_scan<kSplitThreads / 64>(eq, wsum, &s2);
-        if (tid == 0) {
-            base_gt = above1 + s1;
-            base_eq = s2;
-        }
-        __syncthreads();
+        const uint32_t b0 = 2 * (uint32_t)tid, b1 = b0 + 1;
+        const uint32_t gt = tid < 128 ? (b0 > d2 ? p2[0] : 0u) + (b1 > d2 ? p2[1] : 0u) : 0u;
+        const uint32_t eq = tid < 128 ? (b0 == d2 ? p2[0] : 0u) + (b1 == d2 ? p2[1] : 0u) : 0u;
+        block_sum2<kSplitThreads / 64>(gt, eq, wsum, &base_gt, &base_eq);
+        base_gt += above1;
     }
-    const int64_t e0 = lo + (int64_t)kPer * tid;
-    uint32_t keys[kPer];
+    // this wave's keys above tau and equal to it, then the waves before it
+    const KeyCut cut = key_cut((int)tau);
     uint32_t ngt = 0, neq = 0;
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-        const bool valid = e0 + u < hi;
-        keys[u] = valid ? mono_key((uint16_t)(raw[u >> 1] >> (16 * (u & 1)))) : 0u;
-        ngt += (valid && keys[u] > tau) ? 1u : 0u;
-        neq += (valid && keys[u] == tau) ? 1u : 0u;
+    for (int u = 0; u < kBlk; ++u) {
+        ngt += lane_count(cut.gt(h[u]));
+        neq += lane_count(cut.eq(h[u]));
     }
-    uint32_t t;
-    const uint32_t packed = ngt | (neq << 16);  // at most 16384 each
-    const uint32_t excl = block_incl_scan<kSplitThreads / 64>(packed, wsum, &t) - packed;
-    uint32_t gt_before = base_gt + (excl & 0xffffu);
-    uint32_t eq_before = base_eq + (excl >> 16);
-    if (ngt + neq == 0) return;
+    __shared__ uint32_t wgt[kSplitThreads / 64], weq[kSplitThreads / 64];
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if ((tid & 63) == 0) {
+        wgt[wv] = ngt;
+        weq[wv] = neq;
+    }
+    __syncthreads();
+    uint32_t gt_run = base_gt, eq_run = base_eq;
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-        if (e0 + u >= hi) break;
-        const uint32_t pos = gt_before + min(eq_before, rem);  // < K for every kept key
-        if (keys[u] > tau) {
-            if (pos < (uint32_t)r.K) r.out[pos] = (int32_t)(e0 + u);
-            ++gt_before;
-        } else if (keys[u] == tau) {
-            if (eq_before < rem && pos < (uint32_t)r.K) r.out[pos] = (int32_t)(e0 + u);
-            ++eq_before;
-        }
+    for (int w = 0; w < kSplitThreads / 64; ++w) {
+        gt_run += w < wv ? wgt[w] : 0u;
+        eq_run += w < wv ? weq[w] : 0u;
+    }
+    gt_run = __builtin_amdgcn_readfirstlane(gt_run);  // (wave-uniform: kept in scalar registers)
+    eq_run = __builtin_amdgcn_readfirstlane(eq_run);
+    if (ngt + neq == 0) return;
+    // the tests are made again below rather than kept: 64 lane masks would not fit the scalar registers
+#pragma unroll
+    for (int u = 0; u < kBlk; ++u) asm volatile("" : "+v"(h[u]));
+    // in index order, 64 keys at a time: a key's list position is the keys above tau before it plus
+    // the ties before it (at most rem); ties at or past rem are dropped
+    const int64_t e = lane_first(lo);
+#pragma unroll
+    for (int u = 0; u < kBlk; ++u) {
+        const bool gk = cut.gt(h[u]), qk = cut.eq(h[u]);
+        const uint64_t gm = __builtin_amdgcn_ballot_w64(gk), qm = __builtin_amdgcn_ballot_w64(qk);
+        if ((gm | qm) == 0) continue;
+        const uint32_t gb = gt_run + lanes_below(gm), qb = eq_run + lanes_below(qm);
+        const uint32_t pos = gb + min(qb, rem);  // < K for every kept key
+        if ((gk | (qk & (qb < rem))) & (pos < (uint32_t)r.K)) r.out[pos] = (int32_t)(e + 64 * u);
+        gt_run += (uint32_t)__builtin_popcountll(gm);
+        eq_run += (uint32_t)__builtin_popcountll(qm);
     }
 }
 
 // split schedule for few long bf16 rows
 static bool use_split(const TopkArgs& a, int64_t max_n) {
     const int64_t rows = (int64_t)a.B * a.T;
-    return a.score_dtype == LCA_BF16 && rows < 128 && max_n > kChunk;
+    return a.score_dtype == LCA_BF16 && rows < 128 && max_n > kSplitMin;
 }
 
 static int split_chunks(int64_t max_n) { return (int)((max_n + kChunk - 1) / kChunk); }
@@ -593,7 +736,7 @@ size_t topk_ws_bytes(int32_t B, int32_t T, int64_t s_stride, int32_t score_dtype
     a.T = T;
     a.score_dtype = score_dtype;
     if (!use_split(a, s_stride)) return 0;
-    return (size_t)B * T * split_chunks(s_stride) * (512 + 4) * sizeof(uint32_t);
+    return (size_t)B * T * split_chunks(s_stride) * (2 * kTopkHistWords + 4) * sizeof(uint32_t);
 }
 
 int topk_split_chunks(int32_t rows, int64_t max_n, int64_t s_stride, int32_t score_dtype) {

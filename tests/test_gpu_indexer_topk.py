@@ -30,11 +30,11 @@ def _inputs(seed, B, cap, ties=False):
 
 def _check_ws(ws, B, T, s_stride, q_pos, m=4):
     """Every call leaves the part of the workspace that must start at zero zeroed again: the first-pass
-    histograms at its start, 256 words per row and 16384-key chunk when the rows are few and long (the
-    split schedule), else 256 words per row."""
+    histograms at its start, 128 words (16-bit counts) per row and 4096-key chunk when the rows are few
+    and long (more than 16384 candidates: the split schedule), else 256 words per row."""
     rows, max_vis = B * T, max((p + T) // m for p in q_pos)
     split = rows < 128 and max_vis > 16384
-    nz = rows * 1024 * (-(-s_stride // 16384) if split else 1)
+    nz = rows * (512 * -(-s_stride // 4096) if split else 1024)
     assert nz <= ws.numel()
     assert int(ws[:nz].count_nonzero()) == 0
 
