@@ -528,10 +528,10 @@ __global__ void __launch_bounds__(512) attn_mfma(AttnArgs a, int64_t split_len, 
         const int64_t pr = ((int64_t)split * nrows + rowid) * a.H + h;
         float* dst = wo + pr * kC + dbase + 4 * g4;
 #pragma unroll
-        for (int nb = 0; nb < 18; ++nb) *(f32x4*)(dst + 16 * nb) = o[nb];
+        for (int nb = 0; nb < 18; ++nb) __builtin_nontemporal_store(o[nb], (f32x4*)(dst + 16 * nb));
         if (g4 == 0 && dh == 0) {
-            wml[2 * pr] = mrun;
-            wml[2 * pr + 1] = lrun;
+            __builtin_nontemporal_store(mrun, wml + 2 * pr);
+            __builtin_nontemporal_store(lrun, wml + 2 * pr + 1);
         }
         return;
     }
@@ -1146,11 +1146,13 @@ __global__ void __launch_bounds__(256) attn_dec(AttnArgs a, int64_t split_len, i
         float* wml = wo + (int64_t)nsplit * nrows * a.H * kC;
         const int64_t pr = ((int64_t)split * nrows + rowid) * a.H + h;
         float* dst = wo + pr * kC + dbase + 4 * g4;
+        // non-temporal: the merge launch reads them once; written through now, they are not left
+        // dirty in L2 for the end of the launch to write back
 #pragma unroll
-        for (int nb = 0; nb < 9; ++nb) *(f32x4*)(dst + 16 * nb) = o[nb];
+        for (int nb = 0; nb < 9; ++nb) __builtin_nontemporal_store(o[nb], (f32x4*)(dst + 16 * nb));
         if (g4 == 0 && wv == 0) {
-            wml[2 * pr] = mrun;
-            wml[2 * pr + 1] = lrun;
+            __builtin_nontemporal_store(mrun, wml + 2 * pr);
+            __builtin_nontemporal_store(lrun, wml + 2 * pr + 1);
         }
         return;
     }
