@@ -44,6 +44,33 @@ __device__ __forceinline__ uint32_t mono_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Comparisons of mono_key(h) with a key tau done on the raw bf16 bits h: the key grows with h on the
+// non-negative half and falls with h on the negative half (-0 counts as +0), so the raw values whose
+// key is above tau form one interval, and those whose key equals tau are one value (two for tau =
+// +0: +0 and -0).  Raw values sit zero-extended in 32 bits; kNoKey, what a lane past the row holds,
+// passes neither test.
+constexpr uint32_t kNoKey = 0x10000u;
+struct KeyCut {
+    uint32_t gt_lo, gt_span;   // key(h) > tau  <=>  h - gt_lo < gt_span (unsigned)
+    uint32_t eq_mask, eq_raw;  // key(h) == tau <=>  (h & eq_mask) == eq_raw
+    __device__ __forceinline__ bool gt(uint32_t h) const { return h - gt_lo < gt_span; }
+    __device__ __forceinline__ bool eq(uint32_t h) const { return (h & eq_mask) == eq_raw; }
+};
+// tau in [-1, 0xffff]; -1 stands below every key
+__device__ __forceinline__ KeyCut key_cut(int tau) {
+    KeyCut c;
+    if (tau < 0) {
+        c = KeyCut{0u, 0x10000u, 0x1ffffu, 0x20000u};
+    } else if (tau >= 0x8000) {  // a non-negative value with raw bits rt
+        const uint32_t rt = (uint32_t)tau & 0x7fffu;
+        c = KeyCut{rt + 1u, 0x7fffu - rt, rt == 0u ? 0x17fffu : 0x1ffffu, rt};
+    } else {  // a negative value with raw bits rt (0x8000, -0, is no key: the interval then takes it in)
+        const uint32_t rt = ~(uint32_t)tau & 0xffffu;
+        c = KeyCut{0u, rt == 0x8000u ? 0x8001u : rt, 0x1ffffu, rt == 0x8000u ? 0x20000u : rt};
+    }
+    return c;
+}
+
 template <typename TS>
 struct Vec;
 template <>
@@ -61,7 +88,9 @@ struct Vec<float> {
     }
 };
 
-// f(index, key) for every element of row[lo, hi); NT threads, order unspecified.
+// f(index, key) for every element of row[lo, hi); NT threads, order unspecified.  Each thread has
+// kVecs 16-byte loads in flight per round.
+constexpr int kVecs = 8;
 template <typename TS, int NT, typename F>
 __device__ __forceinline__ void for_each_key(const TS* row, int64_t lo, int64_t hi, F f) {
     constexpr int V = Vec<TS>::N;
@@ -73,13 +102,13 @@ __device__ __forceinline__ void for_each_key(const TS* row, int64_t lo, int64_t 
     const int64_t b0 = lo + head;
     const int64_t nv = (hi - b0) / V;
     const u32x4* vp = (const u32x4*)(row + b0);
-    for (int64_t v = tid; v < nv; v += 4 * NT) {
-        u32x4 x[4];
+    for (int64_t v = tid; v < nv; v += kVecs * NT) {
+        u32x4 x[kVecs];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < kVecs; ++j)
             if (v + j * NT < nv) x[j] = vp[v + j * NT];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < kVecs; ++j) {
             if (v + j * NT < nv) {
 #pragma unroll
                 for (int u = 0; u < V; ++u) f(b0 + (v + j * NT) * V + u, Vec<TS>::key(x[j], u));
@@ -87,6 +116,15 @@ __device__ __forceinline__ void for_each_key(const TS* row, int64_t lo, int64_t 
         }
     }
     for (int64_t e = b0 + nv * V + tid; e < hi; e += NT) f(e, mono_key(row[e]));
+}
+
+// lanes of the wave where p holds
+__device__ __forceinline__ uint32_t lane_count(bool p) {
+    return (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(p));
+}
+// lanes below this one in the mask
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 // inclusive prefix sum over the workgroup; also returns the total
@@ -259,6 +297,142 @@ __device__ __forceinline__ void row_tail16(const TS* row, int64_t n, int32_t* ou
     }
 }
 
+// Emission of a row (threshold key tau, rem keys equal to it to take, K in all): the row in index
+// order, kRowIter keys a round; wave w holds keys base + kRowWave w + 64 u + lane (u < kRowBlk), so
+// each u is 64 consecutive keys across the wave and counts and ranks come from lane masks.  The next
+// round's keys are loaded before this round's are ranked (the pass is otherwise one memory round trip
+// per round); the waves' counts meet in LDS, double-buffered by round, one barrier a round.
+constexpr int kRowBlk = 16;
+constexpr int kRowWave = 64 * kRowBlk;
+constexpr int kRowIter = kRowWave * kTopkWaves;
+// (branch-free, so that the compiler can count the loads in flight and wait for one round's loads
+// only: a round inside the first `lim` keys of the row -- n or the row's stride -- loads its keys
+// at constant offsets from one address, the last ones re-read key lim - 1 past it; keys past n are
+// masked where they are used)
+template <typename TS>
+__device__ __forceinline__ void row_load(const TS* row, int64_t lim, int64_t base, uint32_t (&raw)[kRowBlk]) {
+    const int64_t e = base + (int64_t)(threadIdx.x >> 6) * kRowWave + (threadIdx.x & 63);
+    if (base + kRowIter <= lim) {  // (uniform)
+        const TS* p = row + e;
+#pragma unroll
+        for (int u = 0; u < kRowBlk; ++u) {
+            if constexpr (sizeof(TS) == 2) raw[u] = (uint32_t)p[64 * u];
+            else raw[u] = __float_as_uint(p[64 * u]);
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < kRowBlk; ++u) {
+            const int64_t j = min(e + 64 * u, lim - 1);
+            if constexpr (sizeof(TS) == 2) raw[u] = (uint32_t)row[j];
+            else raw[u] = __float_as_uint(row[j]);
+        }
+    }
+}
+// the tests against tau on raw score bits: interval tests for bf16, monotone keys for f32
+template <typename TS>
+struct RowCut;
+template <>
+struct RowCut<uint16_t> {
+    KeyCut c;
+    __device__ explicit RowCut(uint32_t tau) : c(key_cut((int)tau)) {}
+    __device__ __forceinline__ bool gt(uint32_t r) const { return c.gt(r); }
+    __device__ __forceinline__ bool eq(uint32_t r) const { return c.eq(r); }
+};
+template <>
+struct RowCut<float> {
+    uint32_t tau;
+    __device__ explicit RowCut(uint32_t t) : tau(t) {}
+    __device__ __forceinline__ bool gt(uint32_t r) const { return mono_key(__uint_as_float(r)) > tau; }
+    __device__ __forceinline__ bool eq(uint32_t r) const { return mono_key(__uint_as_float(r)) == tau; }
+};
+
+// one round of row_emit: ranks and stores the keys in cur (round base), with the next round's loads
+// into nxt issued first; returns true once every kept key is out.  TAIL: the round reaches the row's
+// end (keys at or past n are masked; other rounds test nothing but the keys).
+template <typename TS, bool TAIL>
+__device__ __forceinline__ bool row_round(const TS* row, int64_t n, int64_t stride, int32_t* out, const RowCut<TS>& cut,
+                                          uint32_t rem, uint32_t K, int64_t base, int wv, int64_t lane0,
+                                          uint32_t (&cur)[kRowBlk], uint32_t (&nxt)[kRowBlk], u32x4 (&wc)[2 * kTopkWaves / 4],
+                                          uint32_t& gt_base, uint32_t& eq_base) {
+    if (!TAIL) row_load<TS>(row, stride, base + kRowIter, nxt);  // (a round before the last: the next exists)
+    const int64_t e = base + lane0;
+    const int lim = TAIL ? (int)min(max(n - e, (int64_t)0), (int64_t)kRowWave) : kRowWave;  // keys of this lane's column
+    uint32_t ngt = 0, neq = 0;
+#pragma unroll
+    for (int u = 0; u < kRowBlk; ++u) {
+        const bool v = !TAIL || 64 * u < lim;
+        ngt += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(v && cut.gt(cur[u])));
+        neq += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(v && cut.eq(cur[u])));
+    }
+    uint32_t* wcw = (uint32_t*)wc;  // the waves' counts: (above, equal) of wave w at 2w, 2w + 1
+    if ((threadIdx.x & 63) == 0) {
+        wcw[2 * wv] = ngt;
+        wcw[2 * wv + 1] = neq;
+    }
+    __syncthreads();
+    uint32_t gr = gt_base, qr = eq_base, tg = 0, tq = 0;
+#pragma unroll
+    for (int j = 0; j < 2 * kTopkWaves / 4; ++j) {  // (16-byte broadcast reads)
+        const u32x4 x = wc[j];
+        gr += (2 * j < wv ? x[0] : 0u) + (2 * j + 1 < wv ? x[2] : 0u);
+        qr += (2 * j < wv ? x[1] : 0u) + (2 * j + 1 < wv ? x[3] : 0u);
+        tg += x[0] + x[2];
+        tq += x[1] + x[3];
+    }
+    gr = __builtin_amdgcn_readfirstlane(gr);
+    qr = __builtin_amdgcn_readfirstlane(qr);
+    if (ngt + neq != 0) {
+#pragma unroll
+        for (int u = 0; u < kRowBlk; ++u) asm volatile("" : "+v"(cur[u]));  // (the tests again, not kept)
+#pragma unroll
+        for (int u = 0; u < kRowBlk; ++u) {
+            const bool v = !TAIL || 64 * u < lim;
+            const bool gk = v && cut.gt(cur[u]), qk = v && cut.eq(cur[u]);
+            const uint64_t gm = __builtin_amdgcn_ballot_w64(gk), qm = __builtin_amdgcn_ballot_w64(qk);
+            if ((gm | qm) == 0) continue;
+            const uint32_t gb = gr + lanes_below(gm), qb = qr + lanes_below(qm);
+            const uint32_t pos = gb + min(qb, rem);  // < K for every kept key
+            if ((gk | (qk & (qb < rem))) & (pos < K)) out[pos] = (int32_t)(e + 64 * u);
+            gr += (uint32_t)__builtin_popcountll(gm);
+            qr += (uint32_t)__builtin_popcountll(qm);
+        }
+    }
+    gt_base += tg;
+    eq_base += tq;
+    return TAIL || (gt_base + min(eq_base, rem) >= K && eq_base >= rem);  // (uniform)
+}
+
+template <typename TS>
+__device__ __forceinline__ void row_emit(const TS* row, int64_t n, int64_t stride, int32_t* out, uint32_t tau,
+                                         uint32_t rem, uint32_t K) {
+    __shared__ u32x4 wc[2][2 * kTopkWaves / 4];
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int64_t lane0 = (int64_t)wv * kRowWave + (threadIdx.x & 63);
+    const RowCut<TS> cut(tau);
+    uint32_t ra[kRowBlk], rb[kRowBlk];
+    row_load<TS>(row, stride, 0, ra);
+    uint32_t gt_base = 0, eq_base = 0;
+    // two rounds per trip, the register sets alternating (no copies between rounds), the LDS counts
+    // of consecutive rounds in different buffers
+    for (int64_t base = 0;; base += 2 * kRowIter) {
+        if (base + kRowIter < n) {
+            if (row_round<TS, false>(row, n, stride, out, cut, rem, K, base, wv, lane0, ra, rb, wc[0], gt_base, eq_base))
+                break;
+        } else {
+            row_round<TS, true>(row, n, stride, out, cut, rem, K, base, wv, lane0, ra, rb, wc[0], gt_base, eq_base);
+            break;
+        }
+        const int64_t b2 = base + kRowIter;
+        if (b2 + kRowIter < n) {
+            if (row_round<TS, false>(row, n, stride, out, cut, rem, K, b2, wv, lane0, rb, ra, wc[1], gt_base, eq_base))
+                break;
+        } else {
+            row_round<TS, true>(row, n, stride, out, cut, rem, K, b2, wv, lane0, rb, ra, wc[1], gt_base, eq_base);
+            break;
+        }
+    }
+}
+
 template <typename TS, int BITS>
 __global__ void __launch_bounds__(kTopkThreads) topk_row(TopkArgs a) {
     const int b = blockIdx.y, i = blockIdx.x;
@@ -327,40 +501,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_row(TopkArgs a) {
         __syncthreads();
     }
     const uint32_t tau = prefix;
-
-    uint32_t gt_base = 0, eq_base = 0;
-    for (int64_t base = 0; base < n; base += 8 * kTopkThreads) {
-        const int64_t e0 = base + 8 * (int64_t)tid;
-        uint32_t keys[8];
-        uint32_t ngt = 0, neq = 0;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const bool valid = e0 + u < n;
-            keys[u] = valid ? mono_key(row[e0 + u]) : 0u;
-            ngt += (valid && keys[u] > tau) ? 1u : 0u;
-            neq += (valid && keys[u] == tau) ? 1u : 0u;
-        }
-        uint32_t tot;
-        const uint32_t packed = ngt | (neq << 16);
-        const uint32_t excl = block_incl_scan<kTopkWaves>(packed, wsum, &tot) - packed;
-        uint32_t gt_before = gt_base + (excl & 0xffffu);
-        uint32_t eq_before = eq_base + (excl >> 16);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            if (e0 + u >= n) break;
-            const uint32_t pos = gt_before + min(eq_before, rem);  // < K for every kept key
-            if (keys[u] > tau) {
-                if (pos < (uint32_t)K) out[pos] = (int32_t)(e0 + u);
-                ++gt_before;
-            } else if (keys[u] == tau) {
-                if (eq_before < rem && pos < (uint32_t)K) out[pos] = (int32_t)(e0 + u);
-                ++eq_before;
-            }
-        }
-        gt_base += tot & 0xffffu;
-        eq_base += tot >> 16;
-        if (gt_base + min(eq_base, rem) >= (uint32_t)K && eq_base >= rem) break;  // all found
-    }
+    row_emit<TS>(row, n, a.s_stride, out, tau, rem, (uint32_t)K);
 }
 
 // ---------------------------------------------------------------------------
@@ -437,41 +578,6 @@ __device__ __forceinline__ void load_keys(const SplitRow& r, int64_t lo, int64_t
 
 __device__ __forceinline__ uint32_t raw_key(const uint32_t* raw, int u) {
     return mono_key((uint16_t)(raw[u >> 1] >> (16 * (u & 1))));
-}
-
-// Comparisons of mono_key(h) with a key tau done on the raw bf16 bits h: the key grows with h on the
-// non-negative half and falls with h on the negative half (-0 counts as +0), so the raw values whose
-// key is above tau form one interval, and those whose key equals tau are one value (two for tau =
-// +0: +0 and -0).  Raw values sit zero-extended in 32 bits; kNoKey, what a lane past the row holds,
-// passes neither test.
-constexpr uint32_t kNoKey = 0x10000u;
-struct KeyCut {
-    uint32_t gt_lo, gt_span;   // key(h) > tau  <=>  h - gt_lo < gt_span (unsigned)
-    uint32_t eq_mask, eq_raw;  // key(h) == tau <=>  (h & eq_mask) == eq_raw
-    __device__ __forceinline__ bool gt(uint32_t h) const { return h - gt_lo < gt_span; }
-    __device__ __forceinline__ bool eq(uint32_t h) const { return (h & eq_mask) == eq_raw; }
-};
-// tau in [-1, 0xffff]; -1 stands below every key
-__device__ __forceinline__ KeyCut key_cut(int tau) {
-    KeyCut c;
-    if (tau < 0) {
-        c = KeyCut{0u, 0x10000u, 0x1ffffu, 0x20000u};
-    } else if (tau >= 0x8000) {  // a non-negative value with raw bits rt
-        const uint32_t rt = (uint32_t)tau & 0x7fffu;
-        c = KeyCut{rt + 1u, 0x7fffu - rt, rt == 0u ? 0x17fffu : 0x1ffffu, rt};
-    } else {  // a negative value with raw bits rt (0x8000, -0, is no key: the interval then takes it in)
-        const uint32_t rt = ~(uint32_t)tau & 0xffffu;
-        c = KeyCut{0u, rt == 0x8000u ? 0x8001u : rt, 0x1ffffu, rt == 0x8000u ? 0x20000u : rt};
-    }
-    return c;
-}
-
-__device__ __forceinline__ uint32_t lane_count(bool p) {
-    return (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(p));
-}
-// lanes below this one in the mask
-__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
-    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 // The second and third launches hold a chunk wave by wave: wave w has keys lo + kWaveKeys w + 64 u +
