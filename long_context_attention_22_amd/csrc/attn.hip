@@ -585,6 +585,7 @@ __global__ void __launch_bounds__(512) attn_mfma(AttnArgs a, int64_t split_len, 
 // latency: the arguments, each thread's first eight partials and wave 0's (m, l) pairs are all
 // fetched in one round, before the weights are formed (wave 0, through LDS).
 constexpr int kCombGroups = 8, kCombQuarters = 4, kCombPer = kC / 4 / kCombQuarters;  // 36 threads x 4 dims
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr int kCombThreads = kCombGroups * kCombPer;
 static int comb_groups(int nsplit) { return nsplit > 32 ? 8 : nsplit > 16 ? 4 : nsplit > 8 ? 2 : 1; }
 // quad = 0: one workgroup per (row, head, dim quarter), ng groups of 36 threads splitting the splits;
@@ -628,16 +629,24 @@ __global__ void __launch_bounds__(kCombThreads) attn_combine(AttnArgs a, int nsp
         vp0[u] = p0[jx * stride + dp / 4];
     }
     if (tid < 64) {
-        // (m, l) of splits lane, lane + 64, ..: the first pair in the same round as the partials
-        float M = -INFINITY;
-        for (int j = lane; j < nsplit; j += 64) M = fmaxf(M, wml[2 * ((j * nrows + rowid) * H + h)]);
+        // (m, l) of splits lane, lane + 64, ..: split `lane`'s pair is loaded once, in the same round
+        // as the partials, and kept for the weights (one round trip, not two, for up to 64 splits)
+        f32x2 ml0 = {-INFINITY, 0.0f};
+        if (lane < nsplit) ml0 = *(const f32x2*)(wml + 2 * (((int64_t)lane * nrows + rowid) * H + h));
+        float M = ml0[0];
+        for (int j = lane + 64; j < nsplit; j += 64) M = fmaxf(M, wml[2 * ((j * nrows + rowid) * H + h)]);
         M = wave_max_dpp(M);
         float mu = M;
         const float z = sink ? sink[h] * kLog2e : -INFINITY;
         if (sink) mu = fmaxf(M, z);
         const float muse = mu == -INFINITY ? 0.0f : mu;
         float den = 0.0f;
-        for (int j = lane; j < nsplit; j += 64) {
+        if (lane < nsplit) {
+            const float wgt = exp2f(ml0[0] - muse);
+            wsp[lane] = wgt;
+            den = ml0[1] * wgt;
+        }
+        for (int j = lane + 64; j < nsplit; j += 64) {
             const int64_t pr = (j * nrows + rowid) * H + h;
             const float wgt = exp2f(wml[2 * pr] - muse);
             wsp[j] = wgt;
