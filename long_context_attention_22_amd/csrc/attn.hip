@@ -844,21 +844,6 @@ __device__ __forceinline__ void dec_load(DecRegs<FMT>& R, int ncs, int w_row, in
 // rows of invalid slots become zeros; flags[r] = slot r valid.
 template <int FMT>
 __device__ __forceinline__ void dec_store(DecRegs<FMT>& R, uint16_t* Kt, uint8_t* flags, int hw, int c) {
-    constexpr int kN = DecRegs<FMT>::kN;
-    if (__builtin_amdgcn_ballot_w64(R.ok != 0xfu)) {  // wave-uniform
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const bool ok = (R.ok >> u) & 1u;
-#pragma unroll
-            for (int q = 0; q < kN; ++q)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) R.v[u][q][i] = ok ? R.v[u][q][i] : 0u;
-            if constexpr (FMT == LCA_FP8) R.sc[u] = ok ? R.sc[u] : 0.0f;
-        }
-        const bool okr = (R.ok >> (c >> 3)) & 1u;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) R.rp[i] = okr ? R.rp[i] : 0u;
-    }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int r = hw + 8 * u;
@@ -881,6 +866,26 @@ __device__ __forceinline__ void dec_store(DecRegs<FMT>& R, uint16_t* Kt, uint8_t
         if (c == 0) flags[r] = (R.ok >> u) & 1u;
     }
     put8(Kt, hw + 8 * (c >> 3), kDN / 8 + (c & 7), R.rp);
+    // Rows of invalid slots (a range's last tile, CSA padding: rare, wave-uniform test) are
+    // overwritten with zeros, so that codes read from row 0 -- NaN ones included -- never reach the
+    // products.  (Clearing the registers before the conversion instead was computed ahead of the
+    // test for every tile.)
+    if (__builtin_amdgcn_ballot_w64(R.ok != 0xfu)) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if ((R.ok >> u) & 1u) continue;
+            const int r = hw + 8 * u;
+            if constexpr (FMT == LCA_FP8) {
+                put8(Kt, r, 2 * c, z);
+                put8(Kt, r, 2 * c + 1, z);
+            } else {
+                put8(Kt, r, c, z);
+                put8(Kt, r, c + 32, z);
+            }
+        }
+        if (!((R.ok >> (c >> 3)) & 1u)) put8(Kt, hw + 8 * (c >> 3), kDN / 8 + (c & 7), z);
+    }
 }
 
 // Tile row trow (if in [0, 32)) is the query row's own window row: after dec_store, the threads that
