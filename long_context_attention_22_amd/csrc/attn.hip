@@ -908,8 +908,12 @@ __device__ __forceinline__ void dec_fix_row(uint16_t* Kt, int hw, int c, const u
 // Grid (x, T, B): query row i = blockIdx.y of sequence b = blockIdx.z, so the row's position
 // comes from the first batch of argument loads.  Along x (a multiple of 8 workgroups, so x mod 8
 // is the XCD): x = 8 j + xcd, head group j mod ng, split (j / ng) * 8 + xcd.
-template <int FMT, bool DENSE, int NP>
+// MT: tiles per split of the launch (its longest split): the tile loop is unrolled for exactly MT
+// tiles and prefetches NPE = min(NP, MT) ahead, so no load is issued for a tile past the split's
+// end (the launch picks MT from the plan).
+template <int FMT, bool DENSE, int NP, int MT>
 __global__ void __launch_bounds__(256) attn_dec(AttnArgs a, int64_t split_len, int nsplit) {
+    constexpr int NPE = NP < MT ? NP : MT;
     __shared__ __attribute__((aligned(16))) uint16_t Kt[3][kTileElems];
     __shared__ __attribute__((aligned(16))) f32x4 Sx[2][4][2][64];  // partial scores, two tiles
     __shared__ uint32_t vflag[3][kKT / 4];
@@ -1001,9 +1005,9 @@ __global__ void __launch_bounds__(256) attn_dec(AttnArgs a, int64_t split_len, i
     const int tl = app ? (int)sm.nslots - 1 - s_begin : -(1 << 30);  // tile row of slot t in tile 0
 
     // (loads of tiles past the end read row 0 and are dropped: the same loads on every path)
-    DecRegs<FMT> R[NP];
+    DecRegs<FMT> R[NPE];
 #pragma unroll
-    for (int j = 0; j < NP; ++j) {
+    for (int j = 0; j < NPE; ++j) {
         dec_load<FMT, DENSE>(R[j], ncs, w_row, s_end, vis, win_cap, P, ent, s_begin, s_begin + j * kKT, hw, c);
         // (tile by tile, in the order the loop consumes them: the loop's waits count on it)
         asm volatile("" ::: "memory");
@@ -1028,8 +1032,8 @@ __global__ void __launch_bounds__(256) attn_dec(AttnArgs a, int64_t split_len, i
     }
     dec_store<FMT>(R[0], &Kt[0][0], (uint8_t*)vflag[0], hw, c);
     if (app) dec_fix_row<FMT>(&Kt[0][0], hw, c, rowt, tl);
-    if (NP < kDecMaxTiles)
-        dec_load<FMT, DENSE>(R[0], ncs, w_row, s_end, vis, win_cap, P, ent, s_begin, s_begin + NP * kKT, hw, c);
+    if (NPE < MT)
+        dec_load<FMT, DENSE>(R[0], ncs, w_row, s_end, vis, win_cap, P, ent, s_begin, s_begin + NPE * kKT, hw, c);
 #pragma unroll
     for (int ks = 0; ks < 5; ++ks) asm volatile("" ::"v"(qf[ks]));
     __syncthreads();
@@ -1043,10 +1047,10 @@ __global__ void __launch_bounds__(256) attn_dec(AttnArgs a, int64_t split_len, i
     const int dbase = 144 * wv;
     const uint32_t vbase = lds_addr(&Kt[0][0]) + 2 * ((4 * g4 + (n >> 2)) * kKS + dbase + 4 * (n & 3));
 
-    // The tile loop is unrolled in full (at most kDecMaxTiles tiles): with no back edge the
-    // compiler counts the loads in flight exactly, and tile t + 1 waits only for its own rows.
+    // The tile loop is unrolled in full (MT tiles): with no back edge the compiler counts the loads
+    // in flight exactly, and tile t + 1 waits only for its own rows.
 #pragma unroll
-    for (int t = 0; t < kDecMaxTiles; ++t) {
+    for (int t = 0; t < MT; ++t) {
         {
             if (t >= ntile) break;
             // partial scores of tile t over this wave's dims
@@ -1067,13 +1071,13 @@ __global__ void __launch_bounds__(256) attn_dec(AttnArgs a, int64_t split_len, i
             Sx[t & 1][wv][1][lane] = s[1];
             // tile t + 1 into the buffer tile t - 2 used; its registers take tile t + 1 + NP (after
             // the last tile: a harmless store of dropped rows into the free buffer)
-            if (t + 1 < kDecMaxTiles) {
-                DecRegs<FMT>& Rn = R[(t + 1) % NP];
+            if (t + 1 < MT) {
+                DecRegs<FMT>& Rn = R[(t + 1) % NPE];
                 dec_store<FMT>(Rn, (uint16_t*)((char*)&Kt[0][0] + bn), (uint8_t*)vflag[fn], hw, c);
                 if (app) dec_fix_row<FMT>((uint16_t*)((char*)&Kt[0][0] + bn), hw, c, rowt, tl - (t + 1) * kKT);
-                if (t + 1 + NP < kDecMaxTiles)
+                if (t + 1 + NPE < MT)
                     dec_load<FMT, DENSE>(Rn, ncs, w_row, s_end, vis, win_cap, P, ent, s_begin,
-                                         s_begin + (t + 1 + NP) * kKT, hw, c);
+                                         s_begin + (t + 1 + NPE) * kKT, hw, c);
             }
             __syncthreads();
             // the four partial sums in a fixed order: identical scores in every wave
@@ -1395,6 +1399,22 @@ hipError_t launch_kv_expand(const ExpandArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// attn_dec for fp8 rows, unrolled for the launch's tile count mt
+template <int FMT, bool DENSE, int NP>
+static void launch_dec(int mt, dim3 grid, hipStream_t st, const AttnArgs& a, int64_t len, int ns) {
+    static_assert(kDecMaxTiles == 8, "one instantiation per tile count");
+    switch (mt) {
+        case 1: hipLaunchKernelGGL((attn_dec<FMT, DENSE, NP, 1>), grid, dim3(256), 0, st, a, len, ns); break;
+        case 2: hipLaunchKernelGGL((attn_dec<FMT, DENSE, NP, 2>), grid, dim3(256), 0, st, a, len, ns); break;
+        case 3: hipLaunchKernelGGL((attn_dec<FMT, DENSE, NP, 3>), grid, dim3(256), 0, st, a, len, ns); break;
+        case 4: hipLaunchKernelGGL((attn_dec<FMT, DENSE, NP, 4>), grid, dim3(256), 0, st, a, len, ns); break;
+        case 5: hipLaunchKernelGGL((attn_dec<FMT, DENSE, NP, 5>), grid, dim3(256), 0, st, a, len, ns); break;
+        case 6: hipLaunchKernelGGL((attn_dec<FMT, DENSE, NP, 6>), grid, dim3(256), 0, st, a, len, ns); break;
+        case 7: hipLaunchKernelGGL((attn_dec<FMT, DENSE, NP, 7>), grid, dim3(256), 0, st, a, len, ns); break;
+        default: hipLaunchKernelGGL((attn_dec<FMT, DENSE, NP, 8>), grid, dim3(256), 0, st, a, len, ns); break;
+    }
+}
+
 // (the decode kernel is taken and its row offsets fit 32 bits)
 static bool dec_launch(const AttnArgs& a, const AttnPlan& p) {
     const int64_t rb = a.comp.fmt == LCA_FP8 ? kDN : 2 * kDN;
@@ -1425,15 +1445,16 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     if (dec_launch(a, p)) {
         dim3 grid((unsigned)((ns + 7) / 8 * 8 * (a.H / 16)), (unsigned)a.T, (unsigned)a.B);
         if (trace_on())
-            trace("  attn_dec<%s, %s>: grid (%u, %u, %u) x 256, %d split(s) of %lld slots%s", a.comp.fmt == LCA_FP8 ? "fp8" : "bf16",
+            trace("  attn_dec<%s, %s>: grid (%u, %u, %u) x 256, %d split(s) of %lld slots (%lld tiles)%s", a.comp.fmt == LCA_FP8 ? "fp8" : "bf16",
                   dense ? "dense" : "selected", grid.x, grid.y, grid.z, ns, (long long)p.len,
-                  a.app_x ? ", window store fused" : "");
+                  (long long)((p.len + kKT - 1) / kKT), a.app_x ? ", window store fused" : "");
+        const int mt = (int)((p.len + kKT - 1) / kKT);  // (1 .. kDecMaxTiles)
         if (a.comp.fmt == LCA_FP8) {
-            if (dense) hipLaunchKernelGGL((attn_dec<LCA_FP8, true, 4>), grid, dim3(256), 0, st, a, p.len, ns);
-            else hipLaunchKernelGGL((attn_dec<LCA_FP8, false, 4>), grid, dim3(256), 0, st, a, p.len, ns);
-        } else {
-            if (dense) hipLaunchKernelGGL((attn_dec<LCA_BF16, true, 3>), grid, dim3(256), 0, st, a, p.len, ns);
-            else hipLaunchKernelGGL((attn_dec<LCA_BF16, false, 3>), grid, dim3(256), 0, st, a, p.len, ns);
+            if (dense) launch_dec<LCA_FP8, true, 4>(mt, grid, st, a, p.len, ns);
+            else launch_dec<LCA_FP8, false, 4>(mt, grid, st, a, p.len, ns);
+        } else {  // (bf16 rows: one tile count)
+            if (dense) hipLaunchKernelGGL((attn_dec<LCA_BF16, true, 3, kDecMaxTiles>), grid, dim3(256), 0, st, a, p.len, ns);
+            else hipLaunchKernelGGL((attn_dec<LCA_BF16, false, 3, kDecMaxTiles>), grid, dim3(256), 0, st, a, p.len, ns);
         }
     } else {
         dim3 grid((unsigned)rows, (unsigned)ns);
