@@ -747,7 +747,11 @@ __global__ void __launch_bounds__(kCombThreads) attn_combine(AttnArgs a, int nsp
 constexpr int kDecRows = 128;      // query rows below which a launch takes the decode kernel
 constexpr int kDecMaxTiles = 8;    // tiles per split at most: the tile loop is unrolled in full
 constexpr int kDecMaxLen = kDecMaxTiles * kKT;
-constexpr int kDecWGs = 256;       // workgroups a decode launch aims for (one per CU)
+constexpr int kDecWGs = 256;       // workgroups a multi-row decode launch (attn_mfma) aims for: one per CU
+// workgroups an attn_dec launch aims for: three per four CUs measured best on the 1M decode step
+// (its HCA layers then take 44 six-tile splits x 4 head groups instead of 52 five-tile ones: 101.0
+// against 101.6 us per step; a target of 160: 104.3 us, 320: 130 us)
+constexpr int kDecTargetWGs = 192;
 
 template <int FMT>
 struct DecRegs {  // one tile's raw rows for this thread
@@ -1293,8 +1297,8 @@ __global__ void __launch_bounds__(64) attn_f32(AttnArgs a) {
 }
 
 // Split policy.  Short launches (rows x head groups <= kDecMaxUnits) take attn_dec: the slot list
-// is cut into ns_t = kDecWGs / (rows x head groups) splits of whole tiles (32 .. kDecMaxLen
-// slots), so that the launch comes near kDecWGs workgroups.  Other launches of fewer than kDecRows
+// is cut into ns_t = kDecTargetWGs / (rows x head groups) splits of whole tiles (32 .. kDecMaxLen
+// slots), so that the launch comes near kDecTargetWGs workgroups.  Other launches of fewer than kDecRows
 // rows take attn_mfma (64 heads per workgroup, which amortises each gathered tile over four times
 // the work) with up to ceil(256 / rows) splits of at least 128 slots; longer launches one split
 // per row.  Either way the split count never exceeds a bound that does not fall as max_keys grows
@@ -1312,7 +1316,7 @@ static bool dec_eligible(int64_t rows, int32_t H, int32_t c) {
 static bool split_eligible(int64_t rows, int32_t c) { return c == kC && rows < kDecRows; }
 static int64_t dec_target(int64_t rows, int32_t H) {
     const int64_t per = rows * (H / 16);  // workgroups per split index
-    return per >= kDecWGs ? 1 : kDecWGs / per;
+    return per >= kDecTargetWGs ? 1 : kDecTargetWGs / per;
 }
 static int64_t split_target(int64_t rows) { return (kDecWGs + rows - 1) / rows; }
 static AttnPlan attn_plan(int64_t rows, int32_t H, int32_t c, int64_t max_keys) {
