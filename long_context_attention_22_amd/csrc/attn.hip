@@ -587,7 +587,8 @@ __global__ void __launch_bounds__(512) attn_mfma(AttnArgs a, int64_t split_len, 
 constexpr int kCombGroups = 8, kCombQuarters = 4, kCombPer = kC / 4 / kCombQuarters;  // 36 threads x 4 dims
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr int kCombThreads = kCombGroups * kCombPer;
-static int comb_groups(int nsplit) { return nsplit > 32 ? 8 : nsplit > 16 ? 4 : nsplit > 8 ? 2 : 1; }
+// (as many groups as eight prefetched splits each need, so that few prefetch slots are padding)
+static int comb_groups(int nsplit) { return nsplit <= 8 ? 1 : min(kCombGroups, (nsplit + 7) / 8); }
 // quad = 0: one workgroup per (row, head, dim quarter), ng groups of 36 threads splitting the splits;
 // quad = 1 (few splits): one workgroup per (row, head), its four groups of 36 threads the four dim
 // quarters, so the head's split weights are formed once and there are four times fewer workgroups.
