@@ -861,10 +861,13 @@ def bench_compressor(seed: int = 1007):
         cap = (p0 + n) // m + 2
         kv = lca.KV.empty(fmt, 1, cap, 512, 64)
         first = p0 - (m if ov else 0)
+        wsz = lca.compress_workspace_size(lca.BF16, m, ov, 512, 64)  # (as the stack's layers pass it)
+        cws = torch.empty(wsz, dtype=torch.uint8, device="cuda") if wsz else None
 
         def launch(x):
             lca.kv_compress(x[0], x[1], x[2] if ov else None, x[3] if ov else None, kv, m=m, overlap=ov,
-                            first_pos=first, bias_a=ba, bias_b=bb if ov else None, gamma=gamma, rope_theta=1e4)
+                            first_pos=first, bias_a=ba, bias_b=bb if ov else None, gamma=gamma, rope_theta=1e4,
+                            ws=cws)
 
         for x in streams[:2]:
             launch(x)

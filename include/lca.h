@@ -125,6 +125,31 @@ int lca_kv_compress(const void* c_a, const void* z_a, const void* c_b, const voi
                     const int64_t* first_pos, lca_kv out, int32_t ring, void* stream);
 
 /*
+ * lca_kv_compress_ws -- lca_kv_compress with a caller workspace (the same
+ * entries, the same arithmetic up to the order in which the rows' softmax
+ * states are merged).  With ws != NULL a call of few long entries -- bf16
+ * inputs, c % 8 == 0, c <= 576, at least 64 rows per entry (m * (1 + overlap))
+ * and at most 128 (entry, sequence) pairs, e.g. a 4096-token chunk's m = 128
+ * blocks -- cuts each entry's rows into ranges pooled by separate workgroups
+ * (at most 256 workgroups in all) and merges the ranges' per-channel states
+ * in a fixed order; other calls ignore ws.  ws: device memory of at least
+ * lca_compress_workspace_size(in_dtype, m, overlap, d_nope, d_rope) bytes,
+ * 16-byte aligned, owned by the caller, no initialisation needed; calls on
+ * one workspace must not overlap.  ws == NULL: exactly lca_kv_compress.
+ * Errors: as lca_kv_compress; LCA_EWORKSPACE when ws is non-NULL but
+ * ws_bytes is below the size the call needs; LCA_EALIGN for a misaligned ws.
+ */
+int lca_kv_compress_ws(const void* c_a, const void* z_a, const void* c_b, const void* z_b,
+                       int32_t in_dtype, const float* bias_a, const float* bias_b,
+                       const float* gamma, float eps, double rope_theta,
+                       int32_t m, int32_t overlap, int32_t B, int64_t n_rows, int64_t in_stride,
+                       const int64_t* first_pos, lca_kv out, int32_t ring, void* ws, size_t ws_bytes,
+                       void* stream);
+/* Workspace bytes for lca_kv_compress_ws over any number of rows and
+ * sequences (256 x 3 x c floats), or 0 when such calls never split. */
+size_t lca_compress_workspace_size(int32_t in_dtype, int32_t m, int32_t overlap, int32_t d_nope, int32_t d_rope);
+
+/*
  * lca_indexer_score -- the lightning indexer of [R] 2.3.1 and [H] CSA: a
  * multi-head dot product scored by ReLU between each query and every
  * compressed indexer key, with BF16 scores as in [R] 5.2.1.

@@ -54,6 +54,10 @@ def lib():
         L.lca_last_error.restype = C.c_char_p
         L.lca_kv_compress.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, f32, f64, i32, i32, i32, i64, i64,
                                       vp, _KV, i32, vp]
+        L.lca_kv_compress_ws.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, f32, f64, i32, i32, i32, i64, i64,
+                                         vp, _KV, i32, vp, sz, vp]
+        L.lca_compress_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+        L.lca_compress_workspace_size.restype = sz
         L.lca_indexer_score.argtypes = [vp, vp, vp, i32, i64, i32, i32, i32, i32, vp, i32, vp, i32, i64,
                                         vp]
         L.lca_indexer_score_mxfp4.argtypes = [vp, vp, _KV, i32, i32, i32, i32, vp, i32, vp, i32, i64, vp]
@@ -78,7 +82,7 @@ def lib():
         L.lca_indexer_topk_workspace_size.restype = sz
         L.lca_attn_workspace_size.argtypes = [i32, i32, i32, i32, i64]
         L.lca_attn_workspace_size.restype = sz
-        for name in ("lca_kv_compress", "lca_indexer_score", "lca_indexer_score_mxfp4", "lca_topk_select",
+        for name in ("lca_kv_compress", "lca_kv_compress_ws", "lca_indexer_score", "lca_indexer_score_mxfp4", "lca_topk_select",
                      "lca_csa_attn", "lca_hca_attn", "lca_hca_attn_noalloc", "lca_csa_attn_append",
                      "lca_hca_attn_append", "lca_linear", "lca_grouped_out_proj", "lca_indexer_topk",
                      "lca_indexer_topk_mxfp4"):
@@ -161,19 +165,28 @@ class KV:
 
 def kv_compress(c_a, z_a, c_b, z_b, out: KV, *, m: int, overlap: int, first_pos, bias_a=None,
                 bias_b=None, gamma=None, eps: float = 1e-6, rope_theta: float = 0.0, ring: int = 0,
-                stream=None):
+                ws=None, stream=None):
     """Inputs [B][n_rows][c]; each may be a row window of a longer per-sequence stream (rows contiguous,
-    the same sequence stride for all four)."""
+    the same sequence stride for all four).  ws: a workspace of compress_workspace_size() bytes, with
+    which calls of few long entries split each entry's rows over several workgroups (lca_kv_compress_ws)."""
     B, n_rows, c = c_a.shape
     for t in (c_a, z_a, c_b, z_b):
         if t is not None and (t.shape != c_a.shape or t.stride() != c_a.stride() or t.stride(2) != 1
                               or t.stride(1) != c):
             raise ValueError("kv_compress inputs must share shape and row-contiguous strides")
     in_stride = c_a.stride(0) // c if B > 1 else n_rows
-    _check(lib().lca_kv_compress(_ptr(c_a), _ptr(z_a), _ptr(c_b), _ptr(z_b), _dtype(c_a), _ptr(bias_a),
-                                 _ptr(bias_b), _ptr(gamma), float(eps), float(rope_theta), int(m),
-                                 int(overlap), int(B), int(n_rows), int(in_stride), _pos(first_pos, B),
-                                 out.c(), int(ring), _stream(stream)))
+    args = (_ptr(c_a), _ptr(z_a), _ptr(c_b), _ptr(z_b), _dtype(c_a), _ptr(bias_a), _ptr(bias_b), _ptr(gamma),
+            float(eps), float(rope_theta), int(m), int(overlap), int(B), int(n_rows), int(in_stride),
+            _pos(first_pos, B), out.c(), int(ring))
+    if ws is None:
+        _check(lib().lca_kv_compress(*args, _stream(stream)))
+    else:
+        _check(lib().lca_kv_compress_ws(*args, _ptr(ws), int(ws.numel() * ws.element_size()), _stream(stream)))
+
+
+def compress_workspace_size(in_dtype: int, m: int, overlap: int, d_nope: int, d_rope: int) -> int:
+    """Bytes of the workspace with which kv_compress splits long entries (0: such calls never split)."""
+    return int(lib().lca_compress_workspace_size(int(in_dtype), int(m), int(overlap), int(d_nope), int(d_rope)))
 
 
 def indexer_score(q, w, k, scores, *, q_pos, m: int, stream=None):

@@ -124,14 +124,23 @@ int lca_version(void) { return LCA_VERSION; }
 
 const char* lca_last_error(void) { return g_err; }
 
-int lca_kv_compress(const void* c_a, const void* z_a, const void* c_b, const void* z_b,
-                    int32_t in_dtype, const float* bias_a, const float* bias_b, const float* gamma,
-                    float eps, double rope_theta, int32_t m, int32_t overlap, int32_t B, int64_t n_rows,
-                    int64_t in_stride, const int64_t* first_pos, lca_kv out, int32_t ring, void* stream) {
-    g_err[0] = 0;
-    LCA_TRACE_CALL("lca_kv_compress B=%d rows=%lld in_dtype=%d m=%d overlap=%d out fmt=%d dims=%d+%d cap=%lld ring=%d "
-                   "first_pos[0]=%lld", B, (long long)n_rows, in_dtype, m, overlap, out.fmt, out.d_nope, out.d_rope,
-                   (long long)out.cap, ring, pos0(first_pos));
+// lca_kv_compress_ws splits entries when the pooled row list is long and the inputs take kv_pool_wide
+static bool compress_splits(int32_t in_dtype, int32_t m, int32_t overlap, int32_t c) {
+    return in_dtype == LCA_BF16 && c > 0 && c % 8 == 0 && c <= 576 && (int64_t)m * (1 + overlap) >= lca::kCompressMinList;
+}
+
+size_t lca_compress_workspace_size(int32_t in_dtype, int32_t m, int32_t overlap, int32_t d_nope, int32_t d_rope) {
+    if (m < 1 || (overlap != 0 && overlap != 1) || d_nope < 0 || d_rope < 0) return 0;
+    const int32_t c = d_nope + d_rope;
+    if (!compress_splits(in_dtype, m, overlap, c)) return 0;
+    return (size_t)lca::kCompressUnits * 3 * (size_t)c * sizeof(float);
+}
+
+static int kv_compress_common(const void* c_a, const void* z_a, const void* c_b, const void* z_b,
+                              int32_t in_dtype, const float* bias_a, const float* bias_b, const float* gamma,
+                              float eps, double rope_theta, int32_t m, int32_t overlap, int32_t B, int64_t n_rows,
+                              int64_t in_stride, const int64_t* first_pos, lca_kv out, int32_t ring, void* ws,
+                              size_t ws_bytes, void* stream) {
     if (!c_a || !z_a) return fail(LCA_EINVAL, "c_a / z_a is NULL");
     if (m < 1) return fail(LCA_EINVAL, "m must be >= 1 (got %d)", m);
     if (overlap != 0 && overlap != 1) return fail(LCA_EINVAL, "overlap must be 0 or 1");
@@ -177,7 +186,51 @@ int lca_kv_compress(const void* c_a, const void* z_a, const void* c_b, const voi
     }
     if (most > 0x7fffffff) return fail(LCA_ESHAPE, "too many entries in one call");
     a.max_entries = most;
+    const int32_t c = out.d_nope + out.d_rope;
+    if (ws && most > 0 && compress_splits(in_dtype, m, overlap, c) && !(m == 1 && !overlap) &&
+        (int64_t)B * most * 2 <= lca::kCompressUnits) {
+        if (!aligned16(ws)) return fail(LCA_EALIGN, "ws must be 16-byte aligned");
+        const int64_t list = (int64_t)m * (1 + overlap);  // rows of an entry's list, at most
+        int64_t parts = lca::kCompressUnits / ((int64_t)B * most);
+        if (parts > lca::kCompressMaxParts) parts = lca::kCompressMaxParts;
+        if (parts > list / lca::kCompressMinRows) parts = list / lca::kCompressMinRows;
+        const int64_t len = (list + parts - 1) / parts;
+        parts = (list + len - 1) / len;
+        const size_t need = (size_t)B * (size_t)most * (size_t)parts * 3 * (size_t)c * sizeof(float);
+        if (ws_bytes < need)
+            return fail(LCA_EWORKSPACE, "compressor workspace too small: %zu < %zu bytes", ws_bytes, need);
+        if (parts > 1) {
+            a.ws = (float*)ws;
+            a.parts = (int32_t)parts;
+            a.part_len = (int32_t)len;
+        }
+    }
     return hip_status(lca::launch_kv_compress(a, (hipStream_t)stream));
+}
+
+int lca_kv_compress(const void* c_a, const void* z_a, const void* c_b, const void* z_b,
+                    int32_t in_dtype, const float* bias_a, const float* bias_b, const float* gamma,
+                    float eps, double rope_theta, int32_t m, int32_t overlap, int32_t B, int64_t n_rows,
+                    int64_t in_stride, const int64_t* first_pos, lca_kv out, int32_t ring, void* stream) {
+    g_err[0] = 0;
+    LCA_TRACE_CALL("lca_kv_compress B=%d rows=%lld in_dtype=%d m=%d overlap=%d out fmt=%d dims=%d+%d cap=%lld ring=%d "
+                   "first_pos[0]=%lld", B, (long long)n_rows, in_dtype, m, overlap, out.fmt, out.d_nope, out.d_rope,
+                   (long long)out.cap, ring, pos0(first_pos));
+    return kv_compress_common(c_a, z_a, c_b, z_b, in_dtype, bias_a, bias_b, gamma, eps, rope_theta, m, overlap, B,
+                              n_rows, in_stride, first_pos, out, ring, nullptr, 0, stream);
+}
+
+int lca_kv_compress_ws(const void* c_a, const void* z_a, const void* c_b, const void* z_b,
+                       int32_t in_dtype, const float* bias_a, const float* bias_b, const float* gamma,
+                       float eps, double rope_theta, int32_t m, int32_t overlap, int32_t B, int64_t n_rows,
+                       int64_t in_stride, const int64_t* first_pos, lca_kv out, int32_t ring, void* ws,
+                       size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    LCA_TRACE_CALL("lca_kv_compress_ws B=%d rows=%lld in_dtype=%d m=%d overlap=%d out fmt=%d dims=%d+%d cap=%lld "
+                   "ring=%d ws=%zu first_pos[0]=%lld", B, (long long)n_rows, in_dtype, m, overlap, out.fmt, out.d_nope,
+                   out.d_rope, (long long)out.cap, ring, ws_bytes, pos0(first_pos));
+    return kv_compress_common(c_a, z_a, c_b, z_b, in_dtype, bias_a, bias_b, gamma, eps, rope_theta, m, overlap, B,
+                              n_rows, in_stride, first_pos, out, ring, ws, ws_bytes, stream);
 }
 
 int lca_indexer_score(const void* q, const float* w, const void* k, int32_t in_dtype, int64_t k_cap,

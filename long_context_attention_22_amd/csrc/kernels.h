@@ -39,8 +39,14 @@ struct CompressArgs {
     Pos first_pos;
     Pos s_lo;
     int64_t max_entries;
+    // bf16 rows of few entries split over workgroups (parts > 1): ws holds the parts' channel states
+    float* ws;
+    int32_t parts, part_len;
 };
 hipError_t launch_kv_compress(const CompressArgs& a, hipStream_t st);
+// Entry parts of a split compression: (entries x sequences) units share kCompressUnits workgroups, at most
+// kCompressMaxParts per entry, each part at least kCompressMinRows rows of the entry's list.
+constexpr int kCompressUnits = 256, kCompressMaxParts = 16, kCompressMinRows = 8, kCompressMinList = 64;
 
 struct IndexerArgs {
     const void* q;

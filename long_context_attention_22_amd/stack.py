@@ -29,10 +29,9 @@ from dataclasses import dataclass
 
 import torch
 
-from . import (BF16, FP8, MXFP4, KV, attn_workspace_size, csa_attn, csa_attn_append, hca_attn, hca_attn_append,
-               indexer_score, indexer_score_mxfp4, indexer_topk, indexer_topk_mxfp4, indexer_topk_workspace_size,
-               kv_compress,
-               topk_select, topk_workspace_size)
+from . import (BF16, FP8, MXFP4, KV, attn_workspace_size, compress_workspace_size, csa_attn, csa_attn_append,
+               hca_attn, hca_attn_append, indexer_score, indexer_score_mxfp4, indexer_topk, indexer_topk_mxfp4,
+               indexer_topk_workspace_size, kv_compress, topk_select, topk_workspace_size)
 
 
 @dataclass
@@ -133,6 +132,9 @@ class Layer:
             self.scores = self.idx = self.topk_ws = self.itk_ws = None
             self.fuse_topk = False
             max_keys = comp_cap + spec.n_win
+        # the compressor's workspace: long blocks (m' = 128) of few entries split over workgroups
+        cws = compress_workspace_size(BF16, spec.m, spec.overlap, spec.d_nope, spec.d_rope)
+        self.comp_ws = torch.empty(cws, dtype=torch.uint8, device=device) if cws > 0 else None
         # split partials are needed only for short launches (few query rows); size for the largest
         ws = max(attn_workspace_size(B, T, spec.H, spec.c, max_keys) for T in range(1, min(t_max, 128) + 1))
         self.ws = torch.zeros(max(16, ws), dtype=torch.uint8, device=device)
@@ -175,7 +177,7 @@ class Layer:
         b_rows = (lambda nm: raw.rows(nm, lo, n)) if s.overlap else (lambda nm: None)
         kv_compress(raw.rows("c_a", lo, n), raw.rows("z_a", lo, n), b_rows("c_b"), b_rows("z_b"), self.comp,
                     bias_a=p.bias_a, bias_b=p.bias_b if s.overlap else None, gamma=p.gamma, eps=s.eps,
-                    rope_theta=s.rope_theta, **kw)
+                    rope_theta=s.rope_theta, ws=self.comp_ws, **kw)
         if s.kind == "csa":
             kv_compress(raw.rows("i_ca", lo, n), raw.rows("i_za", lo, n), b_rows("i_cb"), b_rows("i_zb"),
                         self.keys, bias_a=p.i_bias_a, bias_b=p.i_bias_b, **kw)

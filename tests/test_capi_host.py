@@ -90,6 +90,34 @@ def test_kv_compress_validation(L):
     assert compress(L, in_stride=63) == 2
 
 
+def compress_ws(L, ws=FAKE, ws_bytes=0, **kw):
+    a = dict(c_a=FAKE, z_a=FAKE, c_b=None, z_b=None, in_dtype=lca.BF16, bias_a=None, bias_b=None,
+             gamma=None, eps=1e-6, theta=0.0, m=128, overlap=0, B=1, n_rows=4096, in_stride=0,
+             first_pos=pos(0), out=kv(cap=64), ring=0)
+    a.update(kw)
+    return L.lca_kv_compress_ws(a["c_a"], a["z_a"], a["c_b"], a["z_b"], a["in_dtype"], a["bias_a"], a["bias_b"],
+                                a["gamma"], a["eps"], a["theta"], a["m"], a["overlap"], a["B"], a["n_rows"],
+                                a["in_stride"], a["first_pos"], a["out"], a["ring"], ws, ws_bytes, None)
+
+
+def test_kv_compress_ws_validation(L):
+    """The split compressor's workspace: its size for long blocks, 0 where calls never split, and the call's
+    own need (32 entries x 8 parts x 3 x 576 floats) checked before any launch."""
+    size = L.lca_compress_workspace_size
+    assert size(lca.BF16, 128, 0, 512, 64) == 256 * 3 * 576 * 4
+    assert size(lca.BF16, 32, 1, 512, 64) == 256 * 3 * 576 * 4     # 64 rows per entry with the b-block
+    assert size(lca.BF16, 4, 1, 512, 64) == 0                      # 8 rows per entry: never split
+    assert size(lca.F32, 128, 0, 512, 64) == 0                     # f32 inputs take the per-channel kernel
+    assert size(lca.BF16, 128, 0, 600, 0) == 0                     # wider than the pooling kernel's 576
+    assert size(lca.BF16, 0, 0, 512, 64) == 0
+    need = 32 * 8 * 3 * 576 * 4
+    assert compress_ws(L, ws_bytes=need - 1) == lca.EWORKSPACE
+    assert b"workspace" in L.lca_last_error()
+    assert compress_ws(L, ws=FAKE + 8, ws_bytes=need) == 4
+    assert compress_ws(L, ws_bytes=need, m=0) == 1                 # the plain call's checks still apply
+    assert compress_ws(L, ws_bytes=need, out=kv(cap=8)) == 2
+
+
 def indexer(L, **kw):
     a = dict(q=FAKE, w=None, k=FAKE, dt=lca.BF16, k_cap=100, H=16, d=128, B=1, T=8, q_pos=pos(0), m=4,
              s=FAKE2, sdt=lca.BF16, stride=100)

@@ -27,7 +27,7 @@ def _raw(seed, B, n, c, dtype="bf16"):
 
 @pytest.mark.parametrize("fmt", [orc.F32, orc.BF16, orc.FP8])
 @pytest.mark.parametrize("m,overlap,dn,dr", [(1, 0, 512, 64), (4, 1, 512, 64), (128, 0, 512, 64),
-                                             (4, 1, 128, 0), (4, 1, 48, 16)])
+                                             (4, 1, 128, 0), (4, 1, 48, 16), (16, 0, 512, 64), (16, 1, 512, 64)])
 def test_kv_compress(fmt, m, overlap, dn, dr):
     if fmt == orc.FP8 and dn % 128:
         pytest.skip("fp8 storage needs d_nope % 128 == 0")
@@ -51,6 +51,34 @@ def test_kv_compress(fmt, m, overlap, dn, dr):
                     gamma=None if gamma is None else dev(gamma), rope_theta=theta)
     torch.cuda.synchronize()
     assert_kv_close(kv_host(g), o)
+
+
+@pytest.mark.parametrize("fmt", [orc.F32, orc.BF16, orc.FP8])
+@pytest.mark.parametrize("m,overlap", [(128, 0), (32, 1), (4, 1)])
+def test_kv_compress_split(fmt, m, overlap):
+    """With a workspace, entries of long row lists (m (1 + overlap) >= 64) are pooled by several
+    workgroups each and merged: the same bars against the oracle; m = 4 ignores the workspace."""
+    c, B = 576, 2
+    n = 3 * m + 5 if m > 4 else 203
+    first = [0, 2 * m + 1]
+    ca, za, cb, zb = _raw(51 + m, B, n, c)
+    ba = S.normal(5, "bias_a", (m, c))
+    bb = S.normal(5, "bias_b", (m, c))
+    gamma = (1.0 + 0.1 * S.normal(5, "gamma", (c,))).astype(np.float32)
+    cap = (first[1] + n) // m + 2
+    o = orc.KV.empty(fmt, B, cap, 512, 64)
+    orc.kv_compress(ca, za, cb if overlap else None, zb if overlap else None, o, m=m, overlap=overlap,
+                    first_pos=first, bias_a=ba, bias_b=bb if overlap else None, gamma=gamma, rope_theta=1e4)
+    wsz = lca.compress_workspace_size(orc.BF16, m, overlap, 512, 64)
+    assert (wsz > 0) == (m * (1 + overlap) >= 64)
+    ws = torch.full((max(16, wsz),), 255, dtype=torch.uint8, device="cuda")  # (no initialisation needed)
+    g = lca.KV.empty(fmt, B, cap, 512, 64)
+    for _ in range(2):  # twice on one workspace
+        lca.kv_compress(dev(ca), dev(za), dev(cb) if overlap else None, dev(zb) if overlap else None, g, m=m,
+                        overlap=overlap, first_pos=first, bias_a=dev(ba), bias_b=dev(bb) if overlap else None,
+                        gamma=dev(gamma), rope_theta=1e4, ws=ws)
+        torch.cuda.synchronize()
+        assert_kv_close(kv_host(g), o)
 
 
 def test_kv_compress_ring_and_identity():
@@ -153,7 +181,7 @@ def _q(seed, B, T, H=64):
 @pytest.mark.parametrize("fmt", [orc.BF16, orc.FP8])
 @pytest.mark.parametrize("mode", ["csa", "hca"])
 @pytest.mark.parametrize("B,T,q_pos,k", [(3, 1, [5000, 700, 131], 256), (2, 37, [2100, 64], 64),
-                                         (1, 160, [4000], 128)])
+                                         (1, 160, [4000], 128), (2, 130, [300, 9000], 64)])
 def test_attention(fmt, mode, B, T, q_pos, k):
     m, n_win, H = 4 if mode == "csa" else 128, 128, 64
     ncomp = (max(q_pos) + T) // m + 1
