@@ -404,9 +404,12 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t st) {
     // MXFP4 keys are 68 bytes: a single-token launch gives each workgroup twice the keys
     if (fp4 && tok == 1) kpw *= 2;
     if (kpw < 256) kpw = 256;
-    if (a.th_h1 && a.th_chunked) {  // a workgroup's keys must lie in one chunk of the top-k
+    if (a.th_h1 && a.th_chunked) {
+        // a workgroup's keys must lie in one chunk of the top-k: a power of two, rounded down (rounded
+        // up, a row of 32,769 .. 32,768 + 767 keys took 33 workgroups of 1,024 keys instead of 43 of
+        // 768, and the fused launch ran 15 % behind the plain one)
         int64_t p = 256;
-        while (p < kpw && p < kTopkChunk) p <<= 1;
+        while (2 * p <= kpw && 2 * p <= kTopkChunk) p <<= 1;
         kpw = p;
     }
     const int64_t nsplit = (a.max_vis + kpw - 1) / kpw;
