@@ -253,8 +253,9 @@ int lca_indexer_topk_mxfp4(const void* q, const float* w, lca_kv k, int32_t H_I,
  * An empty set without a sink gives o = 0, lse = -inf.
  * q: [B][T][H][c] (LCA_BF16, or LCA_F32 with f32 caches); out: [B][T][H][c]
  * of out_dtype (LCA_F32 or LCA_BF16).  comp and win share d_nope / d_rope;
- * supported shapes: (d_nope, d_rope) = (512, 64) with H % 16 == 0 for
- * bf16/fp8 caches, any c <= 1024 for f32.  The window ring must hold every
+ * supported shapes: (d_nope, d_rope) = (512, 64) with 1 <= H <= 64 for
+ * bf16/fp8 caches (the kernels take heads 16 at a time; a last partial
+ * group computes on zero queries and stores nothing), any c <= 1024 for f32.  The window ring must hold every
  * needed row: min(n_win - 1, q_pos[b]) + T <= win.cap (n_win = 0: no window).  idx
  * values that are negative (padding) or not visible (e >= vis(t): a block
  * ending after t, or a row past the cache) are skipped, never read: block-level

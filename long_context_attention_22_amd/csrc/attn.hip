@@ -6,7 +6,8 @@
 // plus the sliding window of raw rows, with a per-head sink logit and RoPE
 // applied to the output by -t.
 //
-// bf16 / fp8 caches, c = 512 + 64, H a multiple of 16 (up to 64): MFMA path.
+// bf16 / fp8 caches, c = 512 + 64, H up to 64 (taken 16 heads at a time; the heads of a last
+// partial group past H have zero queries and store nothing): MFMA path.
 //   One workgroup (8 waves) per (query row, key split).  The attended rows are
 //   a list of "slots": compressed slots (idx entries, or 0..vis-1) followed by
 //   window slots.  Per tile of 32 slots the workgroup gathers the rows from HBM
@@ -346,14 +347,16 @@ __global__ void __launch_bounds__(512) attn_mfma(AttnArgs a, int64_t split_len, 
     const int hg = wv & 3, dh = wv >> 2;      // head group, dim half
     const int h0 = 16 * hg, dbase = kHalf * dh;
     const bool active = h0 < a.H;             // wave-uniform
+    const bool hv = h0 + n < a.H;             // this lane's head exists (H need not be a multiple of 16:
+                                              // a missing head has zero queries and stores nothing)
 
     // Q^T fragments: B[k = dim dbase + 32 ks + 8 g4 + e][n = head h0 + n]
     bf16x8 qf[9];
     {
-        const u32x4* qp = (const u32x4*)((const uint16_t*)a.q + (rowid * a.H + h0 + n) * kC + dbase);
+        const u32x4* qp = (const u32x4*)((const uint16_t*)a.q + (rowid * a.H + (hv ? h0 + n : 0)) * kC + dbase);
 #pragma unroll
         for (int ks = 0; ks < 9; ++ks)
-            qf[ks] = __builtin_bit_cast(bf16x8, active ? qp[4 * ks + g4] : u32x4{0u, 0u, 0u, 0u});
+            qf[ks] = __builtin_bit_cast(bf16x8, hv ? qp[4 * ks + g4] : u32x4{0u, 0u, 0u, 0u});
     }
     // O^T: lane holds dims dbase + 16 nb + 4 g4 + i (i < 4) of head h0 + n
     f32x4 o[18];
@@ -521,6 +524,7 @@ __global__ void __launch_bounds__(512) attn_mfma(AttnArgs a, int64_t split_len, 
     // epilogue: head h = h0 + n, dims dbase + 16 nb + 4 g4 + i
     const int h = h0 + n;
     const int64_t nrows = (int64_t)gridDim.x;
+    if (!hv) return;
     if (nsplit > 1) {
         // partial O (unnormalised, f32), then the (max, sum) pairs
         float* wo = (float*)a.ws;
@@ -940,7 +944,7 @@ __global__ void __launch_bounds__(256) attn_dec(AttnArgs a, int64_t split_len, i
                      "s"(pi), "s"(pn0), "s"(pn1), "s"(pr0), "s"(pr1), "s"(ps0), "s"(ps1), "s"(pax), "s"(pag),
                      "s"(aeps), "s"(ast));
     }
-    const uint32_t ng = (uint32_t)H >> 4;
+    const uint32_t ng = ((uint32_t)H + 15) >> 4;  // head groups (the last may be partial)
     const uint32_t L = blockIdx.x, jj = L >> 3;
     const int hg = (int)(jj % ng);
     const int split = (int)((jj / ng) * 8u + (L & 7u));
@@ -958,15 +962,17 @@ __global__ void __launch_bounds__(256) attn_dec(AttnArgs a, int64_t split_len, i
     const int n = lane & 15, g4 = lane >> 4;  // MFMA lane coordinates
     const int hw = tid >> 5, c = tid & 31;     // gather coordinates
     const int h0 = 16 * hg;
+    const bool hv = h0 + n < H;  // this lane's head exists (a partial last group: zero queries, no stores)
 
     // Q^T fragments for this wave's score dims: B[k = dim d0 + 32 ks + 8 g4 + e][n = head h0 + n]
     const int d0 = wv < 2 ? 160 * wv : 320 + 128 * (wv - 2);
     const int nks = wv < 2 ? 5 : 4;
     bf16x8 qf[5];
     {
-        const u32x4* qp = (const u32x4*)((const uint16_t*)a.q + (rowid * a.H + h0 + n) * kC + d0);
+        const u32x4* qp = (const u32x4*)((const uint16_t*)a.q + (rowid * a.H + (hv ? h0 + n : 0)) * kC + d0);
 #pragma unroll
-        for (int ks = 0; ks < 5; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, ks < nks ? qp[4 * ks + g4] : u32x4{0u, 0u, 0u, 0u});
+        for (int ks = 0; ks < 5; ++ks)
+            qf[ks] = __builtin_bit_cast(bf16x8, ks < nks && hv ? qp[4 * ks + g4] : u32x4{0u, 0u, 0u, 0u});
     }
     if constexpr (!DENSE) {  // this split's entry ids
         const int lim = min(ncs, s_end);
@@ -1164,6 +1170,7 @@ __global__ void __launch_bounds__(256) attn_dec(AttnArgs a, int64_t split_len, i
     // epilogue: head h = h0 + n, dims dbase + 16 nb + 4 g4 + i
     const int h = h0 + n;
     const int64_t nrows = (int64_t)a.B * a.T;
+    if (!hv) return;
     if (nsplit > 1) {
         float* wo = (float*)a.ws;
         float* wml = wo + (int64_t)nsplit * nrows * a.H * kC;
@@ -1311,12 +1318,13 @@ struct AttnPlan {
     int nsplit;
     int64_t len;  // slots per split
 };
+static int64_t head_groups(int32_t H) { return ((int64_t)H + 15) / 16; }  // (the last may be partial)
 static bool dec_eligible(int64_t rows, int32_t H, int32_t c) {
-    return c == kC && H >= 16 && rows * (H / 16) <= kDecMaxUnits;
+    return c == kC && H >= 1 && rows * head_groups(H) <= kDecMaxUnits;
 }
 static bool split_eligible(int64_t rows, int32_t c) { return c == kC && rows < kDecRows; }
 static int64_t dec_target(int64_t rows, int32_t H) {
-    const int64_t per = rows * (H / 16);  // workgroups per split index
+    const int64_t per = rows * head_groups(H);  // workgroups per split index
     return per >= kDecTargetWGs ? 1 : kDecTargetWGs / per;
 }
 static int64_t split_target(int64_t rows) { return (kDecWGs + rows - 1) / rows; }
@@ -1448,7 +1456,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t st) {
     // attn_dec addresses one sequence's rows with 32-bit offsets; larger planes take attn_mfma
     // (same splits, same workspace layout)
     if (dec_launch(a, p)) {
-        dim3 grid((unsigned)((ns + 7) / 8 * 8 * (a.H / 16)), (unsigned)a.T, (unsigned)a.B);
+        dim3 grid((unsigned)((ns + 7) / 8 * 8 * head_groups(a.H)), (unsigned)a.T, (unsigned)a.B);
         if (trace_on())
             trace("  attn_dec<%s, %s>: grid (%u, %u, %u) x 256, %d split(s) of %lld slots (%lld tiles)%s", a.comp.fmt == LCA_FP8 ? "fp8" : "bf16",
                   dense ? "dense" : "selected", grid.x, grid.y, grid.z, ns, (long long)p.len,

@@ -173,7 +173,7 @@ def test_attn_validation(L):
     assert attn(L, n_win=-1) == 1
     assert attn(L, odt=2) == 3
     assert attn(L, qdt=lca.F32) == 3                              # bf16 cache with f32 queries
-    assert attn(L, H=40) == 2                                     # MFMA path: multiple of 16
+    assert attn(L, H=72) == 2                                     # MFMA path: at most 64 heads
     assert attn(L, comp=kv(d_nope=256)) == 2                      # MFMA path: 512 + 64
     assert attn(L, win=kv(cap=100)) == 2                          # min(n_win - 1, q_pos) + T > cap
     assert attn(L, q_pos=pos(0), T=100, win=kv(cap=99)) == 2
@@ -191,7 +191,7 @@ def test_attn_validation(L):
     assert L.lca_attn_workspace_size(1, 4096, 64, 576, 2176) == (2 * 2176 + 4096) * 1152
 
 
-@pytest.mark.parametrize("B,T,H", [(1, 1, 64), (1, 1, 16), (32, 1, 64), (3, 5, 48), (1, 127, 64)])
+@pytest.mark.parametrize("B,T,H", [(1, 1, 64), (1, 1, 16), (32, 1, 64), (3, 5, 48), (1, 127, 64), (2, 3, 24)])
 def test_attn_workspace_covers_smaller_launches(L, no_gpu, B, T, H):
     """lca_attn_workspace_size(..., M) covers every launch with at most M attended rows per query: no
     such launch is refused for its workspace (it passes validation and only then fails to launch,

@@ -223,7 +223,7 @@ def test_attention(fmt, mode, B, T, q_pos, k):
     assert np.all(np.abs(gb - o) <= 2e-2 + np.abs(o) * 2 ** -8)
 
 
-@pytest.mark.parametrize("H", [16, 48])
+@pytest.mark.parametrize("H", [16, 48, 8, 40])
 @pytest.mark.parametrize("mode", ["csa", "hca"])
 def test_attention_decode_shapes(mode, H):
     """Short launches (few rows x head groups) take the split decode kernel: fewer than 64 heads,
@@ -247,6 +247,40 @@ def test_attention_decode_shapes(mode, H):
     ws = torch.empty(max(16, lca.attn_workspace_size(B, T, H, 576, maxk)), dtype=torch.uint8, device="cuda")
     out = torch.zeros(B, T, H, 576, dtype=torch.float32, device="cuda")
     lg = torch.zeros(B, T, H, dtype=torch.float32, device="cuda")
+    kw = dict(q_pos=q_pos, comp=kv_dev(comp), m=m, win=kv_dev(win), n_win=n_win, sink=dev(sink),
+              sm_scale=scale, rope_theta=10000.0, lse=lg, ws=ws)
+    if mode == "csa":
+        lca.csa_attn(dev(q), out, idx=dev(idx), **kw)
+    else:
+        lca.hca_attn(dev(q), out, **kw)
+    err = np.abs(host(out) - o).max()
+    assert err <= 2e-2, err
+    np.testing.assert_allclose(host(lg), lse, atol=1e-3, rtol=1e-4)
+
+
+@pytest.mark.parametrize("mode", ["csa", "hca"])
+@pytest.mark.parametrize("T", [40, 150])
+def test_attention_partial_head_group(mode, T):
+    """H = 24 (a last group of 8 heads): the 8-wave kernel with split partials (40 rows) and with one
+    workgroup per row (150 rows; fp8 rows expanded once for HCA)."""
+    B, H, n_win, m = 1, 24, 128, 4 if mode == "csa" else 128
+    q_pos = [9000]
+    ncomp = (q_pos[0] + T) // m + 1
+    comp = _cache(61, B, ncomp, orc.FP8, "comp")
+    win = _cache(62, B, n_win + T + 8, orc.FP8, "win")
+    q = _q(63, B, T, H)
+    sink = S.normal(64, "sink", (H,))
+    idx, k = None, 512
+    if mode == "csa":
+        idx = orc.topk_select(S.normal(65, "sc", (B, T, ncomp)), q_pos=q_pos, m=m, k=k)
+    scale = 1.0 / np.sqrt(576)
+    o, lse = orc.attention(q, q_pos=q_pos, comp=comp, m=m, idx=idx, win=win, n_win=n_win, sink=sink,
+                           sm_scale=scale, rope_theta=10000.0)
+    maxk = (k if mode == "csa" else ncomp) + n_win
+    ws = torch.empty(max(16, lca.attn_workspace_size(B, T, H, 576, maxk)), dtype=torch.uint8, device="cuda")
+    # (a store of a head past H would land on the next row's first heads and fail the comparison)
+    out = torch.full((B, T, H, 576), 7.0, dtype=torch.float32, device="cuda")
+    lg = torch.full((B, T, H), 7.0, dtype=torch.float32, device="cuda")
     kw = dict(q_pos=q_pos, comp=kv_dev(comp), m=m, win=kv_dev(win), n_win=n_win, sink=dev(sink),
               sm_scale=scale, rope_theta=10000.0, lse=lg, ws=ws)
     if mode == "csa":
