@@ -54,10 +54,11 @@ def test_kv_compress(fmt, m, overlap, dn, dr):
 
 
 @pytest.mark.parametrize("fmt", [orc.F32, orc.BF16, orc.FP8])
-@pytest.mark.parametrize("m,overlap", [(128, 0), (32, 1), (4, 1)])
-def test_kv_compress_split(fmt, m, overlap):
+@pytest.mark.parametrize("m,overlap,ring", [(128, 0, 0), (32, 1, 0), (4, 1, 0), (128, 0, 1)])
+def test_kv_compress_split(fmt, m, overlap, ring):
     """With a workspace, entries of long row lists (m (1 + overlap) >= 64) are pooled by several
-    workgroups each and merged: the same bars against the oracle; m = 4 ignores the workspace."""
+    workgroups each and merged: the same bars against the oracle; m = 4 ignores the workspace.  ring:
+    a ring of 2 rows (only the newest entries of the call are written, at s mod 2)."""
     c, B = 576, 2
     n = 3 * m + 5 if m > 4 else 203
     first = [0, 2 * m + 1]
@@ -65,10 +66,11 @@ def test_kv_compress_split(fmt, m, overlap):
     ba = S.normal(5, "bias_a", (m, c))
     bb = S.normal(5, "bias_b", (m, c))
     gamma = (1.0 + 0.1 * S.normal(5, "gamma", (c,))).astype(np.float32)
-    cap = (first[1] + n) // m + 2
+    cap = 2 if ring else (first[1] + n) // m + 2
     o = orc.KV.empty(fmt, B, cap, 512, 64)
     orc.kv_compress(ca, za, cb if overlap else None, zb if overlap else None, o, m=m, overlap=overlap,
-                    first_pos=first, bias_a=ba, bias_b=bb if overlap else None, gamma=gamma, rope_theta=1e4)
+                    first_pos=first, bias_a=ba, bias_b=bb if overlap else None, gamma=gamma, rope_theta=1e4,
+                    ring=ring)
     wsz = lca.compress_workspace_size(orc.BF16, m, overlap, 512, 64)
     assert (wsz > 0) == (m * (1 + overlap) >= 64)
     ws = torch.full((max(16, wsz),), 255, dtype=torch.uint8, device="cuda")  # (no initialisation needed)
@@ -76,7 +78,7 @@ def test_kv_compress_split(fmt, m, overlap):
     for _ in range(2):  # twice on one workspace
         lca.kv_compress(dev(ca), dev(za), dev(cb) if overlap else None, dev(zb) if overlap else None, g, m=m,
                         overlap=overlap, first_pos=first, bias_a=dev(ba), bias_b=dev(bb) if overlap else None,
-                        gamma=dev(gamma), rope_theta=1e4, ws=ws)
+                        gamma=dev(gamma), rope_theta=1e4, ring=ring, ws=ws)
         torch.cuda.synchronize()
         assert_kv_close(kv_host(g), o)
 
@@ -367,8 +369,9 @@ def _nibbles(b: np.ndarray) -> np.ndarray:
     return out
 
 
-@pytest.mark.parametrize("m,overlap,dn", [(4, 1, 128), (1, 0, 128), (1, 0, 64), (1, 0, 576), (128, 0, 128)])
-def test_kv_compress_mxfp4(m, overlap, dn):
+@pytest.mark.parametrize("m,overlap,dn,split", [(4, 1, 128, False), (1, 0, 128, False), (1, 0, 64, False),
+                                               (1, 0, 576, False), (128, 0, 128, False), (128, 0, 128, True)])
+def test_kv_compress_mxfp4(m, overlap, dn, split):
     """MXFP4 rows against the oracle: identical scale bytes and codes, except where the fp32 value the
     library rounds sits within 1e-5 (relative) of a decision boundary of the oracle's fp64 value: a block
     maximum at a power of two (scale one step apart), or an element at a midpoint between two codes."""
@@ -384,8 +387,11 @@ def test_kv_compress_mxfp4(m, overlap, dn):
     o32 = orc.KV.empty(orc.F32, B, cap, dn, 0)
     orc.kv_compress(ca, za, cb if overlap else None, zb if overlap else None, o32, **kw)
     g = lca.KV.empty(orc.MXFP4, B, cap, dn, 0)
+    # split: the rows of each entry pooled by several workgroups, merged by the finish launch
+    ws = torch.empty(lca.compress_workspace_size(orc.BF16, m, overlap, dn, 0), dtype=torch.uint8,
+                     device="cuda") if split else None
     lca.kv_compress(dev(ca), dev(za), dev(cb) if overlap else None, dev(zb) if overlap else None, g, m=m,
-                    overlap=overlap, first_pos=first, bias_a=dev(ba), bias_b=dev(bb) if overlap else None)
+                    overlap=overlap, first_pos=first, bias_a=dev(ba), bias_b=dev(bb) if overlap else None, ws=ws)
     torch.cuda.synchronize()
     gh = kv_host(g)
     y = o32.nope.astype(np.float64).reshape(B, cap, dn // 32, 32)
