@@ -3,7 +3,8 @@
 // vectors): Y[b][m][n] = sum_k X[b][m][k] W[b][n][k], X and W bf16 with K contiguous (W holds one
 // output per row, as a weight matrix), f32 accumulation, Y f32 or bf16.
 //
-// Many rows: MFMA tiles.  A 256-thread workgroup computes a 128 x 128 tile of Y, each wave a
+// Many rows: MFMA tiles (gemm_big's 256 x 256 tiles for maps that have enough of them, below).  A
+// 256-thread workgroup computes a 128 x 128 tile of Y, each wave a
 // 64 x 64 quarter as 4 x 4 blocks of v_mfma_f32_16x16x32_bf16 (both operands K-contiguous: lane l
 // reads 8 consecutive k of row l mod 16 with one ds_read_b128).  K advances 64 at a time through
 // two LDS buffers whose rows are padded to 80 elements (160 bytes; measured against 64, 72, 88 and
@@ -21,6 +22,7 @@ namespace lca {
 
 constexpr int kGT = 128, kGK = 64, kGS = 80;  // tile rows / columns, K slice, LDS row stride
 constexpr int kGemvRows = 4;                  // M at most this: the streaming kernel
+constexpr int64_t kGemmBigTiles = 256;        // 256 x 256 tiles from which a map takes gemm_big
 
 template <typename TY>
 __device__ __forceinline__ void put_y(TY* p, float v);
@@ -141,6 +143,106 @@ __global__ void __launch_bounds__(256) gemm_mfma(GemmArgs a) {
         }
 }
 
+// Large maps (enough 256 x 256 tiles to fill the GPU): a 512-thread workgroup computes a 256 x 256 tile
+// of Y, each of its eight waves a 64 x 128 part as 4 x 8 blocks of v_mfma_f32_16x16x32_bf16 (128
+// accumulator registers, two waves per SIMD).  Per byte brought in from L2 the tile does twice the
+// work of gemm_mfma's 128 x 128 one, whose operand traffic (64 flop per byte) bounds it on this GPU.
+// 64-deep K slices in two LDS buffers (rows padded to 72 elements); the next slice's global loads go
+// out before a slice's products (one register set: a second, for loads two slices ahead, spills), one
+// barrier per slice.  (A four-wave form with 128 x 128 per wave needs all 256 AGPRs for its
+// accumulators, and the register allocator then moved them through VGPRs on every MFMA.)
+constexpr int kBT = 256, kBS = 72;  // tile rows / columns, LDS row stride
+template <typename TY>
+__global__ void __launch_bounds__(512) gemm_big(GemmArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][kBT * kBS];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kBT * kBS];
+    const int b = blockIdx.z;
+    const int m0 = blockIdx.y * kBT, n0 = blockIdx.x * kBT;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int wm = (wv >> 1) * 64, wn = (wv & 1) * 128;
+    const int M = a.M, N = a.N, K = a.K;
+    const uint16_t* X = (const uint16_t*)a.x + (int64_t)b * a.sx;
+    const uint16_t* W = (const uint16_t*)a.w + (int64_t)b * a.sw;
+
+    // chunk q = tid + 512 i (i < 4) of a slice: row tid / 8 + 64 i, elements kk = 8 (tid mod 8) ..; rows past
+    // M / N re-read the last row (not stored), chunks past K read the last chunk and are zeroed when stored
+    const int r0 = tid >> 3, kk = 8 * (tid & 7);
+    const int lo0 = r0 * kBS + kk;
+    uint32_t xo[4], wo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        xo[i] = (uint32_t)((int64_t)min(m0 + r0 + 64 * i, M - 1) * a.ldx);
+        wo[i] = (uint32_t)((int64_t)min(n0 + r0 + 64 * i, N - 1) * a.ldw);
+    }
+    u32x4 rx[4], rw[4];
+    auto load = [&](int k0) {
+        const uint32_t kc = (uint32_t)min(k0 + kk, K - 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            rx[i] = *(const u32x4*)(X + (xo[i] + kc));
+            rw[i] = *(const u32x4*)(W + (wo[i] + kc));
+        }
+    };
+    auto store = [&](int buf, int k0) {
+        const bool ok = k0 + kk < K;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            *(u32x4*)&As[buf][lo0 + 64 * kBS * i] = ok ? rx[i] : u32x4{0u, 0u, 0u, 0u};
+            *(u32x4*)&Bs[buf][lo0 + 64 * kBS * i] = ok ? rw[i] : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+
+    f32x4 acc[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int fr = (lane & 15) * kBS + 8 * (lane >> 4);  // this lane's fragment offset in a block
+    auto compute = [&](int buf) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            bf16x8 af[4], bw[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) af[i] = *(const bf16x8*)&As[buf][(wm + 16 * i) * kBS + fr + 32 * s];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) bw[j] = *(const bf16x8*)&Bs[buf][(wn + 16 * j) * kBS + fr + 32 * s];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bw[j], acc[i][j], 0, 0, 0);
+        }
+    };
+    // slice kt is in LDS buffer kt mod 2; past the last slice the loads re-read it (branch-free) and the
+    // store goes to the free buffer
+    const int nk = (K + kGK - 1) / kGK, klast = (nk - 1) * kGK;
+    load(0);
+    store(0, 0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        load(min((kt + 1) * kGK, klast));
+        asm volatile("" ::: "memory");
+        compute(cur);
+        asm volatile("" ::: "memory");
+        store(cur ^ 1, (kt + 1) * kGK);
+        __syncthreads();
+    }
+
+    TY* Y = (TY*)a.y + (int64_t)b * a.sy;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int n = n0 + wn + 16 * j + (lane & 15);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + wm + 16 * i + 4 * (lane >> 4) + r;
+                if (m < M && n < N) put_y<TY>(Y + (int64_t)m * a.ldy + n, acc[i][j][r]);
+            }
+        }
+}
+
 // KS: the four waves split K over the workgroup's 4 outputs (few outputs: more workgroups); else
 // each wave takes 4 outputs of its own over all of K (16 per workgroup).
 template <int MR, typename TY, bool KS>
@@ -242,6 +344,13 @@ static void launch_gemm_t(const GemmArgs& a, hipStream_t st) {
             else if (a.M == 2) hipLaunchKernelGGL((gemv_stream<2, TY, false>), grid, dim3(256), 0, st, a);
             else hipLaunchKernelGGL((gemv_stream<4, TY, false>), grid, dim3(256), 0, st, a);
         }
+        return;
+    }
+    const int64_t big = (int64_t)((a.N + kBT - 1) / kBT) * ((a.M + kBT - 1) / kBT) * a.batch;
+    if (big >= kGemmBigTiles) {  // enough 256 x 256 tiles to fill the GPU
+        dim3 grid((unsigned)((a.N + kBT - 1) / kBT), (unsigned)((a.M + kBT - 1) / kBT), (unsigned)a.batch);
+        if (trace_on()) trace("  gemm_big: grid (%u, %u, %u) x 512, 256 x 256 tiles", grid.x, grid.y, grid.z);
+        hipLaunchKernelGGL((gemm_big<TY>), grid, dim3(512), 0, st, a);
         return;
     }
     dim3 grid((unsigned)((a.N + kGT - 1) / kGT), (unsigned)((a.M + kGT - 1) / kGT), (unsigned)a.batch);

@@ -519,7 +519,8 @@ def test_attention_append(fmt, mode, B, T, xdt):
 # --------------------------------------------------------------------------
 
 @pytest.mark.parametrize("M,N,K,bt", [(1, 300, 136, 1), (3, 77, 520, 2), (4, 64, 8, 1), (2, 33, 4104, 1),
-                                      (200, 130, 72, 1), (256, 256, 1024, 3), (129, 257, 200, 2)])
+                                      (200, 130, 72, 1), (256, 256, 1024, 3), (129, 257, 200, 2),
+                                      (600, 4400, 200, 5)])  # (the last: 270 tiles of 256 x 256, ragged)
 @pytest.mark.parametrize("ydt", [orc.F32, orc.BF16])
 def test_linear(M, N, K, bt, ydt):
     """Streaming (M <= 4) and tiled (larger M) maps against the oracle: f32 within 1e-5 of the sum of
