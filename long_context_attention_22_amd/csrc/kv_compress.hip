@@ -252,13 +252,13 @@ __device__ __forceinline__ void merge_slots(float (*st)[kPoolSlots][kPoolMaxC], 
 // bf16 inputs, c a multiple of 8 (at most kPoolMaxC): the block's rows are read 16 bytes (8 channels) per
 // lane.  Thread t = (row slot rs = t / (c / 8), chunk ch = t % (c / 8)) pools channels 8 ch .. 8 ch + 7
 // over the rows rs, rs + kPoolSlots, ... of the entry's row list (the a-block's m rows, then the
-// b-block's m rows when overlapping), kPoolRows rows' loads (C, Z and the bias rows) in flight at a time,
-// as an online softmax per channel; the kPoolSlots partial states (max, sum, weighted sum) of a
-// channel are merged through LDS in slot order, then thread j < c finishes channel j as above.  Each
-// wave moves 1 KB per load instruction instead of 128 bytes, and a row is read by c / 8 lanes side by
-// side.  NR: rows per slot in flight, at most kPoolRows -- fewer for short row lists (a CSA entry's 8 rows
-// are one per slot), so that no thread issues padding loads and two workgroups share a CU (the 4096-token
-// chunk's CSA call, 1,024 entries: 25.7 -> 23.1 us).
+// b-block's m rows when overlapping), NR rows' loads (C, Z and the bias rows) in flight at a time, as
+// an online softmax per channel; the kPoolSlots partial states (max, sum, weighted sum) of a channel are
+// merged through LDS in slot order, then thread j < c finishes channel j as above.  Each wave moves 1 KB
+// per load instruction instead of 128 bytes, and a row is read by c / 8 lanes side by side.  NR is
+// kPoolRows for long row lists and the rows a slot holds for short ones (a CSA entry's 8 rows are one per
+// slot), so that no thread issues padding loads and two workgroups share a CU (the 4096-token chunk's CSA
+// call, 1,024 entries: 25.7 -> 23.1 us).
 template <int FMT, int NR>
 __global__ void __launch_bounds__(kPoolMaxC, NR <= 2 ? 5 : 1) kv_pool_wide(CompressArgs a) {
     const int b = blockIdx.y;
