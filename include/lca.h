@@ -344,7 +344,9 @@ int lca_hca_attn_append(const void* q, int32_t q_dtype, int32_t H, int32_t B, in
  * f32 sum).  Element (b, m, k) of x is at x + b sx + m ldx + k, (b, n, k) of
  * w at w + b sw + n ldw + k, (b, m, n) of y at y + b sy + m ldy + n (strides
  * in elements).  Requires K a positive multiple of 8; ldx, ldw >= K and,
- * with sx and sw, multiples of 8; ldy >= N; x, w 16-byte aligned.  M <= 4
+ * with sx and sw, multiples of 8; ldy >= N; x, w 16-byte aligned; one batch
+ * entry of x and of w below 2^32 elements ((M - 1) ldx + K and (N - 1) ldw
+ * + K), else LCA_ESHAPE (the MFMA kernels use 32-bit row offsets).  M <= 4
  * takes a kernel that streams w once (decode); larger M, MFMA tiles.
  */
 int lca_linear(const void* x, int64_t ldx, int64_t sx, const void* w, int64_t ldw, int64_t sw, void* y,

@@ -757,6 +757,12 @@ int lca_hca_attn_noalloc(const void* q, int32_t q_dtype, int32_t H, int32_t B, i
                        out, out_dtype, lse, ws, LCA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
+// The MFMA GEMM kernels address the rows of one batch entry with 32-bit element offsets from its base:
+// (rows - 1) * ld + K must stay below 2^32.
+static bool gemm_offsets_fit(int64_t rows, int64_t ld, int64_t K) {
+    return rows < 1 || (rows - 1) * ld + K <= (int64_t)UINT32_MAX;
+}
+
 int lca_linear(const void* x, int64_t ldx, int64_t sx, const void* w, int64_t ldw, int64_t sw, void* y,
                int32_t y_dtype, int64_t ldy, int64_t sy, int32_t M, int32_t N, int32_t K, int32_t batch,
                void* stream) {
@@ -772,6 +778,8 @@ int lca_linear(const void* x, int64_t ldx, int64_t sx, const void* w, int64_t ld
         return fail(LCA_EALIGN, "x and w strides must be multiples of 8 elements (16-byte rows)");
     if (!aligned16(x) || !aligned16(w) || ((uintptr_t)y & (y_dtype == LCA_F32 ? 3u : 1u)))
         return fail(LCA_EALIGN, "x and w must be 16-byte aligned, y aligned to its element");
+    if (!gemm_offsets_fit(M, ldx, K) || !gemm_offsets_fit(N, ldw, K))
+        return fail(LCA_ESHAPE, "one batch entry of x or w spans 2^32 elements or more");
     lca::GemmArgs a;
     memset(&a, 0, sizeof a);
     a.x = x; a.w = w; a.y = y; a.ldx = ldx; a.sx = sx; a.ldw = ldw; a.sw = sw; a.ldy = ldy; a.sy = sy;
@@ -792,6 +800,9 @@ int lca_grouped_out_proj(const void* o, int32_t T, int32_t H, int32_t c, int32_t
         return fail(LCA_ESHAPE, "(H / g) * c and d_g must be multiples of 8");
     if (!aligned16(o) || !aligned16(wg) || !aligned16(wo) || !aligned16(mid) || !aligned16(out))
         return fail(LCA_EALIGN, "pointers must be 16-byte aligned");
+    if (!gemm_offsets_fit(T, (int64_t)H * c, kg) || !gemm_offsets_fit(d_g, kg, kg) ||
+        !gemm_offsets_fit(T, (int64_t)g * d_g, (int64_t)g * d_g) || !gemm_offsets_fit(d, (int64_t)g * d_g, (int64_t)g * d_g))
+        return fail(LCA_ESHAPE, "an operand spans 2^32 elements or more");
     if (T == 0) return LCA_OK;
     lca::GemmArgs a;
     memset(&a, 0, sizeof a);

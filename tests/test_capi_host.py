@@ -272,6 +272,13 @@ def test_linear_validation(L):
     assert call(x=FAKE + 8) == 4
     assert L.lca_grouped_out_proj(FAKE, 4, 6, 64, 4, FAKE2, 64, FAKE2, 96, FAKE2, FAKE2, lca.F32, None) == 2  # H % g
     assert L.lca_grouped_out_proj(FAKE, 4, 8, 63, 4, FAKE2, 64, FAKE2, 96, FAKE2, FAKE2, lca.F32, None) == 2  # (H/g) c % 8
+    # one batch entry's rows are addressed with 32-bit element offsets: 2^32 elements or more are refused
+    assert call(M=1 << 20, ldx=4096, ldw=4096, K=4096) == 2          # x: (2^20 - 1) 4096 + 4096 = 2^32
+    assert b"2^32" in L.lca_last_error()
+    assert call(N=1 << 20, ldx=4096, ldw=4096, K=4096, ldy=1 << 20) == 2
+    assert b"2^32" in L.lca_last_error()
+    assert L.lca_grouped_out_proj(FAKE, 1 << 17, 64, 576, 8, FAKE2, 1024, FAKE2, 4096, FAKE2, FAKE2,
+                                  lca.F32, None) == 2              # o: 2^17 tokens x 36,864
 
 
 def test_cache_validation(L):
