@@ -361,7 +361,8 @@ int lca_linear(const void* x, int64_t ldx, int64_t sx, const void* w, int64_t ld
  * d_g]), and mid is projected to d dims by wo (bf16 [d][g * d_g]) into out
  * ([T][d], out_dtype LCA_F32 or LCA_BF16).  Two lca_linear launches.
  * Requires H % g == 0, (H / g) * c and d_g multiples of 8, 16-byte aligned
- * pointers.
+ * pointers, and each of o, wg, mid and wo below 2^32 elements as lca_linear
+ * addresses them (else LCA_ESHAPE).
  */
 int lca_grouped_out_proj(const void* o, int32_t T, int32_t H, int32_t c, int32_t g, const void* wg,
                          int32_t d_g, const void* wo, int32_t d, void* mid, void* out, int32_t out_dtype,
