@@ -75,8 +75,14 @@ def test_kv_compress_split(fmt, m, overlap, ring):
     assert (wsz > 0) == (m * (1 + overlap) >= 64)
     ws = torch.full((max(16, wsz),), 255, dtype=torch.uint8, device="cuda")  # (no initialisation needed)
     g = lca.KV.empty(fmt, B, cap, 512, 64)
-    for _ in range(2):  # twice on one workspace
-        lca.kv_compress(dev(ca), dev(za), dev(cb) if overlap else None, dev(zb) if overlap else None, g, m=m,
+
+    def window(x):  # the rows as a window of a longer per-sequence stream (sequence stride n + 24 rows)
+        full = torch.zeros(B, n + 24, c, dtype=torch.bfloat16, device="cuda")
+        full[:, 16:16 + n] = dev(x)
+        return full[:, 16:16 + n]
+    for strided in (False, True):  # twice on one workspace, the second time through row windows
+        src = window if strided else dev
+        lca.kv_compress(src(ca), src(za), src(cb) if overlap else None, src(zb) if overlap else None, g, m=m,
                         overlap=overlap, first_pos=first, bias_a=dev(ba), bias_b=dev(bb) if overlap else None,
                         gamma=dev(gamma), rope_theta=1e4, ring=ring, ws=ws)
         torch.cuda.synchronize()
