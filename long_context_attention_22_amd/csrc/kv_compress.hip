@@ -160,8 +160,33 @@ __global__ void __launch_bounds__(1024) kv_compress_kernel(CompressArgs a) {
 // wave moves 1 KB per load instruction instead of 128 bytes, and a row is read by c / 8 lanes side by
 // side.
 constexpr int kPoolSlots = 8;
-constexpr int kPoolRows = 6;    // rows whose loads a thread has in flight at once (registers: 16 each)
+constexpr int kPoolRows = 4;    // rows whose loads a thread has in flight at once (registers: 16 each)
 constexpr int kPoolMaxC = 576;  // (the merge's LDS: 3 x 8 x 576 floats, so two workgroups fit a CU)
+constexpr int kPairRows = 2;    // kv_pool_pair: rows of each of its two entries in flight at once
+constexpr int64_t kPoolPairMin = 512;  // (entry, sequence) pairs from which kv_pool_pair serves a call
+
+// One row of a thread's 8 channels into their online-softmax states: zw, cw the row's Z and C values (bf16
+// pairs), bs its 8 bias values.
+__device__ __forceinline__ void pool_row(const u32x4& zw4, const u32x4& cw4, const f32x4* bs, float* mx, float* den,
+                                         float* num) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t zw = zw4[i >> 1], cw = cw4[i >> 1];
+        const float z = __uint_as_float((i & 1) ? (zw & 0xffff0000u) : (zw << 16)) + bs[i >> 2][i & 3];
+        const float cv = __uint_as_float((i & 1) ? (cw & 0xffff0000u) : (cw << 16));
+        // lazy rescaling: the reference moves only when a logit exceeds it by more than 16
+        // (weights stay <= e^16), so most rows cost one exponential instead of two
+        if (z > mx[i] + 16.0f) {
+            const float corr = __expf(mx[i] - z);  // (reference -inf: 0)
+            den[i] *= corr;
+            num[i] *= corr;
+            mx[i] = z;
+        }
+        const float e = __expf(z - mx[i]);
+        den[i] += e;
+        num[i] = fmaf(e, cv, num[i]);
+    }
+}
 
 // Online softmax of this thread's rows k_lo + rs, k_lo + rs + kPoolSlots, ... (below k_hi) of entry s's row
 // list, channels 8 ch .. 8 ch + 7, NR rows' loads in flight at a time.
@@ -187,8 +212,10 @@ __device__ __forceinline__ void pool_wide_rows(const CompressArgs& a, int b, int
             const uint16_t* zp = (const uint16_t*)(bb ? a.z_b : a.z_a) + row * c + 8 * ch;
             const uint16_t* cp = (const uint16_t*)(bb ? a.c_b : a.c_a) + row * c + 8 * ch;
             const float* bp = bb ? a.bias_b : a.bias_a;
-            zc[u][0] = *(const u32x4*)zp;
-            zc[u][1] = *(const u32x4*)cp;
+            // C and Z rows are read by this entry only: non-temporal, so they do not push the bias
+            // rows (read by every entry) out of the caches
+            zc[u][0] = __builtin_nontemporal_load((const u32x4*)zp);
+            zc[u][1] = __builtin_nontemporal_load((const u32x4*)cp);
             if (bp) {
                 bs[u][0] = *(const f32x4*)(bp + (int64_t)i * c + 8 * ch);
                 bs[u][1] = *(const f32x4*)(bp + (int64_t)i * c + 8 * ch + 4);
@@ -197,26 +224,51 @@ __device__ __forceinline__ void pool_wide_rows(const CompressArgs& a, int b, int
             }
         }
 #pragma unroll
-        for (int u = 0; u < NR; ++u) {
-            if (!ok[u]) continue;
+        for (int u = 0; u < NR; ++u)
+            if (ok[u]) pool_row(zc[u][0], zc[u][1], bs[u], mx, den, num);
+    }
+}
+
+// Two consecutive entries s, s + 1 of a call without overlap (each list is its own block's m rows), as
+// pool_wide_rows for each, with each bias row loaded once for both: the rows of entry s + 1 are m rows
+// further.  two = false (s + 1 past the call's entries): the second state repeats the first entry's rows
+// and is dropped.
+template <int NR>
+__device__ __forceinline__ void pool_pair_rows(const CompressArgs& a, int b, int64_t s, bool two, int rs, int ch,
+                                               int c, float* mx, float* den, float* num, float* mx2, float* den2,
+                                               float* num2) {
+    const int m = a.m;
+    const int64_t p0 = a.first_pos.v[b];
+    const int64_t ra = (int64_t)b * a.in_stride + (s * m - p0);  // entry s's first row
+    const int64_t d2 = two ? (int64_t)m * c : 0;                 // entry s + 1's rows, in elements
+    for (int k0 = rs; k0 < m; k0 += NR * kPoolSlots) {
+        u32x4 zc[NR][4];
+        f32x4 bs[NR][2];
+        bool ok[NR];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t zw = zc[u][0][i >> 1], cw = zc[u][1][i >> 1];
-                const float z = __uint_as_float((i & 1) ? (zw & 0xffff0000u) : (zw << 16)) + bs[u][i >> 2][i & 3];
-                const float cv = __uint_as_float((i & 1) ? (cw & 0xffff0000u) : (cw << 16));
-                // lazy rescaling: the reference moves only when a logit exceeds it by more than 16
-                // (weights stay <= e^16), so most rows cost one exponential instead of two
-                if (z > mx[i] + 16.0f) {
-                    const float corr = __expf(mx[i] - z);  // (reference -inf: 0)
-                    den[i] *= corr;
-                    num[i] *= corr;
-                    mx[i] = z;
-                }
-                const float e = __expf(z - mx[i]);
-                den[i] += e;
-                num[i] = fmaf(e, cv, num[i]);
+        for (int u = 0; u < NR; ++u) {
+            const int k = k0 + u * kPoolSlots;
+            ok[u] = k < m;
+            const int i = ok[u] ? k : 0;  // a slot past the block reads its first row (dropped below)
+            const uint16_t* zp = (const uint16_t*)a.z_a + (ra + i) * c + 8 * ch;
+            const uint16_t* cp = (const uint16_t*)a.c_a + (ra + i) * c + 8 * ch;
+            zc[u][0] = __builtin_nontemporal_load((const u32x4*)zp);
+            zc[u][1] = __builtin_nontemporal_load((const u32x4*)cp);
+            zc[u][2] = __builtin_nontemporal_load((const u32x4*)(zp + d2));
+            zc[u][3] = __builtin_nontemporal_load((const u32x4*)(cp + d2));
+            if (a.bias_a) {
+                bs[u][0] = *(const f32x4*)(a.bias_a + (int64_t)i * c + 8 * ch);
+                bs[u][1] = *(const f32x4*)(a.bias_a + (int64_t)i * c + 8 * ch + 4);
+            } else {
+                bs[u][0] = bs[u][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             }
         }
+#pragma unroll
+        for (int u = 0; u < NR; ++u)
+            if (ok[u]) {
+                pool_row(zc[u][0], zc[u][1], bs[u], mx, den, num);
+                pool_row(zc[u][2], zc[u][3], bs[u], mx2, den2, num2);
+            }
     }
 }
 
@@ -258,7 +310,10 @@ __device__ __forceinline__ void merge_slots(float (*st)[kPoolSlots][kPoolMaxC], 
 // per load instruction instead of 128 bytes, and a row is read by c / 8 lanes side by side.  NR is
 // kPoolRows for long row lists and the rows a slot holds for short ones (a CSA entry's 8 rows are one per
 // slot), so that no thread issues padding loads and two workgroups share a CU (the 4096-token chunk's CSA
-// call, 1,024 entries: 25.7 -> 23.1 us).
+// call, 1,024 entries: 25.7 -> 23.1 us).  An HCA entry's 128 rows are 16 per slot, four rounds of
+// kPoolRows = 4 (115 VGPRs, one workgroup per CU); with the C / Z loads non-temporal a 65,536-row call
+// took 38.9 us this way against 41.4 us at six rows in flight (three rounds, two of the 18 row loads
+// padding) and 39.5 us at three -- such calls now go to kv_pool_pair below (35 us).
 template <int FMT, int NR>
 __global__ void __launch_bounds__(kPoolMaxC, NR <= 2 ? 5 : 1) kv_pool_wide(CompressArgs a) {
     const int b = blockIdx.y;
@@ -289,12 +344,50 @@ __global__ void __launch_bounds__(kPoolMaxC, NR <= 2 ? 5 : 1) kv_pool_wide(Compr
     finish_entry<FMT>(a, y, b, s, red, ys);
 }
 
+// Many entries of long blocks without overlap (a prefill's m = 128 blocks: kPoolPairMin or more (entry,
+// sequence) pairs): one workgroup per two consecutive entries (grid (ceil(entries / 2), B)), each row slot
+// of a thread pooling both through pool_pair_rows, so that the bias rows -- the same for every entry, twice
+// the bytes of its C and Z rows in f32 -- are read once per two entries; then kv_pool_wide's merge and
+// finish for the first entry and for the second.  A 65,536-row call: 256 workgroups, one per CU.
+template <int FMT, int NR>
+__global__ void __launch_bounds__(kPoolMaxC, 1) kv_pool_pair(CompressArgs a) {
+    const int b = blockIdx.y;
+    const int m = a.m;
+    const int64_t p0 = a.first_pos.v[b];
+    const int64_t s = a.s_lo.v[b] + 2 * (int64_t)blockIdx.x;
+    const int64_t s_hi = (p0 + a.n_rows) / m;
+    if (s >= s_hi) return;            // uniform over the workgroup
+    const bool two = s + 1 < s_hi;    // (uniform too)
+    const int c = a.out.d_nope + a.out.d_rope;
+    const int nch = c >> 3;
+    const int t = threadIdx.x;
+    const int rs = t / nch, ch = t - rs * nch;
+    __shared__ float red[16];
+    __shared__ float ys[1024];
+    __shared__ float st[3][kPoolSlots][kPoolMaxC];
+    float mx[8], den[8], num[8], mx2[8], den2[8], num2[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        mx[i] = mx2[i] = -INFINITY;
+        den[i] = den2[i] = 0.0f;
+        num[i] = num2[i] = 0.0f;
+    }
+    pool_pair_rows<NR>(a, b, s, two, rs, ch, c, mx, den, num, mx2, den2, num2);
+    float M, dn, nu;
+    merge_slots(st, rs, ch, c, mx, den, num, M, dn, nu);
+    finish_entry<FMT>(a, t < c ? nu / dn : 0.0f, b, s, red, ys);
+    if (!two) return;
+    __syncthreads();  // every thread is past the first merge's reads of st and the first finish's of red, ys
+    merge_slots(st, rs, ch, c, mx2, den2, num2, M, dn, nu);
+    finish_entry<FMT>(a, t < c ? nu / dn : 0.0f, b, s + 1, red, ys);
+}
+
 // Few entries (a 4096-token chunk's m = 128 blocks: 32 workgroups of kv_pool_wide would leave most of the
 // GPU idle): with a workspace the call cuts each entry's row list into a.parts ranges of a.part_len rows,
 // one workgroup each (kv_pool_part, grid (entries x parts, B)), which stores the range's merged state of
 // every channel -- reference, sum, weighted sum: ws[((b E + e) parts + p)][3][c], E = a.max_entries --
 // and kv_pool_finish (grid (entries, B)) merges an entry's parts in part order and finishes it.  NR: a part's
-// rows per row slot (part_len / kPoolSlots, rounded up), so that a part issues no padding loads.
+// rows per row slot (part_len / kPoolSlots, rounded up) when that is 1 or 2, else kPoolRows.
 template <int NR>
 __global__ void __launch_bounds__(kPoolMaxC) kv_pool_part(CompressArgs a) {
     const int b = blockIdx.y;
@@ -421,7 +514,6 @@ template <int FMT>
 static void launch_pool_wide(int per_slot, dim3 grid, dim3 block, hipStream_t st, const CompressArgs& a) {
     if (per_slot <= 1) hipLaunchKernelGGL((kv_pool_wide<FMT, 1>), grid, block, 0, st, a);
     else if (per_slot <= 2) hipLaunchKernelGGL((kv_pool_wide<FMT, 2>), grid, block, 0, st, a);
-    else if (per_slot <= 4) hipLaunchKernelGGL((kv_pool_wide<FMT, 4>), grid, block, 0, st, a);
     else hipLaunchKernelGGL((kv_pool_wide<FMT, kPoolRows>), grid, block, 0, st, a);
 }
 
@@ -465,7 +557,6 @@ hipError_t launch_kv_compress(const CompressArgs& a, hipStream_t st) {
             const int nr = (a.part_len + kPoolSlots - 1) / kPoolSlots;
             if (nr == 1) hipLaunchKernelGGL(kv_pool_part<1>, pgrid, wblock, 0, st, a);
             else if (nr == 2) hipLaunchKernelGGL(kv_pool_part<2>, pgrid, wblock, 0, st, a);
-            else if (nr <= 4) hipLaunchKernelGGL(kv_pool_part<4>, pgrid, wblock, 0, st, a);
             else hipLaunchKernelGGL(kv_pool_part<kPoolRows>, pgrid, wblock, 0, st, a);
             switch (a.out.fmt) {
                 case LCA_F32: hipLaunchKernelGGL((kv_pool_finish<LCA_F32>), grid, wblock, 0, st, a); break;
@@ -476,6 +567,17 @@ hipError_t launch_kv_compress(const CompressArgs& a, hipStream_t st) {
             return hipGetLastError();
         }
         const int per_slot = (a.m * (1 + a.overlap) + kPoolSlots - 1) / kPoolSlots;  // rows per slot, at most
+        if (!a.overlap && per_slot > 2 && a.max_entries * a.B >= kPoolPairMin) {
+            const dim3 pgrid((unsigned)((a.max_entries + 1) / 2), grid.y);
+            if (trace_on()) trace("  compress: kv_pool_pair grid (%u, %u)", pgrid.x, pgrid.y);
+            switch (a.out.fmt) {
+                case LCA_F32: hipLaunchKernelGGL((kv_pool_pair<LCA_F32, kPairRows>), pgrid, wblock, 0, st, a); break;
+                case LCA_BF16: hipLaunchKernelGGL((kv_pool_pair<LCA_BF16, kPairRows>), pgrid, wblock, 0, st, a); break;
+                case LCA_MXFP4: hipLaunchKernelGGL((kv_pool_pair<LCA_MXFP4, kPairRows>), pgrid, wblock, 0, st, a); break;
+                default: hipLaunchKernelGGL((kv_pool_pair<LCA_FP8, kPairRows>), pgrid, wblock, 0, st, a); break;
+            }
+            return hipGetLastError();
+        }
         switch (a.out.fmt) {
             case LCA_F32: launch_pool_wide<LCA_F32>(per_slot, grid, wblock, st, a); break;
             case LCA_BF16: launch_pool_wide<LCA_BF16>(per_slot, grid, wblock, st, a); break;

@@ -89,6 +89,34 @@ def test_kv_compress_split(fmt, m, overlap, ring):
         assert_kv_close(kv_host(g), o)
 
 
+@pytest.mark.parametrize("fmt", [orc.F32, orc.BF16, orc.FP8])
+@pytest.mark.parametrize("bias,ws", [(True, False), (False, False), (True, True)])
+def test_kv_compress_pairs(fmt, bias, ws):
+    """Calls of 512 or more m = 128 entries (entries x sequences) pool two consecutive entries per
+    workgroup; sequence 0 has an odd count (its last workgroup pools one entry), sequence 1 starts mid-block.
+    ws: the same call with a workspace (too many entries to split them), which takes the same path."""
+    m, c, B = 128, 576, 2
+    n = 257 * m + 5
+    first = [0, 2 * m + 1]
+    ca, za, _, _ = _raw(71, B, n, c)
+    ba = S.normal(7, "bias_a", (m, c)) if bias else None
+    gamma = (1.0 + 0.1 * S.normal(7, "gamma", (c,))).astype(np.float32)
+    cap = (first[1] + n) // m + 2
+    o = orc.KV.empty(fmt, B, cap, 512, 64)
+    cnt = orc.kv_compress(ca, za, None, None, o, m=m, overlap=0, first_pos=first, bias_a=ba, gamma=gamma,
+                          rope_theta=1e4)
+    assert cnt == 257 + 256
+    g = lca.KV.empty(fmt, B, cap, 512, 64)
+    w = None
+    if ws:
+        wsz = lca.compress_workspace_size(orc.BF16, m, 0, 512, 64)
+        w = torch.full((max(16, wsz),), 255, dtype=torch.uint8, device="cuda")
+    lca.kv_compress(dev(ca), dev(za), None, None, g, m=m, overlap=0, first_pos=first,
+                    bias_a=None if ba is None else dev(ba), gamma=dev(gamma), rope_theta=1e4, ws=w)
+    torch.cuda.synchronize()
+    assert_kv_close(kv_host(g), o)
+
+
 def test_kv_compress_ring_and_identity():
     """m = 1 without norm / RoPE stores the raw rows exactly; a ring keeps the newest cap rows."""
     B, n, c = 3, 300, 576
