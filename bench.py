@@ -1082,6 +1082,8 @@ def main():
     ap.add_argument("--paged", action="store_true", help="with --no-extra: still time the paged-cache decode")
     ap.add_argument("--prefill-only", action="store_true",
                     help="profiling mode: build the 1M stack, run its 4096-token chunk (3 reps), print nothing else")
+    ap.add_argument("--compressor-only", action="store_true",
+                    help="profiling mode: time the compressor's three calls, print their figures, nothing else")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB device copy (reference for rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -1099,6 +1101,11 @@ def main():
         pf = bench_prefill_1m(base, reps=3)
         log(f"1M prefill chunk: {pf['ms']:.2f} ms ({pf['tokens_per_s']:.0f} tok/s); kernels (ms): "
             + ", ".join(f"{k} {v:.3f}" for k, v in pf['kernel_ms'].items()))
+        return
+    if args.compressor_only:
+        cp = bench_compressor()
+        log("compressor: " + ", ".join(f"{k} {v['launch_ms'] * 1e3:.1f} us = {v['gbs']:.0f} GB/s ({v['bytes']} B)"
+                                       for k, v in cp.items()))
         return
 
     d = bench_decode_1m(W, K, R)
