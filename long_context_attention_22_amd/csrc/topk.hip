@@ -146,27 +146,6 @@ __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* wsum, 
     return v + off;
 }
 
-// sums of a and of b over the workgroup's NW waves, in every thread (wsum: 2 NW words)
-template <int NW>
-__device__ __forceinline__ void block_sum2(uint32_t a, uint32_t b, uint32_t* wsum, uint32_t* sa, uint32_t* sb) {
-    const int wv = threadIdx.x >> 6;
-    a = wave_lane63(wave_incl_scan(a));
-    b = wave_lane63(wave_incl_scan(b));
-    if ((threadIdx.x & 63) == 0) {
-        wsum[wv] = a;
-        wsum[NW + wv] = b;
-    }
-    __syncthreads();
-    uint32_t x = 0, y = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        x += wsum[w];
-        y += wsum[NW + w];
-    }
-    *sa = x;
-    *sb = y;
-}
-
 // Find the digit d with (count of digits > d) < rem <= (count of digits >= d).
 // Run by one wave over hsum[256]; writes *digit and *rem_out (rem minus keys above d).
 __device__ __forceinline__ void pick_digit(const uint32_t* hsum, uint32_t rem, uint32_t* digit,
@@ -670,6 +649,45 @@ __device__ __forceinline__ void store_packed(const uint32_t* hs, uint32_t* col) 
     if (t < kTopkHistWords) col[t] = hs[2 * t] | (hs[2 * t + 1] << 16);
 }
 
+// After col_sums: lane l of wave 0 takes bins 4l .. 4l + 3 (words 2l, 2l + 1 of the packed columns) --
+// their totals over every chunk and their sums over the chunks before g_me -- from col_sums' LDS parts.
+__device__ __forceinline__ void col_quad(const uint32_t* red, int l, uint32_t* tot, uint32_t* pre) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int w = 2 * l + (j >> 1), hf = j & 1;
+        tot[j] = red[hf * 128 + w] + red[(4 + hf) * 128 + w] + red[(8 + hf) * 128 + w] + red[(12 + hf) * 128 + w];
+        pre[j] = red[(2 + hf) * 128 + w] + red[(6 + hf) * 128 + w] + red[(10 + hf) * 128 + w] +
+                 red[(14 + hf) * 128 + w];
+    }
+}
+
+// pick_digit on bins held in registers, four per lane of one wave (lane l: bins 4l .. 4l + 3); every lane
+// of the wave gets the digit and the remainder.  0 < rem <= the bins' total, so one lane's bins hold it.
+__device__ __forceinline__ void pick_digit_regs(const uint32_t* hq, uint32_t rem, uint32_t* digit,
+                                                uint32_t* rem_out) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t loc = hq[0] + hq[1] + hq[2] + hq[3];
+    const uint32_t incl = wave_incl_scan(loc);
+    const uint32_t above = wave_lane63(incl) - incl;
+    const bool mine = above < rem && above + loc >= rem;
+    uint32_t d = 0, ro = 0;
+    if (mine) {
+        uint32_t acc = above;
+        for (int j = 3; j >= 0; --j) {
+            if (acc + hq[j] >= rem) {
+                d = 4 * lane + j;
+                ro = rem - acc;
+                break;
+            }
+            acc += hq[j];
+        }
+    }
+    const uint64_t m = __builtin_amdgcn_ballot_w64(mine);
+    const int src = m ? (int)__builtin_ctzll(m) : 0;
+    *digit = (uint32_t)__builtin_amdgcn_readlane((int)d, src);
+    *rem_out = (uint32_t)__builtin_amdgcn_readlane((int)ro, src);
+}
+
 __global__ void __launch_bounds__(kSplitThreads) topk_split_h1(TopkArgs a, int G) {
     const SplitRow r = split_row(a, G);
     const int g = blockIdx.x;
@@ -685,56 +703,56 @@ __global__ void __launch_bounds__(kSplitThreads) topk_split_h1(TopkArgs a, int G
 
 // Second digit: every chunk finds the high byte d1 from the column totals of h1 and counts the low
 // bytes of its keys in bucket d1; it also leaves, for the third launch, the number of keys above
-// d1 in the chunks before it.
+// d1 in the chunks before it.  Wave 0 finishes the column sums and picks d1 in registers; only
+// bucket d1's keys are counted, so the low-byte histogram keeps four LDS copies (lane mod 4),
+// cleared before the column sums' barrier.
 __global__ void __launch_bounds__(kSplitThreads) topk_split_h2(TopkArgs a, int G) {
     const SplitRow r = split_row(a, G);
     const int g = blockIdx.x, tid = threadIdx.x;
     const int64_t lo = (int64_t)g * kChunk;
-    __shared__ uint32_t hist[256 * 16];  // (also the column sums' LDS)
-    __shared__ uint32_t hs[256];
-    __shared__ uint32_t d1, rem1;
-    __shared__ uint32_t wsum[2 * (kSplitThreads / 64)];
+    __shared__ uint32_t red[16 * 128];  // the column sums' LDS
+    __shared__ uint32_t hl[4 * 256];    // low-byte counts: bin b, copy c at 4 b + c
+    __shared__ uint32_t d1, rem1, above1;
+    for (int j = tid; j < 4 * 256; j += kSplitThreads) hl[j] = 0;
     uint32_t h[kBlk];
     load_lane_keys(r, lo, h);
     uint32_t t1[2] = {0u, 0u}, p1[2] = {0u, 0u};
-    col_sums(r.h1, G, g, hist, t1, p1);
+    col_sums(r.h1, G, g, red, t1, p1);
     if (r.n <= r.K) return;  // (uniform) every candidate is kept: the emit launch lists them
     mask_lane_keys(lo, min(lo + kChunk, r.n), h);
-    if (tid < 128) {
-        hs[2 * tid] = t1[0];
-        hs[2 * tid + 1] = t1[1];
+    if (tid < 64) {
+        uint32_t tq[4], pq[4], d, rm;
+        col_quad(red, tid, tq, pq);
+        pick_digit_regs(tq, (uint32_t)r.K, &d, &rm);
+        uint32_t pa = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pa += (uint32_t)(4 * tid + j) > d ? pq[j] : 0u;
+        const uint32_t ab = wave_lane63(wave_incl_scan(pa));
+        if (tid == 0) {
+            d1 = d;
+            rem1 = rm;
+            above1 = ab;
+        }
     }
     __syncthreads();
-    if (tid < 64) pick_digit(hs, (uint32_t)r.K, &d1, &rem1);
-    __syncthreads();
     const uint32_t hb = d1;
-    uint32_t above, unused;
-    const uint32_t pa = tid < 128 ? ((uint32_t)(2 * tid) > hb ? p1[0] : 0u) + ((uint32_t)(2 * tid + 1) > hb ? p1[1] : 0u)
-                                  : 0u;
-    block_sum2<kSplitThreads / 64>(pa, 0u, wsum, &above, &unused);
-    if (tid == 0) *(u32x4*)(r.meta + 4 * g) = u32x4{above, hb, rem1, 0u};
     // low bytes of the keys in bucket hb: keys above (hb, 0) - 1 and not above (hb, 255); the bucket
     // holds keys of one sign, so the low byte is the raw one, inverted for negatives
     const KeyCut in_lo = key_cut((int)(hb << 8) - 1), in_hi = key_cut((int)((hb << 8) | 255u));
     const uint32_t flip = hb >= 0x80u ? 0u : 255u;
-    for (int j = tid; j < 256 * 16; j += kSplitThreads) hist[j] = 0;
-    __syncthreads();
-    const int sub = tid & 15;
+    const int sub = tid & 3;
 #pragma unroll
     for (int u = 0; u < kBlk; ++u) {
         const bool in = in_lo.gt(h[u]) && !in_hi.gt(h[u]);
         if (__builtin_amdgcn_ballot_w64(in) != 0 && in)
-            atomicAdd(&hist[(((h[u] & 255u) ^ flip) << 4) + sub], 1u);
+            atomicAdd(&hl[(((h[u] & 255u) ^ flip) << 2) + sub], 1u);
     }
     __syncthreads();
-    if (tid < 256) {
-        uint32_t s = 0;
-#pragma unroll
-        for (int c = 0; c < 16; ++c) s += hist[tid * 16 + ((c + tid) & 15)];
-        hs[tid] = s;
+    if (tid == 0) *(u32x4*)(r.meta + 4 * g) = u32x4{above1, hb, rem1, 0u};
+    if (tid < kTopkHistWords) {  // bins 2 tid and 2 tid + 1, packed
+        const uint32_t* q = hl + 8 * tid;
+        r.h2[g * kTopkHistWords + tid] = (q[0] + q[1] + q[2] + q[3]) | ((q[4] + q[5] + q[6] + q[7]) << 16);
     }
-    __syncthreads();
-    store_packed(hs, r.h2 + g * kTopkHistWords);
 }
 
 // Emission: the threshold key tau = (d1, d2) and the number rem of keys equal to it to keep; keys
@@ -762,29 +780,32 @@ __global__ void __launch_bounds__(kSplitThreads) topk_split_emit(TopkArgs a, int
     }
     const int64_t hi = min(lo + kChunk, r.n);
     mask_lane_keys(lo, hi, h);
-    __shared__ uint32_t tot2[256];
-    __shared__ uint32_t d2, rem2;
-    __shared__ uint32_t wsum[2 * (kSplitThreads / 64)];
-    if (tid < 128) {
-        tot2[2 * tid] = t2[0];
-        tot2[2 * tid + 1] = t2[1];
-    }
-    __syncthreads();
+    // wave 0: the low byte d2 of tau from h2's column totals, and the keys above tau and equal to it in
+    // the chunks before this one
+    __shared__ uint32_t d2, rem2, bgt, beq;
     const uint32_t above1 = mt[0], d1 = mt[1], rem1 = mt[2];
-    if (tid < 64) pick_digit(tot2, rem1, &d2, &rem2);
+    if (tid < 64) {
+        uint32_t tq[4], pq[4], d, rm;
+        col_quad(red, tid, tq, pq);
+        pick_digit_regs(tq, rem1, &d, &rm);
+        uint32_t gt = 0, eq = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            gt += (uint32_t)(4 * tid + j) > d ? pq[j] : 0u;
+            eq += (uint32_t)(4 * tid + j) == d ? pq[j] : 0u;
+        }
+        const uint32_t sg = wave_lane63(wave_incl_scan(gt)), se = wave_lane63(wave_incl_scan(eq));
+        if (tid == 0) {
+            d2 = d;
+            rem2 = rm;
+            bgt = sg;
+            beq = se;
+        }
+    }
     __syncthreads();
     const uint32_t tau = (d1 << 8) | d2, rem = rem2;
     if (g == 0)
         for (int64_t j = r.K + tid; j < kk; j += kSplitThreads) r.out[j] = -1;
-    // keys above tau and equal to tau in the chunks before this one (threads t < 128: low bytes 2t, 2t + 1)
-    uint32_t base_gt, base_eq;
-    {
-        const uint32_t b0 = 2 * (uint32_t)tid, b1 = b0 + 1;
-        const uint32_t gt = tid < 128 ? (b0 > d2 ? p2[0] : 0u) + (b1 > d2 ? p2[1] : 0u) : 0u;
-        const uint32_t eq = tid < 128 ? (b0 == d2 ? p2[0] : 0u) + (b1 == d2 ? p2[1] : 0u) : 0u;
-        block_sum2<kSplitThreads / 64>(gt, eq, wsum, &base_gt, &base_eq);
-        base_gt += above1;
-    }
     // this wave's keys above tau and equal to it, then the waves before it
     const KeyCut cut = key_cut((int)tau);
     uint32_t ngt = 0, neq = 0;
@@ -800,7 +821,7 @@ __global__ void __launch_bounds__(kSplitThreads) topk_split_emit(TopkArgs a, int
         weq[wv] = neq;
     }
     __syncthreads();
-    uint32_t gt_run = base_gt, eq_run = base_eq;
+    uint32_t gt_run = above1 + bgt, eq_run = beq;
 #pragma unroll
     for (int w = 0; w < kSplitThreads / 64; ++w) {
         gt_run += w < wv ? wgt[w] : 0u;
