@@ -403,13 +403,16 @@ def _nibbles(b: np.ndarray) -> np.ndarray:
     return out
 
 
-@pytest.mark.parametrize("m,overlap,dn,split", [(4, 1, 128, False), (1, 0, 128, False), (1, 0, 64, False),
-                                               (1, 0, 576, False), (128, 0, 128, False), (128, 0, 128, True)])
-def test_kv_compress_mxfp4(m, overlap, dn, split):
+@pytest.mark.parametrize("m,overlap,dn,split,nblk", [(4, 1, 128, False, 0), (1, 0, 128, False, 0),
+                                                    (1, 0, 64, False, 0), (1, 0, 576, False, 0),
+                                                    (128, 0, 128, False, 3), (128, 0, 128, True, 3),
+                                                    (128, 0, 128, False, 257)])
+def test_kv_compress_mxfp4(m, overlap, dn, split, nblk):
     """MXFP4 rows against the oracle: identical scale bytes and codes, except where the fp32 value the
     library rounds sits within 1e-5 (relative) of a decision boundary of the oracle's fp64 value: a block
-    maximum at a power of two (scale one step apart), or an element at a midpoint between two codes."""
-    B, n = 2, 203 if m < 128 else 3 * m + 5
+    maximum at a power of two (scale one step apart), or an element at a midpoint between two codes.
+    nblk = 257: 513 entries over the two sequences, pooled two per workgroup."""
+    B, n = 2, 203 if m < 128 else nblk * m + 5
     first = [0, 2 * m + 1]
     ca, za, cb, zb = _raw(31 + m, B, n, dn)
     ba = S.normal(4, "bias_a", (m, dn))
