@@ -10,7 +10,8 @@
 // compacts the winners with a block-wide exclusive scan, which yields the
 // ascending output and the lower-index tie rule directly.  Histograms live
 // in LDS with 16 copies (one per lane mod 16) so that lanes sharing a bin
-// rarely hit the same LDS word.
+// rarely hit the same LDS word; the split schedule's second-digit histogram,
+// which counts only the threshold bucket's keys, keeps four.
 //
 // Two schedules:
 //   row   -- one 1024-thread workgroup per row (many rows: prefill); rows are
